@@ -1,0 +1,406 @@
+"""Plain, slow, obviously-correct CPU oracle of the fused deterministic MoE layer.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or call this module.  The GPU library never uses
+it, shares no code with it, and must fail loudly rather than fall back to it.
+
+Everything is float64 numpy.  Inputs arrive as numpy arrays (bf16 values are
+widened exactly through float32).  Library primitives used as steps: stable
+argsort, bincount, cumsum and dense matmul.  No blocking, no fusion and no
+reordering beyond the definitions below.
+
+Pages followed (cited by title and section):
+  [kucoin]  kucoin.com, «Cursor's MoK réalise une amélioration des performances
+            de 2,37x sur NVIDIA GB300 NVL72», sections 01, 02 and 03.
+  [fluid]   fluidifia.com, «Cursor ouvre MoK, un mégakernel qui accélère
+            l'entraînement MoE», sections «Quand la communication devient le
+            vrai problème» and «Comment MoK tente de gratter des millisecondes
+            partout».
+  [martel]  laura-martel.com post on Cursor's Mixture-of-Kittens, section «Le
+            déterminisme est la partie sous-estimée».
+
+What the layer computes (the method reaches exactly this result, only fused and
+faster; [kucoin §03] says the benchmarked layer covers routing, expert FFNs,
+combine and the final weighted sum):
+  1. router: each token picks k experts from its router logits [kucoin §01];
+  2. layout: count the pairs per expert, place every pair in an expert-
+     contiguous buffer [kucoin §01, §02 (pull dispatch places rows locally)];
+  3. expert FFN (SwiGLU, [kucoin §02 on MXFP8 fused into SwiGLU]) per expert
+     over its contiguous rows (a grouped GEMM [kucoin §01]);
+  4. combine: send every expert output back to its token and take the
+     gate-weighted sum [kucoin §01, §03];
+  5. backward: the same steps mirrored (reverse-combine, expert backward,
+     reverse-dispatch) [kucoin §01, §02].
+
+Readings taken where the pages are silent:
+  * gates: softmax over all E logits, then top-k, no renormalisation;
+  * top-k compares the raw float32 logits; ties go to the lower expert index;
+    slot j = 0 is the largest;
+  * expert rows are stable: within an expert, ascending pair id p = t*k + j;
+  * offsets: unpadded exclusive prefix sum with E+1 entries;
+  * dropless (no capacity) [fluid, «Comment MoK…»: the ring buffer avoids
+    throwing tokens away];
+  * FFN: h = silu(x W1^T) * (x W3^T), y = h W2^T, W1 = gate, W3 = up, no bias;
+  * the gate multiplies y in the combine; combine sums over j = 0..k-1 in
+    ascending order (any fixed order gives run-to-run identical results, which
+    is what [martel] claims; j order is the plainest);
+  * MXFP8 follows the OCP Microscaling v1.0 conversion (blocks of 32 along the
+    contraction axis, E8M0 shared scale 2^(floor(log2 amax) - 8), elements
+    rounded to nearest-even E4M3 with saturation at +-448).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "route", "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
+    "forward", "backward", "combine", "loss",
+    "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
+    "forward_token",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ router
+
+def route(logits, k: int):
+    """Softmax routing with stable top-k.
+
+    The router decides per step and per token which experts it goes to, and each
+    token selects several experts [kucoin §01].  Order of experts for token t:
+    a precedes b iff logit_a > logit_b, or the logits are equal and a < b.  The
+    comparison uses the raw float32 logits (so the GPU and CPU agree exactly on
+    the selection); the probabilities are float64.
+
+    Returns idx [T,k] int32, gate [T,k] float64 (softmax probability of the
+    chosen experts, not renormalised), lse [T] float64, p [T,E] float64.
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    if l32.ndim != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = l32.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    if not np.isfinite(l32).all():
+        raise ValueError("router logits must be finite")
+    # stable sort of the negated logits keeps equal logits in index order;
+    # -0.0 and +0.0 compare equal, as in the comparison above.
+    order = np.argsort(-l32, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    l = l32.astype(np.float64)
+    m = l.max(axis=1, keepdims=True) if E else np.zeros((T, 1))
+    ex = np.exp(l - m)
+    s = ex.sum(axis=1, keepdims=True)
+    p = ex / s
+    lse = (m + np.log(s))[:, 0]
+    gate = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    return idx, gate, lse, p
+
+
+# ------------------------------------------------------------------ layout
+
+def layout(idx, E: int, expert_begin: int = 0, expert_end: int | None = None):
+    """Counting-sort placement of token-expert pairs into expert-contiguous rows.
+
+    First count the pairs per expert, then decide where each pair goes, keeping
+    one expert's rows together so a grouped GEMM sees structured input
+    [kucoin §01]; the receiver chooses its own local placement [kucoin §02].
+    Only experts in [expert_begin, expert_end) are local; other pairs get no row.
+
+    Pair id p = t*k + j.  Rows are ordered by (expert, p): stable within an
+    expert.  Returns counts [E] int64 (0 for non-local experts), offsets [E+1]
+    (exclusive prefix sum, offsets[E] = P), row_of_pair [T*k] int64 (-1 where
+    non-local) and pair_of_row [P] int64.
+    """
+    idx = np.asarray(idx)
+    if expert_end is None:
+        expert_end = E
+    e = idx.reshape(-1).astype(np.int64)
+    local = (e >= expert_begin) & (e < expert_end)
+    counts = np.bincount(e[local], minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    local_pairs = np.nonzero(local)[0]
+    pair_of_row = local_pairs[np.argsort(e[local], kind="stable")]
+    row_of_pair = np.full(e.shape[0], -1, dtype=np.int64)
+    row_of_pair[pair_of_row] = np.arange(pair_of_row.shape[0], dtype=np.int64)
+    return counts, offsets, row_of_pair, pair_of_row
+
+
+def permute(x, pair_of_row, k: int):
+    """Dispatch: row r of the expert-contiguous buffer is the activation of the
+    token of pair pair_of_row[r] (token = pair // k) [kucoin §01, §02]."""
+    return _f64(x)[np.asarray(pair_of_row) // k]
+
+
+def unpermute_sum(rows, row_of_pair, T: int, k: int, weights=None):
+    """out[t] = sum over j = 0..k-1 (ascending) of weights[t,j] * rows[row(t,j)],
+    skipping pairs with no row.  weights None means all ones."""
+    rows = _f64(rows)
+    rop = np.asarray(row_of_pair).reshape(T, k)
+    out = np.zeros((T,) + rows.shape[1:], dtype=np.float64)
+    for j in range(k):
+        sel = rop[:, j]
+        m = sel >= 0
+        w = 1.0 if weights is None else _f64(weights)[m, j][:, None]
+        out[m] += w * rows[sel[m]]
+    return out
+
+
+def combine(Y, gate, row_of_pair, T: int, k: int):
+    """Combine and the final weighted sum: out_t = sum_j gate[t,j] * y_(t,j),
+    j ascending [kucoin §01, §03; martel on determinism]."""
+    return unpermute_sum(Y, row_of_pair, T, k, weights=gate)
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def silu(z):
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def expert_ffn(Xe, W1e, W3e, W2e):
+    """SwiGLU expert [kucoin §02 names SwiGLU as the activation]:
+    a = X W1^T, b = X W3^T, h = silu(a) * b, y = h W2^T."""
+    Xe = _f64(Xe)
+    a = Xe @ _f64(W1e).T
+    b = Xe @ _f64(W3e).T
+    h = silu(a) * b
+    y = h @ _f64(W2e).T
+    return a, b, h, y
+
+
+# ------------------------------------------------------------------ MXFP8
+
+E4M3_MAX = 448.0
+_E4M3_EMAX = 8          # exponent of the largest power of two <= 448
+
+
+def e4m3_encode(v):
+    """Round float64 values to OCP E4M3 (bias 7, no infinities) codes.
+
+    Round to nearest, ties to even; magnitudes above 448 saturate to 448; the
+    sign of zero is kept.  Normal values have 3 fraction bits, so the spacing in
+    [2^e, 2^(e+1)) is 2^(e-3); below 2^-6 the spacing is 2^-9 (subnormals)."""
+    v = _f64(v)
+    if not np.isfinite(v).all():
+        raise ValueError("e4m3_encode expects finite values")
+    sign = np.signbit(v)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    _, ex = np.frexp(a)                       # a = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                # floor(log2 a), at least -6
+    q = np.ldexp(1.0, e - 3)                  # spacing of representable values
+    n = np.rint(a / q)                        # exact division by a power of 2; RNE
+    val = n * q                               # representable (may move up a binade)
+    _, ex2 = np.frexp(val)
+    e2 = ex2 - 1
+    normal = val >= 2.0 ** -6
+    code_norm = ((e2 + 7) << 3) | (np.rint(np.ldexp(val, -e2) * 8).astype(np.int64) - 8)
+    code_sub = np.rint(val / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_norm, code_sub)
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_decode(codes):
+    """Value of E4M3 codes (S.EEEE.MMM, bias 7; S.1111.111 is NaN)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return s * val
+
+
+def mxfp8_quantize(v, block: int = 32):
+    """MX block quantisation along the last axis [kucoin §02: MXFP8 activation
+    quantisation fused into the dispatch, grouped GEMM and SwiGLU paths].
+
+    Per block of 32: X = 2^(floor(log2 amax) - 8), stored as E8M0 byte
+    (unbiased exponent + 127, exponent clamped to [-127, 127]); an all-zero block
+    stores byte 0.  Elements become E4M3(v / X).  Returns (codes uint8 of v's
+    shape, scales uint8 of shape [..., K/32])."""
+    v = _f64(v)
+    K = v.shape[-1]
+    if K % block:
+        raise ValueError("last axis must be a multiple of the block size")
+    vb = v.reshape(v.shape[:-1] + (K // block, block))
+    amax = np.abs(vb).max(axis=-1)
+    _, ex = np.frexp(amax)
+    sexp = np.clip(ex - 1 - _E4M3_EMAX, -127, 127)
+    sexp = np.where(amax == 0, -127, sexp)
+    codes = e4m3_encode(vb / np.ldexp(1.0, sexp)[..., None])
+    return codes.reshape(v.shape), (sexp + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales, block: int = 32):
+    c = e4m3_decode(codes)
+    K = c.shape[-1]
+    cb = c.reshape(c.shape[:-1] + (K // block, block))
+    x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)[..., None]
+    return (cb * x).reshape(c.shape)
+
+
+def mxfp8_qdq(v, block: int = 32):
+    return mxfp8_dequantize(*mxfp8_quantize(v, block), block)
+
+
+# ------------------------------------------------------------------ forward
+
+def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: int | None = None,
+            mxfp8: bool = False):
+    """Whole-layer forward in float64.
+
+    x [T,d]; logits [T,E] float32; W1, W3 [E_loc,F,d]; W2 [E_loc,d,F] with
+    E_loc = expert_end - expert_begin (weights of expert e at e - expert_begin).
+    In MXFP8 mode x rows and W1/W3 rows are quantised along d, W2 rows along F,
+    and h along F before the second product (gates, softmax and the combine stay
+    float64).  Returns a dict with idx, gate, lse, p, counts, offsets,
+    row_of_pair, pair_of_row, A, B, H, Y (per row, unscaled) and out [T,d].
+    """
+    x = _f64(x)
+    T, d = x.shape
+    E = np.asarray(logits).shape[1]
+    if expert_end is None:
+        expert_end = E
+    idx, gate, lse, p = route(logits, k)
+    counts, offsets, row_of_pair, pair_of_row = layout(idx, E, expert_begin, expert_end)
+    Xp = permute(x, pair_of_row, k)
+    F = np.asarray(W1).shape[1]
+    P = pair_of_row.shape[0]
+    A = np.zeros((P, F)); B = np.zeros((P, F)); H = np.zeros((P, F)); Y = np.zeros((P, d))
+    for e in range(expert_begin, expert_end):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r0 == r1:
+            continue
+        w1, w3, w2 = W1[e - expert_begin], W3[e - expert_begin], W2[e - expert_begin]
+        Xe = Xp[r0:r1]
+        if mxfp8:
+            Xe, w1, w3, w2 = mxfp8_qdq(Xe), mxfp8_qdq(w1), mxfp8_qdq(w3), mxfp8_qdq(w2)
+            a = Xe @ _f64(w1).T
+            b = Xe @ _f64(w3).T
+            h = mxfp8_qdq(silu(a) * b)
+            y = h @ _f64(w2).T
+        else:
+            a, b, h, y = expert_ffn(Xe, w1, w3, w2)
+        A[r0:r1], B[r0:r1], H[r0:r1], Y[r0:r1] = a, b, h, y
+    out = combine(Y, gate, row_of_pair, T, k)
+    return dict(idx=idx, gate=gate, lse=lse, p=p, counts=counts, offsets=offsets,
+                row_of_pair=row_of_pair, pair_of_row=pair_of_row, A=A, B=B, H=H, Y=Y, out=out)
+
+
+def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int = 0,
+                  expert_end: int | None = None, mxfp8: bool = False):
+    """Output of one token alone (for sampled checks at full size): its top-k
+    experts from its own logits, the FFN of each local one, the gate-weighted
+    sum in slot order.  Returns (idx [k], gate [k], out [d], y per slot)."""
+    idx, gate, _, _ = route(np.asarray(logits_t, dtype=np.float32)[None, :], k)
+    E = np.asarray(logits_t).shape[0]
+    if expert_end is None:
+        expert_end = E
+    xt = _f64(x_t)[None, :]
+    out = np.zeros(xt.shape[1])
+    ys = []
+    for j in range(k):
+        e = int(idx[0, j])
+        if not expert_begin <= e < expert_end:
+            ys.append(None)
+            continue
+        w1, w3, w2 = W1[e - expert_begin], W3[e - expert_begin], W2[e - expert_begin]
+        if mxfp8:
+            xq = mxfp8_qdq(xt)
+            h = mxfp8_qdq(silu(xq @ mxfp8_qdq(w1).T) * (xq @ mxfp8_qdq(w3).T))
+            y = (h @ mxfp8_qdq(w2).T)[0]
+        else:
+            y = expert_ffn(xt, w1, w3, w2)[3][0]
+        ys.append(y)
+        out += gate[0, j] * y
+    return idx[0], gate[0], out, ys
+
+
+# ------------------------------------------------------------------ backward
+
+def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
+             expert_begin: int = 0, expert_end: int | None = None):
+    """Gradients of L = sum(out * dout) in float64.
+
+    The backward pass mirrors the forward: reverse-combine, expert backward,
+    reverse-dispatch [kucoin §01: two more communication steps in the reverse
+    direction; §02: pull reverse-combine, push reverse-dispatch].  The gradient
+    through the top-k selection itself is zero.
+
+      dgate[t,j]  = <dout_t, y_(t,j)>                       (0 for non-local pairs)
+      dlogits     = p * (G - <p, G>),  G[t,e] = dgate at the chosen e, else 0
+      dy_r        = gate_r * dout_t(r)                      (reverse-combine)
+      dh          = dy W2_e
+      da          = dh * b * sigmoid(a) * (1 + a (1 - sigmoid(a)))
+      db          = dh * silu(a)
+      dx_r        = da W1_e + db W3_e
+      dx_t        = sum_j dx_(t,j), j ascending              (reverse-dispatch)
+      dW2_e = dy_e^T h_e,  dW1_e = da_e^T x_e,  dW3_e = db_e^T x_e
+    """
+    x = _f64(x)
+    g = _f64(dout)
+    T, d = x.shape
+    E = np.asarray(logits).shape[1]
+    if expert_end is None:
+        expert_end = E
+    if fwd is None:
+        fwd = forward(x, logits, W1, W3, W2, k, expert_begin, expert_end)
+    gate, p, Y = fwd["gate"], fwd["p"], fwd["Y"]
+    rop = fwd["row_of_pair"].reshape(T, k)
+    offsets, pair_of_row = fwd["offsets"], fwd["pair_of_row"]
+    A, B, H = fwd["A"], fwd["B"], fwd["H"]
+
+    dgate = np.zeros((T, k))
+    for j in range(k):
+        m = rop[:, j] >= 0
+        dgate[m, j] = np.einsum("td,td->t", g[m], Y[rop[m, j]])
+    G = np.zeros((T, E))
+    np.put_along_axis(G, fwd["idx"].astype(np.int64), dgate, axis=1)
+    dlogits = p * (G - (p * G).sum(axis=1, keepdims=True))
+
+    tok = pair_of_row // k
+    slot = pair_of_row % k
+    dY = gate[tok, slot][:, None] * g[tok]
+    Xp = permute(x, pair_of_row, k)
+    F = np.asarray(W1).shape[1]
+    P = pair_of_row.shape[0]
+    dXp = np.zeros((P, d))
+    dA = np.zeros((P, F)); dB = np.zeros((P, F))
+    E_loc = expert_end - expert_begin
+    dW1 = np.zeros((E_loc, F, d)); dW3 = np.zeros((E_loc, F, d)); dW2 = np.zeros((E_loc, d, F))
+    for e in range(expert_begin, expert_end):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r0 == r1:
+            continue
+        i = e - expert_begin
+        a, b, h, dy = A[r0:r1], B[r0:r1], H[r0:r1], dY[r0:r1]
+        dh = dy @ _f64(W2[i])
+        s = sigmoid(a)
+        da = dh * b * s * (1.0 + a * (1.0 - s))
+        db = dh * silu(a)
+        dXp[r0:r1] = da @ _f64(W1[i]) + db @ _f64(W3[i])
+        dW2[i] = dy.T @ h
+        dW1[i] = da.T @ Xp[r0:r1]
+        dW3[i] = db.T @ Xp[r0:r1]
+        dA[r0:r1], dB[r0:r1] = da, db
+    dx = unpermute_sum(dXp, fwd["row_of_pair"], T, k)
+    return dict(dx=dx, dW1=dW1, dW3=dW3, dW2=dW2, dgate=dgate, dlogits=dlogits,
+                dY=dY, dA=dA, dB=dB, dXp=dXp)
+
+
+def loss(out, dout) -> float:
+    """L = sum(out * dout): the scalar whose gradients backward() returns."""
+    return float((_f64(out) * _f64(dout)).sum())

@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against things other than itself: brute force on tiny
+inputs, closed forms, invariants, special cases that reduce to a dense FFN,
+finite differences, and the E4M3 table of the OCP OFP8 specification."""
+import functools
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mok_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- router
+
+def _brute_topk(row, k):
+    """Selection by repeated scan: take the largest remaining logit, the lowest
+    index among equals, k times."""
+    remaining = list(range(len(row)))
+    out = []
+    for _ in range(k):
+        best = remaining[0]
+        for e in remaining[1:]:
+            if row[e] > row[best]:
+                best = e
+        out.append(best)
+        remaining.remove(best)
+    return out
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 2), (7, 3), (7, 7), (16, 6), (33, 8)])
+def test_topk_matches_brute_force_with_ties(E, k):
+    rng = _rng(E * 100 + k)
+    logits = rng.integers(-3, 4, size=(40, E)).astype(np.float32) * np.float32(0.5)
+    idx, _, _, _ = O.route(logits, k)
+    for t in range(logits.shape[0]):
+        assert list(idx[t]) == _brute_topk([float(v) for v in logits[t]], k)
+
+
+def test_topk_invariants_and_special_cases():
+    rng = _rng(1)
+    logits = rng.standard_normal((64, 32)).astype(np.float32)
+    idx, gate, _, p = O.route(logits, 5)
+    for t in range(64):
+        sel = set(idx[t].tolist())
+        unsel = [e for e in range(32) if e not in sel]
+        assert logits[t, idx[t]].min() >= logits[t, unsel].max()
+        assert all(logits[t, idx[t][j]] >= logits[t, idx[t][j + 1]] for j in range(4))
+    # all-equal logits: the k lowest indices, in order
+    idx_eq, gate_eq, _, _ = O.route(np.zeros((3, 10), np.float32), 4)
+    assert (idx_eq == np.arange(4)).all()
+    np.testing.assert_allclose(gate_eq, 0.1, rtol=0, atol=1e-15)
+    # k = E gives the full rank order
+    row = np.array([[0.5, -1.0, 2.0, 0.5, 3.0]], np.float32)
+    assert O.route(row, 5)[0][0].tolist() == [4, 2, 0, 3, 1]
+    # -0.0 and +0.0 tie; the lower index wins
+    z = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert O.route(z, 1)[0][0, 0] == 0
+    z2 = np.array([[0.0, -0.0, -1.0]], np.float32)
+    assert O.route(z2, 1)[0][0, 0] == 0
+    with pytest.raises(ValueError):
+        O.route(np.array([[np.nan, 1.0]], np.float32), 1)
+
+
+def test_softmax_closed_forms():
+    rng = _rng(2)
+    logits = (rng.standard_normal((50, 9)) * 4).astype(np.float32)
+    idx, gate, lse, p = O.route(logits, 3)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert ((gate > 0) & (gate <= 1)).all()
+    # lse = log sum exp, checked with math.fsum on each row
+    for t in range(5):
+        l = [float(v) for v in logits[t]]
+        assert abs(lse[t] - math.log(math.fsum(math.exp(v) for v in l))) < 1e-12
+    # two experts: p0 = 1 / (1 + exp(l1 - l0))
+    two = np.array([[1.25, -0.5]], np.float32)
+    _, g2, lse2, _ = O.route(two, 2)
+    assert abs(g2[0, 0] - 1.0 / (1.0 + math.exp(-1.75))) < 1e-15
+    assert abs(g2[0, 1] - 1.0 / (1.0 + math.exp(1.75))) < 1e-15
+    # equal logits c: lse = c + log E
+    _, _, lse3, _ = O.route(np.full((1, 6), 2.5, np.float32), 2)
+    assert abs(lse3[0] - (2.5 + math.log(6))) < 1e-14
+
+
+# ---------------------------------------------------------------- layout
+
+def _brute_layout(idx, E, b, e_end):
+    """Bucket placement: walk the experts in order, and within one expert walk
+    the pairs in id order, handing out consecutive rows."""
+    flat = [int(v) for v in np.asarray(idx).reshape(-1)]
+    row_of_pair = [-1] * len(flat)
+    pair_of_row = []
+    counts = [0] * E
+    for e in range(b, e_end):
+        for p, ep in enumerate(flat):
+            if ep == e:
+                row_of_pair[p] = len(pair_of_row)
+                pair_of_row.append(p)
+                counts[e] += 1
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    return counts, offsets, row_of_pair, pair_of_row
+
+
+@pytest.mark.parametrize("T,E,k,b,e_end", [(1, 1, 1, 0, 1), (13, 5, 2, 0, 5), (40, 8, 3, 2, 6),
+                                          (64, 16, 4, 0, 4), (37, 9, 9, 0, 9), (20, 6, 2, 5, 6)])
+def test_layout_matches_brute_force(T, E, k, b, e_end):
+    rng = _rng(T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx = O.route(logits, k)[0]
+    c, o, rop, por = O.layout(idx, E, b, e_end)
+    bc, bo, brop, bpor = _brute_layout(idx, E, b, e_end)
+    assert c.tolist() == bc and o.tolist() == bo
+    assert rop.tolist() == brop and por.tolist() == bpor
+
+
+def test_layout_invariants_with_empty_experts():
+    rng = _rng(3)
+    T, E, k = 500, 32, 6
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 7] -= 50.0          # expert 7 never chosen
+    logits[:, 3] += 50.0          # expert 3 always chosen
+    idx = O.route(logits, k)[0]
+    c, o, rop, por = O.layout(idx, E)
+    P = T * k
+    assert c.sum() == P and o[-1] == P and c[7] == 0 and c[3] == T
+    assert sorted(rop.tolist()) == list(range(P))            # bijection onto [0, P)
+    assert (rop[por] == np.arange(P)).all()
+    flat = idx.reshape(-1)
+    for e in range(E):
+        seg = por[o[e]:o[e + 1]]
+        assert (flat[seg] == e).all()
+        assert (np.diff(seg) > 0).all()                       # stable: pair ids ascend
+
+
+def test_permute_round_trip_and_all_ones_combine():
+    rng = _rng(4)
+    T, d, E, k = 30, 12, 6, 3
+    x = rng.standard_normal((T, d))
+    idx = O.route(rng.standard_normal((T, E)).astype(np.float32), k)[0]
+    _, _, rop, por = O.layout(idx, E)
+    Xp = O.permute(x, por, k)
+    rr = rop.reshape(T, k)
+    for t in range(T):
+        for j in range(k):
+            assert (Xp[rr[t, j]] == x[t]).all()
+    np.testing.assert_array_equal(O.unpermute_sum(Xp, rop, T, k), k * x)
+    ones = np.ones((T, k))
+    np.testing.assert_array_equal(O.combine(Xp, ones, rop, T, k), k * x)
+
+
+# ---------------------------------------------------------------- FFN
+
+def _scalar_swiglu(xv, W1, W3, W2):
+    """Pure-Python loops: a_f = sum_i W1[f][i] x_i, b_f likewise with W3,
+    h_f = a_f / (1 + e^-a_f) * b_f, y_n = sum_f W2[n][f] h_f."""
+    F, d = len(W1), len(xv)
+    h = []
+    for f in range(F):
+        a = math.fsum(W1[f][i] * xv[i] for i in range(d))
+        b = math.fsum(W3[f][i] * xv[i] for i in range(d))
+        h.append(a / (1.0 + math.exp(-a)) * b)
+    return [math.fsum(W2[n][f] * h[f] for f in range(F)) for n in range(len(W2))]
+
+
+def test_single_expert_top1_is_dense_ffn():
+    rng = _rng(5)
+    T, d, F = 4, 5, 7
+    x = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((1, F, d)); W3 = rng.standard_normal((1, F, d)); W2 = rng.standard_normal((1, d, F))
+    logits = rng.standard_normal((T, 1)).astype(np.float32)
+    r = O.forward(x, logits, W1, W3, W2, 1)
+    np.testing.assert_array_equal(r["gate"], 1.0)
+    for t in range(T):
+        ref = _scalar_swiglu(list(x[t]), W1[0].tolist(), W3[0].tolist(), W2[0].tolist())
+        np.testing.assert_allclose(r["out"][t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_shift_matrices_closed_form():
+    """W1 = cyclic shift by +1, W3 = 2 * identity, W2 = cyclic shift by +2 (n = d = F):
+    a_f = x_(f+1), b_f = 2 x_f, h_f = 2 x_f silu(x_(f+1)), y_i = h_(i+2).
+    A transposed operand would shift the other way."""
+    n = 6
+    S1 = np.zeros((n, n)); S2 = np.zeros((n, n))
+    for f in range(n):
+        S1[f, (f + 1) % n] = 1.0
+        S2[f, (f + 2) % n] = 1.0
+    x = np.array([[0.3, -1.2, 2.0, 0.7, -0.4, 1.1]])
+    r = O.forward(x, np.zeros((1, 1), np.float32), S1[None], 2 * np.eye(n)[None], S2[None], 1)
+    xs = x[0]
+    h = [2 * xs[f] * xs[(f + 1) % n] / (1 + math.exp(-xs[(f + 1) % n])) for f in range(n)]
+    expect = [h[(i + 2) % n] for i in range(n)]
+    np.testing.assert_allclose(r["out"][0], expect, rtol=1e-14, atol=1e-15)
+
+
+def test_identical_experts_scale_by_gate_sum():
+    rng = _rng(6)
+    T, d, F, E, k = 10, 8, 12, 5, 3
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((F, d)); w3 = rng.standard_normal((F, d)); w2 = rng.standard_normal((d, F))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = O.forward(x, logits, np.stack([w1] * E), np.stack([w3] * E), np.stack([w2] * E), k)
+    dense = O.expert_ffn(x, w1, w3, w2)[3]
+    np.testing.assert_allclose(r["out"], r["gate"].sum(axis=1)[:, None] * dense, rtol=1e-12, atol=1e-13)
+
+
+def test_combine_top1_unit_gate_and_linearity():
+    rng = _rng(7)
+    T, k, d = 9, 2, 4
+    Y = rng.standard_normal((T * k, d))
+    rop = rng.permutation(T * k)
+    g1 = rng.random((T, k)); g2 = rng.random((T, k))
+    a = O.combine(Y, g1 + 2 * g2, rop, T, k)
+    b = O.combine(Y, g1, rop, T, k) + 2 * O.combine(Y, g2, rop, T, k)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    rop1 = rng.permutation(T)
+    np.testing.assert_array_equal(O.combine(Y[:T], np.ones((T, 1)), rop1, T, 1), Y[:T][rop1])
+
+
+def test_local_expert_range_matches_masking():
+    """With a local range, out equals the full-range forward with the weights of
+    non-local experts set to zero."""
+    rng = _rng(8)
+    T, d, F, E, k, b, e_end = 25, 6, 10, 8, 3, 2, 5
+    x = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((E, F, d)); W3 = rng.standard_normal((E, F, d)); W2 = rng.standard_normal((E, d, F))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    part = O.forward(x, logits, W1[b:e_end], W3[b:e_end], W2[b:e_end], k, b, e_end)
+    Wz = W2.copy(); Wz[:b] = 0; Wz[e_end:] = 0
+    full = O.forward(x, logits, W1, W3, Wz, k)
+    np.testing.assert_allclose(part["out"], full["out"], rtol=1e-13, atol=1e-14)
+    assert part["offsets"][-1] == sum(1 for v in full["idx"].reshape(-1) if b <= v < e_end)
+
+
+# ---------------------------------------------------------------- backward
+
+def _fd_setup(seed=9, T=24, d=10, E=5, k=2, F=14):
+    rng = _rng(seed)
+    x = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((E, F, d)) * 0.3
+    W3 = rng.standard_normal((E, F, d)) * 0.3
+    W2 = rng.standard_normal((E, d, F)) * 0.3
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    g = rng.standard_normal((T, d))
+    return x, logits, W1, W3, W2, g, k
+
+
+def _L(x, logits, W1, W3, W2, g, k):
+    return O.loss(O.forward(x, logits, W1, W3, W2, k)["out"], g)
+
+
+def test_backward_matches_central_finite_differences():
+    x, logits, W1, W3, W2, g, k = _fd_setup()
+    bw = O.backward(g, x, logits, W1, W3, W2, k)
+    h = 1e-6
+    rng = _rng(10)
+
+    def check(name, arr, grad, n=25):
+        flat = arr.reshape(-1)
+        scale = np.abs(grad).max()
+        for i in rng.choice(flat.size, size=min(n, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + h; lp = _L(x, logits, W1, W3, W2, g, k)
+            flat[i] = old - h; lm = _L(x, logits, W1, W3, W2, g, k)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad.reshape(-1)[i]) <= 1e-6 * scale, (name, i, fd, grad.reshape(-1)[i])
+
+    check("x", x, bw["dx"])
+    check("W1", W1, bw["dW1"])
+    check("W3", W3, bw["dW3"])
+    check("W2", W2, bw["dW2"])
+    # logits: only tokens whose k-th / (k+1)-th margin keeps the selection fixed.
+    # The logits are float32 for the selection, so perturb a float64 copy that
+    # route() would round; instead check d(loss)/d(logit) through the gates with
+    # the selection frozen: L(l) = sum_j softmax(l)[idx_j] * <g, y_j>.
+    fw = O.forward(x, logits, W1, W3, W2, k)
+    T, E = logits.shape
+    srt = np.sort(logits.astype(np.float64), axis=1)[:, ::-1]
+    ok = np.nonzero(srt[:, k - 1] - srt[:, k] > 1e-4)[0]
+    assert ok.size > 10
+    for t in ok[:10]:
+        yj = [fw["Y"][fw["row_of_pair"][t * k + j]] for j in range(k)]
+        coef = [float(np.dot(g[t], yj[j])) for j in range(k)]
+        l = logits[t].astype(np.float64)
+        for e in range(E):
+            def f(v):
+                ll = l.copy(); ll[e] = v
+                pp = np.exp(ll - ll.max()); pp /= pp.sum()
+                return sum(pp[fw["idx"][t, j]] * coef[j] for j in range(k))
+            fd = (f(l[e] + h) - f(l[e] - h)) / (2 * h)
+            assert abs(fd - bw["dlogits"][t, e]) <= 1e-8 + 1e-6 * np.abs(bw["dlogits"][t]).max()
+    # dgate is the derivative of the loss with respect to each gate value
+    for t in range(3):
+        for j in range(k):
+            assert abs(bw["dgate"][t, j] - float(np.dot(g[t], fw["Y"][fw["row_of_pair"][t * k + j]]))) < 1e-12
+
+
+def test_backward_dense_special_case():
+    """E = 1, k = 1: the layer is a dense SwiGLU FFN; check dx and dW against
+    finite differences of the scalar-loop FFN."""
+    rng = _rng(11)
+    T, d, F = 3, 4, 5
+    x = rng.standard_normal((T, d)); g = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((1, F, d)); W3 = rng.standard_normal((1, F, d)); W2 = rng.standard_normal((1, d, F))
+    logits = np.zeros((T, 1), np.float32)
+    bw = O.backward(g, x, logits, W1, W3, W2, 1)
+
+    def Ls(xx, w1, w3, w2):
+        return math.fsum(g[t][n] * v for t in range(T)
+                         for n, v in enumerate(_scalar_swiglu(list(xx[t]), w1.tolist(), w3.tolist(), w2.tolist())))
+    h = 1e-6
+    for arr, grad, args in [(x, bw["dx"], None), (W1[0], bw["dW1"][0], None), (W2[0], bw["dW2"][0], None)]:
+        flat = arr.reshape(-1)
+        for i in range(0, flat.size, 3):
+            old = flat[i]
+            flat[i] = old + h; lp = Ls(x, W1[0], W3[0], W2[0])
+            flat[i] = old - h; lm = Ls(x, W1[0], W3[0], W2[0])
+            flat[i] = old
+            assert abs((lp - lm) / (2 * h) - grad.reshape(-1)[i]) < 1e-6 * max(1.0, np.abs(grad).max())
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def _golden_e4m3():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_ocp_ofp8.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                c, v = line.split()
+                rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def test_e4m3_table_from_ofp8_spec():
+    rows = _golden_e4m3()
+    codes = np.array([c for c, _ in rows])
+    vals = np.array([v for _, v in rows])
+    dec = O.e4m3_decode(codes)
+    np.testing.assert_array_equal(dec, vals)
+    np.testing.assert_array_equal(np.signbit(dec), np.signbit(vals))
+    np.testing.assert_array_equal(O.e4m3_encode(vals), codes.astype(np.uint8))
+    assert np.isnan(O.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+
+
+def test_e4m3_every_code_round_trips_and_rounding_rules():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    np.testing.assert_array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes.astype(np.uint8))
+    enc = lambda v: int(O.e4m3_encode(np.array([v]))[0])
+    assert enc(1.0625) == 0x38            # tie between 1.0 and 1.125 -> even (1.0)
+    assert enc(1.1875) == 0x3A            # tie between 1.125 and 1.25 -> even (1.25)
+    assert enc(1.0625 + 1e-9) == 0x39     # just above the tie rounds up
+    assert enc(0.5 * 2 ** -9) == 0x00     # subnormal tie -> even (0)
+    assert enc(1.5 * 2 ** -9) == 0x02     # subnormal tie -> even (2 * 2^-9)
+    assert enc(2 ** -6 - 2 ** -11) == 0x08  # rounds up into the first normal binade
+    assert enc(464.0) == 0x7E and enc(500.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(-1e-6) == 0x80             # sign of zero kept
+    assert enc(15.5) == 0x58              # tie between 15 and 16 -> 16 = 0x58 (even mantissa)
+
+
+def test_mxfp8_quantize_invariants_and_hand_blocks():
+    rng = _rng(12)
+    v = rng.standard_normal((16, 256)) * np.exp(rng.standard_normal((16, 1)) * 3)
+    codes, scales = O.mxfp8_quantize(v)
+    q = O.e4m3_decode(codes)
+    assert np.abs(q).max() <= 448
+    dq = O.mxfp8_dequantize(codes, scales)
+    vb = v.reshape(16, 8, 32)
+    amax = np.abs(vb).max(axis=-1)
+    # scale exponent = floor(log2 amax) - 8
+    np.testing.assert_array_equal(scales.astype(np.int64) - 127, np.floor(np.log2(amax)).astype(np.int64) - 8)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+    normal = np.abs(vb) / X >= 2.0 ** -6
+    rel = np.abs(dq.reshape(16, 8, 32) - vb) / np.abs(vb)
+    assert rel[normal & (np.abs(vb) / X <= 448)].max() <= 2.0 ** -4
+    np.testing.assert_array_equal(O.mxfp8_qdq(dq), dq)       # idempotent
+    # all-zero block
+    c0, s0 = O.mxfp8_quantize(np.zeros((1, 32)))
+    assert s0[0, 0] == 0 and (c0 == 0).all()
+    # amax exactly 2^5: scale 2^-3, the amax element is 256 = code 0x78
+    blk = np.zeros((1, 32)); blk[0, 3] = -32.0; blk[0, 9] = 1.0
+    c1, s1 = O.mxfp8_quantize(blk)
+    assert s1[0, 0] == 127 - 3 and c1[0, 3] == 0xF8 and c1[0, 9] == 0x50   # 1.0 / 2^-3 = 8.0
+    # amax in (448 X, 512 X) saturates: amax 62.5 -> X = 2^-3, 62.5 / X = 500 -> 448
+    blk2 = np.zeros((1, 32)); blk2[0, 0] = 62.5
+    c2, s2 = O.mxfp8_quantize(blk2)
+    assert s2[0, 0] == 124 and c2[0, 0] == 0x7E
+    assert O.mxfp8_dequantize(c2, s2)[0, 0] == 56.0
+
+
+def test_mxfp8_forward_reduces_to_plain_when_exact():
+    """Values that MXFP8 represents exactly pass through unchanged; with an
+    identity-like W2 and representable h the MXFP8 forward equals the plain one."""
+    rng = _rng(13)
+    T, d, F = 6, 32, 32
+    x = O.mxfp8_qdq(rng.standard_normal((T, d)))
+    W1 = O.mxfp8_qdq(rng.standard_normal((1, F, d)) * 0.1)
+    np.testing.assert_array_equal(O.mxfp8_qdq(x), x)
+    np.testing.assert_array_equal(O.mxfp8_qdq(W1), W1)
+    W3 = O.mxfp8_qdq(rng.standard_normal((1, F, d)) * 0.1)
+    W2 = np.eye(d)[None]
+    logits = np.zeros((T, 1), np.float32)
+    m = O.forward(x, logits, W1, W3, W2, 1, mxfp8=True)
+    p = O.forward(x, logits, W1, W3, W2, 1)
+    np.testing.assert_allclose(m["out"], O.mxfp8_qdq(p["H"]), rtol=0, atol=0)
