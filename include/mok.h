@@ -1,0 +1,197 @@
+/*
+ * mok.h — C ABI of the fused, deterministic mixture-of-experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (forward): router softmax + stable top-k, counting-sort dispatch
+ * of token-expert pairs into an expert-contiguous buffer, expert-grouped
+ * SwiGLU FFN GEMMs (BF16, MXFP8 or FP32), and a gate-weighted combine in a
+ * fixed summation order.  Backward mirrors it and returns dX, dW1/dW3/dW2,
+ * d(gate) and d(router logits).
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [kucoin] kucoin.com, "Cursor's MoK réalise une amélioration des
+ *            performances de 2,37x sur NVIDIA GB300 NVL72", sections 01-03;
+ *   [fluid]  fluidifia.com, "Cursor ouvre MoK, un mégakernel qui accélère
+ *            l'entraînement MoE";
+ *   [ixtr]   ixtr.ca, "Introduction à Mixture-of-Kittens", section
+ *            "Écosystème Logiciel" (a light package exposing the kernel API
+ *            as a drop-in MoE routine);
+ *   [martel] laura-martel.com post on Mixture-of-Kittens, sections "Ce qu'il
+ *            fait réellement" (one kernel, one launch, no host round trip
+ *            inside the layer) and "Le déterminisme est la partie
+ *            sous-estimée" (same inputs, same hardware, same result).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates or frees device memory and never synchronises
+ *     the host: every call validates its arguments on the host, enqueues its
+ *     kernels on `stream` (a hipStream_t passed as void*, NULL = the default
+ *     stream) and returns.  Outputs are valid once the stream reaches them.
+ *   - Row-major layouts.  T tokens, hidden size d, E experts, top-k k,
+ *     expert FFN width F (cfg->ffn).  Local experts are
+ *     [expert_begin, expert_end); E_loc = expert_end - expert_begin and the
+ *     weights of expert e sit at index e - expert_begin.
+ *   - Activation element type: bf16 for MOK_PREC_BF16 and MOK_PREC_MXFP8
+ *     (x, out, dout, dx), fp32 for MOK_PREC_F32.
+ *   - Pair id p = t*k + j (slot j = 0 is the highest-ranked expert).
+ *   - Errors: a non-MOK_OK status is returned and nothing is enqueued.
+ *     No exception crosses the ABI.  Results are bit-identical from run to
+ *     run for identical inputs on the same device [martel].
+ *   - T = 0 is a valid no-op.
+ */
+#ifndef MOK_H_
+#define MOK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOK_OK = 0,
+  MOK_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misalignment          */
+  MOK_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement     */
+  MOK_ERR_WORKSPACE = 3,     /* ring smaller than one minibatch                 */
+  MOK_ERR_HIP = 4,           /* a HIP runtime call failed (launch error)        */
+  MOK_ERR_DEVICE = 5         /* reported by a device-side check                 */
+} mok_status;
+
+typedef enum {
+  MOK_PREC_F32 = 0,          /* fp32 activations and weights, fp32 arithmetic   */
+  MOK_PREC_BF16 = 1,         /* bf16 operands, fp32 accumulation (MFMA)         */
+  MOK_PREC_MXFP8 = 2         /* E4M3 operands + E8M0 scale per 32 along K       */
+} mok_precision;
+
+/* Forward writes the intermediates backward needs (A, B pre-activations). */
+#define MOK_FLAG_SAVE_FOR_BACKWARD 0x1u
+
+typedef struct mok_moe_config {
+  int32_t T;                 /* tokens in this call (>= 0)                      */
+  int32_t d;                 /* hidden size                                     */
+  int32_t E;                 /* experts routed over (1..1024)                   */
+  int32_t ffn;               /* expert FFN width F                              */
+  int32_t expert_begin;      /* first local expert                              */
+  int32_t expert_end;        /* one past the last local expert                  */
+  int32_t precision;         /* mok_precision                                   */
+  int32_t minibatch_rows;    /* R: rows of the expert-sorted buffer processed
+                                per minibatch; 0 = the whole layer at once.
+                                The pages' minibatch trade-off ([kucoin §02]).  */
+  int64_t ring_bytes;        /* fixed ring token buffer for dispatched rows
+                                ([fluid], [kucoin §02] "macrobatch"); 0 = no
+                                ring: the dispatch buffer holds every row.      */
+  uint32_t flags;            /* MOK_FLAG_*                                      */
+  uint32_t reserved;         /* must be 0                                       */
+} mok_moe_config;
+
+/* Byte offsets of the arrays inside the opaque `saved` buffer (from its base,
+ * each 256-byte aligned).  P_max = T*k rows are reserved; only the first P
+ * (= expert_offsets[E]) are meaningful. */
+typedef struct mok_saved_layout {
+  size_t lse;                /* float  [T]        log-sum-exp of each logit row */
+  size_t topk_idx;           /* int32  [T*k]                                    */
+  size_t topk_gate;          /* float  [T*k]                                    */
+  size_t offsets;            /* int32  [E+1]                                    */
+  size_t row_of_pair;        /* int32  [T*k]      -1 where the expert is remote */
+  size_t pair_of_row;        /* int32  [P_max]                                  */
+  size_t A;                  /* act    [P_max, F] x W1^T (pre-activation)       */
+  size_t B;                  /* act    [P_max, F] x W3^T                        */
+  size_t H;                  /* act    [P_max, F] silu(A) * B                   */
+  size_t Y;                  /* act    [P_max, d] expert output, unscaled       */
+  size_t total;
+} mok_saved_layout;
+
+/* Sizes of the caller-provided buffers for this configuration.
+ *   workspace_bytes: scratch for one forward or backward call (dispatch ring
+ *                    or full dispatch buffer, counting-sort tables, backward
+ *                    intermediates).  Not preserved between calls.
+ *   saved_bytes:     what forward writes and backward reads (see
+ *                    mok_saved_layout).
+ * Returns MOK_ERR_INVALID_ARG for invalid shapes. */
+mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k,
+                                   size_t* workspace_bytes, size_t* saved_bytes);
+
+/* Offsets of the arrays inside `saved` (host-only computation). */
+mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out);
+
+/*
+ * Forward pass of the MoE layer ([kucoin §01-§03]: router, layout, dispatch,
+ * grouped expert GEMMs, combine and the final weighted sum).
+ *
+ *   x              act   [T, d]
+ *   router_logits  float [T, E]    finite values
+ *   W1, W3         [E_loc, F, d]   gate / up projections (act type; E4M3
+ *                                  bytes for MXFP8)
+ *   W2             [E_loc, d, F]   down projection (act type; E4M3 for MXFP8)
+ *   w_scales       MXFP8 only, else NULL: E8M0 bytes, concatenated
+ *                  [E_loc, F, d/32] for W1, then [E_loc, F, d/32] for W3,
+ *                  then [E_loc, d, F/32] for W2 (see mok_quantize_mxfp8)
+ *   out            act   [T, d]    sum_j gate[t,j] * y(t,j), j ascending, in
+ *                                  fp32, rounded once; rows of tokens with no
+ *                                  local pair are 0
+ *   topk_idx       int32 [T, k]    experts by (logit desc, index asc)
+ *   topk_gate      float [T, k]    softmax over all E at those experts (not
+ *                                  renormalised)
+ *   expert_counts  int32 [E]       local pairs per expert (0 for remote)
+ *   expert_offsets int32 [E+1]     exclusive prefix sum of expert_counts
+ *   saved          mok_saved_layout.total bytes
+ *   workspace      workspace_bytes bytes
+ * Alignment: every pointer 16-byte aligned.  Constraints: 1 <= k <= E <= 1024,
+ * d and F multiples of 64 (bf16 and MXFP8) or 8 (fp32), T*k < 2^31.
+ */
+mok_status mok_moe_forward(const void* x, const float* router_logits,
+                           const void* W1, const void* W3, const void* W2, int32_t k,
+                           const mok_moe_config* cfg, const uint8_t* w_scales,
+                           void* out, int32_t* topk_idx, float* topk_gate,
+                           int32_t* expert_counts, int32_t* expert_offsets,
+                           void* saved, void* workspace, void* stream);
+
+/*
+ * Backward pass: gradients of L = sum(out * dout), mirroring the forward
+ * ([kucoin §01]: two more communication steps in the reverse direction;
+ * [kucoin §02]: reverse-combine, then reverse-dispatch).  Requires a forward
+ * call with MOK_FLAG_SAVE_FOR_BACKWARD on the same inputs and `saved`.
+ *
+ *   dout           act   [T, d]
+ *   dx             act   [T, d]    expert path only: sum_j of the pair
+ *                                  gradients, j ascending, fp32, rounded once
+ *   dW1, dW3       float [E_loc, F, d]   overwritten (not accumulated)
+ *   dW2            float [E_loc, d, F]   overwritten
+ *   dgate          float [T, k]    <dout_t, y(t,j)>; 0 for remote pairs
+ *   drouter_logits float [T, E]    p * (G - <p, G>), G = dgate scattered
+ * BF16 and FP32 precisions only (MXFP8 backward: MOK_ERR_UNSUPPORTED).
+ */
+mok_status mok_moe_backward(const void* dout, const void* x, const float* router_logits,
+                            const void* W1, const void* W3, const void* W2, int32_t k,
+                            const mok_moe_config* cfg, const void* saved,
+                            void* dx, float* dW1, float* dW3, float* dW2,
+                            float* dgate, float* drouter_logits,
+                            void* workspace, void* stream);
+
+/*
+ * MXFP8 quantisation of a bf16 matrix along its rows ([kucoin §02]: MXFP8
+ * activation quantisation; the rule is OCP Microscaling v1.0): per block of
+ * 32 consecutive elements of a row, scale X = 2^(floor(log2 amax) - 8) stored
+ * as an E8M0 byte (exponent + 127, clamped to [0, 254]; an all-zero block
+ * stores 0), elements E4M3(v / X) rounded to nearest even, saturating at 448.
+ *   src_bf16  [rows, K]      K a multiple of 32
+ *   dst_e4m3  [rows, K]      bytes
+ *   dst_e8m0  [rows, K/32]   bytes
+ * Used for the weights (once per weight update, outside the layer call); the
+ * layer quantises activations itself, inside its dispatch and SwiGLU steps.
+ */
+mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K,
+                              uint8_t* dst_e4m3, uint8_t* dst_e8m0, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* mok_status_string(mok_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t mok_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_H_ */

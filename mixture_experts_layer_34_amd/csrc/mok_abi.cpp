@@ -1,0 +1,321 @@
+// C ABI of the MoE layer (include/mok.h): argument validation, buffer layouts
+// and the launch sequence of one layer call.  Everything here runs on the
+// host before any launch; a call enqueues its kernels on the caller's stream
+// and returns without synchronising or allocating (the pages' layer has no
+// host round trip inside it: laura-martel.com post on Mixture-of-Kittens,
+// section "Ce qu'il fait réellement"; fluidifia.com, "Cursor ouvre MoK, un
+// mégakernel qui accélère l'entraînement MoE", section "Quand la
+// communication devient le vrai problème").
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "../../include/mok.h"
+#include "mok_internal.h"
+
+using namespace mok;
+
+namespace {
+
+enum { KIND_UP = 0, KIND_DOWN = 1, KIND_DH = 2, KIND_DX = 3, KIND_DW2 = 4, KIND_DW13 = 5 };
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_size(const mok_moe_config& c) { return c.precision == MOK_PREC_F32 ? 4 : 2; }
+
+mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
+  if (!cfg) return MOK_ERR_INVALID_ARG;
+  const mok_moe_config& c = *cfg;
+  if (c.T < 0 || c.d <= 0 || c.ffn <= 0 || c.E < 1 || c.E > 1024) return MOK_ERR_INVALID_ARG;
+  if (k < 1 || k > c.E) return MOK_ERR_INVALID_ARG;
+  if (c.expert_begin < 0 || c.expert_end <= c.expert_begin || c.expert_end > c.E) return MOK_ERR_INVALID_ARG;
+  if (c.precision != MOK_PREC_F32 && c.precision != MOK_PREC_BF16 && c.precision != MOK_PREC_MXFP8)
+    return MOK_ERR_INVALID_ARG;
+  const int mult = c.precision == MOK_PREC_F32 ? 16 : 64;
+  if (c.d % mult || c.ffn % mult) return MOK_ERR_INVALID_ARG;
+  if ((int64_t)c.T * k >= (int64_t(1) << 31)) return MOK_ERR_INVALID_ARG;
+  if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
+    return MOK_ERR_INVALID_ARG;
+  if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
+  if (c.flags & ~MOK_FLAG_SAVE_FOR_BACKWARD) return MOK_ERR_INVALID_ARG;
+  return MOK_OK;
+}
+
+void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_t* tile_prefix_off) {
+  const size_t Tk = (size_t)c.T * k, A = act_size(c);
+  const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
+  size_t o = 0;
+  s->lse = o;          o = align256(o + (size_t)c.T * 4);
+  s->topk_idx = o;     o = align256(o + Tk * 4);
+  s->topk_gate = o;    o = align256(o + Tk * 4);
+  s->offsets = o;      o = align256(o + ((size_t)c.E + 1) * 4);
+  *tile_prefix_off = o; o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
+  s->row_of_pair = o;  o = align256(o + Tk * 4);
+  s->pair_of_row = o;  o = align256(o + Tk * 4);
+  s->A = o;            o = align256(o + Tk * c.ffn * A);
+  s->B = o;            o = align256(o + Tk * c.ffn * A);
+  s->H = o;            o = align256(o + Tk * c.ffn * A);
+  s->Y = o;            o = align256(o + Tk * c.d * A);
+  s->total = o;
+}
+
+void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
+  const size_t Tk = (size_t)c.T * k, A = act_size(c);
+  const int64_t nchunks = ((int64_t)Tk + kSortChunk - 1) / kSortChunk;
+  const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
+  const bool mx = c.precision == MOK_PREC_MXFP8;
+  w->nchunks = (int)nchunks;
+  w->xp_rows = (int64_t)Tk;
+  size_t o = 0;
+  w->status = o;        o = align256(o + 256);
+  w->chunk_counts = o;  o = align256(o + (size_t)nchunks * c.E * 4);
+  w->chunk_base = o;    o = align256(o + (size_t)nchunks * c.E * 4);
+  w->tile_prefix = o;   o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
+  w->xp = o;            o = align256(o + (size_t)w->xp_rows * c.d * (mx ? 1 : A));
+  w->xp_scale = o;      o = align256(o + (mx ? (size_t)w->xp_rows * (c.d / 32) : 0));
+  w->hq = o;            o = align256(o + (mx ? Tk * c.ffn : 0));
+  w->hq_scale = o;      o = align256(o + (mx ? Tk * (c.ffn / 32) : 0));
+  w->dy = o;            o = align256(o + (mx ? 0 : Tk * c.d * A));
+  w->dab = o;           o = align256(o + (mx ? 0 : Tk * 2 * c.ffn * A));
+  w->dxp = o;           o = align256(o + (mx ? 0 : Tk * c.d * A));
+  w->mb_table = o;      o = align256(o + 256);
+  w->total = o;
+}
+
+template <typename T> T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <typename T> const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+hipError_t run_gemm(int prec, int kind, const GroupedGemmArgs& g, hipStream_t s) {
+  if (prec == MOK_PREC_F32) return gemm_f32(kind, g, s);
+  if (prec == MOK_PREC_MXFP8) return gemm_mxfp8(kind, g, s);
+  return gemm_bf16(kind, g, s);
+}
+
+#define MOK_HIP(call)                          \
+  do {                                         \
+    if ((call) != hipSuccess) return MOK_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* mok_status_string(mok_status s) {
+  switch (s) {
+    case MOK_OK: return "MOK_OK";
+    case MOK_ERR_INVALID_ARG: return "MOK_ERR_INVALID_ARG: invalid argument (null pointer, shape or alignment)";
+    case MOK_ERR_UNSUPPORTED: return "MOK_ERR_UNSUPPORTED: request not implemented by this library";
+    case MOK_ERR_WORKSPACE: return "MOK_ERR_WORKSPACE: ring buffer smaller than one minibatch";
+    case MOK_ERR_HIP: return "MOK_ERR_HIP: a HIP runtime call failed";
+    case MOK_ERR_DEVICE: return "MOK_ERR_DEVICE: a device-side check failed";
+  }
+  return "unknown mok_status";
+}
+
+int32_t mok_version(void) { return 100; }
+
+mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k, size_t* workspace_bytes,
+                                   size_t* saved_bytes) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!workspace_bytes || !saved_bytes) return MOK_ERR_INVALID_ARG;
+  WorkspaceLayout w;
+  workspace_layout(*cfg, k, &w);
+  mok_saved_layout s;
+  size_t tp;
+  saved_layout(*cfg, k, &s, &tp);
+  *workspace_bytes = w.total;
+  *saved_bytes = s.total;
+  return MOK_OK;
+}
+
+mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!out) return MOK_ERR_INVALID_ARG;
+  size_t tp;
+  saved_layout(*cfg, k, out, &tp);
+  return MOK_OK;
+}
+
+mok_status mok_moe_forward(const void* x, const float* router_logits, const void* W1, const void* W3,
+                           const void* W2, int32_t k, const mok_moe_config* cfg, const uint8_t* w_scales,
+                           void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                           int32_t* expert_offsets, void* saved, void* workspace, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  const void* ptrs[] = {x, router_logits, W1, W3, W2, out, topk_idx, topk_gate, expert_counts, expert_offsets,
+                        saved, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  const bool mx = c.precision == MOK_PREC_MXFP8;
+  if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
+  if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
+  if (c.minibatch_rows > 0 || c.ring_bytes > 0) return MOK_ERR_UNSUPPORTED;
+  if (mx && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_UNSUPPORTED;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
+  const int bf16 = c.precision != MOK_PREC_F32;
+  mok_saved_layout sl;
+  size_t tp_off;
+  saved_layout(c, k, &sl, &tp_off);
+  WorkspaceLayout wl;
+  workspace_layout(c, k, &wl);
+
+  int32_t* s_idx = at<int32_t>(saved, sl.topk_idx);
+  float* s_gate = at<float>(saved, sl.topk_gate);
+  float* s_lse = at<float>(saved, sl.lse);
+  int32_t* s_off = at<int32_t>(saved, sl.offsets);
+  int32_t* s_tp = at<int32_t>(saved, tp_off);
+  int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
+  int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
+
+  MOK_HIP(launch_router_topk(router_logits, T, E, k, topk_idx, topk_gate, s_idx, s_gate, s_lse, s));
+  MOK_HIP(launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
+                               at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
+                               s_rop, s_por, s));
+  GroupedGemmArgs g{};
+  g.offsets = s_off;
+  g.tile_prefix = s_tp;
+  g.eb = eb;
+  g.E_loc = E_loc;
+  g.d = d;
+  g.F = F;
+  g.P_max = (int64_t)T * k;
+  if (mx) {
+    uint8_t* xq = at<uint8_t>(workspace, wl.xp);
+    uint8_t* xs = at<uint8_t>(workspace, wl.xp_scale);
+    MOK_HIP(launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, s));
+    const size_t w13_scales = (size_t)E_loc * F * (d / 32);
+    g.A = xq;
+    g.a_scale = xs;
+    g.B0 = W1;
+    g.B1 = W3;
+    g.b_scale0 = w_scales;
+    g.b_scale1 = w_scales + w13_scales;
+    g.out0 = at<uint8_t>(workspace, wl.hq);
+    g.out_scale = at<uint8_t>(workspace, wl.hq_scale);
+    MOK_HIP(run_gemm(c.precision, KIND_UP, g, s));
+    GroupedGemmArgs g2 = g;
+    g2.A = at<uint8_t>(workspace, wl.hq);
+    g2.a_scale = at<uint8_t>(workspace, wl.hq_scale);
+    g2.B0 = W2;
+    g2.B1 = nullptr;
+    g2.b_scale0 = w_scales + 2 * w13_scales;
+    g2.b_scale1 = nullptr;
+    g2.out0 = at<void>(saved, sl.Y);
+    g2.out_scale = nullptr;
+    MOK_HIP(run_gemm(c.precision, KIND_DOWN, g2, s));
+  } else {
+    void* xp = at<void>(workspace, wl.xp);
+    MOK_HIP(launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+    g.A = xp;
+    g.B0 = W1;
+    g.B1 = W3;
+    g.out0 = at<void>(saved, sl.H);
+    g.save_a = at<void>(saved, sl.A);
+    g.save_b = at<void>(saved, sl.B);
+    g.save = (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ? 1 : 0;
+    MOK_HIP(run_gemm(c.precision, KIND_UP, g, s));
+    GroupedGemmArgs g2 = g;
+    g2.A = at<void>(saved, sl.H);
+    g2.B0 = W2;
+    g2.B1 = nullptr;
+    g2.out0 = at<void>(saved, sl.Y);
+    g2.save = 0;
+    MOK_HIP(run_gemm(c.precision, KIND_DOWN, g2, s));
+  }
+  MOK_HIP(launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, out, s));
+  return MOK_OK;
+}
+
+mok_status mok_moe_backward(const void* dout, const void* x, const float* router_logits, const void* W1,
+                            const void* W3, const void* W2, int32_t k, const mok_moe_config* cfg,
+                            const void* saved, void* dx, float* dW1, float* dW3, float* dW2, float* dgate,
+                            float* drouter_logits, void* workspace, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  const void* ptrs[] = {dout, x, router_logits, W1, W3, W2, saved, dx, dW1, dW3, dW2, dgate, drouter_logits,
+                        workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  if (c.precision == MOK_PREC_MXFP8) return MOK_ERR_UNSUPPORTED;
+  if (!(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
+  if (c.minibatch_rows > 0 || c.ring_bytes > 0) return MOK_ERR_UNSUPPORTED;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
+  const int bf16 = c.precision != MOK_PREC_F32;
+  mok_saved_layout sl;
+  size_t tp_off;
+  saved_layout(c, k, &sl, &tp_off);
+  WorkspaceLayout wl;
+  workspace_layout(c, k, &wl);
+  const int32_t* s_idx = at<int32_t>(saved, sl.topk_idx);
+  const float* s_gate = at<float>(saved, sl.topk_gate);
+  const float* s_lse = at<float>(saved, sl.lse);
+  const int32_t* s_off = at<int32_t>(saved, sl.offsets);
+  const int32_t* s_tp = at<int32_t>(saved, tp_off);
+  const int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
+  void* dy = at<void>(workspace, wl.dy);
+  void* dab = at<void>(workspace, wl.dab);
+  void* dxp = at<void>(workspace, wl.dxp);
+  void* xp = at<void>(workspace, wl.xp);
+
+  // reverse-combine with the router backward
+  MOK_HIP(launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
+                               bf16, dgate, drouter_logits, dy, s));
+  GroupedGemmArgs g{};
+  g.offsets = s_off;
+  g.tile_prefix = s_tp;
+  g.eb = eb;
+  g.E_loc = E_loc;
+  g.d = d;
+  g.F = F;
+  g.P_max = (int64_t)T * k;
+  // dH = dY W2 -> dA, dB
+  g.A = dy;
+  g.B0 = W2;
+  g.save_a = const_cast<void*>(at<void>(saved, sl.A));
+  g.save_b = const_cast<void*>(at<void>(saved, sl.B));
+  g.out0 = dab;
+  MOK_HIP(run_gemm(c.precision, KIND_DH, g, s));
+  // dX_perm = dA W1 + dB W3, then the reverse-dispatch reduction
+  GroupedGemmArgs gx = g;
+  gx.A = dab;
+  gx.B0 = W1;
+  gx.B1 = W3;
+  gx.out0 = dxp;
+  MOK_HIP(run_gemm(c.precision, KIND_DX, gx, s));
+  MOK_HIP(launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, dx, s));
+  // weight gradients
+  GroupedGemmArgs gw = g;
+  gw.A = dy;
+  gw.B0 = at<void>(saved, sl.H);
+  gw.out0 = dW2;
+  MOK_HIP(run_gemm(c.precision, KIND_DW2, gw, s));
+  MOK_HIP(launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+  GroupedGemmArgs g13 = g;
+  g13.A = dab;
+  g13.B0 = xp;
+  g13.out0 = dW1;
+  g13.out1 = dW3;
+  MOK_HIP(run_gemm(c.precision, KIND_DW13, g13, s));
+  return MOK_OK;
+}
+
+mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K, uint8_t* dst_e4m3, uint8_t* dst_e8m0,
+                              void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOK_ERR_INVALID_ARG;
+  if (rows == 0) return MOK_OK;
+  if (!src_bf16 || !dst_e4m3 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e4m3)) return MOK_ERR_INVALID_ARG;
+  MOK_HIP(launch_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, (hipStream_t)stream));
+  return MOK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Host-side launchers of the MoE layer kernels and the buffer layouts they
+// share.  Internal to libmok; the public interface is include/mok.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mok {
+
+// Pairs handled by one wave in the counting sort.
+constexpr int kSortChunk = 4096;
+// Row-tile heights for which per-expert tile prefixes are precomputed.
+constexpr int kNumTileBM = 3;
+constexpr int kTileBM[kNumTileBM] = {64, 128, 256};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct WorkspaceLayout {
+  size_t status;        // uint32 device status word
+  size_t chunk_counts;  // int32 [nchunks, E]
+  size_t chunk_base;    // int32 [nchunks, E]
+  size_t tile_prefix;   // int32 [kNumTileBM, E_loc + 1]
+  size_t xp;            // dispatched rows: act [rows, d] or e4m3 [rows, d]
+  size_t xp_scale;      // MXFP8: e8m0 [rows, d/32]
+  size_t hq;            // MXFP8: e4m3 [P_max, F]
+  size_t hq_scale;      // MXFP8: e8m0 [P_max, F/32]
+  size_t dy;            // backward: act [P_max, d]
+  size_t dab;           // backward: act [P_max, 2F]  (dA | dB)
+  size_t dxp;           // backward: act [P_max, d]
+  size_t mb_table;      // minibatch bookkeeping (int32)
+  size_t total;
+  int nchunks;
+  int64_t xp_rows;      // rows held by the dispatch buffer (P_max, or the ring)
+};
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx_out,
+                              float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
+                              hipStream_t s);
+
+hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
+                                int nchunks, int32_t* chunk_counts, int32_t* chunk_base,
+                                int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
+                                int32_t* tile_prefix, int32_t* row_of_pair, int32_t* pair_of_row,
+                                hipStream_t s);
+
+// X_perm[row(t,j)] = x[t] (act = bf16 when bf16 != 0, else fp32).
+hipError_t launch_dispatch_gather(const void* x, const int32_t* row_of_pair, int T, int k, int d,
+                                  int bf16, void* xp, hipStream_t s);
+// Same, quantising each row to MXFP8 (E4M3 + E8M0 per 32 along d).
+hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pair, int T, int k,
+                                        int d, uint8_t* xq, uint8_t* xs, hipStream_t s);
+hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q,
+                                 uint8_t* sc, hipStream_t s);
+
+// out[t] = sum_j w[t,j] * rows[row(t,j)] (w = gate, or 1 when gate == nullptr).
+hipError_t launch_combine(const void* rows, const float* gate, const int32_t* row_of_pair, int T,
+                          int k, int d, int bf16, void* out, hipStream_t s);
+
+// Reverse-combine and router backward: dgate, dlogits and dY rows.
+hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate,
+                                const int32_t* idx, const int32_t* row_of_pair,
+                                const float* logits, const float* lse, int T, int k, int E, int d,
+                                int bf16, float* dgate, float* dlogits, void* dy, hipStream_t s);
+
+// Grouped GEMMs of the expert FFN.  `offsets` is the global [E+1] array,
+// experts [eb, eb + E_loc) are local.  tile_prefix is the [kNumTileBM, E_loc+1]
+// table written by the counting sort.
+struct GroupedGemmArgs {
+  const void* A;          // activations (rows grouped by expert)
+  const void* B0;         // per-expert weights
+  const void* B1;         // second weights (W3) where used
+  const int32_t* offsets;
+  const int32_t* tile_prefix;
+  int eb, E_loc;
+  int d, F;
+  int64_t P_max;
+  void* out0;             // H / Y / dAB / dXp / dW
+  void* out1;             // second output where used (dW3)
+  void* save_a;           // A (pre-activation) rows
+  void* save_b;           // B rows
+  const uint8_t* a_scale; // MXFP8 activation scales
+  const uint8_t* b_scale0;
+  const uint8_t* b_scale1;
+  uint8_t* out_scale;     // MXFP8 H scales
+  int save;               // write A and B (forward)
+};
+
+// Expert-grouped GEMM of one kind (GemmKind in gemm_common.h) per precision:
+// 0 UP (H = silu(X W1^T) * (X W3^T)), 1 DOWN (Y = H W2^T), 2 DH (dA, dB from
+// dY W2), 3 DX (dA W1 + dB W3), 4 DW2 (dY^T H), 5 DW13 (dA^T X, dB^T X).
+hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
+hipError_t gemm_f32(int kind, const GroupedGemmArgs& g, hipStream_t s);
+hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
+
+}  // namespace mok

@@ -1,0 +1,275 @@
+// Router softmax + stable top-k, and the counting sort that lays token-expert
+// pairs out expert-contiguously.
+//
+// The router picks several experts per token at every step, and before any
+// token moves the system counts the tokens of each expert and decides where
+// each one lands, keeping one expert's tokens together for the grouped GEMM
+// (kucoin.com, "Cursor's MoK réalise une amélioration des performances de
+// 2,37x sur NVIDIA GB300 NVL72", section 01).  The receiver chooses the local
+// placement itself (same page, section 02, pull dispatch).
+//
+// Selection order: logit descending, expert index ascending on ties, comparing
+// the raw fp32 logits.  Placement is stable: within one expert, rows ascend by
+// pair id p = t*k + j.  Both are integer-exact and run-to-run identical.
+#include "mok_device.h"
+#include "mok_internal.h"
+
+namespace mok {
+
+// ------------------------------------------------------------------ router
+// One wave per token; lane l holds logits e = l + 64 i.  k rounds of a wave
+// arg-max under the (value desc, index asc) order.
+template <int EPL>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int k, int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ gate_out,
+                                                          int32_t* __restrict__ idx_saved,
+                                                          float* __restrict__ gate_saved,
+                                                          float* __restrict__ lse_out) {
+  const int lane = lane_id();
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  for (int t = wave; t < T; t += nwaves) {
+    const float* row = logits + (int64_t)t * E;
+    float v[EPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      int e = lane + 64 * i;
+      v[i] = e < E ? row[e] : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
+    m = wave_max(m);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      int e = lane + 64 * i;
+      if (e < E) s += expf(v[i] - m);
+    }
+    s = wave_sum(s);
+    const float inv_s = 1.0f / s;
+    uint32_t taken = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+          bv = v[i];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oe = __shfl_xor(be, o, 64);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      if (lane == 0) {
+        float g = expf(bv - m) * inv_s;
+        idx_out[(int64_t)t * k + j] = be;
+        gate_out[(int64_t)t * k + j] = g;
+        idx_saved[(int64_t)t * k + j] = be;
+        gate_saved[(int64_t)t * k + j] = g;
+      }
+    }
+    if (lane == 0) lse_out[t] = m + logf(s);
+  }
+}
+
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx_out,
+                              float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int blocks = (T + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
+  dim3 g(blocks), b(256);
+#define MOK_ROUTER(EPLV) \
+  hipLaunchKernelGGL(router_topk_kernel<EPLV>, g, b, 0, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse)
+  if (E <= 64) MOK_ROUTER(1);
+  else if (E <= 128) MOK_ROUTER(2);
+  else if (E <= 256) MOK_ROUTER(4);
+  else if (E <= 512) MOK_ROUTER(8);
+  else MOK_ROUTER(16);
+#undef MOK_ROUTER
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ counting sort
+// Lanes of a wave holding the same expert: AND over the expert-id bits of the
+// ballot of each bit (or of its complement), restricted to valid lanes.
+__device__ __forceinline__ uint64_t peer_mask(int e, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    bool bit = (e >> b) & 1;
+    uint64_t bm = __ballot(bit);
+    m &= bit ? bm : ~bm;
+  }
+  return m;
+}
+
+// Pass 1: per-chunk expert histogram.  One wave per chunk of kSortChunk pairs;
+// the lowest lane of each group of equal experts adds the group's size.
+__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ idx, int64_t npairs,
+                                                        int E, int eb, int ee, int nbits, int nchunks,
+                                                        int32_t* __restrict__ chunk_counts) {
+  extern __shared__ int32_t hist_smem[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int c = blockIdx.x * 4 + w;
+  int32_t* hist = hist_smem + w * E;
+  for (int e = lane; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  if (c < nchunks) {
+    const int64_t base = (int64_t)c * kSortChunk;
+    for (int it = 0; it < kSortChunk / 64; ++it) {
+      int64_t p = base + it * 64 + lane;
+      int e = p < npairs ? idx[p] : -1;
+      bool valid = e >= eb && e < ee;
+      uint64_t m = peer_mask(e, valid, nbits);
+      if (valid && lane == __ffsll((unsigned long long)m) - 1) hist[e] += __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)c * E + e] = hist[e];
+}
+
+// Pass 2: one block.  Thread e scans its expert over the chunks (chunk bases),
+// the block scans the totals over experts (offsets), and the row-tile prefix
+// of the local experts is written for each tile height.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                         int nchunks, int E, int eb, int ee,
+                                                         int32_t* __restrict__ chunk_base,
+                                                         int32_t* __restrict__ counts_out,
+                                                         int32_t* __restrict__ offsets_out,
+                                                         int32_t* __restrict__ offsets_saved,
+                                                         int32_t* __restrict__ tile_prefix) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t tsum[kNumTileBM][16];
+  const int e = threadIdx.x;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      int v = chunk_counts[(int64_t)c * E + e];
+      chunk_base[(int64_t)c * E + e] = run;
+      run += v;
+    }
+  }
+  // exclusive scan of run over e (1024 threads = 16 waves)
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  // tile counts of local expert i = e - eb for each tile height
+  const int E_loc = ee - eb;
+  const int i_loc = e - eb;
+  int tinc[kNumTileBM];
+#pragma unroll
+  for (int b = 0; b < kNumTileBM; ++b) {
+    int tc = (i_loc >= 0 && i_loc < E_loc) ? (run + kTileBM[b] - 1) / kTileBM[b] : 0;
+    int x = tc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int u = __shfl_up(x, o, 64);
+      if (lane >= o) x += u;
+    }
+    tinc[b] = x;
+    if (lane == 63) tsum[b][w] = x;
+  }
+  __syncthreads();
+  int wbase = 0;
+  int tbase[kNumTileBM] = {0, 0, 0};
+  for (int q = 0; q < w; ++q) {
+    wbase += wsum[q];
+#pragma unroll
+    for (int b = 0; b < kNumTileBM; ++b) tbase[b] += tsum[b][q];
+  }
+  const int off = wbase + incl - run;
+  if (e < E) {
+    counts_out[e] = run;
+    offsets_out[e] = off;
+    offsets_saved[e] = off;
+    if (e == E - 1) {
+      offsets_out[E] = off + run;
+      offsets_saved[E] = off + run;
+    }
+    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
+  }
+  if (i_loc >= 0 && i_loc < E_loc) {
+#pragma unroll
+    for (int b = 0; b < kNumTileBM; ++b) {
+      int inc = tbase[b] + tinc[b];
+      int* tp = tile_prefix + b * (E_loc + 1);
+      tp[i_loc + 1] = inc;
+      if (i_loc == 0) tp[0] = 0;
+    }
+  }
+}
+
+// Pass 3: stable placement.  Each wave re-walks its chunk in pair order with a
+// running row per expert (in LDS) started at the chunk base; a pair's row is
+// that running value plus its rank among the equal-expert lanes before it.
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ idx, int64_t npairs,
+                                                           int E, int eb, int ee, int nbits, int nchunks,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ row_of_pair,
+                                                           int32_t* __restrict__ pair_of_row) {
+  extern __shared__ int32_t run_smem[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int c = blockIdx.x * 4 + w;
+  int32_t* run = run_smem + w * E;
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) run[e] = chunk_base[(int64_t)c * E + e];
+  __syncthreads();
+  if (c >= nchunks) return;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = (int64_t)c * kSortChunk;
+  for (int it = 0; it < kSortChunk / 64; ++it) {
+    int64_t p = base + it * 64 + lane;
+    bool inb = p < npairs;
+    int e = inb ? idx[p] : -1;
+    bool valid = e >= eb && e < ee;
+    uint64_t m = peer_mask(e, valid, nbits);
+    int row = -1;
+    if (valid) row = run[e] + __popcll(m & lt);
+    __builtin_amdgcn_wave_barrier();
+    if (valid && lane == __ffsll((unsigned long long)m) - 1) run[e] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+    if (inb) row_of_pair[p] = row;
+    if (valid) pair_of_row[row] = (int32_t)p;
+  }
+}
+
+hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee, int nchunks,
+                                int32_t* chunk_counts, int32_t* chunk_base, int32_t* counts_out,
+                                int32_t* offsets_out, int32_t* offsets_saved, int32_t* tile_prefix,
+                                int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t s) {
+  const int64_t npairs = (int64_t)T * k;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int blocks = (nchunks + 3) / 4;
+  const size_t smem = (size_t)4 * E * sizeof(int32_t);
+  if (blocks > 0) {
+    hipLaunchKernelGGL(sort_hist_kernel, dim3(blocks), dim3(256), smem, s, idx, npairs, E, eb, ee, nbits,
+                       nchunks, chunk_counts);
+  }
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E, eb, ee,
+                     chunk_base, counts_out, offsets_out, offsets_saved, tile_prefix);
+  if (blocks > 0) {
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(256), smem, s, idx, npairs, E, eb, ee, nbits,
+                       nchunks, chunk_base, row_of_pair, pair_of_row);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mok

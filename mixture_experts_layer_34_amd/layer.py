@@ -1,0 +1,108 @@
+"""Torch plumbing around the C ABI: device buffers for one layer call and the
+calls themselves.  PyTorch only allocates memory and provides the stream; the
+layer's arithmetic runs in libmok's kernels."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import mok
+
+
+@dataclass
+class MoeShape:
+    T: int
+    d: int
+    E: int
+    k: int
+    F: int
+    precision: str = "bf16"
+    expert_begin: int = 0
+    expert_end: int = -1
+    minibatch_rows: int = 0
+    ring_bytes: int = 0
+    save_for_backward: bool = False
+
+    @property
+    def e_end(self):
+        return self.E if self.expert_end < 0 else self.expert_end
+
+    @property
+    def E_loc(self):
+        return self.e_end - self.expert_begin
+
+    def config(self) -> mok.mok_moe_config:
+        return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
+                               self.minibatch_rows, self.ring_bytes,
+                               mok.MOK_FLAG_SAVE_FOR_BACKWARD if self.save_for_backward else 0)
+
+    @property
+    def act_dtype(self):
+        return torch.float32 if self.precision == "f32" else torch.bfloat16
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class MoeBuffers:
+    """Outputs, saved state and workspace of one layer configuration on a device."""
+
+    def __init__(self, shape: MoeShape, device="cuda"):
+        self.shape = s = shape
+        self.cfg = s.config()
+        ws, sv = mok.mok_moe_workspace_query(self.cfg, s.k)
+        self.layout = mok.mok_moe_saved_layout(self.cfg, s.k)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        self.saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=device)
+        self.out = torch.empty((s.T, s.d), dtype=s.act_dtype, device=device)
+        self.topk_idx = torch.empty((s.T, s.k), dtype=torch.int32, device=device)
+        self.topk_gate = torch.empty((s.T, s.k), dtype=torch.float32, device=device)
+        self.counts = torch.empty(s.E, dtype=torch.int32, device=device)
+        self.offsets = torch.empty(s.E + 1, dtype=torch.int32, device=device)
+        self.grads = None
+
+    def alloc_grads(self):
+        s = self.shape
+        dev = self.out.device
+        self.grads = dict(
+            dx=torch.empty((s.T, s.d), dtype=s.act_dtype, device=dev),
+            dW1=torch.empty((s.E_loc, s.F, s.d), dtype=torch.float32, device=dev),
+            dW3=torch.empty((s.E_loc, s.F, s.d), dtype=torch.float32, device=dev),
+            dW2=torch.empty((s.E_loc, s.d, s.F), dtype=torch.float32, device=dev),
+            dgate=torch.empty((s.T, s.k), dtype=torch.float32, device=dev),
+            dlogits=torch.empty((s.T, s.E), dtype=torch.float32, device=dev))
+        return self.grads
+
+    def saved_view(self, name: str, dtype, shape):
+        """A view of one array inside the saved buffer (see mok_saved_layout)."""
+        off = self.layout[name]
+        n = 1
+        for v in shape:
+            n *= v
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.saved[off:off + nbytes].view(dtype).view(*shape)
+
+    def forward(self, x, logits, W1, W3, W2, w_scales=None, stream=None):
+        mok.mok_moe_forward(x, logits, W1, W3, W2, self.shape.k, self.cfg, w_scales, self.out, self.topk_idx,
+                            self.topk_gate, self.counts, self.offsets, self.saved, self.workspace,
+                            _stream() if stream is None else stream)
+        return self.out
+
+    def backward(self, dout, x, logits, W1, W3, W2, stream=None):
+        g = self.grads or self.alloc_grads()
+        mok.mok_moe_backward(dout, x, logits, W1, W3, W2, self.shape.k, self.cfg, self.saved, g["dx"], g["dW1"],
+                             g["dW3"], g["dW2"], g["dgate"], g["dlogits"], self.workspace,
+                             _stream() if stream is None else stream)
+        return g
+
+
+def quantize_mxfp8(w: torch.Tensor):
+    """E4M3 codes and E8M0 scales of a bf16 tensor along its last axis."""
+    K = w.shape[-1]
+    rows = w.numel() // K
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    sc = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+    mok.mok_quantize_mxfp8(w, rows, K, q, sc, _stream())
+    return q, sc

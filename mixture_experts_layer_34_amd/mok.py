@@ -1,0 +1,132 @@
+"""ctypes binding of libmok (include/mok.h), entry point by entry point.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmok.so.  Tensor arguments may be torch tensors (their data_ptr() is passed)
+or raw integer device addresses.  A non-OK status raises MokError.  If the
+library is not built the first call raises; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmok.so")
+
+MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE, MOK_ERR_HIP, MOK_ERR_DEVICE = range(6)
+MOK_PREC_F32, MOK_PREC_BF16, MOK_PREC_MXFP8 = range(3)
+MOK_FLAG_SAVE_FOR_BACKWARD = 0x1
+PRECISIONS = {"f32": MOK_PREC_F32, "bf16": MOK_PREC_BF16, "mxfp8": MOK_PREC_MXFP8}
+
+
+class mok_moe_config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("expert_begin", ctypes.c_int32), ("expert_end", ctypes.c_int32),
+                ("precision", ctypes.c_int32), ("minibatch_rows", ctypes.c_int32),
+                ("ring_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class mok_saved_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("lse", "topk_idx", "topk_gate", "offsets", "row_of_pair", "pair_of_row", "A", "B", "H", "Y",
+                 "total")]
+
+
+class MokError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mok_status_string(status)}")
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmok.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with mixture_experts_layer_34_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mok_status_string.restype = ctypes.c_char_p
+        L.mok_status_string.argtypes = [ctypes.c_int]
+        L.mok_version.restype = ctypes.c_int32
+        L.mok_moe_workspace_query.restype = ctypes.c_int
+        L.mok_moe_workspace_query.argtypes = [ctypes.POINTER(mok_moe_config), ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.mok_moe_saved_layout.restype = ctypes.c_int
+        L.mok_moe_saved_layout.argtypes = [ctypes.POINTER(mok_moe_config), ctypes.c_int32,
+                                           ctypes.POINTER(mok_saved_layout)]
+        L.mok_moe_forward.restype = ctypes.c_int
+        L.mok_moe_forward.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _P]
+        L.mok_moe_backward.restype = ctypes.c_int
+        L.mok_moe_backward.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
+                                       _P, _P, _P, _P, _P, _P, _P, _P]
+        L.mok_quantize_mxfp8.restype = ctypes.c_int
+        L.mok_quantize_mxfp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(v):
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v
+    return v.data_ptr()
+
+
+def _check(status: int, where: str):
+    if status != MOK_OK:
+        raise MokError(status, where)
+
+
+def make_config(T, d, E, ffn, expert_begin=0, expert_end=None, precision="bf16", minibatch_rows=0,
+                ring_bytes=0, flags=0, reserved=0) -> mok_moe_config:
+    prec = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
+    return mok_moe_config(T, d, E, ffn, expert_begin, E if expert_end is None else expert_end, prec,
+                          minibatch_rows, ring_bytes, flags, reserved)
+
+
+def mok_status_string(status: int) -> str:
+    return lib().mok_status_string(int(status)).decode()
+
+
+def mok_version() -> int:
+    return int(lib().mok_version())
+
+
+def mok_moe_workspace_query(cfg: mok_moe_config, k: int):
+    ws, sv = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().mok_moe_workspace_query(ctypes.byref(cfg), k, ctypes.byref(ws), ctypes.byref(sv)),
+           "mok_moe_workspace_query")
+    return ws.value, sv.value
+
+
+def mok_moe_saved_layout(cfg: mok_moe_config, k: int) -> dict:
+    out = mok_saved_layout()
+    _check(lib().mok_moe_saved_layout(ctypes.byref(cfg), k, ctypes.byref(out)), "mok_moe_saved_layout")
+    return {n: getattr(out, n) for n, _ in mok_saved_layout._fields_}
+
+
+def mok_moe_forward(x, router_logits, W1, W3, W2, k, cfg, w_scales, out, topk_idx, topk_gate, expert_counts,
+                    expert_offsets, saved, workspace, stream=0):
+    _check(lib().mok_moe_forward(_ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W3), _ptr(W2), k, ctypes.byref(cfg),
+                                 _ptr(w_scales), _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(expert_counts),
+                                 _ptr(expert_offsets), _ptr(saved), _ptr(workspace), stream or None),
+           "mok_moe_forward")
+
+
+def mok_moe_backward(dout, x, router_logits, W1, W3, W2, k, cfg, saved, dx, dW1, dW3, dW2, dgate, drouter_logits,
+                     workspace, stream=0):
+    _check(lib().mok_moe_backward(_ptr(dout), _ptr(x), _ptr(router_logits), _ptr(W1), _ptr(W3), _ptr(W2), k,
+                                  ctypes.byref(cfg), _ptr(saved), _ptr(dx), _ptr(dW1), _ptr(dW3), _ptr(dW2),
+                                  _ptr(dgate), _ptr(drouter_logits), _ptr(workspace), stream or None),
+           "mok_moe_backward")
+
+
+def mok_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, stream=0):
+    _check(lib().mok_quantize_mxfp8(_ptr(src_bf16), rows, K, _ptr(dst_e4m3), _ptr(dst_e8m0), stream or None),
+           "mok_quantize_mxfp8")

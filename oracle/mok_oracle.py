@@ -56,7 +56,7 @@ __all__ = [
     "route", "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
     "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
-    "forward_token",
+    "forward_token", "backward_token", "expert_weight_grads",
 ]
 
 
@@ -404,3 +404,52 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
 def loss(out, dout) -> float:
     """L = sum(out * dout): the scalar whose gradients backward() returns."""
     return float((_f64(out) * _f64(dout)).sum())
+
+
+def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int = 0,
+                   expert_end: int | None = None):
+    """Backward of one token alone (sampled checks at full size): the pair
+    gradients of its local experts summed in slot order, and its router
+    gradient.  Same equations as backward(), restricted to one token; every
+    pair's backward depends only on that pair.  Returns (dx [d], dgate [k],
+    dlogits [E])."""
+    l32 = np.asarray(logits_t, dtype=np.float32)[None, :]
+    E = l32.shape[1]
+    if expert_end is None:
+        expert_end = E
+    idx, gate, _, p = route(l32, k)
+    xt = _f64(x_t)[None, :]
+    g = _f64(dout_t)
+    dx = np.zeros(xt.shape[1])
+    dgate = np.zeros(k)
+    for j in range(k):
+        e = int(idx[0, j])
+        if not expert_begin <= e < expert_end:
+            continue
+        i = e - expert_begin
+        a, b, h, y = expert_ffn(xt, W1[i], W3[i], W2[i])
+        dgate[j] = float(np.dot(g, y[0]))
+        dy = gate[0, j] * g[None, :]
+        dh = dy @ _f64(W2[i])
+        s = sigmoid(a)
+        da = dh * b * s * (1.0 + a * (1.0 - s))
+        db = dh * silu(a)
+        dx += (da @ _f64(W1[i]) + db @ _f64(W3[i]))[0]
+    G = np.zeros(E)
+    G[idx[0].astype(np.int64)] = dgate
+    dlogits = p[0] * (G - np.dot(p[0], G))
+    return dx, dgate, dlogits
+
+
+def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e):
+    """dW1_e, dW3_e, dW2_e of one expert from its rows alone: X_e [R,d] the
+    activations of its pairs, gate_e [R] their gates, dout_e [R,d] the output
+    gradients of their tokens (row order does not matter)."""
+    X = _f64(X_e)
+    a, b, h, _ = expert_ffn(X, W1e, W3e, W2e)
+    dy = _f64(gate_e)[:, None] * _f64(dout_e)
+    dh = dy @ _f64(W2e)
+    s = sigmoid(a)
+    da = dh * b * s * (1.0 + a * (1.0 - s))
+    db = dh * silu(a)
+    return da.T @ X, db.T @ X, dy.T @ h

@@ -411,3 +411,27 @@ def test_mxfp8_forward_reduces_to_plain_when_exact():
     m = O.forward(x, logits, W1, W3, W2, 1, mxfp8=True)
     p = O.forward(x, logits, W1, W3, W2, 1)
     np.testing.assert_allclose(m["out"], O.mxfp8_qdq(p["H"]), rtol=0, atol=0)
+
+
+def test_per_token_and_per_expert_backward_match_full_backward():
+    rng = _rng(14)
+    T, d, F, E, k, b, e_end = 30, 8, 12, 6, 2, 1, 5
+    x = rng.standard_normal((T, d)); g = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((4, F, d)); W3 = rng.standard_normal((4, F, d)); W2 = rng.standard_normal((4, d, F))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    fw = O.forward(x, logits, W1, W3, W2, k, b, e_end)
+    bw = O.backward(g, x, logits, W1, W3, W2, k, fw, b, e_end)
+    for t in (0, 7, 29):
+        dx, dg, dl = O.backward_token(x[t], logits[t], g[t], W1, W3, W2, k, b, e_end)
+        np.testing.assert_allclose(dx, bw["dx"][t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dg, bw["dgate"][t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dl, bw["dlogits"][t], rtol=1e-12, atol=1e-12)
+        idx, gate, out, _ = O.forward_token(t, x[t], logits[t], W1, W3, W2, k, b, e_end)
+        np.testing.assert_allclose(out, fw["out"][t], rtol=1e-12, atol=1e-12)
+    for e in range(b, e_end):
+        rows = fw["pair_of_row"][fw["offsets"][e]:fw["offsets"][e + 1]]
+        tok, slot = rows // k, rows % k
+        gW1, gW3, gW2 = O.expert_weight_grads(x[tok], fw["gate"][tok, slot], g[tok], W1[e - b], W3[e - b], W2[e - b])
+        np.testing.assert_allclose(gW1, bw["dW1"][e - b], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(gW3, bw["dW3"][e - b], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(gW2, bw["dW2"][e - b], rtol=1e-12, atol=1e-12)
