@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+One step = one forward + backward pass of the whole layer (router, counting
+sort, dispatch, grouped SwiGLU GEMMs, combine, and the mirrored backward) over
+one batch of synthetic tokens already resident in HBM.  Default workload:
+T=8192 tokens, d=4096, E=128 experts, top-8, F=1536, Zipf(1.2) expert
+popularity, bf16 with fp32 accumulation.
+
+Prints one JSON line: tokens/s for the whole job, the roofline position of the
+dominant kernel (timed with HIP events recorded by the library around each of
+its stages, on the stream the kernels run on), grouped-GEMM TFLOP/s per GEMM,
+and the CPU oracle timed on a bounded sample of the same workload."""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s fwd+bwd (BF16, MXFP8) + grouped-GEMM % MFMA peak, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (the library records them)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            out[i] = ev
+        return out
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        r = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        return ms.value if r == 0 else float("nan")
+
+
+def stage_work(w, P, U):
+    """Algorithmic work of one launch of each stage: FLOPs for the GEMMs,
+    HBM bytes for the data movement (each operand read or written once)."""
+    d, F, E, k, T = w.d, w.F, w.E, w.k, U
+    s = 4 if w.precision == "f32" else 2
+    flops = {"gemm_up": 4.0 * P * d * F, "gemm_down": 2.0 * P * F * d, "gemm_dh": 2.0 * P * d * F,
+             "gemm_dx": 4.0 * P * F * d, "gemm_dw2": 2.0 * P * d * F, "gemm_dw13": 4.0 * P * F * d}
+    nbytes = {"router": T * E * 4 + T * k * 8 * 2 + T * 4,
+              "dispatch": (U + P) * d * s, "regather": (U + P) * d * s,
+              "combine": P * d * s + T * d * s + P * 8,
+              "bwd_gate": T * d * s + 2 * P * d * s + 2 * T * E * 4 + P * 8,
+              "reduce_dx": P * d * s + T * d * s + P * 4,
+              "sort": T * k * 4 * 4 + P * 4}
+    return flops, nbytes
+
+
+def cpu_baseline(w, inp, sample_tokens: int):
+    """The oracle (float64 numpy) on the first `sample_tokens` tokens with
+    their full routing, forward + backward; tokens/s = sample / seconds."""
+    import numpy as np
+    from oracle import mok_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    S = min(sample_tokens, inp["x"].shape[0])
+    x = inp["x"][:S].float().cpu().numpy()
+    lg = inp["logits"][:S].cpu().numpy()
+    g = inp["dout"][:S].float().cpu().numpy() if "dout" in inp else None
+    W1 = inp["W1"].float().cpu().numpy()
+    W3 = inp["W3"].float().cpu().numpy()
+    W2 = inp["W2"].float().cpu().numpy()
+    t0 = time.perf_counter()
+    fw = O.forward(x, lg, W1, W3, W2, w.k, w.expert_begin, w.e_end)
+    if g is not None:
+        O.backward(g, x, lg, W1, W3, W2, w.k, fw, w.expert_begin, w.e_end)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {inp['x'].shape[0]} tokens with all their top-{w.k} pairs, "
+                      f"{'forward+backward' if g is not None else 'forward'}, float64 numpy oracle, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_train")
+    ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from mixture_experts_layer_34_amd import mok
+    from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp8
+
+    w = W.get(args.workload)
+    backward = w.backward and not args.forward_only and w.precision != "mxfp8"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(w, device=dev)
+    T = inp["x"].shape[0]
+    shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision, expert_begin=w.expert_begin,
+                     expert_end=w.e_end, save_for_backward=backward)
+    buf = MoeBuffers(shape, device=dev)
+    W1, W3, W2, scales = inp["W1"], inp["W3"], inp["W2"], None
+    if w.precision == "mxfp8":
+        q1, s1 = quantize_mxfp8(W1)
+        q3, s3 = quantize_mxfp8(W3)
+        q2, s2 = quantize_mxfp8(W2)
+        W1, W3, W2 = q1, q3, q2
+        scales = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ev = HipEvents()
+    K, Wm = args.steps, args.warmup
+    stage_ev = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(K)]
+    start, stop = ev.create(2)
+
+    def step(events=None):
+        buf.cfg.stage_events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+        buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales, stream=sh)
+        if backward:
+            buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"], stream=sh)
+
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(start, sh)
+    for i in range(K):
+        step(stage_ev[i])
+    ev.record(stop, sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev.elapsed_ms(start, stop)
+    buf.cfg.stage_events = None
+    ms_step = ms_total / K
+
+    # per-stage averages over the timed steps
+    stages = {}
+    for s, name in enumerate(mok.STAGES):
+        vals = [ev.elapsed_ms(stage_ev[i][2 * s], stage_ev[i][2 * s + 1]) for i in range(K)]
+        if backward or s <= mok.STAGES.index("combine"):
+            stages[name] = sum(vals) / len(vals)
+    P = int(buf.offsets[-1].item())
+    U = int((buf.topk_idx.ge(w.expert_begin) & buf.topk_idx.lt(w.e_end)).any(dim=1).sum().item())
+    flops, nbytes = stage_work(w, P, U)
+    dom = max(stages, key=stages.get)
+    peak = PEAK_TFLOPS[w.precision]
+    if dom in flops:
+        ach = flops[dom] / (stages[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel": dom,
+                "per_launch": f"{flops[dom] / 1e9:.1f} GFLOP", "avg_ms": round(stages[dom], 4)}
+    else:
+        ach = nbytes[dom] / (stages[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "per_launch": f"{nbytes[dom] / 1e6:.1f} MB", "avg_ms": round(stages[dom], 4)}
+    gemm = {n: {"ms": round(stages[n], 4), "tflops": round(flops[n] / (stages[n] * 1e-3) / 1e12, 1),
+                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / peak, 4)}
+            for n in flops if n in stages}
+    gemm_ms = sum(stages[n] for n in flops if n in stages)
+    gemm_flops = sum(flops[n] for n in flops if n in stages)
+    hbm = {n: {"ms": round(stages[n], 4), "gbs": round(nbytes[n] / (stages[n] * 1e-3) / 1e9, 1)}
+           for n in nbytes if n in stages}
+
+    result = {
+        "metric": METRIC,
+        "value": round(T * K / (ms_total * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.precision, "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={T} d={w.d} E={w.E} k={w.k} F={w.F} "
+                               f"local experts [{w.expert_begin},{w.e_end}) pairs P={P}, "
+                               f"{'forward+backward' if backward else 'forward'}",
+                   "global_batch": T, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+                         "frac_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4), "per_gemm": gemm},
+        "data_movement": hbm,
+        "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

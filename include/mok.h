@@ -37,7 +37,8 @@
  *   - Errors: a non-MOK_OK status is returned and nothing is enqueued.
  *     No exception crosses the ABI.  Results are bit-identical from run to
  *     run for identical inputs on the same device [martel].
- *   - T = 0 is a valid no-op.
+ *   - T = 0 is valid: counts and offsets become 0, dW outputs 0; pointers
+ *     to arrays with zero elements may be NULL.
  */
 #ifndef MOK_H_
 #define MOK_H_
@@ -83,7 +84,30 @@ typedef struct mok_moe_config {
                                 ring: the dispatch buffer holds every row.      */
   uint32_t flags;            /* MOK_FLAG_*                                      */
   uint32_t reserved;         /* must be 0                                       */
+  void* const* stage_events; /* NULL, or 2*MOK_NUM_STAGES hipEvent_t handles
+                                (created by the caller): the call records
+                                events[2s] on its stream before stage s and
+                                events[2s+1] after it, for every stage it runs,
+                                so the caller can time each kernel.            */
 } mok_moe_config;
+
+/* Stages of one forward or backward call, in launch order. */
+typedef enum {
+  MOK_STAGE_ROUTER = 0,      /* softmax + top-k                                 */
+  MOK_STAGE_SORT = 1,        /* counting sort (histogram, scan, placement)      */
+  MOK_STAGE_DISPATCH = 2,    /* gather rows (+ MXFP8 quantise)                  */
+  MOK_STAGE_GEMM_UP = 3,     /* H = silu(X W1^T) * (X W3^T)                     */
+  MOK_STAGE_GEMM_DOWN = 4,   /* Y = H W2^T                                      */
+  MOK_STAGE_COMBINE = 5,     /* out = sum_j gate * Y                            */
+  MOK_STAGE_BWD_GATE = 6,    /* dgate, drouter_logits, dY = gate * dout         */
+  MOK_STAGE_GEMM_DH = 7,     /* dA, dB from dY W2                               */
+  MOK_STAGE_GEMM_DX = 8,     /* dX_perm = dA W1 + dB W3                         */
+  MOK_STAGE_REDUCE_DX = 9,   /* dx = sum_j dX_perm                              */
+  MOK_STAGE_GEMM_DW2 = 10,   /* dW2 = dY^T H                                    */
+  MOK_STAGE_REGATHER = 11,   /* gather X rows again for dW1, dW3                */
+  MOK_STAGE_GEMM_DW13 = 12,  /* dW1 = dA^T X, dW3 = dB^T X                      */
+  MOK_NUM_STAGES = 13
+} mok_stage;
 
 /* Byte offsets of the arrays inside the opaque `saved` buffer (from its base,
  * each 256-byte aligned).  P_max = T*k rows are reserved; only the first P
@@ -138,7 +162,7 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *   saved          mok_saved_layout.total bytes
  *   workspace      workspace_bytes bytes
  * Alignment: every pointer 16-byte aligned.  Constraints: 1 <= k <= E <= 1024,
- * d and F multiples of 64 (bf16 and MXFP8) or 8 (fp32), T*k < 2^31.
+ * d and F multiples of 64 (bf16 and MXFP8) or 16 (fp32), T*k < 2^31.
  */
 mok_status mok_moe_forward(const void* x, const float* router_logits,
                            const void* W1, const void* W3, const void* W2, int32_t k,

@@ -93,6 +93,25 @@ hipError_t run_gemm(int prec, int kind, const GroupedGemmArgs& g, hipStream_t s)
   return gemm_bf16(kind, g, s);
 }
 
+// Records the caller's stage events around one stage (no-op without events).
+struct StageMark {
+  const mok_moe_config& c;
+  hipStream_t s;
+  int stage;
+  StageMark(const mok_moe_config& cfg, hipStream_t st, int sg) : c(cfg), s(st), stage(sg) {
+    if (c.stage_events) (void)hipEventRecord((hipEvent_t)c.stage_events[2 * stage], s);
+  }
+  ~StageMark() {
+    if (c.stage_events) (void)hipEventRecord((hipEvent_t)c.stage_events[2 * stage + 1], s);
+  }
+};
+
+#define MOK_STAGE(stage, call)                 \
+  do {                                         \
+    StageMark mark_(c, s, stage);              \
+    if ((call) != hipSuccess) return MOK_ERR_HIP; \
+  } while (0)
+
 #define MOK_HIP(call)                          \
   do {                                         \
     if ((call) != hipSuccess) return MOK_ERR_HIP; \
@@ -147,10 +166,12 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   mok_status st = validate_config(cfg, k);
   if (st != MOK_OK) return st;
   const mok_moe_config& c = *cfg;
-  const void* ptrs[] = {x, router_logits, W1, W3, W2, out, topk_idx, topk_gate, expert_counts, expert_offsets,
-                        saved, workspace};
-  for (const void* p : ptrs)
+  const void* always[] = {W1, W3, W2, expert_counts, expert_offsets, saved, workspace};
+  const void* per_token[] = {x, router_logits, out, topk_idx, topk_gate};
+  for (const void* p : always)
     if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
   const bool mx = c.precision == MOK_PREC_MXFP8;
   if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
   if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
@@ -174,8 +195,8 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
   int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
 
-  MOK_HIP(launch_router_topk(router_logits, T, E, k, topk_idx, topk_gate, s_idx, s_gate, s_lse, s));
-  MOK_HIP(launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
+  MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, topk_idx, topk_gate, s_idx, s_gate, s_lse, s));
+  MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
                                at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
                                s_rop, s_por, s));
   GroupedGemmArgs g{};
@@ -189,7 +210,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   if (mx) {
     uint8_t* xq = at<uint8_t>(workspace, wl.xp);
     uint8_t* xs = at<uint8_t>(workspace, wl.xp_scale);
-    MOK_HIP(launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, s));
+    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, s));
     const size_t w13_scales = (size_t)E_loc * F * (d / 32);
     g.A = xq;
     g.a_scale = xs;
@@ -199,7 +220,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g.b_scale1 = w_scales + w13_scales;
     g.out0 = at<uint8_t>(workspace, wl.hq);
     g.out_scale = at<uint8_t>(workspace, wl.hq_scale);
-    MOK_HIP(run_gemm(c.precision, KIND_UP, g, s));
+    MOK_STAGE(MOK_STAGE_GEMM_UP, run_gemm(c.precision, KIND_UP, g, s));
     GroupedGemmArgs g2 = g;
     g2.A = at<uint8_t>(workspace, wl.hq);
     g2.a_scale = at<uint8_t>(workspace, wl.hq_scale);
@@ -209,10 +230,10 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g2.b_scale1 = nullptr;
     g2.out0 = at<void>(saved, sl.Y);
     g2.out_scale = nullptr;
-    MOK_HIP(run_gemm(c.precision, KIND_DOWN, g2, s));
+    MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   } else {
     void* xp = at<void>(workspace, wl.xp);
-    MOK_HIP(launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
     g.A = xp;
     g.B0 = W1;
     g.B1 = W3;
@@ -220,16 +241,16 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g.save_a = at<void>(saved, sl.A);
     g.save_b = at<void>(saved, sl.B);
     g.save = (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ? 1 : 0;
-    MOK_HIP(run_gemm(c.precision, KIND_UP, g, s));
+    MOK_STAGE(MOK_STAGE_GEMM_UP, run_gemm(c.precision, KIND_UP, g, s));
     GroupedGemmArgs g2 = g;
     g2.A = at<void>(saved, sl.H);
     g2.B0 = W2;
     g2.B1 = nullptr;
     g2.out0 = at<void>(saved, sl.Y);
     g2.save = 0;
-    MOK_HIP(run_gemm(c.precision, KIND_DOWN, g2, s));
+    MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   }
-  MOK_HIP(launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, out, s));
+  MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, out, s));
   return MOK_OK;
 }
 
@@ -240,10 +261,12 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   mok_status st = validate_config(cfg, k);
   if (st != MOK_OK) return st;
   const mok_moe_config& c = *cfg;
-  const void* ptrs[] = {dout, x, router_logits, W1, W3, W2, saved, dx, dW1, dW3, dW2, dgate, drouter_logits,
-                        workspace};
-  for (const void* p : ptrs)
+  const void* always[] = {W1, W3, W2, saved, dW1, dW3, dW2, workspace};
+  const void* per_token[] = {dout, x, router_logits, dx, dgate, drouter_logits};
+  for (const void* p : always)
     if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
   if (c.precision == MOK_PREC_MXFP8) return MOK_ERR_UNSUPPORTED;
   if (!(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
   if (c.minibatch_rows > 0 || c.ring_bytes > 0) return MOK_ERR_UNSUPPORTED;
@@ -268,7 +291,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   void* xp = at<void>(workspace, wl.xp);
 
   // reverse-combine with the router backward
-  MOK_HIP(launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
+  MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
                                bf16, dgate, drouter_logits, dy, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
@@ -284,28 +307,28 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   g.save_a = const_cast<void*>(at<void>(saved, sl.A));
   g.save_b = const_cast<void*>(at<void>(saved, sl.B));
   g.out0 = dab;
-  MOK_HIP(run_gemm(c.precision, KIND_DH, g, s));
+  MOK_STAGE(MOK_STAGE_GEMM_DH, run_gemm(c.precision, KIND_DH, g, s));
   // dX_perm = dA W1 + dB W3, then the reverse-dispatch reduction
   GroupedGemmArgs gx = g;
   gx.A = dab;
   gx.B0 = W1;
   gx.B1 = W3;
   gx.out0 = dxp;
-  MOK_HIP(run_gemm(c.precision, KIND_DX, gx, s));
-  MOK_HIP(launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, dx, s));
+  MOK_STAGE(MOK_STAGE_GEMM_DX, run_gemm(c.precision, KIND_DX, gx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, dx, s));
   // weight gradients
   GroupedGemmArgs gw = g;
   gw.A = dy;
   gw.B0 = at<void>(saved, sl.H);
   gw.out0 = dW2;
-  MOK_HIP(run_gemm(c.precision, KIND_DW2, gw, s));
-  MOK_HIP(launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+  MOK_STAGE(MOK_STAGE_GEMM_DW2, run_gemm(c.precision, KIND_DW2, gw, s));
+  MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
   GroupedGemmArgs g13 = g;
   g13.A = dab;
   g13.B0 = xp;
   g13.out0 = dW1;
   g13.out1 = dW3;
-  MOK_HIP(run_gemm(c.precision, KIND_DW13, g13, s));
+  MOK_STAGE(MOK_STAGE_GEMM_DW13, run_gemm(c.precision, KIND_DW13, g13, s));
   return MOK_OK;
 }
 

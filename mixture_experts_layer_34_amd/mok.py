@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(_HERE, "libmok.so")
 MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE, MOK_ERR_HIP, MOK_ERR_DEVICE = range(6)
 MOK_PREC_F32, MOK_PREC_BF16, MOK_PREC_MXFP8 = range(3)
 MOK_FLAG_SAVE_FOR_BACKWARD = 0x1
+STAGES = ["router", "sort", "dispatch", "gemm_up", "gemm_down", "combine", "bwd_gate", "gemm_dh", "gemm_dx",
+          "reduce_dx", "gemm_dw2", "regather", "gemm_dw13"]
+MOK_NUM_STAGES = len(STAGES)
 PRECISIONS = {"f32": MOK_PREC_F32, "bf16": MOK_PREC_BF16, "mxfp8": MOK_PREC_MXFP8}
 
 
@@ -23,7 +26,8 @@ class mok_moe_config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("expert_begin", ctypes.c_int32), ("expert_end", ctypes.c_int32),
                 ("precision", ctypes.c_int32), ("minibatch_rows", ctypes.c_int32),
-                ("ring_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("ring_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("stage_events", ctypes.c_void_p)]
 
 
 class mok_saved_layout(ctypes.Structure):
