@@ -13,75 +13,120 @@
 //   DW2   dW2_e = dY_e^T H_e                         [d, F] fp32
 //   DW13  dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e     [F, d] fp32
 //
-// Tiling: a workgroup computes a BM x BN output tile with WM x WN waves, each
-// wave a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles, over K in steps of BK
-// staged through double-buffered LDS (K-contiguous [row][k] layout, padded).
-// Row-grouped kinds walk a persistent loop over the tiles of all local experts;
-// the per-expert tile prefix comes from the counting sort on the device, so
-// the host never needs the data-dependent row count.  Every output element is
-// produced by one workgroup with a fixed K order: results are run-to-run
-// identical (no split-K, no atomics).
+// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile (per B
+// matrix; UP computes the W1 and W3 tiles of the same columns), each wave a
+// (BM/2) x (BN/2) block of 32x32 MFMA tiles, over K in steps of 64 staged
+// through double-buffered LDS in a K-contiguous [row][k] layout: 128-byte rows
+// of eight 16-byte chunks, XOR-swizzled so that the 16-byte fragment reads of
+// 16 consecutive rows hit distinct banks.  Operands stored K-contiguous go
+// from HBM straight to LDS (buffer_load_dwordx4 ... lds, 1 KB per wave
+// instruction, no VGPRs), through buffer resources rebased on each tile so
+// that rows past the expert's end read as zero.  Operands stored M- or
+// N-contiguous (the backward products) are loaded as 8 x 8 blocks and
+// transposed in registers (v_perm_b32) before 16-byte LDS stores.
+//
+// Scheduling: row-grouped kinds run a persistent loop over the tiles of all
+// local experts in (expert, n-tile, m-tile) order, with the tile prefix of
+// each expert computed on the device by the counting sort, so the host never
+// needs the data-dependent row count.  Workgroup b runs on XCD b mod 8; the
+// loop hands each XCD a contiguous run of tiles so that m-tiles sharing a
+// weight tile meet in one L2.  Every output element is produced by one
+// workgroup with a fixed K order: results are run-to-run identical (no
+// split-K, no atomics).
 #include "mok_device.h"
 #include "mok_internal.h"
 #include "gemm_common.h"
 
 namespace mok {
 
-// Row-grouped epilogues: one output element (row, col) from the fp32
-// accumulator v (and u, the W3 accumulator, for UP).
-template <int KIND>
-__device__ __forceinline__ void epilogue_rows(const GroupedGemmArgs& args, const GemmGeom& G, int row, int col,
-                                              float v, float u) {
-  const int64_t o = (int64_t)row * G.N + col;
-  if constexpr (KIND == KIND_UP) {
-    ((bf16_t*)args.out0)[o] = f2bf(v * sigmoidf_(v) * u);
-    if (args.save) {
-      ((bf16_t*)args.save_a)[o] = f2bf(v);
-      ((bf16_t*)args.save_b)[o] = f2bf(u);
-    }
-  } else if constexpr (KIND == KIND_DH) {
-    const float a = bf2f(((const bf16_t*)args.save_a)[o]);
-    const float b = bf2f(((const bf16_t*)args.save_b)[o]);
-    const float sg = sigmoidf_(a);
-    bf16_t* dab = (bf16_t*)args.out0 + (int64_t)row * 2 * args.F;
-    dab[col] = f2bf(v * b * sg * (1.0f + a * (1.0f - sg)));
-    dab[args.F + col] = f2bf(v * a * sg);
-  } else {
-    ((bf16_t*)args.out0)[o] = f2bf(v);
+constexpr int kBK = 64;           // K step; one LDS row holds 64 bf16 = 128 bytes = 8 chunks
+constexpr int kRowBytes = kBK * 2;
+
+// Physical 16-byte chunk of logical chunk c in LDS row r.  This XOR swizzle
+// keeps fragment reads (32 consecutive rows, one chunk) and the transposed
+// block stores below free of bank conflicts for 64 banks with 16-lane phases
+// and for 32 banks with 8-lane phases alike.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+// Grouped raster inside one expert: groups of GM m-tiles, n-tiles outer and
+// m-tiles inner within a group, so that a run of consecutive tiles forms a
+// GM x (run / GM) block that reuses both operands.
+__device__ __forceinline__ void tile_mn(int local, int mt, int ntn, int& m, int& n) {
+  constexpr int GM = 4;
+  const int g = local / (GM * ntn);
+  const int gm0 = g * GM;
+  const int gsz = mt - gm0 < GM ? mt - gm0 : GM;
+  const int rem = local - g * GM * ntn;
+  n = rem / gsz;
+  m = gm0 + rem % gsz;
+}
+
+// Store the transpose of an 8 x 8 block of 16-bit values into a swizzled LDS
+// tile: in[i] holds K-row i (8 consecutive M/N values starting at 8 * mb);
+// LDS row 8 * mb + t receives chunk kb = those 8 K values of column t.
+// Lanes with bit 3 of mb set write the rows of each pair in swapped order,
+// which removes the remaining bank conflicts (only the v_perm selector
+// changes per lane).
+__device__ __forceinline__ void transposed_store(const u32x4_t in[8], uint8_t* tile, int mb, int kb) {
+  const uint32_t x = (mb >> 3) & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = j ^ (int)x;
+    const uint32_t sel = ((j & 1) ^ x) ? 0x07060302u : 0x05040100u;
+    u32x4_t o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][j >> 1], in[2 * w][j >> 1], sel);
+    const int r = mb * 8 + t;
+    *reinterpret_cast<u32x4_t*>(&tile[r * kRowBytes + swz_chunk(r, kb) * 16]) = o;
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KIND>
-__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
+template <int KIND, int BM, int BN>
+struct TileCfg {
   using Tr = Traits<KIND>;
-  constexpr int NT = WM * WN * 64;
-  constexpr int NB = Tr::NB;
-  constexpr int PAD = 8;
-  constexpr int LDS_K = BK + PAD;           // row stride in elements
-  constexpr int TM = BM / WM, TN = BN / WN; // wave tile
-  constexpr int FM = TM / 32, FN = TN / 32; // 32x32 MFMA tiles per wave
-  constexpr int BROWS = NB * BN;
-  static_assert(TM % 32 == 0 && TN % 32 == 0 && BK % 16 == 0, "bad tile");
-  constexpr int CHA = BM * BK / 8 / NT;
-  constexpr int CHB = BROWS * BK / 8 / NT;
-  static_assert(BM * BK / 8 % NT == 0 && BROWS * BK / 8 % NT == 0, "tile must split evenly");
+  static constexpr int NT = 256, WM = 2, WN = 2;
+  static constexpr int NB = Tr::NB;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int BROWS = NB * BN;
+  // K-contiguous operand: direct-to-LDS loads of 8 rows (1 KB) per wave instruction
+  static constexpr int DMA_A = Tr::A_MN ? 0 : BM / 8 / 4;
+  static constexpr int DMA_B = Tr::B_MN ? 0 : BROWS / 8 / 4;
+  // MN-contiguous operand: 8x8 blocks per thread, transposed in registers
+  static constexpr int BLA = Tr::A_MN ? (kBK / 8) * (BM / 8) / NT : 0;
+  static constexpr int BLB = Tr::B_MN ? (kBK / 8) * (BROWS / 8) / NT : 0;
+  static_assert(!Tr::A_MN || BLA >= 1, "MN tile too small");
+  static_assert(!Tr::B_MN || BLB >= 1, "MN tile too small");
+  static_assert(BM % 32 == 0 && BROWS % 32 == 0, "tile rows");
+};
 
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDS_K];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BROWS * LDS_K];
+template <int KIND, int BM, int BN>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
+  using Tr = Traits<KIND>;
+  using C = TileCfg<KIND, BM, BN>;
+  constexpr int NT = C::NT, NB = C::NB, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, BROWS = C::BROWS;
+
+  // One LDS arena: two stages of the A and B tiles during the K loop, then
+  // four per-wave staging regions for the epilogue.
+  constexpr int kArena = 2 * (BM + BROWS) * kRowBytes;
+  static_assert(kArena >= 4 * 32768, "epilogue staging needs 32 KB per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
   __shared__ int32_t s_tp[1025];
+  uint8_t (*sA)[BM * kRowBytes] = reinterpret_cast<uint8_t (*)[BM * kRowBytes]>(arena);
+  uint8_t (*sB)[BROWS * kRowBytes] = reinterpret_cast<uint8_t (*)[BROWS * kRowBytes]>(arena + 2 * BM * kRowBytes);
 
   const GemmGeom G = geom_of<KIND>(args.d, args.F);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WN, wn = wid % WN;
+  const int wm = wid / C::WN, wn = wid % C::WN;
   const bf16_t* __restrict__ Abase = (const bf16_t*)args.A;
   const bf16_t* __restrict__ B0 = (const bf16_t*)args.B0;
   const bf16_t* __restrict__ B1 = (const bf16_t*)args.B1;
   const int E_loc = args.E_loc;
+  const int ntn = (G.N + BN - 1) / BN;
 
-  // ---------------------------------------------------------------- tiles
-  int total;
-  int ntn = (G.N + BN - 1) / BN;
-  int ntm_k = 0;  // GROUP_K: m tiles per expert
+  int total, ntm_k = 0;
+  constexpr int NZ = KIND == KIND_DW13 ? 2 : 1;  // DW13 computes dW1 (z = 0) and dW3 (z = 1)
   if constexpr (!Tr::GROUP_K) {
     const int bidx = (BM == 64) ? 0 : (BM == 128 ? 1 : 2);
     const int32_t* tp = args.tile_prefix + bidx * (E_loc + 1);
@@ -90,115 +135,176 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_bf16_kernel(Grouped
     total = s_tp[E_loc] * ntn;
   } else {
     ntm_k = (G.M + BM - 1) / BM;
-    total = E_loc * ntm_k * ntn;
+    total = E_loc * NZ * ntm_k * ntn;
   }
-
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    int e_loc, row0, row_end, m0 = 0, n0;
+  // Row-grouped kinds: equal-sized tiles in a static round-robin.  XCD-aware
+  // order: workgroup b (on XCD b % 8) takes tiles from the contiguous run
+  // [x * G/8, (x+1) * G/8) of each round of G tiles.  Weight-gradient kinds:
+  // the work of a tile grows with its expert's rows, so tiles are pulled from
+  // a device-side counter, heaviest expert first (each tile is still computed
+  // whole by one workgroup: the results do not depend on the assignment).
+  const int G_ = gridDim.x;
+  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+  __shared__ int s_next;
+  auto next_tile = [&](int cur) -> int {
     if constexpr (!Tr::GROUP_K) {
-      const int total_m = s_tp[E_loc];
-      const int mt = tile % total_m;
-      n0 = (tile / total_m) * BN;
-      int lo = 0, hi = E_loc - 1;  // largest i with s_tp[i] <= mt
+      return cur < 0 ? vb : cur + G_;
+    } else {
+      if (tid == 0) s_next = atomicAdd(args.queue, 1);
+      __syncthreads();
+      const int t = s_next;
+      __syncthreads();
+      return t;
+    }
+  };
+
+  for (int tile = next_tile(-1); tile < total; tile = next_tile(tile)) {
+    int e_loc, row0, row_end, m0 = 0, n0, z = 0;
+    if constexpr (!Tr::GROUP_K) {
+      // (expert, n-tile, m-tile) order; expert e owns tiles [s_tp[e]*ntn, s_tp[e+1]*ntn)
+      int lo = 0, hi = E_loc - 1;
       while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (s_tp[mid] <= mt) lo = mid; else hi = mid - 1;
+        if (s_tp[mid] * ntn <= tile) lo = mid; else hi = mid - 1;
       }
       e_loc = lo;
+      int mt, nt;
+      tile_mn(tile - s_tp[e_loc] * ntn, s_tp[e_loc + 1] - s_tp[e_loc], ntn, mt, nt);
+      n0 = nt * BN;
       const int e = args.eb + e_loc;
-      row0 = args.offsets[e] + (mt - s_tp[e_loc]) * BM;
+      row0 = args.offsets[e] + mt * BM;
       row_end = args.offsets[e + 1];
     } else {
-      e_loc = tile / (ntm_k * ntn);
-      const int rem = tile % (ntm_k * ntn);
-      m0 = (rem % ntm_k) * BM;
-      n0 = (rem / ntm_k) * BN;
+      const int per_z = ntm_k * ntn;
+      e_loc = args.expert_order[tile / (NZ * per_z)];
+      const int rem = tile % (NZ * per_z);
+      z = rem / per_z;
+      int mt, nt;
+      tile_mn(rem % per_z, ntm_k, ntn, mt, nt);
+      m0 = mt * BM;
+      n0 = nt * BN;
       const int e = args.eb + e_loc;
       row0 = args.offsets[e];
       row_end = args.offsets[e + 1];
     }
-    const int z = KIND == KIND_DW13 ? blockIdx.y : 0;
-
-    // K extent
+    // The tile coordinates are wave-uniform; say so, so that addresses and
+    // buffer resources live in scalar registers (a divergent resource would
+    // make every buffer load a waterfall loop).
+    e_loc = __builtin_amdgcn_readfirstlane(e_loc);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    row_end = __builtin_amdgcn_readfirstlane(row_end);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    z = __builtin_amdgcn_readfirstlane(z);
     const int kbeg = Tr::GROUP_K ? row0 : 0;
     const int kend = Tr::GROUP_K ? row_end : G.K;
-    const int nk = (kend - kbeg + BK - 1) / BK;
+    const int nk = (kend - kbeg + kBK - 1) / kBK;
 
-    u32x4_t ra[CHA], rb[CHB];
+    // ------------------------------------------------------------ direct-to-LDS sources
+    // Buffer resources rebased on this tile: rows past the expert's end (A) or
+    // past N (B) fall outside num_records and read as zero.
+    __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, 0, 0x00020000);
+    __amdgpu_buffer_rsrc_t rsB0 = rsA, rsB1 = rsA;
+    uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
+    if constexpr (!Tr::A_MN) {
+      const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
+      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + (int64_t)row0 * G.lda), (short)0,
+                                              (int)((int64_t)rows * G.lda * 2), 0x00020000);
+#pragma unroll
+      for (int q = 0; q < C::DMA_A; ++q) {
+        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
+        offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
+      }
+    }
+    if constexpr (!Tr::B_MN) {
+      const int nb_rows = G.N - n0 < BN ? G.N - n0 : BN;  // this tile's rows of each B matrix
+      const bf16_t* b0 = B0 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
+      rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)b0, (short)0, (int)((int64_t)nb_rows * G.ldb * 2), 0x00020000);
+      if constexpr (NB == 2) {
+        const bf16_t* b1 = B1 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
+        rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)b1, (short)0, (int)((int64_t)nb_rows * G.ldb * 2),
+                                                 0x00020000);
+      }
+#pragma unroll
+      for (int q = 0; q < C::DMA_B; ++q) {
+        const int r = (wid * C::DMA_B + q) * 8 + (lane >> 3);      // LDS row
+        const int rl = (NB == 2 && r >= BN) ? r - BN : r;          // row within its matrix
+        offB[q] = (uint32_t)(rl * G.ldb * 2 + swz_chunk(r, lane & 7) * 16);
+      }
+    }
 
-    auto load_a = [&](int k0) {
+    u32x4_t ta[C::BLA > 0 ? C::BLA : 1][8], tb[C::BLB > 0 ? C::BLB : 1][8];
+
+    // Issue the loads of K-step k0 into LDS stage `buf` (direct) or registers (MN).
+    auto issue = [&](int k0, int buf) {
+      if constexpr (!Tr::A_MN) {
 #pragma unroll
-      for (int q = 0; q < CHA; ++q) {
-        const int c = tid + q * NT;
-        if constexpr (!Tr::A_MN) {
-          const int i = c / (BK / 8), kc = c % (BK / 8);
-          int r = row0 + i;
-          r = r < row_end ? r : row_end - 1;
-          ra[q] = *reinterpret_cast<const u32x4_t*>(Abase + (int64_t)r * G.lda + k0 + kc * 8);
-        } else {
-          const int kk = c / (BM / 8), mc = c % (BM / 8);
-          const int kr = k0 + kk, m = m0 + mc * 8;
-          const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
-          ra[q] = (kr < kend && m < G.M) ? *reinterpret_cast<const u32x4_t*>(p + (int64_t)kr * G.lda + m)
-                                         : u32x4_t{0u, 0u, 0u, 0u};
+        for (int q = 0; q < C::DMA_A; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (void __attribute__((address_space(3)))*)
+                                                   &sA[buf][(wid * C::DMA_A + q) * 1024], 16, offA[q], k0 * 2, 0, 0);
+      } else {
+        const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
+#pragma unroll
+        for (int q = 0; q < C::BLA; ++q) {
+          const int blk = tid + q * NT;
+          const int mb = blk % (BM / 8), kb = blk / (BM / 8);
+          const int m = m0 + mb * 8;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kr = k0 + kb * 8 + i;
+            ta[q][i] = (kr < kend && m < G.M) ? *reinterpret_cast<const u32x4_t*>(p + (int64_t)kr * G.lda + m)
+                                              : u32x4_t{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+      if constexpr (!Tr::B_MN) {
+#pragma unroll
+        for (int q = 0; q < C::DMA_B; ++q) {
+          const int r = (wid * C::DMA_B + q) * 8;
+          auto dst = (void __attribute__((address_space(3)))*)&sB[buf][(wid * C::DMA_B + q) * 1024];
+          if (NB == 2 && r >= BN)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, offB[q], k0 * 2, 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, offB[q], k0 * 2, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::BLB; ++q) {
+          const int blk = tid + q * NT;
+          const int nb = blk % (BROWS / 8), kb = blk / (BROWS / 8);
+          const int n = n0 + nb * 8;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kr = k0 + kb * 8 + i;
+            const bf16_t* src;
+            bool ok;
+            if constexpr (!Tr::GROUP_K) {
+              const int krl = kr < G.ksplit ? kr : kr - G.ksplit;
+              src = (kr < G.ksplit ? B0 : B1) + (int64_t)e_loc * G.b_estride + (int64_t)krl * G.ldb + n;
+              ok = n < G.N;
+            } else {
+              src = B0 + (int64_t)kr * G.ldb + n;
+              ok = kr < kend && n < G.N;
+            }
+            tb[q][i] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+          }
         }
       }
     };
-    auto load_b = [&](int k0) {
+    // Transpose the register-staged (MN) blocks into LDS stage `buf`.
+    auto commit = [&](int buf) {
+      if constexpr (Tr::A_MN) {
 #pragma unroll
-      for (int q = 0; q < CHB; ++q) {
-        const int c = tid + q * NT;
-        if constexpr (!Tr::B_MN) {
-          const int i = c / (BK / 8), kc = c % (BK / 8);
-          const int which = (NB == 2 && i >= BN) ? 1 : 0;
-          int n = n0 + i - which * BN;
-          n = n < G.N ? n : G.N - 1;
-          const bf16_t* base = (which ? B1 : B0) + (int64_t)e_loc * G.b_estride;
-          rb[q] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)n * G.ldb + k0 + kc * 8);
-        } else if constexpr (!Tr::GROUP_K) {
-          const int kk = c / (BN / 8), nc = c % (BN / 8);
-          const int kr = k0 + kk, n = n0 + nc * 8;
-          const bf16_t* base = (kr < G.ksplit ? B0 : B1) + (int64_t)e_loc * G.b_estride;
-          const int krl = kr < G.ksplit ? kr : kr - G.ksplit;
-          rb[q] = n < G.N ? *reinterpret_cast<const u32x4_t*>(base + (int64_t)krl * G.ldb + n)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-        } else {
-          const int kk = c / (BN / 8), nc = c % (BN / 8);
-          const int kr = k0 + kk, n = n0 + nc * 8;
-          rb[q] = (kr < kend && n < G.N) ? *reinterpret_cast<const u32x4_t*>(B0 + (int64_t)kr * G.ldb + n)
-                                         : u32x4_t{0u, 0u, 0u, 0u};
+        for (int q = 0; q < C::BLA; ++q) {
+          const int blk = tid + q * NT;
+          transposed_store(ta[q], sA[buf], blk % (BM / 8), blk / (BM / 8));
         }
       }
-    };
-    auto store_a = [&](int buf) {
+      if constexpr (Tr::B_MN) {
 #pragma unroll
-      for (int q = 0; q < CHA; ++q) {
-        const int c = tid + q * NT;
-        if constexpr (!Tr::A_MN) {
-          const int i = c / (BK / 8), kc = c % (BK / 8);
-          *reinterpret_cast<u32x4_t*>(&sA[buf][i * LDS_K + kc * 8]) = ra[q];
-        } else {
-          const int kk = c / (BM / 8), mc = c % (BM / 8);
-          const u32x4_t w = ra[q];
-#pragma unroll
-          for (int h = 0; h < 8; ++h)
-            sA[buf][(mc * 8 + h) * LDS_K + kk] = (bf16_t)((h & 1) ? (w[h >> 1] >> 16) : (w[h >> 1] & 0xFFFF));
-        }
-      }
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < CHB; ++q) {
-        const int c = tid + q * NT;
-        if constexpr (!Tr::B_MN) {
-          const int i = c / (BK / 8), kc = c % (BK / 8);
-          *reinterpret_cast<u32x4_t*>(&sB[buf][i * LDS_K + kc * 8]) = rb[q];
-        } else {
-          const int kk = c / (BN / 8), nc = c % (BN / 8);
-          const u32x4_t w = rb[q];
-#pragma unroll
-          for (int h = 0; h < 8; ++h)
-            sB[buf][(nc * 8 + h) * LDS_K + kk] = (bf16_t)((h & 1) ? (w[h >> 1] >> 16) : (w[h >> 1] & 0xFFFF));
+        for (int q = 0; q < C::BLB; ++q) {
+          const int blk = tid + q * NT;
+          transposed_store(tb[q], sB[buf], blk % (BROWS / 8), blk / (BROWS / 8));
         }
       }
     };
@@ -214,33 +320,32 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_bf16_kernel(Grouped
           for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
 
     if (nk > 0) {
-      load_a(kbeg);
-      load_b(kbeg);
-      store_a(0);
-      store_b(0);
+      issue(kbeg, 0);
+      commit(0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < nk) {
-        load_a(kbeg + (kt + 1) * BK);
-        load_b(kbeg + (kt + 1) * BK);
-      }
-      const bf16_t* a_s = sA[buf];
-      const bf16_t* b_s = sB[buf];
+      if (kt + 1 < nk) issue(kbeg + (kt + 1) * kBK, buf ^ 1);
+      const uint8_t* a_s = sA[buf];
+      const uint8_t* b_s = sB[buf];
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int koff = kk * 16 + (lane >> 5) * 8;
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int lc = kk * 2 + (lane >> 5);
         bf16x8_t af[FM], bfr[NB][FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(&a_s[(wm * TM + i * 32 + (lane & 31)) * LDS_K + koff]);
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8_t*>(&a_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(
-                &b_s[(b * BN + wn * TN + j * 32 + (lane & 31)) * LDS_K + koff]);
+          for (int j = 0; j < FN; ++j) {
+            const int r = b * BN + wn * TN + j * 32 + (lane & 31);
+            bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(&b_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
+          }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -249,70 +354,163 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_bf16_kernel(Grouped
             for (int j = 0; j < FN; ++j)
               acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) {
-        store_a(buf ^ 1);
-        store_b(buf ^ 1);
-      }
+      if (kt + 1 < nk) commit(buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
 
     // ---------------------------------------------------------------- epilogue
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    // Each wave stages its accumulators in its own 32 KB LDS region, then
+    // every lane handles 8 consecutive columns of one row: 16-byte loads and
+    // stores along rows.
+    float* ep = reinterpret_cast<float*>(arena + wid * 32768);
+    const int wrow0 = wm * TM, wcol0 = wn * TN;
+    if constexpr (NB == 2) {
+      // UP: gate (W1) and up (W3) accumulators of one 32-column fragment
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * TN + j * 32 + (lane & 31);
-        const bool col_ok = col < G.N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rit = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float v = acc[0][i][j][r];
-          const float u = acc[NB - 1][i][j][r];
-          if constexpr (!Tr::GROUP_K) {
-            const int row = row0 + rit;
-            if (col_ok && row < row_end) epilogue_rows<KIND>(args, G, row, col, v, u);
-          } else {
-            const int m = m0 + rit;
-            if (col_ok && m < G.M) {
-              float* outp = (float*)(KIND == KIND_DW13 && z ? args.out1 : args.out0);
-              outp[(int64_t)e_loc * G.M * G.N + (int64_t)m * G.N + col] = v;
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
+            ep[4096 + rr * 32 + (lane & 31)] = acc[NB - 1][i][j][r];
+          }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 2
+        for (int q = 0; q < TM * 32 / 8 / 64; ++q) {
+          const int seg = q * 64 + lane;
+          const int rr = seg >> 2, c8 = (seg & 3) * 8;
+          const int row = row0 + wrow0 + rr, col = n0 + wcol0 + j * 32 + c8;
+          if (row < row_end && col < G.N) {
+            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
+            const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[4096 + rr * 32 + c8]);
+            const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
+            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+            u32x4_t h, a, b;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float h0 = v[2 * t] * sigmoidf_(v[2 * t]) * u[2 * t];
+              const float h1 = v[2 * t + 1] * sigmoidf_(v[2 * t + 1]) * u[2 * t + 1];
+              h[t] = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
+              a[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+              b[t] = (uint32_t)f2bf(u[2 * t]) | ((uint32_t)f2bf(u[2 * t + 1]) << 16);
+            }
+            const int64_t o = (int64_t)row * G.N + col;
+            *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = h;
+            if (args.save) {
+              *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_a + o) = a;
+              *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_b + o) = b;
             }
           }
         }
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else {
+#pragma unroll
+      for (int jp = 0; jp < FN / 2; ++jp) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
+            }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 2
+        for (int q = 0; q < TM * 64 / 8 / 64; ++q) {
+          const int seg = q * 64 + lane;
+          const int rr = seg >> 3, c8 = (seg & 7) * 8;
+          const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
+          const f32x4_t v0 = pv[0], v1 = pv[1];
+          const int col = n0 + wcol0 + jp * 64 + c8;
+          if constexpr (!Tr::GROUP_K) {
+            const int row = row0 + wrow0 + rr;
+            if (row < row_end && col < G.N) {
+              float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+              const int64_t o = (int64_t)row * G.N + col;
+              if constexpr (KIND == KIND_DH) {
+                const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_a + o);
+                const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_b + o);
+                u32x4_t da, db;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  float dav[2], dbv[2];
+#pragma unroll
+                  for (int hh = 0; hh < 2; ++hh) {
+                    const float a = __uint_as_float(hh ? (av[t] & 0xFFFF0000u) : (av[t] << 16));
+                    const float b = __uint_as_float(hh ? (bv[t] & 0xFFFF0000u) : (bv[t] << 16));
+                    const float sg = sigmoidf_(a);
+                    const float dh = v[2 * t + hh];
+                    dav[hh] = dh * b * sg * (1.0f + a * (1.0f - sg));
+                    dbv[hh] = dh * a * sg;
+                  }
+                  da[t] = (uint32_t)f2bf(dav[0]) | ((uint32_t)f2bf(dav[1]) << 16);
+                  db[t] = (uint32_t)f2bf(dbv[0]) | ((uint32_t)f2bf(dbv[1]) << 16);
+                }
+                bf16_t* dab = (bf16_t*)args.out0 + (int64_t)row * 2 * args.F;
+                *reinterpret_cast<u32x4_t*>(dab + col) = da;
+                *reinterpret_cast<u32x4_t*>(dab + args.F + col) = db;
+              } else {
+                u32x4_t y;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+                *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = y;
+              }
+            }
+          } else {
+            const int m = m0 + wrow0 + rr;
+            if (m < G.M && col < G.N) {
+              float* outp = (float*)(KIND == KIND_DW13 && z ? args.out1 : args.out0);
+              f32x4_t* dst = reinterpret_cast<f32x4_t*>(outp + (int64_t)e_loc * G.M * G.N + (int64_t)m * G.N + col);
+              dst[0] = v0;
+              dst[1] = v1;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
       }
     }
-    __syncthreads();
+    __syncthreads();  // staging regions overlap the next tile's first K stage
   }
+#endif
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int KIND>
+template <int KIND, int BM, int BN>
 static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   const GemmGeom G = geom_of<KIND>(g.d, g.F);
   const int ntn = (G.N + BN - 1) / BN;
   int blocks;
   dim3 grid;
   if constexpr (Traits<KIND>::GROUP_K) {
-    blocks = g.E_loc * ((G.M + BM - 1) / BM) * ntn;
-    grid = dim3(blocks, KIND == KIND_DW13 ? 2 : 1);
+    // persistent workers over the tile counter (zeroed earlier on the stream)
+    const int64_t tiles = (int64_t)g.E_loc * (KIND == KIND_DW13 ? 2 : 1) * ((G.M + BM - 1) / BM) * ntn;
+    blocks = (int)(tiles < 256 ? tiles : 256);
+    grid = dim3(blocks);
   } else {
-    // persistent over the device-side tile count; bounded by the worst case
+    // persistent: one workgroup per CU, bounded by the worst-case tile count
     const int64_t worst = ((g.P_max + BM - 1) / BM + g.E_loc) * (int64_t)ntn;
-    blocks = (int)(worst < 1024 ? worst : 1024);
+    blocks = (int)(worst < 256 ? worst : 256);
     grid = dim3(blocks);
   }
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WM, WN, KIND>), grid, dim3(WM * WN * 64), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<KIND, BM, BN>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
-    case KIND_UP:   return run_bf16<128, 128, 64, 2, 2, KIND_UP>(g, s);
-    case KIND_DOWN: return run_bf16<128, 128, 64, 2, 2, KIND_DOWN>(g, s);
-    case KIND_DH:   return run_bf16<128, 128, 64, 2, 2, KIND_DH>(g, s);
-    case KIND_DX:   return run_bf16<128, 128, 64, 2, 2, KIND_DX>(g, s);
-    case KIND_DW2:  return run_bf16<128, 128, 64, 2, 2, KIND_DW2>(g, s);
-    case KIND_DW13: return run_bf16<128, 128, 64, 2, 2, KIND_DW13>(g, s);
+    case KIND_UP:   return run_bf16<KIND_UP, 256, 128>(g, s);
+    case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256>(g, s);
+    case KIND_DH:   return run_bf16<KIND_DH, 256, 256>(g, s);
+    case KIND_DX:   return run_bf16<KIND_DX, 256, 256>(g, s);
+    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256>(g, s);
+    case KIND_DW13: return run_bf16<KIND_DW13, 256, 256>(g, s);
   }
   return hipErrorInvalidValue;
 }

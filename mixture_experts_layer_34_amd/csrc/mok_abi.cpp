@@ -41,7 +41,15 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   return MOK_OK;
 }
 
-void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_t* tile_prefix_off) {
+// Public arrays (mok_saved_layout) plus two internal ones: the per-expert
+// row-tile prefix and the experts ranked by row count.
+struct SavedLayout {
+  mok_saved_layout pub;
+  size_t tile_prefix, expert_order;
+};
+
+void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_t* tile_prefix_off,
+                  size_t* expert_order_off) {
   const size_t Tk = (size_t)c.T * k, A = act_size(c);
   const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
   size_t o = 0;
@@ -50,6 +58,7 @@ void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_
   s->topk_gate = o;    o = align256(o + Tk * 4);
   s->offsets = o;      o = align256(o + ((size_t)c.E + 1) * 4);
   *tile_prefix_off = o; o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
+  *expert_order_off = o; o = align256(o + E_loc * 4);
   s->row_of_pair = o;  o = align256(o + Tk * 4);
   s->pair_of_row = o;  o = align256(o + Tk * 4);
   s->A = o;            o = align256(o + Tk * c.ffn * A);
@@ -78,7 +87,7 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->dy = o;            o = align256(o + (mx ? 0 : Tk * c.d * A));
   w->dab = o;           o = align256(o + (mx ? 0 : Tk * 2 * c.ffn * A));
   w->dxp = o;           o = align256(o + (mx ? 0 : Tk * c.d * A));
-  w->mb_table = o;      o = align256(o + 256);
+  w->queue = o;         o = align256(o + 256);
   w->total = o;
 }
 
@@ -143,8 +152,8 @@ mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k, size_t*
   WorkspaceLayout w;
   workspace_layout(*cfg, k, &w);
   mok_saved_layout s;
-  size_t tp;
-  saved_layout(*cfg, k, &s, &tp);
+  size_t tp, eo;
+  saved_layout(*cfg, k, &s, &tp, &eo);
   *workspace_bytes = w.total;
   *saved_bytes = s.total;
   return MOK_OK;
@@ -154,8 +163,8 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
   mok_status st = validate_config(cfg, k);
   if (st != MOK_OK) return st;
   if (!out) return MOK_ERR_INVALID_ARG;
-  size_t tp;
-  saved_layout(*cfg, k, out, &tp);
+  size_t tp, eo;
+  saved_layout(*cfg, k, out, &tp, &eo);
   return MOK_OK;
 }
 
@@ -182,8 +191,8 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
   const int bf16 = c.precision != MOK_PREC_F32;
   mok_saved_layout sl;
-  size_t tp_off;
-  saved_layout(c, k, &sl, &tp_off);
+  size_t tp_off, eo_off;
+  saved_layout(c, k, &sl, &tp_off, &eo_off);
   WorkspaceLayout wl;
   workspace_layout(c, k, &wl);
 
@@ -192,16 +201,18 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   float* s_lse = at<float>(saved, sl.lse);
   int32_t* s_off = at<int32_t>(saved, sl.offsets);
   int32_t* s_tp = at<int32_t>(saved, tp_off);
+  int32_t* s_order = at<int32_t>(saved, eo_off);
   int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
   int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
 
   MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, topk_idx, topk_gate, s_idx, s_gate, s_lse, s));
   MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
                                at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
-                               s_rop, s_por, s));
+                               s_order, s_rop, s_por, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;
+  g.expert_order = s_order;
   g.eb = eb;
   g.E_loc = E_loc;
   g.d = d;
@@ -275,8 +286,8 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
   const int bf16 = c.precision != MOK_PREC_F32;
   mok_saved_layout sl;
-  size_t tp_off;
-  saved_layout(c, k, &sl, &tp_off);
+  size_t tp_off, eo_off;
+  saved_layout(c, k, &sl, &tp_off, &eo_off);
   WorkspaceLayout wl;
   workspace_layout(c, k, &wl);
   const int32_t* s_idx = at<int32_t>(saved, sl.topk_idx);
@@ -284,7 +295,9 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   const float* s_lse = at<float>(saved, sl.lse);
   const int32_t* s_off = at<int32_t>(saved, sl.offsets);
   const int32_t* s_tp = at<int32_t>(saved, tp_off);
+  const int32_t* s_order = at<int32_t>(saved, eo_off);
   const int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
+  int32_t* queue = at<int32_t>(workspace, wl.queue);
   void* dy = at<void>(workspace, wl.dy);
   void* dab = at<void>(workspace, wl.dab);
   void* dxp = at<void>(workspace, wl.dxp);
@@ -292,10 +305,11 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 
   // reverse-combine with the router backward
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
-                               bf16, dgate, drouter_logits, dy, s));
+                               bf16, dgate, drouter_logits, dy, queue, 2, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;
+  g.expert_order = s_order;
   g.eb = eb;
   g.E_loc = E_loc;
   g.d = d;
@@ -321,6 +335,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   gw.A = dy;
   gw.B0 = at<void>(saved, sl.H);
   gw.out0 = dW2;
+  gw.queue = queue;
   MOK_STAGE(MOK_STAGE_GEMM_DW2, run_gemm(c.precision, KIND_DW2, gw, s));
   MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
   GroupedGemmArgs g13 = g;
@@ -328,6 +343,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   g13.B0 = xp;
   g13.out0 = dW1;
   g13.out1 = dW3;
+  g13.queue = queue + 1;
   MOK_STAGE(MOK_STAGE_GEMM_DW13, run_gemm(c.precision, KIND_DW13, g13, s));
   return MOK_OK;
 }

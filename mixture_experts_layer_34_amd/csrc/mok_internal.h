@@ -27,7 +27,7 @@ struct WorkspaceLayout {
   size_t dy;            // backward: act [P_max, d]
   size_t dab;           // backward: act [P_max, 2F]  (dA | dB)
   size_t dxp;           // backward: act [P_max, d]
-  size_t mb_table;      // minibatch bookkeeping (int32)
+  size_t queue;         // int32 tile counters of the weight-gradient GEMMs
   size_t total;
   int nchunks;
   int64_t xp_rows;      // rows held by the dispatch buffer (P_max, or the ring)
@@ -41,8 +41,8 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t*
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
                                 int nchunks, int32_t* chunk_counts, int32_t* chunk_base,
                                 int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
-                                int32_t* tile_prefix, int32_t* row_of_pair, int32_t* pair_of_row,
-                                hipStream_t s);
+                                int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
+                                int32_t* pair_of_row, hipStream_t s);
 
 // X_perm[row(t,j)] = x[t] (act = bf16 when bf16 != 0, else fp32).
 hipError_t launch_dispatch_gather(const void* x, const int32_t* row_of_pair, int T, int k, int d,
@@ -61,7 +61,8 @@ hipError_t launch_combine(const void* rows, const float* gate, const int32_t* ro
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate,
                                 const int32_t* idx, const int32_t* row_of_pair,
                                 const float* logits, const float* lse, int T, int k, int E, int d,
-                                int bf16, float* dgate, float* dlogits, void* dy, hipStream_t s);
+                                int bf16, float* dgate, float* dlogits, void* dy, int32_t* queue_zero,
+                                int nqueue, hipStream_t s);
 
 // Grouped GEMMs of the expert FFN.  `offsets` is the global [E+1] array,
 // experts [eb, eb + E_loc) are local.  tile_prefix is the [kNumTileBM, E_loc+1]
@@ -72,6 +73,8 @@ struct GroupedGemmArgs {
   const void* B1;         // second weights (W3) where used
   const int32_t* offsets;
   const int32_t* tile_prefix;
+  const int32_t* expert_order;  // local experts by descending row count (ties: lower index)
+  int32_t* queue;               // tile counter of the weight-gradient kinds (zeroed on device)
   int eb, E_loc;
   int d, F;
   int64_t P_max;

@@ -265,8 +265,11 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
                                                             const float* __restrict__ logits,
                                                             const float* __restrict__ lse, int ntok, int k, int E,
                                                             int d, float* __restrict__ dgate,
-                                                            float* __restrict__ dlogits, T* __restrict__ dy) {
+                                                            float* __restrict__ dlogits, T* __restrict__ dy,
+                                                            int32_t* __restrict__ queue_zero, int nqueue) {
   __shared__ float red[4];
+  // the tile counters of the weight-gradient GEMMs that follow on the stream
+  if (blockIdx.x == 0 && (int)threadIdx.x < nqueue) queue_zero[threadIdx.x] = 0;
   __shared__ float dg[kMaxK];
   __shared__ int32_t sel[kMaxK];
   const int nv = d / 8;
@@ -315,17 +318,17 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
 
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate, const int32_t* idx,
                                 const int32_t* row_of_pair, const float* logits, const float* lse, int T, int k,
-                                int E, int d, int bf16, float* dgate, float* dlogits, void* dy, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  int blocks = T < 16384 ? T : 16384;
+                                int E, int d, int bf16, float* dgate, float* dlogits, void* dy, int32_t* queue_zero,
+                                int nqueue, hipStream_t s) {
+  int blocks = T < 16384 ? (T > 0 ? T : 1) : 16384;  // at least one block: it zeroes the counters
   if (bf16)
     hipLaunchKernelGGL(backward_gate_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)dout,
                        (const bf16_t*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits,
-                       (bf16_t*)dy);
+                       (bf16_t*)dy, queue_zero, nqueue);
   else
     hipLaunchKernelGGL(backward_gate_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dout,
                        (const float*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits,
-                       (float*)dy);
+                       (float*)dy, queue_zero, nqueue);
   return hipGetLastError();
 }
 

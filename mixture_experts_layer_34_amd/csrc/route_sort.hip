@@ -149,8 +149,10 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ counts_out,
                                                          int32_t* __restrict__ offsets_out,
                                                          int32_t* __restrict__ offsets_saved,
-                                                         int32_t* __restrict__ tile_prefix) {
+                                                         int32_t* __restrict__ tile_prefix,
+                                                         int32_t* __restrict__ expert_order) {
   __shared__ int32_t wsum[16];
+  __shared__ int32_t s_cnt[1024];
   __shared__ int32_t tsum[kNumTileBM][16];
   const int e = threadIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
@@ -205,6 +207,18 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     }
     for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
   }
+  // local experts ranked by descending row count, ties by lower index (the
+  // weight-gradient GEMMs start with the heaviest experts)
+  if (i_loc >= 0 && i_loc < E_loc) s_cnt[i_loc] = run;
+  __syncthreads();
+  if (i_loc >= 0 && i_loc < E_loc) {
+    int rank = 0;
+    for (int q = 0; q < E_loc; ++q) {
+      const int cq = s_cnt[q];
+      rank += (cq > run || (cq == run && q < i_loc)) ? 1 : 0;
+    }
+    expert_order[rank] = i_loc;
+  }
   if (i_loc >= 0 && i_loc < E_loc) {
 #pragma unroll
     for (int b = 0; b < kNumTileBM; ++b) {
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee, int nchunks,
                                 int32_t* chunk_counts, int32_t* chunk_base, int32_t* counts_out,
                                 int32_t* offsets_out, int32_t* offsets_saved, int32_t* tile_prefix,
-                                int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t s) {
+                                int32_t* expert_order, int32_t* row_of_pair, int32_t* pair_of_row, hipStream_t s) {
   const int64_t npairs = (int64_t)T * k;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -264,7 +278,7 @@ hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb,
                        nchunks, chunk_counts);
   }
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E, eb, ee,
-                     chunk_base, counts_out, offsets_out, offsets_saved, tile_prefix);
+                     chunk_base, counts_out, offsets_out, offsets_saved, tile_prefix, expert_order);
   if (blocks > 0) {
     hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(256), smem, s, idx, npairs, E, eb, ee, nbits,
                        nchunks, chunk_base, row_of_pair, pair_of_row);
