@@ -110,7 +110,7 @@ def main():
     ap.add_argument("--workload", default="bf16_train")
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (HBM counter calibration)")
     args = ap.parse_args()
