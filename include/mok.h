@@ -162,7 +162,7 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *   saved          mok_saved_layout.total bytes
  *   workspace      workspace_bytes bytes
  * Alignment: every pointer 16-byte aligned.  Constraints: 1 <= k <= E <= 1024,
- * d and F multiples of 64 (bf16 and MXFP8) or 16 (fp32), T*k < 2^31.
+ * d and F multiples of 64 (bf16), 128 (MXFP8) or 16 (fp32), T*k < 2^31.
  */
 mok_status mok_moe_forward(const void* x, const float* router_logits,
                            const void* W1, const void* W3, const void* W2, int32_t k,

@@ -31,7 +31,8 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if (c.expert_begin < 0 || c.expert_end <= c.expert_begin || c.expert_end > c.E) return MOK_ERR_INVALID_ARG;
   if (c.precision != MOK_PREC_F32 && c.precision != MOK_PREC_BF16 && c.precision != MOK_PREC_MXFP8)
     return MOK_ERR_INVALID_ARG;
-  const int mult = c.precision == MOK_PREC_F32 ? 16 : 64;
+  // bf16: K steps of 64; MXFP8: K steps of 128 bytes (and whole MX blocks); fp32: 16
+  const int mult = c.precision == MOK_PREC_F32 ? 16 : (c.precision == MOK_PREC_MXFP8 ? 128 : 64);
   if (c.d % mult || c.ffn % mult) return MOK_ERR_INVALID_ARG;
   if ((int64_t)c.T * k >= (int64_t(1) << 31)) return MOK_ERR_INVALID_ARG;
   if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
