@@ -178,10 +178,12 @@ def main():
 
     # per-stage averages over the timed steps
     stages = {}
+    ran = mok.STAGES if backward else mok.STAGES[:mok.STAGES.index("combine") + 1]
     for s, name in enumerate(mok.STAGES):
+        if name not in ran:
+            continue  # never recorded: asking for its time would be an error
         vals = [ev.elapsed_ms(stage_ev[i][2 * s], stage_ev[i][2 * s + 1]) for i in range(K)]
-        if backward or s <= mok.STAGES.index("combine"):
-            stages[name] = sum(vals) / len(vals)
+        stages[name] = sum(vals) / len(vals)
     P = int(buf.offsets[-1].item())
     U = int((buf.topk_idx.ge(w.expert_begin) & buf.topk_idx.lt(w.e_end)).any(dim=1).sum().item())
     flops, nbytes = stage_work(w, P, U)

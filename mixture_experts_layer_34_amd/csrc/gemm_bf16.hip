@@ -208,12 +208,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
     if constexpr (!Tr::A_MN) {
       const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
-      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + (int64_t)row0 * G.lda), (short)0,
-                                              (int)((int64_t)rows * G.lda * 2), 0x00020000);
+      if (args.gather_rows) {
+        // pull dispatch: each row comes straight from its token's row of x
+        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0,
+                                                (int)(args.gather_src_rows * G.lda * 2), 0x00020000);
 #pragma unroll
-      for (int q = 0; q < C::DMA_A; ++q) {
-        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
-        offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
+        for (int q = 0; q < C::DMA_A; ++q) {
+          const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
+          const int tok = r < rows ? args.gather_rows[row0 + r] / args.k_top : -1;
+          offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_chunk(r, lane & 7) * 16) : 0xFFFFFFF0u;
+        }
+      } else {
+        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + (int64_t)row0 * G.lda), (short)0,
+                                                (int)((int64_t)rows * G.lda * 2), 0x00020000);
+#pragma unroll
+        for (int q = 0; q < C::DMA_A; ++q) {
+          const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
+          offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
+        }
       }
     }
     if constexpr (!Tr::B_MN) {

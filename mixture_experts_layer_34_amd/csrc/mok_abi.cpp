@@ -116,6 +116,21 @@ struct StageMark {
   }
 };
 
+// A stage folded into another kernel still gets its (empty) pair of events,
+// so that callers timing every stage find them all recorded.
+inline void mark_empty_stage(const mok_moe_config& c, hipStream_t s, int stage) {
+  if (c.stage_events) {
+    (void)hipEventRecord((hipEvent_t)c.stage_events[2 * stage], s);
+    (void)hipEventRecord((hipEvent_t)c.stage_events[2 * stage + 1], s);
+  }
+}
+
+// BF16 without a ring pulls the dispatched rows straight from x inside the
+// GEMM loads (32-bit buffer offsets: x must stay below 2 GB).
+inline bool fused_pull(const mok_moe_config& c) {
+  return c.precision == MOK_PREC_BF16 && c.minibatch_rows == 0 && (int64_t)c.T * c.d * 2 < (int64_t(1) << 31);
+}
+
 #define MOK_STAGE(stage, call)                 \
   do {                                         \
     StageMark mark_(c, s, stage);              \
@@ -245,8 +260,16 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   } else {
     void* xp = at<void>(workspace, wl.xp);
-    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
-    g.A = xp;
+    if (fused_pull(c)) {
+      mark_empty_stage(c, s, MOK_STAGE_DISPATCH);
+      g.A = x;
+      g.gather_rows = s_por;
+      g.k_top = k;
+      g.gather_src_rows = T;
+    } else {
+      MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+      g.A = xp;
+    }
     g.B0 = W1;
     g.B1 = W3;
     g.out0 = at<void>(saved, sl.H);
@@ -260,6 +283,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g2.B1 = nullptr;
     g2.out0 = at<void>(saved, sl.Y);
     g2.save = 0;
+    g2.gather_rows = nullptr;
     MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   }
   MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, out, s));
@@ -338,6 +362,8 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   gw.out0 = dW2;
   gw.queue = queue;
   MOK_STAGE(MOK_STAGE_GEMM_DW2, run_gemm(c.precision, KIND_DW2, gw, s));
+  // X rows again, expert-sorted (the transposed operand of dW1/dW3 wants
+  // them contiguous: a gather inside its loads would chain two loads)
   MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
   GroupedGemmArgs g13 = g;
   g13.A = dab;

@@ -87,6 +87,12 @@ struct GroupedGemmArgs {
   const uint8_t* b_scale1;
   uint8_t* out_scale;     // MXFP8 H scales
   int save;               // write A and B (forward)
+  // Pull dispatch fused into the GEMM loads: when non-null, row r of the
+  // expert-sorted A operand of UP is row gather_rows[r] / k_top of the token
+  // matrix (x, with gather_src_rows rows) instead of row r.
+  const int32_t* gather_rows;
+  int k_top;
+  int64_t gather_src_rows;
 };
 
 // Expert-grouped GEMM of one kind (GemmKind in gemm_common.h) per precision:
