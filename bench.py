@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--minibatch-rows", type=int, default=0,
+                    help="ring pipeline minibatch rows R (0 = whole layer at once)")
+    ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (HBM counter calibration)")
     args = ap.parse_args()
@@ -131,7 +134,8 @@ def main():
     inp = W.make_inputs(w, device=dev)
     T = inp["x"].shape[0]
     shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision, expert_begin=w.expert_begin,
-                     expert_end=w.e_end, save_for_backward=backward)
+                     expert_end=w.e_end, save_for_backward=backward, minibatch_rows=args.minibatch_rows,
+                     ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0)
     buf = MoeBuffers(shape, device=dev)
     W1, W3, W2, scales = inp["W1"], inp["W3"], inp["W2"], None
     if w.precision == "mxfp8":
@@ -217,7 +221,9 @@ def main():
         "dtype": w.precision, "data": "synthetic",
         "config": {"workload": f"{w.name}: T={T} d={w.d} E={w.E} k={w.k} F={w.F} "
                                f"local experts [{w.expert_begin},{w.e_end}) pairs P={P}, "
-                               f"{'forward+backward' if backward else 'forward'}",
+                               f"{'forward+backward' if backward else 'forward'}"
+                               + (f", ring pipeline R={args.minibatch_rows} rows, {args.ring_mib} MiB ring"
+                                  if args.minibatch_rows else ""),
                    "global_batch": T, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),

@@ -54,7 +54,7 @@ typedef enum {
   MOK_OK = 0,
   MOK_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misalignment          */
   MOK_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement     */
-  MOK_ERR_WORKSPACE = 3,     /* ring smaller than one minibatch                 */
+  MOK_ERR_WORKSPACE = 3,     /* ring smaller than two minibatch slots           */
   MOK_ERR_HIP = 4,           /* a HIP runtime call failed (launch error)        */
   MOK_ERR_DEVICE = 5         /* reported by a device-side check                 */
 } mok_status;
@@ -78,10 +78,16 @@ typedef struct mok_moe_config {
   int32_t precision;         /* mok_precision                                   */
   int32_t minibatch_rows;    /* R: rows of the expert-sorted buffer processed
                                 per minibatch; 0 = the whole layer at once.
-                                The pages' minibatch trade-off ([kucoin §02]).  */
+                                The pages' minibatch trade-off ([kucoin §02]).
+                                R > 0 (BF16 only) runs the ring pipeline: one
+                                launch per minibatch m copies minibatch m+1
+                                into its ring slot while UP runs on m and DOWN
+                                on m-1.  Results are bitwise those of R = 0.  */
   int64_t ring_bytes;        /* fixed ring token buffer for dispatched rows
-                                ([fluid], [kucoin §02] "macrobatch"); 0 = no
-                                ring: the dispatch buffer holds every row.      */
+                                ([fluid], [kucoin §02] "macrobatch"), used
+                                with R > 0: floor(ring_bytes / (2 d R)) slots
+                                of R rows, at least 2 (else
+                                MOK_ERR_WORKSPACE); must be 0 when R = 0.       */
   uint32_t flags;            /* MOK_FLAG_*                                      */
   uint32_t reserved;         /* must be 0                                       */
   void* const* stage_events; /* NULL, or 2*MOK_NUM_STAGES hipEvent_t handles

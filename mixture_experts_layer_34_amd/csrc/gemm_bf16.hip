@@ -100,28 +100,337 @@ struct TileCfg {
   static_assert(BM % 32 == 0 && BROWS % 32 == 0, "tile rows");
 };
 
+// One output tile: K loop over double-buffered LDS stages, then the
+// LDS-staged epilogue.  Called by every thread of the workgroup with
+// wave-uniform tile coordinates; ends with a barrier (the epilogue staging
+// overlaps the next tile's first K stage).
 template <int KIND, int BM, int BN>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
-#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
+__device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* arena, int e_loc, int row0,
+                                          int row_end, int m0, int n0, int z) {
   using Tr = Traits<KIND>;
   using C = TileCfg<KIND, BM, BN>;
   constexpr int NT = C::NT, NB = C::NB, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, BROWS = C::BROWS;
-
-  // One LDS arena: two stages of the A and B tiles during the K loop, then
-  // four per-wave staging regions for the epilogue.
-  constexpr int kArena = 2 * (BM + BROWS) * kRowBytes;
-  static_assert(kArena >= 4 * 32768, "epilogue staging needs 32 KB per wave");
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
-  __shared__ int32_t s_tp[1025];
   uint8_t (*sA)[BM * kRowBytes] = reinterpret_cast<uint8_t (*)[BM * kRowBytes]>(arena);
   uint8_t (*sB)[BROWS * kRowBytes] = reinterpret_cast<uint8_t (*)[BROWS * kRowBytes]>(arena + 2 * BM * kRowBytes);
-
   const GemmGeom G = geom_of<KIND>(args.d, args.F);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / C::WN, wn = wid % C::WN;
   const bf16_t* __restrict__ Abase = (const bf16_t*)args.A;
   const bf16_t* __restrict__ B0 = (const bf16_t*)args.B0;
   const bf16_t* __restrict__ B1 = (const bf16_t*)args.B1;
+  const int kbeg = Tr::GROUP_K ? row0 : 0;
+  const int kend = Tr::GROUP_K ? row_end : G.K;
+  const int nk = (kend - kbeg + kBK - 1) / kBK;
+
+  // ------------------------------------------------------------ direct-to-LDS sources
+  // Buffer resources rebased on this tile: rows past the expert's end (A) or
+  // past N (B) fall outside num_records and read as zero.
+  __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rsB0 = rsA, rsB1 = rsA;
+  uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
+  if constexpr (!Tr::A_MN) {
+    const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
+    if (args.gather_rows) {
+      // pull dispatch: each row comes straight from its token's row of x
+      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0,
+                                              (int)(args.gather_src_rows * G.lda * 2), 0x00020000);
+#pragma unroll
+      for (int q = 0; q < C::DMA_A; ++q) {
+        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
+        const int tok = r < rows ? args.gather_rows[row0 + r] / args.k_top : -1;
+        offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_chunk(r, lane & 7) * 16) : 0xFFFFFFF0u;
+      }
+    } else {
+      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + ((int64_t)row0 - args.a_row_shift) * G.lda),
+                                              (short)0, (int)((int64_t)rows * G.lda * 2), 0x00020000);
+#pragma unroll
+      for (int q = 0; q < C::DMA_A; ++q) {
+        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
+        offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
+      }
+    }
+  }
+  if constexpr (!Tr::B_MN) {
+    const int nb_rows = G.N - n0 < BN ? G.N - n0 : BN;  // this tile's rows of each B matrix
+    const bf16_t* b0 = B0 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
+    rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)b0, (short)0, (int)((int64_t)nb_rows * G.ldb * 2), 0x00020000);
+    if constexpr (NB == 2) {
+      const bf16_t* b1 = B1 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
+      rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)b1, (short)0, (int)((int64_t)nb_rows * G.ldb * 2),
+                                               0x00020000);
+    }
+#pragma unroll
+    for (int q = 0; q < C::DMA_B; ++q) {
+      const int r = (wid * C::DMA_B + q) * 8 + (lane >> 3);      // LDS row
+      const int rl = (NB == 2 && r >= BN) ? r - BN : r;          // row within its matrix
+      offB[q] = (uint32_t)(rl * G.ldb * 2 + swz_chunk(r, lane & 7) * 16);
+    }
+  }
+
+  u32x4_t ta[C::BLA > 0 ? C::BLA : 1][8], tb[C::BLB > 0 ? C::BLB : 1][8];
+
+  // Issue the loads of K-step k0 into LDS stage `buf` (direct) or registers (MN).
+  auto issue = [&](int k0, int buf) {
+    if constexpr (!Tr::A_MN) {
+#pragma unroll
+      for (int q = 0; q < C::DMA_A; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (void __attribute__((address_space(3)))*)
+                                                 &sA[buf][(wid * C::DMA_A + q) * 1024], 16, offA[q], k0 * 2, 0, 0);
+    } else {
+      const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
+#pragma unroll
+      for (int q = 0; q < C::BLA; ++q) {
+        const int blk = tid + q * NT;
+        const int mb = blk % (BM / 8), kb = blk / (BM / 8);
+        const int m = m0 + mb * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kr = k0 + kb * 8 + i;
+          ta[q][i] = (kr < kend && m < G.M) ? *reinterpret_cast<const u32x4_t*>(p + (int64_t)kr * G.lda + m)
+                                            : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    if constexpr (!Tr::B_MN) {
+#pragma unroll
+      for (int q = 0; q < C::DMA_B; ++q) {
+        const int r = (wid * C::DMA_B + q) * 8;
+        auto dst = (void __attribute__((address_space(3)))*)&sB[buf][(wid * C::DMA_B + q) * 1024];
+        if (NB == 2 && r >= BN)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, offB[q], k0 * 2, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, offB[q], k0 * 2, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::BLB; ++q) {
+        const int blk = tid + q * NT;
+        const int nb = blk % (BROWS / 8), kb = blk / (BROWS / 8);
+        const int n = n0 + nb * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kr = k0 + kb * 8 + i;
+          const bf16_t* src;
+          bool ok;
+          if constexpr (!Tr::GROUP_K) {
+            const int krl = kr < G.ksplit ? kr : kr - G.ksplit;
+            src = (kr < G.ksplit ? B0 : B1) + (int64_t)e_loc * G.b_estride + (int64_t)krl * G.ldb + n;
+            ok = n < G.N;
+          } else {
+            ok = kr < kend && n < G.N;
+            // ring mode keeps no expert-sorted copy of X: pull the token rows
+            const int64_t srow = args.gather_rows ? (ok ? args.gather_rows[kr] / args.k_top : 0) : kr;
+            src = B0 + srow * G.ldb + n;
+          }
+          tb[q][i] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+  // Transpose the register-staged (MN) blocks into LDS stage `buf`.
+  auto commit = [&](int buf) {
+    if constexpr (Tr::A_MN) {
+#pragma unroll
+      for (int q = 0; q < C::BLA; ++q) {
+        const int blk = tid + q * NT;
+        transposed_store(ta[q], sA[buf], blk % (BM / 8), blk / (BM / 8));
+      }
+    }
+    if constexpr (Tr::B_MN) {
+#pragma unroll
+      for (int q = 0; q < C::BLB; ++q) {
+        const int blk = tid + q * NT;
+        transposed_store(tb[q], sB[buf], blk % (BROWS / 8), blk / (BROWS / 8));
+      }
+    }
+  };
+
+  f32x16_t acc[NB][FM][FN];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+
+  if (nk > 0) {
+    issue(kbeg, 0);
+    commit(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(kbeg + (kt + 1) * kBK, buf ^ 1);
+    const uint8_t* a_s = sA[buf];
+    const uint8_t* b_s = sB[buf];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int lc = kk * 2 + (lane >> 5);
+      bf16x8_t af[FM], bfr[NB][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&a_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int r = b * BN + wn * TN + j * 32 + (lane & 31);
+          bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(&b_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
+        }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) commit(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // Each wave stages its accumulators in its own 32 KB LDS region, then
+  // every lane handles 8 consecutive columns of one row: 16-byte loads and
+  // stores along rows.
+  float* ep = reinterpret_cast<float*>(arena + wid * 32768);
+  const int wrow0 = wm * TM, wcol0 = wn * TN;
+  if constexpr (NB == 2) {
+    // UP: gate (W1) and up (W3) accumulators of one 32-column fragment
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
+          ep[4096 + rr * 32 + (lane & 31)] = acc[NB - 1][i][j][r];
+        }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 2
+      for (int q = 0; q < TM * 32 / 8 / 64; ++q) {
+        const int seg = q * 64 + lane;
+        const int rr = seg >> 2, c8 = (seg & 3) * 8;
+        const int row = row0 + wrow0 + rr, col = n0 + wcol0 + j * 32 + c8;
+        if (row < row_end && col < G.N) {
+          const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
+          const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[4096 + rr * 32 + c8]);
+          const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
+          float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+          u32x4_t h, a, b;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float h0 = v[2 * t] * sigmoidf_(v[2 * t]) * u[2 * t];
+            const float h1 = v[2 * t + 1] * sigmoidf_(v[2 * t + 1]) * u[2 * t + 1];
+            h[t] = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
+            a[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+            b[t] = (uint32_t)f2bf(u[2 * t]) | ((uint32_t)f2bf(u[2 * t + 1]) << 16);
+          }
+          const int64_t o = (int64_t)row * G.N + col;
+          *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = h;
+          if (args.save) {
+            *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_a + o) = a;
+            *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_b + o) = b;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int jp = 0; jp < FN / 2; ++jp) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
+          }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 2
+      for (int q = 0; q < TM * 64 / 8 / 64; ++q) {
+        const int seg = q * 64 + lane;
+        const int rr = seg >> 3, c8 = (seg & 7) * 8;
+        const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
+        const f32x4_t v0 = pv[0], v1 = pv[1];
+        const int col = n0 + wcol0 + jp * 64 + c8;
+        if constexpr (!Tr::GROUP_K) {
+          const int row = row0 + wrow0 + rr;
+          if (row < row_end && col < G.N) {
+            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            const int64_t o = (int64_t)row * G.N + col;
+            if constexpr (KIND == KIND_DH) {
+              const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_a + o);
+              const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_b + o);
+              u32x4_t da, db;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                float dav[2], dbv[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                  const float a = __uint_as_float(hh ? (av[t] & 0xFFFF0000u) : (av[t] << 16));
+                  const float b = __uint_as_float(hh ? (bv[t] & 0xFFFF0000u) : (bv[t] << 16));
+                  const float sg = sigmoidf_(a);
+                  const float dh = v[2 * t + hh];
+                  dav[hh] = dh * b * sg * (1.0f + a * (1.0f - sg));
+                  dbv[hh] = dh * a * sg;
+                }
+                da[t] = (uint32_t)f2bf(dav[0]) | ((uint32_t)f2bf(dav[1]) << 16);
+                db[t] = (uint32_t)f2bf(dbv[0]) | ((uint32_t)f2bf(dbv[1]) << 16);
+              }
+              bf16_t* dab = (bf16_t*)args.out0 + (int64_t)row * 2 * args.F;
+              *reinterpret_cast<u32x4_t*>(dab + col) = da;
+              *reinterpret_cast<u32x4_t*>(dab + args.F + col) = db;
+            } else {
+              u32x4_t y;
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+              *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = y;
+            }
+          }
+        } else {
+          const int m = m0 + wrow0 + rr;
+          if (m < G.M && col < G.N) {
+            float* outp = (float*)(KIND == KIND_DW13 && z ? args.out1 : args.out0);
+            f32x4_t* dst = reinterpret_cast<f32x4_t*>(outp + (int64_t)e_loc * G.M * G.N + (int64_t)m * G.N + col);
+            dst[0] = v0;
+            dst[1] = v1;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();  // staging regions overlap the next tile's first K stage
+}
+
+template <int KIND, int BM, int BN>
+__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
+  using Tr = Traits<KIND>;
+  using C = TileCfg<KIND, BM, BN>;
+  constexpr int NT = C::NT;
+
+  // One LDS arena: two stages of the A and B tiles during the K loop, then
+  // four per-wave staging regions for the epilogue.
+  constexpr int kArena = 2 * (BM + C::BROWS) * kRowBytes;
+  static_assert(kArena >= 4 * 32768, "epilogue staging needs 32 KB per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
+  __shared__ int32_t s_tp[1025];
+
+  const GemmGeom G = geom_of<KIND>(args.d, args.F);
+  const int tid = threadIdx.x;
   const int E_loc = args.E_loc;
   const int ntn = (G.N + BN - 1) / BN;
 
@@ -196,299 +505,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     m0 = __builtin_amdgcn_readfirstlane(m0);
     n0 = __builtin_amdgcn_readfirstlane(n0);
     z = __builtin_amdgcn_readfirstlane(z);
-    const int kbeg = Tr::GROUP_K ? row0 : 0;
-    const int kend = Tr::GROUP_K ? row_end : G.K;
-    const int nk = (kend - kbeg + kBK - 1) / kBK;
-
-    // ------------------------------------------------------------ direct-to-LDS sources
-    // Buffer resources rebased on this tile: rows past the expert's end (A) or
-    // past N (B) fall outside num_records and read as zero.
-    __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, 0, 0x00020000);
-    __amdgpu_buffer_rsrc_t rsB0 = rsA, rsB1 = rsA;
-    uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
-    if constexpr (!Tr::A_MN) {
-      const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
-      if (args.gather_rows) {
-        // pull dispatch: each row comes straight from its token's row of x
-        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0,
-                                                (int)(args.gather_src_rows * G.lda * 2), 0x00020000);
-#pragma unroll
-        for (int q = 0; q < C::DMA_A; ++q) {
-          const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
-          const int tok = r < rows ? args.gather_rows[row0 + r] / args.k_top : -1;
-          offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_chunk(r, lane & 7) * 16) : 0xFFFFFFF0u;
-        }
-      } else {
-        rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + (int64_t)row0 * G.lda), (short)0,
-                                                (int)((int64_t)rows * G.lda * 2), 0x00020000);
-#pragma unroll
-        for (int q = 0; q < C::DMA_A; ++q) {
-          const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
-          offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
-        }
-      }
-    }
-    if constexpr (!Tr::B_MN) {
-      const int nb_rows = G.N - n0 < BN ? G.N - n0 : BN;  // this tile's rows of each B matrix
-      const bf16_t* b0 = B0 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-      rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)b0, (short)0, (int)((int64_t)nb_rows * G.ldb * 2), 0x00020000);
-      if constexpr (NB == 2) {
-        const bf16_t* b1 = B1 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-        rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)b1, (short)0, (int)((int64_t)nb_rows * G.ldb * 2),
-                                                 0x00020000);
-      }
-#pragma unroll
-      for (int q = 0; q < C::DMA_B; ++q) {
-        const int r = (wid * C::DMA_B + q) * 8 + (lane >> 3);      // LDS row
-        const int rl = (NB == 2 && r >= BN) ? r - BN : r;          // row within its matrix
-        offB[q] = (uint32_t)(rl * G.ldb * 2 + swz_chunk(r, lane & 7) * 16);
-      }
-    }
-
-    u32x4_t ta[C::BLA > 0 ? C::BLA : 1][8], tb[C::BLB > 0 ? C::BLB : 1][8];
-
-    // Issue the loads of K-step k0 into LDS stage `buf` (direct) or registers (MN).
-    auto issue = [&](int k0, int buf) {
-      if constexpr (!Tr::A_MN) {
-#pragma unroll
-        for (int q = 0; q < C::DMA_A; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (void __attribute__((address_space(3)))*)
-                                                   &sA[buf][(wid * C::DMA_A + q) * 1024], 16, offA[q], k0 * 2, 0, 0);
-      } else {
-        const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
-#pragma unroll
-        for (int q = 0; q < C::BLA; ++q) {
-          const int blk = tid + q * NT;
-          const int mb = blk % (BM / 8), kb = blk / (BM / 8);
-          const int m = m0 + mb * 8;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int kr = k0 + kb * 8 + i;
-            ta[q][i] = (kr < kend && m < G.M) ? *reinterpret_cast<const u32x4_t*>(p + (int64_t)kr * G.lda + m)
-                                              : u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-      if constexpr (!Tr::B_MN) {
-#pragma unroll
-        for (int q = 0; q < C::DMA_B; ++q) {
-          const int r = (wid * C::DMA_B + q) * 8;
-          auto dst = (void __attribute__((address_space(3)))*)&sB[buf][(wid * C::DMA_B + q) * 1024];
-          if (NB == 2 && r >= BN)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, offB[q], k0 * 2, 0, 0);
-          else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, offB[q], k0 * 2, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < C::BLB; ++q) {
-          const int blk = tid + q * NT;
-          const int nb = blk % (BROWS / 8), kb = blk / (BROWS / 8);
-          const int n = n0 + nb * 8;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int kr = k0 + kb * 8 + i;
-            const bf16_t* src;
-            bool ok;
-            if constexpr (!Tr::GROUP_K) {
-              const int krl = kr < G.ksplit ? kr : kr - G.ksplit;
-              src = (kr < G.ksplit ? B0 : B1) + (int64_t)e_loc * G.b_estride + (int64_t)krl * G.ldb + n;
-              ok = n < G.N;
-            } else {
-              src = B0 + (int64_t)kr * G.ldb + n;
-              ok = kr < kend && n < G.N;
-            }
-            tb[q][i] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-    };
-    // Transpose the register-staged (MN) blocks into LDS stage `buf`.
-    auto commit = [&](int buf) {
-      if constexpr (Tr::A_MN) {
-#pragma unroll
-        for (int q = 0; q < C::BLA; ++q) {
-          const int blk = tid + q * NT;
-          transposed_store(ta[q], sA[buf], blk % (BM / 8), blk / (BM / 8));
-        }
-      }
-      if constexpr (Tr::B_MN) {
-#pragma unroll
-        for (int q = 0; q < C::BLB; ++q) {
-          const int blk = tid + q * NT;
-          transposed_store(tb[q], sB[buf], blk % (BROWS / 8), blk / (BROWS / 8));
-        }
-      }
-    };
-
-    f32x16_t acc[NB][FM][FN];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
-
-    if (nk > 0) {
-      issue(kbeg, 0);
-      commit(0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) issue(kbeg + (kt + 1) * kBK, buf ^ 1);
-      const uint8_t* a_s = sA[buf];
-      const uint8_t* b_s = sB[buf];
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int lc = kk * 2 + (lane >> 5);
-        bf16x8_t af[FM], bfr[NB][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8_t*>(&a_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int r = b * BN + wn * TN + j * 32 + (lane & 31);
-            bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(&b_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
-          }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) commit(buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-
-    // ---------------------------------------------------------------- epilogue
-    // Each wave stages its accumulators in its own 32 KB LDS region, then
-    // every lane handles 8 consecutive columns of one row: 16-byte loads and
-    // stores along rows.
-    float* ep = reinterpret_cast<float*>(arena + wid * 32768);
-    const int wrow0 = wm * TM, wcol0 = wn * TN;
-    if constexpr (NB == 2) {
-      // UP: gate (W1) and up (W3) accumulators of one 32-column fragment
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
-            ep[4096 + rr * 32 + (lane & 31)] = acc[NB - 1][i][j][r];
-          }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll 2
-        for (int q = 0; q < TM * 32 / 8 / 64; ++q) {
-          const int seg = q * 64 + lane;
-          const int rr = seg >> 2, c8 = (seg & 3) * 8;
-          const int row = row0 + wrow0 + rr, col = n0 + wcol0 + j * 32 + c8;
-          if (row < row_end && col < G.N) {
-            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
-            const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[4096 + rr * 32 + c8]);
-            const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
-            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-            u32x4_t h, a, b;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float h0 = v[2 * t] * sigmoidf_(v[2 * t]) * u[2 * t];
-              const float h1 = v[2 * t + 1] * sigmoidf_(v[2 * t + 1]) * u[2 * t + 1];
-              h[t] = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
-              a[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
-              b[t] = (uint32_t)f2bf(u[2 * t]) | ((uint32_t)f2bf(u[2 * t + 1]) << 16);
-            }
-            const int64_t o = (int64_t)row * G.N + col;
-            *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = h;
-            if (args.save) {
-              *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_a + o) = a;
-              *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_b + o) = b;
-            }
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    } else {
-#pragma unroll
-      for (int jp = 0; jp < FN / 2; ++jp) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
-            }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll 2
-        for (int q = 0; q < TM * 64 / 8 / 64; ++q) {
-          const int seg = q * 64 + lane;
-          const int rr = seg >> 3, c8 = (seg & 7) * 8;
-          const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
-          const f32x4_t v0 = pv[0], v1 = pv[1];
-          const int col = n0 + wcol0 + jp * 64 + c8;
-          if constexpr (!Tr::GROUP_K) {
-            const int row = row0 + wrow0 + rr;
-            if (row < row_end && col < G.N) {
-              float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-              const int64_t o = (int64_t)row * G.N + col;
-              if constexpr (KIND == KIND_DH) {
-                const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_a + o);
-                const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_b + o);
-                u32x4_t da, db;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  float dav[2], dbv[2];
-#pragma unroll
-                  for (int hh = 0; hh < 2; ++hh) {
-                    const float a = __uint_as_float(hh ? (av[t] & 0xFFFF0000u) : (av[t] << 16));
-                    const float b = __uint_as_float(hh ? (bv[t] & 0xFFFF0000u) : (bv[t] << 16));
-                    const float sg = sigmoidf_(a);
-                    const float dh = v[2 * t + hh];
-                    dav[hh] = dh * b * sg * (1.0f + a * (1.0f - sg));
-                    dbv[hh] = dh * a * sg;
-                  }
-                  da[t] = (uint32_t)f2bf(dav[0]) | ((uint32_t)f2bf(dav[1]) << 16);
-                  db[t] = (uint32_t)f2bf(dbv[0]) | ((uint32_t)f2bf(dbv[1]) << 16);
-                }
-                bf16_t* dab = (bf16_t*)args.out0 + (int64_t)row * 2 * args.F;
-                *reinterpret_cast<u32x4_t*>(dab + col) = da;
-                *reinterpret_cast<u32x4_t*>(dab + args.F + col) = db;
-              } else {
-                u32x4_t y;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                  y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
-                *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = y;
-              }
-            }
-          } else {
-            const int m = m0 + wrow0 + rr;
-            if (m < G.M && col < G.N) {
-              float* outp = (float*)(KIND == KIND_DW13 && z ? args.out1 : args.out0);
-              f32x4_t* dst = reinterpret_cast<f32x4_t*>(outp + (int64_t)e_loc * G.M * G.N + (int64_t)m * G.N + col);
-              dst[0] = v0;
-              dst[1] = v1;
-            }
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-    __syncthreads();  // staging regions overlap the next tile's first K stage
+    gemm_tile<KIND, BM, BN>(args, arena, e_loc, row0, row_end, m0, n0, z);
   }
 #endif
 }
@@ -525,6 +542,116 @@ hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_DW13: return run_bf16<KIND_DW13, 256, 256>(g, s);
   }
   return hipErrorInvalidValue;
+}
+
+
+// ------------------------------------------------------------------ ring pipeline
+// Tile prefix of the local experts restricted to rows [r0, r1): expert i owns
+// ceil(|[off_i, off_i+1) n [r0, r1)| / BM) row tiles.  256 threads, E_loc <= 1024.
+template <int BM>
+__device__ void range_tile_prefix(const GroupedGemmArgs& g, int r0, int r1, int32_t* s_tp, int32_t* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int c[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * tid + q;
+    c[q] = 0;
+    if (i < g.E_loc) {
+      const int lo = max(g.offsets[g.eb + i], r0), hi = min(g.offsets[g.eb + i + 1], r1);
+      c[q] = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+    }
+    sum += c[q];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) s_wsum[wid] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += s_wsum[w];
+  int excl = base + incl - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * tid + q;
+    if (i < g.E_loc) s_tp[i] = excl;
+    excl += c[q];
+  }
+  if (tid == 255) s_tp[g.E_loc] = base + incl;
+  __syncthreads();
+}
+
+// Expert and row span of tile t of a range prefix (expert-major, m fastest).
+__device__ __forceinline__ void range_tile(const GroupedGemmArgs& g, const int32_t* s_tp, int ntn, int BM, int r0,
+                                           int r1, int t, int& e_loc, int& row0, int& row_end, int& n0, int BN) {
+  int lo = 0, hi = g.E_loc - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_tp[mid] * ntn <= t) lo = mid; else hi = mid - 1;
+  }
+  e_loc = lo;
+  const int mt_e = s_tp[e_loc + 1] - s_tp[e_loc];
+  const int local = t - s_tp[e_loc] * ntn;
+  n0 = (local / mt_e) * BN;
+  row0 = max(g.offsets[g.eb + e_loc], r0) + (local % mt_e) * BM;
+  row_end = min(g.offsets[g.eb + e_loc + 1], r1);
+}
+
+[[maybe_unused]] constexpr int kCopyRows = 16;  // rows per mover task
+
+__global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kArena = 2 * (256 + 256) * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
+  __shared__ int32_t s_up[1025], s_dn[1025], s_wsum[4];
+  const int tid = threadIdx.x;
+  const GroupedGemmArgs& gu = a.up;
+  const int P = gu.offsets[gu.eb + gu.E_loc];  // local rows
+  const int u0 = min(a.up0, P), u1 = min(a.up1, P);
+  const int d0 = min(a.dn0, P), d1 = min(a.dn1, P);
+  const int c0 = min(a.cp0, P), c1 = min(a.cp1, P);
+  range_tile_prefix<256>(gu, u0, u1, s_up, s_wsum);
+  range_tile_prefix<256>(a.down, d0, d1, s_dn, s_wsum);
+  const int ntn_up = (gu.F + 127) / 128, ntn_dn = (gu.d + 255) / 256;
+  const int n_cp = (c1 - c0 + kCopyRows - 1) / kCopyRows;
+  const int n_up = s_up[gu.E_loc] * ntn_up;
+  const int n_dn = s_dn[gu.E_loc] * ntn_dn;
+  const int total = n_cp + n_up + n_dn;
+  const int G_ = gridDim.x;
+  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int t = vb; t < total; t += G_) {
+    if (t < n_cp) {
+      // mover task: rows [c0 + t*16, ...) of the next minibatch into its slot
+      const int d = gu.d, nv = d / 8;
+      const int rb = c0 + t * kCopyRows, re = min(rb + kCopyRows, c1);
+      for (int v = tid; v < (re - rb) * nv; v += 256) {
+        const int r = rb + v / nv, c = v % nv;
+        const int tok = a.pair_of_row[r] / a.k;
+        const u32x4_t val = reinterpret_cast<const u32x4_t*>((const bf16_t*)a.x + (int64_t)tok * d)[c];
+        reinterpret_cast<u32x4_t*>((bf16_t*)a.ring_dst + (int64_t)(r - c0) * d)[c] = val;
+      }
+    } else if (t < n_cp + n_up) {
+      int e_loc, row0, row_end, n0;
+      range_tile(gu, s_up, ntn_up, 256, u0, u1, t - n_cp, e_loc, row0, row_end, n0, 128);
+      gemm_tile<KIND_UP, 256, 128>(gu, arena, __builtin_amdgcn_readfirstlane(e_loc),
+                                   __builtin_amdgcn_readfirstlane(row0), __builtin_amdgcn_readfirstlane(row_end), 0,
+                                   __builtin_amdgcn_readfirstlane(n0), 0);
+    } else {
+      int e_loc, row0, row_end, n0;
+      range_tile(a.down, s_dn, ntn_dn, 256, d0, d1, t - n_cp - n_up, e_loc, row0, row_end, n0, 256);
+      gemm_tile<KIND_DOWN, 256, 256>(a.down, arena, __builtin_amdgcn_readfirstlane(e_loc),
+                                     __builtin_amdgcn_readfirstlane(row0), __builtin_amdgcn_readfirstlane(row_end), 0,
+                                     __builtin_amdgcn_readfirstlane(n0), 0);
+    }
+  }
+#endif
+}
+
+hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(minibatch_step_kernel, dim3(256), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace mok

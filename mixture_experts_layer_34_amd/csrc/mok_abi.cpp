@@ -15,6 +15,8 @@
 
 using namespace mok;
 
+typedef uint16_t bf16_t_;  // bf16 storage (host side)
+
 namespace {
 
 enum { KIND_UP = 0, KIND_DOWN = 1, KIND_DH = 2, KIND_DX = 3, KIND_DW2 = 4, KIND_DW13 = 5 };
@@ -39,7 +41,22 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
     return MOK_ERR_INVALID_ARG;
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
   if (c.flags & ~MOK_FLAG_SAVE_FOR_BACKWARD) return MOK_ERR_INVALID_ARG;
+  if (c.ring_bytes > 0 && c.minibatch_rows == 0) return MOK_ERR_INVALID_ARG;  // a ring needs a minibatch size
+  if (c.minibatch_rows > 0) {
+    if (c.precision != MOK_PREC_BF16) return MOK_ERR_UNSUPPORTED;
+    // two slots at least: minibatch m+1 is copied while m is read
+    if (c.ring_bytes < 2 * (int64_t)c.minibatch_rows * c.d * 2) return MOK_ERR_WORKSPACE;
+  }
   return MOK_OK;
+}
+
+// Ring slots of R rows each (minibatch mode), never more than minibatches.
+int ring_slots(const mok_moe_config& c, int32_t k) {
+  const int64_t R = c.minibatch_rows, Tk = (int64_t)c.T * k;
+  const int64_t M = (Tk + R - 1) / R;
+  int64_t S = c.ring_bytes / ((int64_t)c.d * 2) / R;
+  if (S > M) S = M;
+  return (int)(S < 1 ? 1 : S);
 }
 
 // Public arrays (mok_saved_layout) plus two internal ones: the per-expert
@@ -75,7 +92,7 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
   const bool mx = c.precision == MOK_PREC_MXFP8;
   w->nchunks = (int)nchunks;
-  w->xp_rows = (int64_t)Tk;
+  w->xp_rows = c.minibatch_rows > 0 ? (int64_t)ring_slots(c, k) * c.minibatch_rows : (int64_t)Tk;
   size_t o = 0;
   w->status = o;        o = align256(o + 256);
   w->chunk_counts = o;  o = align256(o + (size_t)nchunks * c.E * 4);
@@ -151,7 +168,7 @@ const char* mok_status_string(mok_status s) {
     case MOK_OK: return "MOK_OK";
     case MOK_ERR_INVALID_ARG: return "MOK_ERR_INVALID_ARG: invalid argument (null pointer, shape or alignment)";
     case MOK_ERR_UNSUPPORTED: return "MOK_ERR_UNSUPPORTED: request not implemented by this library";
-    case MOK_ERR_WORKSPACE: return "MOK_ERR_WORKSPACE: ring buffer smaller than one minibatch";
+    case MOK_ERR_WORKSPACE: return "MOK_ERR_WORKSPACE: ring buffer smaller than two minibatch slots";
     case MOK_ERR_HIP: return "MOK_ERR_HIP: a HIP runtime call failed";
     case MOK_ERR_DEVICE: return "MOK_ERR_DEVICE: a device-side check failed";
   }
@@ -200,7 +217,6 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   const bool mx = c.precision == MOK_PREC_MXFP8;
   if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
   if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
-  if (c.minibatch_rows > 0 || c.ring_bytes > 0) return MOK_ERR_UNSUPPORTED;
   if (mx && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
@@ -258,6 +274,52 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g2.out0 = at<void>(saved, sl.Y);
     g2.out_scale = nullptr;
     MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
+  } else if (c.minibatch_rows > 0) {
+    // Ring-buffer minibatch pipeline ([kucoin §02]: tunable minibatches drawn
+    // from a fixed ring token buffer; [fluid «Comment MoK…»]): launch m copies
+    // minibatch m+1 into its slot, runs UP on minibatch m and DOWN on m-1.
+    const int R = c.minibatch_rows, S = ring_slots(c, k);
+    const int M = (int)(((int64_t)T * k + R - 1) / R);
+    bf16_t_* ring = at<bf16_t_>(workspace, wl.xp);
+    MinibatchStepArgs ms{};
+    ms.up = g;
+    ms.up.A = ring;
+    ms.up.B0 = W1;
+    ms.up.B1 = W3;
+    ms.up.out0 = at<void>(saved, sl.H);
+    ms.up.save_a = at<void>(saved, sl.A);
+    ms.up.save_b = at<void>(saved, sl.B);
+    ms.up.save = (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ? 1 : 0;
+    ms.down = g;
+    ms.down.A = at<void>(saved, sl.H);
+    ms.down.B0 = W2;
+    ms.down.out0 = at<void>(saved, sl.Y);
+    ms.x = x;
+    ms.pair_of_row = s_por;
+    ms.k = k;
+    mark_empty_stage(c, s, MOK_STAGE_DISPATCH);
+    {
+      StageMark mark(c, s, MOK_STAGE_GEMM_UP);  // the whole pipeline
+      for (int m = -1; m <= M; ++m) {
+        ms.up0 = ms.up1 = ms.dn0 = ms.dn1 = ms.cp0 = ms.cp1 = 0;
+        if (m >= 0 && m < M) {
+          ms.up0 = m * R;
+          ms.up1 = m * R + R;
+          ms.up.a_row_shift = (int64_t)m * R - (int64_t)(m % S) * R;
+        }
+        if (m >= 1) {
+          ms.dn0 = (m - 1) * R;
+          ms.dn1 = m * R;
+        }
+        if (m + 1 < M) {
+          ms.cp0 = (m + 1) * R;
+          ms.cp1 = (m + 1) * R + R;
+          ms.ring_dst = ring + (int64_t)((m + 1) % S) * R * d;
+        }
+        MOK_HIP(launch_minibatch_step(ms, s));
+      }
+    }
+    mark_empty_stage(c, s, MOK_STAGE_GEMM_DOWN);
   } else {
     void* xp = at<void>(workspace, wl.xp);
     if (fused_pull(c)) {
@@ -305,7 +367,6 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
     if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
   if (c.precision == MOK_PREC_MXFP8) return MOK_ERR_UNSUPPORTED;
   if (!(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
-  if (c.minibatch_rows > 0 || c.ring_bytes > 0) return MOK_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
@@ -362,12 +423,22 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   gw.out0 = dW2;
   gw.queue = queue;
   MOK_STAGE(MOK_STAGE_GEMM_DW2, run_gemm(c.precision, KIND_DW2, gw, s));
-  // X rows again, expert-sorted (the transposed operand of dW1/dW3 wants
-  // them contiguous: a gather inside its loads would chain two loads)
-  MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
   GroupedGemmArgs g13 = g;
   g13.A = dab;
-  g13.B0 = xp;
+  if (c.minibatch_rows > 0) {
+    // ring mode holds no expert-sorted copy of X: pull the token rows inside
+    // the loads of the transposed operand
+    mark_empty_stage(c, s, MOK_STAGE_REGATHER);
+    g13.B0 = x;
+    g13.gather_rows = at<int32_t>(saved, sl.pair_of_row);
+    g13.k_top = k;
+    g13.gather_src_rows = T;
+  } else {
+    // X rows again, expert-sorted (the transposed operand of dW1/dW3 wants
+    // them contiguous: a gather inside its loads chains two loads)
+    MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+    g13.B0 = xp;
+  }
   g13.out0 = dW1;
   g13.out1 = dW3;
   g13.queue = queue + 1;

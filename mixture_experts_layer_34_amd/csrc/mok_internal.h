@@ -88,17 +88,37 @@ struct GroupedGemmArgs {
   uint8_t* out_scale;     // MXFP8 H scales
   int save;               // write A and B (forward)
   // Pull dispatch fused into the GEMM loads: when non-null, row r of the
-  // expert-sorted A operand of UP is row gather_rows[r] / k_top of the token
-  // matrix (x, with gather_src_rows rows) instead of row r.
+  // expert-sorted operand (A of UP; B of DW13 in ring mode) is row
+  // gather_rows[r] / k_top of the token matrix (x, with gather_src_rows rows).
   const int32_t* gather_rows;
   int k_top;
   int64_t gather_src_rows;
+  // Ring mode: the A operand of UP holds row r at A row r - a_row_shift.
+  int64_t a_row_shift;
 };
 
 // Expert-grouped GEMM of one kind (GemmKind in gemm_common.h) per precision:
 // 0 UP (H = silu(X W1^T) * (X W3^T)), 1 DOWN (Y = H W2^T), 2 DH (dA, dB from
 // dY W2), 3 DX (dA W1 + dB W3), 4 DW2 (dY^T H), 5 DW13 (dA^T X, dB^T X).
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
+
+// One step of the ring-buffer minibatch pipeline (bf16): in a single launch,
+// mover tiles copy the rows of minibatch m+1 into their ring slot, compute
+// tiles run UP on minibatch m (rows read from its ring slot) and DOWN on
+// minibatch m-1.  Row ranges are half-open in the expert-sorted row space and
+// are clipped on the device to the local row count.
+struct MinibatchStepArgs {
+  GroupedGemmArgs up;     // A = ring (a_row_shift maps row r to its slot row)
+  GroupedGemmArgs down;   // A = H
+  int up0, up1;           // rows of minibatch m   (up0 == up1: none)
+  int dn0, dn1;           // rows of minibatch m-1 (dn0 == dn1: none)
+  int cp0, cp1;           // rows of minibatch m+1 to copy (cp0 == cp1: none)
+  const void* x;          // [T, d] bf16 token rows
+  const int32_t* pair_of_row;
+  int k;
+  void* ring_dst;         // ring slot receiving row cp0
+};
+hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s);
 hipError_t gemm_f32(int kind, const GroupedGemmArgs& g, hipStream_t s);
 hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
 

@@ -47,6 +47,7 @@ class LazyExperts:
 
 
 def shape_of(w: W.Workload, T: int, backward: bool) -> MoeShape:
+    """Whole-layer shape of a workload (no ring; tests set ring fields themselves)."""
     return MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision, expert_begin=w.expert_begin,
                     expert_end=w.e_end, save_for_backward=backward)
 

@@ -108,3 +108,22 @@ def test_quantize_rejects_bad_shapes():
     assert L.mok_quantize_mxfp8(0x1000, -1, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_quantize_mxfp8(None, 4, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_quantize_mxfp8(0x1000, 0, 64, 0x2000, 0x3000, None) == mok.MOK_OK
+
+
+def test_ring_mode_validation():
+    # a ring needs a minibatch size
+    with pytest.raises(mok.MokError) as ei:
+        mok.mok_moe_workspace_query(_cfg(ring_bytes=1 << 20), 2)
+    assert ei.value.status == mok.MOK_ERR_INVALID_ARG
+    # ring mode is bf16 only
+    with pytest.raises(mok.MokError) as ei:
+        mok.mok_moe_workspace_query(_cfg(precision="f32", d=128, minibatch_rows=64, ring_bytes=1 << 20), 2)
+    assert ei.value.status == mok.MOK_ERR_UNSUPPORTED
+    # fewer than two slots
+    with pytest.raises(mok.MokError) as ei:
+        mok.mok_moe_workspace_query(_cfg(minibatch_rows=64, ring_bytes=64 * 128 * 2), 2)
+    assert ei.value.status == mok.MOK_ERR_WORKSPACE
+    # the dispatch buffer shrinks to the ring
+    full_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096), 2)
+    ring_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096, minibatch_rows=256, ring_bytes=2 * 256 * 128 * 2), 2)
+    assert full_ws - ring_ws >= (4096 * 2 - 512) * 128 * 2
