@@ -50,8 +50,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, OUT)
+    # profiling driver (no PyTorch): runs the layer through the C ABI
+    drv = os.path.join(PKG, "mok_profile")
+    cmd = [HIPCC, *FLAGS, "-o", drv + ".tmp", os.path.join(CSRC, "mok_profile_main.cpp"), "-L" + PKG, "-lmok",
+           "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("profiling driver build failed:\n" + r.stderr)
+    os.replace(drv + ".tmp", drv)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", drv)
     return OUT
 
 

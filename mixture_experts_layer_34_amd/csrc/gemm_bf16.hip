@@ -113,7 +113,8 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
   uint8_t (*sA)[BM * kRowBytes] = reinterpret_cast<uint8_t (*)[BM * kRowBytes]>(arena);
   uint8_t (*sB)[BROWS * kRowBytes] = reinterpret_cast<uint8_t (*)[BROWS * kRowBytes]>(arena + 2 * BM * kRowBytes);
   const GemmGeom G = geom_of<KIND>(args.d, args.F);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
   const int wm = wid / C::WN, wn = wid % C::WN;
   const bf16_t* __restrict__ Abase = (const bf16_t*)args.A;
   const bf16_t* __restrict__ B0 = (const bf16_t*)args.B0;
@@ -125,15 +126,14 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
   // ------------------------------------------------------------ direct-to-LDS sources
   // Buffer resources rebased on this tile: rows past the expert's end (A) or
   // past N (B) fall outside num_records and read as zero.
-  __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, 0, 0x00020000);
-  __amdgpu_buffer_rsrc_t rsB0 = rsA, rsB1 = rsA;
+  i32x4_t rsA = make_rsrc(Abase, 0u);
+  i32x4_t rsB0 = rsA, rsB1 = rsA;
   uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
   if constexpr (!Tr::A_MN) {
     const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
     if (args.gather_rows) {
       // pull dispatch: each row comes straight from its token's row of x
-      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0,
-                                              (int)(args.gather_src_rows * G.lda * 2), 0x00020000);
+      rsA = make_rsrc(Abase, (uint32_t)(args.gather_src_rows * G.lda * 2));
 #pragma unroll
       for (int q = 0; q < C::DMA_A; ++q) {
         const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
@@ -141,8 +141,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
         offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_chunk(r, lane & 7) * 16) : 0xFFFFFFF0u;
       }
     } else {
-      rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(Abase + ((int64_t)row0 - args.a_row_shift) * G.lda),
-                                              (short)0, (int)((int64_t)rows * G.lda * 2), 0x00020000);
+      rsA = make_rsrc(Abase + ((int64_t)row0 - args.a_row_shift) * G.lda, (uint32_t)((int64_t)rows * G.lda * 2));
 #pragma unroll
       for (int q = 0; q < C::DMA_A; ++q) {
         const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
@@ -153,11 +152,10 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
   if constexpr (!Tr::B_MN) {
     const int nb_rows = G.N - n0 < BN ? G.N - n0 : BN;  // this tile's rows of each B matrix
     const bf16_t* b0 = B0 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-    rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)b0, (short)0, (int)((int64_t)nb_rows * G.ldb * 2), 0x00020000);
+    rsB0 = make_rsrc(b0, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
     if constexpr (NB == 2) {
       const bf16_t* b1 = B1 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-      rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)b1, (short)0, (int)((int64_t)nb_rows * G.ldb * 2),
-                                               0x00020000);
+      rsB1 = make_rsrc(b1, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
     }
 #pragma unroll
     for (int q = 0; q < C::DMA_B; ++q) {
@@ -174,8 +172,7 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
     if constexpr (!Tr::A_MN) {
 #pragma unroll
       for (int q = 0; q < C::DMA_A; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (void __attribute__((address_space(3)))*)
-                                                 &sA[buf][(wid * C::DMA_A + q) * 1024], 16, offA[q], k0 * 2, 0, 0);
+        dma_b128(rsA, lds_addr(&sA[buf][(wid * C::DMA_A + q) * 1024]), offA[q], k0 * 2);
     } else {
       const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
 #pragma unroll
@@ -195,11 +192,8 @@ __device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* 
 #pragma unroll
       for (int q = 0; q < C::DMA_B; ++q) {
         const int r = (wid * C::DMA_B + q) * 8;
-        auto dst = (void __attribute__((address_space(3)))*)&sB[buf][(wid * C::DMA_B + q) * 1024];
-        if (NB == 2 && r >= BN)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, offB[q], k0 * 2, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, offB[q], k0 * 2, 0, 0);
+        dma_b128((NB == 2 && r >= BN) ? rsB1 : rsB0, lds_addr(&sB[buf][(wid * C::DMA_B + q) * 1024]), offB[q],
+                 k0 * 2);
       }
     } else {
 #pragma unroll
@@ -443,15 +437,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     __syncthreads();
     total = s_tp[E_loc] * ntn;
   } else {
+    // this XCD's share: its experts' tiles, NZ * ntm * ntn per expert
     ntm_k = (G.M + BM - 1) / BM;
-    total = E_loc * NZ * ntm_k * ntn;
+    const int x = blockIdx.x % 8;
+    total = (args.expert_order[x + 1] - args.expert_order[x]) * NZ * ntm_k * ntn;
   }
   // Row-grouped kinds: equal-sized tiles in a static round-robin.  XCD-aware
   // order: workgroup b (on XCD b % 8) takes tiles from the contiguous run
   // [x * G/8, (x+1) * G/8) of each round of G tiles.  Weight-gradient kinds:
-  // the work of a tile grows with its expert's rows, so tiles are pulled from
-  // a device-side counter, heaviest expert first (each tile is still computed
-  // whole by one workgroup: the results do not depend on the assignment).
+  // the work of a tile grows with its expert's rows, so the experts are dealt
+  // to the XCDs longest-first (by the counting sort) and the workgroups of
+  // XCD x pull that share's tiles from counter x, heaviest expert first; an
+  // expert's tiles then share one L2.  Each tile is still computed whole by one
+  // workgroup, so the results do not depend on the assignment.
   const int G_ = gridDim.x;
   const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
   __shared__ int s_next;
@@ -459,7 +457,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     if constexpr (!Tr::GROUP_K) {
       return cur < 0 ? vb : cur + G_;
     } else {
-      if (tid == 0) s_next = atomicAdd(args.queue, 1);
+      if (tid == 0) s_next = atomicAdd(args.queue + blockIdx.x % 8, 1);
       __syncthreads();
       const int t = s_next;
       __syncthreads();
@@ -485,7 +483,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
       row_end = args.offsets[e + 1];
     } else {
       const int per_z = ntm_k * ntn;
-      e_loc = args.expert_order[tile / (NZ * per_z)];
+      e_loc = args.expert_order[16 + args.expert_order[blockIdx.x % 8] + tile / (NZ * per_z)];
       const int rem = tile % (NZ * per_z);
       z = rem / per_z;
       int mt, nt;
@@ -517,9 +515,9 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   int blocks;
   dim3 grid;
   if constexpr (Traits<KIND>::GROUP_K) {
-    // persistent workers over the tile counter (zeroed earlier on the stream)
-    const int64_t tiles = (int64_t)g.E_loc * (KIND == KIND_DW13 ? 2 : 1) * ((G.M + BM - 1) / BM) * ntn;
-    blocks = (int)(tiles < 256 ? tiles : 256);
+    // persistent workers over the 8 per-XCD tile counters (zeroed earlier on
+    // the stream); a multiple of 8 workgroups so that every counter is served
+    blocks = 256;
     grid = dim3(blocks);
   } else {
     // persistent: one workgroup per CU, bounded by the worst-case tile count

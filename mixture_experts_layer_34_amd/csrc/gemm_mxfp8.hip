@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
   const int N = KIND == KIND_UP ? args.F : args.d;
   const int KS = K / 32;                      // scale bytes per row
   const int64_t b_estride = (int64_t)args.F * args.d;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
   const int wm = wid / 2, wn = wid % 2;
   const uint8_t* __restrict__ A = (const uint8_t*)args.A;
   const uint8_t* __restrict__ B0 = (const uint8_t*)args.B0;
@@ -92,13 +93,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
 
     // direct-to-LDS sources (rows past the tile's data read as zero)
     const int rows = row_end - row0 < BM ? row_end - row0 : BM;
-    const __amdgpu_buffer_rsrc_t rsA =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)row0 * K), (short)0, rows * K, 0x00020000);
+    const i32x4_t rsA = make_rsrc(A + (int64_t)row0 * K, (uint32_t)(rows * K));
     const int nb_rows = N - n0 < BN ? N - n0 : BN;
     const uint8_t* b0 = B0 + (int64_t)e_loc * b_estride + (int64_t)n0 * K;
-    const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc((void*)b0, (short)0, nb_rows * K, 0x00020000);
+    const i32x4_t rsB0 = make_rsrc(b0, (uint32_t)(nb_rows * K));
     const uint8_t* b1 = (NB == 2 ? B1 : B0) + (int64_t)e_loc * b_estride + (int64_t)n0 * K;
-    const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)b1, (short)0, nb_rows * K, 0x00020000);
+    const i32x4_t rsB1 = make_rsrc(b1, (uint32_t)(nb_rows * K));
     uint32_t offA[DMA_A], offB[DMA_B];
 #pragma unroll
     for (int q = 0; q < DMA_A; ++q) {
@@ -141,15 +141,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
     auto issue = [&](int k0, int buf) {
 #pragma unroll
       for (int q = 0; q < DMA_A; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (void __attribute__((address_space(3)))*)
-                                                 &sA[buf][(wid * DMA_A + q) * 1024], 16, offA[q], k0, 0, 0);
+        dma_b128(rsA, lds_addr(&sA[buf][(wid * DMA_A + q) * 1024]), offA[q], k0);
 #pragma unroll
       for (int q = 0; q < DMA_B; ++q) {
-        auto dst = (void __attribute__((address_space(3)))*)&sB[buf][(wid * DMA_B + q) * 1024];
-        if (NB == 2 && (wid * DMA_B + q) * 8 >= BN)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB1, dst, 16, offB[q], k0, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB0, dst, 16, offB[q], k0, 0, 0);
+        dma_b128((NB == 2 && (wid * DMA_B + q) * 8 >= BN) ? rsB1 : rsB0,
+                 lds_addr(&sB[buf][(wid * DMA_B + q) * 1024]), offB[q], k0);
       }
     };
 

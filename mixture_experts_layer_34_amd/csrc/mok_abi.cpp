@@ -76,7 +76,7 @@ void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_
   s->topk_gate = o;    o = align256(o + Tk * 4);
   s->offsets = o;      o = align256(o + ((size_t)c.E + 1) * 4);
   *tile_prefix_off = o; o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
-  *expert_order_off = o; o = align256(o + E_loc * 4);
+  *expert_order_off = o; o = align256(o + (E_loc + 16) * 4);
   s->row_of_pair = o;  o = align256(o + Tk * 4);
   s->pair_of_row = o;  o = align256(o + Tk * 4);
   s->A = o;            o = align256(o + Tk * c.ffn * A);
@@ -391,7 +391,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 
   // reverse-combine with the router backward
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
-                               bf16, dgate, drouter_logits, dy, queue, 2, s));
+                               bf16, dgate, drouter_logits, dy, queue, 16, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;
@@ -441,7 +441,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   }
   g13.out0 = dW1;
   g13.out1 = dW3;
-  g13.queue = queue + 1;
+  g13.queue = queue + 8;
   MOK_STAGE(MOK_STAGE_GEMM_DW13, run_gemm(c.precision, KIND_DW13, g13, s));
   return MOK_OK;
 }

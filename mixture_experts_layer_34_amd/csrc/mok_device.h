@@ -75,3 +75,38 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   int s = ef - 127 - 8;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
+
+// ------------------------------------------------------------ HBM -> LDS DMA
+// Buffer resource (V#) of `bytes` bytes at p: stride 0, raw addressing;
+// offsets at or past `bytes` read as zero.  All fields must be wave-uniform.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return i32x4_t{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)bytes, 0x00020000};
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave copies 64 x 16 bytes from the buffer (lane offset voff + soff) to
+// LDS [lds, lds + 1024), lane i's bytes landing at lds + 16 i.  Written as
+// inline assembly on purpose: the compiler cannot tell these LDS writes from
+// the fragment reads of another pipeline stage, and would otherwise wait for
+// every outstanding copy before each LDS read.  The caller owns the ordering:
+// s_waitcnt vmcnt(n) (copies complete in issue order) and then a workgroup
+// barrier before any wave reads what was copied.  `lds` must be wave-uniform;
+// M0 is restored afterwards.
+__device__ __forceinline__ void dma_b128(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}

@@ -73,8 +73,8 @@ struct GroupedGemmArgs {
   const void* B1;         // second weights (W3) where used
   const int32_t* offsets;
   const int32_t* tile_prefix;
-  const int32_t* expert_order;  // local experts by descending row count (ties: lower index)
-  int32_t* queue;               // tile counter of the weight-gradient kinds (zeroed on device)
+  const int32_t* expert_order;  // [0..8] XCD list starts, [16..) local experts grouped by XCD
+  int32_t* queue;               // 8 per-XCD tile counters of a weight-gradient kind (zeroed on device)
   int eb, E_loc;
   int d, F;
   int64_t P_max;
