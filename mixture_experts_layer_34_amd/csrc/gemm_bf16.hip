@@ -15,38 +15,537 @@
 //
 // Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile (per B
 // matrix; UP computes the W1 and W3 tiles of the same columns), each wave a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles, over K in steps of 64 staged
-// through double-buffered LDS in a K-contiguous [row][k] layout: 128-byte rows
-// of eight 16-byte chunks, XOR-swizzled so that the 16-byte fragment reads of
-// 16 consecutive rows hit distinct banks.  Operands stored K-contiguous go
-// from HBM straight to LDS (buffer_load_dwordx4 ... lds, 1 KB per wave
-// instruction, no VGPRs), through buffer resources rebased on each tile so
-// that rows past the expert's end read as zero.  Operands stored M- or
-// N-contiguous (the backward products) are loaded as 8 x 8 blocks and
-// transposed in registers (v_perm_b32) before 16-byte LDS stores.
+// (BM/2) x (BN/2) block of 32x32 MFMA tiles.  K advances in stages of 32
+// through a ring of NS LDS stage buffers (five, 160 KB, in the grouped GEMMs),
+// so NS - 1 stages are in flight while one is multiplied.  Every operand goes from HBM straight to LDS
+// (buffer_load_dwordx4 ... lds, 1 KB per wave instruction, no VGPRs),
+// through buffer resources rebased on the tile so that rows past the data
+// read as zero, in the layout it has in memory:
+//   K-contiguous operands ([row][k]): 64-byte LDS rows of four 16-byte
+//     chunks, XOR-swizzled; fragments are 16-byte reads (ds_read_b128).
+//   M- or N-contiguous operands ([k][row], the backward products): LDS rows
+//     of one k, 64-byte chunks XOR-swizzled by k; fragments are transposing
+//     reads (ds_read_b64_tr_b16), which hand each lane four consecutive k of
+//     one row, so no transpose pass through registers is needed.
+// The swizzles make fragment reads bank-conflict free.  Fragments of the
+// next 16-K slice are read while the MFMAs of the current one run; the one
+// workgroup barrier per stage sits between the two MFMA halves of a stage.
 //
 // Scheduling: row-grouped kinds run a persistent loop over the tiles of all
 // local experts in (expert, n-tile, m-tile) order, with the tile prefix of
 // each expert computed on the device by the counting sort, so the host never
 // needs the data-dependent row count.  Workgroup b runs on XCD b mod 8; the
 // loop hands each XCD a contiguous run of tiles so that m-tiles sharing a
-// weight tile meet in one L2.  Every output element is produced by one
-// workgroup with a fixed K order: results are run-to-run identical (no
-// split-K, no atomics).
+// weight tile meet in one L2.  The first stages of the next tile are loaded
+// while the current tile's epilogue runs.  Every output element is produced
+// by one workgroup with a fixed K order: results are run-to-run identical
+// (no split-K, no float atomics).
 #include "mok_device.h"
 #include "mok_internal.h"
 #include "gemm_common.h"
 
 namespace mok {
 
-constexpr int kBK = 64;           // K step; one LDS row holds 64 bf16 = 128 bytes = 8 chunks
-constexpr int kRowBytes = kBK * 2;
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.  This XOR swizzle
-// keeps fragment reads (32 consecutive rows, one chunk) and the transposed
-// block stores below free of bank conflicts for 64 banks with 16-lane phases
-// and for 32 banks with 8-lane phases alike.
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// K-contiguous stage layout: physical 16-byte chunk of logical chunk c in
+// row r, for rows of BK = 32 (64 bytes, 4 chunks) or 64 (128 bytes, 8
+// chunks).  Sixteen consecutive rows read at one logical chunk hit 16
+// distinct 16-byte bank groups (64 banks), and any 8 consecutive rows hit 8
+// distinct ones (32 banks).
+template <int BK>
+__device__ __forceinline__ int swz_k(int r, int c) {
+  if constexpr (BK == 32) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
+  else return c ^ ((r ^ (r >> 3)) & 7);
+}
+// M/N-contiguous stage layout: physical 64-byte chunk of logical chunk c in
+// the row of k = r.  A transposing read touches rows k..k+3 at one chunk:
+// they land in four distinct 64-byte bank groups.
+__device__ __forceinline__ int swz_mn(int r, int c) { return c ^ (r & 3); }
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding and its LDS reads have returned, then meet the workgroup.  The
+// LDS wait is also issued through the builtin so that the compiler's own
+// counter model knows the reads have returned (it does not look inside asm).
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt not waited on
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Two consecutive int32 at a wave-uniform address through the scalar cache
+// (p[1] is read only when valid1): no vector-memory counter is touched, so
+// the copies in flight are not waited for.
+__device__ __forceinline__ void sload_pair(const int32_t* p, bool valid1, int32_t& v0, int32_t& v1) {
+  const int32_t* p1 = valid1 ? p + 1 : p;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v0), "=s"(v1)
+               : "s"(p), "s"(p1)
+               : "memory");
+}
+
+__device__ __forceinline__ int32_t sload(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Block until this wave has at most `later` stages of D copies outstanding
+// (later <= MAXL), then meet the workgroup.
+template <int D, int MAXL>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (MAXL >= 4 && later >= 4) vm_wait_barrier<(MAXL >= 4 ? 4 : 0) * D>();
+  else if (MAXL >= 3 && later >= 3) vm_wait_barrier<(MAXL >= 3 ? 3 : 0) * D>();
+  else if (MAXL >= 2 && later >= 2) vm_wait_barrier<(MAXL >= 2 ? 2 : 0) * D>();
+  else if (later >= 1) vm_wait_barrier<D>();
+  else vm_wait_barrier<0>();
+}
+
+// One operand's share of an LDS stage: ROWS tile rows (M or N) by BK.
+template <bool MN, int ROWS, int BK>
+struct OpGeo {
+  static constexpr int BYTES = ROWS * BK * 2;    // per stage
+  static constexpr int INST = BYTES / 1024 / 4;  // DMA instructions per wave per stage
+  static constexpr int ROWB = ROWS * 2;          // MN: bytes of one k row
+  static constexpr int LPR = ROWS / 8;           // MN: lanes per k row in a DMA instruction
+  static constexpr int RPI = 64 / LPR;           // MN: k rows per DMA instruction
+  static constexpr int KLPR = BK / 8;            // K-contiguous: lanes per row in a DMA instruction
+  static constexpr int KRPI = 64 / KLPR;         // K-contiguous: rows per DMA instruction
+  static_assert(INST >= 1 && BYTES % 4096 == 0, "stage share must fill whole wave DMA instructions");
+  static_assert(!MN || (ROWS % 128 == 0 && RPI >= 1), "M/N-contiguous tile rows");
+};
+
+struct TileCoord {
+  int e_loc, row0, row_end, m0, n0, z;
+};
+
+// One output tile: its DMA sources, K loop and epilogue, with NS LDS stage
+// buffers of BK (32 or 64) K values.  All members are wave-uniform except the
+// per-lane DMA offsets.
+template <int KIND, int BM, int BN, int NS, int BK>
+struct TileJob {
+  using Tr = Traits<KIND>;
+  static constexpr int NB = Tr::NB, BROWS = NB * BN;
+  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  using GA = OpGeo<Tr::A_MN, BM, BK>;
+  using GB = OpGeo<Tr::B_MN, BROWS, BK>;
+  static constexpr int KK = BK / 16;  // 16-K MFMA slices per stage
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static constexpr int A_BYTES = GA::BYTES;
+  static constexpr int STAGE = GA::BYTES + GB::BYTES;
+  static constexpr int D = GA::INST + GB::INST;  // DMA instructions per wave per stage
+  static_assert(STAGE / 4 >= 8192, "epilogue staging needs 8 KB per wave");
+  static_assert(NS >= 2 && NS <= 5 && (NS - 1) * D <= 63, "stage count (vmcnt holds at most 63)");
+  static_assert(!(NB == 2 && Tr::B_MN), "paired B matrices are K-contiguous");
+
+  struct Frags {
+    bf16x8_t a[FM];
+    bf16x8_t b[NB][FN];
+  };
+
+  const GroupedGemmArgs* args;
+  GemmGeom G;
+  TileCoord c;
+  int wid, lane, wm, wn;
+  int kbeg, kend, nk;
+  i32x4_t rsA, rsB0, rsB1;  // K-contiguous sources (whole tile)
+  uint32_t offA[GA::INST], offB[GB::INST];
+
+  __device__ __forceinline__ void init(const GroupedGemmArgs& a, const TileCoord& tc) {
+    args = &a;
+    G = geom_of<KIND>(a.d, a.F);
+    c = tc;
+    lane = threadIdx.x & 63;
+    wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wm = wid >> 1;
+    wn = wid & 1;
+    kbeg = Tr::GROUP_K ? c.row0 : 0;
+    kend = Tr::GROUP_K ? c.row_end : G.K;
+    nk = (kend - kbeg + BK - 1) / BK;
+    const bf16_t* Abase = (const bf16_t*)a.A;
+    rsA = rsB0 = rsB1 = make_rsrc(Abase, 0u);
+    // ---- A
+    if constexpr (!Tr::A_MN) {
+      const int rows = c.row_end - c.row0 < BM ? c.row_end - c.row0 : BM;
+      if (a.gather_rows) {
+        // pull dispatch: each row comes straight from its token's row of x
+        rsA = make_rsrc(Abase, (uint32_t)(a.gather_src_rows * G.lda * 2));
+#pragma unroll
+        for (int q = 0; q < GA::INST; ++q) {
+          const int r = (wid * GA::INST + q) * GA::KRPI + lane / GA::KLPR;
+          const int tok = r < rows ? a.gather_rows[c.row0 + r] / a.k_top : -1;
+          offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_k<BK>(r, lane % GA::KLPR) * 16) : 0xFFFFFFF0u;
+        }
+      } else {
+        rsA = make_rsrc(Abase + ((int64_t)c.row0 - a.a_row_shift) * G.lda, (uint32_t)((int64_t)rows * G.lda * 2));
+#pragma unroll
+        for (int q = 0; q < GA::INST; ++q) {
+          const int r = (wid * GA::INST + q) * GA::KRPI + lane / GA::KLPR;
+          offA[q] = (uint32_t)(r * G.lda * 2 + swz_k<BK>(r, lane % GA::KLPR) * 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < GA::INST; ++q) {
+        const int r = (wid * GA::INST + q) * GA::RPI + lane / GA::LPR;  // k row in the stage
+        const int p = lane % GA::LPR;
+        const int col = swz_mn(r, p >> 2) * 32 + (p & 3) * 8;           // logical column of this 16 B
+        offA[q] = (uint32_t)((r * G.lda + col) * 2);
+      }
+    }
+    // ---- B
+    if constexpr (!Tr::B_MN) {
+      const int nb_rows = G.N - c.n0 < BN ? G.N - c.n0 : BN;
+      const bf16_t* b0 = (const bf16_t*)a.B0 + (int64_t)c.e_loc * G.b_estride + (int64_t)c.n0 * G.ldb;
+      rsB0 = make_rsrc(b0, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
+      if constexpr (NB == 2) {
+        const bf16_t* b1 = (const bf16_t*)a.B1 + (int64_t)c.e_loc * G.b_estride + (int64_t)c.n0 * G.ldb;
+        rsB1 = make_rsrc(b1, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
+      }
+#pragma unroll
+      for (int q = 0; q < GB::INST; ++q) {
+        const int r = (wid * GB::INST + q) * GB::KRPI + lane / GB::KLPR;  // LDS row
+        const int rl = (NB == 2 && r >= BN) ? r - BN : r;                 // row within its matrix
+        offB[q] = (uint32_t)(rl * G.ldb * 2 + swz_k<BK>(r, lane % GB::KLPR) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < GB::INST; ++q) {
+        const int r = (wid * GB::INST + q) * GB::RPI + lane / GB::LPR;
+        const int p = lane % GB::LPR;
+        const int col = swz_mn(r, p >> 2) * 32 + (p & 3) * 8;
+        offB[q] = Tr::GROUP_K && a.gather_rows ? (uint32_t)(col * 2) : (uint32_t)((r * G.ldb + col) * 2);
+      }
+    }
+  }
+
+  // Issue the copies of stage s into LDS stage buffer s % NS.
+  __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
+
+  // Copies [Q0, Q1) of the D of a stage (A's first, then B's), so that a
+  // stage's copies can be spread between MFMAs.
+  template <int Q0, int Q1>
+  __device__ __forceinline__ void issue_part(int s, uint8_t* arena) const {
+    constexpr int QB = GA::INST;  // index of the first B copy
+    uint8_t* st = arena + (s % NS) * STAGE;
+    const int k0 = kbeg + s * BK;
+    if constexpr (Q0 >= QB) {
+      // no A copies in this part
+    } else if constexpr (!Tr::A_MN) {
+#pragma unroll
+      for (int q = Q0; q < (Q1 < QB ? Q1 : QB); ++q)
+        dma_b128(rsA, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], k0 * 2);
+    } else {
+      // rows [k0, kend) of columns [m0, ...) of this expert's rows; rows past kend read zero
+      const int64_t col0 = c.m0 + (KIND == KIND_DW13 ? (int64_t)c.z * args->F : 0);
+      const bf16_t* p = (const bf16_t*)args->A + (int64_t)k0 * G.lda + col0;
+      const int64_t bytes = ((int64_t)(kend - k0) * G.lda - col0) * 2;
+      const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
+#pragma unroll
+      for (int q = Q0; q < (Q1 < QB ? Q1 : QB); ++q)
+        dma_b128(rs, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], 0);
+    }
+    uint8_t* sb = st + A_BYTES;
+    constexpr int B0q = Q0 > QB ? Q0 - QB : 0, B1q = Q1 > QB ? Q1 - QB : 0;  // this part's B copies
+    if constexpr (B1q <= B0q) {
+      // no B copies in this part
+    } else if constexpr (!Tr::B_MN) {
+#pragma unroll
+      for (int q = B0q; q < B1q; ++q)
+        dma_b128((NB == 2 && (wid * GB::INST + q) * GB::KRPI >= BN) ? rsB1 : rsB0,
+                 lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], k0 * 2);
+    } else if constexpr (!Tr::GROUP_K) {
+      // weights [K][N] of this expert; DX takes k < F from W1 and the rest from W3
+      const bool second = k0 >= G.ksplit;
+      const int kl = second ? k0 - G.ksplit : k0;
+      const bf16_t* base = (const bf16_t*)(second ? args->B1 : args->B0) + (int64_t)c.e_loc * G.b_estride;
+      const int krows = second ? G.K - G.ksplit : G.ksplit;
+      const bf16_t* p = base + (int64_t)kl * G.ldb + c.n0;
+      const int64_t bytes = ((int64_t)(krows - kl) * G.ldb - c.n0) * 2;
+      const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
+#pragma unroll
+      for (int q = B0q; q < B1q; ++q) dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
+    } else if (!args->gather_rows) {
+      const bf16_t* p = (const bf16_t*)args->B0 + (int64_t)k0 * G.ldb + c.n0;
+      const int64_t bytes = ((int64_t)(kend - k0) * G.ldb - c.n0) * 2;
+      const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
+#pragma unroll
+      for (int q = B0q; q < B1q; ++q) dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
+    } else {
+      // B rows are token rows of x: row k of the expert is x[gather_rows[k] / k_top]
+      static_assert(GB::RPI == 2, "gathered rows: two k rows per DMA instruction");
+      const i32x4_t rs = make_rsrc(args->B0, (uint32_t)(args->gather_src_rows * G.ldb * 2));
+#pragma unroll
+      for (int q = B0q; q < B1q; ++q) {
+        const int kr = k0 + (wid * GB::INST + q) * 2;
+        int32_t i0 = -1, i1 = -1;
+        if (kr < kend) sload_pair(args->gather_rows + kr, kr + 1 < kend, i0, i1);
+        i1 = kr + 1 < kend ? i1 : -1;
+        const int32_t pr = (lane >> 5) ? i1 : i0;
+        const uint32_t off =
+            pr >= 0 ? (uint32_t)(((int64_t)(pr / args->k_top) * G.ldb + c.n0) * 2) + offB[q] : 0xFFFFFFF0u;
+        dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), off, 0);
+      }
+    }
+  }
+
+  // Fragment of tile rows [rb, rb + 32) from an M/N-contiguous stage: lane l
+  // gets k = 16 kk + 8 (l / 32) + 0..7 of row rb + l % 32.  In each group of
+  // 16 lanes, lane j names four consecutive values of k row j / 4 (columns
+  // 4 (j % 4) + 0..3 of the group's 16) and the transposing read returns to
+  // lane j the values of column j from k rows 0..3.
+  template <int ROWB>
+  __device__ __forceinline__ bf16x8_t read_tr(const uint8_t* base, int rb, int kk) const {
+    const int g = lane >> 4, jj = lane & 15;
+    const int kr = kk * 16 + 8 * (g >> 1) + (jj >> 2);
+    const int col = rb + 16 * (g & 1) + 4 * (jj & 3);
+    const uint8_t* p0 = base + kr * ROWB + swz_mn(kr, col >> 5) * 64 + (col & 31) * 2;
+    const i16x4_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const __attribute__((address_space(3))) void*)p0);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(const __attribute__((address_space(3))) void*)(p0 + 4 * ROWB));
+    const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+
+  // Fragments of 16-K slice kk (0 or 1) of the stage in buffer `buf`.
+  __device__ __forceinline__ void read(int buf, int kk, const uint8_t* arena, Frags& f) const {
+    const uint8_t* st = arena + buf * STAGE;
+    if constexpr (!Tr::A_MN) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + (lane & 31);
+        f.a[i] = *reinterpret_cast<const bf16x8_t*>(st + r * (BK * 2) + swz_k<BK>(r, kk * 2 + (lane >> 5)) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) f.a[i] = read_tr<GA::ROWB>(st, wm * TM + i * 32, kk);
+    }
+    const uint8_t* sb = st + A_BYTES;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int rb = b * BN + wn * TN + j * 32;
+        if constexpr (!Tr::B_MN) {
+          const int r = rb + (lane & 31);
+          f.b[b][j] = *reinterpret_cast<const bf16x8_t*>(sb + r * (BK * 2) + swz_k<BK>(r, kk * 2 + (lane >> 5)) * 16);
+        } else {
+          f.b[b][j] = read_tr<GB::ROWB>(sb, rb, kk);
+        }
+      }
+  }
+
+  __device__ __forceinline__ static void mma(f32x16_t (&acc)[NB][FM][FN], const Frags& f) { mma_part<0, 1>(acc, f); }
+
+  // MFMAs [g, g + 1) / NG of a slice, in (b, i, j) order.
+  template <int g, int NG>
+  __device__ __forceinline__ static void mma_part(f32x16_t (&acc)[NB][FM][FN], const Frags& f) {
+    constexpr int TOT = NB * FM * FN, L0 = g * TOT / NG, L1 = (g + 1) * TOT / NG;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int L = (b * FM + i) * FN + j;
+          if (L >= L0 && L < L1)
+            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
+        }
+  }
+
+  // The last slice of a stage with the next stage's copies spread between
+  // its MFMAs (four groups).
+  template <int G>
+  __device__ __forceinline__ void mma_issue(f32x16_t (&acc)[NB][FM][FN], const Frags& f, bool copy, int s,
+                                            uint8_t* arena) const {
+    if constexpr (G < 4) {
+      if (copy) issue_part<G * D / 4, (G + 1) * D / 4>(s, arena);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_part<G, 4>(acc, f);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_issue<G + 1>(acc, f, copy, s, arena);
+    }
+  }
+
+  // K loop.  On entry the copies of stages 0 .. min(nk, NS) - 1 have been
+  // issued in order; on exit every stage has been read by this wave (the
+  // caller meets the workgroup before reusing the buffers).
+  __device__ __forceinline__ void mainloop(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena) const {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+    if (nk <= 0) return;
+    wait_stages<D, NS - 1>(nk - 1 < NS - 1 ? nk - 1 : NS - 1);  // stages issued after stage 0
+    // (sched_barrier: keep each batch of fragment reads ahead of the MFMAs
+    // that hide its latency; the scheduler would otherwise sink them).
+    // Slice kk of a stage sits in fa for even kk and in fb for odd kk.
+    Frags fa, fb;
+    read(0, 0, arena, fa);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        read(kt % NS, kk + 1, arena, (kk & 1) ? fa : fb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(acc, (kk & 1) ? fb : fa);
+      }
+      // stage kt + 1 landed (the NS - 2 after it may still fly), and every
+      // wave is done with stage kt, whose buffer takes stage kt + NS
+      wait_stages<D, NS - 2>(nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2);
+      read((kt + 1) % NS, 0, arena, fa);
+      mma_issue<0>(acc, fb, kt + NS < nk, kt + NS, arena);  // slice KK - 1 (KK is even)
+    }
+    // last stage (peeled: its last slice follows no barrier)
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      read((nk - 1) % NS, kk + 1, arena, (kk & 1) ? fa : fb);
+      mma(acc, (kk & 1) ? fb : fa);
+    }
+    mma(acc, fb);
+  }
+
+  // Epilogue.  bf16 outputs go through this wave's own 8 KB of `staging`
+  // (32 KB for the workgroup): 16-byte row-contiguous stores.  fp32 weight
+  // gradients are stored straight from the accumulators: each half-wave
+  // writes 32 consecutive floats of one row, a whole 128-byte line.
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging) const {
+    float* ep = reinterpret_cast<float*>(staging + wid * 8192);
+    const GroupedGemmArgs& a = *args;
+    const int wrow0 = wm * TM, wcol0 = wn * TN;
+    if constexpr (Tr::GROUP_K) {
+      // M and N are multiples of 32: a 32 x 32 block is wholly in or out
+      float* outp = (float*)(KIND == KIND_DW13 && c.z ? a.out1 : a.out0) + (int64_t)c.e_loc * G.M * G.N;
+      float* lp = outp + (int64_t)(c.m0 + wrow0 + (lane >> 5) * 4) * G.N + c.n0 + wcol0 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (c.m0 + wrow0 + i * 32 >= G.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (c.n0 + wcol0 + j * 32 >= G.N) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            lp[(int64_t)(i * 32 + (r >> 2) * 8 + (r & 3)) * G.N + j * 32] = acc[0][i][j][r];
+        }
+      }
+    } else if constexpr (NB == 2) {
+      // UP: gate (W1) and up (W3) accumulators of one 32 x 32 block per round
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
+            ep[1024 + rr * 32 + (lane & 31)] = acc[1][i][j][r];
+          }
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int seg = q * 64 + lane;
+            const int rr = seg >> 2, c8 = (seg & 3) * 8;
+            const int row = c.row0 + wrow0 + i * 32 + rr, col = c.n0 + wcol0 + j * 32 + c8;
+            if (row < c.row_end && col < G.N) {
+              const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
+              const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[1024 + rr * 32 + c8]);
+              const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
+              const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+              const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+              u32x4_t h, av, bv;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float h0 = v[2 * t] * sigmoidf_(v[2 * t]) * u[2 * t];
+                const float h1 = v[2 * t + 1] * sigmoidf_(v[2 * t + 1]) * u[2 * t + 1];
+                h[t] = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
+                av[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+                bv[t] = (uint32_t)f2bf(u[2 * t]) | ((uint32_t)f2bf(u[2 * t + 1]) << 16);
+              }
+              const int64_t o = (int64_t)row * G.N + col;
+              *reinterpret_cast<u32x4_t*>((bf16_t*)a.out0 + o) = h;
+              if (a.save) {
+                *reinterpret_cast<u32x4_t*>((bf16_t*)a.save_a + o) = av;
+                *reinterpret_cast<u32x4_t*>((bf16_t*)a.save_b + o) = bv;
+              }
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+    } else {
+      // one 32 x 64 block per round
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
+            }
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int seg = q * 64 + lane;
+            const int rr = seg >> 3, c8 = (seg & 7) * 8;
+            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
+            const f32x4_t v0 = pv[0], v1 = pv[1];
+            const int col = c.n0 + wcol0 + jp * 64 + c8;
+            {
+              const int row = c.row0 + wrow0 + i * 32 + rr;
+              if (row < c.row_end && col < G.N) {
+                const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const int64_t o = (int64_t)row * G.N + col;
+                if constexpr (KIND == KIND_DH) {
+                  const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o);
+                  const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o);
+                  u32x4_t da, db;
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) {
+                    float dav[2], dbv[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                      const float x1 = __uint_as_float(hh ? (av[t] & 0xFFFF0000u) : (av[t] << 16));
+                      const float x3 = __uint_as_float(hh ? (bv[t] & 0xFFFF0000u) : (bv[t] << 16));
+                      const float sg = sigmoidf_(x1);
+                      const float dh = v[2 * t + hh];
+                      dav[hh] = dh * x3 * sg * (1.0f + x1 * (1.0f - sg));
+                      dbv[hh] = dh * x1 * sg;
+                    }
+                    da[t] = (uint32_t)f2bf(dav[0]) | ((uint32_t)f2bf(dav[1]) << 16);
+                    db[t] = (uint32_t)f2bf(dbv[0]) | ((uint32_t)f2bf(dbv[1]) << 16);
+                  }
+                  bf16_t* dab = (bf16_t*)a.out0 + (int64_t)row * 2 * a.F;
+                  *reinterpret_cast<u32x4_t*>(dab + col) = da;
+                  *reinterpret_cast<u32x4_t*>(dab + a.F + col) = db;
+                } else {
+                  u32x4_t y;
+#pragma unroll
+                  for (int t = 0; t < 4; ++t)
+                    y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+                  *reinterpret_cast<u32x4_t*>((bf16_t*)a.out0 + o) = y;
+                }
+              }
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+    }
+  }
+};
 
 // Grouped raster inside one expert: groups of GM m-tiles, n-tiles outer and
 // m-tiles inner within a group, so that a run of consecutive tiles forms a
@@ -61,487 +560,204 @@ __device__ __forceinline__ void tile_mn(int local, int mt, int ntn, int& m, int&
   m = gm0 + rem % gsz;
 }
 
-// Store the transpose of an 8 x 8 block of 16-bit values into a swizzled LDS
-// tile: in[i] holds K-row i (8 consecutive M/N values starting at 8 * mb);
-// LDS row 8 * mb + t receives chunk kb = those 8 K values of column t.
-// Lanes with bit 3 of mb set write the rows of each pair in swapped order,
-// which removes the remaining bank conflicts (only the v_perm selector
-// changes per lane).
-__device__ __forceinline__ void transposed_store(const u32x4_t in[8], uint8_t* tile, int mb, int kb) {
-  const uint32_t x = (mb >> 3) & 1;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = j ^ (int)x;
-    const uint32_t sel = ((j & 1) ^ x) ? 0x07060302u : 0x05040100u;
-    u32x4_t o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][j >> 1], in[2 * w][j >> 1], sel);
-    const int r = mb * 8 + t;
-    *reinterpret_cast<u32x4_t*>(&tile[r * kRowBytes + swz_chunk(r, kb) * 16]) = o;
-  }
+// The tile coordinates are wave-uniform; say so, so that addresses and
+// buffer resources live in scalar registers.
+__device__ __forceinline__ TileCoord uniform(TileCoord c) {
+  c.e_loc = __builtin_amdgcn_readfirstlane(c.e_loc);
+  c.row0 = __builtin_amdgcn_readfirstlane(c.row0);
+  c.row_end = __builtin_amdgcn_readfirstlane(c.row_end);
+  c.m0 = __builtin_amdgcn_readfirstlane(c.m0);
+  c.n0 = __builtin_amdgcn_readfirstlane(c.n0);
+  c.z = __builtin_amdgcn_readfirstlane(c.z);
+  return c;
 }
 
-template <int KIND, int BM, int BN>
-struct TileCfg {
-  using Tr = Traits<KIND>;
-  static constexpr int NT = 256, WM = 2, WN = 2;
-  static constexpr int NB = Tr::NB;
-  static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int BROWS = NB * BN;
-  // K-contiguous operand: direct-to-LDS loads of 8 rows (1 KB) per wave instruction
-  static constexpr int DMA_A = Tr::A_MN ? 0 : BM / 8 / 4;
-  static constexpr int DMA_B = Tr::B_MN ? 0 : BROWS / 8 / 4;
-  // MN-contiguous operand: 8x8 blocks per thread, transposed in registers
-  static constexpr int BLA = Tr::A_MN ? (kBK / 8) * (BM / 8) / NT : 0;
-  static constexpr int BLB = Tr::B_MN ? (kBK / 8) * (BROWS / 8) / NT : 0;
-  static_assert(!Tr::A_MN || BLA >= 1, "MN tile too small");
-  static_assert(!Tr::B_MN || BLB >= 1, "MN tile too small");
-  static_assert(BM % 32 == 0 && BROWS % 32 == 0, "tile rows");
-};
-
-// One output tile: K loop over double-buffered LDS stages, then the
-// LDS-staged epilogue.  Called by every thread of the workgroup with
-// wave-uniform tile coordinates; ends with a barrier (the epilogue staging
-// overlaps the next tile's first K stage).
-template <int KIND, int BM, int BN>
-__device__ __forceinline__ void gemm_tile(const GroupedGemmArgs& args, uint8_t* arena, int e_loc, int row0,
-                                          int row_end, int m0, int n0, int z) {
-  using Tr = Traits<KIND>;
-  using C = TileCfg<KIND, BM, BN>;
-  constexpr int NT = C::NT, NB = C::NB, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, BROWS = C::BROWS;
-  uint8_t (*sA)[BM * kRowBytes] = reinterpret_cast<uint8_t (*)[BM * kRowBytes]>(arena);
-  uint8_t (*sB)[BROWS * kRowBytes] = reinterpret_cast<uint8_t (*)[BROWS * kRowBytes]>(arena + 2 * BM * kRowBytes);
-  const GemmGeom G = geom_of<KIND>(args.d, args.F);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
-  const int wm = wid / C::WN, wn = wid % C::WN;
-  const bf16_t* __restrict__ Abase = (const bf16_t*)args.A;
-  const bf16_t* __restrict__ B0 = (const bf16_t*)args.B0;
-  const bf16_t* __restrict__ B1 = (const bf16_t*)args.B1;
-  const int kbeg = Tr::GROUP_K ? row0 : 0;
-  const int kend = Tr::GROUP_K ? row_end : G.K;
-  const int nk = (kend - kbeg + kBK - 1) / kBK;
-
-  // ------------------------------------------------------------ direct-to-LDS sources
-  // Buffer resources rebased on this tile: rows past the expert's end (A) or
-  // past N (B) fall outside num_records and read as zero.
-  i32x4_t rsA = make_rsrc(Abase, 0u);
-  i32x4_t rsB0 = rsA, rsB1 = rsA;
-  uint32_t offA[C::DMA_A > 0 ? C::DMA_A : 1], offB[C::DMA_B > 0 ? C::DMA_B : 1];
-  if constexpr (!Tr::A_MN) {
-    const int rows = row_end - row0 < BM ? row_end - row0 : BM;  // this tile's rows
-    if (args.gather_rows) {
-      // pull dispatch: each row comes straight from its token's row of x
-      rsA = make_rsrc(Abase, (uint32_t)(args.gather_src_rows * G.lda * 2));
-#pragma unroll
-      for (int q = 0; q < C::DMA_A; ++q) {
-        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
-        const int tok = r < rows ? args.gather_rows[row0 + r] / args.k_top : -1;
-        offA[q] = tok >= 0 ? (uint32_t)(tok * G.lda * 2 + swz_chunk(r, lane & 7) * 16) : 0xFFFFFFF0u;
-      }
-    } else {
-      rsA = make_rsrc(Abase + ((int64_t)row0 - args.a_row_shift) * G.lda, (uint32_t)((int64_t)rows * G.lda * 2));
-#pragma unroll
-      for (int q = 0; q < C::DMA_A; ++q) {
-        const int r = (wid * C::DMA_A + q) * 8 + (lane >> 3);
-        offA[q] = (uint32_t)(r * G.lda * 2 + swz_chunk(r, lane & 7) * 16);
-      }
-    }
-  }
-  if constexpr (!Tr::B_MN) {
-    const int nb_rows = G.N - n0 < BN ? G.N - n0 : BN;  // this tile's rows of each B matrix
-    const bf16_t* b0 = B0 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-    rsB0 = make_rsrc(b0, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
-    if constexpr (NB == 2) {
-      const bf16_t* b1 = B1 + (int64_t)e_loc * G.b_estride + (int64_t)n0 * G.ldb;
-      rsB1 = make_rsrc(b1, (uint32_t)((int64_t)nb_rows * G.ldb * 2));
-    }
-#pragma unroll
-    for (int q = 0; q < C::DMA_B; ++q) {
-      const int r = (wid * C::DMA_B + q) * 8 + (lane >> 3);      // LDS row
-      const int rl = (NB == 2 && r >= BN) ? r - BN : r;          // row within its matrix
-      offB[q] = (uint32_t)(rl * G.ldb * 2 + swz_chunk(r, lane & 7) * 16);
-    }
-  }
-
-  u32x4_t ta[C::BLA > 0 ? C::BLA : 1][8], tb[C::BLB > 0 ? C::BLB : 1][8];
-
-  // Issue the loads of K-step k0 into LDS stage `buf` (direct) or registers (MN).
-  auto issue = [&](int k0, int buf) {
-    if constexpr (!Tr::A_MN) {
-#pragma unroll
-      for (int q = 0; q < C::DMA_A; ++q)
-        dma_b128(rsA, lds_addr(&sA[buf][(wid * C::DMA_A + q) * 1024]), offA[q], k0 * 2);
-    } else {
-      const bf16_t* p = Abase + (KIND == KIND_DW13 ? (int64_t)z * args.F : 0);
-#pragma unroll
-      for (int q = 0; q < C::BLA; ++q) {
-        const int blk = tid + q * NT;
-        const int mb = blk % (BM / 8), kb = blk / (BM / 8);
-        const int m = m0 + mb * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kr = k0 + kb * 8 + i;
-          ta[q][i] = (kr < kend && m < G.M) ? *reinterpret_cast<const u32x4_t*>(p + (int64_t)kr * G.lda + m)
-                                            : u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    if constexpr (!Tr::B_MN) {
-#pragma unroll
-      for (int q = 0; q < C::DMA_B; ++q) {
-        const int r = (wid * C::DMA_B + q) * 8;
-        dma_b128((NB == 2 && r >= BN) ? rsB1 : rsB0, lds_addr(&sB[buf][(wid * C::DMA_B + q) * 1024]), offB[q],
-                 k0 * 2);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < C::BLB; ++q) {
-        const int blk = tid + q * NT;
-        const int nb = blk % (BROWS / 8), kb = blk / (BROWS / 8);
-        const int n = n0 + nb * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kr = k0 + kb * 8 + i;
-          const bf16_t* src;
-          bool ok;
-          if constexpr (!Tr::GROUP_K) {
-            const int krl = kr < G.ksplit ? kr : kr - G.ksplit;
-            src = (kr < G.ksplit ? B0 : B1) + (int64_t)e_loc * G.b_estride + (int64_t)krl * G.ldb + n;
-            ok = n < G.N;
-          } else {
-            ok = kr < kend && n < G.N;
-            // ring mode keeps no expert-sorted copy of X: pull the token rows
-            const int64_t srow = args.gather_rows ? (ok ? args.gather_rows[kr] / args.k_top : 0) : kr;
-            src = B0 + srow * G.ldb + n;
-          }
-          tb[q][i] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  // Transpose the register-staged (MN) blocks into LDS stage `buf`.
-  auto commit = [&](int buf) {
-    if constexpr (Tr::A_MN) {
-#pragma unroll
-      for (int q = 0; q < C::BLA; ++q) {
-        const int blk = tid + q * NT;
-        transposed_store(ta[q], sA[buf], blk % (BM / 8), blk / (BM / 8));
-      }
-    }
-    if constexpr (Tr::B_MN) {
-#pragma unroll
-      for (int q = 0; q < C::BLB; ++q) {
-        const int blk = tid + q * NT;
-        transposed_store(tb[q], sB[buf], blk % (BROWS / 8), blk / (BROWS / 8));
-      }
-    }
-  };
-
-  f32x16_t acc[NB][FM][FN];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
-
-  if (nk > 0) {
-    issue(kbeg, 0);
-    commit(0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue(kbeg + (kt + 1) * kBK, buf ^ 1);
-    const uint8_t* a_s = sA[buf];
-    const uint8_t* b_s = sB[buf];
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int lc = kk * 2 + (lane >> 5);
-      bf16x8_t af[FM], bfr[NB][FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * TM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&a_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = b * BN + wn * TN + j * 32 + (lane & 31);
-          bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(&b_s[r * kRowBytes + swz_chunk(r, lc) * 16]);
-        }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) commit(buf ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- epilogue
-  // Each wave stages its accumulators in its own 32 KB LDS region, then
-  // every lane handles 8 consecutive columns of one row: 16-byte loads and
-  // stores along rows.
-  float* ep = reinterpret_cast<float*>(arena + wid * 32768);
-  const int wrow0 = wm * TM, wcol0 = wn * TN;
-  if constexpr (NB == 2) {
-    // UP: gate (W1) and up (W3) accumulators of one 32-column fragment
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
-          ep[4096 + rr * 32 + (lane & 31)] = acc[NB - 1][i][j][r];
-        }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll 2
-      for (int q = 0; q < TM * 32 / 8 / 64; ++q) {
-        const int seg = q * 64 + lane;
-        const int rr = seg >> 2, c8 = (seg & 3) * 8;
-        const int row = row0 + wrow0 + rr, col = n0 + wcol0 + j * 32 + c8;
-        if (row < row_end && col < G.N) {
-          const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
-          const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[4096 + rr * 32 + c8]);
-          const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
-          float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-          u32x4_t h, a, b;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float h0 = v[2 * t] * sigmoidf_(v[2 * t]) * u[2 * t];
-            const float h1 = v[2 * t + 1] * sigmoidf_(v[2 * t + 1]) * u[2 * t + 1];
-            h[t] = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
-            a[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
-            b[t] = (uint32_t)f2bf(u[2 * t]) | ((uint32_t)f2bf(u[2 * t + 1]) << 16);
-          }
-          const int64_t o = (int64_t)row * G.N + col;
-          *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = h;
-          if (args.save) {
-            *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_a + o) = a;
-            *reinterpret_cast<u32x4_t*>((bf16_t*)args.save_b + o) = b;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  } else {
-#pragma unroll
-    for (int jp = 0; jp < FN / 2; ++jp) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
-          }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll 2
-      for (int q = 0; q < TM * 64 / 8 / 64; ++q) {
-        const int seg = q * 64 + lane;
-        const int rr = seg >> 3, c8 = (seg & 7) * 8;
-        const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
-        const f32x4_t v0 = pv[0], v1 = pv[1];
-        const int col = n0 + wcol0 + jp * 64 + c8;
-        if constexpr (!Tr::GROUP_K) {
-          const int row = row0 + wrow0 + rr;
-          if (row < row_end && col < G.N) {
-            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            const int64_t o = (int64_t)row * G.N + col;
-            if constexpr (KIND == KIND_DH) {
-              const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_a + o);
-              const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)args.save_b + o);
-              u32x4_t da, db;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                float dav[2], dbv[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                  const float a = __uint_as_float(hh ? (av[t] & 0xFFFF0000u) : (av[t] << 16));
-                  const float b = __uint_as_float(hh ? (bv[t] & 0xFFFF0000u) : (bv[t] << 16));
-                  const float sg = sigmoidf_(a);
-                  const float dh = v[2 * t + hh];
-                  dav[hh] = dh * b * sg * (1.0f + a * (1.0f - sg));
-                  dbv[hh] = dh * a * sg;
-                }
-                da[t] = (uint32_t)f2bf(dav[0]) | ((uint32_t)f2bf(dav[1]) << 16);
-                db[t] = (uint32_t)f2bf(dbv[0]) | ((uint32_t)f2bf(dbv[1]) << 16);
-              }
-              bf16_t* dab = (bf16_t*)args.out0 + (int64_t)row * 2 * args.F;
-              *reinterpret_cast<u32x4_t*>(dab + col) = da;
-              *reinterpret_cast<u32x4_t*>(dab + args.F + col) = db;
-            } else {
-              u32x4_t y;
-#pragma unroll
-              for (int t = 0; t < 4; ++t)
-                y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
-              *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + o) = y;
-            }
-          }
-        } else {
-          const int m = m0 + wrow0 + rr;
-          if (m < G.M && col < G.N) {
-            float* outp = (float*)(KIND == KIND_DW13 && z ? args.out1 : args.out0);
-            f32x4_t* dst = reinterpret_cast<f32x4_t*>(outp + (int64_t)e_loc * G.M * G.N + (int64_t)m * G.N + col);
-            dst[0] = v0;
-            dst[1] = v1;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  __syncthreads();  // staging regions overlap the next tile's first K stage
-}
-
-template <int KIND, int BM, int BN>
+// Persistent grouped GEMM.  LDS: the NS stage buffers, then either the
+// 32 KB bf16 epilogue staging area (row kinds; 160 KB in all) or the mailbox
+// through which wave 0 hands the tile taken from the queue to the workgroup
+// (weight-gradient kinds).  The tile-prefix table is searched in global
+// memory through the scalar cache.
+template <int KIND, int BM, int BN, int NS, int BK>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
   using Tr = Traits<KIND>;
-  using C = TileCfg<KIND, BM, BN>;
-  constexpr int NT = C::NT;
-
-  // One LDS arena: two stages of the A and B tiles during the K loop, then
-  // four per-wave staging regions for the epilogue.
-  constexpr int kArena = 2 * (BM + C::BROWS) * kRowBytes;
-  static_assert(kArena >= 4 * 32768, "epilogue staging needs 32 KB per wave");
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
-  __shared__ int32_t s_tp[1025];
+  using Job = TileJob<KIND, BM, BN, NS, BK>;
+  constexpr int kExtra = Tr::GROUP_K ? 256 : 32768;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[NS * Job::STAGE + kExtra];
+  uint8_t* const staging = arena + NS * Job::STAGE;
+  int* const mbox = reinterpret_cast<int*>(staging);
 
   const GemmGeom G = geom_of<KIND>(args.d, args.F);
   const int tid = threadIdx.x;
   const int E_loc = args.E_loc;
   const int ntn = (G.N + BN - 1) / BN;
-
-  int total, ntm_k = 0;
+  const int xcd = blockIdx.x % 8;
   constexpr int NZ = KIND == KIND_DW13 ? 2 : 1;  // DW13 computes dW1 (z = 0) and dW3 (z = 1)
+  const int32_t* tp = args.tile_prefix + ((BM == 64) ? 0 : (BM == 128 ? 1 : 2)) * (E_loc + 1);
+
+  int total, ntm_k = 0, tbeg = 0;
   if constexpr (!Tr::GROUP_K) {
-    const int bidx = (BM == 64) ? 0 : (BM == 128 ? 1 : 2);
-    const int32_t* tp = args.tile_prefix + bidx * (E_loc + 1);
-    for (int i = tid; i <= E_loc; i += NT) s_tp[i] = tp[i];
-    __syncthreads();
-    total = s_tp[E_loc] * ntn;
+    total = sload(tp + E_loc) * ntn;
   } else {
-    // this XCD's share: its experts' tiles, NZ * ntm * ntn per expert
+    // This XCD's share of the heaviest-first tile sequence (expert-major,
+    // T tiles per expert): the run of tiles whose cumulative work falls in
+    // the XCD's eighth of the total.
     ntm_k = (G.M + BM - 1) / BM;
-    const int x = blockIdx.x % 8;
-    total = (args.expert_order[x + 1] - args.expert_order[x]) * NZ * ntm_k * ntn;
+    const int T = NZ * ntm_k * ntn;
+    const int32_t* wp = args.expert_order + E_loc;  // work prefix over ranks
+    auto bound = [&](int x) -> int {
+      if (x <= 0 || E_loc == 0) return 0;
+      if (x >= 8) return E_loc * T;
+      const int64_t target = (int64_t)T * sload(wp + E_loc) * x / 8;
+      int lo = 0, hi = E_loc - 1;  // last rank whose tiles start at or before target
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)T * sload(wp + mid) <= target) lo = mid; else hi = mid - 1;
+      }
+      const int w0 = sload(wp + lo), w1 = sload(wp + lo + 1);
+      const int64_t j = (target - (int64_t)T * w0) / (w1 - w0);  // whole tiles of rank lo by target
+      return lo * T + (int)(j < T ? j : T);
+    };
+    tbeg = bound(xcd);
+    total = bound(xcd + 1) - tbeg;
   }
   // Row-grouped kinds: equal-sized tiles in a static round-robin.  XCD-aware
   // order: workgroup b (on XCD b % 8) takes tiles from the contiguous run
   // [x * G/8, (x+1) * G/8) of each round of G tiles.  Weight-gradient kinds:
-  // the work of a tile grows with its expert's rows, so the experts are dealt
-  // to the XCDs longest-first (by the counting sort) and the workgroups of
-  // XCD x pull that share's tiles from counter x, heaviest expert first; an
-  // expert's tiles then share one L2.  Each tile is still computed whole by one
+  // the work of a tile grows with its expert's rows, so the tiles are taken
+  // heaviest expert first (rank order of the counting sort), the sequence is
+  // cut into 8 runs of equal work and the workgroups of XCD x pull run x's
+  // tiles from counter x: an expert's tiles mostly share one L2, and an
+  // expert heavier than an eighth of the work spreads over several XCDs.  Each tile is still computed whole by one
   // workgroup, so the results do not depend on the assignment.
   const int G_ = gridDim.x;
-  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
-  __shared__ int s_next;
-  auto next_tile = [&](int cur) -> int {
-    if constexpr (!Tr::GROUP_K) {
-      return cur < 0 ? vb : cur + G_;
-    } else {
-      if (tid == 0) s_next = atomicAdd(args.queue + blockIdx.x % 8, 1);
-      __syncthreads();
-      const int t = s_next;
-      __syncthreads();
-      return t;
+  const int vb = (G_ % 8 == 0) ? xcd * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+  // Weight-gradient kinds: thread 0 takes the tile after the current one from
+  // the queue as the current one starts, so the atomic's latency is hidden.
+  int taken = 0;
+  auto take = [&]() {
+    if constexpr (Tr::GROUP_K) {
+      if (tid == 0) taken = atomicAdd(args.queue + xcd, 1);
     }
   };
-
-  for (int tile = next_tile(-1); tile < total; tile = next_tile(tile)) {
-    int e_loc, row0, row_end, m0 = 0, n0, z = 0;
+  auto coord = [&](int tile) -> TileCoord {
+    TileCoord c{};
     if constexpr (!Tr::GROUP_K) {
-      // (expert, n-tile, m-tile) order; expert e owns tiles [s_tp[e]*ntn, s_tp[e+1]*ntn)
+      // (expert, n-tile, m-tile) order; expert e owns tiles [tp[e]*ntn, tp[e+1]*ntn),
+      // so e is the last expert with tp[e] <= tile / ntn
+      const int q = tile / ntn;
       int lo = 0, hi = E_loc - 1;
       while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (s_tp[mid] * ntn <= tile) lo = mid; else hi = mid - 1;
+        const int mid = (lo + hi + 1) >> 1;
+        if (sload(tp + mid) <= q) lo = mid; else hi = mid - 1;
       }
-      e_loc = lo;
+      c.e_loc = lo;
+      const int t0 = sload(tp + lo), t1 = sload(tp + lo + 1);
       int mt, nt;
-      tile_mn(tile - s_tp[e_loc] * ntn, s_tp[e_loc + 1] - s_tp[e_loc], ntn, mt, nt);
-      n0 = nt * BN;
-      const int e = args.eb + e_loc;
-      row0 = args.offsets[e] + mt * BM;
-      row_end = args.offsets[e + 1];
+      tile_mn(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
+      c.n0 = nt * BN;
+      const int e = args.eb + lo;
+      c.row0 = sload(args.offsets + e) + mt * BM;
+      c.row_end = sload(args.offsets + e + 1);
     } else {
       const int per_z = ntm_k * ntn;
-      e_loc = args.expert_order[16 + args.expert_order[blockIdx.x % 8] + tile / (NZ * per_z)];
-      const int rem = tile % (NZ * per_z);
-      z = rem / per_z;
+      const int g = tbeg + tile;  // position in the heaviest-first sequence
+      c.e_loc = sload(args.expert_order + g / (NZ * per_z));
+      const int rem = g % (NZ * per_z);
+      c.z = rem / per_z;
       int mt, nt;
       tile_mn(rem % per_z, ntm_k, ntn, mt, nt);
-      m0 = mt * BM;
-      n0 = nt * BN;
-      const int e = args.eb + e_loc;
-      row0 = args.offsets[e];
-      row_end = args.offsets[e + 1];
+      c.m0 = mt * BM;
+      c.n0 = nt * BN;
+      const int e = args.eb + c.e_loc;
+      c.row0 = sload(args.offsets + e);
+      c.row_end = sload(args.offsets + e + 1);
     }
-    // The tile coordinates are wave-uniform; say so, so that addresses and
-    // buffer resources live in scalar registers (a divergent resource would
-    // make every buffer load a waterfall loop).
-    e_loc = __builtin_amdgcn_readfirstlane(e_loc);
-    row0 = __builtin_amdgcn_readfirstlane(row0);
-    row_end = __builtin_amdgcn_readfirstlane(row_end);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    n0 = __builtin_amdgcn_readfirstlane(n0);
-    z = __builtin_amdgcn_readfirstlane(z);
-    gemm_tile<KIND, BM, BN>(args, arena, e_loc, row0, row_end, m0, n0, z);
+    return uniform(c);
+  };
+
+  int tile = vb;
+  if constexpr (Tr::GROUP_K) {
+    take();
+    if (tid == 0) *mbox = taken;
+    lds_barrier();
+    tile = __builtin_amdgcn_readfirstlane(*mbox);
+    lds_barrier();
+  }
+  if (tile >= total) return;
+  Job cur;
+  cur.init(args, coord(tile));
+  for (int s = 0; s < NS && s < cur.nk; ++s) cur.issue(s, arena);
+  f32x16_t acc[Job::NB][Job::FM][Job::FN];
+  while (true) {
+    take();
+    cur.mainloop(acc, arena);
+    int nt = tile + G_;
+    if constexpr (Tr::GROUP_K) {
+      if (tid == 0) *mbox = taken;
+    }
+    lds_barrier();  // every wave is done with the stage buffers (and sees the mailbox)
+    if constexpr (Tr::GROUP_K) nt = __builtin_amdgcn_readfirstlane(*mbox);
+    Job nxt = cur;
+    if (nt < total) {
+      nxt.init(args, coord(nt));
+      for (int s = 0; s < NS && s < nxt.nk; ++s) nxt.issue(s, arena);
+    }
+    // the next mailbox write follows a barrier of the next K loop, which
+    // has one whenever it has a stage
+    if (Tr::GROUP_K && (nt >= total || nxt.nk == 0)) lds_barrier();
+    cur.epilogue(acc, staging);
+    if (nt >= total) break;
+    cur = nxt;
+    tile = nt;
   }
 #endif
 }
 
-template <int KIND, int BM, int BN>
+template <int KIND, int BM, int BN, int NS, int BK>
 static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   const GemmGeom G = geom_of<KIND>(g.d, g.F);
   const int ntn = (G.N + BN - 1) / BN;
   int blocks;
-  dim3 grid;
   if constexpr (Traits<KIND>::GROUP_K) {
     // persistent workers over the 8 per-XCD tile counters (zeroed earlier on
     // the stream); a multiple of 8 workgroups so that every counter is served
     blocks = 256;
-    grid = dim3(blocks);
   } else {
     // persistent: one workgroup per CU, bounded by the worst-case tile count
     const int64_t worst = ((g.P_max + BM - 1) / BM + g.E_loc) * (int64_t)ntn;
     blocks = (int)(worst < 256 ? worst : 256);
-    grid = dim3(blocks);
   }
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<KIND, BM, BN>), grid, dim3(256), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<KIND, BM, BN, NS, BK>), dim3(blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
+// Stage depth (BK) and count (NS) per kind: 32 x 4 or 64 x 2 fill the LDS.
+#ifndef MOK_BK_UP
+#define MOK_NS_UP 4
+#define MOK_BK_UP 32
+#define MOK_NS_DOWN 4
+#define MOK_BK_DOWN 32
+#define MOK_NS_DH 4
+#define MOK_BK_DH 32
+#define MOK_NS_DX 4
+#define MOK_BK_DX 32
+#define MOK_NS_DW 4
+#define MOK_BK_DW 32
+#endif
+
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
-    case KIND_UP:   return run_bf16<KIND_UP, 256, 128>(g, s);
-    case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256>(g, s);
-    case KIND_DH:   return run_bf16<KIND_DH, 256, 256>(g, s);
-    case KIND_DX:   return run_bf16<KIND_DX, 256, 256>(g, s);
-    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256>(g, s);
-    case KIND_DW13: return run_bf16<KIND_DW13, 256, 256>(g, s);
+    case KIND_UP:   return run_bf16<KIND_UP, 256, 128, MOK_NS_UP, MOK_BK_UP>(g, s);
+    case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, MOK_NS_DOWN, MOK_BK_DOWN>(g, s);
+    case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH>(g, s);
+    case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX>(g, s);
+    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW>(g, s);
+    case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW>(g, s);
   }
   return hipErrorInvalidValue;
 }
-
 
 // ------------------------------------------------------------------ ring pipeline
 // Tile prefix of the local experts restricted to rows [r0, r1): expert i owns
@@ -582,27 +798,46 @@ __device__ void range_tile_prefix(const GroupedGemmArgs& g, int r0, int r1, int3
 }
 
 // Expert and row span of tile t of a range prefix (expert-major, m fastest).
-__device__ __forceinline__ void range_tile(const GroupedGemmArgs& g, const int32_t* s_tp, int ntn, int BM, int r0,
-                                           int r1, int t, int& e_loc, int& row0, int& row_end, int& n0, int BN) {
+__device__ __forceinline__ TileCoord range_tile(const GroupedGemmArgs& g, const int32_t* s_tp, int ntn, int BM,
+                                                int r0, int r1, int t, int BN) {
   int lo = 0, hi = g.E_loc - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_tp[mid] * ntn <= t) lo = mid; else hi = mid - 1;
   }
-  e_loc = lo;
-  const int mt_e = s_tp[e_loc + 1] - s_tp[e_loc];
-  const int local = t - s_tp[e_loc] * ntn;
-  n0 = (local / mt_e) * BN;
-  row0 = max(g.offsets[g.eb + e_loc], r0) + (local % mt_e) * BM;
-  row_end = min(g.offsets[g.eb + e_loc + 1], r1);
+  TileCoord c{};
+  c.e_loc = lo;
+  const int mt_e = s_tp[lo + 1] - s_tp[lo];
+  const int local = t - s_tp[lo] * ntn;
+  c.n0 = (local / mt_e) * BN;
+  c.row0 = max(g.offsets[g.eb + lo], r0) + (local % mt_e) * BM;
+  c.row_end = min(g.offsets[g.eb + lo + 1], r1);
+  return uniform(c);
+}
+
+// A whole tile with no overlap between tiles (issue, K loop, epilogue), with
+// four stage buffers (the ring kernel keeps its range tables in LDS too).
+constexpr int kRingStages = 4;
+template <int KIND, int BM, int BN>
+__device__ __forceinline__ void run_tile(const GroupedGemmArgs& g, const TileCoord& c, uint8_t* arena) {
+  using Job = TileJob<KIND, BM, BN, kRingStages, 32>;
+  Job job;
+  job.init(g, c);
+  for (int s = 0; s < kRingStages && s < job.nk; ++s) job.issue(s, arena);
+  f32x16_t acc[Job::NB][Job::FM][Job::FN];
+  job.mainloop(acc, arena);
+  lds_barrier();
+  job.epilogue(acc, arena + (kRingStages - 1) * Job::STAGE);  // the last stage buffer, free now
+  lds_barrier();
 }
 
 [[maybe_unused]] constexpr int kCopyRows = 16;  // rows per mover task
 
 __global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int kArena = 2 * (256 + 256) * kRowBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
+  using JobUp = TileJob<KIND_UP, 256, 128, kRingStages, 32>;
+  static_assert(JobUp::STAGE == TileJob<KIND_DOWN, 256, 256, kRingStages, 32>::STAGE, "one arena");
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kRingStages * JobUp::STAGE];
   __shared__ int32_t s_up[1025], s_dn[1025], s_wsum[4];
   const int tid = threadIdx.x;
   const GroupedGemmArgs& gu = a.up;
@@ -631,17 +866,10 @@ __global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a
         reinterpret_cast<u32x4_t*>((bf16_t*)a.ring_dst + (int64_t)(r - c0) * d)[c] = val;
       }
     } else if (t < n_cp + n_up) {
-      int e_loc, row0, row_end, n0;
-      range_tile(gu, s_up, ntn_up, 256, u0, u1, t - n_cp, e_loc, row0, row_end, n0, 128);
-      gemm_tile<KIND_UP, 256, 128>(gu, arena, __builtin_amdgcn_readfirstlane(e_loc),
-                                   __builtin_amdgcn_readfirstlane(row0), __builtin_amdgcn_readfirstlane(row_end), 0,
-                                   __builtin_amdgcn_readfirstlane(n0), 0);
+      run_tile<KIND_UP, 256, 128>(gu, range_tile(gu, s_up, ntn_up, 256, u0, u1, t - n_cp, 128), arena);
     } else {
-      int e_loc, row0, row_end, n0;
-      range_tile(a.down, s_dn, ntn_dn, 256, d0, d1, t - n_cp - n_up, e_loc, row0, row_end, n0, 256);
-      gemm_tile<KIND_DOWN, 256, 256>(a.down, arena, __builtin_amdgcn_readfirstlane(e_loc),
-                                     __builtin_amdgcn_readfirstlane(row0), __builtin_amdgcn_readfirstlane(row_end), 0,
-                                     __builtin_amdgcn_readfirstlane(n0), 0);
+      run_tile<KIND_DOWN, 256, 256>(a.down, range_tile(a.down, s_dn, ntn_dn, 256, d0, d1, t - n_cp - n_up, 256),
+                                    arena);
     }
   }
 #endif

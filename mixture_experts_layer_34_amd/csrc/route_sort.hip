@@ -208,13 +208,12 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
   }
   // Weight-gradient schedule: local experts ranked by descending row count
-  // (ties: lower index), then dealt to the 8 XCDs by greedy longest-first
-  // (each expert goes to the XCD with the least work so far, work = K steps
-  // of 64 rows + 2 per tile for its prologue and epilogue).  All tiles of an
-  // expert then run on one XCD and share its L2.  Output layout:
-  // expert_order[0..8] = first list position of each XCD (+ end),
-  // expert_order[16 + pos] = the experts, grouped by XCD, heaviest first.
-  __shared__ int32_t s_rank_e[1024], s_xcd[1024];
+  // (ties: lower index), with the prefix of their work in K stages of 32
+  // rows plus 2 per tile for its prologue and epilogue.  The weight-gradient
+  // GEMMs cut this heaviest-first tile sequence into 8 runs of equal work,
+  // one per XCD.  Output layout: expert_order[r] = expert of rank r,
+  // expert_order[E_loc + r] = work of ranks 0 .. r-1 (r = 0 .. E_loc).
+  __shared__ int32_t s_rank_e[1024];
   if (i_loc >= 0 && i_loc < E_loc) s_cnt[i_loc] = run;
   __syncthreads();
   if (i_loc >= 0 && i_loc < E_loc) {
@@ -224,40 +223,26 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
       rank += (cq > run || (cq == run && q < i_loc)) ? 1 : 0;
     }
     s_rank_e[rank] = i_loc;
+    expert_order[rank] = i_loc;
   }
   __syncthreads();
-  if (w == 0) {
-    int load = 0;  // lane x < 8: work dealt to XCD x
-    for (int q = 0; q < E_loc; ++q) {
-      const int c = (s_cnt[s_rank_e[q]] + 63) / 64 + 2;
-      int best = lane < 8 ? load : 0x7FFFFFFF, bx = lane;
+  {
+    // thread r: work of rank r, block-wide inclusive scan
+    const int r = threadIdx.x;
+    const int wr = r < E_loc ? (s_cnt[s_rank_e[r]] + 31) / 32 + 10 : 0;
+    int x = wr;
 #pragma unroll
-      for (int o = 4; o > 0; o >>= 1) {
-        const int ob = __shfl_xor(best, o, 64), ox = __shfl_xor(bx, o, 64);
-        if (ob < best || (ob == best && ox < bx)) { best = ob; bx = ox; }
-      }
-      const int x = __shfl(bx, 0, 64);
-      if (lane == x) load += c;
-      if (lane == 0) s_xcd[q] = x;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(x, o, 64);
+      if (lane >= o) x += u;
     }
-    // per-XCD counts -> first positions, then place in rank order
-    int cntx = 0;
-    for (int q = 0; q < E_loc; ++q) cntx += (lane < 8 && s_xcd[q] == lane) ? 1 : 0;
-    int incl = cntx;
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      const int u = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += u;
-    }
-    int pos = incl - cntx;  // lane x: next free position of XCD x
-    if (lane < 8) expert_order[lane] = pos;
-    if (lane == 7) expert_order[8] = incl;
-    for (int q = 0; q < E_loc; ++q) {
-      if (lane == s_xcd[q]) {
-        expert_order[16 + pos] = s_rank_e[q];
-        ++pos;
-      }
-    }
+    __syncthreads();  // wsum is reused
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int base = 0;
+    for (int q = 0; q < w; ++q) base += wsum[q];
+    if (r < E_loc) expert_order[E_loc + r + 1] = base + x;
+    if (r == 0) expert_order[E_loc] = 0;
   }
   if (i_loc >= 0 && i_loc < E_loc) {
 #pragma unroll
