@@ -92,6 +92,11 @@ __device__ __forceinline__ void sload_pair(const int32_t* p, bool valid1, int32_
                : "memory");
 }
 
+__device__ __forceinline__ i32x4_t sload4(const int32_t* p) {  // p 16-byte aligned
+  i32x4_t v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
 __device__ __forceinline__ int32_t sload(const int32_t* p) {
   int32_t v;
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
@@ -149,6 +154,11 @@ struct TileJob {
   struct Frags {
     bf16x8_t a[FM];
     bf16x8_t b[NB][FN];
+  };
+  // DH epilogue operands of one round (the saved A and B at this lane's four
+  // 8-column pieces), loaded a round ahead.
+  struct SavedAB {
+    u32x4_t a[4], b[4];
   };
 
   const GroupedGemmArgs* args;
@@ -420,8 +430,32 @@ struct TileJob {
   // Epilogue.  bf16 outputs go through this wave's own 8 KB of `staging`
   // (32 KB for the workgroup): 16-byte row-contiguous stores.  fp32 weight
   // gradients are stored straight from the accumulators: each half-wave
-  // writes 32 consecutive floats of one row, a whole 128-byte line.
-  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging) const {
+  // writes 32 consecutive floats of one row, a whole 128-byte line (measured
+  // faster than 16-byte stores from transposed accumulators, whose
+  // instructions each touch 32 rows).
+  // Saved A and B of DH epilogue round (i, jp); rows past the expert read as zero.
+  __device__ __forceinline__ void load_saved(int i, int jp, SavedAB& p) const {
+    const GroupedGemmArgs& a = *args;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int seg = q * 64 + lane;
+      const int row = c.row0 + wm * TM + i * 32 + (seg >> 3), col = c.n0 + wn * TN + jp * 64 + (seg & 7) * 8;
+      const bool ok = row < c.row_end && col < G.N;
+      const int64_t o = ok ? (int64_t)row * G.N + col : 0;
+      p.a[q] = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o) : u32x4_t{0u, 0u, 0u, 0u};
+      p.b[q] = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // First round's epilogue loads, issued before the next tile's copies so
+  // that waiting for them does not wait for those copies too.
+  __device__ __forceinline__ void epilogue_prefetch(SavedAB& p0) const {
+    if constexpr (KIND == KIND_DH) load_saved(0, 0, p0);
+  }
+
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging,
+                                           SavedAB& p0) const {
+    SavedAB p1;
     float* ep = reinterpret_cast<float*>(staging + wid * 8192);
     const GroupedGemmArgs& a = *args;
     const int wrow0 = wm * TM, wcol0 = wn * TN;
@@ -489,6 +523,11 @@ struct TileJob {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int jp = 0; jp < FN / 2; ++jp) {
+          const int t = i * (FN / 2) + jp;  // round
+          SavedAB& cur = (t & 1) ? p1 : p0;
+          if constexpr (KIND == KIND_DH) {
+            if (t + 1 < FM * (FN / 2)) load_saved((t + 1) / (FN / 2), (t + 1) % (FN / 2), (t & 1) ? p0 : p1);
+          }
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -510,8 +549,7 @@ struct TileJob {
                 const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 const int64_t o = (int64_t)row * G.N + col;
                 if constexpr (KIND == KIND_DH) {
-                  const u32x4_t av = *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o);
-                  const u32x4_t bv = *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o);
+                  const u32x4_t av = cur.a[q], bv = cur.b[q];
                   u32x4_t da, db;
 #pragma unroll
                   for (int t = 0; t < 4; ++t) {
@@ -604,17 +642,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     // the XCD's eighth of the total.
     ntm_k = (G.M + BM - 1) / BM;
     const int T = NZ * ntm_k * ntn;
-    const int32_t* wp = args.expert_order + E_loc;  // work prefix over ranks
+    const int32_t* rk = args.expert_order;  // per rank {expert, row0, row_end, work prefix}
     auto bound = [&](int x) -> int {
       if (x <= 0 || E_loc == 0) return 0;
       if (x >= 8) return E_loc * T;
-      const int64_t target = (int64_t)T * sload(wp + E_loc) * x / 8;
+      const int64_t target = (int64_t)T * sload(rk + 4 * E_loc + 3) * x / 8;
       int lo = 0, hi = E_loc - 1;  // last rank whose tiles start at or before target
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)T * sload(wp + mid) <= target) lo = mid; else hi = mid - 1;
+        if ((int64_t)T * sload(rk + 4 * mid + 3) <= target) lo = mid; else hi = mid - 1;
       }
-      const int w0 = sload(wp + lo), w1 = sload(wp + lo + 1);
+      const int w0 = sload(rk + 4 * lo + 3), w1 = sload(rk + 4 * lo + 7);
       const int64_t j = (target - (int64_t)T * w0) / (w1 - w0);  // whole tiles of rank lo by target
       return lo * T + (int)(j < T ? j : T);
     };
@@ -662,16 +700,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     } else {
       const int per_z = ntm_k * ntn;
       const int g = tbeg + tile;  // position in the heaviest-first sequence
-      c.e_loc = sload(args.expert_order + g / (NZ * per_z));
+      const i32x4_t rec = sload4(args.expert_order + 4 * (g / (NZ * per_z)));
+      c.e_loc = rec[0];
+      c.row0 = rec[1];
+      c.row_end = rec[2];
       const int rem = g % (NZ * per_z);
       c.z = rem / per_z;
       int mt, nt;
       tile_mn(rem % per_z, ntm_k, ntn, mt, nt);
       c.m0 = mt * BM;
       c.n0 = nt * BN;
-      const int e = args.eb + c.e_loc;
-      c.row0 = sload(args.offsets + e);
-      c.row_end = sload(args.offsets + e + 1);
     }
     return uniform(c);
   };
@@ -698,6 +736,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     }
     lds_barrier();  // every wave is done with the stage buffers (and sees the mailbox)
     if constexpr (Tr::GROUP_K) nt = __builtin_amdgcn_readfirstlane(*mbox);
+    typename Job::SavedAB pre;
+    cur.epilogue_prefetch(pre);
     Job nxt = cur;
     if (nt < total) {
       nxt.init(args, coord(nt));
@@ -706,7 +746,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     // the next mailbox write follows a barrier of the next K loop, which
     // has one whenever it has a stage
     if (Tr::GROUP_K && (nt >= total || nxt.nk == 0)) lds_barrier();
-    cur.epilogue(acc, staging);
+    cur.epilogue(acc, staging, pre);
     if (nt >= total) break;
     cur = nxt;
     tile = nt;
@@ -827,7 +867,9 @@ __device__ __forceinline__ void run_tile(const GroupedGemmArgs& g, const TileCoo
   f32x16_t acc[Job::NB][Job::FM][Job::FN];
   job.mainloop(acc, arena);
   lds_barrier();
-  job.epilogue(acc, arena + (kRingStages - 1) * Job::STAGE);  // the last stage buffer, free now
+  typename Job::SavedAB pre;
+  job.epilogue_prefetch(pre);
+  job.epilogue(acc, arena + (kRingStages - 1) * Job::STAGE, pre);  // the last stage buffer, free now
   lds_barrier();
 }
 

@@ -76,7 +76,7 @@ void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_
   s->topk_gate = o;    o = align256(o + Tk * 4);
   s->offsets = o;      o = align256(o + ((size_t)c.E + 1) * 4);
   *tile_prefix_off = o; o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
-  *expert_order_off = o; o = align256(o + (2 * E_loc + 1) * 4);
+  *expert_order_off = o; o = align256(o + (size_t)(E_loc + 1) * 16);
   s->row_of_pair = o;  o = align256(o + Tk * 4);
   s->pair_of_row = o;  o = align256(o + Tk * 4);
   s->A = o;            o = align256(o + Tk * c.ffn * A);

@@ -73,7 +73,7 @@ struct GroupedGemmArgs {
   const void* B1;         // second weights (W3) where used
   const int32_t* offsets;
   const int32_t* tile_prefix;
-  const int32_t* expert_order;  // [r] local expert of rank r (heaviest first), [E_loc + r] work prefix
+  const int32_t* expert_order;  // int4 per rank (heaviest first): {expert, row0, row_end, work prefix}
   int32_t* queue;               // 8 per-XCD tile counters of a weight-gradient kind (zeroed on device)
   int eb, E_loc;
   int d, F;

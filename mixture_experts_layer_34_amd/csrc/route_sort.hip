@@ -209,12 +209,16 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
   }
   // Weight-gradient schedule: local experts ranked by descending row count
   // (ties: lower index), with the prefix of their work in K stages of 32
-  // rows plus 2 per tile for its prologue and epilogue.  The weight-gradient
-  // GEMMs cut this heaviest-first tile sequence into 8 runs of equal work,
-  // one per XCD.  Output layout: expert_order[r] = expert of rank r,
-  // expert_order[E_loc + r] = work of ranks 0 .. r-1 (r = 0 .. E_loc).
-  __shared__ int32_t s_rank_e[1024];
-  if (i_loc >= 0 && i_loc < E_loc) s_cnt[i_loc] = run;
+  // rows plus 10 per tile (a tile's fixed set-up and epilogue cost about as
+  // much as ten stages).  The weight-gradient GEMMs cut this heaviest-first
+  // tile sequence into 8 runs of equal work, one per XCD.  Output: one
+  // 16-byte record per rank r < E_loc, {local expert, first row, end row,
+  // work of ranks 0 .. r-1}, and record E_loc = {0, 0, 0, total work}.
+  __shared__ int32_t s_rank_e[1024], s_off[1024];
+  if (i_loc >= 0 && i_loc < E_loc) {
+    s_cnt[i_loc] = run;
+    s_off[i_loc] = off;
+  }
   __syncthreads();
   if (i_loc >= 0 && i_loc < E_loc) {
     int rank = 0;
@@ -223,13 +227,13 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
       rank += (cq > run || (cq == run && q < i_loc)) ? 1 : 0;
     }
     s_rank_e[rank] = i_loc;
-    expert_order[rank] = i_loc;
   }
   __syncthreads();
   {
     // thread r: work of rank r, block-wide inclusive scan
     const int r = threadIdx.x;
-    const int wr = r < E_loc ? (s_cnt[s_rank_e[r]] + 31) / 32 + 10 : 0;
+    const int er = r < E_loc ? s_rank_e[r] : 0;
+    const int wr = r < E_loc ? (s_cnt[er] + 31) / 32 + 10 : 0;
     int x = wr;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -241,8 +245,18 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     __syncthreads();
     int base = 0;
     for (int q = 0; q < w; ++q) base += wsum[q];
-    if (r < E_loc) expert_order[E_loc + r + 1] = base + x;
-    if (r == 0) expert_order[E_loc] = 0;
+    if (r < E_loc) {
+      int32_t* rec = expert_order + 4 * r;
+      rec[0] = er;
+      rec[1] = s_off[er];
+      rec[2] = s_off[er] + s_cnt[er];
+      rec[3] = base + x - wr;
+    }
+    if (r == E_loc - 1 || (E_loc == 0 && r == 0)) {
+      int32_t* rec = expert_order + 4 * E_loc;
+      rec[0] = rec[1] = rec[2] = 0;
+      rec[3] = E_loc ? base + x : 0;
+    }
   }
   if (i_loc >= 0 && i_loc < E_loc) {
 #pragma unroll
