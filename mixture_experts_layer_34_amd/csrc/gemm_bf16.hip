@@ -43,6 +43,7 @@
 #include "mok_device.h"
 #include "mok_internal.h"
 #include "gemm_common.h"
+#include "gemm_pipe.h"
 
 namespace mok {
 
@@ -50,69 +51,6 @@ namespace mok {
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-// K-contiguous stage layout: physical 16-byte chunk of logical chunk c in
-// row r, for rows of BK = 32 (64 bytes, 4 chunks) or 64 (128 bytes, 8
-// chunks).  Sixteen consecutive rows read at one logical chunk hit 16
-// distinct 16-byte bank groups (64 banks), and any 8 consecutive rows hit 8
-// distinct ones (32 banks).
-template <int BK>
-__device__ __forceinline__ int swz_k(int r, int c) {
-  if constexpr (BK == 32) return c ^ (((r >> 1) ^ (r >> 2)) & 3);
-  else return c ^ ((r ^ (r >> 3)) & 7);
-}
-// M/N-contiguous stage layout: physical 64-byte chunk of logical chunk c in
-// the row of k = r.  A transposing read touches rows k..k+3 at one chunk:
-// they land in four distinct 64-byte bank groups.
-__device__ __forceinline__ int swz_mn(int r, int c) { return c ^ (r & 3); }
-
-// Wait until at most N of this wave's vector memory operations are
-// outstanding and its LDS reads have returned, then meet the workgroup.  The
-// LDS wait is also issued through the builtin so that the compiler's own
-// counter model knows the reads have returned (it does not look inside asm).
-constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), vmcnt and expcnt not waited on
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Two consecutive int32 at a wave-uniform address through the scalar cache
-// (p[1] is read only when valid1): no vector-memory counter is touched, so
-// the copies in flight are not waited for.
-__device__ __forceinline__ void sload_pair(const int32_t* p, bool valid1, int32_t& v0, int32_t& v1) {
-  const int32_t* p1 = valid1 ? p + 1 : p;
-  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-               : "=s"(v0), "=s"(v1)
-               : "s"(p), "s"(p1)
-               : "memory");
-}
-
-__device__ __forceinline__ i32x4_t sload4(const int32_t* p) {  // p 16-byte aligned
-  i32x4_t v;
-  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ int32_t sload(const int32_t* p) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-
-// Block until this wave has at most `later` stages of D copies outstanding
-// (later <= MAXL), then meet the workgroup.
-template <int D, int MAXL>
-__device__ __forceinline__ void wait_stages(int later) {
-  if (MAXL >= 4 && later >= 4) vm_wait_barrier<(MAXL >= 4 ? 4 : 0) * D>();
-  else if (MAXL >= 3 && later >= 3) vm_wait_barrier<(MAXL >= 3 ? 3 : 0) * D>();
-  else if (MAXL >= 2 && later >= 2) vm_wait_barrier<(MAXL >= 2 ? 2 : 0) * D>();
-  else if (later >= 1) vm_wait_barrier<D>();
-  else vm_wait_barrier<0>();
-}
 
 // One operand's share of an LDS stage: ROWS tile rows (M or N) by BK.
 template <bool MN, int ROWS, int BK>
@@ -126,10 +64,6 @@ struct OpGeo {
   static constexpr int KRPI = 64 / KLPR;         // K-contiguous: rows per DMA instruction
   static_assert(INST >= 1 && BYTES % 4096 == 0, "stage share must fill whole wave DMA instructions");
   static_assert(!MN || (ROWS % 128 == 0 && RPI >= 1), "M/N-contiguous tile rows");
-};
-
-struct TileCoord {
-  int e_loc, row0, row_end, m0, n0, z;
 };
 
 // One output tile: its DMA sources, K loop and epilogue, with NS LDS stage
@@ -239,6 +173,11 @@ struct TileJob {
 
   // Issue the copies of stage s into LDS stage buffer s % NS.
   __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
+
+  // The first NS stages.
+  __device__ __forceinline__ void prologue(uint8_t* arena) const {
+    for (int s = 0; s < NS && s < nk; ++s) issue(s, arena);
+  }
 
   // Copies [Q0, Q1) of the D of a stage (A's first, then B's), so that a
   // stage's copies can be spread between MFMAs.
@@ -585,31 +524,6 @@ struct TileJob {
   }
 };
 
-// Grouped raster inside one expert: groups of GM m-tiles, n-tiles outer and
-// m-tiles inner within a group, so that a run of consecutive tiles forms a
-// GM x (run / GM) block that reuses both operands.
-__device__ __forceinline__ void tile_mn(int local, int mt, int ntn, int& m, int& n) {
-  constexpr int GM = 4;
-  const int g = local / (GM * ntn);
-  const int gm0 = g * GM;
-  const int gsz = mt - gm0 < GM ? mt - gm0 : GM;
-  const int rem = local - g * GM * ntn;
-  n = rem / gsz;
-  m = gm0 + rem % gsz;
-}
-
-// The tile coordinates are wave-uniform; say so, so that addresses and
-// buffer resources live in scalar registers.
-__device__ __forceinline__ TileCoord uniform(TileCoord c) {
-  c.e_loc = __builtin_amdgcn_readfirstlane(c.e_loc);
-  c.row0 = __builtin_amdgcn_readfirstlane(c.row0);
-  c.row_end = __builtin_amdgcn_readfirstlane(c.row_end);
-  c.m0 = __builtin_amdgcn_readfirstlane(c.m0);
-  c.n0 = __builtin_amdgcn_readfirstlane(c.n0);
-  c.z = __builtin_amdgcn_readfirstlane(c.z);
-  return c;
-}
-
 // Persistent grouped GEMM.  LDS: the NS stage buffers, then either the
 // 32 KB bf16 epilogue staging area (row kinds; 160 KB in all) or the mailbox
 // through which wave 0 hands the tile taken from the queue to the workgroup
@@ -725,7 +639,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
   if (tile >= total) return;
   Job cur;
   cur.init(args, coord(tile));
-  for (int s = 0; s < NS && s < cur.nk; ++s) cur.issue(s, arena);
+  cur.prologue(arena);
   f32x16_t acc[Job::NB][Job::FM][Job::FN];
   while (true) {
     take();
@@ -741,7 +655,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     Job nxt = cur;
     if (nt < total) {
       nxt.init(args, coord(nt));
-      for (int s = 0; s < NS && s < nxt.nk; ++s) nxt.issue(s, arena);
+      nxt.prologue(arena);
     }
     // the next mailbox write follows a barrier of the next K loop, which
     // has one whenever it has a stage
@@ -863,7 +777,7 @@ __device__ __forceinline__ void run_tile(const GroupedGemmArgs& g, const TileCoo
   using Job = TileJob<KIND, BM, BN, kRingStages, 32>;
   Job job;
   job.init(g, c);
-  for (int s = 0; s < kRingStages && s < job.nk; ++s) job.issue(s, arena);
+  job.prologue(arena);
   f32x16_t acc[Job::NB][Job::FM][Job::FN];
   job.mainloop(acc, arena);
   lds_barrier();

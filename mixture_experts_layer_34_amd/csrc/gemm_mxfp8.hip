@@ -8,148 +8,181 @@
 // section 02): X rows are quantised by the dispatch gather, H by this UP
 // epilogue, and the scaled MFMA consumes both without dequantising.
 //
-// A K step is 128 fp8 values = 128 bytes per row, so the LDS tiles, the XOR
-// swizzle, the direct-to-LDS loads and the tile scheduling are those of the
-// BF16 kernel.  Scaled-MFMA operand layout on gfx950 (checked on the device):
-// for each 64-wide K sub-step, lane l holds row l % 32; with h = l / 32 its
-// bytes 0-15 are K [16h, 16h + 16) and bytes 16-31 are K [32 + 16h, +16), and
-// the scale it supplies covers the 32-block h of the sub-step.
+// The pipeline is the bf16 one (gemm_bf16.hip) with one-byte elements: a
+// stage is 64 K values = one scaled-MFMA K step = 64-byte LDS rows, four
+// stages in flight, the same swizzle, direct-to-LDS copies, barrier placement
+// and tile schedule.  Each stage also carries the two E8M0 bytes of every
+// tile row (2-byte copies that land zero-extended in one LDS dword per row).
+// Scaled-MFMA operand layout on gfx950 (checked on the device): lane l holds
+// row l % 32; with h = l / 32 its bytes 0-15 are K [16h, 16h + 16) and bytes
+// 16-31 are K [32 + 16h, +16), and the scale it supplies covers the 32-block
+// h of the step — byte h of the row's scale dword, shifted down to byte 0.
 #include "mok_device.h"
 #include "mok_internal.h"
 #include "gemm_common.h"
+#include "gemm_pipe.h"
 
 namespace mok {
 
-namespace {
+constexpr int kMxNS = 5;     // LDS stage buffers
+constexpr int kMxBK = 64;    // K (bytes) per stage
 
-[[maybe_unused]] constexpr int kBKq = 128;          // K per stage (fp8 elements = bytes)
-[[maybe_unused]] constexpr int kRowB = 128;         // LDS row bytes
+// One MXFP8 output tile (UP: 256 rows x 64 columns of W1 and W3; DOWN:
+// 256 x 128): 128 accumulators per lane, which leaves the register file room
+// for the fragments (at one byte per element this tile moves the same L2
+// bytes per FLOP as the 256 x 256 bf16 tile).  Wave-uniform members except
+// the per-lane DMA offsets.
+template <int KIND>
+struct MxJob {
+  static constexpr int NB = KIND == KIND_UP ? 2 : 1;
+  static constexpr int BM = 256, BN = KIND == KIND_UP ? 64 : 128, BROWS = NB * BN;
+  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  static constexpr int A_BYTES = BM * kMxBK, B_BYTES = BROWS * kMxBK;
+  static constexpr int SCA = A_BYTES + B_BYTES;       // A scale dwords: row r at dword r
+  static constexpr int SCB = SCA + BM * 4;            // B scale dwords: row r at dword 64 (r / 32) + r % 32
+  static constexpr int STAGE = SCB + 256 * 4;
+  static constexpr int IA = A_BYTES / 1024 / 4, IB = B_BYTES / 1024 / 4;  // 16-byte copies per wave
+  static constexpr int D = IA + IB + 2;               // + one 2-byte copy per wave for each scale set
+  static_assert(BM == 256 && BROWS == 128, "scale copies: A 64 rows, B 32 rows per wave");
+  static_assert((kMxNS - 1) * D <= 63, "vmcnt holds at most 63");
 
-[[maybe_unused]] __device__ __forceinline__ int swzq(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+  struct AFrag {  // one 32-row block of A for one K step, with its scales
+    i32x8_t v;
+    uint32_t s;
+  };
+  struct BFrags {  // all B blocks of a wave for one K step
+    i32x8_t v[NB][FN];
+    uint32_t s[NB][FN];
+  };
 
-[[maybe_unused]] __device__ __forceinline__ void tile_mn_q(int local, int mt, int ntn, int& m, int& n) {
-  constexpr int GM = 4;
-  const int g = local / (GM * ntn);
-  const int gm0 = g * GM;
-  const int gsz = mt - gm0 < GM ? mt - gm0 : GM;
-  const int rem = local - g * GM * ntn;
-  n = rem / gsz;
-  m = gm0 + rem % gsz;
-}
+  const GroupedGemmArgs* args;
+  int K, N, KS;
+  TileCoord c;
+  int wid, lane, wm, wn, nk;
+  i32x4_t rsA, rsB0, rsB1, rsSA, rsSB0, rsSB1;
+  uint32_t offA[IA], offB[IB], offSA, offSB;
 
-}  // namespace
-
-template <int KIND, int BM, int BN>
-__global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs args) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NB = KIND == KIND_UP ? 2 : 1;
-  constexpr int BROWS = NB * BN;
-  constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-  constexpr int DMA_A = BM / 8 / 4, DMA_B = BROWS / 8 / 4;
-  constexpr int kArena = 2 * (BM + BROWS) * kRowB;
-  static_assert(kArena >= 4 * 32768, "epilogue staging needs 32 KB per wave");
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kArena];
-  __shared__ int32_t s_tp[1025];
-  uint8_t (*sA)[BM * kRowB] = reinterpret_cast<uint8_t (*)[BM * kRowB]>(arena);
-  uint8_t (*sB)[BROWS * kRowB] = reinterpret_cast<uint8_t (*)[BROWS * kRowB]>(arena + 2 * BM * kRowB);
-
-  // K (contraction) and N (output columns) of this kind
-  const int K = KIND == KIND_UP ? args.d : args.F;
-  const int N = KIND == KIND_UP ? args.F : args.d;
-  const int KS = K / 32;                      // scale bytes per row
-  const int64_t b_estride = (int64_t)args.F * args.d;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps DMA operands scalar
-  const int wm = wid / 2, wn = wid % 2;
-  const uint8_t* __restrict__ A = (const uint8_t*)args.A;
-  const uint8_t* __restrict__ B0 = (const uint8_t*)args.B0;
-  const uint8_t* __restrict__ B1 = (const uint8_t*)args.B1;
-  const int E_loc = args.E_loc;
-  const int ntn = (N + BN - 1) / BN;
-
-  const int32_t* tp = args.tile_prefix + 2 * (E_loc + 1);  // 256-row tiles
-  for (int i = tid; i <= E_loc; i += 256) s_tp[i] = tp[i];
-  __syncthreads();
-  const int total = s_tp[E_loc] * ntn;
-  const int G_ = gridDim.x;
-  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
-
-  for (int tile = vb; tile < total; tile += G_) {
-    int lo = 0, hi = E_loc - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_tp[mid] * ntn <= tile) lo = mid; else hi = mid - 1;
-    }
-    int e_loc = lo, mt, nt;
-    tile_mn_q(tile - s_tp[e_loc] * ntn, s_tp[e_loc + 1] - s_tp[e_loc], ntn, mt, nt);
-    int n0 = nt * BN;
-    int row0 = args.offsets[args.eb + e_loc] + mt * BM;
-    int row_end = args.offsets[args.eb + e_loc + 1];
-    e_loc = __builtin_amdgcn_readfirstlane(e_loc);
-    n0 = __builtin_amdgcn_readfirstlane(n0);
-    row0 = __builtin_amdgcn_readfirstlane(row0);
-    row_end = __builtin_amdgcn_readfirstlane(row_end);
-    const int nk = K / kBKq;
-
-    // direct-to-LDS sources (rows past the tile's data read as zero)
-    const int rows = row_end - row0 < BM ? row_end - row0 : BM;
-    const i32x4_t rsA = make_rsrc(A + (int64_t)row0 * K, (uint32_t)(rows * K));
-    const int nb_rows = N - n0 < BN ? N - n0 : BN;
-    const uint8_t* b0 = B0 + (int64_t)e_loc * b_estride + (int64_t)n0 * K;
-    const i32x4_t rsB0 = make_rsrc(b0, (uint32_t)(nb_rows * K));
-    const uint8_t* b1 = (NB == 2 ? B1 : B0) + (int64_t)e_loc * b_estride + (int64_t)n0 * K;
-    const i32x4_t rsB1 = make_rsrc(b1, (uint32_t)(nb_rows * K));
-    uint32_t offA[DMA_A], offB[DMA_B];
+  __device__ __forceinline__ void init(const GroupedGemmArgs& a, const TileCoord& tc) {
+    args = &a;
+    K = KIND == KIND_UP ? a.d : a.F;
+    N = KIND == KIND_UP ? a.F : a.d;
+    KS = K / 32;
+    c = tc;
+    lane = threadIdx.x & 63;
+    wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wm = wid >> 1;
+    wn = wid & 1;
+    nk = K / kMxBK;
+    const int rows = c.row_end - c.row0 < BM ? c.row_end - c.row0 : BM;
+    const int nb_rows = N - c.n0 < BN ? N - c.n0 : BN;
+    const int64_t wst = (int64_t)a.F * a.d;  // bytes per expert of one weight matrix
+    rsA = make_rsrc((const uint8_t*)a.A + (int64_t)c.row0 * K, (uint32_t)(rows * K));
+    rsB0 = make_rsrc((const uint8_t*)a.B0 + c.e_loc * wst + (int64_t)c.n0 * K, (uint32_t)(nb_rows * K));
+    rsB1 = make_rsrc((const uint8_t*)(NB == 2 ? a.B1 : a.B0) + c.e_loc * wst + (int64_t)c.n0 * K,
+                     (uint32_t)(nb_rows * K));
+    rsSA = make_rsrc(a.a_scale + (int64_t)c.row0 * KS, (uint32_t)(rows * KS));
+    rsSB0 = make_rsrc(a.b_scale0 + ((int64_t)c.e_loc * N + c.n0) * KS, (uint32_t)(nb_rows * KS));
+    rsSB1 = make_rsrc((NB == 2 ? a.b_scale1 : a.b_scale0) + ((int64_t)c.e_loc * N + c.n0) * KS,
+                      (uint32_t)(nb_rows * KS));
 #pragma unroll
-    for (int q = 0; q < DMA_A; ++q) {
-      const int r = (wid * DMA_A + q) * 8 + (lane >> 3);
-      offA[q] = (uint32_t)(r * K + swzq(r, lane & 7) * 16);
+    for (int q = 0; q < IA; ++q) {
+      const int r = (wid * IA + q) * 16 + (lane >> 2);
+      offA[q] = (uint32_t)(r * K + swz_k<32>(r, lane & 3) * 16);
     }
 #pragma unroll
-    for (int q = 0; q < DMA_B; ++q) {
-      const int r = (wid * DMA_B + q) * 8 + (lane >> 3);
+    for (int q = 0; q < IB; ++q) {
+      const int r = (wid * IB + q) * 16 + (lane >> 2);
       const int rl = (NB == 2 && r >= BN) ? r - BN : r;
-      offB[q] = (uint32_t)(rl * K + swzq(r, lane & 7) * 16);
+      offB[q] = (uint32_t)(rl * K + swz_k<32>(r, lane & 3) * 16);
     }
-    // scale rows of this lane's fragments (clamped into the data rows)
-    const uint8_t* sa_rows[FM];
-    const uint8_t* sb_rows[NB][FN];
+    // scale copies: wave w brings A rows 64 w .. 64 w + 63 and, in lanes 0-31,
+    // B rows 32 w .. 32 w + 31 (UP: of W1 for w < 2, of W3 after); lanes 32-63
+    // of the B copy read past the resource and land zero in unused dwords
+    offSA = (uint32_t)((wid * 64 + lane) * KS);
+    const int rb = wid * 32 + lane;
+    offSB = lane < 32 ? (uint32_t)(((NB == 2 && rb >= BN) ? rb - BN : rb) * KS) : 0xFFFFFFF0u;
+  }
+
+  // Copies [Q0, Q1) of stage s (A data, B data, A scales, B scales).
+  template <int Q0, int Q1>
+  __device__ __forceinline__ void issue_part(int s, uint8_t* arena) const {
+    uint8_t* st = arena + (s % kMxNS) * STAGE;
+    const int k0 = s * kMxBK;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      int r = row0 + wm * TM + i * 32 + (lane & 31);
-      r = r < row_end ? r : row_end - 1;
-      sa_rows[i] = args.a_scale + (int64_t)r * KS;
-    }
+    for (int q = 0; q < IA; ++q)
+      if (q >= Q0 && q < Q1) dma_b128(rsA, lds_addr(st + (wid * IA + q) * 1024), offA[q], k0);
+#pragma unroll
+    for (int q = 0; q < IB; ++q)
+      if (IA + q >= Q0 && IA + q < Q1)
+        dma_b128((NB == 2 && (wid * IB + q) * 16 >= BN) ? rsB1 : rsB0, lds_addr(st + A_BYTES + (wid * IB + q) * 1024),
+                 offB[q], k0);
+    if (IA + IB >= Q0 && IA + IB < Q1) dma_u16(rsSA, lds_addr(st + SCA + wid * 256), offSA, k0 / 32);
+    if (IA + IB + 1 >= Q0 && IA + IB + 1 < Q1)
+      dma_u16((NB == 2 && wid * 32 >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB, k0 / 32);
+  }
+  __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
+
+  __device__ __forceinline__ void read_a(int buf, int i, const uint8_t* arena, AFrag& f) const {
+    const uint8_t* st = arena + buf * STAGE;
+    const int h = lane >> 5;
+    const int r = wm * TM + i * 32 + (lane & 31);
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, h) * 16);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, 2 + h) * 16);
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.s = *reinterpret_cast<const uint32_t*>(st + SCA + r * 4) >> (8 * h);
+  }
+  __device__ __forceinline__ void read_b(int buf, const uint8_t* arena, BFrags& f) const {
+    const uint8_t* st = arena + buf * STAGE;
+    const int h = lane >> 5;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        int n = n0 + wn * TN + j * 32 + (lane & 31);
-        n = n < N ? n : N - 1;
-        sb_rows[b][j] = (b ? args.b_scale1 : args.b_scale0) + ((int64_t)e_loc * N + n) * KS;
+        const int r = b * BN + wn * TN + j * 32 + (lane & 31);
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, h) * 16);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, 2 + h) * 16);
+        f.v[b][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.s[b][j] = *reinterpret_cast<const uint32_t*>(st + SCB + ((r >> 5) * 64 + (r & 31)) * 4) >> (8 * h);
       }
-    const int hsh = 8 * (lane >> 5);  // this lane's scale byte within each pair of 32-blocks
-    uint32_t scA[FM], scB[NB][FN];
-    auto load_scales = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) scA[i] = *reinterpret_cast<const uint32_t*>(sa_rows[i] + k0 / 32) >> hsh;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) scB[b][j] = *reinterpret_cast<const uint32_t*>(sb_rows[b][j] + k0 / 32) >> hsh;
-    };
-    auto issue = [&](int k0, int buf) {
-#pragma unroll
-      for (int q = 0; q < DMA_A; ++q)
-        dma_b128(rsA, lds_addr(&sA[buf][(wid * DMA_A + q) * 1024]), offA[q], k0);
-#pragma unroll
-      for (int q = 0; q < DMA_B; ++q) {
-        dma_b128((NB == 2 && (wid * DMA_B + q) * 8 >= BN) ? rsB1 : rsB0,
-                 lds_addr(&sB[buf][(wid * DMA_B + q) * 1024]), offB[q], k0);
-      }
-    };
+  }
 
-    f32x16_t acc[NB][FM][FN];
+  // MFMAs of row block i (all B blocks), [g, g + 1) / NG of them.
+  template <int g, int NG>
+  __device__ __forceinline__ static void mma_row(f32x16_t (&acc)[NB][FM][FN], int i, const AFrag& fa,
+                                                 const BFrags& fb) {
+    constexpr int TOT = NB * FN, L0 = g * TOT / NG, L1 = (g + 1) * TOT / NG;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int L = b * FN + j;
+        if (L >= L0 && L < L1)
+          acc[b][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa.v, fb.v[b][j], acc[b][i][j], 0, 0, 0,
+                                                                          (int)fa.s, 0, (int)fb.s[b][j]);
+      }
+  }
+
+  // Last row block's MFMAs with stage s's copies spread between them.
+  template <int G, int NG>
+  __device__ __forceinline__ void mma_issue(f32x16_t (&acc)[NB][FM][FN], const AFrag& fa, const BFrags& fb,
+                                            bool copy, int s, uint8_t* arena) const {
+    if constexpr (G < NG) {
+      if (copy) issue_part<G * D / NG, (G + 1) * D / NG>(s, arena);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_row<G, NG>(acc, FM - 1, fa, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_issue<G + 1, NG>(acc, fa, fb, copy, s, arena);
+    }
+  }
+
+  // K loop, one MFMA K step per stage.  A stage's B blocks are read during the
+  // previous stage; its A row blocks are read one block ahead of the MFMAs
+  // that use them.  Once a wave has read the stage's last A block, it waits
+  // for the next stage and meets the workgroup (every wave is then done with
+  // this stage's buffer), reads the next stage's B blocks and first A block,
+  // and runs the last row block's MFMAs with the copies of stage kt + NS
+  // spread between them.  On entry stages 0 .. min(nk, NS) - 1 are issued.
+  __device__ __forceinline__ void mainloop(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena) const {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -158,166 +191,210 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
-
-    issue(0, 0);
-    load_scales(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      uint32_t cA[FM], cB[NB][FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) cA[i] = scA[i];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) cB[b][j] = scB[b][j];
-      if (kt + 1 < nk) {
-        issue((kt + 1) * kBKq, buf ^ 1);
-        load_scales((kt + 1) * kBKq);
-      }
-      const uint8_t* a_s = sA[buf];
-      const uint8_t* b_s = sB[buf];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = ks * 4 + (lane >> 5), c1 = c0 + 2;
-        i32x8_t af[FM], bfr[NB][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 32 + (lane & 31);
-          const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(&a_s[r * kRowB + swzq(r, c0) * 16]);
-          const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(&a_s[r * kRowB + swzq(r, c1) * 16]);
-          af[i] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                          (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int r = b * BN + wn * TN + j * 32 + (lane & 31);
-            const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(&b_s[r * kRowB + swzq(r, c0) * 16]);
-            const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(&b_s[r * kRowB + swzq(r, c1) * 16]);
-            bfr[b][j] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-          }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              if (ks == 0)
-                acc[b][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[b][j], acc[b][i][j], 0, 0,
-                                                                                0, (int)cA[i], 0, (int)cB[b][j]);
-              else
-                acc[b][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[b][j], acc[b][i][j], 0, 0,
-                                                                                2, (int)cA[i], 2, (int)cB[b][j]);
-            }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+    if (nk <= 0) return;
+    wait_stages<D, kMxNS - 1>(nk - 1 < kMxNS - 1 ? nk - 1 : kMxNS - 1);
+    BFrags b0, b1;
+    AFrag a0, a1;
+    read_b(0, arena, b0);
+    read_a(0, 0, arena, a0);
+    // two stages per iteration so that the roles of b0 and b1 are fixed
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+      step(acc, arena, kt, b0, b1, a0, a1);
+      step(acc, arena, kt + 1, b1, b0, a0, a1);
     }
+    if (kt < nk) step(acc, arena, kt, b0, b1, a0, a1);
+  }
 
-    // ---------------------------------------------------------------- epilogue (LDS staged)
-    float* ep = reinterpret_cast<float*>(arena + wid * 32768);
+  // Stage kt: its B blocks are in bc and its first A block in a0; on return
+  // (unless it was the last stage) the next stage's are in bn and a0.
+  __device__ __forceinline__ void step(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, BFrags& bc, BFrags& bn,
+                                       AFrag& a0, AFrag& a1) const {
+    const int buf = kt % kMxNS;
+#pragma unroll
+    for (int i = 0; i + 1 < FM; ++i) {
+      read_a(buf, i + 1, arena, (i & 1) ? a0 : a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_row<0, 1>(acc, i, (i & 1) ? a1 : a0, bc);
+    }
+    // the last row block is in a1 (FM even)
+    if (kt + 1 < nk) {
+      wait_stages<D, kMxNS - 2>(nk - 2 - kt < kMxNS - 2 ? nk - 2 - kt : kMxNS - 2);
+      read_b((kt + 1) % kMxNS, arena, bn);
+      read_a((kt + 1) % kMxNS, 0, arena, a0);
+      mma_issue<0, 4>(acc, a1, bc, kt + kMxNS < nk, kt + kMxNS, arena);
+    } else {
+      mma_row<0, 1>(acc, FM - 1, a1, bc);
+    }
+  }
+
+  // Epilogue through this wave's 4 KB of the staging area, 16 rows per round.
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging) const {
+    // The lane index passes through an empty asm so that the compiler cannot
+    // compute the epilogue's per-lane addresses before the K loop (they would
+    // stay live across it and push the loop into register spills).
+    int lane = this->lane;
+    asm volatile("" : "+v"(lane));
+    float* ep = reinterpret_cast<float*>(staging + wid * 4096);
+    const GroupedGemmArgs& a = *args;
     const int wrow0 = wm * TM, wcol0 = wn * TN;
     if constexpr (KIND == KIND_UP) {
-      uint8_t* hq = (uint8_t*)args.out0;
+      // gate and up of 16 rows x 32 columns per round; 4 consecutive lanes
+      // hold the 32 columns (one MX block) of a row
+      uint8_t* hq = (uint8_t*)a.out0;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
-            ep[4096 + rr * 32 + (lane & 31)] = acc[NB - 1][i][j][r];
-          }
-        __builtin_amdgcn_wave_barrier();
-        // 4 consecutive lanes hold the 32 columns of one row's MX block
-        for (int q = 0; q < TM * 32 / 8 / 64; ++q) {
-          const int seg = q * 64 + lane;
-          const int rr = seg >> 2, c8 = (seg & 3) * 8;
-          const int row = row0 + wrow0 + rr, col = n0 + wcol0 + j * 32 + c8;
-          const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
-          const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[4096 + rr * 32 + c8]);
-          const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
-          const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-          float h[8];
-          float amax = 0.f;
+          for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            h[t] = v[t] * sigmoidf_(v[t]) * u[t];
-            amax = fmaxf(amax, fabsf(h[t]));
-          }
-          amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-          amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-          const int se = mx_scale_exp(amax);
-          uint32_t c[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) c[t] = e4m3_rne(ldexpf(h[t], -se));
-          if (row < row_end && col < N) {
-            u32x2_t codes;
-            codes[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
-            if (c8 == 0) args.out_scale[(int64_t)row * (N / 32) + col / 32] = (uint8_t)(se + 127);
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    } else {
-#pragma unroll
-      for (int jp = 0; jp < FN / 2; ++jp) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
+            for (int r = 0; r < 8; ++r) {
+              const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // 0..15
+              ep[rr * 32 + (lane & 31)] = acc[0][i][j][8 * half + r];
+              ep[512 + rr * 32 + (lane & 31)] = acc[1][i][j][8 * half + r];
             }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll 2
-        for (int q = 0; q < TM * 64 / 8 / 64; ++q) {
-          const int seg = q * 64 + lane;
-          const int rr = seg >> 3, c8 = (seg & 7) * 8;
-          const int row = row0 + wrow0 + rr, col = n0 + wcol0 + jp * 64 + c8;
-          if (row < row_end && col < N) {
-            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
-            const f32x4_t v0 = pv[0], v1 = pv[1];
+            __builtin_amdgcn_wave_barrier();
+            const int rr = lane >> 2, c8 = (lane & 3) * 8;
+            const int row = c.row0 + wrow0 + i * 32 + half * 16 + rr, col = c.n0 + wcol0 + j * 32 + c8;
+            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
+            const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[512 + rr * 32 + c8]);
+            const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
             const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            u32x4_t y;
+            const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+            float hv[8];
+            float amax = 0.f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
-            *reinterpret_cast<u32x4_t*>((bf16_t*)args.out0 + (int64_t)row * N + col) = y;
+            for (int t = 0; t < 8; ++t) {
+              hv[t] = v[t] * sigmoidf_(v[t]) * u[t];
+              amax = fmaxf(amax, fabsf(hv[t]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const int se = mx_scale_exp(amax);
+            uint32_t cd[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cd[t] = e4m3_rne(ldexpf(hv[t], -se));
+            if (row < c.row_end && col < N) {
+              u32x2_t codes;
+              codes[0] = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+              codes[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+              *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
+              if (c8 == 0) a.out_scale[(int64_t)row * (N / 32) + col / 32] = (uint8_t)(se + 127);
+            }
+            __builtin_amdgcn_wave_barrier();
           }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
+    } else {
+      // 16 rows x 64 columns per round, 8 lanes per row
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][8 * half + r];
+              }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int seg = q * 64 + lane;
+              const int rr = seg >> 3, c8 = (seg & 7) * 8;
+              const int row = c.row0 + wrow0 + i * 32 + half * 16 + rr, col = c.n0 + wcol0 + jp * 64 + c8;
+              if (row < c.row_end && col < N) {
+                const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
+                const f32x4_t v0 = pv[0], v1 = pv[1];
+                const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                u32x4_t y;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  y[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+                *reinterpret_cast<u32x4_t*>((bf16_t*)a.out0 + (int64_t)row * N + col) = y;
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+          }
     }
-    __syncthreads();
+  }
+};
+
+// Persistent loop over the row tiles of the local experts (same order and
+// XCD-aware mapping as the bf16 kernel); the next tile's first stages are
+// issued before the current tile's epilogue.
+template <int KIND>
+__global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using Job = MxJob<KIND>;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kMxNS * Job::STAGE + 16384];
+  static_assert(kMxNS * Job::STAGE + 16384 <= 163840, "LDS");
+  uint8_t* const staging = arena + kMxNS * Job::STAGE;
+  const int N = KIND == KIND_UP ? args.F : args.d;
+  const int E_loc = args.E_loc;
+  const int ntn = (N + Job::BN - 1) / Job::BN;
+  const int32_t* tp = args.tile_prefix + 2 * (E_loc + 1);  // 256-row tiles
+  const int total = sload(tp + E_loc) * ntn;
+  const int G_ = gridDim.x;
+  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+  auto coord = [&](int tile) -> TileCoord {
+    const int q = tile / ntn;
+    int lo = 0, hi = E_loc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sload(tp + mid) <= q) lo = mid; else hi = mid - 1;
+    }
+    TileCoord c{};
+    c.e_loc = lo;
+    const int t0 = sload(tp + lo), t1 = sload(tp + lo + 1);
+    int mt, nt;
+    tile_mn(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
+    c.n0 = nt * Job::BN;
+    c.row0 = sload(args.offsets + args.eb + lo) + mt * Job::BM;
+    c.row_end = sload(args.offsets + args.eb + lo + 1);
+    return uniform(c);
+  };
+  int tile = vb;
+  if (tile >= total) return;
+  Job cur;
+  cur.init(args, coord(tile));
+  for (int s = 0; s < kMxNS && s < cur.nk; ++s) cur.issue(s, arena);
+  f32x16_t acc[Job::NB][Job::FM][Job::FN];
+  while (true) {
+    cur.mainloop(acc, arena);
+    lds_barrier();  // every wave is done with the stage buffers
+    const int nt = tile + G_;
+    Job nxt = cur;
+    if (nt < total) {
+      nxt.init(args, coord(nt));
+      for (int s = 0; s < kMxNS && s < nxt.nk; ++s) nxt.issue(s, arena);
+    }
+    cur.epilogue(acc, staging);
+    if (nt >= total) break;
+    cur = nxt;
+    tile = nt;
   }
 #endif
 }
 
-template <int KIND, int BM, int BN>
+template <int KIND>
 static hipError_t run_mx(const GroupedGemmArgs& g, hipStream_t s) {
+  using Job = MxJob<KIND>;
   const int N = KIND == KIND_UP ? g.F : g.d;
-  const int ntn = (N + BN - 1) / BN;
-  const int64_t worst = ((g.P_max + BM - 1) / BM + g.E_loc) * (int64_t)ntn;
+  const int ntn = (N + Job::BN - 1) / Job::BN;
+  const int64_t worst = ((g.P_max + Job::BM - 1) / Job::BM + g.E_loc) * (int64_t)ntn;
   const int blocks = (int)(worst < 256 ? worst : 256);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND, BM, BN>), dim3(blocks), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND>), dim3(blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
-    case KIND_UP:   return run_mx<KIND_UP, 256, 128>(g, s);
-    case KIND_DOWN: return run_mx<KIND_DOWN, 256, 256>(g, s);
+    case KIND_UP:   return run_mx<KIND_UP>(g, s);
+    case KIND_DOWN: return run_mx<KIND_DOWN>(g, s);
   }
   return hipErrorNotSupported;
 }

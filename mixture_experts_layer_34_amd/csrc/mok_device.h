@@ -110,3 +110,18 @@ __device__ __forceinline__ void dma_b128(i32x4_t rsrc, uint32_t lds, uint32_t vo
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory");
 }
+
+// Like dma_b128 with 2 bytes per lane (any alignment): lane i's two bytes land
+// zero-extended in the dword at lds + 4 i.
+__device__ __forceinline__ void dma_u16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_ushort %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
