@@ -141,6 +141,8 @@ def main():
     ap.add_argument("--minibatch-rows", type=int, default=0,
                     help="ring pipeline minibatch rows R (0 = whole layer at once)")
     ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the same step captured in a HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (HBM counter calibration)")
     args = ap.parse_args()
@@ -207,6 +209,35 @@ def main():
     buf.cfg.stage_events = None
     ms_step = ms_total / K
 
+    # The same step captured once into a HIP graph and replayed K times (the
+    # library only enqueues kernels, so it captures as is): launch gaps removed.
+    graph_res = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            buf.cfg.stage_events = None
+            buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
+            if backward:
+                buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"])
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
+            if backward:
+                buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"])
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev.create(2)
+        ev.record(g0, sh)
+        for _ in range(K):
+            graph.replay()
+        ev.record(g1, sh)
+        g_ms = ev.elapsed_ms(g0, g1)
+        graph_res = {"ms_per_step": round(g_ms / K, 4), "tokens_per_s": round(T * K / (g_ms * 1e-3), 1)}
+        del graph
+
     # per-stage averages over the timed steps
     stages = {}
     ran = mok.STAGES if backward else mok.STAGES[:mok.STAGES.index("combine") + 1]
@@ -262,6 +293,7 @@ def main():
                          "frac_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4), "per_gemm": gemm},
         "data_movement": hbm,
         "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
+        "graph_replay": graph_res,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
