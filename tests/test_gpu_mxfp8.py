@@ -87,6 +87,23 @@ def test_mxfp8_forward_small_matches_oracle():
     assert err <= 3e-2
 
 
+@pytest.mark.parametrize("name,over", [
+    ("skewed", dict(T=700, d=256, E=8, k=2, F=256, notes={"zipf": 2.0})),
+    ("local", dict(T=500, d=128, E=10, k=3, F=384, expert_begin=3, expert_end=8)),
+])
+def test_mxfp8_forward_small_cases(name, over):
+    """Skewed loads (one expert over several row tiles, empty experts) and a
+    local expert range; the smallest K (d = 128: two 64-K stages)."""
+    import workloads as W
+    base = "bf16_train" if "zipf" in over.get("notes", {}) else "bf16_fwd"
+    w = W.scaled(base, precision="mxfp8", backward=False, **over)
+    note(f"mxfp8 {name}")
+    inp = W.make_inputs(w, device="cuda")
+    err = _run_and_oracle(w, inp)
+    note(f"  out error {err:.3e}")
+    assert err <= 3e-2
+
+
 def test_mxfp8_forward_ep_share_full_size_sampled():
     import workloads as W
     w = W.get("ep_mxfp8")

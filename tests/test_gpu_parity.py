@@ -118,6 +118,13 @@ SMALL_CASES = [
     ("bf16-ragged", dict(T=512, d=256, E=8, k=2, F=192), True),
     ("bf16-skewed", dict(T=777, d=128, E=16, k=4, F=320, notes={"zipf": 1.2}), True),
     ("bf16-local", dict(T=600, d=192, E=12, k=3, F=128, expert_begin=4, expert_end=9), True),
+    # smallest dimensions: K loops of 2 stages, shorter than the stage ring
+    ("bf16-min", dict(T=37, d=64, E=4, k=2, F=64), True),
+    ("bf16-one-token", dict(T=1, d=64, E=8, k=3, F=128), True),
+    # every token on every expert (k = E)
+    ("bf16-k-eq-E", dict(T=130, d=128, E=4, k=4, F=128), True),
+    # one expert takes nearly every row (several row tiles), others few or none
+    ("bf16-one-hot", dict(T=700, d=128, E=6, k=1, F=192, notes={"zipf": 4.0}), True),
 ]
 
 
@@ -144,10 +151,14 @@ def test_layer_small_matches_oracle(name, over, backward):
         errs["dx"] = rel_inf(to_np(g["dx"]), bw["dx"])
         errs["dgate"] = rel_inf(to_np(g["dgate"]), bw["dgate"])
         errs["dlogits"] = rel_inf(to_np(g["dlogits"]), bw["dlogits"])
+        counts = to_np(buf.counts)
         for n in ("dW1", "dW3", "dW2"):
             gw = to_np(g[n])
             for i in range(w.E_loc):
                 errs[f"{n}[{i}]"] = rel_inf(gw[i], bw[n][i])
+                if counts[w.expert_begin + i] == 0:
+                    # an expert without rows has an exactly zero gradient
+                    assert not gw[i].any(), f"{n}[{i}] of an empty expert is not zero"
     note(f"  max errors: {max(errs.values()):.3e} ({max(errs, key=errs.get)})")
     bad = {k: v for k, v in errs.items() if v > tol}
     assert not bad, bad
