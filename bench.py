@@ -58,10 +58,12 @@ class HipEvents:
         return ms.value if r == 0 else float("nan")
 
 
-def stage_work(w, P, U):
+def stage_work(w, P, U, save_for_backward=True):
     """Algorithmic work of one launch of each stage: FLOPs for the GEMMs,
-    HBM bytes for the data movement (each operand read or written once)."""
+    HBM bytes for every stage (each operand read once, each output written
+    once; a GEMM's weights are those of the E_loc local experts)."""
     d, F, E, k, T = w.d, w.F, w.E, w.k, U
+    El = w.e_end - w.expert_begin
     s = 4 if w.precision == "f32" else 2
     flops = {"gemm_up": 4.0 * P * d * F, "gemm_down": 2.0 * P * F * d, "gemm_dh": 2.0 * P * d * F,
              "gemm_dx": 4.0 * P * F * d, "gemm_dw2": 2.0 * P * d * F, "gemm_dw13": 4.0 * P * F * d}
@@ -71,7 +73,33 @@ def stage_work(w, P, U):
               "bwd_gate": T * d * s + 2 * P * d * s + 2 * T * E * 4 + P * 8,
               "reduce_dx": P * d * s + T * d * s + P * 4,
               "sort": T * k * 4 * 4 + P * 4}
+    # GEMM operands: bf16 (or fp32) elements, or MXFP8 codes plus one E8M0
+    # scale per 32; fp32 weight gradients.
+    q = 1 + 1 / 32 if w.precision == "mxfp8" else s
+    gemm_bytes = {
+        "gemm_up": P * d * q + 2 * El * F * d * q + P * F * q + (2 * P * F * s if save_for_backward else 0),
+        "gemm_down": P * F * q + El * d * F * q + P * d * s,
+        "gemm_dh": P * d * s + El * d * F * s + 2 * P * F * s + 2 * P * F * s,
+        "gemm_dx": 2 * P * F * s + 2 * El * F * d * s + P * d * s,
+        "gemm_dw2": P * d * s + P * F * s + El * d * F * 4,
+        "gemm_dw13": 2 * P * F * s + P * d * s + 2 * El * F * d * 4,
+    }
+    nbytes.update(gemm_bytes)
     return flops, nbytes
+
+
+def roof_of(flops_n, bytes_n, ms, peak_tflops):
+    """Roofline position of one launch: the bound is whichever of the MFMA
+    time (FLOPs / peak) and the HBM time (bytes / 8 TB/s) is longer."""
+    t_mfma = flops_n / (peak_tflops * 1e12) if flops_n else 0.0
+    t_hbm = bytes_n / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = flops_n / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_tflops, "unit": "TFLOP/s",
+                "frac": round(ach / peak_tflops, 4)}
+    ach = bytes_n / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_bf16_train_hbm_traffic.md")
@@ -248,31 +276,27 @@ def main():
         stages[name] = sum(vals) / len(vals)
     P = int(buf.offsets[-1].item())
     U = int((buf.topk_idx.ge(w.expert_begin) & buf.topk_idx.lt(w.e_end)).any(dim=1).sum().item())
-    flops, nbytes = stage_work(w, P, U)
+    flops, nbytes = stage_work(w, P, U, save_for_backward=backward)
     if w.precision == "bf16" and not args.minibatch_rows and T * w.d * 2 < (1 << 31):
         # the library fuses the dispatch into the UP GEMM's loads (pull
         # dispatch): the stage is recorded empty and moves no bytes of its own
         nbytes.pop("dispatch", None)
     dom = max(stages, key=stages.get)
     peak = PEAK_TFLOPS[w.precision]
-    if dom in flops:
-        ach = flops[dom] / (stages[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(w.name, dom) if not args.minibatch_rows else None, "kernel": dom,
-                "per_launch": f"{flops[dom] / 1e9:.1f} GFLOP", "avg_ms": round(stages[dom], 4)}
-    else:
-        ach = nbytes[dom] / (stages[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
-                "per_launch": f"{nbytes[dom] / 1e6:.1f} MB", "avg_ms": round(stages[dom], 4)}
+    roof = roof_of(flops.get(dom, 0.0), nbytes[dom], stages[dom], peak)
+    roof.update({"traffic": measured_traffic(w.name, dom) if dom in flops and not args.minibatch_rows else None,
+                 "kernel": dom, "avg_ms": round(stages[dom], 4),
+                 "per_launch": (f"{flops[dom] / 1e9:.1f} GFLOP, " if dom in flops else "")
+                 + f"{nbytes[dom] / 1e6:.1f} MB"})
     gemm = {n: {"ms": round(stages[n], 4), "tflops": round(flops[n] / (stages[n] * 1e-3) / 1e12, 1),
-                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / peak, 4)}
+                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / peak, 4),
+                "roof": {k_: v for k_, v in roof_of(flops[n], nbytes[n], stages[n], peak).items()
+                         if k_ in ("bound", "frac")}}
             for n in flops if n in stages}
     gemm_ms = sum(stages[n] for n in flops if n in stages)
     gemm_flops = sum(flops[n] for n in flops if n in stages)
     hbm = {n: {"ms": round(stages[n], 4), "gbs": round(nbytes[n] / (stages[n] * 1e-3) / 1e9, 1)}
-           for n in nbytes if n in stages}
+           for n in nbytes if n in stages and n not in flops}
 
     result = {
         "metric": METRIC,

@@ -16,8 +16,9 @@
 // Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile (per B
 // matrix; UP computes the W1 and W3 tiles of the same columns), each wave a
 // (BM/2) x (BN/2) block of 32x32 MFMA tiles.  K advances in stages of 32
-// through a ring of NS LDS stage buffers (five, 160 KB, in the grouped GEMMs),
-// so NS - 1 stages are in flight while one is multiplied.  Every operand goes from HBM straight to LDS
+// through a ring of NS LDS stage buffers (four of 32 KB in the grouped
+// GEMMs), so NS - 1 stages are in flight while one is multiplied.  Every
+// operand goes from HBM straight to LDS
 // (buffer_load_dwordx4 ... lds, 1 KB per wave instruction, no VGPRs),
 // through buffer resources rebased on the tile so that rows past the data
 // read as zero, in the layout it has in memory:
@@ -547,29 +548,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
   constexpr int NZ = KIND == KIND_DW13 ? 2 : 1;  // DW13 computes dW1 (z = 0) and dW3 (z = 1)
   const int32_t* tp = args.tile_prefix + ((BM == 64) ? 0 : (BM == 128 ? 1 : 2)) * (E_loc + 1);
 
-  int total, ntm_k = 0, tbeg = 0;
+  // Weight-gradient kinds: the heaviest-first tile sequence (expert-major,
+  // T tiles per expert) is cut into eight runs; bound(x) is the start of run
+  // x, the first tile whose cumulative work reaches x eighths of the total.
+  const int ntm_k = Tr::GROUP_K ? (G.M + BM - 1) / BM : 0;
+  const int T = NZ * ntm_k * ntn;
+  const int32_t* rk = args.expert_order;  // per rank {expert, row0, row_end, work prefix}
+  auto bound = [&](int x) -> int {
+    if (x <= 0 || E_loc == 0) return 0;
+    if (x >= 8) return E_loc * T;
+    const int64_t target = (int64_t)T * sload(rk + 4 * E_loc + 3) * x / 8;
+    int lo = 0, hi = E_loc - 1;  // last rank whose tiles start at or before target
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)T * sload(rk + 4 * mid + 3) <= target) lo = mid; else hi = mid - 1;
+    }
+    const int w0 = sload(rk + 4 * lo + 3), w1 = sload(rk + 4 * lo + 7);
+    const int64_t j = (target - (int64_t)T * w0) / (w1 - w0);  // whole tiles of rank lo by target
+    return lo * T + (int)(j < T ? j : T);
+  };
+  int total, tbeg = 0;
   if constexpr (!Tr::GROUP_K) {
     total = sload(tp + E_loc) * ntn;
   } else {
-    // This XCD's share of the heaviest-first tile sequence (expert-major,
-    // T tiles per expert): the run of tiles whose cumulative work falls in
-    // the XCD's eighth of the total.
-    ntm_k = (G.M + BM - 1) / BM;
-    const int T = NZ * ntm_k * ntn;
-    const int32_t* rk = args.expert_order;  // per rank {expert, row0, row_end, work prefix}
-    auto bound = [&](int x) -> int {
-      if (x <= 0 || E_loc == 0) return 0;
-      if (x >= 8) return E_loc * T;
-      const int64_t target = (int64_t)T * sload(rk + 4 * E_loc + 3) * x / 8;
-      int lo = 0, hi = E_loc - 1;  // last rank whose tiles start at or before target
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)T * sload(rk + 4 * mid + 3) <= target) lo = mid; else hi = mid - 1;
-      }
-      const int w0 = sload(rk + 4 * lo + 3), w1 = sload(rk + 4 * lo + 7);
-      const int64_t j = (target - (int64_t)T * w0) / (w1 - w0);  // whole tiles of rank lo by target
-      return lo * T + (int)(j < T ? j : T);
-    };
     tbeg = bound(xcd);
     total = bound(xcd + 1) - tbeg;
   }
@@ -580,18 +581,46 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
   // heaviest expert first (rank order of the counting sort), the sequence is
   // cut into 8 runs of equal work and the workgroups of XCD x pull run x's
   // tiles from counter x: an expert's tiles mostly share one L2, and an
-  // expert heavier than an eighth of the work spreads over several XCDs.  Each tile is still computed whole by one
-  // workgroup, so the results do not depend on the assignment.
+  // expert heavier than an eighth of the work spreads over several XCDs.
+  // A workgroup whose run is exhausted goes on to the runs of the next
+  // XCDs in turn (x + 1, x + 2, ... mod 8), so that the tail of a run of
+  // long tiles is shared out instead of keeping the other XCDs waiting.
+  // Each tile is still computed whole by one workgroup, so the results do
+  // not depend on the assignment.
   const int G_ = gridDim.x;
   const int vb = (G_ % 8 == 0) ? xcd * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
   // Weight-gradient kinds: thread 0 takes the tile after the current one from
   // the queue as the current one starts, so the atomic's latency is hidden.
-  int taken = 0;
+  // vx is the XCD whose run is being taken, [vbeg, vbeg + vcnt) that run.
+  int taken = 0, vx = xcd, vbeg = tbeg, vcnt = total, hops = 0;
   auto take = [&]() {
     if constexpr (Tr::GROUP_K) {
-      if (tid == 0) taken = atomicAdd(args.queue + xcd, 1);
+      if (tid == 0) taken = atomicAdd(args.queue + vx, 1);
     }
   };
+  // Position in the heaviest-first sequence of the v-th tile taken from run
+  // vx, moving on to the next runs while v is past the end; -1 once all
+  // eight runs are exhausted.  Called by every wave with the same v, right
+  // after the mailbox has been read.
+  auto resolve = [&](int v) -> int {
+    if constexpr (Tr::GROUP_K) {
+      while (v >= vcnt) {
+        if (hops == 7) return -1;
+        ++hops;
+        vx = (vx + 1) & 7;
+        vbeg = bound(vx);
+        vcnt = bound(vx + 1) - vbeg;
+        lds_barrier();  // every wave has read the mailbox
+        if (tid == 0) *mbox = atomicAdd(args.queue + vx, 1);
+        lds_barrier();
+        v = __builtin_amdgcn_readfirstlane(*mbox);
+      }
+      return vbeg + v;
+    } else {
+      return v;
+    }
+  };
+  auto done = [&](int t) { return Tr::GROUP_K ? t < 0 : t >= total; };
   auto coord = [&](int tile) -> TileCoord {
     TileCoord c{};
     if constexpr (!Tr::GROUP_K) {
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
       c.row_end = sload(args.offsets + e + 1);
     } else {
       const int per_z = ntm_k * ntn;
-      const int g = tbeg + tile;  // position in the heaviest-first sequence
+      const int g = tile;  // position in the heaviest-first sequence
       const i32x4_t rec = sload4(args.expert_order + 4 * (g / (NZ * per_z)));
       c.e_loc = rec[0];
       c.row0 = rec[1];
@@ -621,7 +650,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
       const int rem = g % (NZ * per_z);
       c.z = rem / per_z;
       int mt, nt;
-      tile_mn(rem % per_z, ntm_k, ntn, mt, nt);
+      tile_mn<2>(rem % per_z, ntm_k, ntn, mt, nt);
       c.m0 = mt * BM;
       c.n0 = nt * BN;
     }
@@ -633,10 +662,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
     take();
     if (tid == 0) *mbox = taken;
     lds_barrier();
-    tile = __builtin_amdgcn_readfirstlane(*mbox);
+    tile = resolve(__builtin_amdgcn_readfirstlane(*mbox));
     lds_barrier();
   }
-  if (tile >= total) return;
+  if (done(tile)) return;
   Job cur;
   cur.init(args, coord(tile));
   cur.prologue(arena);
@@ -649,19 +678,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
       if (tid == 0) *mbox = taken;
     }
     lds_barrier();  // every wave is done with the stage buffers (and sees the mailbox)
-    if constexpr (Tr::GROUP_K) nt = __builtin_amdgcn_readfirstlane(*mbox);
+    if constexpr (Tr::GROUP_K) nt = resolve(__builtin_amdgcn_readfirstlane(*mbox));
     typename Job::SavedAB pre;
     cur.epilogue_prefetch(pre);
     Job nxt = cur;
-    if (nt < total) {
+    if (!done(nt)) {
       nxt.init(args, coord(nt));
       nxt.prologue(arena);
     }
     // the next mailbox write follows a barrier of the next K loop, which
     // has one whenever it has a stage
-    if (Tr::GROUP_K && (nt >= total || nxt.nk == 0)) lds_barrier();
+    if (Tr::GROUP_K && (done(nt) || nxt.nk == 0)) lds_barrier();
     cur.epilogue(acc, staging, pre);
-    if (nt >= total) break;
+    if (done(nt)) break;
     cur = nxt;
     tile = nt;
   }

@@ -76,9 +76,10 @@ struct TileCoord {
 
 // Grouped raster inside one expert: groups of GM m-tiles, n-tiles outer and
 // m-tiles inner within a group, so that a run of consecutive tiles forms a
-// GM x (run / GM) block that reuses both operands.
+// GM x (run / GM) block that reuses both operands.  The weight-gradient
+// GEMMs measure best with GM = 2, the row GEMMs with 4.
+template <int GM = 4>
 __device__ __forceinline__ void tile_mn(int local, int mt, int ntn, int& m, int& n) {
-  constexpr int GM = 4;
   const int g = local / (GM * ntn);
   const int gm0 = g * GM;
   const int gsz = mt - gm0 < GM ? mt - gm0 : GM;
