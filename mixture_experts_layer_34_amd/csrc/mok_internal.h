@@ -8,7 +8,7 @@
 namespace mok {
 
 // Pairs handled by one wave in the counting sort.
-constexpr int kSortChunk = 4096;
+constexpr int kSortChunk = 512;
 // Row-tile heights for which per-expert tile prefixes are precomputed.
 constexpr int kNumTileBM = 3;
 constexpr int kTileBM[kNumTileBM] = {64, 128, 256};

@@ -113,6 +113,19 @@ __device__ __forceinline__ uint64_t peer_mask(int e, bool valid, int nbits) {
   return m;
 }
 
+// A wave's chunk of expert ids, all loaded at once (pair base + 64 i + lane in
+// ev[i]) so that the walk over the chunk waits for memory only once; -1 past
+// the end.
+constexpr int kChunkIters = kSortChunk / 64;
+__device__ __forceinline__ void load_chunk(const int32_t* __restrict__ idx, int64_t npairs, int64_t base,
+                                           int lane, int (&ev)[kChunkIters]) {
+#pragma unroll
+  for (int it = 0; it < kChunkIters; ++it) {
+    const int64_t p = base + it * 64 + lane;
+    ev[it] = p < npairs ? idx[p] : -1;
+  }
+}
+
 // Pass 1: per-chunk expert histogram.  One wave per chunk of kSortChunk pairs;
 // the lowest lane of each group of equal experts adds the group's size.
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ idx, int64_t npairs,
@@ -125,10 +138,11 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
   for (int e = lane; e < E; e += 64) hist[e] = 0;
   __syncthreads();
   if (c < nchunks) {
-    const int64_t base = (int64_t)c * kSortChunk;
-    for (int it = 0; it < kSortChunk / 64; ++it) {
-      int64_t p = base + it * 64 + lane;
-      int e = p < npairs ? idx[p] : -1;
+    int ev[kChunkIters];
+    load_chunk(idx, npairs, (int64_t)c * kSortChunk, lane, ev);
+#pragma unroll
+    for (int it = 0; it < kChunkIters; ++it) {
+      const int e = ev[it];
       bool valid = e >= eb && e < ee;
       uint64_t m = peer_mask(e, valid, nbits);
       if (valid && lane == __ffsll((unsigned long long)m) - 1) hist[e] += __popcll(m);
@@ -140,9 +154,12 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
     for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)c * E + e] = hist[e];
 }
 
-// Pass 2: one block.  Thread e scans its expert over the chunks (chunk bases),
-// the block scans the totals over experts (offsets), and the row-tile prefix
-// of the local experts is written for each tile height.
+// Pass 2: one block.  The chunks of each expert are split among G = 1024 / E
+// threads (thread g * E + e takes the g-th contiguous share of chunks); the
+// shares' sums give each expert's total and each share's starting count.  The
+// block scans the totals over experts (offsets), each share then writes its
+// chunk bases, and the row-tile prefix of the local experts is written for
+// each tile height.
 __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                          int nchunks, int E, int eb, int ee,
                                                          int32_t* __restrict__ chunk_base,
@@ -154,16 +171,25 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
   __shared__ int32_t wsum[16];
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t tsum[kNumTileBM][16];
+  __shared__ int32_t s_part[1024], s_offE[1024];
   const int e = threadIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      int v = chunk_counts[(int64_t)c * E + e];
-      chunk_base[(int64_t)c * E + e] = run;
-      run += v;
-    }
+  // shares: thread (tg, te) = (threadIdx.x / E, threadIdx.x % E), tg < G
+  const int G = 1024 / E;
+  const int te = threadIdx.x % E, tg = threadIdx.x / E;
+  const bool share = tg < G;
+  const int c0 = share ? (int)((int64_t)nchunks * tg / G) : 0;
+  const int c1 = share ? (int)((int64_t)nchunks * (tg + 1) / G) : 0;
+  {
+    int part = 0;
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) part += chunk_counts[(int64_t)c * E + te];
+    if (share) s_part[threadIdx.x] = part;
   }
+  __syncthreads();
+  int run = 0;  // expert e's total
+  if (e < E)
+    for (int q = 0; q < G; ++q) run += s_part[q * E + e];
   // exclusive scan of run over e (1024 threads = 16 waves)
   int incl = run;
 #pragma unroll
@@ -201,11 +227,11 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     counts_out[e] = run;
     offsets_out[e] = off;
     offsets_saved[e] = off;
+    s_offE[e] = off;
     if (e == E - 1) {
       offsets_out[E] = off + run;
       offsets_saved[E] = off + run;
     }
-    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
   }
   // Weight-gradient schedule: local experts ranked by descending row count
   // (ties: lower index), with the prefix of their work in K stages of 32
@@ -220,6 +246,18 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     s_off[i_loc] = off;
   }
   __syncthreads();
+  if (share) {
+    // chunk bases of this share: the expert's first row, the counts of the
+    // earlier shares, then a running sum over the share's chunks
+    int r = s_offE[te];
+    for (int q = 0; q < tg; ++q) r += s_part[q * E + te];
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const int v = chunk_counts[(int64_t)c * E + te];
+      chunk_base[(int64_t)c * E + te] = r;
+      r += v;
+    }
+  }
   if (i_loc >= 0 && i_loc < E_loc) {
     int rank = 0;
     for (int q = 0; q < E_loc; ++q) {
@@ -287,10 +325,13 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
   if (c >= nchunks) return;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t base = (int64_t)c * kSortChunk;
-  for (int it = 0; it < kSortChunk / 64; ++it) {
-    int64_t p = base + it * 64 + lane;
-    bool inb = p < npairs;
-    int e = inb ? idx[p] : -1;
+  int ev[kChunkIters];
+  load_chunk(idx, npairs, base, lane, ev);
+#pragma unroll
+  for (int it = 0; it < kChunkIters; ++it) {
+    const int64_t p = base + it * 64 + lane;
+    const bool inb = p < npairs;
+    const int e = ev[it];
     bool valid = e >= eb && e < ee;
     uint64_t m = peer_mask(e, valid, nbits);
     int row = -1;
