@@ -46,6 +46,25 @@
 #include "gemm_common.h"
 #include "gemm_pipe.h"
 
+// Non-temporal copies of the GEMM operands, per kind family and operand: the
+// weight-gradient GEMMs' B copies (X rows for dW1/dW3, H rows for dW2) carry
+// the hint.  Measured on dW1/dW3: 2.6-2.8 ms with the hint on B (or on A, or
+// both) against 3.0-3.1 ms without; dW2 is unaffected.  The row kinds keep
+// their weight and row tiles in L2 for the other tiles that share them: the
+// hint on either operand makes UP and DOWN 10-35 % slower.
+#ifndef MOK_DW_NT_A
+#define MOK_DW_NT_A 0
+#endif
+#ifndef MOK_DW_NT_B
+#define MOK_DW_NT_B 1
+#endif
+#ifndef MOK_ROW_NT_A
+#define MOK_ROW_NT_A 0
+#endif
+#ifndef MOK_ROW_NT_B
+#define MOK_ROW_NT_B 0
+#endif
+
 namespace mok {
 
 
@@ -85,6 +104,9 @@ struct TileJob {
   static_assert(STAGE / 4 >= 8192, "epilogue staging needs 8 KB per wave");
   static_assert(NS >= 2 && NS <= 5 && (NS - 1) * D <= 63, "stage count (vmcnt holds at most 63)");
   static_assert(!(NB == 2 && Tr::B_MN), "paired B matrices are K-contiguous");
+  // Which operand copies carry the non-temporal hint (see the macros above).
+  static constexpr bool kNtA = Tr::GROUP_K ? MOK_DW_NT_A : MOK_ROW_NT_A;
+  static constexpr bool kNtB = Tr::GROUP_K ? MOK_DW_NT_B : MOK_ROW_NT_B;
 
   struct Frags {
     bf16x8_t a[FM];
@@ -192,7 +214,7 @@ struct TileJob {
     } else if constexpr (!Tr::A_MN) {
 #pragma unroll
       for (int q = Q0; q < (Q1 < QB ? Q1 : QB); ++q)
-        dma_b128(rsA, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], k0 * 2);
+        dma_b128<kNtA>(rsA, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], k0 * 2);
     } else {
       // rows [k0, kend) of columns [m0, ...) of this expert's rows; rows past kend read zero
       const int64_t col0 = c.m0 + (KIND == KIND_DW13 ? (int64_t)c.z * args->F : 0);
@@ -201,7 +223,7 @@ struct TileJob {
       const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
 #pragma unroll
       for (int q = Q0; q < (Q1 < QB ? Q1 : QB); ++q)
-        dma_b128(rs, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], 0);
+        dma_b128<kNtA>(rs, lds_addr(st + (wid * GA::INST + q) * 1024), offA[q], 0);
     }
     uint8_t* sb = st + A_BYTES;
     constexpr int B0q = Q0 > QB ? Q0 - QB : 0, B1q = Q1 > QB ? Q1 - QB : 0;  // this part's B copies
@@ -210,7 +232,7 @@ struct TileJob {
     } else if constexpr (!Tr::B_MN) {
 #pragma unroll
       for (int q = B0q; q < B1q; ++q)
-        dma_b128((NB == 2 && (wid * GB::INST + q) * GB::KRPI >= BN) ? rsB1 : rsB0,
+        dma_b128<kNtB>((NB == 2 && (wid * GB::INST + q) * GB::KRPI >= BN) ? rsB1 : rsB0,
                  lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], k0 * 2);
     } else if constexpr (!Tr::GROUP_K) {
       // weights [K][N] of this expert; DX takes k < F from W1 and the rest from W3
@@ -222,13 +244,13 @@ struct TileJob {
       const int64_t bytes = ((int64_t)(krows - kl) * G.ldb - c.n0) * 2;
       const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
 #pragma unroll
-      for (int q = B0q; q < B1q; ++q) dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
+      for (int q = B0q; q < B1q; ++q) dma_b128<kNtB>(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
     } else if (!args->gather_rows) {
       const bf16_t* p = (const bf16_t*)args->B0 + (int64_t)k0 * G.ldb + c.n0;
       const int64_t bytes = ((int64_t)(kend - k0) * G.ldb - c.n0) * 2;
       const i32x4_t rs = make_rsrc(p, bytes > 0 ? (uint32_t)bytes : 0u);
 #pragma unroll
-      for (int q = B0q; q < B1q; ++q) dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
+      for (int q = B0q; q < B1q; ++q) dma_b128<kNtB>(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), offB[q], 0);
     } else {
       // B rows are token rows of x: row k of the expert is x[gather_rows[k] / k_top]
       static_assert(GB::RPI == 2, "gathered rows: two k rows per DMA instruction");
@@ -242,7 +264,7 @@ struct TileJob {
         const int32_t pr = (lane >> 5) ? i1 : i0;
         const uint32_t off =
             pr >= 0 ? (uint32_t)(((int64_t)(pr / args->k_top) * G.ldb + c.n0) * 2) + offB[q] : 0xFFFFFFF0u;
-        dma_b128(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), off, 0);
+        dma_b128<kNtB>(rs, lds_addr(sb + (wid * GB::INST + q) * 1024), off, 0);
       }
     }
   }

@@ -98,17 +98,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // s_waitcnt vmcnt(n) (copies complete in issue order) and then a workgroup
 // barrier before any wave reads what was copied.  `lds` must be wave-uniform;
 // M0 is restored afterwards.
+// With NT, the copy carries the non-temporal hint (the lines it brings into
+// L2 are the first to be replaced).
+template <bool NT = false>
 __device__ __forceinline__ void dma_b128(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+  }
 }
 
 // Like dma_b128 with 2 bytes per lane (any alignment): lane i's two bytes land
