@@ -33,7 +33,13 @@ combine and the final weighted sum):
      reverse-dispatch) [kucoin §01, §02].
 
 Readings taken where the pages are silent:
-  * gates: softmax over all E logits, then top-k, no renormalisation;
+  * gates: softmax over all E logits, then top-k, no renormalisation (the
+    default).  Router variants, for the DeepSeek-V3-type models the pages
+    name as the target ([fluid], «Comment MoK…»): sigmoid affinities instead
+    of softmax, and/or gates renormalised over the k chosen experts
+    (gate_j = a_j / sum_i a_i).  The selection is the same in every variant
+    (sigmoid is monotonic, so the top-k of the logits is the top-k of the
+    affinities);
   * top-k compares the raw float32 logits; ties go to the lower expert index;
     slot j = 0 is the largest;
   * expert rows are stable: within an expert, ascending pair id p = t*k + j;
@@ -53,7 +59,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "route", "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
+    "route", "route_backward", "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
     "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
     "forward_token", "backward_token", "expert_weight_grads",
@@ -66,18 +72,27 @@ def _f64(a) -> np.ndarray:
 
 # ------------------------------------------------------------------ router
 
-def route(logits, k: int):
-    """Softmax routing with stable top-k.
+GATINGS = ("softmax", "sigmoid")
+
+
+def route(logits, k: int, gating: str = "softmax", renorm: bool = False):
+    """Routing with stable top-k.
 
     The router decides per step and per token which experts it goes to, and each
     token selects several experts [kucoin §01].  Order of experts for token t:
     a precedes b iff logit_a > logit_b, or the logits are equal and a < b.  The
     comparison uses the raw float32 logits (so the GPU and CPU agree exactly on
-    the selection); the probabilities are float64.
+    the selection); the affinities are float64.
 
-    Returns idx [T,k] int32, gate [T,k] float64 (softmax probability of the
-    chosen experts, not renormalised), lse [T] float64, p [T,E] float64.
+    Affinities a: softmax over the E logits ("softmax", the default) or the
+    sigmoid of each logit ("sigmoid").  gate_j = a[idx_j], or with renorm
+    a[idx_j] / sum_i a[idx_i] (i over the k chosen experts).
+
+    Returns idx [T,k] int32, gate [T,k] float64, lse [T] float64 (log-sum-exp
+    of the logits, whatever the gating), p [T,E] float64 (the affinities).
     """
+    if gating not in GATINGS:
+        raise ValueError(f"gating must be one of {GATINGS}")
     l32 = np.asarray(logits, dtype=np.float32)
     if l32.ndim != 2:
         raise ValueError("logits must be [T, E]")
@@ -94,10 +109,39 @@ def route(logits, k: int):
     m = l.max(axis=1, keepdims=True) if E else np.zeros((T, 1))
     ex = np.exp(l - m)
     s = ex.sum(axis=1, keepdims=True)
-    p = ex / s
     lse = (m + np.log(s))[:, 0]
+    p = ex / s if gating == "softmax" else sigmoid(l)
     gate = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if renorm:
+        gate = gate / gate.sum(axis=1, keepdims=True)
     return idx, gate, lse, p
+
+
+def route_backward(p, idx, gate, dgate, gating: str = "softmax", renorm: bool = False):
+    """d(logits) from d(gate), by the chain rule through route().
+
+    p [T,E] affinities, idx [T,k], gate [T,k] (as route() returns them),
+    dgate [T,k].  Two steps:
+      1. d(affinity) of the chosen experts: dgate itself, or with renorm
+         (gate_j = a_j / S, S = sum_i a_i) da_i = (dgate_i - sum_j gate_j dgate_j) / S;
+         the other experts' affinities do not reach the gates (0);
+      2. d(logit) through the affinity: softmax Jacobian p * (DA - <p, DA>),
+         or the sigmoid's a (1 - a) DA, with DA [T,E] holding step 1.
+    The selection itself has zero gradient.
+    """
+    p = _f64(p); gate = _f64(gate); dgate = _f64(dgate)
+    i64 = np.asarray(idx).astype(np.int64)
+    a_sel = np.take_along_axis(p, i64, axis=1)
+    if renorm:
+        S = a_sel.sum(axis=1, keepdims=True)
+        da = (dgate - (gate * dgate).sum(axis=1, keepdims=True)) / S
+    else:
+        da = dgate
+    DA = np.zeros_like(p)
+    np.put_along_axis(DA, i64, da, axis=1)
+    if gating == "softmax":
+        return p * (DA - (p * DA).sum(axis=1, keepdims=True))
+    return p * (1.0 - p) * DA
 
 
 # ------------------------------------------------------------------ layout
@@ -259,7 +303,7 @@ def mxfp8_qdq(v, block: int = 32):
 # ------------------------------------------------------------------ forward
 
 def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: int | None = None,
-            mxfp8: bool = False):
+            mxfp8: bool = False, gating: str = "softmax", renorm: bool = False):
     """Whole-layer forward in float64.
 
     x [T,d]; logits [T,E] float32; W1, W3 [E_loc,F,d]; W2 [E_loc,d,F] with
@@ -274,7 +318,7 @@ def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: in
     E = np.asarray(logits).shape[1]
     if expert_end is None:
         expert_end = E
-    idx, gate, lse, p = route(logits, k)
+    idx, gate, lse, p = route(logits, k, gating, renorm)
     counts, offsets, row_of_pair, pair_of_row = layout(idx, E, expert_begin, expert_end)
     Xp = permute(x, pair_of_row, k)
     F = np.asarray(W1).shape[1]
@@ -297,15 +341,17 @@ def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: in
         A[r0:r1], B[r0:r1], H[r0:r1], Y[r0:r1] = a, b, h, y
     out = combine(Y, gate, row_of_pair, T, k)
     return dict(idx=idx, gate=gate, lse=lse, p=p, counts=counts, offsets=offsets,
-                row_of_pair=row_of_pair, pair_of_row=pair_of_row, A=A, B=B, H=H, Y=Y, out=out)
+                row_of_pair=row_of_pair, pair_of_row=pair_of_row, A=A, B=B, H=H, Y=Y, out=out,
+                gating=gating, renorm=renorm)
 
 
 def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int = 0,
-                  expert_end: int | None = None, mxfp8: bool = False):
+                  expert_end: int | None = None, mxfp8: bool = False, gating: str = "softmax",
+                  renorm: bool = False):
     """Output of one token alone (for sampled checks at full size): its top-k
     experts from its own logits, the FFN of each local one, the gate-weighted
     sum in slot order.  Returns (idx [k], gate [k], out [d], y per slot)."""
-    idx, gate, _, _ = route(np.asarray(logits_t, dtype=np.float32)[None, :], k)
+    idx, gate, _, _ = route(np.asarray(logits_t, dtype=np.float32)[None, :], k, gating, renorm)
     E = np.asarray(logits_t).shape[0]
     if expert_end is None:
         expert_end = E
@@ -332,7 +378,8 @@ def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int =
 # ------------------------------------------------------------------ backward
 
 def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
-             expert_begin: int = 0, expert_end: int | None = None):
+             expert_begin: int = 0, expert_end: int | None = None, gating: str = "softmax",
+             renorm: bool = False):
     """Gradients of L = sum(out * dout) in float64.
 
     The backward pass mirrors the forward: reverse-combine, expert backward,
@@ -341,7 +388,8 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     through the top-k selection itself is zero.
 
       dgate[t,j]  = <dout_t, y_(t,j)>                       (0 for non-local pairs)
-      dlogits     = p * (G - <p, G>),  G[t,e] = dgate at the chosen e, else 0
+      dlogits     = route_backward(p, idx, gate, dgate)     (softmax, no renorm:
+                    p * (G - <p, G>), G[t,e] = dgate at the chosen e, else 0)
       dy_r        = gate_r * dout_t(r)                      (reverse-combine)
       dh          = dy W2_e
       da          = dh * b * sigmoid(a) * (1 + a (1 - sigmoid(a)))
@@ -357,7 +405,8 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     if expert_end is None:
         expert_end = E
     if fwd is None:
-        fwd = forward(x, logits, W1, W3, W2, k, expert_begin, expert_end)
+        fwd = forward(x, logits, W1, W3, W2, k, expert_begin, expert_end, gating=gating, renorm=renorm)
+    gating, renorm = fwd.get("gating", gating), fwd.get("renorm", renorm)
     gate, p, Y = fwd["gate"], fwd["p"], fwd["Y"]
     rop = fwd["row_of_pair"].reshape(T, k)
     offsets, pair_of_row = fwd["offsets"], fwd["pair_of_row"]
@@ -367,9 +416,7 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     for j in range(k):
         m = rop[:, j] >= 0
         dgate[m, j] = np.einsum("td,td->t", g[m], Y[rop[m, j]])
-    G = np.zeros((T, E))
-    np.put_along_axis(G, fwd["idx"].astype(np.int64), dgate, axis=1)
-    dlogits = p * (G - (p * G).sum(axis=1, keepdims=True))
+    dlogits = route_backward(p, fwd["idx"], gate, dgate, gating, renorm)
 
     tok = pair_of_row // k
     slot = pair_of_row % k
@@ -407,7 +454,7 @@ def loss(out, dout) -> float:
 
 
 def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int = 0,
-                   expert_end: int | None = None):
+                   expert_end: int | None = None, gating: str = "softmax", renorm: bool = False):
     """Backward of one token alone (sampled checks at full size): the pair
     gradients of its local experts summed in slot order, and its router
     gradient.  Same equations as backward(), restricted to one token; every
@@ -417,7 +464,7 @@ def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int 
     E = l32.shape[1]
     if expert_end is None:
         expert_end = E
-    idx, gate, _, p = route(l32, k)
+    idx, gate, _, p = route(l32, k, gating, renorm)
     xt = _f64(x_t)[None, :]
     g = _f64(dout_t)
     dx = np.zeros(xt.shape[1])
@@ -435,9 +482,7 @@ def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int 
         da = dh * b * s * (1.0 + a * (1.0 - s))
         db = dh * silu(a)
         dx += (da @ _f64(W1[i]) + db @ _f64(W3[i]))[0]
-    G = np.zeros(E)
-    G[idx[0].astype(np.int64)] = dgate
-    dlogits = p[0] * (G - np.dot(p[0], G))
+    dlogits = route_backward(p, idx, gate, dgate[None, :], gating, renorm)[0]
     return dx, dgate, dlogits
 
 

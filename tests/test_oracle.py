@@ -88,6 +88,113 @@ def test_softmax_closed_forms():
     assert abs(lse3[0] - (2.5 + math.log(6))) < 1e-14
 
 
+# ---------------------------------------------------------------- router variants
+
+VARIANTS = [("softmax", False), ("softmax", True), ("sigmoid", False), ("sigmoid", True)]
+
+
+def _dyadic_logits(rng, T, E, spacing=2.0 ** -5):
+    """Distinct logits on a grid of 2^-5 (exact in float32, and so is any
+    value +- 2^-10), shuffled per row: the top-k cannot change under a
+    perturbation of 2^-10."""
+    base = (np.arange(E) - E / 2) * spacing * 7
+    return np.stack([rng.permutation(base) for _ in range(T)]).astype(np.float32)
+
+
+def test_router_variant_gates_closed_forms():
+    rng = _rng(31)
+    T, E, k = 9, 11, 4
+    lg = _dyadic_logits(rng, T, E)
+    idx, g_sig, _, _ = O.route(lg, k, "sigmoid", False)
+    _, g_sm_n, _, _ = O.route(lg, k, "softmax", True)
+    _, g_sig_n, _, _ = O.route(lg, k, "sigmoid", True)
+    idx0, _, _, _ = O.route(lg, k)
+    np.testing.assert_array_equal(idx, idx0)  # same selection in every variant
+    for t in range(T):
+        chosen = [float(lg[t, e]) for e in idx[t]]
+        sig = [1.0 / (1.0 + math.exp(-v)) for v in chosen]
+        # sigmoid gates: the logistic function of each chosen logit
+        np.testing.assert_allclose(g_sig[t], sig, rtol=1e-15)
+        # renormalised softmax = the softmax of the chosen logits alone
+        m = max(chosen)
+        ex = [math.exp(v - m) for v in chosen]
+        np.testing.assert_allclose(g_sm_n[t], [v / math.fsum(ex) for v in ex], rtol=1e-14)
+        # renormalised sigmoid: proportional to the sigmoid, summing to one
+        np.testing.assert_allclose(g_sig_n[t], [v / math.fsum(sig) for v in sig], rtol=1e-14)
+        assert abs(math.fsum(g_sig_n[t]) - 1.0) < 1e-15
+
+
+def test_router_variant_special_cases():
+    rng = _rng(32)
+    T, E = 6, 7
+    lg = _dyadic_logits(rng, T, E)
+    # k = E: renormalising the softmax over all experts changes nothing
+    _, g_all, _, p = O.route(lg, E, "softmax", True)
+    _, g_plain, _, _ = O.route(lg, E, "softmax", False)
+    np.testing.assert_allclose(g_all, g_plain, rtol=1e-14)
+    # k = 1 with renormalisation: the gate is exactly 1 and no gradient reaches the logits
+    for gating in ("softmax", "sigmoid"):
+        idx, g1, _, p1 = O.route(lg, 1, gating, True)
+        np.testing.assert_array_equal(g1, 1.0)
+        dl = O.route_backward(p1, idx, g1, rng.standard_normal((T, 1)), gating, True)
+        np.testing.assert_allclose(dl, 0.0, atol=1e-15)
+    # sigmoid without renormalisation: only the chosen logits get a gradient
+    idx, g, _, ps = O.route(lg, 3, "sigmoid", False)
+    dl = O.route_backward(ps, idx, g, np.ones((T, 3)), "sigmoid", False)
+    mask = np.zeros((T, E), bool)
+    np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+    np.testing.assert_array_equal(dl[~mask], 0.0)
+
+
+@pytest.mark.parametrize("gating,renorm", VARIANTS)
+def test_route_backward_central_differences(gating, renorm):
+    """d/dl of sum_j w_j gate_j(l), from route() itself at l +- 2^-10 (exact in
+    float32, selection unchanged), against route_backward()."""
+    rng = _rng(33)
+    T, E, k = 5, 9, 3
+    lg = _dyadic_logits(rng, T, E)
+    w = rng.standard_normal((T, k))
+    idx, gate, _, p = O.route(lg, k, gating, renorm)
+    dl = O.route_backward(p, idx, gate, w, gating, renorm)
+    h = 2.0 ** -10
+    for t in range(T):
+        for e in range(E):
+            vals = []
+            for sgn in (1, -1):
+                l2 = lg.copy()
+                l2[t, e] = np.float32(float(lg[t, e]) + sgn * h)
+                i2, g2, _, _ = O.route(l2, k, gating, renorm)
+                np.testing.assert_array_equal(i2, idx)
+                vals.append(float((w[t] * g2[t]).sum()))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert abs(fd - dl[t, e]) <= 2e-7 + 1e-5 * np.abs(dl[t]).max(), (gating, renorm, t, e, fd, dl[t, e])
+
+
+@pytest.mark.parametrize("gating,renorm", VARIANTS[1:])
+def test_layer_backward_router_variants_central_differences(gating, renorm):
+    """Whole-layer d(loss)/d(logits) in each router variant from finite
+    differences of forward() (dyadic logits, selection unchanged)."""
+    rng = _rng(34)
+    T, d, E, k, F = 6, 8, 7, 3, 10
+    x = rng.standard_normal((T, d))
+    W1 = rng.standard_normal((E, F, d)) * 0.3
+    W3 = rng.standard_normal((E, F, d)) * 0.3
+    W2 = rng.standard_normal((E, d, F)) * 0.3
+    g = rng.standard_normal((T, d))
+    lg = _dyadic_logits(rng, T, E)
+    bw = O.backward(g, x, lg, W1, W3, W2, k, gating=gating, renorm=renorm)
+    h = 2.0 ** -10
+    for t in range(T):
+        for e in range(E):
+            vals = []
+            for sgn in (1, -1):
+                l2 = lg.copy()
+                l2[t, e] = np.float32(float(lg[t, e]) + sgn * h)
+                vals.append(O.loss(O.forward(x, l2, W1, W3, W2, k, gating=gating, renorm=renorm)["out"], g))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            assert abs(fd - bw["dlogits"][t, e]) <= 1e-6 + 1e-5 * np.abs(bw["dlogits"][t]).max()
+
+
 # ---------------------------------------------------------------- layout
 
 def _brute_layout(idx, E, b, e_end):
