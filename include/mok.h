@@ -67,6 +67,20 @@ typedef enum {
 
 /* Forward writes the intermediates backward needs (A, B pre-activations). */
 #define MOK_FLAG_SAVE_FOR_BACKWARD 0x1u
+/* Router variants, for the DeepSeek-V3-type models the pages name as the
+ * target ([fluid], section "Comment MoK tente de gratter des millisecondes
+ * partout").  The selection is the same in every variant: the top-k of the
+ * raw fp32 logits (value descending, index ascending).  The gates are the
+ * chosen experts' affinities a_e:
+ *   default                 a = softmax of the E logits;
+ *   MOK_FLAG_SIGMOID_GATES  a_e = sigmoid(logit_e);
+ *   MOK_FLAG_RENORM_GATES   gate_j = a_j / (a_0 + ... + a_(k-1)), the sum
+ *                           over the k chosen experts in slot order (fp32).
+ * The backward call must be given the same flags as its forward call; its
+ * d(router logits) is the chain rule through the chosen gates and then the
+ * affinity (softmax Jacobian, or a (1 - a) for the sigmoid). */
+#define MOK_FLAG_SIGMOID_GATES 0x2u
+#define MOK_FLAG_RENORM_GATES 0x4u
 
 typedef struct mok_moe_config {
   int32_t T;                 /* tokens in this call (>= 0)                      */

@@ -40,7 +40,8 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
     return MOK_ERR_INVALID_ARG;
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
-  if (c.flags & ~MOK_FLAG_SAVE_FOR_BACKWARD) return MOK_ERR_INVALID_ARG;
+  if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES))
+    return MOK_ERR_INVALID_ARG;
   if (c.ring_bytes > 0 && c.minibatch_rows == 0) return MOK_ERR_INVALID_ARG;  // a ring needs a minibatch size
   if (c.minibatch_rows > 0) {
     if (c.precision != MOK_PREC_BF16) return MOK_ERR_UNSUPPORTED;
@@ -148,6 +149,11 @@ inline bool fused_pull(const mok_moe_config& c) {
   return c.precision == MOK_PREC_BF16 && c.minibatch_rows == 0 && (int64_t)c.T * c.d * 2 < (int64_t(1) << 31);
 }
 
+// The router variant of a call (kGateSigmoid, kGateRenorm bits).
+static int gating_of(const mok_moe_config& c) {
+  return ((c.flags & MOK_FLAG_SIGMOID_GATES) ? kGateSigmoid : 0) | ((c.flags & MOK_FLAG_RENORM_GATES) ? kGateRenorm : 0);
+}
+
 #define MOK_STAGE(stage, call)                 \
   do {                                         \
     StageMark mark_(c, s, stage);              \
@@ -237,7 +243,8 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
   int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
 
-  MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, topk_idx, topk_gate, s_idx, s_gate, s_lse, s));
+  MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx,
+                                                 s_gate, s_lse, s));
   MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
                                at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
                                s_order, s_rop, s_por, s));
@@ -391,7 +398,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 
   // reverse-combine with the router backward
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
-                               bf16, dgate, drouter_logits, dy, queue, 16, s));
+                               gating_of(c), bf16, dgate, drouter_logits, dy, queue, 16, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;

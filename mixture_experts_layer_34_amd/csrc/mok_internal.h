@@ -34,7 +34,11 @@ struct WorkspaceLayout {
 };
 
 // ----------------------------------------------------------------- launchers
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx_out,
+// Router variant: bit 0 = sigmoid affinities (else softmax), bit 1 = gates
+// renormalised over the chosen experts.
+constexpr int kGateSigmoid = 1, kGateRenorm = 2;
+
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int gating, int32_t* idx_out,
                               float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
                               hipStream_t s);
 
@@ -61,8 +65,8 @@ hipError_t launch_combine(const void* rows, const float* gate, const int32_t* ro
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate,
                                 const int32_t* idx, const int32_t* row_of_pair,
                                 const float* logits, const float* lse, int T, int k, int E, int d,
-                                int bf16, float* dgate, float* dlogits, void* dy, int32_t* queue_zero,
-                                int nqueue, hipStream_t s);
+                                int gating, int bf16, float* dgate, float* dlogits, void* dy,
+                                int32_t* queue_zero, int nqueue, hipStream_t s);
 
 // Grouped GEMMs of the expert FFN.  `offsets` is the global [E+1] array,
 // experts [eb, eb + E_loc) are local.  tile_prefix is the [kNumTileBM, E_loc+1]

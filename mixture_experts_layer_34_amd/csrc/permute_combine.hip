@@ -255,9 +255,18 @@ hipError_t launch_combine(const void* rows, const float* gate, const int32_t* ro
 
 // ------------------------------------------------------------------ reverse-combine + router backward
 // Per token: dgate_j = <dout_t, Y[row_j]> (fixed-order block reduction),
-// dY[row_j] = gate_j * dout_t, then dlogits = p * (G - sum_j gate_j dgate_j)
-// with p = exp(l - lse) and G the dgate values at the chosen experts.
-template <typename T>
+// dY[row_j] = gate_j * dout_t, then d(logits) by the router variant, with
+// s = sum_j gate_j dgate_j (slot order) and G the dgate values at the chosen
+// experts:
+//   softmax:            dlogits = p * (G - s), p = exp(l - lse), every expert;
+//   softmax, renorm:    gate_e * (G_e - s) at the chosen experts, 0 elsewhere;
+//   sigmoid:            gate_e * (1 - sigmoid(l_e)) * G_e at the chosen experts;
+//   sigmoid, renorm:    gate_e * (1 - sigmoid(l_e)) * (G_e - s) there.
+// (With renorm, gate_j = a_j / S and d(a_i) = (G_i - s) / S; the softmax
+// Jacobian then gives p_e (G_e - s) / S = gate_e (G_e - s) at the chosen
+// experts and 0 elsewhere, since the chosen (G_i - s) average to zero under
+// p; the sigmoid's derivative a (1 - a) gives the sigmoid lines.)
+template <typename T, int GATING>
 __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict__ dout, const T* __restrict__ Y,
                                                             const float* __restrict__ gate,
                                                             const int32_t* __restrict__ idx,
@@ -301,16 +310,32 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
       }
       __syncthreads();
     }
+    constexpr bool SIGM = GATING & kGateSigmoid, RENORM = GATING & kGateRenorm;
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s = fmaf(gate[(int64_t)t * k + j], dg[j], s);
+    if (!SIGM || RENORM)
+      for (int j = 0; j < k; ++j) s = fmaf(gate[(int64_t)t * k + j], dg[j], s);
     for (int j = threadIdx.x; j < k; j += 256) dgate[(int64_t)t * k + j] = dg[j];
     const float l0 = lse[t];
     for (int e = threadIdx.x; e < E; e += 256) {
-      const float p = expf(logits[(int64_t)t * E + e] - l0);
-      float G = 0.f;
+      const float l = logits[(int64_t)t * E + e];
+      float G = 0.f, ge = 0.f;
+      bool chosen = false;
       for (int j = 0; j < k; ++j)
-        if (sel[j] == e) G = dg[j];
-      dlogits[(int64_t)t * E + e] = p * (G - s);
+        if (sel[j] == e) {
+          G = dg[j];
+          ge = gate[(int64_t)t * k + j];
+          chosen = true;
+        }
+      float out;
+      if constexpr (!SIGM && !RENORM) {
+        out = expf(l - l0) * (G - s);
+      } else if (!chosen) {
+        out = 0.f;
+      } else {
+        const float c = SIGM ? 1.0f - 1.0f / (1.0f + expf(-l)) : 1.0f;
+        out = ge * c * (G - s);
+      }
+      dlogits[(int64_t)t * E + e] = out;
     }
     __syncthreads();
   }
@@ -318,17 +343,26 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
 
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate, const int32_t* idx,
                                 const int32_t* row_of_pair, const float* logits, const float* lse, int T, int k,
-                                int E, int d, int bf16, float* dgate, float* dlogits, void* dy, int32_t* queue_zero,
-                                int nqueue, hipStream_t s) {
+                                int E, int d, int gating, int bf16, float* dgate, float* dlogits, void* dy,
+                                int32_t* queue_zero, int nqueue, hipStream_t s) {
   int blocks = T < 16384 ? (T > 0 ? T : 1) : 16384;  // at least one block: it zeroes the counters
-  if (bf16)
-    hipLaunchKernelGGL(backward_gate_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)dout,
-                       (const bf16_t*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits,
-                       (bf16_t*)dy, queue_zero, nqueue);
-  else
-    hipLaunchKernelGGL(backward_gate_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)dout,
-                       (const float*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits,
-                       (float*)dy, queue_zero, nqueue);
+#define MOK_BWD_GATE(TT, GV)                                                                                     \
+  hipLaunchKernelGGL((backward_gate_kernel<TT, GV>), dim3(blocks), dim3(256), 0, s, (const TT*)dout, (const TT*)Y, \
+                     gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits, (TT*)dy, queue_zero, nqueue)
+#define MOK_BWD_GATE_T(TT)                                         \
+  switch (gating & (kGateSigmoid | kGateRenorm)) {                 \
+    case 0: MOK_BWD_GATE(TT, 0); break;                            \
+    case kGateSigmoid: MOK_BWD_GATE(TT, kGateSigmoid); break;      \
+    case kGateRenorm: MOK_BWD_GATE(TT, kGateRenorm); break;        \
+    default: MOK_BWD_GATE(TT, kGateSigmoid | kGateRenorm); break; \
+  }
+  if (bf16) {
+    MOK_BWD_GATE_T(bf16_t)
+  } else {
+    MOK_BWD_GATE_T(float)
+  }
+#undef MOK_BWD_GATE_T
+#undef MOK_BWD_GATE
   return hipGetLastError();
 }
 

@@ -18,14 +18,18 @@ namespace mok {
 
 // ------------------------------------------------------------------ router
 // One wave per token; lane l holds logits e = l + 64 i.  k rounds of a wave
-// arg-max under the (value desc, index asc) order.
-template <int EPL>
+// arg-max under the (value desc, index asc) order.  Gates: the softmax
+// probability of the chosen expert, or its sigmoid (SIGM); with RENORM each
+// is divided by their sum over the k chosen experts (slot order, fp32).
+constexpr int kRouterMaxK = 1024;  // k <= E <= 1024
+template <int EPL, bool SIGM, bool RENORM>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int32_t* __restrict__ idx_out,
                                                           float* __restrict__ gate_out,
                                                           int32_t* __restrict__ idx_saved,
                                                           float* __restrict__ gate_saved,
                                                           float* __restrict__ lse_out) {
+  __shared__ float renorm_buf[RENORM ? 4 * kRouterMaxK : 1];
   const int lane = lane_id();
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
@@ -49,6 +53,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     s = wave_sum(s);
     const float inv_s = 1.0f / s;
     uint32_t taken = 0;
+    float gsum = 0.f;
+    float* graw = RENORM ? renorm_buf + (threadIdx.x >> 6) * kRouterMaxK : renorm_buf;  // this wave's raw gates
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int be = 0x7FFFFFFF;
@@ -71,32 +77,59 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       }
       if ((be & 63) == lane) taken |= 1u << (be >> 6);
       if (lane == 0) {
-        float g = expf(bv - m) * inv_s;
+        const float g = SIGM ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) * inv_s;
         idx_out[(int64_t)t * k + j] = be;
-        gate_out[(int64_t)t * k + j] = g;
         idx_saved[(int64_t)t * k + j] = be;
-        gate_saved[(int64_t)t * k + j] = g;
+        if constexpr (RENORM) {
+          graw[j] = g;
+          gsum += g;
+        } else {
+          gate_out[(int64_t)t * k + j] = g;
+          gate_saved[(int64_t)t * k + j] = g;
+        }
       }
     }
-    if (lane == 0) lse_out[t] = m + logf(s);
+    if (lane == 0) {
+      lse_out[t] = m + logf(s);
+      if constexpr (RENORM) {
+        for (int j = 0; j < k; ++j) {
+          const float g = graw[j] / gsum;
+          gate_out[(int64_t)t * k + j] = g;
+          gate_saved[(int64_t)t * k + j] = g;
+        }
+      }
+    }
   }
 }
 
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* idx_out,
-                              float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
-                              hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  int blocks = (T + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
-  dim3 g(blocks), b(256);
-#define MOK_ROUTER(EPLV) \
-  hipLaunchKernelGGL(router_topk_kernel<EPLV>, g, b, 0, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse)
+template <bool SIGM, bool RENORM>
+static void launch_router_variant(dim3 g, dim3 b, hipStream_t s, const float* logits, int T, int E, int k,
+                                  int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved,
+                                  float* lse) {
+#define MOK_ROUTER(EPLV)                                                                                   \
+  hipLaunchKernelGGL((router_topk_kernel<EPLV, SIGM, RENORM>), g, b, 0, s, logits, T, E, k, idx_out, gate_out, \
+                     idx_saved, gate_saved, lse)
   if (E <= 64) MOK_ROUTER(1);
   else if (E <= 128) MOK_ROUTER(2);
   else if (E <= 256) MOK_ROUTER(4);
   else if (E <= 512) MOK_ROUTER(8);
   else MOK_ROUTER(16);
 #undef MOK_ROUTER
+}
+
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int gating, int32_t* idx_out,
+                              float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int blocks = (T + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 g(blocks), b(256);
+  switch (gating & (kGateSigmoid | kGateRenorm)) {
+    case 0: launch_router_variant<false, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
+    case kGateSigmoid: launch_router_variant<true, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
+    case kGateRenorm: launch_router_variant<false, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
+    default: launch_router_variant<true, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
+  }
   return hipGetLastError();
 }
 

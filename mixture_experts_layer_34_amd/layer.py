@@ -23,6 +23,8 @@ class MoeShape:
     minibatch_rows: int = 0
     ring_bytes: int = 0
     save_for_backward: bool = False
+    gating: str = "softmax"       # router affinities: "softmax" or "sigmoid"
+    renorm: bool = False          # gates renormalised over the k chosen experts
 
     @property
     def e_end(self):
@@ -33,9 +35,13 @@ class MoeShape:
         return self.e_end - self.expert_begin
 
     def config(self) -> mok.mok_moe_config:
+        if self.gating not in ("softmax", "sigmoid"):
+            raise ValueError(f"gating must be 'softmax' or 'sigmoid', not {self.gating!r}")
+        flags = ((mok.MOK_FLAG_SAVE_FOR_BACKWARD if self.save_for_backward else 0)
+                 | (mok.MOK_FLAG_SIGMOID_GATES if self.gating == "sigmoid" else 0)
+                 | (mok.MOK_FLAG_RENORM_GATES if self.renorm else 0))
         return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
-                               self.minibatch_rows, self.ring_bytes,
-                               mok.MOK_FLAG_SAVE_FOR_BACKWARD if self.save_for_backward else 0)
+                               self.minibatch_rows, self.ring_bytes, flags)
 
     @property
     def act_dtype(self):

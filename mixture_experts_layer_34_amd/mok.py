@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libmok.so")
 MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE, MOK_ERR_HIP, MOK_ERR_DEVICE = range(6)
 MOK_PREC_F32, MOK_PREC_BF16, MOK_PREC_MXFP8 = range(3)
 MOK_FLAG_SAVE_FOR_BACKWARD = 0x1
+MOK_FLAG_SIGMOID_GATES = 0x2
+MOK_FLAG_RENORM_GATES = 0x4
 STAGES = ["router", "sort", "dispatch", "gemm_up", "gemm_down", "combine", "bwd_gate", "gemm_dh", "gemm_dx",
           "reduce_dx", "gemm_dw2", "regather", "gemm_dw13"]
 MOK_NUM_STAGES = len(STAGES)

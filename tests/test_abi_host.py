@@ -51,6 +51,13 @@ def test_workspace_query_rejects_bad_configs(over, k):
     assert ei.value.status == mok.MOK_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("flags", [mok.MOK_FLAG_SIGMOID_GATES, mok.MOK_FLAG_RENORM_GATES,
+                                   mok.MOK_FLAG_SIGMOID_GATES | mok.MOK_FLAG_RENORM_GATES | mok.MOK_FLAG_SAVE_FOR_BACKWARD])
+def test_workspace_query_accepts_router_variants(flags):
+    ws, sv = mok.mok_moe_workspace_query(_cfg(flags=flags), 2)
+    assert ws > 0 and sv > 0
+
+
 def test_saved_layout_is_ordered_and_aligned():
     cfg = _cfg(T=1000, d=256, E=16, ffn=192)
     lay = mok.mok_moe_saved_layout(cfg, 4)
