@@ -168,9 +168,10 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *   W1, W3         [E_loc, F, d]   gate / up projections (act type; E4M3
  *                                  bytes for MXFP8)
  *   W2             [E_loc, d, F]   down projection (act type; E4M3 for MXFP8)
- *   w_scales       MXFP8 only, else NULL: E8M0 bytes, concatenated
- *                  [E_loc, F, d/32] for W1, then [E_loc, F, d/32] for W3,
- *                  then [E_loc, d, F/32] for W2 (see mok_quantize_mxfp8)
+ *   w_scales       MXFP8 only, else NULL: E8M0 bytes, concatenated: those
+ *                  of W1 as a [E_loc*F, d] matrix, then of W3 (same), then
+ *                  of W2 as a [E_loc*d, F] matrix, each in the pair-plane
+ *                  layout that mok_quantize_mxfp8 writes
  *   out            act   [T, d]    sum_j gate[t,j] * y(t,j), j ascending, in
  *                                  fp32, rounded once; rows of tokens with no
  *                                  local pair are 0
@@ -219,11 +220,18 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
  * 32 consecutive elements of a row, scale X = 2^(floor(log2 amax) - 8) stored
  * as an E8M0 byte (exponent + 127, clamped to [0, 254]; an all-zero block
  * stores 0), elements E4M3(v / X) rounded to nearest even, saturating at 448.
- *   src_bf16  [rows, K]      K a multiple of 32
+ *   src_bf16  [rows, K]      K a multiple of 64, rows * K / 32 < 2^32
  *   dst_e4m3  [rows, K]      bytes
- *   dst_e8m0  [rows, K/32]   bytes
+ *   dst_e8m0  rows * K / 32 bytes in pair planes: the scale of block b of
+ *             row r (elements 32 b .. 32 b + 31) at byte
+ *             (b / 2) * 2 rows + 2 r + (b % 2), i.e. a [K/64, rows, 2] array,
+ *             so that the scales of consecutive rows for one 64-wide K step
+ *             are adjacent (the GEMMs copy them 128 contiguous bytes at a
+ *             time; the layer's own activation scales use the same layout)
  * Used for the weights (once per weight update, outside the layer call); the
  * layer quantises activations itself, inside its dispatch and SwiGLU steps.
+ * Errors: MOK_ERR_INVALID_ARG for a null or misaligned pointer, K not a
+ * multiple of 64, or a scale array of 2^32 bytes or more.
  */
 mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K,
                               uint8_t* dst_e4m3, uint8_t* dst_e8m0, void* stream);

@@ -13,6 +13,9 @@
 // stages in flight, the same swizzle, direct-to-LDS copies, barrier placement
 // and tile schedule.  Each stage also carries the two E8M0 bytes of every
 // tile row (2-byte copies that land zero-extended in one LDS dword per row).
+// Scales are stored in pair planes (see mok_quantize_mxfp8): the two bytes of
+// one row for one stage are a 2-byte word of plane k0 / 64, next to those of
+// the next row, so a wave's scale copy reads 128 contiguous bytes.
 // Scaled-MFMA operand layout on gfx950 (checked on the device): lane l holds
 // row l % 32; with h = l / 32 its bytes 0-15 are K [16h, 16h + 16) and bytes
 // 16-31 are K [32 + 16h, +16), and the scale it supplies covers the 32-block
@@ -56,7 +59,8 @@ struct MxJob {
   };
 
   const GroupedGemmArgs* args;
-  int K, N, KS;
+  int K, N;
+  uint32_t psA, psB;  // bytes per scale plane of A (P_max rows) and of B (E_loc * N rows)
   TileCoord c;
   int wid, lane, wm, wn, nk;
   i32x4_t rsA, rsB0, rsB1, rsSA, rsSB0, rsSB1;
@@ -66,7 +70,6 @@ struct MxJob {
     args = &a;
     K = KIND == KIND_UP ? a.d : a.F;
     N = KIND == KIND_UP ? a.F : a.d;
-    KS = K / 32;
     c = tc;
     lane = threadIdx.x & 63;
     wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -80,10 +83,17 @@ struct MxJob {
     rsB0 = make_rsrc((const uint8_t*)a.B0 + c.e_loc * wst + (int64_t)c.n0 * K, (uint32_t)(nb_rows * K));
     rsB1 = make_rsrc((const uint8_t*)(NB == 2 ? a.B1 : a.B0) + c.e_loc * wst + (int64_t)c.n0 * K,
                      (uint32_t)(nb_rows * K));
-    rsSA = make_rsrc(a.a_scale + (int64_t)c.row0 * KS, (uint32_t)(rows * KS));
-    rsSB0 = make_rsrc(a.b_scale0 + ((int64_t)c.e_loc * N + c.n0) * KS, (uint32_t)(nb_rows * KS));
-    rsSB1 = make_rsrc((NB == 2 ? a.b_scale1 : a.b_scale0) + ((int64_t)c.e_loc * N + c.n0) * KS,
-                      (uint32_t)(nb_rows * KS));
+    // scale resources from this tile's first row to the end of the last
+    // plane; rows past the tile read other rows' bytes (finite E8M0 codes, or
+    // zero past the end), which only reach output rows that are not stored
+    const int64_t pa = (int64_t)a.P_max * 2, pb = (int64_t)a.E_loc * N * 2;
+    psA = (uint32_t)pa;
+    psB = (uint32_t)pb;
+    const int64_t planes = K / 64;
+    const int64_t fb = ((int64_t)c.e_loc * N + c.n0) * 2;
+    rsSA = make_rsrc(a.a_scale + (int64_t)c.row0 * 2, (uint32_t)(planes * pa - (int64_t)c.row0 * 2));
+    rsSB0 = make_rsrc(a.b_scale0 + fb, (uint32_t)(planes * pb - fb));
+    rsSB1 = make_rsrc((NB == 2 ? a.b_scale1 : a.b_scale0) + fb, (uint32_t)(planes * pb - fb));
 #pragma unroll
     for (int q = 0; q < IA; ++q) {
       const int r = (wid * IA + q) * 16 + (lane >> 2);
@@ -98,9 +108,9 @@ struct MxJob {
     // scale copies: wave w brings A rows 64 w .. 64 w + 63 and, in lanes 0-31,
     // B rows 32 w .. 32 w + 31 (UP: of W1 for w < 2, of W3 after); lanes 32-63
     // of the B copy read past the resource and land zero in unused dwords
-    offSA = (uint32_t)((wid * 64 + lane) * KS);
+    offSA = (uint32_t)((wid * 64 + lane) * 2);
     const int rb = wid * 32 + lane;
-    offSB = lane < 32 ? (uint32_t)(((NB == 2 && rb >= BN) ? rb - BN : rb) * KS) : 0xFFFFFFF0u;
+    offSB = lane < 32 ? (uint32_t)(((NB == 2 && rb >= BN) ? rb - BN : rb) * 2) : 0xFFFFFFF0u;
   }
 
   // Copies [Q0, Q1) of stage s (A data, B data, A scales, B scales).
@@ -116,9 +126,10 @@ struct MxJob {
       if (IA + q >= Q0 && IA + q < Q1)
         dma_b128((NB == 2 && (wid * IB + q) * 16 >= BN) ? rsB1 : rsB0, lds_addr(st + A_BYTES + (wid * IB + q) * 1024),
                  offB[q], k0);
-    if (IA + IB >= Q0 && IA + IB < Q1) dma_u16(rsSA, lds_addr(st + SCA + wid * 256), offSA, k0 / 32);
+    if (IA + IB >= Q0 && IA + IB < Q1) dma_u16(rsSA, lds_addr(st + SCA + wid * 256), offSA, (uint32_t)s * psA);
     if (IA + IB + 1 >= Q0 && IA + IB + 1 < Q1)
-      dma_u16((NB == 2 && wid * 32 >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB, k0 / 32);
+      dma_u16((NB == 2 && wid * 32 >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB,
+              (uint32_t)s * psB);
   }
   __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
 
@@ -280,7 +291,10 @@ struct MxJob {
               codes[0] = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
               codes[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
               *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
-              if (c8 == 0) a.out_scale[(int64_t)row * (N / 32) + col / 32] = (uint8_t)(se + 127);
+              if (c8 == 0) {
+                const int b = col / 32;  // pair-plane layout of H's scales, P_max rows per plane
+                a.out_scale[(int64_t)(b >> 1) * a.P_max * 2 + (int64_t)row * 2 + (b & 1)] = (uint8_t)(se + 127);
+              }
             }
             __builtin_amdgcn_wave_barrier();
           }

@@ -42,6 +42,13 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
   if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES))
     return MOK_ERR_INVALID_ARG;
+  if (c.precision == MOK_PREC_MXFP8) {
+    // every E8M0 scale array (x and H rows, each weight matrix) fits a 32-bit buffer range
+    const int64_t Tk = (int64_t)c.T * k, kmax = c.d > c.ffn ? c.d : c.ffn;
+    const int64_t E_loc = c.expert_end - c.expert_begin;
+    if (Tk * (kmax / 32) >= (int64_t(1) << 32) || E_loc * c.ffn * (int64_t)(c.d / 32) >= (int64_t(1) << 32))
+      return MOK_ERR_INVALID_ARG;
+  }
   if (c.ring_bytes > 0 && c.minibatch_rows == 0) return MOK_ERR_INVALID_ARG;  // a ring needs a minibatch size
   if (c.minibatch_rows > 0) {
     if (c.precision != MOK_PREC_BF16) return MOK_ERR_UNSUPPORTED;
@@ -260,7 +267,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   if (mx) {
     uint8_t* xq = at<uint8_t>(workspace, wl.xp);
     uint8_t* xs = at<uint8_t>(workspace, wl.xp_scale);
-    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, s));
+    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, wl.xp_rows, s));
     const size_t w13_scales = (size_t)E_loc * F * (d / 32);
     g.A = xq;
     g.a_scale = xs;
@@ -455,7 +462,8 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 
 mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K, uint8_t* dst_e4m3, uint8_t* dst_e8m0,
                               void* stream) {
-  if (rows < 0 || K <= 0 || K % 32) return MOK_ERR_INVALID_ARG;
+  if (rows < 0 || K <= 0 || K % 64) return MOK_ERR_INVALID_ARG;
+  if (rows * (K / 32) >= (int64_t(1) << 32)) return MOK_ERR_INVALID_ARG;  // scale planes addressed in 32 bits
   if (rows == 0) return MOK_OK;
   if (!src_bf16 || !dst_e4m3 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e4m3)) return MOK_ERR_INVALID_ARG;
   MOK_HIP(launch_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, (hipStream_t)stream));

@@ -53,7 +53,7 @@ hipError_t launch_dispatch_gather(const void* x, const int32_t* row_of_pair, int
                                   int bf16, void* xp, hipStream_t s);
 // Same, quantising each row to MXFP8 (E4M3 + E8M0 per 32 along d).
 hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pair, int T, int k,
-                                        int d, uint8_t* xq, uint8_t* xs, hipStream_t s);
+                                        int d, uint8_t* xq, uint8_t* xs, int64_t xs_rows, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q,
                                  uint8_t* sc, hipStream_t s);
 

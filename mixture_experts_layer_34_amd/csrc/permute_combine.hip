@@ -93,7 +93,7 @@ __device__ __forceinline__ void mx_quant8(const uint4 v, uint2& codes, uint8_t& 
 __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ rop, int ntok,
                                                                     int k, int d, uint8_t* __restrict__ xq,
-                                                                    uint8_t* __restrict__ xs) {
+                                                                    uint8_t* __restrict__ xs, int64_t xs_rows) {
   __shared__ int32_t rows[kMaxK];
   __shared__ int nloc;
   const int nv = d / 8;            // multiple of 4: blocks of 32 never straddle lanes groups
@@ -120,7 +120,10 @@ __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t
       if (act) {
         for (int j = 0; j < n; ++j) {
           reinterpret_cast<uint2*>(xq + (int64_t)rows[j] * d)[v] = codes;
-          if ((v & 3) == 0) xs[(int64_t)rows[j] * (d / 32) + (v >> 2)] = sb;
+          if ((v & 3) == 0) {  // pair-plane scale layout, xs_rows rows per plane
+            const int b = v >> 2;
+            xs[(int64_t)(b >> 1) * xs_rows * 2 + (int64_t)rows[j] * 2 + (b & 1)] = sb;
+          }
         }
       }
     }
@@ -129,18 +132,21 @@ __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t
 }
 
 hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pair, int T, int k, int d,
-                                        uint8_t* xq, uint8_t* xs, hipStream_t s) {
+                                        uint8_t* xq, uint8_t* xs, int64_t xs_rows, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = T < 16384 ? T : 16384;
   hipLaunchKernelGGL(dispatch_gather_mxfp8_kernel, dim3(blocks), dim3(256), 0, s, (const bf16_t*)x,
-                     row_of_pair, T, k, d, xq, xs);
+                     row_of_pair, T, k, d, xq, xs, xs_rows);
   return hipGetLastError();
 }
 
 // Quantise a [rows, K] bf16 matrix along its rows.  Vector i covers elements
-// [8i, 8i + 8); K % 32 == 0 keeps each block of 32 inside one row.
+// [8i, 8i + 8); K % 64 == 0 keeps each block of 32 (and each pair of blocks)
+// inside one row.  Scales in pair planes: block b of row r at
+// (b / 2) * 2 rows + 2 r + b % 2.
 __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16_t* __restrict__ src, int64_t nvec,
-                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+                                                             int64_t rows, int64_t K, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sc) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   const int64_t iters = (nvec + stride - 1) / stride;
   for (int64_t it = 0; it < iters; ++it) {
@@ -152,7 +158,10 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16_t* __res
     mx_quant8(val, codes, sb);
     if (act) {
       reinterpret_cast<uint2*>(q)[v] = codes;
-      if ((v & 3) == 0) sc[v >> 2] = sb;
+      if ((v & 3) == 0) {
+        const int64_t r = (8 * v) / K, b = ((8 * v) % K) / 32;
+        sc[(b >> 1) * rows * 2 + r * 2 + (b & 1)] = sb;
+      }
     }
   }
 }
@@ -164,7 +173,7 @@ hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)src, nvec,
-                     q, sc);
+                     rows, K, q, sc);
   return hipGetLastError();
 }
 

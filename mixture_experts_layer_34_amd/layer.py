@@ -105,10 +105,19 @@ class MoeBuffers:
 
 
 def quantize_mxfp8(w: torch.Tensor):
-    """E4M3 codes and E8M0 scales of a bf16 tensor along its last axis."""
+    """E4M3 codes and E8M0 scales of a bf16 tensor along its last axis.
+
+    Scales come in the library's pair-plane layout, shape [K/64, rows, 2]
+    with rows = numel / K (see scales_by_row for the [rows, K/32] view)."""
     K = w.shape[-1]
     rows = w.numel() // K
     q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    sc = torch.empty(w.shape[:-1] + (K // 32,), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((K // 64, rows, 2), dtype=torch.uint8, device=w.device)
     mok.mok_quantize_mxfp8(w, rows, K, q, sc, _stream())
     return q, sc
+
+
+def scales_by_row(sc: torch.Tensor) -> torch.Tensor:
+    """[rows, K/32] view (a copy) of pair-plane scales [K/64, rows, 2]."""
+    planes, rows, _ = sc.shape
+    return sc.permute(1, 0, 2).reshape(rows, planes * 2)

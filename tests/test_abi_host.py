@@ -112,6 +112,7 @@ def test_backward_error_paths_before_launch():
 def test_quantize_rejects_bad_shapes():
     L = mok.lib()
     assert L.mok_quantize_mxfp8(0x1000, 4, 48, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_quantize_mxfp8(0x1000, 4, 96, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG  # K % 64
     assert L.mok_quantize_mxfp8(0x1000, -1, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_quantize_mxfp8(None, 4, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_quantize_mxfp8(0x1000, 0, 64, 0x2000, 0x3000, None) == mok.MOK_OK

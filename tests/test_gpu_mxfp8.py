@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import mok_oracle as O
-from mixture_experts_layer_34_amd.layer import quantize_mxfp8
+from mixture_experts_layer_34_amd.layer import quantize_mxfp8, scales_by_row
 from tests.gpu_case import note
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,12 @@ def test_quantize_mxfp8_bit_exact():
     q, sc = quantize_mxfp8(w.cuda())
     torch.cuda.synchronize()
     ref_q, ref_s = O.mxfp8_quantize(w.float().numpy())
-    assert np.array_equal(sc.cpu().numpy(), ref_s), "E8M0 scales differ"
+    assert np.array_equal(scales_by_row(sc).cpu().numpy(), ref_s), "E8M0 scales differ"
+    # the pair-plane layout itself: block b of row r at (b / 2) * 2 rows + 2 r + b % 2
+    flat = sc.reshape(-1).cpu().numpy()
+    rows, nb = ref_s.shape
+    for r, b in [(0, 0), (0, 1), (1, 0), (5, 3), (rows - 1, nb - 1), (rows // 2, nb // 2 + 1)]:
+        assert flat[(b // 2) * 2 * rows + 2 * r + b % 2] == ref_s[r, b]
     assert np.array_equal(q.cpu().numpy(), ref_q), "E4M3 codes differ"
 
 
@@ -55,10 +60,11 @@ def test_quantize_mxfp8_batched_weights_layout():
     w = (torch.randn(3, 64, 256, generator=g) * 0.02).to(torch.bfloat16)
     q, sc = quantize_mxfp8(w.cuda())
     torch.cuda.synchronize()
-    assert q.shape == (3, 64, 256) and sc.shape == (3, 64, 8)
+    assert q.shape == (3, 64, 256) and sc.shape == (4, 3 * 64, 2)
+    by_row = scales_by_row(sc).reshape(3, 64, 8)
     for e in range(3):
         rq, rs = O.mxfp8_quantize(w[e].float().numpy())
-        assert np.array_equal(q[e].cpu().numpy(), rq) and np.array_equal(sc[e].cpu().numpy(), rs)
+        assert np.array_equal(q[e].cpu().numpy(), rq) and np.array_equal(by_row[e].cpu().numpy(), rs)
 
 
 def _run_and_oracle(w, inp, tokens=None):
