@@ -59,7 +59,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "route", "route_backward", "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
+    "route", "route_backward", "router_logits", "router_logits_backward",
+    "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
     "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
     "forward_token", "backward_token", "expert_weight_grads",
@@ -142,6 +143,20 @@ def route_backward(p, idx, gate, dgate, gating: str = "softmax", renorm: bool = 
     if gating == "softmax":
         return p * (DA - (p * DA).sum(axis=1, keepdims=True))
     return p * (1.0 - p) * DA
+
+
+def router_logits(x, Wr):
+    """Router GEMM: logits [T,E] = x [T,d] . Wr^T, Wr [E,d] one row per expert
+    (the router's linear layer).  The benchmarked layer covers routing as
+    well as the expert FFNs [kucoin §03]; float64."""
+    return _f64(x) @ _f64(Wr).T
+
+
+def router_logits_backward(x, Wr, dlogits):
+    """Gradients through router_logits: dx = dlogits . Wr [T,d] and
+    dWr = dlogits^T . x [E,d]; float64."""
+    g = _f64(dlogits)
+    return g @ _f64(Wr), g.T @ _f64(x)
 
 
 # ------------------------------------------------------------------ layout

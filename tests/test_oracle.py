@@ -88,6 +88,41 @@ def test_softmax_closed_forms():
     assert abs(lse3[0] - (2.5 + math.log(6))) < 1e-14
 
 
+# ---------------------------------------------------------------- router GEMM
+
+def test_router_logits_closed_forms():
+    """One-hot tokens pick columns of Wr^T; a shifted identity moves them; E = 1
+    is a dot product in scalar math.  A transposed operand fails the first."""
+    d, E = 6, 4
+    Wr = np.arange(E * d, dtype=np.float64).reshape(E, d) / 7.0
+    x = np.zeros((d, d)); x[np.arange(d), np.arange(d)] = 1.0       # token i = e_i
+    np.testing.assert_array_equal(O.router_logits(x, Wr), Wr.T)    # logit[i, e] = Wr[e, i]
+    S = np.roll(np.eye(d), 1, axis=1)                               # Wr row e = e_(e+1)
+    expect = [[1.0 if i == e + 1 else 0.0 for e in range(E)] for i in range(d)]  # token i hits expert i - 1
+    np.testing.assert_array_equal(O.router_logits(x, S[:E]), expect)
+    rng = _rng(41)
+    xv, w = rng.standard_normal((3, 9)), rng.standard_normal((1, 9))
+    for t in range(3):
+        assert abs(O.router_logits(xv, w)[t, 0] - math.fsum(xv[t, i] * w[0, i] for i in range(9))) < 1e-14
+
+
+def test_router_logits_backward_central_differences():
+    rng = _rng(42)
+    T, d, E = 5, 7, 3
+    x, Wr, G = rng.standard_normal((T, d)), rng.standard_normal((E, d)), rng.standard_normal((T, E))
+    dx, dWr = O.router_logits_backward(x, Wr, G)
+    L = lambda xx, ww: float((O.router_logits(xx, ww) * G).sum())
+    h = 1e-6
+    for t in range(T):
+        for i in range(d):
+            xp, xm = x.copy(), x.copy(); xp[t, i] += h; xm[t, i] -= h
+            assert abs((L(xp, Wr) - L(xm, Wr)) / (2 * h) - dx[t, i]) < 1e-7
+    for e in range(E):
+        for i in range(d):
+            wp, wm = Wr.copy(), Wr.copy(); wp[e, i] += h; wm[e, i] -= h
+            assert abs((L(x, wp) - L(x, wm)) / (2 * h) - dWr[e, i]) < 1e-7
+
+
 # ---------------------------------------------------------------- router variants
 
 VARIANTS = [("softmax", False), ("softmax", True), ("sigmoid", False), ("sigmoid", True)]
