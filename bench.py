@@ -157,6 +157,46 @@ def cpu_baseline(w, inp, sample_tokens: int):
                       f"{dt:.1f} s"}
 
 
+def router_gemm_bench(w, x, K, Wm, ev, sh):
+    """The router GEMM logits = x Wr^T and its backward (dx, dWr) at this
+    workload's T, d, E with a synthetic Wr and dlogits, timed apart from the
+    layer step (the layer takes the logits as an input).  Roofline per call:
+    algorithmic bytes = each operand read once and each output written once;
+    flops = 2 T d E per product; bound = the longer of HBM and bf16 MFMA time."""
+    import torch
+
+    import workloads as W
+    from mixture_experts_layer_34_amd import mok
+
+    T, d = x.shape
+    E = w.E
+    r = W.make_router_inputs(w.seed, 1, d, E, device=x.device)
+    Wr = r["Wr"]
+    g = W.normal(w.seed, W.S_DLOGIT, torch.arange(T, device=x.device), E)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    dx = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    dWr = torch.empty((E, d), dtype=torch.float32, device=x.device)
+    fwd = lambda: mok.mok_router_logits(x, Wr, T, d, E, logits, sh)
+    bwd = lambda: mok.mok_router_logits_backward(x, Wr, g, T, d, E, dx, dWr, sh)
+    out = {"shape": f"T={T} d={d} E={E}"}
+    for name, fn, flops, nbytes in (
+            ("forward", fwd, 2.0 * T * d * E, T * d * 2 + E * d * 2 + T * E * 4),
+            ("backward", bwd, 4.0 * T * d * E, T * E * 4 + E * d * 2 + T * d * 2 + T * d * 4 + E * d * 4)):
+        for _ in range(Wm):
+            fn()
+        a, b = ev.create(2)
+        ev.record(a, sh)
+        for _ in range(K):
+            fn()
+        ev.record(b, sh)
+        ms = ev.elapsed_ms(a, b) / K
+        roof = roof_of(flops, nbytes, ms, PEAK_TFLOPS["bf16"])
+        out[name] = {"ms": round(ms, 4), "bound": roof["bound"], "achieved": roof["achieved"], "unit": roof["unit"],
+                     "frac": roof["frac"], "per_call": f"{flops / 1e9:.2f} GFLOP, {nbytes / 1e6:.1f} MB"}
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +360,8 @@ def main():
         "graph_replay": graph_res,
         "wall_s": round(wall, 3),
     }
+    if inp["x"].dtype == torch.bfloat16 and not args.minibatch_rows:
+        result["router_gemm"] = router_gemm_bench(w, inp["x"], K, Wm, ev, sh)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
     else:

@@ -236,6 +236,40 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K,
                               uint8_t* dst_e4m3, uint8_t* dst_e8m0, void* stream);
 
+/*
+ * Router GEMM: the scores the router step consumes ([kucoin §01]: the router
+ * scores each token against every expert before the top-k choice; here a
+ * score is the dot product of the token with the expert's router vector):
+ *   logits[t, e] = sum_i x[t, i] * Wr[e, i]
+ *   x       bf16  [T, d]
+ *   Wr      bf16  [E, d]   one row per expert
+ *   logits  float [T, E]   overwritten; products exact, fp32 accumulation in
+ *                          an order fixed by (T, d, E)
+ * d a multiple of 64 and at most 65536, 1 <= E <= 1024, 0 <= T <= 2^24;
+ * x and Wr 16-byte aligned.  The result feeds mok_moe_forward's
+ * router_logits.
+ * Errors: MOK_ERR_INVALID_ARG for a null or misaligned pointer or a shape
+ * outside these bounds; MOK_ERR_HIP for a failed launch.
+ */
+mok_status mok_router_logits(const void* x, const void* Wr, int32_t T, int32_t d, int32_t E,
+                             float* logits, void* stream);
+
+/*
+ * Gradients through mok_router_logits of L = sum(logits * dlogits):
+ *   dlogits float [T, E]   e.g. mok_moe_backward's drouter_logits
+ *   dx      float [T, d] = dlogits . Wr     (overwritten)
+ *   dWr     float [E, d] = dlogits^T . x    (overwritten; T = 0 gives 0)
+ * dlogits enters the bf16 matrix cores as a bf16 value plus a bf16 residual
+ * (relative residual below 2^-17); x and Wr are exact.  dWr sums the tokens
+ * in slices whose partial products are kept in dx's memory before dx is
+ * written, then adds the slices in ascending order: dx must not overlap
+ * dWr, x, Wr or dlogits.  Shapes and pointers as for mok_router_logits;
+ * dx and dWr 16-byte aligned.
+ * Errors: MOK_ERR_INVALID_ARG, MOK_ERR_HIP as for mok_router_logits.
+ */
+mok_status mok_router_logits_backward(const void* x, const void* Wr, const float* dlogits, int32_t T,
+                                      int32_t d, int32_t E, float* dx, float* dWr, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* mok_status_string(mok_status s);
 

@@ -12,6 +12,7 @@
 
 #include "../../include/mok.h"
 #include "mok_internal.h"
+#include "router_gemm.h"
 
 using namespace mok;
 
@@ -467,6 +468,38 @@ mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K, uin
   if (rows == 0) return MOK_OK;
   if (!src_bf16 || !dst_e4m3 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e4m3)) return MOK_ERR_INVALID_ARG;
   MOK_HIP(launch_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, (hipStream_t)stream));
+  return MOK_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// Token arrays (x, logits, dlogits, dx) may be NULL when T = 0.
+mok_status validate_router(const void* x, const void* Wr, int32_t T, int32_t d, int32_t E) {
+  if (T < 0 || T > (1 << 24) || d <= 0 || d % 64 || d > 65536 || E < 1 || E > 1024) return MOK_ERR_INVALID_ARG;
+  if ((T > 0 && !x) || !Wr || !aligned16(x) || !aligned16(Wr)) return MOK_ERR_INVALID_ARG;
+  return MOK_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mok_status mok_router_logits(const void* x, const void* Wr, int32_t T, int32_t d, int32_t E, float* logits,
+                             void* stream) {
+  const mok_status st = validate_router(x, Wr, T, d, E);
+  if (st != MOK_OK) return st;
+  if (T == 0) return MOK_OK;
+  if (!logits) return MOK_ERR_INVALID_ARG;
+  MOK_HIP(launch_router_logits(x, Wr, T, d, E, logits, (hipStream_t)stream));
+  return MOK_OK;
+}
+
+mok_status mok_router_logits_backward(const void* x, const void* Wr, const float* dlogits, int32_t T, int32_t d,
+                                      int32_t E, float* dx, float* dWr, void* stream) {
+  const mok_status st = validate_router(x, Wr, T, d, E);
+  if (st != MOK_OK) return st;
+  if ((T > 0 && (!dlogits || !dx)) || !dWr || !aligned16(dx) || !aligned16(dWr)) return MOK_ERR_INVALID_ARG;
+  MOK_HIP(launch_router_logits_backward(x, Wr, dlogits, T, d, E, dx, dWr, (hipStream_t)stream));
   return MOK_OK;
 }
 

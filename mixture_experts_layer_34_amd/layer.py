@@ -121,3 +121,28 @@ def scales_by_row(sc: torch.Tensor) -> torch.Tensor:
     """[rows, K/32] view (a copy) of pair-plane scales [K/64, rows, 2]."""
     planes, rows, _ = sc.shape
     return sc.permute(1, 0, 2).reshape(rows, planes * 2)
+
+
+def router_logits(x: torch.Tensor, Wr: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 logits [T, E] = x [T, d] . Wr^T for bf16 x and Wr [E, d]."""
+    T, d = x.shape
+    E = Wr.shape[0]
+    if x.dtype != torch.bfloat16 or Wr.dtype != torch.bfloat16 or Wr.shape[1] != d:
+        raise ValueError("router_logits: bf16 x [T, d] and Wr [E, d] expected")
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    mok.mok_router_logits(x.contiguous(), Wr.contiguous(), T, d, E, out, _stream())
+    return out
+
+
+def router_logits_backward(x: torch.Tensor, Wr: torch.Tensor, dlogits: torch.Tensor):
+    """(dx, dWr) = (dlogits . Wr, dlogits^T . x), both fp32."""
+    T, d = x.shape
+    E = Wr.shape[0]
+    if dlogits.dtype != torch.float32 or tuple(dlogits.shape) != (T, E):
+        raise ValueError("router_logits_backward: fp32 dlogits [T, E] expected")
+    dx = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    dWr = torch.empty((E, d), dtype=torch.float32, device=x.device)
+    mok.mok_router_logits_backward(x.contiguous(), Wr.contiguous(), dlogits.contiguous(), T, d, E, dx, dWr,
+                                   _stream())
+    return dx, dWr

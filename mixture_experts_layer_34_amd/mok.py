@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
                                        _P, _P, _P, _P, _P, _P, _P, _P]
         L.mok_quantize_mxfp8.restype = ctypes.c_int
         L.mok_quantize_mxfp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]
+        L.mok_router_logits.restype = ctypes.c_int
+        L.mok_router_logits.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
+        L.mok_router_logits_backward.restype = ctypes.c_int
+        L.mok_router_logits_backward.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                                 _P]
         _lib = L
     return _lib
 
@@ -136,3 +141,12 @@ def mok_moe_backward(dout, x, router_logits, W1, W3, W2, k, cfg, saved, dx, dW1,
 def mok_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, stream=0):
     _check(lib().mok_quantize_mxfp8(_ptr(src_bf16), rows, K, _ptr(dst_e4m3), _ptr(dst_e8m0), stream or None),
            "mok_quantize_mxfp8")
+
+
+def mok_router_logits(x, Wr, T, d, E, logits, stream=0):
+    _check(lib().mok_router_logits(_ptr(x), _ptr(Wr), T, d, E, _ptr(logits), stream or None), "mok_router_logits")
+
+
+def mok_router_logits_backward(x, Wr, dlogits, T, d, E, dx, dWr, stream=0):
+    _check(lib().mok_router_logits_backward(_ptr(x), _ptr(Wr), _ptr(dlogits), T, d, E, _ptr(dx), _ptr(dWr),
+                                            stream or None), "mok_router_logits_backward")

@@ -118,6 +118,32 @@ def test_quantize_rejects_bad_shapes():
     assert L.mok_quantize_mxfp8(0x1000, 0, 64, 0x2000, 0x3000, None) == mok.MOK_OK
 
 
+@pytest.mark.parametrize("T,d,E", [(-1, 128, 8), (64, 96, 8), (64, 0, 8), (64, 65600, 8), (64, 128, 0),
+                                   (64, 128, 1025), ((1 << 24) + 1, 128, 8)])
+def test_router_gemm_rejects_bad_shapes(T, d, E):
+    L = mok.lib()
+    assert L.mok_router_logits(0x1000, 0x2000, T, d, E, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_router_logits_backward(0x1000, 0x2000, 0x3000, T, d, E, 0x4000, 0x5000, None) == \
+        mok.MOK_ERR_INVALID_ARG
+
+
+def test_router_gemm_rejects_bad_pointers():
+    L = mok.lib()
+    assert L.mok_router_logits(None, 0x2000, 8, 64, 4, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_router_logits(0x1008, 0x2000, 8, 64, 4, 0x3000, None) == mok.MOK_ERR_INVALID_ARG  # x misaligned
+    assert L.mok_router_logits(0x1000, 0x2000, 8, 64, 4, None, None) == mok.MOK_ERR_INVALID_ARG
+    bw = L.mok_router_logits_backward
+    assert bw(0x1000, 0x2000, None, 8, 64, 4, 0x4000, 0x5000, None) == mok.MOK_ERR_INVALID_ARG
+    assert bw(0x1000, 0x2000, 0x3000, 8, 64, 4, 0x4004, 0x5000, None) == mok.MOK_ERR_INVALID_ARG  # dx misaligned
+    assert bw(0x1000, 0x2008, 0x3000, 8, 64, 4, 0x4000, 0x5000, None) == mok.MOK_ERR_INVALID_ARG  # Wr misaligned
+    assert bw(0x1000, 0x2000, 0x3000, 8, 64, 4, 0x4000, None, None) == mok.MOK_ERR_INVALID_ARG
+    # no tokens: nothing to compute, nothing enqueued; empty token arrays may be NULL
+    assert L.mok_router_logits(0x1000, 0x2000, 0, 64, 4, 0x3000, None) == mok.MOK_OK
+    assert L.mok_router_logits(None, 0x2000, 0, 64, 4, None, None) == mok.MOK_OK
+    assert L.mok_router_logits(None, None, 0, 64, 4, None, None) == mok.MOK_ERR_INVALID_ARG
+    assert bw(None, 0x2000, None, 0, 64, 4, None, None, None) == mok.MOK_ERR_INVALID_ARG  # dWr is not empty
+
+
 def test_ring_mode_validation():
     # a ring needs a minibatch size
     with pytest.raises(mok.MokError) as ei:

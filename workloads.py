@@ -15,7 +15,8 @@ the other rather than relying on cross-device equality of that last step.
 
 Stream ids: 0 = x, 1 = logit noise, 2 = W1, 3 = W3, 4 = W2, 5 = Wr (router
 weight of the tiny workload), 6 = per-expert logit bias, 7 = incoming output
-gradient, 8 = expert popularity permutation.
+gradient, 8 = expert popularity permutation, 9 = incoming router-logit
+gradient (router GEMM inputs).
 
 Workloads (sizes from the pages' layer benchmark: expert parallelism of 64 with
 2,048 tokens per GPU before routing, and the Kimi-2.5 shape with hidden 7168 and
@@ -42,7 +43,7 @@ _C1 = 0x7FEB352D
 _C2 = 0x5BD1E995
 _GOLD = 0x9E3779B9
 
-S_X, S_LOGIT, S_W1, S_W3, S_W2, S_WR, S_BIAS, S_DOUT, S_PERM = range(9)
+S_X, S_LOGIT, S_W1, S_W3, S_W2, S_WR, S_BIAS, S_DOUT, S_PERM, S_DLOGIT = range(10)
 
 
 def _mix32(x: torch.Tensor) -> torch.Tensor:
@@ -282,3 +283,13 @@ def make_weights(w: Workload, device="cpu") -> dict:
 def regenerate_x_rows(w: Workload, token_ids: torch.Tensor) -> torch.Tensor:
     """Activations of the given tokens, regenerated from their ids alone."""
     return normal(w.seed, S_X, token_ids, w.d).to(w.act_dtype)
+
+
+def make_router_inputs(seed: int, T: int, d: int, E: int, device="cpu") -> dict:
+    """Inputs of the router GEMM: x [T, d] bf16 ~ N(0, 1) (the layer's token
+    stream), Wr [E, d] bf16 ~ N(0, 0.02^2), one row per expert, and an
+    incoming gradient dlogits [T, E] fp32 ~ N(0, 1)."""
+    ids = _rows(T, device)
+    return {"x": normal(seed, S_X, ids, d).to(torch.bfloat16),
+            "Wr": normal(seed, S_WR, _rows(E, device), d, std=0.02).to(torch.bfloat16),
+            "dlogits": normal(seed, S_DLOGIT, ids, E)}
