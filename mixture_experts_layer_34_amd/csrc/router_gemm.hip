@@ -85,12 +85,25 @@ struct Staged {
 };
 
 // a[u] = ap[k0 + ac + u] where k0 + ac + u < alim, else 0; the sixteen bf16
-// at bp + (k0 + br) ld where k0 + br < blim, else 0.
+// at bp + (k0 + br) ld where k0 + br < blim, else 0.  VEC: ap + k0 + ac is
+// 16-byte aligned and alim a multiple of 4, so the eight floats come as two
+// 16-byte loads, each wholly inside or wholly outside the limit.
+template <bool VEC>
 __device__ __forceinline__ Staged stage_load(const float* ap, int ac, int alim, const bf16_t* bp, int br,
                                              int64_t ld, int blim, int k0) {
   Staged v;
+  if constexpr (VEC) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v.a[u] = k0 + ac + u < alim ? ap[k0 + ac + u] : 0.0f;
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + ac + 4 * h;
+      const f32x4_t q = k < alim ? *reinterpret_cast<const f32x4_t*>(ap + k) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v.a[4 * h + u] = q[u];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v.a[u] = k0 + ac + u < alim ? ap[k0 + ac + u] : 0.0f;
+  }
   if (k0 + br < blim) {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(bp + (int64_t)(k0 + br) * ld);
     v.b0 = p[0];
@@ -195,13 +208,39 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
   store_tile(logits + (int64_t)m0 * E + e0, E, acc, 0, wid * 32, mrows, erows, lane);
 }
 
+// Both backward kernels stream K in chunks of 32 through one LDS buffer,
+// with the next two chunks held in registers while a chunk is multiplied.
+constexpr int kBK = 32;
+constexpr int kKStride = kBK * 2 + 16;  // bytes per k-contiguous row (80: 16 rows hit distinct banks)
+
+// Chunk v into LDS once every wave has finished with the previous one.
+__device__ __forceinline__ void stage_chunk(const Staged& v, uint8_t* ah, uint8_t* al, uint8_t* b) {
+  __syncthreads();
+  stage_store(v, ah, al, b);
+  __syncthreads();
+}
+
 // --------------------------------------------------------------- dx = g Wr
-// Tile 64 tokens x 128 columns of d, K = experts in chunks of 32.  Waves
-// 2 x 2: rows 32 wm.., columns 64 wn.. (two 32-wide MFMA tiles).
-constexpr int kDxBM = 64, kDxBN = 128, kBK = 32;
-constexpr int kKStride = kBK * 2 + 16;     // bytes per k-contiguous row (80: 16 rows hit distinct banks)
+// Tile 64 tokens x 128 columns of d, K = experts.  Waves 2 x 2: rows 32 wm..,
+// columns 64 wn.. (two 32-wide MFMA tiles).
+constexpr int kDxBM = 64, kDxBN = 128;
 constexpr int kDxBStride = kDxBN * 2 + 64;  // bytes per k row of the 128 columns (320: conflict-free transposing reads)
 
+__device__ __forceinline__ void dx_mma(f32x16_t (&acc)[2], const uint8_t* ahi, const uint8_t* alo, const uint8_t* bs,
+                                       int wm, int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const bf16x8_t fh = read_k(ahi, kKStride, wm * 32, kk, lane), fl = read_k(alo, kKStride, wm * 32, kk, lane);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16x8_t fb = read_tr(bs, kDxBStride, wn * 64 + nt * 32, kk, lane);
+      acc[nt] = mfma(fh, fb, acc[nt]);
+      acc[nt] = mfma(fl, fb, acc[nt]);
+    }
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ g, const bf16_t* __restrict__ Wr,
                                                         int T, int d, int E, float* __restrict__ dx) {
   __shared__ __attribute__((aligned(16))) uint8_t ahi[kDxBM * kKStride], alo[kDxBM * kKStride];
@@ -210,26 +249,21 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
   const int m0 = blockIdx.x * kDxBM, n0 = blockIdx.y * kDxBN;
   // staging: A rows tid / 4, eight experts from 8 (tid % 4); B k row tid / 8, sixteen columns from 16 (tid % 8)
   const int ar = tid >> 2, ac = (tid & 3) * 8, br = tid >> 3, bc = (tid & 7) * 16;
-  const bool arow = m0 + ar < T, bcol = n0 + bc < d;
   const float* gp = g + (int64_t)(m0 + ar) * E;
   const bf16_t* wp = Wr + n0 + bc;
+  const int alim = m0 + ar < T ? E : 0, blim = n0 + bc < d ? E : 0;
+  uint8_t *sah = ahi + ar * kKStride + ac * 2, *sal = alo + ar * kKStride + ac * 2, *sb = bs + br * kDxBStride + bc * 2;
   f32x16_t acc[2] = {};
-  Staged v = stage_load(gp, ac, arow ? E : 0, wp, br, d, bcol ? E : 0, 0);
-  for (int k0 = 0; k0 < E; k0 += kBK) {
-    __syncthreads();  // the previous chunk's fragments have been read
-    stage_store(v, ahi + ar * kKStride + ac * 2, alo + ar * kKStride + ac * 2, bs + br * kDxBStride + bc * 2);
-    __syncthreads();
-    if (k0 + kBK < E) v = stage_load(gp, ac, arow ? E : 0, wp, br, d, bcol ? E : 0, k0 + kBK);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t fh = read_k(ahi, kKStride, wm * 32, kk, lane), fl = read_k(alo, kKStride, wm * 32, kk, lane);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const bf16x8_t fb = read_tr(bs, kDxBStride, wn * 64 + nt * 32, kk, lane);
-        acc[nt] = mfma(fh, fb, acc[nt]);
-        acc[nt] = mfma(fl, fb, acc[nt]);
-      }
-    }
+  Staged v0 = stage_load<VEC>(gp, ac, alim, wp, br, d, blim, 0), v1;
+  if (kBK < E) v1 = stage_load<VEC>(gp, ac, alim, wp, br, d, blim, kBK);
+  for (int k0 = 0; k0 < E; k0 += 2 * kBK) {
+    stage_chunk(v0, sah, sal, sb);
+    if (k0 + 2 * kBK < E) v0 = stage_load<VEC>(gp, ac, alim, wp, br, d, blim, k0 + 2 * kBK);
+    dx_mma(acc, ahi, alo, bs, wm, wn, lane);
+    if (k0 + kBK >= E) break;
+    stage_chunk(v1, sah, sal, sb);
+    if (k0 + 3 * kBK < E) v1 = stage_load<VEC>(gp, ac, alim, wp, br, d, blim, k0 + 3 * kBK);
+    dx_mma(acc, ahi, alo, bs, wm, wn, lane);
   }
   const int nr = min(kDxBM, T - m0), nc = min(kDxBN, d - n0);
 #pragma unroll
@@ -245,6 +279,32 @@ constexpr int kDwBM = 64, kDwBN = 128;
 constexpr int kDwAStride = kDwBM * 2 + 64;  // 192 bytes per token row of 64 experts
 constexpr int kDwBStride = kDwBN * 2 + 64;  // 320 bytes per token row of 128 columns
 
+__device__ __forceinline__ void dw_mma(f32x16_t (&acc)[2], const uint8_t* ghi, const uint8_t* glo, const uint8_t* xs,
+                                       int wm, int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const bf16x8_t fh = read_tr(ghi, kDwAStride, wm * 32, kk, lane), fl = read_tr(glo, kDwAStride, wm * 32, kk, lane);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const bf16x8_t fb = read_tr(xs, kDwBStride, wn * 64 + nt * 32, kk, lane);
+      acc[nt] = mfma(fh, fb, acc[nt]);
+      acc[nt] = mfma(fl, fb, acc[nt]);
+    }
+  }
+}
+
+// Token row k0 + r of a chunk: eight gradient values from expert e0 + ac
+// (those below E) and sixteen columns of x from n0 + bc.
+template <bool VEC>
+__device__ __forceinline__ Staged dw_load(const float* g, const bf16_t* x, int64_t d, int E, int e0, int n0, int r,
+                                          int ac, int bc, bool bcol, int t1, int k0) {
+  const int t = k0 + r;
+  const bool trow = t < t1;
+  return stage_load<VEC>(g + (int64_t)t * E + e0, ac, trow ? E - e0 : 0, x + (int64_t)t * d + n0 + bc, 0, 0,
+                         (trow && bcol) ? 1 : 0, 0);
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ g, const bf16_t* __restrict__ x,
                                                         int T, int d, int E, int tslice,
                                                         float* __restrict__ part) {
@@ -257,31 +317,18 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
   // sixteen columns from 16 (tid % 8)
   const int r = tid >> 3, ac = (tid & 7) * 8, bc = (tid & 7) * 16;
   const bool bcol = n0 + bc < d;
-  // chunk k0: token row k0 + r; experts e0 + ac + u below E, rows below t1
-  const int ecount = E - e0 - ac;  // valid experts from e0 + ac on
-  auto load = [=](int k0) -> Staged {
-    const int t = k0 + r;
-    const bool trow = t < t1;
-    return stage_load(g + (int64_t)t * E + e0, ac, trow ? ecount + ac : 0, x + (int64_t)t * d + n0 + bc, 0, 0,
-                      (trow && bcol) ? 1 : 0, 0);
-  };
+  uint8_t *sgh = ghi + r * kDwAStride + ac * 2, *sgl = glo + r * kDwAStride + ac * 2, *sx = xs + r * kDwBStride + bc * 2;
   f32x16_t acc[2] = {};
-  Staged v = load(t0);
-  for (int k0 = t0; k0 < t1; k0 += kBK) {
-    __syncthreads();
-    stage_store(v, ghi + r * kDwAStride + ac * 2, glo + r * kDwAStride + ac * 2, xs + r * kDwBStride + bc * 2);
-    __syncthreads();
-    if (k0 + kBK < t1) v = load(k0 + kBK);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t fh = read_tr(ghi, kDwAStride, wm * 32, kk, lane), fl = read_tr(glo, kDwAStride, wm * 32, kk, lane);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const bf16x8_t fb = read_tr(xs, kDwBStride, wn * 64 + nt * 32, kk, lane);
-        acc[nt] = mfma(fh, fb, acc[nt]);
-        acc[nt] = mfma(fl, fb, acc[nt]);
-      }
-    }
+  Staged v0 = dw_load<VEC>(g, x, d, E, e0, n0, r, ac, bc, bcol, t1, t0), v1;
+  if (t0 + kBK < t1) v1 = dw_load<VEC>(g, x, d, E, e0, n0, r, ac, bc, bcol, t1, t0 + kBK);
+  for (int k0 = t0; k0 < t1; k0 += 2 * kBK) {
+    stage_chunk(v0, sgh, sgl, sx);
+    if (k0 + 2 * kBK < t1) v0 = dw_load<VEC>(g, x, d, E, e0, n0, r, ac, bc, bcol, t1, k0 + 2 * kBK);
+    dw_mma(acc, ghi, glo, xs, wm, wn, lane);
+    if (k0 + kBK >= t1) break;
+    stage_chunk(v1, sgh, sgl, sx);
+    if (k0 + 3 * kBK < t1) v1 = dw_load<VEC>(g, x, d, E, e0, n0, r, ac, bc, bcol, t1, k0 + 3 * kBK);
+    dw_mma(acc, ghi, glo, xs, wm, wn, lane);
   }
   float* out = part + (int64_t)blockIdx.z * E * d + (int64_t)e0 * d + n0;
   const int nr = min(kDwBM, E - e0), nc = min(kDwBN, d - n0);
@@ -326,8 +373,11 @@ hipError_t launch_router_logits_backward(const void* x, const void* Wr, const fl
   const int slice = std::max(cdiv(cdiv(T, splits), kBK), 1) * kBK;
   const int nz = std::max(cdiv(T, slice), 1);  // T = 0: one slice of nothing, dWr = 0
   float* part = nz > 1 ? dx : dWr;
-  hipLaunchKernelGGL(router_dw_kernel, dim3(cdiv(E, kDwBM), cdiv(d, kDwBN), nz), dim3(256), 0, s, dlogits,
-                     (const bf16_t*)x, T, d, E, slice, part);
+  // 16-byte gradient loads when every row starts 16-byte aligned
+  const bool vec = E % 4 == 0 && ((uintptr_t)dlogits & 15) == 0;
+  const dim3 gw(cdiv(E, kDwBM), cdiv(d, kDwBN), nz);
+  if (vec) hipLaunchKernelGGL(router_dw_kernel<true>, gw, dim3(256), 0, s, dlogits, (const bf16_t*)x, T, d, E, slice, part);
+  else hipLaunchKernelGGL(router_dw_kernel<false>, gw, dim3(256), 0, s, dlogits, (const bf16_t*)x, T, d, E, slice, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nz > 1) {
@@ -338,8 +388,9 @@ hipError_t launch_router_logits_backward(const void* x, const void* Wr, const fl
     if (e != hipSuccess) return e;
   }
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(router_dx_kernel, dim3(cdiv(T, kDxBM), cdiv(d, kDxBN)), dim3(256), 0, s, dlogits,
-                     (const bf16_t*)Wr, T, d, E, dx);
+  const dim3 gx(cdiv(T, kDxBM), cdiv(d, kDxBN));
+  if (vec) hipLaunchKernelGGL(router_dx_kernel<true>, gx, dim3(256), 0, s, dlogits, (const bf16_t*)Wr, T, d, E, dx);
+  else hipLaunchKernelGGL(router_dx_kernel<false>, gx, dim3(256), 0, s, dlogits, (const bf16_t*)Wr, T, d, E, dx);
   return hipGetLastError();
 }
 
