@@ -24,31 +24,30 @@ constexpr int kMaxK = 1024;
 
 // ------------------------------------------------------------------ dispatch
 // One block per token: read x[t] once (16-byte vectors), write it to the
-// rows of its local pairs.
+// rows of its local pairs.  The token's row indices are the same for every
+// lane (scalar loads, no block barrier); they are taken in groups of eight,
+// x[t] being re-read (from cache) per group when k > 8.
+constexpr int kSlotGroup = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restrict__ x,
                                                               const int32_t* __restrict__ rop, int ntok,
                                                               int k, int d, T* __restrict__ xp) {
-  __shared__ int32_t rows[kMaxK];
-  __shared__ int nloc;
   const int nv = d * (int)sizeof(T) / 16;
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int j = 0; j < k; ++j) {
-        int r = rop[(int64_t)t * k + j];
-        if (r >= 0) rows[n++] = r;
-      }
-      nloc = n;
-    }
-    __syncthreads();
-    const int n = nloc;
+    const int32_t* tr = rop + (int64_t)t * k;
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * d);
-    for (int v = threadIdx.x; v < nv; v += 256) {
-      uint4 val = src[v];
-      for (int j = 0; j < n; ++j) reinterpret_cast<uint4*>(xp + (int64_t)rows[j] * d)[v] = val;
+    for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+      int r[kSlotGroup];
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) r[i] = (j0 + i < k) ? tr[j0 + i] : -1;
+      for (int v = threadIdx.x; v < nv; v += 256) {
+        const uint4 val = src[v];
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i)
+          if (r[i] >= 0) reinterpret_cast<uint4*>(xp + (int64_t)r[i] * d)[v] = val;
+      }
     }
-    __syncthreads();
   }
 }
 
@@ -178,17 +177,40 @@ hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8
 }
 
 // ------------------------------------------------------------------ combine
+// Raw 16-byte pieces of 8 elements: loaded first, widened to fp32 later, so
+// that the loads of all rows a thread needs are in flight together.
 template <typename T> struct Vec8;
+// A row seen through a buffer resource: `row_bytes` bytes for a local slot
+// (r >= 0), none for a remote one (r = -1), whose loads then return zeros and
+// whose stores are dropped, without a branch or a memory access.  The index
+// is the same for every lane, so the resource sits in scalar registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, int32_t r, int row_bytes) {
+  const char* p = (const char*)base + (r >= 0 ? (int64_t)r * row_bytes : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, r >= 0 ? row_bytes : 0, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t rs, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t rs, int off, uint4 u) {
+  __builtin_amdgcn_raw_buffer_store_b128(decltype(__builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0)){u.x, u.y, u.z, u.w},
+                                         rs, off, 0, 0);
+}
+
 template <> struct Vec8<bf16_t> {
-  __device__ static void load(const bf16_t* p, float* f) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  struct Raw { uint4 v; };
+  // elements [8v, 8v + 8) of a row
+  __device__ static Raw load_raw(rsrc_t rs, int v) { return {buf_load16(rs, 16 * v)}; }
+  __device__ static void widen(const Raw& r, float* f) {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  __device__ static void load(const bf16_t* p, float* f) { widen({*reinterpret_cast<const uint4*>(p)}, f); }
   __device__ static void store(bf16_t* p, const float* f) {
     uint4 v;
     v.x = (uint32_t)f2bf(f[0]) | ((uint32_t)f2bf(f[1]) << 16);
@@ -197,55 +219,97 @@ template <> struct Vec8<bf16_t> {
     v.w = (uint32_t)f2bf(f[6]) | ((uint32_t)f2bf(f[7]) << 16);
     *reinterpret_cast<uint4*>(p) = v;
   }
+  __device__ static void store(rsrc_t rs, int v, const float* f) {
+    uint4 u;
+    u.x = (uint32_t)f2bf(f[0]) | ((uint32_t)f2bf(f[1]) << 16);
+    u.y = (uint32_t)f2bf(f[2]) | ((uint32_t)f2bf(f[3]) << 16);
+    u.z = (uint32_t)f2bf(f[4]) | ((uint32_t)f2bf(f[5]) << 16);
+    u.w = (uint32_t)f2bf(f[6]) | ((uint32_t)f2bf(f[7]) << 16);
+    buf_store16(rs, 16 * v, u);
+  }
 };
 template <> struct Vec8<float> {
+  struct Raw { float4 a, b; };
+  __device__ static Raw load_raw(rsrc_t rs, int v) {
+    const uint4 a = buf_load16(rs, 32 * v), b = buf_load16(rs, 32 * v + 16);
+    return {make_float4(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)),
+            make_float4(__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w))};
+  }
+  __device__ static void widen(const Raw& r, float* f) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w; f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
   __device__ static void load(const float* p, float* f) {
-    float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    widen({reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]}, f);
   }
   __device__ static void store(float* p, const float* f) {
     reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
     reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
   }
+  __device__ static void store(rsrc_t rs, int v, const float* f) {
+    buf_store16(rs, 32 * v, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                                       __float_as_uint(f[3])));
+    buf_store16(rs, 32 * v + 16, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                                            __float_as_uint(f[7])));
+  }
 };
+
+// In the combine, the kSlotGroup slots of a group are loaded before the first
+// is used: a gather is bound by how many loads are in flight.
 
 // out[t] = sum_{j ascending} w_j * rows[row(t,j)] in fp32, rounded once.
 // w_j = gate[t,j], or 1 when gate is null (the reverse-dispatch reduction).
-template <typename T>
+// Remote slots (row -1) are skipped.  The token's row indices and gates are
+// the same for every lane, so they come through the scalar cache and no
+// block barrier is needed.
+template <typename T, bool GATED>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows, const float* __restrict__ gate,
                                                       const int32_t* __restrict__ rop, int ntok, int k, int d,
                                                       T* __restrict__ out) {
-  __shared__ int32_t rr[kMaxK];
-  __shared__ float ww[kMaxK];
-  __shared__ int nloc;
   const int nv = d / 8;
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int j = 0; j < k; ++j) {
-        int r = rop[(int64_t)t * k + j];
-        if (r >= 0) {
-          rr[n] = r;
-          ww[n] = gate ? gate[(int64_t)t * k + j] : 1.0f;
-          ++n;
-        }
-      }
-      nloc = n;
+    const int32_t* tr = rop + (int64_t)t * k;
+    const float* tg = gate + (int64_t)t * k;
+    // resources and weights of the first group, read once per token (the
+    // loads are clamped to slot k - 1 so that they can all be issued at once)
+    rsrc_t rs0[kSlotGroup];
+    float w0[kSlotGroup];
+#pragma unroll
+    for (int i = 0; i < kSlotGroup; ++i) {
+      const int jc = i < k ? i : k - 1;
+      const int32_t rv = tr[jc];
+      const float gv = GATED ? tg[jc] : 1.0f;
+      const int32_t r = (i < k) ? rv : -1;
+      w0[i] = r < 0 ? 0.f : gv;
+      rs0[i] = row_rsrc(rows, r, d * (int)sizeof(T));
     }
-    __syncthreads();
-    const int n = nloc;
     for (int v = threadIdx.x; v < nv; v += 256) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < n; ++j) {
-        float y[8];
-        Vec8<T>::load(rows + (int64_t)rr[j] * d + 8 * v, y);
-        const float w = ww[j];
+      for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+        typename Vec8<T>::Raw raw[kSlotGroup];
+        float w[kSlotGroup];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(w, y[q], acc[q]);
+        for (int i = 0; i < kSlotGroup; ++i) {
+          rsrc_t rs = rs0[i];
+          w[i] = w0[i];
+          if (j0 > 0) {
+            const int32_t r = (j0 + i < k) ? tr[j0 + i] : -1;
+            w[i] = r < 0 ? 0.f : (GATED ? tg[j0 + i] : 1.0f);
+            rs = row_rsrc(rows, r, d * (int)sizeof(T));
+          }
+          raw[i] = Vec8<T>::load_raw(rs, v);
+        }
+        // a remote slot adds w * 0 = +-0 to an accumulator that is never -0:
+        // the sum is the one over the local slots alone
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i) {
+          float y[8];
+          Vec8<T>::widen(raw[i], y);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[i], y[q], acc[q]);
+        }
       }
       Vec8<T>::store(out + (int64_t)t * d + 8 * v, acc);
     }
-    __syncthreads();
   }
 }
 
@@ -253,12 +317,15 @@ hipError_t launch_combine(const void* rows, const float* gate, const int32_t* ro
                           int bf16, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = T < 16384 ? T : 16384;
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)rows, gate,
-                       row_of_pair, T, k, d, (bf16_t*)out);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)rows, gate,
-                       row_of_pair, T, k, d, (float*)out);
+#define MOK_COMBINE(TT, G)                                                                                 \
+  hipLaunchKernelGGL((combine_kernel<TT, G>), dim3(blocks), dim3(256), 0, s, (const TT*)rows, gate, row_of_pair, T, \
+                     k, d, (TT*)out)
+  if (bf16) {
+    if (gate) MOK_COMBINE(bf16_t, true); else MOK_COMBINE(bf16_t, false);
+  } else {
+    if (gate) MOK_COMBINE(float, true); else MOK_COMBINE(float, false);
+  }
+#undef MOK_COMBINE
   return hipGetLastError();
 }
 
@@ -285,7 +352,7 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
                                                             int d, float* __restrict__ dgate,
                                                             float* __restrict__ dlogits, T* __restrict__ dy,
                                                             int32_t* __restrict__ queue_zero, int nqueue) {
-  __shared__ float red[4];
+  __shared__ float red[4][kSlotGroup];
   // the tile counters of the weight-gradient GEMMs that follow on the stream
   if (blockIdx.x == 0 && (int)threadIdx.x < nqueue) queue_zero[threadIdx.x] = 0;
   __shared__ float dg[kMaxK];
@@ -293,28 +360,59 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
   const int nv = d / 8;
   const int lane = lane_id(), w = threadIdx.x >> 6;
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
-    for (int j = 0; j < k; ++j) {
-      const int r = rop[(int64_t)t * k + j];
-      const float g = gate[(int64_t)t * k + j];
-      float part = 0.f;
-      if (r >= 0) {
-        for (int v = threadIdx.x; v < nv; v += 256) {
-          float o[8], y[8], z[8];
-          Vec8<T>::load(dout + (int64_t)t * d + 8 * v, o);
-          Vec8<T>::load(Y + (int64_t)r * d + 8 * v, y);
+    const int32_t* tr = rop + (int64_t)t * k;
+    const float* tg = gate + (int64_t)t * k;
+    // Slots in groups: each thread's partial dot products of one group run
+    // over its vectors in ascending order (v, then element), then one wave
+    // sum and a fixed tree over the four waves.
+    for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+      int r[kSlotGroup];
+      float g[kSlotGroup], part[kSlotGroup];
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) {
+        const int jc = j0 + i < k ? j0 + i : k - 1;  // clamped: all loads issued at once
+        const int32_t rv = tr[jc];
+        const float gv = tg[jc];
+        r[i] = (j0 + i < k) ? rv : -1;
+        g[i] = (j0 + i < k) ? gv : 0.f;
+        part[i] = 0.f;
+      }
+      rsrc_t yr[kSlotGroup], dyr[kSlotGroup];
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) {
+        yr[i] = row_rsrc(Y, r[i], d * (int)sizeof(T));
+        dyr[i] = row_rsrc(dy, r[i], d * (int)sizeof(T));
+      }
+      for (int v = threadIdx.x; v < nv; v += 256) {
+        typename Vec8<T>::Raw raw[kSlotGroup];
+        float o[8];
+        Vec8<T>::load(dout + (int64_t)t * d + 8 * v, o);
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i) raw[i] = Vec8<T>::load_raw(yr[i], v);
+        // a remote slot reads zeros (its partial stays +0, reduced to 0 and
+        // replaced by 0 below) and its store is dropped
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i) {
+          float y[8], z[8];
+          Vec8<T>::widen(raw[i], y);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            part = fmaf(o[q], y[q], part);
-            z[q] = g * o[q];
+            part[i] = fmaf(o[q], y[q], part[i]);
+            z[q] = g[i] * o[q];
           }
-          Vec8<T>::store(dy + (int64_t)r * d + 8 * v, z);
+          Vec8<T>::store(dyr[i], v, z);
         }
       }
-      part = wave_sum(part);
-      if (lane == 0) red[w] = part;
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) {
+        const float ws = wave_sum(part[i]);
+        if (lane == 0) red[w][i] = ws;
+      }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        dg[j] = (r >= 0) ? ((red[0] + red[1]) + (red[2] + red[3])) : 0.f;
+      if ((int)threadIdx.x < kSlotGroup && j0 + (int)threadIdx.x < k) {
+        const int i = threadIdx.x, j = j0 + i;
+        const int rj = tr[j];
+        dg[j] = (rj >= 0) ? ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) : 0.f;
         sel[j] = idx[(int64_t)t * k + j];
       }
       __syncthreads();
