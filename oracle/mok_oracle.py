@@ -357,7 +357,7 @@ def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: in
     out = combine(Y, gate, row_of_pair, T, k)
     return dict(idx=idx, gate=gate, lse=lse, p=p, counts=counts, offsets=offsets,
                 row_of_pair=row_of_pair, pair_of_row=pair_of_row, A=A, B=B, H=H, Y=Y, out=out,
-                gating=gating, renorm=renorm)
+                gating=gating, renorm=renorm, mxfp8=mxfp8)
 
 
 def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int = 0,
@@ -394,7 +394,7 @@ def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int =
 
 def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
              expert_begin: int = 0, expert_end: int | None = None, gating: str = "softmax",
-             renorm: bool = False):
+             renorm: bool = False, mxfp8: bool = False):
     """Gradients of L = sum(out * dout) in float64.
 
     The backward pass mirrors the forward: reverse-combine, expert backward,
@@ -412,6 +412,17 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
       dx_r        = da W1_e + db W3_e
       dx_t        = sum_j dx_(t,j), j ascending              (reverse-dispatch)
       dW2_e = dy_e^T h_e,  dW1_e = da_e^T x_e,  dW3_e = db_e^T x_e
+
+    MXFP8 mode (the pages report MXFP8 backward timings, [kucoin §03], but give
+    no recipe; this is the reading taken): the forward is the MXFP8 one
+    (fwd computed with mxfp8=True, so a, b and y come from quantised x, W1,
+    W3, h and W2), and each backward product whose result flows on to dx
+    quantises both operands along its own contraction axis:
+      dh   = Q(dy) Q(W2_e^T)^T            (dy rows and W2_e columns along d)
+      dx_r = Q(da) Q(W1_e^T)^T + Q(db) Q(W3_e^T)^T   (along F)
+    where Q is mxfp8_qdq over the last axis.  The weight gradients take the
+    unquantised operands: dW2_e = dy_e^T h_e with h = silu(a) * b before its
+    quantisation, dW1_e = da_e^T x_e, dW3_e = db_e^T x_e.
     """
     x = _f64(x)
     g = _f64(dout)
@@ -420,8 +431,11 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     if expert_end is None:
         expert_end = E
     if fwd is None:
-        fwd = forward(x, logits, W1, W3, W2, k, expert_begin, expert_end, gating=gating, renorm=renorm)
+        fwd = forward(x, logits, W1, W3, W2, k, expert_begin, expert_end, mxfp8=mxfp8, gating=gating,
+                      renorm=renorm)
     gating, renorm = fwd.get("gating", gating), fwd.get("renorm", renorm)
+    if mxfp8 != fwd.get("mxfp8", False):
+        raise ValueError("backward(mxfp8=...) needs the forward of the same precision")
     gate, p, Y = fwd["gate"], fwd["p"], fwd["Y"]
     rop = fwd["row_of_pair"].reshape(T, k)
     offsets, pair_of_row = fwd["offsets"], fwd["pair_of_row"]
@@ -449,11 +463,19 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
             continue
         i = e - expert_begin
         a, b, h, dy = A[r0:r1], B[r0:r1], H[r0:r1], dY[r0:r1]
-        dh = dy @ _f64(W2[i])
+        if mxfp8:
+            h = silu(a) * b
+            dh = mxfp8_qdq(dy) @ mxfp8_qdq(_f64(W2[i]).T).T
+        else:
+            dh = dy @ _f64(W2[i])
         s = sigmoid(a)
         da = dh * b * s * (1.0 + a * (1.0 - s))
         db = dh * silu(a)
-        dXp[r0:r1] = da @ _f64(W1[i]) + db @ _f64(W3[i])
+        if mxfp8:
+            dXp[r0:r1] = (mxfp8_qdq(da) @ mxfp8_qdq(_f64(W1[i]).T).T
+                          + mxfp8_qdq(db) @ mxfp8_qdq(_f64(W3[i]).T).T)
+        else:
+            dXp[r0:r1] = da @ _f64(W1[i]) + db @ _f64(W3[i])
         dW2[i] = dy.T @ h
         dW1[i] = da.T @ Xp[r0:r1]
         dW3[i] = db.T @ Xp[r0:r1]
@@ -469,7 +491,8 @@ def loss(out, dout) -> float:
 
 
 def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int = 0,
-                   expert_end: int | None = None, gating: str = "softmax", renorm: bool = False):
+                   expert_end: int | None = None, gating: str = "softmax", renorm: bool = False,
+                   mxfp8: bool = False):
     """Backward of one token alone (sampled checks at full size): the pair
     gradients of its local experts summed in slot order, and its router
     gradient.  Same equations as backward(), restricted to one token; every
@@ -489,26 +512,47 @@ def backward_token(x_t, logits_t, dout_t, W1, W3, W2, k: int, expert_begin: int 
         if not expert_begin <= e < expert_end:
             continue
         i = e - expert_begin
-        a, b, h, y = expert_ffn(xt, W1[i], W3[i], W2[i])
+        if mxfp8:
+            a, b, y = _mx_expert_forward(xt, W1[i], W3[i], W2[i])
+        else:
+            a, b, h, y = expert_ffn(xt, W1[i], W3[i], W2[i])
         dgate[j] = float(np.dot(g, y[0]))
         dy = gate[0, j] * g[None, :]
-        dh = dy @ _f64(W2[i])
+        dh = (mxfp8_qdq(dy) @ mxfp8_qdq(_f64(W2[i]).T).T) if mxfp8 else dy @ _f64(W2[i])
         s = sigmoid(a)
         da = dh * b * s * (1.0 + a * (1.0 - s))
         db = dh * silu(a)
-        dx += (da @ _f64(W1[i]) + db @ _f64(W3[i]))[0]
+        if mxfp8:
+            dx += (mxfp8_qdq(da) @ mxfp8_qdq(_f64(W1[i]).T).T + mxfp8_qdq(db) @ mxfp8_qdq(_f64(W3[i]).T).T)[0]
+        else:
+            dx += (da @ _f64(W1[i]) + db @ _f64(W3[i]))[0]
     dlogits = route_backward(p, idx, gate, dgate[None, :], gating, renorm)[0]
     return dx, dgate, dlogits
 
 
-def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e):
+def _mx_expert_forward(X, W1e, W3e, W2e):
+    """MXFP8 forward of one expert's rows (as in forward(mxfp8=True)):
+    a, b from quantised x and W1/W3 rows, y from quantised h and W2 rows."""
+    xq = mxfp8_qdq(X)
+    a = xq @ mxfp8_qdq(W1e).T
+    b = xq @ mxfp8_qdq(W3e).T
+    y = mxfp8_qdq(silu(a) * b) @ mxfp8_qdq(W2e).T
+    return a, b, y
+
+
+def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e, mxfp8: bool = False):
     """dW1_e, dW3_e, dW2_e of one expert from its rows alone: X_e [R,d] the
     activations of its pairs, gate_e [R] their gates, dout_e [R,d] the output
-    gradients of their tokens (row order does not matter)."""
+    gradients of their tokens (row order does not matter).  MXFP8 as in
+    backward(mxfp8=True)."""
     X = _f64(X_e)
-    a, b, h, _ = expert_ffn(X, W1e, W3e, W2e)
+    if mxfp8:
+        a, b, _ = _mx_expert_forward(X, W1e, W3e, W2e)
+        h = silu(a) * b
+    else:
+        a, b, h, _ = expert_ffn(X, W1e, W3e, W2e)
     dy = _f64(gate_e)[:, None] * _f64(dout_e)
-    dh = dy @ _f64(W2e)
+    dh = (mxfp8_qdq(dy) @ mxfp8_qdq(_f64(W2e).T).T) if mxfp8 else dy @ _f64(W2e)
     s = sigmoid(a)
     da = dh * b * s * (1.0 + a * (1.0 - s))
     db = dh * silu(a)
