@@ -75,17 +75,35 @@ def stage_work(w, P, U, save_for_backward=True):
               "sort": T * k * 4 * 4 + P * 4}
     # GEMM operands: bf16 (or fp32) elements, or MXFP8 codes plus one E8M0
     # scale per 32; fp32 weight gradients.
-    q = 1 + 1 / 32 if w.precision == "mxfp8" else s
+    mx = w.precision == "mxfp8"
+    q = 1 + 1 / 32 if mx else s
+    # MXFP8: the dispatch writes MXFP8 rows; UP also saves H before its
+    # quantisation; the reverse-combine also writes dY in MXFP8; DH and DX read
+    # MXFP8 operands, and DH writes [dA | dB] both as bf16 (for the weight
+    # gradients) and as MXFP8 (for DX)
+    saved_up = (3 if mx else 2) * P * F * s if save_for_backward else 0
+    if mx:
+        nbytes["bwd_gate"] += P * d * q
+        nbytes["dispatch"] = U * d * s + P * d * q
     gemm_bytes = {
-        "gemm_up": P * d * q + 2 * El * F * d * q + P * F * q + (2 * P * F * s if save_for_backward else 0),
+        "gemm_up": P * d * q + 2 * El * F * d * q + P * F * q + saved_up,
         "gemm_down": P * F * q + El * d * F * q + P * d * s,
-        "gemm_dh": P * d * s + El * d * F * s + 2 * P * F * s + 2 * P * F * s,
-        "gemm_dx": 2 * P * F * s + 2 * El * F * d * s + P * d * s,
+        "gemm_dh": P * d * q + El * d * F * q + 2 * P * F * s + 2 * P * F * s + (2 * P * F * q if mx else 0),
+        "gemm_dx": 2 * P * F * q + 2 * El * F * d * q + P * d * s,
         "gemm_dw2": P * d * s + P * F * s + El * d * F * 4,
         "gemm_dw13": 2 * P * F * s + P * d * s + 2 * El * F * d * 4,
     }
     nbytes.update(gemm_bytes)
     return flops, nbytes
+
+
+def gemm_peak(precision: str, name: str) -> float:
+    """Dense MFMA peak of one GEMM: in an MXFP8 layer the forward GEMMs and
+    the two backward products that lead to dx run on scaled MFMA (MXFP8
+    peak); the weight-gradient GEMMs stay bf16."""
+    if precision == "mxfp8":
+        return PEAK_TFLOPS["bf16"] if name in ("gemm_dw2", "gemm_dw13") else PEAK_TFLOPS["mxfp8"]
+    return PEAK_TFLOPS[precision]
 
 
 def roof_of(flops_n, bytes_n, ms, peak_tflops):
@@ -197,35 +215,20 @@ def router_gemm_bench(w, x, K, Wm, ev, sh):
     return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="bf16_train")
-    ap.add_argument("--forward-only", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--minibatch-rows", type=int, default=0,
-                    help="ring pipeline minibatch rows R (0 = whole layer at once)")
-    ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="skip the extra timing of the same step captured in a HIP graph")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="run one plain device copy of this size first (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name: str, args, extras: bool):
+    """Times `steps` layer steps of one workload (after `warmup` untimed
+    ones); `extras` adds the copy calibration and the graph-replay timing.
+    Returns the result record, the workload, its inputs and the timing
+    handles (for the router GEMM and the CPU baseline)."""
     import torch
 
     import workloads as W
     from mixture_experts_layer_34_amd import mok
-    from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp8
+    from mixture_experts_layer_34_amd.layer import (MoeBuffers, MoeShape, quantize_mxfp8,
+                                                    quantize_mxfp8_backward_weights)
 
-    w = W.get(args.workload)
-    backward = w.backward and not args.forward_only and w.precision != "mxfp8"
+    w = W.get(name)
+    backward = w.backward and not args.forward_only
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = W.make_inputs(w, device=dev)
@@ -241,10 +244,11 @@ def main():
         q2, s2 = quantize_mxfp8(W2)
         W1, W3, W2 = q1, q3, q2
         scales = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
+    wt = quantize_mxfp8_backward_weights(inp["W1"], inp["W3"], inp["W2"]) if w.precision == "mxfp8" else None
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
-    if args.copy_calibration_mib:
+    if args.copy_calibration_mib and extras:
         n = args.copy_calibration_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -257,11 +261,17 @@ def main():
     stage_ev = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(K)]
     start, stop = ev.create(2)
 
+    def bwd(stream=None):
+        if wt is not None:
+            buf.backward_mxfp8(inp["dout"], inp["x"], inp["logits"], wt, stream=stream)
+        else:
+            buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"], stream=stream)
+
     def step(events=None):
         buf.cfg.stage_events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
         buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales, stream=sh)
         if backward:
-            buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"], stream=sh)
+            bwd(sh)
 
     for _ in range(Wm):
         step()
@@ -280,21 +290,21 @@ def main():
     # The same step captured once into a HIP graph and replayed K times (the
     # library only enqueues kernels, so it captures as is): launch gaps removed.
     graph_res = None
-    if not args.no_graph:
+    if not args.no_graph and extras:
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
             buf.cfg.stage_events = None
             buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
             if backward:
-                buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"])
+                bwd()
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
             if backward:
-                buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"])
+                bwd()
         graph.replay()
         torch.cuda.synchronize()
         g0, g1 = ev.create(2)
@@ -322,19 +332,22 @@ def main():
         # dispatch): the stage is recorded empty and moves no bytes of its own
         nbytes.pop("dispatch", None)
     dom = max(stages, key=stages.get)
-    peak = PEAK_TFLOPS[w.precision]
-    roof = roof_of(flops.get(dom, 0.0), nbytes[dom], stages[dom], peak)
+    roof = roof_of(flops.get(dom, 0.0), nbytes[dom], stages[dom], gemm_peak(w.precision, dom))
     roof.update({"traffic": measured_traffic(w.name, dom) if dom in flops and not args.minibatch_rows else None,
                  "kernel": dom, "avg_ms": round(stages[dom], 4),
                  "per_launch": (f"{flops[dom] / 1e9:.1f} GFLOP, " if dom in flops else "")
                  + f"{nbytes[dom] / 1e6:.1f} MB"})
     gemm = {n: {"ms": round(stages[n], 4), "tflops": round(flops[n] / (stages[n] * 1e-3) / 1e12, 1),
-                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / peak, 4),
-                "roof": {k_: v for k_, v in roof_of(flops[n], nbytes[n], stages[n], peak).items()
+                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / gemm_peak(w.precision, n), 4),
+                "roof": {k_: v for k_, v in roof_of(flops[n], nbytes[n], stages[n],
+                                                    gemm_peak(w.precision, n)).items()
                          if k_ in ("bound", "frac")}}
             for n in flops if n in stages}
     gemm_ms = sum(stages[n] for n in flops if n in stages)
     gemm_flops = sum(flops[n] for n in flops if n in stages)
+    # the GEMMs' combined peak: their FLOPs over the time they would take,
+    # each at its own peak
+    gemm_peak_all = gemm_flops / sum(flops[n] / gemm_peak(w.precision, n) for n in flops if n in stages)
     hbm = {n: {"ms": round(stages[n], 4), "gbs": round(nbytes[n] / (stages[n] * 1e-3) / 1e9, 1)}
            for n in nbytes if n in stages and n not in flops}
 
@@ -354,18 +367,57 @@ def main():
                    "global_batch": T, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
-                         "frac_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / peak, 4), "per_gemm": gemm},
+                         "frac_peak": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / gemm_peak_all, 4),
+                         "per_gemm": gemm},
         "data_movement": hbm,
         "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
         "graph_replay": graph_res,
         "wall_s": round(wall, 3),
     }
+    return result, w, inp, (K, Wm, ev, sh)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_train")
+    ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--minibatch-rows", type=int, default=0,
+                    help="ring pipeline minibatch rows R (0 = whole layer at once)")
+    ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the same step captured in a HIP graph")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the MXFP8 forward+backward leg after the bf16 training workload")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    result, w, inp, (K, Wm, ev, sh) = measure(args.workload, args, extras=True)
     if inp["x"].dtype == torch.bfloat16 and not args.minibatch_rows:
         result["router_gemm"] = router_gemm_bench(w, inp["x"], K, Wm, ev, sh)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
     else:
         result["cpu_baseline"] = None
+    if args.workload == "bf16_train" and not (args.no_mxfp8 or args.minibatch_rows or args.forward_only):
+        # the MXFP8 leg of the metric: the same layer, inputs and routing with
+        # MXFP8 forward GEMMs and MXFP8 dx products in the backward
+        del inp
+        torch.cuda.empty_cache()
+        mx, _, _, _ = measure("mxfp8_train", args, extras=False)
+        result["mxfp8_train"] = {k_: mx[k_] for k_ in ("value", "unit", "ms_per_step", "dtype", "roofline",
+                                                        "grouped_gemm", "data_movement", "stages_ms")}
+        result["mxfp8_train"]["config"] = mx["config"]["workload"]
     print(json.dumps(result), flush=True)
 
 

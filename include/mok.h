@@ -205,7 +205,8 @@ mok_status mok_moe_forward(const void* x, const float* router_logits,
  *   dW2            float [E_loc, d, F]   overwritten
  *   dgate          float [T, k]    <dout_t, y(t,j)>; 0 for remote pairs
  *   drouter_logits float [T, E]    p * (G - <p, G>), G = dgate scattered
- * BF16 and FP32 precisions only (MXFP8 backward: MOK_ERR_UNSUPPORTED).
+ * BF16 and FP32 precisions (MXFP8: mok_moe_backward_mxfp8; this call then
+ * returns MOK_ERR_UNSUPPORTED).
  */
 mok_status mok_moe_backward(const void* dout, const void* x, const float* router_logits,
                             const void* W1, const void* W3, const void* W2, int32_t k,
@@ -213,6 +214,49 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
                             void* dx, float* dW1, float* dW3, float* dW2,
                             float* dgate, float* drouter_logits,
                             void* workspace, void* stream);
+
+/*
+ * MXFP8 backward ([kucoin §03] reports the layer's backward time in MXFP8;
+ * the pages give no recipe, so this is the reading taken): the same outputs
+ * as mok_moe_backward, after an MXFP8 forward call with
+ * MOK_FLAG_SAVE_FOR_BACKWARD (which then also saves A, B and H before its
+ * quantisation as bf16).  The two products that lead to dx run on scaled
+ * MFMA with each operand quantised along the axis it contracts:
+ *   dH = Q_d(dY) Q_d(W2^T)^T, then dA, dB by the SwiGLU backward,
+ *   dX_perm = Q_F(dA) Q_F(W1^T)^T + Q_F(dB) Q_F(W3^T)^T,
+ * dY (= gate * dout) quantised inside the reverse-combine and [dA | dB]
+ * inside the dH epilogue.  The weight gradients are bf16 products of the
+ * unquantised operands (dY, H, dA, dB and x rows), fp32 results.
+ *   wt_e4m3, wt_e8m0  the transposed weights from
+ *                     mok_quantize_mxfp8_backward_weights
+ *   dout, x            bf16 [T, d]; other arguments as in mok_moe_backward
+ * Errors: MOK_ERR_INVALID_ARG unless cfg->precision is MOK_PREC_MXFP8 and the
+ * save flag is set, plus mok_moe_backward's checks.
+ */
+mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* router_logits, int32_t k,
+                                  const mok_moe_config* cfg, const uint8_t* wt_e4m3,
+                                  const uint8_t* wt_e8m0, const void* saved, void* dx, float* dW1,
+                                  float* dW3, float* dW2, float* dgate, float* drouter_logits,
+                                  void* workspace, void* stream);
+
+/*
+ * Transposed MXFP8 copies of the expert weights for mok_moe_backward_mxfp8
+ * (quantisation rule of mok_quantize_mxfp8; once per weight update, outside
+ * the layer call, like the forward's weights):
+ *   W1, W3   bf16 [E_loc, F, d];  W2  bf16 [E_loc, d, F]
+ *   wt_e4m3  3 * E_loc * F * d bytes: W2^T as [E_loc, F, d] (each row a
+ *            column of W2_e, quantised along d), then [W1^T | W3^T] as
+ *            [E_loc, d, 2F] (row i holds column i of W1_e, then of W3_e,
+ *            quantised along F)
+ *   wt_e8m0  3 * E_loc * F * d / 32 bytes: the scales of W2^T as pair planes
+ *            [d/64, E_loc*F, 2], then those of [W1^T | W3^T] as
+ *            [2F/64, E_loc*d, 2] (the layout of mok_quantize_mxfp8)
+ * Errors: MOK_ERR_INVALID_ARG for a null or misaligned pointer, E_loc < 1,
+ * d or F not a multiple of 128, or a scale array of 2^32 bytes or more.
+ */
+mok_status mok_quantize_mxfp8_backward_weights(const void* W1, const void* W3, const void* W2, int32_t E_loc,
+                                               int32_t d, int32_t F, uint8_t* wt_e4m3, uint8_t* wt_e8m0,
+                                               void* stream);
 
 /*
  * MXFP8 quantisation of a bf16 matrix along its rows ([kucoin §02]: MXFP8

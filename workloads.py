@@ -145,6 +145,9 @@ WORKLOADS = {
     "bf16_train": Workload("bf16_train", T=8192, d=4096, E=128, k=8, F=1536, precision="bf16", seed=5,
                            backward=True, minibatch_rows=(512, 1024, 2048, 4096), ring_bytes=268435456,
                            notes={"zipf": 1.2}),
+    # the same layer, inputs and routing in MXFP8 (forward and backward)
+    "mxfp8_train": Workload("mxfp8_train", T=8192, d=4096, E=128, k=8, F=1536, precision="mxfp8", seed=5,
+                            backward=True, notes={"zipf": 1.2}),
 }
 
 
