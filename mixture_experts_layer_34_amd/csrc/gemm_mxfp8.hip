@@ -270,8 +270,35 @@ struct MxJob {
     }
   }
 
+  // DH: the saved A and B of a lane's 8 elements in each epilogue round
+  // (round t: row block i = t / (2 FN), column block j = t / 2 % FN, half
+  // t % 2), kept kPre rounds ahead in a ring of registers.  The first kPre
+  // rounds are loaded before the next tile's stage copies are issued, so that
+  // waiting for them does not wait for those copies too.
+  static constexpr int kRounds = FM * FN * 2, kPre = 4;
+  struct SavedPre {
+    u32x4_t a[kPre], b[kPre];
+  };
+  __device__ __forceinline__ void dh_load(int t, SavedPre& p) const {
+    const GroupedGemmArgs& a = *args;
+    const int i = t / (2 * FN), j = (t / 2) % FN, half = t % 2;
+    const int row = c.row0 + wm * TM + i * 32 + half * 16 + (lane >> 2);
+    const int col = c.n0 + wn * TN + j * 32 + (lane & 3) * 8;
+    const bool ok = row < c.row_end && col < N;
+    const int64_t o = ok ? (int64_t)row * N + col : 0;
+    p.a[t % kPre] = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o) : u32x4_t{0u, 0u, 0u, 0u};
+    p.b[t % kPre] = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ void epilogue_prefetch(SavedPre& p) const {
+    if constexpr (KIND == KIND_DH) {
+#pragma unroll
+      for (int t = 0; t < kPre; ++t) dh_load(t, p);
+    }
+  }
+
   // Epilogue through this wave's 4 KB of the staging area, 16 rows per round.
-  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging) const {
+  __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging,
+                                           SavedPre& pre) const {
     // The lane index passes through an empty asm so that the compiler cannot
     // compute the epilogue's per-lane addresses before the K loop (they would
     // stay live across it and push the loop into register spills).
@@ -363,9 +390,9 @@ struct MxJob {
             const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
             const f32x4_t v0 = pv[0], v1 = pv[1];
             const float dh[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            const int64_t o = (int64_t)row * N + col;
-            const u32x4_t av = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_a + o) : u32x4_t{0u, 0u, 0u, 0u};
-            const u32x4_t bv = ok ? *reinterpret_cast<const u32x4_t*>((const bf16_t*)a.save_b + o) : u32x4_t{0u, 0u, 0u, 0u};
+            const int t = (i * FN + j) * 2 + half;
+            const u32x4_t av = pre.a[t % kPre], bv = pre.b[t % kPre];
+            if (t + kPre < kRounds) dh_load(t + kPre, pre);
             float da[8], db[8];
             float amax_a = 0.f, amax_b = 0.f;
 #pragma unroll
@@ -477,16 +504,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
   cur.init(args, coord(tile));
   for (int s = 0; s < kMxNS && s < cur.nk; ++s) cur.issue(s, arena);
   f32x16_t acc[Job::NB][Job::FM][Job::FN];
+  typename Job::SavedPre pre;
   while (true) {
     cur.mainloop(acc, arena);
     lds_barrier();  // every wave is done with the stage buffers
+    cur.epilogue_prefetch(pre);
     const int nt = tile + G_;
     Job nxt = cur;
     if (nt < total) {
       nxt.init(args, coord(nt));
       for (int s = 0; s < kMxNS && s < nxt.nk; ++s) nxt.issue(s, arena);
     }
-    cur.epilogue(acc, staging);
+    cur.epilogue(acc, staging, pre);
     if (nt >= total) break;
     cur = nxt;
     tile = nt;
