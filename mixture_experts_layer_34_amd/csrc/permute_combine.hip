@@ -22,11 +22,37 @@ namespace mok {
 
 constexpr int kMaxK = 1024;
 
+// A row seen through a buffer resource: `row_bytes` bytes for a local slot
+// (r >= 0), none for a remote one (r = -1), whose loads then return zeros and
+// whose stores are dropped, without a branch or a memory access.  The index
+// is the same for every lane, so the resource sits in scalar registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, int32_t r, int row_bytes) {
+  const char* p = (const char*)base + (r >= 0 ? (int64_t)r * row_bytes : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, r >= 0 ? row_bytes : 0, 0x00020000);
+}
+// The rows gathered by the combine and the reverse-combine are read once per
+// call, so those loads carry the non-temporal hint (cache policy bit 1): the
+// combine went from 118 to 106 us at T 8192, d 4096, k 8 (5.7 TB/s).  On the
+// stores the same hint was faster in isolation (a dispatch, 117 to 103 us)
+// but slower inside the layer (the regather 117 to 141 us, the reverse-
+// combine 219 to 230 us), so stores keep the default policy.
+constexpr int kNT = 2;
+__device__ __forceinline__ uint4 buf_load16(rsrc_t rs, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t rs, int off, uint4 u) {
+  __builtin_amdgcn_raw_buffer_store_b128(decltype(__builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0)){u.x, u.y, u.z, u.w},
+                                         rs, off, 0, 0);
+}
+
 // ------------------------------------------------------------------ dispatch
 // One block per token: read x[t] once (16-byte vectors), write it to the
 // rows of its local pairs.  The token's row indices are the same for every
 // lane (scalar loads, no block barrier); they are taken in groups of eight,
-// x[t] being re-read (from cache) per group when k > 8.
+// x[t] being re-read (from cache) per group when k > 8.  Each destination row
+// is a buffer resource of size 0 for a remote slot, whose stores are dropped.
 constexpr int kSlotGroup = 8;
 
 template <typename T>
@@ -38,14 +64,17 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restric
     const int32_t* tr = rop + (int64_t)t * k;
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * d);
     for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
-      int r[kSlotGroup];
+      rsrc_t rs[kSlotGroup];
 #pragma unroll
-      for (int i = 0; i < kSlotGroup; ++i) r[i] = (j0 + i < k) ? tr[j0 + i] : -1;
+      for (int i = 0; i < kSlotGroup; ++i) {
+        const int jc = j0 + i < k ? j0 + i : k - 1;
+        const int32_t rv = tr[jc];
+        rs[i] = row_rsrc(xp, (j0 + i < k) ? rv : -1, d * (int)sizeof(T));
+      }
       for (int v = threadIdx.x; v < nv; v += 256) {
         const uint4 val = src[v];
 #pragma unroll
-        for (int i = 0; i < kSlotGroup; ++i)
-          if (r[i] >= 0) reinterpret_cast<uint4*>(xp + (int64_t)r[i] * d)[v] = val;
+        for (int i = 0; i < kSlotGroup; ++i) buf_store16(rs[i], 16 * v, val);  // dropped for remote slots
       }
     }
   }
@@ -237,24 +266,6 @@ hipError_t launch_quantize_mxfp8_t(const void* src, int nmat, int R, int C, uint
 // Raw 16-byte pieces of 8 elements: loaded first, widened to fp32 later, so
 // that the loads of all rows a thread needs are in flight together.
 template <typename T> struct Vec8;
-// A row seen through a buffer resource: `row_bytes` bytes for a local slot
-// (r >= 0), none for a remote one (r = -1), whose loads then return zeros and
-// whose stores are dropped, without a branch or a memory access.  The index
-// is the same for every lane, so the resource sits in scalar registers.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t row_rsrc(const void* base, int32_t r, int row_bytes) {
-  const char* p = (const char*)base + (r >= 0 ? (int64_t)r * row_bytes : 0);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, r >= 0 ? row_bytes : 0, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(rsrc_t rs, int off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void buf_store16(rsrc_t rs, int off, uint4 u) {
-  __builtin_amdgcn_raw_buffer_store_b128(decltype(__builtin_amdgcn_raw_buffer_load_b128(rs, 0, 0, 0)){u.x, u.y, u.z, u.w},
-                                         rs, off, 0, 0);
-}
-
 template <> struct Vec8<bf16_t> {
   struct Raw { uint4 v; };
   // elements [8v, 8v + 8) of a row
