@@ -118,44 +118,62 @@ __device__ __forceinline__ void mx_quant8(const uint4 v, uint2& codes, uint8_t& 
   scale_byte = (uint8_t)(se + 127);
 }
 
+// One block per token, 16 elements per lane: two lanes hold one MX block of
+// 32, four lanes the two blocks of one 64-wide K step, whose scale bytes are
+// adjacent in the pair-plane layout and go out as one 2-byte store.  Codes go
+// out as 16-byte stores through per-row buffer resources (size 0, stores
+// dropped, for remote slots).  d % 64 == 0, so a group of four lanes is
+// active or inactive as a whole.
 __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ rop, int ntok,
                                                                     int k, int d, uint8_t* __restrict__ xq,
                                                                     uint8_t* __restrict__ xs, int64_t xs_rows) {
-  __shared__ int32_t rows[kMaxK];
-  __shared__ int nloc;
-  const int nv = d / 8;            // multiple of 4: blocks of 32 never straddle lanes groups
-  const int iters = (nv + 255) / 256;
+  const int nv = d / 16;
+  const int lane = lane_id();
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int j = 0; j < k; ++j) {
-        int r = rop[(int64_t)t * k + j];
-        if (r >= 0) rows[n++] = r;
-      }
-      nloc = n;
-    }
-    __syncthreads();
-    const int n = nloc;
+    const int32_t* tr = rop + (int64_t)t * k;
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * d);
-    for (int it = 0; it < iters; ++it) {
-      const int v = it * 256 + threadIdx.x;
-      const bool act = v < nv;
-      uint4 val = act ? src[v] : make_uint4(0, 0, 0, 0);
-      uint2 codes;
-      uint8_t sb;
-      mx_quant8(val, codes, sb);
-      if (act) {
-        for (int j = 0; j < n; ++j) {
-          reinterpret_cast<uint2*>(xq + (int64_t)rows[j] * d)[v] = codes;
-          if ((v & 3) == 0) {  // pair-plane scale layout, xs_rows rows per plane
-            const int b = v >> 2;
-            xs[(int64_t)(b >> 1) * xs_rows * 2 + (int64_t)rows[j] * 2 + (b & 1)] = sb;
-          }
+    for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+      int32_t r[kSlotGroup];
+      rsrc_t rs[kSlotGroup];
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) {
+        const int jc = j0 + i < k ? j0 + i : k - 1;
+        const int32_t rv = tr[jc];
+        r[i] = (j0 + i < k) ? rv : -1;
+        rs[i] = row_rsrc(xq, r[i], d);
+      }
+      for (int v = threadIdx.x; v < nv; v += 256) {
+        const uint4 w0 = src[2 * v], w1 = src[2 * v + 1];
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float f[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          f[2 * i] = __uint_as_float(w[i] << 16);
+          f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+          amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const int se = mx_scale_exp(amax);
+        uint32_t c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = e4m3_rne(ldexpf(f[i], -se));
+        const uint4 codes = make_uint4(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24),
+                                       c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24),
+                                       c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24));
+        // scale byte of the second block of this 64-wide step, from lane + 2
+        const int se_hi = __shfl(se, (lane & ~3) + 2, 64);
+        const uint16_t pair = (uint16_t)((se + 127) | ((se_hi + 127) << 8));
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i) {
+          buf_store16(rs[i], 16 * v, codes);
+          if (r[i] >= 0 && (v & 3) == 0)  // pair plane v / 4, row r
+            *reinterpret_cast<uint16_t*>(xs + (int64_t)(v >> 2) * xs_rows * 2 + (int64_t)r[i] * 2) = pair;
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -475,14 +493,18 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
           }
           Vec8<T>::store(dyr[i], v, z);
           if constexpr (MX) {
-            // lanes 4m .. 4m + 3 hold the 32 values of one block (nv % 4 == 0,
-            // so a group of four is active or inactive as a whole)
+            // lanes 4m .. 4m + 3 hold the 32 values of one block (d % 64 == 0
+            // in MXFP8, so a group of eight lanes is active or inactive as a
+            // whole)
             float amax = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(z[q]));
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
             const int se = mx_scale_exp(amax);
+            // the second block of this 64-wide K step is four lanes up; the
+            // two scale bytes are adjacent in the pair plane (d % 64 == 0)
+            const int se_hi = __shfl(se, (lane & ~7) + 4, 64);
             uint32_t cd[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) cd[q] = e4m3_rne(ldexpf(z[q], -se));
@@ -491,10 +513,9 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
               codes.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
               codes.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
               reinterpret_cast<uint2*>(dyq + (int64_t)r[i] * d)[v] = codes;
-              if ((v & 3) == 0) {
-                const int b = v >> 2;
-                dys[(int64_t)(b >> 1) * dys_rows * 2 + (int64_t)r[i] * 2 + (b & 1)] = (uint8_t)(se + 127);
-              }
+              if ((v & 7) == 0)
+                *reinterpret_cast<uint16_t*>(dys + (int64_t)(v >> 3) * dys_rows * 2 + (int64_t)r[i] * 2) =
+                    (uint16_t)((se + 127) | ((se_hi + 127) << 8));
             }
           }
         }
