@@ -316,6 +316,25 @@ def measure(name: str, args, extras: bool):
         graph_res = {"ms_per_step": round(g_ms / K, 4), "tokens_per_s": round(T * K / (g_ms * 1e-3), 1)}
         del graph
 
+    # Cold steps: a 512 MiB device write before each step evicts the 256 MB
+    # last-level cache (MALL), so weights and activations come from HBM; each
+    # step timed alone, the median reported.
+    cold_res = None
+    if extras and not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ce = [ev.create(2) for _ in range(K)]
+        for i in range(K):
+            flush.fill_(i & 0xFF)
+            ev.record(ce[i][0], sh)
+            step()
+            ev.record(ce[i][1], sh)
+        vals = sorted(ev.elapsed_ms(a, b) for a, b in ce)
+        med = vals[len(vals) // 2]
+        cold_res = {"ms_per_step_median": round(med, 4), "tokens_per_s": round(T / (med * 1e-3), 1),
+                    "flush": "512 MiB device write before each step, outside the timed events"}
+        del flush
+        torch.cuda.synchronize()
+
     # per-stage averages over the timed steps
     stages = {}
     ran = mok.STAGES if backward else mok.STAGES[:mok.STAGES.index("combine") + 1]
@@ -372,6 +391,7 @@ def measure(name: str, args, extras: bool):
         "data_movement": hbm,
         "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
         "graph_replay": graph_res,
+        "cold": cold_res,
         "wall_s": round(wall, 3),
     }
     return result, w, inp, (K, Wm, ev, sh)
@@ -391,6 +411,8 @@ def main():
     ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra timing of the same step captured in a HIP graph")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the extra timing of steps that start with the last-level cache flushed")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8 forward+backward leg after the bf16 training workload")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
