@@ -156,3 +156,25 @@ def test_mxfp8_backward_reruns_bitwise_identical():
         again = [buf.out] + [buf.grads[n] for n in names]
         for a, b in zip(first, again):
             assert torch.equal(a, b), f"rerun {rep} differs"
+
+
+def test_mxfp8_backward_zero_tokens():
+    """T = 0: nothing to route; every weight gradient is written as zeros."""
+    w = W.scaled("bf16_fwd", precision="mxfp8", backward=True, T=0, d=128, E=8, k=2, F=128)
+    note("mxfp8 backward zero tokens")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    assert to_np(buf.counts).sum() == 0
+    for n in ("dW1", "dW3", "dW2"):
+        assert not buf.grads[n].any(), f"{n} not zero"
+
+
+def test_mxfp8_backward_one_token():
+    w = W.scaled("bf16_fwd", precision="mxfp8", backward=True, T=1, d=256, E=8, k=3, F=512)
+    note("mxfp8 backward one token")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    errs = _errors(w, inp, buf)
+    note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items() if "[" not in k))
+    bad = {k: v for k, v in errs.items() if v > TOL_MX}
+    assert not bad, bad
