@@ -33,7 +33,11 @@
 
 namespace mok {
 
-constexpr int kMxNS = 5;     // LDS stage buffers
+constexpr int kMxNS = 5;     // LDS stage buffers (4-wave workgroups)
+#ifndef MOK_MX_WAVES
+#define MOK_MX_WAVES 8
+#endif
+constexpr int kMxWaves = MOK_MX_WAVES;
 
 __device__ __forceinline__ u32x4_t pack_bf16x8(const float* v) {
   u32x4_t w;
@@ -66,19 +70,32 @@ template <int KIND> __host__ __device__ inline int mx_n(int d, int F) {
   return KIND == KIND_UP || KIND == KIND_DH ? F : d;
 }
 
-template <int KIND>
+// NW waves per workgroup: NW = 4 as 2 x 2 waves of 128 x TN (128
+// accumulators); NW = 8 as 4 x 2 waves of 64 x TN (64 accumulators, two waves
+// per SIMD, so that one wave's MFMAs can run while the other waits to issue
+// its copies).
+template <int KIND, int NW>
 struct MxJob {
   static constexpr int NB = KIND == KIND_UP ? 2 : 1;
   static constexpr int BM = 256, BN = KIND == KIND_UP ? 64 : 128, BROWS = NB * BN;
-  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  static constexpr int WM = NW / 2;                   // waves along M (2 along N)
+  static constexpr int TM = BM / WM, TN = BN / 2, FM = TM / 32, FN = TN / 32;
+  static constexpr int NS = NW == 4 ? kMxNS : 4;      // LDS stage buffers
   static constexpr int A_BYTES = BM * kMxBK, B_BYTES = BROWS * kMxBK;
-  static constexpr int SCA = A_BYTES + B_BYTES;       // A scale dwords: row r at dword r
-  static constexpr int SCB = SCA + BM * 4;            // B scale dwords: row r at dword 64 (r / 32) + r % 32
-  static constexpr int STAGE = SCB + 256 * 4;
-  static constexpr int IA = A_BYTES / 1024 / 4, IB = B_BYTES / 1024 / 4;  // 16-byte copies per wave
+  // Scale dwords (each 2-byte copy lands zero-extended in one dword); every
+  // wave issues one A-scale and one B-scale copy of RA resp. RB rows, whose
+  // lanes past those rows read outside the resource into unused dwords:
+  //   A row r at dword 64 (r / RA) + r % RA, B row r at dword 64 (r / RB) + r % RB.
+  static constexpr int RA = BM / NW, RB = BROWS / NW;
+  static constexpr int SCA = A_BYTES + B_BYTES;
+  static constexpr int SCB = SCA + NW * 256;
+  static constexpr int STAGE = SCB + NW * 256;
+  static constexpr int IA = A_BYTES / 1024 / NW, IB = B_BYTES / 1024 / NW;  // 1 KB copies per wave
   static constexpr int D = IA + IB + 2;               // + one 2-byte copy per wave for each scale set
-  static_assert(BM == 256 && BROWS == 128, "scale copies: A 64 rows, B 32 rows per wave");
-  static_assert((kMxNS - 1) * D <= 63, "vmcnt holds at most 63");
+  static constexpr int STAGING = NW * 4096;           // epilogue staging, 4 KB per wave
+  static_assert(BM == 256 && BROWS == 128 && FM % 2 == 0, "tile");
+  static_assert((NS - 1) * D <= 63, "vmcnt holds at most 63");
+  static_assert(NS * STAGE + STAGING <= 163840, "LDS");
 
   struct AFrag {  // one 32-row block of A for one K step, with its scales
     i32x8_t v;
@@ -139,15 +156,15 @@ struct MxJob {
     // scale copies: wave w brings A rows 64 w .. 64 w + 63 and, in lanes 0-31,
     // B rows 32 w .. 32 w + 31 (UP: of W1 for w < 2, of W3 after); lanes 32-63
     // of the B copy read past the resource and land zero in unused dwords
-    offSA = (uint32_t)((wid * 64 + lane) * 2);
-    const int rb = wid * 32 + lane;
-    offSB = lane < 32 ? (uint32_t)(((NB == 2 && rb >= BN) ? rb - BN : rb) * 2) : 0xFFFFFFF0u;
+    offSA = lane < RA ? (uint32_t)((wid * RA + lane) * 2) : 0xFFFFFFF0u;
+    const int rb = wid * RB + lane;
+    offSB = lane < RB ? (uint32_t)(((NB == 2 && rb >= BN) ? rb - BN : rb) * 2) : 0xFFFFFFF0u;
   }
 
   // Copies [Q0, Q1) of stage s (A data, B data, A scales, B scales).
   template <int Q0, int Q1>
   __device__ __forceinline__ void issue_part(int s, uint8_t* arena) const {
-    uint8_t* st = arena + (s % kMxNS) * STAGE;
+    uint8_t* st = arena + (s % NS) * STAGE;
     const int k0 = s * kMxBK;
 #pragma unroll
     for (int q = 0; q < IA; ++q)
@@ -159,7 +176,7 @@ struct MxJob {
                  offB[q], k0);
     if (IA + IB >= Q0 && IA + IB < Q1) dma_u16(rsSA, lds_addr(st + SCA + wid * 256), offSA, (uint32_t)s * psA);
     if (IA + IB + 1 >= Q0 && IA + IB + 1 < Q1)
-      dma_u16((NB == 2 && wid * 32 >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB,
+      dma_u16((NB == 2 && wid * RB >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB,
               (uint32_t)s * psB);
   }
   __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
@@ -171,7 +188,7 @@ struct MxJob {
     const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, h) * 16);
     const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, 2 + h) * 16);
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    f.s = *reinterpret_cast<const uint32_t*>(st + SCA + r * 4) >> (8 * h);
+    f.s = *reinterpret_cast<const uint32_t*>(st + SCA + (64 * (r / RA) + r % RA) * 4) >> (8 * h);
   }
   __device__ __forceinline__ void read_b(int buf, const uint8_t* arena, BFrags& f) const {
     const uint8_t* st = arena + buf * STAGE;
@@ -184,7 +201,7 @@ struct MxJob {
         const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, h) * 16);
         const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, 2 + h) * 16);
         f.v[b][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        f.s[b][j] = *reinterpret_cast<const uint32_t*>(st + SCB + ((r >> 5) * 64 + (r & 31)) * 4) >> (8 * h);
+        f.s[b][j] = *reinterpret_cast<const uint32_t*>(st + SCB + (64 * (r / RB) + r % RB) * 4) >> (8 * h);
       }
   }
 
@@ -234,7 +251,7 @@ struct MxJob {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
     if (nk <= 0) return;
-    wait_stages<D, kMxNS - 1>(nk - 1 < kMxNS - 1 ? nk - 1 : kMxNS - 1);
+    wait_stages<D, NS - 1>(nk - 1 < NS - 1 ? nk - 1 : NS - 1);
     BFrags b0, b1;
     AFrag a0, a1;
     read_b(0, arena, b0);
@@ -252,7 +269,7 @@ struct MxJob {
   // (unless it was the last stage) the next stage's are in bn and a0.
   __device__ __forceinline__ void step(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, BFrags& bc, BFrags& bn,
                                        AFrag& a0, AFrag& a1) const {
-    const int buf = kt % kMxNS;
+    const int buf = kt % NS;
 #pragma unroll
     for (int i = 0; i + 1 < FM; ++i) {
       read_a(buf, i + 1, arena, (i & 1) ? a0 : a1);
@@ -261,10 +278,10 @@ struct MxJob {
     }
     // the last row block is in a1 (FM even)
     if (kt + 1 < nk) {
-      wait_stages<D, kMxNS - 2>(nk - 2 - kt < kMxNS - 2 ? nk - 2 - kt : kMxNS - 2);
-      read_b((kt + 1) % kMxNS, arena, bn);
-      read_a((kt + 1) % kMxNS, 0, arena, a0);
-      mma_issue<0, 4>(acc, a1, bc, kt + kMxNS < nk, kt + kMxNS, arena);
+      wait_stages<D, NS - 2>(nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2);
+      read_b((kt + 1) % NS, arena, bn);
+      read_a((kt + 1) % NS, 0, arena, a0);
+      mma_issue<0, 4>(acc, a1, bc, kt + NS < nk, kt + NS, arena);
     } else {
       mma_row<0, 1>(acc, FM - 1, a1, bc);
     }
@@ -467,13 +484,12 @@ struct MxJob {
 // Persistent loop over the row tiles of the local experts (same order and
 // XCD-aware mapping as the bf16 kernel); the next tile's first stages are
 // issued before the current tile's epilogue.
-template <int KIND>
-__global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs args) {
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using Job = MxJob<KIND>;
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kMxNS * Job::STAGE + 16384];
-  static_assert(kMxNS * Job::STAGE + 16384 <= 163840, "LDS");
-  uint8_t* const staging = arena + kMxNS * Job::STAGE;
+  using Job = MxJob<KIND, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[Job::NS * Job::STAGE + Job::STAGING];
+  uint8_t* const staging = arena + Job::NS * Job::STAGE;
   const int N = mx_n<KIND>(args.d, args.F);
   const int E_loc = args.E_loc;
   const int ntn = (N + Job::BN - 1) / Job::BN;
@@ -502,7 +518,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
   if (tile >= total) return;
   Job cur;
   cur.init(args, coord(tile));
-  for (int s = 0; s < kMxNS && s < cur.nk; ++s) cur.issue(s, arena);
+  for (int s = 0; s < Job::NS && s < cur.nk; ++s) cur.issue(s, arena);
   f32x16_t acc[Job::NB][Job::FM][Job::FN];
   typename Job::SavedPre pre;
   while (true) {
@@ -513,7 +529,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
     Job nxt = cur;
     if (nt < total) {
       nxt.init(args, coord(nt));
-      for (int s = 0; s < kMxNS && s < nxt.nk; ++s) nxt.issue(s, arena);
+      for (int s = 0; s < Job::NS && s < nxt.nk; ++s) nxt.issue(s, arena);
     }
     cur.epilogue(acc, staging, pre);
     if (nt >= total) break;
@@ -523,24 +539,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs
 #endif
 }
 
-template <int KIND>
+template <int KIND, int NW>
 static hipError_t run_mx(const GroupedGemmArgs& g, hipStream_t s) {
-  using Job = MxJob<KIND>;
+  using Job = MxJob<KIND, NW>;
   const int N = mx_n<KIND>(g.d, g.F);
   const int ntn = (N + Job::BN - 1) / Job::BN;
   const int64_t worst = ((g.P_max + Job::BM - 1) / Job::BM + g.E_loc) * (int64_t)ntn;
   const int blocks = (int)(worst < 256 ? worst : 256);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND>), dim3(blocks), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND, NW>), dim3(blocks), dim3(NW * 64), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
-    case KIND_UP:   return run_mx<KIND_UP>(g, s);
-    case KIND_DOWN: return run_mx<KIND_DOWN>(g, s);
-    case KIND_DH:   return run_mx<KIND_DH>(g, s);
-    case KIND_DX:   return run_mx<KIND_DX>(g, s);
+    case KIND_UP:   return run_mx<KIND_UP, kMxWaves>(g, s);
+    case KIND_DOWN: return run_mx<KIND_DOWN, kMxWaves>(g, s);
+    case KIND_DH:   return run_mx<KIND_DH, kMxWaves>(g, s);
+    case KIND_DX:   return run_mx<KIND_DX, kMxWaves>(g, s);
   }
   return hipErrorNotSupported;
 }
