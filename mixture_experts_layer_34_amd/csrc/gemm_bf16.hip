@@ -72,30 +72,38 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// One operand's share of an LDS stage: ROWS tile rows (M or N) by BK.
-template <bool MN, int ROWS, int BK>
+// One operand's share of an LDS stage: ROWS tile rows (M or N) by BK, copied
+// by NW waves.
+template <bool MN, int ROWS, int BK, int NW>
 struct OpGeo {
-  static constexpr int BYTES = ROWS * BK * 2;    // per stage
-  static constexpr int INST = BYTES / 1024 / 4;  // DMA instructions per wave per stage
+  static constexpr int BYTES = ROWS * BK * 2;     // per stage
+  static constexpr int INST = BYTES / 1024 / NW;  // DMA instructions per wave per stage
   static constexpr int ROWB = ROWS * 2;          // MN: bytes of one k row
   static constexpr int LPR = ROWS / 8;           // MN: lanes per k row in a DMA instruction
   static constexpr int RPI = 64 / LPR;           // MN: k rows per DMA instruction
   static constexpr int KLPR = BK / 8;            // K-contiguous: lanes per row in a DMA instruction
   static constexpr int KRPI = 64 / KLPR;         // K-contiguous: rows per DMA instruction
-  static_assert(INST >= 1 && BYTES % 4096 == 0, "stage share must fill whole wave DMA instructions");
+  static_assert(INST >= 1 && BYTES % (1024 * NW) == 0, "stage share must fill whole wave DMA instructions");
   static_assert(!MN || (ROWS % 128 == 0 && RPI >= 1), "M/N-contiguous tile rows");
 };
 
 // One output tile: its DMA sources, K loop and epilogue, with NS LDS stage
-// buffers of BK (32 or 64) K values.  All members are wave-uniform except the
-// per-lane DMA offsets.
-template <int KIND, int BM, int BN, int NS, int BK>
+// buffers of BK (32 or 64) K values, computed by NW waves, WMW along M and
+// NW / WMW along N.  NW = 4 (2 x 2): 128 x 128 per wave, 256 accumulators.
+// NW = 8, two waves per SIMD with 128 accumulators each, so that one wave's
+// MFMAs run while the other waits to issue its copies or for its fragments:
+// 4 x 2 (64 x 128 per wave; each B fragment is read by four waves) or 2 x 4
+// (128 x 64; each A fragment read by four), the latter for kinds whose B
+// fragments come from the slower transposing LDS reads.
+// All members are wave-uniform except the per-lane DMA offsets.
+template <int KIND, int BM, int BN, int NS, int BK, int NW = 4, int WMW = 2>
 struct TileJob {
   using Tr = Traits<KIND>;
-  static constexpr int NB = Tr::NB, BROWS = NB * BN;
-  static constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-  using GA = OpGeo<Tr::A_MN, BM, BK>;
-  using GB = OpGeo<Tr::B_MN, BROWS, BK>;
+  static constexpr int NB = Tr::NB, BROWS = NB * BN, WNW = NW / WMW;
+  static constexpr int TM = BM / WMW, TN = BN / WNW, FM = TM / 32, FN = TN / 32;
+  static_assert(FM >= 1 && FN >= 1 && (FN % 2 == 0 || NB == 2 || Tr::GROUP_K), "wave tile");
+  using GA = OpGeo<Tr::A_MN, BM, BK, NW>;
+  using GB = OpGeo<Tr::B_MN, BROWS, BK, NW>;
   static constexpr int KK = BK / 16;  // 16-K MFMA slices per stage
   static_assert(BK == 32 || BK == 64, "stage depth");
   static constexpr int A_BYTES = GA::BYTES;
@@ -132,8 +140,8 @@ struct TileJob {
     c = tc;
     lane = threadIdx.x & 63;
     wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wm = wid >> 1;
-    wn = wid & 1;
+    wm = wid / WNW;
+    wn = wid % WNW;
     kbeg = Tr::GROUP_K ? c.row0 : 0;
     kend = Tr::GROUP_K ? c.row_end : G.K;
     nk = (kend - kbeg + BK - 1) / BK;
@@ -547,17 +555,18 @@ struct TileJob {
   }
 };
 
-// Persistent grouped GEMM.  LDS: the NS stage buffers, then either the
-// 32 KB bf16 epilogue staging area (row kinds; 160 KB in all) or the mailbox
-// through which wave 0 hands the tile taken from the queue to the workgroup
+// Persistent grouped GEMM.  LDS: the NS stage buffers, then either the bf16
+// epilogue staging area (row kinds; 8 KB per wave) or the mailbox through
+// which wave 0 hands the tile taken from the queue to the workgroup
 // (weight-gradient kinds).  The tile-prefix table is searched in global
 // memory through the scalar cache.
-template <int KIND, int BM, int BN, int NS, int BK>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
+template <int KIND, int BM, int BN, int NS, int BK, int NW, int WMW>
+__global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_kernel(GroupedGemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
   using Tr = Traits<KIND>;
-  using Job = TileJob<KIND, BM, BN, NS, BK>;
-  constexpr int kExtra = Tr::GROUP_K ? 256 : 32768;
+  using Job = TileJob<KIND, BM, BN, NS, BK, NW, WMW>;
+  constexpr int kExtra = Tr::GROUP_K ? 256 : NW * 8192;
+  static_assert(NS * Job::STAGE + kExtra <= 163840, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t arena[NS * Job::STAGE + kExtra];
   uint8_t* const staging = arena + NS * Job::STAGE;
   int* const mbox = reinterpret_cast<int*>(staging);
@@ -719,7 +728,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GroupedGemmArgs 
 #endif
 }
 
-template <int KIND, int BM, int BN, int NS, int BK>
+template <int KIND, int BM, int BN, int NS, int BK, int NW, int WMW>
 static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
   const GemmGeom G = geom_of<KIND>(g.d, g.F);
   const int ntn = (G.N + BN - 1) / BN;
@@ -734,15 +743,14 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
     blocks = (int)(worst < 256 ? worst : 256);
   }
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<KIND, BM, BN, NS, BK>), dim3(blocks), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<KIND, BM, BN, NS, BK, NW, WMW>), dim3(blocks), dim3(NW * 64), 0, s,
+                     g);
   return hipGetLastError();
 }
 
 // Stage depth (BK) and count (NS) per kind: 32 x 4 or 64 x 2 fill the LDS.
 #ifndef MOK_BK_UP
-#define MOK_NS_UP 4
 #define MOK_BK_UP 32
-#define MOK_NS_DOWN 4
 #define MOK_BK_DOWN 32
 #define MOK_NS_DH 4
 #define MOK_BK_DH 32
@@ -752,14 +760,26 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
 #define MOK_BK_DW 32
 #endif
 
+// Waves per workgroup and their layout per kind.  UP and DOWN (both operands
+// K-contiguous) run eight waves, 4 x 2, with three stage buffers (their
+// staging then takes 64 KB of the LDS): 2.05 -> 1.90 ms and 1.14 -> 1.05 ms
+// at T 8192, d 4096, E 128, k 8, F 1536.  DH, DX and the weight-gradient
+// kinds measured slower with eight waves in either layout (DH 1.30 -> 1.44-
+// 1.51 ms, DX 2.19 -> 2.34-2.40, dW1/dW3 2.74 -> 2.83) and keep four.
+#ifndef MOK_BF16_WAVES_FWD
+#define MOK_BF16_WAVES_FWD 8
+#endif
+constexpr int kWF = MOK_BF16_WAVES_FWD;
+constexpr int kNsFwd = kWF == 8 ? 3 : 4;
+
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
-    case KIND_UP:   return run_bf16<KIND_UP, 256, 128, MOK_NS_UP, MOK_BK_UP>(g, s);
-    case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, MOK_NS_DOWN, MOK_BK_DOWN>(g, s);
-    case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH>(g, s);
-    case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX>(g, s);
-    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW>(g, s);
-    case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW>(g, s);
+    case KIND_UP:   return run_bf16<KIND_UP, 256, 128, kNsFwd, MOK_BK_UP, kWF, kWF / 2>(g, s);
+    case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, kNsFwd, MOK_BK_DOWN, kWF, kWF / 2>(g, s);
+    case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH, 4, 2>(g, s);
+    case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX, 4, 2>(g, s);
+    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
+    case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
   }
   return hipErrorInvalidValue;
 }
