@@ -52,6 +52,10 @@
 // both) against 3.0-3.1 ms without; dW2 is unaffected.  The row kinds keep
 // their weight and row tiles in L2 for the other tiles that share them: the
 // hint on either operand makes UP and DOWN 10-35 % slower.
+// Row tiles: skip the MFMAs of 32-row blocks wholly past the expert's end.
+#ifndef MOK_SKIP_PAD
+#define MOK_SKIP_PAD 1
+#endif
 #ifndef MOK_DW_NT_A
 #define MOK_DW_NT_A 0
 #endif
@@ -131,6 +135,7 @@ struct TileJob {
   TileCoord c;
   int wid, lane, wm, wn;
   int kbeg, kend, nk;
+  int nvb;  // this wave's 32-row blocks that hold rows of the expert (the rest: no MFMAs)
   i32x4_t rsA, rsB0, rsB1;  // K-contiguous sources (whole tile)
   uint32_t offA[GA::INST], offB[GB::INST];
 
@@ -145,6 +150,13 @@ struct TileJob {
     kbeg = Tr::GROUP_K ? c.row0 : 0;
     kend = Tr::GROUP_K ? c.row_end : G.K;
     nk = (kend - kbeg + BK - 1) / BK;
+    nvb = FM;
+    if constexpr (!Tr::GROUP_K && MOK_SKIP_PAD && NW == 8) {  // (256 accumulators: the branches spill)
+      // rows past the expert's end are zero padding and are never stored:
+      // their MFMAs are skipped (less work, less power)
+      const int left = c.row_end - (c.row0 + wm * TM);
+      nvb = left <= 0 ? 0 : (left >= TM ? FM : (left + 31) / 32);
+    }
     const bf16_t* Abase = (const bf16_t*)a.A;
     rsA = rsB0 = rsB1 = make_rsrc(Abase, 0u);
     // ---- A
@@ -324,11 +336,11 @@ struct TileJob {
       }
   }
 
-  __device__ __forceinline__ static void mma(f32x16_t (&acc)[NB][FM][FN], const Frags& f) { mma_part<0, 1>(acc, f); }
+  __device__ __forceinline__ void mma(f32x16_t (&acc)[NB][FM][FN], const Frags& f) const { mma_part<0, 1>(acc, f); }
 
   // MFMAs [g, g + 1) / NG of a slice, in (b, i, j) order.
   template <int g, int NG>
-  __device__ __forceinline__ static void mma_part(f32x16_t (&acc)[NB][FM][FN], const Frags& f) {
+  __device__ __forceinline__ void mma_part(f32x16_t (&acc)[NB][FM][FN], const Frags& f) const {
     constexpr int TOT = NB * FM * FN, L0 = g * TOT / NG, L1 = (g + 1) * TOT / NG;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -337,7 +349,7 @@ struct TileJob {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int L = (b * FM + i) * FN + j;
-          if (L >= L0 && L < L1)
+          if (L >= L0 && L < L1 && i < nvb)
             acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[b][j], acc[b][i][j], 0, 0, 0);
         }
   }

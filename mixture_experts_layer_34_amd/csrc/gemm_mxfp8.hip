@@ -34,6 +34,10 @@
 namespace mok {
 
 constexpr int kMxNS = 5;     // LDS stage buffers (4-wave workgroups)
+// Row tiles: skip the MFMAs of 32-row blocks wholly past the expert's end.
+#ifndef MOK_SKIP_PAD
+#define MOK_SKIP_PAD 1
+#endif
 #ifndef MOK_MX_WAVES
 #define MOK_MX_WAVES 8
 #endif
@@ -111,6 +115,7 @@ struct MxJob {
   uint32_t psA, psB;  // bytes per scale plane of A (P_max rows) and of B (E_loc * N rows)
   TileCoord c;
   int wid, lane, wm, wn, nk;
+  int nvb;  // this wave's 32-row blocks that hold rows of the expert (the rest: no MFMAs)
   i32x4_t rsA, rsB0, rsB1, rsSA, rsSB0, rsSB1;
   uint32_t offA[IA], offB[IB], offSA, offSB;
 
@@ -124,6 +129,13 @@ struct MxJob {
     wm = wid >> 1;
     wn = wid & 1;
     nk = K / kMxBK;
+    nvb = FM;
+    if (MOK_SKIP_PAD) {
+      // rows past the expert's end are zero padding and are never stored:
+      // their MFMAs are skipped (less work, less power)
+      const int left = c.row_end - (c.row0 + wm * TM);
+      nvb = left <= 0 ? 0 : (left >= TM ? FM : (left + 31) / 32);
+    }
     const int rows = c.row_end - c.row0 < BM ? c.row_end - c.row0 : BM;
     const int nb_rows = N - c.n0 < BN ? N - c.n0 : BN;
     const int64_t wst = (int64_t)N * K;  // bytes per expert of one weight matrix
@@ -207,8 +219,9 @@ struct MxJob {
 
   // MFMAs of row block i (all B blocks), [g, g + 1) / NG of them.
   template <int g, int NG>
-  __device__ __forceinline__ static void mma_row(f32x16_t (&acc)[NB][FM][FN], int i, const AFrag& fa,
-                                                 const BFrags& fb) {
+  __device__ __forceinline__ void mma_row(f32x16_t (&acc)[NB][FM][FN], int i, const AFrag& fa,
+                                          const BFrags& fb) const {
+    if (i >= nvb) return;
     constexpr int TOT = NB * FN, L0 = g * TOT / NG, L1 = (g + 1) * TOT / NG;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
