@@ -775,13 +775,22 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
 // Waves per workgroup and their layout per kind.  UP and DOWN (both operands
 // K-contiguous) run eight waves, 4 x 2, with three stage buffers (their
 // staging then takes 64 KB of the LDS): 2.05 -> 1.90 ms and 1.14 -> 1.05 ms
-// at T 8192, d 4096, E 128, k 8, F 1536.  DH, DX and the weight-gradient
-// kinds measured slower with eight waves in either layout (DH 1.30 -> 1.44-
-// 1.51 ms, DX 2.19 -> 2.34-2.40, dW1/dW3 2.74 -> 2.83) and keep four.
+// at T 8192, d 4096, E 128, k 8, F 1536.  DH and DX measured slower with
+// eight waves in either layout (DH 1.30 -> 1.44-1.51 ms, DX 2.19 -> 2.34-
+// 2.40) and keep four.
 #ifndef MOK_BF16_WAVES_FWD
 #define MOK_BF16_WAVES_FWD 8
 #endif
 constexpr int kWF = MOK_BF16_WAVES_FWD;
+// dW2 runs eight waves, 2 x 4 (same-box A/B: 1.44 -> 1.34-1.38 ms); dW1/dW3
+// keeps four (eight, 2 x 4 or 4 x 2: 2.68-2.73 -> 2.80-2.84 ms).
+#ifndef MOK_BF16_WAVES_DW
+#define MOK_BF16_WAVES_DW 8
+#endif
+#ifndef MOK_BF16_WM_DW
+#define MOK_BF16_WM_DW 2
+#endif
+constexpr int kWDW = MOK_BF16_WAVES_DW, kWmDW = MOK_BF16_WM_DW;
 constexpr int kNsFwd = kWF == 8 ? 3 : 4;
 
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
@@ -790,7 +799,7 @@ hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, kNsFwd, MOK_BK_DOWN, kWF, kWF / 2>(g, s);
     case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH, 4, 2>(g, s);
     case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX, 4, 2>(g, s);
-    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
+    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW, kWDW, kWmDW>(g, s);
     case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
   }
   return hipErrorInvalidValue;
