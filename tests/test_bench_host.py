@@ -34,3 +34,31 @@ def test_traffic_null_after_source_change(tmp_path, monkeypatch):
 def test_traffic_null_without_record(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
     assert bench.measured_traffic("wl", "gemm_x") is None
+
+
+def test_gemm_peaks_per_precision():
+    """MXFP8 layer: the forward GEMMs and the dH / dX products against the
+    MXFP8 peak, the bf16 weight-gradient GEMMs against the bf16 one."""
+    for n in ("gemm_up", "gemm_down", "gemm_dh", "gemm_dx"):
+        assert bench.gemm_peak("mxfp8", n) == bench.PEAK_TFLOPS["mxfp8"]
+    for n in ("gemm_dw2", "gemm_dw13"):
+        assert bench.gemm_peak("mxfp8", n) == bench.PEAK_TFLOPS["bf16"]
+        assert bench.gemm_peak("bf16", n) == bench.PEAK_TFLOPS["bf16"]
+
+
+def test_stage_work_mxfp8_bytes():
+    """Algorithmic bytes of the MXFP8 training step: one byte per element plus
+    one scale per 32 for the quantised operands, bf16 for the rest."""
+    import workloads as W
+    w = W.get("mxfp8_train")
+    P, U = 1024, 200
+    flops, nb = bench.stage_work(w, P, U, save_for_backward=True)
+    b = W.get("bf16_train")
+    fb, nbb = bench.stage_work(b, P, U, save_for_backward=True)
+    assert flops == fb                                       # same products
+    q, d, F, E = 1 + 1 / 32, w.d, w.F, w.E
+    assert nb["dispatch"] == U * d * 2 + P * d * q           # bf16 in, MXFP8 rows out
+    assert nb["bwd_gate"] == nbb["bwd_gate"] + P * d * q     # dY also written in MXFP8
+    assert nb["gemm_dx"] == 2 * P * F * q + 2 * E * F * d * q + P * d * 2
+    assert nb["gemm_up"] == P * d * q + 2 * E * F * d * q + P * F * q + 3 * P * F * 2
+    assert nb["gemm_dw13"] == nbb["gemm_dw13"] and nb["gemm_dw2"] == nbb["gemm_dw2"]
