@@ -164,6 +164,9 @@ inline bool fused_pull(const mok_moe_config& c) {
   return c.precision == MOK_PREC_BF16 && c.minibatch_rows == 0 && (int64_t)c.T * c.d * 2 < (int64_t(1) << 31);
 }
 
+// The call owns every expert (no remote slots).
+inline int all_local(const mok_moe_config& c) { return c.expert_begin == 0 && c.expert_end == c.E; }
+
 // The router variant of a call (kGateSigmoid, kGateRenorm bits).
 static int gating_of(const mok_moe_config& c) {
   return ((c.flags & MOK_FLAG_SIGMOID_GATES) ? kGateSigmoid : 0) | ((c.flags & MOK_FLAG_RENORM_GATES) ? kGateRenorm : 0);
@@ -377,7 +380,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g2.gather_rows = nullptr;
     MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   }
-  MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, out, s));
+  MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, all_local(c), out, s));
   return MOK_OK;
 }
 
@@ -444,7 +447,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   gx.B1 = W3;
   gx.out0 = dxp;
   MOK_STAGE(MOK_STAGE_GEMM_DX, run_gemm(c.precision, KIND_DX, gx, s));
-  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, dx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, all_local(c), dx, s));
   // weight gradients
   GroupedGemmArgs gw = g;
   gw.A = dy;
@@ -575,7 +578,7 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
   gx.b_scale0 = wt_e8m0 + n / 32;
   gx.out0 = dxp;
   MOK_STAGE(MOK_STAGE_GEMM_DX, gemm_mxfp8(KIND_DX, gx, s));
-  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, dx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, all_local(c), dx, s));
   // weight gradients: bf16 products of the unquantised operands
   GroupedGemmArgs gw = g;
   gw.A = dy;

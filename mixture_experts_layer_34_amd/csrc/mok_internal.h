@@ -63,8 +63,9 @@ hipError_t launch_quantize_mxfp8_t(const void* src, int nmat, int R, int C, uint
                                    int64_t q_ld, int q_koff, uint8_t* sc, int64_t rows, hipStream_t s);
 
 // out[t] = sum_j w[t,j] * rows[row(t,j)] (w = gate, or 1 when gate == nullptr).
+// all_local: the call owns every expert (else the kernel for mostly remote slots).
 hipError_t launch_combine(const void* rows, const float* gate, const int32_t* row_of_pair, int T,
-                          int k, int d, int bf16, void* out, hipStream_t s);
+                          int k, int d, int bf16, int all_local, void* out, hipStream_t s);
 
 // Reverse-combine and router backward: dgate, dlogits and dY rows.
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate,
