@@ -56,6 +56,9 @@
 #ifndef MOK_SKIP_PAD
 #define MOK_SKIP_PAD 1
 #endif
+#ifndef MOK_ROW_GM
+#define MOK_ROW_GM 4  // m-tiles per raster group of the row-grouped kinds (tile_mn)
+#endif
 #ifndef MOK_DW_NT_A
 #define MOK_DW_NT_A 0
 #endif
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_kernel(GroupedGemmA
       c.e_loc = lo;
       const int t0 = sload(tp + lo), t1 = sload(tp + lo + 1);
       int mt, nt;
-      tile_mn(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
+      tile_mn<MOK_ROW_GM>(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
       c.n0 = nt * BN;
       const int e = args.eb + lo;
       c.row0 = sload(args.offsets + e) + mt * BM;

@@ -38,6 +38,9 @@ constexpr int kMxNS = 5;     // LDS stage buffers (4-wave workgroups)
 #ifndef MOK_SKIP_PAD
 #define MOK_SKIP_PAD 1
 #endif
+#ifndef MOK_MX_GM
+#define MOK_MX_GM 4  // m-tiles per raster group (tile_mn)
+#endif
 #ifndef MOK_MX_WAVES
 #define MOK_MX_WAVES 8
 #endif
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_mxfp8_kernel(GroupedGemm
     c.e_loc = lo;
     const int t0 = sload(tp + lo), t1 = sload(tp + lo + 1);
     int mt, nt;
-    tile_mn(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
+    tile_mn<MOK_MX_GM>(tile - t0 * ntn, t1 - t0, ntn, mt, nt);
     c.n0 = nt * Job::BN;
     c.row0 = sload(args.offsets + args.eb + lo) + mt * Job::BM;
     c.row_end = sload(args.offsets + args.eb + lo + 1);
