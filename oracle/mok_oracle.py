@@ -62,7 +62,7 @@ __all__ = [
     "route", "route_backward", "router_logits", "router_logits_backward",
     "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
-    "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq",
+    "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq", "mxfp8_qdq_rows",
     "forward_token", "backward_token", "expert_weight_grads",
 ]
 
@@ -315,6 +315,18 @@ def mxfp8_qdq(v, block: int = 32):
     return mxfp8_dequantize(*mxfp8_quantize(v, block), block)
 
 
+def mxfp8_qdq_rows(M, block: int = 32):
+    """MX quantise-dequantise of a [rows, cols] matrix along its rows: each
+    column is cut into blocks of 32 consecutive rows starting at row 0, and
+    a last partial block takes its scale from the rows it has (zero rows
+    appended to fill it change no block maximum)."""
+    M = _f64(M)
+    R = M.shape[0]
+    pad = (-R) % block
+    Mp = np.concatenate([M, np.zeros((pad,) + M.shape[1:])], axis=0) if pad else M
+    return mxfp8_qdq(Mp.T, block).T[:R]
+
+
 # ------------------------------------------------------------------ forward
 
 def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: int | None = None,
@@ -394,7 +406,7 @@ def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int =
 
 def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
              expert_begin: int = 0, expert_end: int | None = None, gating: str = "softmax",
-             renorm: bool = False, mxfp8: bool = False):
+             renorm: bool = False, mxfp8: bool = False, mxfp8_wgrad: bool = False):
     """Gradients of L = sum(out * dout) in float64.
 
     The backward pass mirrors the forward: reverse-combine, expert backward,
@@ -423,6 +435,12 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     where Q is mxfp8_qdq over the last axis.  The weight gradients take the
     unquantised operands: dW2_e = dy_e^T h_e with h = silu(a) * b before its
     quantisation, dW1_e = da_e^T x_e, dW3_e = db_e^T x_e.
+
+    mxfp8_wgrad (with mxfp8) also runs the weight gradients in MXFP8: their
+    contraction runs over the expert's rows, so each operand is quantised
+    along the rows of the expert's segment (mxfp8_qdq_rows, blocks of 32 rows
+    from the expert's first row in the placement order):
+      dW2_e = Qr(dy_e)^T Qr(h_e),  dW1_e = Qr(da_e)^T Qr(x_e),  dW3_e = Qr(db_e)^T Qr(x_e).
     """
     x = _f64(x)
     g = _f64(dout)
@@ -436,6 +454,8 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     gating, renorm = fwd.get("gating", gating), fwd.get("renorm", renorm)
     if mxfp8 != fwd.get("mxfp8", False):
         raise ValueError("backward(mxfp8=...) needs the forward of the same precision")
+    if mxfp8_wgrad and not mxfp8:
+        raise ValueError("mxfp8_wgrad needs mxfp8")
     gate, p, Y = fwd["gate"], fwd["p"], fwd["Y"]
     rop = fwd["row_of_pair"].reshape(T, k)
     offsets, pair_of_row = fwd["offsets"], fwd["pair_of_row"]
@@ -476,9 +496,15 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
                           + mxfp8_qdq(db) @ mxfp8_qdq(_f64(W3[i]).T).T)
         else:
             dXp[r0:r1] = da @ _f64(W1[i]) + db @ _f64(W3[i])
-        dW2[i] = dy.T @ h
-        dW1[i] = da.T @ Xp[r0:r1]
-        dW3[i] = db.T @ Xp[r0:r1]
+        if mxfp8_wgrad:
+            xq = mxfp8_qdq_rows(Xp[r0:r1])
+            dW2[i] = mxfp8_qdq_rows(dy).T @ mxfp8_qdq_rows(h)
+            dW1[i] = mxfp8_qdq_rows(da).T @ xq
+            dW3[i] = mxfp8_qdq_rows(db).T @ xq
+        else:
+            dW2[i] = dy.T @ h
+            dW1[i] = da.T @ Xp[r0:r1]
+            dW3[i] = db.T @ Xp[r0:r1]
         dA[r0:r1], dB[r0:r1] = da, db
     dx = unpermute_sum(dXp, fwd["row_of_pair"], T, k)
     return dict(dx=dx, dW1=dW1, dW3=dW3, dW2=dW2, dgate=dgate, dlogits=dlogits,
@@ -540,11 +566,12 @@ def _mx_expert_forward(X, W1e, W3e, W2e):
     return a, b, y
 
 
-def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e, mxfp8: bool = False):
+def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e, mxfp8: bool = False, mxfp8_wgrad: bool = False):
     """dW1_e, dW3_e, dW2_e of one expert from its rows alone: X_e [R,d] the
     activations of its pairs, gate_e [R] their gates, dout_e [R,d] the output
-    gradients of their tokens (row order does not matter).  MXFP8 as in
-    backward(mxfp8=True)."""
+    gradients of their tokens (row order does not matter, except with
+    mxfp8_wgrad, whose blocks of 32 rows need the placement order).  MXFP8 as
+    in backward(mxfp8=True, mxfp8_wgrad=...)."""
     X = _f64(X_e)
     if mxfp8:
         a, b, _ = _mx_expert_forward(X, W1e, W3e, W2e)
@@ -556,4 +583,10 @@ def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e, mxfp8: bool = False)
     s = sigmoid(a)
     da = dh * b * s * (1.0 + a * (1.0 - s))
     db = dh * silu(a)
+    if mxfp8_wgrad:
+        if not mxfp8:
+            raise ValueError("mxfp8_wgrad needs mxfp8")
+        xq = mxfp8_qdq_rows(X)
+        return (mxfp8_qdq_rows(da).T @ xq, mxfp8_qdq_rows(db).T @ xq,
+                mxfp8_qdq_rows(dy).T @ mxfp8_qdq_rows(h))
     return da.T @ X, db.T @ X, dy.T @ h

@@ -203,3 +203,115 @@ def test_mxfp8_token_and_expert_views_match_the_layer():
         np.testing.assert_allclose(dW3, bw["dW3"][e], rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(dW2, bw["dW2"][e], rtol=1e-10, atol=1e-12)
     assert (rop >= 0).all()
+
+
+def _brute_wgrad_rows(x, logits, g, W1, W3, W2, k):
+    """MXFP8 weight gradients by scalar loops, each operand quantised along
+    the rows of its expert's segment: the segment lists the expert's (token,
+    slot) pairs in ascending pair index t*k + j (the counting sort's stable
+    order), blocks of 32 rows from its first row, the last block partial."""
+    T, d = x.shape
+    E, F = W1.shape[0], W1.shape[1]
+    w1q = [_qdq_rows(W1[e].tolist()) for e in range(E)]
+    w3q = [_qdq_rows(W3[e].tolist()) for e in range(E)]
+    w2q = [_qdq_rows(W2[e].tolist()) for e in range(E)]
+    w2tq = [_qdq_rows(_transpose(W2[e].tolist())) for e in range(E)]
+    seg = {e: [] for e in range(E)}   # per expert: rows of (x, dy, h, da, db)
+    for t in range(T):
+        lt = [float(v) for v in logits[t]]
+        m = max(lt)
+        z = sum(math.exp(v - m) for v in lt)
+        p = [math.exp(v - m) / z for v in lt]
+        order = sorted(range(E), key=lambda e: (-lt[e], e))[:k]
+        xq = _qdq_row(list(x[t]))
+        for e in order:           # slot j ascending: pair index t*k + j ascending
+            a = _matmul_nt([xq], w1q[e])[0]
+            b = _matmul_nt([xq], w3q[e])[0]
+            h = [_silu(ai) * bi for ai, bi in zip(a, b)]
+            dy = [p[e] * float(gi) for gi in g[t]]
+            dh = _matmul_nt([_qdq_row(dy)], w2tq[e])[0]
+            da = [dh[f] * b[f] * _sig(a[f]) * (1.0 + a[f] * (1.0 - _sig(a[f]))) for f in range(F)]
+            db = [dh[f] * _silu(a[f]) for f in range(F)]
+            seg[e].append((list(map(float, x[t])), dy, h, da, db))
+    out = {"dW1": np.zeros((E, F, d)), "dW3": np.zeros((E, F, d)), "dW2": np.zeros((E, d, F))}
+    for e in range(E):
+        if not seg[e]:
+            continue
+        # quantise every column along the segment's rows
+        cols = [_qdq_rows(_transpose([r[i] for r in seg[e]])) for i in range(5)]   # [col][row]
+        X, DY, H, DA, DB = cols
+        n = len(seg[e])
+        for f in range(F):
+            for c in range(d):
+                out["dW1"][e, f, c] = sum(DA[f][r] * X[c][r] for r in range(n))
+                out["dW3"][e, f, c] = sum(DB[f][r] * X[c][r] for r in range(n))
+        for c in range(d):
+            for f in range(F):
+                out["dW2"][e, c, f] = sum(DY[c][r] * H[f][r] for r in range(n))
+    return out
+
+
+def test_mxfp8_row_quantised_weight_grads_match_scalar_loops():
+    rng = np.random.default_rng(23)
+    T, d, F, E, k = 41, 32, 32, 3, 2
+    x = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 1] += 1.5    # expert 1 takes more than one block of rows
+    W1 = (0.3 * rng.standard_normal((E, F, d))).astype(np.float32).astype(np.float64)
+    W3 = (0.3 * rng.standard_normal((E, F, d))).astype(np.float32).astype(np.float64)
+    W2 = (0.3 * rng.standard_normal((E, d, F))).astype(np.float32).astype(np.float64)
+    g = rng.standard_normal((T, d))
+    fwd = O.forward(x, logits, W1, W3, W2, k, mxfp8=True)
+    sizes = np.diff(fwd["offsets"])
+    # segments longer than one block, starting off a 32-row boundary
+    assert sizes.max() > 32 and any(o % 32 for o in fwd["offsets"][1:-1])
+    bw = O.backward(g, x, logits, W1, W3, W2, k, fwd=fwd, mxfp8=True, mxfp8_wgrad=True)
+    ref = _brute_wgrad_rows(x, logits, g, W1, W3, W2, k)
+    for name in ("dW1", "dW3", "dW2"):
+        err = np.abs(bw[name] - ref[name]).max() / np.abs(ref[name]).max()
+        assert err < 1e-9, (name, err)
+    # the row quantisation is not a no-op, and blocks aligned to the buffer's
+    # row 0 instead of each expert's first row give another result
+    plain = O.backward(g, x, logits, W1, W3, W2, k, fwd=fwd, mxfp8=True)
+    assert np.abs(plain["dW1"] - bw["dW1"]).max() > 1e-3 * np.abs(bw["dW1"]).max()
+    e = int(np.argmax([o % 32 != 0 for o in fwd["offsets"][:-1]]))
+    r0, r1 = fwd["offsets"][e], fwd["offsets"][e + 1]
+    glob = O.mxfp8_qdq_rows(bw["dA"])[r0:r1].T @ O.mxfp8_qdq_rows(O.permute(x, fwd["pair_of_row"], k))[r0:r1]
+    assert np.abs(glob - bw["dW1"][e]).max() > 1e-3 * np.abs(bw["dW1"][e]).max()
+    # the other backward outputs are those of the bf16-weight-gradient reading
+    for name in ("dx", "dgate", "dlogits"):
+        np.testing.assert_array_equal(plain[name], bw[name])
+
+
+def test_row_quantisation_partial_block():
+    """A partial last block takes its scale from its own rows: a segment of
+    33 rows whose last row is tiny keeps that row to E4M3 precision, and the
+    first 32 rows quantise as a block of their own."""
+    rng = np.random.default_rng(3)
+    M = rng.standard_normal((33, 4))
+    M[32] = 1e-6 * rng.standard_normal(4)
+    q = O.mxfp8_qdq_rows(M)
+    np.testing.assert_array_equal(q[:32], O.mxfp8_qdq_rows(M[:32]))
+    assert np.all(np.abs(q[32] - M[32]) <= 2.0 ** -4 * np.abs(M[32]))
+    assert np.all(q[32] != 0)
+
+
+def test_expert_view_row_quantised():
+    rng = np.random.default_rng(8)
+    T, d, F, E, k = 48, 64, 64, 2, 2
+    x = rng.standard_normal((T, d)).astype(np.float32).astype(np.float64)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    W1 = (0.1 * rng.standard_normal((E, F, d))).astype(np.float64)
+    W3 = (0.1 * rng.standard_normal((E, F, d))).astype(np.float64)
+    W2 = (0.1 * rng.standard_normal((E, d, F))).astype(np.float64)
+    g = rng.standard_normal((T, d))
+    fwd = O.forward(x, logits, W1, W3, W2, k, mxfp8=True)
+    bw = O.backward(g, x, logits, W1, W3, W2, k, fwd=fwd, mxfp8=True, mxfp8_wgrad=True)
+    por = fwd["pair_of_row"]
+    for e in range(E):
+        r0, r1 = fwd["offsets"][e], fwd["offsets"][e + 1]
+        toks, slots = por[r0:r1] // k, por[r0:r1] % k
+        got = O.expert_weight_grads(x[toks], fwd["gate"][toks, slots], g[toks], W1[e], W3[e], W2[e],
+                                    mxfp8=True, mxfp8_wgrad=True)
+        for gv, name in zip(got, ("dW1", "dW3", "dW2")):
+            np.testing.assert_allclose(gv, bw[name][e], rtol=1e-10, atol=1e-12)
