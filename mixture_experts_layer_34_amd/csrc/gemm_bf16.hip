@@ -774,6 +774,12 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
 #define MOK_NS_DW 4
 #define MOK_BK_DW 32
 #endif
+// dW2 takes 64-K stages, two of them (same-box A/B: 1.43 -> 1.40 ms); dW1/dW3
+// keeps 32 x 4 (64 x 2: 2.74 -> 2.83 ms).
+#ifndef MOK_BK_DW2
+#define MOK_NS_DW2 2
+#define MOK_BK_DW2 64
+#endif
 
 // Waves per workgroup and their layout per kind.  UP and DOWN (both operands
 // K-contiguous) run eight waves, 4 x 2, with three stage buffers (their
@@ -802,7 +808,7 @@ hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, kNsFwd, MOK_BK_DOWN, kWF, kWF / 2>(g, s);
     case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH, 4, 2>(g, s);
     case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX, 4, 2>(g, s);
-    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW, MOK_BK_DW, kWDW, kWmDW>(g, s);
+    case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW2, MOK_BK_DW2, kWDW, kWmDW>(g, s);
     case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
   }
   return hipErrorInvalidValue;
