@@ -13,16 +13,17 @@
 //   DW2   dW2_e = dY_e^T H_e                         [d, F] fp32
 //   DW13  dW1_e = dA_e^T X_e, dW3_e = dB_e^T X_e     [F, d] fp32
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x BN tile (per B
-// matrix; UP computes the W1 and W3 tiles of the same columns), each wave a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles.  K advances in stages of 32
-// through a ring of NS LDS stage buffers (four of 32 KB in the grouped
-// GEMMs), so NS - 1 stages are in flight while one is multiplied.  Every
+// Tiling: a workgroup of NW waves (four as 2 x 2, or eight as 4 x 2 or
+// 2 x 4; the choice per kind is in gemm_bf16() below) computes a BM x BN
+// tile (per B matrix; UP computes the W1 and W3 tiles of the same columns),
+// each wave a block of 32x32 MFMA tiles.  K advances in stages of BK (32 or
+// 64) through a ring of NS LDS stage buffers (per kind, below), so NS - 1
+// stages are in flight while one is multiplied.  Every
 // operand goes from HBM straight to LDS
 // (buffer_load_dwordx4 ... lds, 1 KB per wave instruction, no VGPRs),
 // through buffer resources rebased on the tile so that rows past the data
 // read as zero, in the layout it has in memory:
-//   K-contiguous operands ([row][k]): 64-byte LDS rows of four 16-byte
+//   K-contiguous operands ([row][k]): LDS rows of BK * 2 bytes in 16-byte
 //     chunks, XOR-swizzled; fragments are 16-byte reads (ds_read_b128).
 //   M- or N-contiguous operands ([k][row], the backward products): LDS rows
 //     of one k, 64-byte chunks XOR-swizzled by k; fragments are transposing
