@@ -15,13 +15,17 @@
 // epilogue, and the scaled MFMA consumes both without dequantising.
 //
 // The pipeline is the bf16 one (gemm_bf16.hip) with one-byte elements: a
-// stage is 64 K values = one scaled-MFMA K step = 64-byte LDS rows, four
-// stages in flight, the same swizzle, direct-to-LDS copies, barrier placement
-// and tile schedule.  Each stage also carries the two E8M0 bytes of every
-// tile row (2-byte copies that land zero-extended in one LDS dword per row).
-// Scales are stored in pair planes (see mok_quantize_mxfp8): the two bytes of
-// one row for one stage are a 2-byte word of plane k0 / 64, next to those of
-// the next row, so a wave's scale copy reads 128 contiguous bytes.
+// stage is 128 K values = two scaled-MFMA K steps = 128-byte LDS rows, two
+// stage buffers, the same swizzle, direct-to-LDS copies, barrier placement
+// and tile schedule.  The copy path serves whole 128-byte row pieces about
+// twice as fast as 64-byte ones: against 64-K stages (four buffers) at T
+// 8192, d 4096, E 128, k 8, F 1536, UP 1.69 -> 1.59 ms, DOWN 0.90 -> 0.82,
+// DH 1.07 -> 1.03, DX 1.60 -> 1.45 (same-box A/B).  Each stage also carries
+// the two E8M0 bytes of every tile row for each of its K steps (2-byte
+// copies that land zero-extended in one LDS dword per row).  Scales are
+// stored in pair planes (see mok_quantize_mxfp8): the two bytes of one row
+// for one K step are a 2-byte word of plane k / 64, next to those of the
+// next row, so a wave's scale copy reads 128 contiguous bytes.
 // Scaled-MFMA operand layout on gfx950 (checked on the device): lane l holds
 // row l % 32; with h = l / 32 its bytes 0-15 are K [16h, 16h + 16) and bytes
 // 16-31 are K [32 + 16h, +16), and the scale it supplies covers the 32-block
@@ -62,7 +66,12 @@ __device__ __forceinline__ u32x2_t pack_e4m3x8(const float* v, int se) {
   w[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
   return w;
 }
-constexpr int kMxBK = 64;    // K (bytes) per stage
+#ifndef MOK_MX_BK
+#define MOK_MX_BK 128
+#endif
+constexpr int kMxBK = MOK_MX_BK;    // K (bytes) per stage: one (64) or two (128) MFMA K steps
+constexpr int kMxSub = kMxBK / 64;  // MFMA K steps per stage
+constexpr int kMxLPR = kMxBK / 16;  // lanes per row in a 1 KB copy
 
 // One MXFP8 output tile (UP: 256 rows x 64 columns of W1 and W3; DOWN:
 // 256 x 128): 128 accumulators per lane, which leaves the register file room
@@ -87,7 +96,7 @@ struct MxJob {
   static constexpr int BM = 256, BN = KIND == KIND_UP ? 64 : 128, BROWS = NB * BN;
   static constexpr int WM = NW / 2;                   // waves along M (2 along N)
   static constexpr int TM = BM / WM, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-  static constexpr int NS = NW == 4 ? kMxNS : 4;      // LDS stage buffers
+  static constexpr int NS = NW == 4 ? kMxNS : (kMxSub == 1 ? 4 : 2);  // LDS stage buffers
   static constexpr int A_BYTES = BM * kMxBK, B_BYTES = BROWS * kMxBK;
   // Scale dwords (each 2-byte copy lands zero-extended in one dword); every
   // wave issues one A-scale and one B-scale copy of RA resp. RB rows, whose
@@ -95,10 +104,10 @@ struct MxJob {
   //   A row r at dword 64 (r / RA) + r % RA, B row r at dword 64 (r / RB) + r % RB.
   static constexpr int RA = BM / NW, RB = BROWS / NW;
   static constexpr int SCA = A_BYTES + B_BYTES;
-  static constexpr int SCB = SCA + NW * 256;
-  static constexpr int STAGE = SCB + NW * 256;
+  static constexpr int SCB = SCA + kMxSub * NW * 256;   // (one scale set per MFMA K step)
+  static constexpr int STAGE = SCB + kMxSub * NW * 256;
   static constexpr int IA = A_BYTES / 1024 / NW, IB = B_BYTES / 1024 / NW;  // 1 KB copies per wave
-  static constexpr int D = IA + IB + 2;               // + one 2-byte copy per wave for each scale set
+  static constexpr int D = IA + IB + 2 * kMxSub;      // + one 2-byte copy per wave for each scale set
   static constexpr int STAGING = NW * 4096;           // epilogue staging, 4 KB per wave
   static_assert(BM == 256 && BROWS == 128 && FM % 2 == 0, "tile");
   static_assert((NS - 1) * D <= 63, "vmcnt holds at most 63");
@@ -159,14 +168,14 @@ struct MxJob {
     rsSB1 = make_rsrc((NB == 2 ? a.b_scale1 : a.b_scale0) + fb, (uint32_t)(planes * pb - fb));
 #pragma unroll
     for (int q = 0; q < IA; ++q) {
-      const int r = (wid * IA + q) * 16 + (lane >> 2);
-      offA[q] = (uint32_t)(r * K + swz_k<32>(r, lane & 3) * 16);
+      const int r = (wid * IA + q) * (64 / kMxLPR) + lane / kMxLPR;
+      offA[q] = (uint32_t)(r * K + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
     }
 #pragma unroll
     for (int q = 0; q < IB; ++q) {
-      const int r = (wid * IB + q) * 16 + (lane >> 2);
+      const int r = (wid * IB + q) * (64 / kMxLPR) + lane / kMxLPR;
       const int rl = (NB == 2 && r >= BN) ? r - BN : r;
-      offB[q] = (uint32_t)(rl * K + swz_k<32>(r, lane & 3) * 16);
+      offB[q] = (uint32_t)(rl * K + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
     }
     // scale copies: wave w brings A rows 64 w .. 64 w + 63 and, in lanes 0-31,
     // B rows 32 w .. 32 w + 31 (UP: of W1 for w < 2, of W3 after); lanes 32-63
@@ -187,25 +196,32 @@ struct MxJob {
 #pragma unroll
     for (int q = 0; q < IB; ++q)
       if (IA + q >= Q0 && IA + q < Q1)
-        dma_b128((NB == 2 && (wid * IB + q) * 16 >= BN) ? rsB1 : rsB0, lds_addr(st + A_BYTES + (wid * IB + q) * 1024),
-                 offB[q], k0);
-    if (IA + IB >= Q0 && IA + IB < Q1) dma_u16(rsSA, lds_addr(st + SCA + wid * 256), offSA, (uint32_t)s * psA);
-    if (IA + IB + 1 >= Q0 && IA + IB + 1 < Q1)
-      dma_u16((NB == 2 && wid * RB >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + wid * 256), offSB,
-              (uint32_t)s * psB);
+        dma_b128((NB == 2 && (wid * IB + q) * (64 / kMxLPR) >= BN) ? rsB1 : rsB0,
+                 lds_addr(st + A_BYTES + (wid * IB + q) * 1024), offB[q], k0);
+#pragma unroll
+    for (int p = 0; p < kMxSub; ++p) {  // scale plane s * kMxSub + p
+      const uint32_t plane = (uint32_t)(s * kMxSub + p);
+      if (IA + IB + 2 * p >= Q0 && IA + IB + 2 * p < Q1)
+        dma_u16(rsSA, lds_addr(st + SCA + (p * NW + wid) * 256), offSA, plane * psA);
+      if (IA + IB + 2 * p + 1 >= Q0 && IA + IB + 2 * p + 1 < Q1)
+        dma_u16((NB == 2 && wid * RB >= BN) ? rsSB1 : rsSB0, lds_addr(st + SCB + (p * NW + wid) * 256), offSB,
+                plane * psB);
+    }
   }
   __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
 
-  __device__ __forceinline__ void read_a(int buf, int i, const uint8_t* arena, AFrag& f) const {
+  // Fragments of MFMA K step `sub` of a stage: 16-byte chunks 4 sub + h and
+  // 4 sub + 2 + h of the row (h = lane / 32), and that step's scale set.
+  __device__ __forceinline__ void read_a(int buf, int i, int sub, const uint8_t* arena, AFrag& f) const {
     const uint8_t* st = arena + buf * STAGE;
     const int h = lane >> 5;
     const int r = wm * TM + i * 32 + (lane & 31);
-    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, h) * 16);
-    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + r * 64 + swz_k<32>(r, 2 + h) * 16);
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + r * kMxBK + swz_k<kMxBK / 2>(r, 4 * sub + h) * 16);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + r * kMxBK + swz_k<kMxBK / 2>(r, 4 * sub + 2 + h) * 16);
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    f.s = *reinterpret_cast<const uint32_t*>(st + SCA + (64 * (r / RA) + r % RA) * 4) >> (8 * h);
+    f.s = *reinterpret_cast<const uint32_t*>(st + SCA + sub * NW * 256 + (64 * (r / RA) + r % RA) * 4) >> (8 * h);
   }
-  __device__ __forceinline__ void read_b(int buf, const uint8_t* arena, BFrags& f) const {
+  __device__ __forceinline__ void read_b(int buf, int sub, const uint8_t* arena, BFrags& f) const {
     const uint8_t* st = arena + buf * STAGE;
     const int h = lane >> 5;
 #pragma unroll
@@ -213,10 +229,12 @@ struct MxJob {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = b * BN + wn * TN + j * 32 + (lane & 31);
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, h) * 16);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + A_BYTES + r * 64 + swz_k<32>(r, 2 + h) * 16);
+        const uint8_t* row = st + A_BYTES + r * kMxBK;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + h) * 16);
+        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + 2 + h) * 16);
         f.v[b][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        f.s[b][j] = *reinterpret_cast<const uint32_t*>(st + SCB + (64 * (r / RB) + r % RB) * 4) >> (8 * h);
+        f.s[b][j] =
+            *reinterpret_cast<const uint32_t*>(st + SCB + sub * NW * 256 + (64 * (r / RB) + r % RB) * 4) >> (8 * h);
       }
   }
 
@@ -270,33 +288,60 @@ struct MxJob {
     wait_stages<D, NS - 1>(nk - 1 < NS - 1 ? nk - 1 : NS - 1);
     BFrags b0, b1;
     AFrag a0, a1;
-    read_b(0, arena, b0);
-    read_a(0, 0, arena, a0);
-    // two stages per iteration so that the roles of b0 and b1 are fixed
-    int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
-      step(acc, arena, kt, b0, b1, a0, a1);
-      step(acc, arena, kt + 1, b1, b0, a0, a1);
+    read_b(0, 0, arena, b0);
+    read_a(0, 0, 0, arena, a0);
+    if constexpr (kMxSub == 1) {
+      // two stages per iteration so that the roles of b0 and b1 are fixed
+      int kt = 0;
+      for (; kt + 2 <= nk; kt += 2) {
+        step(acc, arena, kt, 0, b0, b1, a0, a1);
+        step(acc, arena, kt + 1, 0, b1, b0, a0, a1);
+      }
+      if (kt < nk) step(acc, arena, kt, 0, b0, b1, a0, a1);
+    } else {
+      // two K steps per stage: the first reads the second's fragments from
+      // the same buffer, the second waits for the next stage
+      for (int kt = 0; kt < nk; ++kt) {
+        first_half(acc, arena, kt, b0, b1, a0, a1);
+        step(acc, arena, kt, 1, b1, b0, a0, a1);
+      }
     }
-    if (kt < nk) step(acc, arena, kt, b0, b1, a0, a1);
   }
 
-  // Stage kt: its B blocks are in bc and its first A block in a0; on return
-  // (unless it was the last stage) the next stage's are in bn and a0.
-  __device__ __forceinline__ void step(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, BFrags& bc, BFrags& bn,
-                                       AFrag& a0, AFrag& a1) const {
+  // K step 0 of stage kt (two-step stages): its B blocks are in bc and its
+  // first A block in a0; on return step 1's are in bn and a0.
+  __device__ __forceinline__ void first_half(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, BFrags& bc,
+                                             BFrags& bn, AFrag& a0, AFrag& a1) const {
     const int buf = kt % NS;
 #pragma unroll
     for (int i = 0; i + 1 < FM; ++i) {
-      read_a(buf, i + 1, arena, (i & 1) ? a0 : a1);
+      read_a(buf, i + 1, 0, arena, (i & 1) ? a0 : a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_row<0, 1>(acc, i, (i & 1) ? a1 : a0, bc);
+    }
+    read_b(buf, 1, arena, bn);
+    read_a(buf, 0, 1, arena, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_row<0, 1>(acc, FM - 1, a1, bc);
+  }
+
+  // Last K step `sub` of stage kt: its B blocks are in bc and its first A
+  // block in a0; on return (unless it was the last stage) the next stage's
+  // first step's are in bn and a0.
+  __device__ __forceinline__ void step(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, int sub, BFrags& bc,
+                                       BFrags& bn, AFrag& a0, AFrag& a1) const {
+    const int buf = kt % NS;
+#pragma unroll
+    for (int i = 0; i + 1 < FM; ++i) {
+      read_a(buf, i + 1, sub, arena, (i & 1) ? a0 : a1);
       __builtin_amdgcn_sched_barrier(0);
       mma_row<0, 1>(acc, i, (i & 1) ? a1 : a0, bc);
     }
     // the last row block is in a1 (FM even)
     if (kt + 1 < nk) {
       wait_stages<D, NS - 2>(nk - 2 - kt < NS - 2 ? nk - 2 - kt : NS - 2);
-      read_b((kt + 1) % NS, arena, bn);
-      read_a((kt + 1) % NS, 0, arena, a0);
+      read_b((kt + 1) % NS, 0, arena, bn);
+      read_a((kt + 1) % NS, 0, 0, arena, a0);
       mma_issue<0, 4>(acc, a1, bc, kt + NS < nk, kt + NS, arena);
     } else {
       mma_row<0, 1>(acc, FM - 1, a1, bc);
