@@ -113,6 +113,11 @@ struct TileJob {
   using GA = OpGeo<Tr::A_MN, BM, BK, NW>;
   using GB = OpGeo<Tr::B_MN, BROWS, BK, NW>;
   static constexpr int KK = BK / 16;  // 16-K MFMA slices per stage
+  // Epilogue staging per wave: a round of 32 rows (8 KB), or of 16 rows (4 KB)
+  // for the eight-wave row kinds with 64-K stages (two stages of 64 KB leave
+  // 32 KB for the staging).
+  static constexpr int HR = (!Tr::GROUP_K && NW == 8 && BK == 64) ? 16 : 32;
+  static constexpr int EP_BYTES = HR * 256;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static constexpr int A_BYTES = GA::BYTES;
   static constexpr int STAGE = GA::BYTES + GB::BYTES;
@@ -442,7 +447,7 @@ struct TileJob {
   __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[NB][FM][FN], uint8_t* staging,
                                            SavedAB& p0) const {
     SavedAB p1;
-    float* ep = reinterpret_cast<float*>(staging + wid * 8192);
+    float* ep = reinterpret_cast<float*>(staging + wid * EP_BYTES);
     const GroupedGemmArgs& a = *args;
     const int wrow0 = wm * TM, wcol0 = wn * TN;
     if constexpr (Tr::GROUP_K) {
@@ -461,26 +466,28 @@ struct TileJob {
         }
       }
     } else if constexpr (NB == 2) {
-      // UP: gate (W1) and up (W3) accumulators of one 32 x 32 block per round
+      // UP: gate (W1) and up (W3) accumulators of one HR x 32 block per round
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        for (int hf = 0; hf < 32 / HR; ++hf) {
+#pragma unroll
+          for (int r = hf * HR / 2; r < (hf + 1) * HR / 2; ++r) {
+            const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) - hf * HR;
             ep[rr * 32 + (lane & 31)] = acc[0][i][j][r];
-            ep[1024 + rr * 32 + (lane & 31)] = acc[1][i][j][r];
+            ep[HR * 32 + rr * 32 + (lane & 31)] = acc[1][i][j][r];
           }
           __builtin_amdgcn_wave_barrier();
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
+          for (int q = 0; q < HR / 16; ++q) {
             const int seg = q * 64 + lane;
             const int rr = seg >> 2, c8 = (seg & 3) * 8;
-            const int row = c.row0 + wrow0 + i * 32 + rr, col = c.n0 + wcol0 + j * 32 + c8;
+            const int row = c.row0 + wrow0 + i * 32 + hf * HR + rr, col = c.n0 + wcol0 + j * 32 + c8;
             if (row < c.row_end && col < G.N) {
               const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 32 + c8]);
-              const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[1024 + rr * 32 + c8]);
+              const f32x4_t* pu = reinterpret_cast<const f32x4_t*>(&ep[HR * 32 + rr * 32 + c8]);
               const f32x4_t v0 = pv[0], v1 = pv[1], u0 = pu[0], u1 = pu[1];
               const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
               const float u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
@@ -504,11 +511,14 @@ struct TileJob {
           __builtin_amdgcn_wave_barrier();
         }
     } else {
-      // one 32 x 64 block per round
+      // one HR x 64 block per round (DH: HR = 32)
+      static_assert(KIND != KIND_DH || HR == 32, "DH prefetches whole 32-row rounds");
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int jp = 0; jp < FN / 2; ++jp) {
+        for (int jp = 0; jp < FN / 2; ++jp)
+#pragma unroll
+        for (int hf = 0; hf < 32 / HR; ++hf) {
           const int t = i * (FN / 2) + jp;  // round
           SavedAB& cur = (t & 1) ? p1 : p0;
           if constexpr (KIND == KIND_DH) {
@@ -517,20 +527,20 @@ struct TileJob {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            for (int r = hf * HR / 2; r < (hf + 1) * HR / 2; ++r) {
+              const int rr = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) - hf * HR;
               ep[rr * 64 + jj * 32 + (lane & 31)] = acc[0][i][2 * jp + jj][r];
             }
           __builtin_amdgcn_wave_barrier();
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < HR / 8; ++q) {
             const int seg = q * 64 + lane;
             const int rr = seg >> 3, c8 = (seg & 7) * 8;
             const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(&ep[rr * 64 + c8]);
             const f32x4_t v0 = pv[0], v1 = pv[1];
             const int col = c.n0 + wcol0 + jp * 64 + c8;
             {
-              const int row = c.row0 + wrow0 + i * 32 + rr;
+              const int row = c.row0 + wrow0 + i * 32 + hf * HR + rr;
               if (row < c.row_end && col < G.N) {
                 const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 const int64_t o = (int64_t)row * G.N + col;
@@ -572,7 +582,7 @@ struct TileJob {
 };
 
 // Persistent grouped GEMM.  LDS: the NS stage buffers, then either the bf16
-// epilogue staging area (row kinds; 8 KB per wave) or the mailbox through
+// epilogue staging area (row kinds; 4 or 8 KB per wave) or the mailbox through
 // which wave 0 hands the tile taken from the queue to the workgroup
 // (weight-gradient kinds).  The tile-prefix table is searched in global
 // memory through the scalar cache.
@@ -581,7 +591,7 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_bf16_kernel(GroupedGemmA
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only builtins; the host pass needs only the launch stub
   using Tr = Traits<KIND>;
   using Job = TileJob<KIND, BM, BN, NS, BK, NW, WMW>;
-  constexpr int kExtra = Tr::GROUP_K ? 256 : NW * 8192;
+  constexpr int kExtra = Tr::GROUP_K ? 256 : NW * Job::EP_BYTES;
   static_assert(NS * Job::STAGE + kExtra <= 163840, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t arena[NS * Job::STAGE + kExtra];
   uint8_t* const staging = arena + NS * Job::STAGE;
@@ -769,9 +779,15 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
 // 128-byte pieces, which the copy path serves about twice as fast as 64-byte
 // ones (same-box A/B at T 8192, d 4096, E 128, k 8, F 1536: DH 1.32 -> 1.23
 // ms, DX 2.19 -> 2.01 ms).
+// UP and DOWN (eight waves) take two 64-K stages too, with 16-row epilogue
+// rounds (4 KB of staging per wave): same-box A/B UP 1.94 -> 1.86 ms, DOWN
+// 1.03 -> 0.99 ms against three 32-K stages.
+#ifndef MOK_UPDN_BK64
+#define MOK_UPDN_BK64 1
+#endif
 #ifndef MOK_BK_UP
-#define MOK_BK_UP 32
-#define MOK_BK_DOWN 32
+#define MOK_BK_UP (MOK_UPDN_BK64 ? 64 : 32)
+#define MOK_BK_DOWN (MOK_UPDN_BK64 ? 64 : 32)
 #define MOK_NS_DH 2
 #define MOK_BK_DH 64
 #define MOK_NS_DX 2
@@ -805,7 +821,7 @@ constexpr int kWF = MOK_BF16_WAVES_FWD;
 #define MOK_BF16_WM_DW 2
 #endif
 constexpr int kWDW = MOK_BF16_WAVES_DW, kWmDW = MOK_BF16_WM_DW;
-constexpr int kNsFwd = kWF == 8 ? 3 : 4;
+constexpr int kNsFwd = MOK_UPDN_BK64 ? 2 : (kWF == 8 ? 3 : 4);
 
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
   switch (kind) {
