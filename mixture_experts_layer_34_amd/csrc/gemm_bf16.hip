@@ -807,7 +807,7 @@ static hipError_t run_bf16(const GroupedGemmArgs& g, hipStream_t s) {
 // staging then takes 64 KB of the LDS): 2.05 -> 1.90 ms and 1.14 -> 1.05 ms
 // at T 8192, d 4096, E 128, k 8, F 1536.  DH and DX measured slower with
 // eight waves in either layout (DH 1.30 -> 1.44-1.51 ms, DX 2.19 -> 2.34-
-// 2.40) and keep four.
+// 2.40) with 32-K stages.
 #ifndef MOK_BF16_WAVES_FWD
 #define MOK_BF16_WAVES_FWD 8
 #endif
@@ -821,6 +821,14 @@ constexpr int kWF = MOK_BF16_WAVES_FWD;
 #define MOK_BF16_WM_DW 2
 #endif
 constexpr int kWDW = MOK_BF16_WAVES_DW, kWmDW = MOK_BF16_WM_DW;
+// DX with 64-K stages runs eight waves, 2 x 4 (its transposing B reads then
+// serve two waves per fragment; 16-row epilogue rounds): same-box A/B 2.00 ->
+// 1.82 ms (4 x 2: 1.84 ms).  DH keeps four (its epilogue prefetches whole
+// 32-row rounds of the saved A and B).
+#ifndef MOK_DX_WAVES
+#define MOK_DX_WAVES 8
+#define MOK_DX_WM 2
+#endif
 constexpr int kNsFwd = MOK_UPDN_BK64 ? 2 : (kWF == 8 ? 3 : 4);
 
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
@@ -828,7 +836,7 @@ hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_UP:   return run_bf16<KIND_UP, 256, 128, kNsFwd, MOK_BK_UP, kWF, kWF / 2>(g, s);
     case KIND_DOWN: return run_bf16<KIND_DOWN, 256, 256, kNsFwd, MOK_BK_DOWN, kWF, kWF / 2>(g, s);
     case KIND_DH:   return run_bf16<KIND_DH, 256, 256, MOK_NS_DH, MOK_BK_DH, 4, 2>(g, s);
-    case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX, 4, 2>(g, s);
+    case KIND_DX:   return run_bf16<KIND_DX, 256, 256, MOK_NS_DX, MOK_BK_DX, MOK_DX_WAVES, MOK_DX_WM>(g, s);
     case KIND_DW2:  return run_bf16<KIND_DW2, 256, 256, MOK_NS_DW2, MOK_BK_DW2, kWDW, kWmDW>(g, s);
     case KIND_DW13: return run_bf16<KIND_DW13, 256, 256, MOK_NS_DW, MOK_BK_DW, 4, 2>(g, s);
   }
