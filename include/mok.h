@@ -159,6 +159,52 @@ mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k,
 /* Offsets of the arrays inside `saved` (host-only computation). */
 mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out);
 
+/* Byte offsets inside the `workspace` buffer (from its base, each 256-byte
+ * aligned; host-only computation).  Its contents are scratch of one call,
+ * except for the status word, which the caller may read after the call.
+ *
+ *   status    two int32 words.  Every forward and backward call clears them
+ *             when it starts (its first kernel, on the call's stream).  A
+ *             device-side check that fails stores MOK_ERR_DEVICE in word 0
+ *             and ORs its bit into word 1; the call's outputs are then not
+ *             meaningful.  The checks:
+ *               MOK_CHECK_LOGITS  a router logit row holds NaN or +-Inf (the
+ *                                 chosen indices still lie in [0, E): a NaN
+ *                                 ranks below every number);
+ *               MOK_CHECK_INDEX   an entry of the row maps or of topk_idx that
+ *                                 a backward call reads from `saved` lies
+ *                                 outside its range (the slot is then treated
+ *                                 as remote, so no access leaves a buffer);
+ *               MOK_CHECK_STALL   a bounded wait of the ring pipeline gave up
+ *                                 (the persistent kernel then drains without
+ *                                 finishing its work).
+ *             The library never synchronises: read the words (8 bytes at this
+ *             offset) once the stream has passed the call, e.g. with a device
+ *             to host copy at the caller's own synchronisation point.
+ *   xp        the dispatch buffer, or the ring of minibatch slots, then (MXFP8
+ *             backward) the dY codes [P_max, d];
+ *   xp_scale  MXFP8: its E8M0 scales in pair planes [d/64, xp_rows, 2];
+ *   xp_rows   rows held by xp (P_max = T*k, or the ring's rows);
+ *   dy, dab, dxp  backward row buffers dY [P_max, d], [dA | dB] [P_max, 2F],
+ *             dX_perm [P_max, d] (bf16; absent from an MXFP8 forward-only
+ *             configuration);
+ *   total     workspace_bytes. */
+#define MOK_CHECK_LOGITS 0x1
+#define MOK_CHECK_INDEX 0x2
+#define MOK_CHECK_STALL 0x4
+typedef struct mok_workspace_layout {
+  size_t status;
+  size_t xp;
+  size_t xp_scale;
+  int64_t xp_rows;
+  size_t dy;
+  size_t dab;
+  size_t dxp;
+  size_t total;
+} mok_workspace_layout;
+
+mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_workspace_layout* out);
+
 /*
  * Forward pass of the MoE layer ([kucoin §01-§03]: router, layout, dispatch,
  * grouped expert GEMMs, combine and the final weighted sum).

@@ -1,0 +1,36 @@
+/*
+ * mok_diag.h — diagnostics of the matrix cores the MoE layer runs on
+ * (libmok_diag.so, separate from the layer's libmok.so).  Test support only.
+ */
+#ifndef MOK_DIAG_H_
+#define MOK_DIAG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * One block of the gfx950 scaled matrix instruction the MXFP8 GEMMs use
+ * (32 x 32 outputs, K = 64, E4M3 operands, one E8M0 scale per 32 K values of
+ * each row; the MXFP8 format of kucoin.com, "Cursor's MoK réalise une
+ * amélioration des performances de 2,37x sur NVIDIA GB300 NVL72", section 02):
+ *   C_out[i][j] = C_in[i][j] + sum_{k < 64} A[i][k] 2^(sa[i][k/32] - 127)
+ *                                          * B[j][k] 2^(sb[j][k/32] - 127)
+ * as the hardware computes it, so that a caller can compare it with the
+ * exact sum.
+ *   a, b        device, uint8 [32][64] E4M3 codes (rows i of A, rows j of B)
+ *   sa, sb      device, uint8 [32][2] E8M0 scale bytes
+ *   c_in, c_out device, float [32][32], row-major
+ * One wave on `stream` (a hipStream_t as void*); returns 0, 1 for a null
+ * pointer, 4 for a failed launch.
+ */
+int32_t mok_diag_mfma_scale_block(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                  const float* c_in, float* c_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_DIAG_H_ */

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmok.so")
+DIAG = os.path.join(PKG, "libmok_diag.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["route_sort.hip", "permute_combine.hip", "gemm_bf16.hip", "gemm_f32.hip", "gemm_mxfp8.hip", "router_gemm.hip",
            "mok_abi.cpp"]
@@ -58,6 +59,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("profiling driver build failed:\n" + r.stderr)
     os.replace(drv + ".tmp", drv)
+    # matrix-core diagnostics (test support), a library of their own
+    dobj = _compile("diag_mfma.hip")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", DIAG + ".tmp", dobj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("diagnostics link failed:\n" + r.stderr)
+    os.replace(DIAG + ".tmp", DIAG)
     if verbose:
         print("built", OUT, "and", drv)
     return OUT

@@ -56,6 +56,9 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if (c.ring_bytes > 0 && c.minibatch_rows == 0) return MOK_ERR_INVALID_ARG;  // a ring needs a minibatch size
   if (c.minibatch_rows > 0) {
     if (c.precision != MOK_PREC_BF16) return MOK_ERR_UNSUPPORTED;
+    // the ring's row copies and the backward's gathered x rows address x
+    // through 32-bit buffer offsets
+    if ((int64_t)c.T * c.d * 2 >= (int64_t(1) << 31)) return MOK_ERR_INVALID_ARG;
     // two slots at least: minibatch m+1 is copied while m is read
     if (c.ring_bytes < 2 * (int64_t)c.minibatch_rows * c.d * 2) return MOK_ERR_WORKSPACE;
   }
@@ -216,6 +219,23 @@ mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k, size_t*
   return MOK_OK;
 }
 
+mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_workspace_layout* out) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!out) return MOK_ERR_INVALID_ARG;
+  WorkspaceLayout w;
+  workspace_layout(*cfg, k, &w);
+  out->status = w.status;
+  out->xp = w.xp;
+  out->xp_scale = w.xp_scale;
+  out->xp_rows = w.xp_rows;
+  out->dy = w.dy;
+  out->dab = w.dab;
+  out->dxp = w.dxp;
+  out->total = w.total;
+  return MOK_OK;
+}
+
 mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out) {
   mok_status st = validate_config(cfg, k);
   if (st != MOK_OK) return st;
@@ -260,8 +280,11 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   int32_t* s_rop = at<int32_t>(saved, sl.row_of_pair);
   int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
 
+  int32_t* status = at<int32_t>(workspace, wl.status);
+  const int64_t P_max = (int64_t)T * k;
+  MOK_HIP(launch_status_reset(status, s));
   MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx,
-                                                 s_gate, s_lse, s));
+                                                 s_gate, s_lse, status, s));
   MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
                                at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
                                s_order, s_rop, s_por, s));
@@ -277,7 +300,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
   if (mx) {
     uint8_t* xq = at<uint8_t>(workspace, wl.xp);
     uint8_t* xs = at<uint8_t>(workspace, wl.xp_scale);
-    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, wl.xp_rows, s));
+    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, wl.xp_rows, status, s));
     const size_t w13_scales = (size_t)E_loc * F * (d / 32);
     g.A = xq;
     g.a_scale = xs;
@@ -361,7 +384,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
       g.k_top = k;
       g.gather_src_rows = T;
     } else {
-      MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+      MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, wl.xp_rows, status, s));
       g.A = xp;
     }
     g.B0 = W1;
@@ -380,7 +403,8 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     g2.gather_rows = nullptr;
     MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
   }
-  MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, all_local(c), out, s));
+  MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, all_local(c), out,
+                                              P_max, status, s));
   return MOK_OK;
 }
 
@@ -420,10 +444,14 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   void* dab = at<void>(workspace, wl.dab);
   void* dxp = at<void>(workspace, wl.dxp);
   void* xp = at<void>(workspace, wl.xp);
+  int32_t* status = at<int32_t>(workspace, wl.status);
+  const int64_t P_max = (int64_t)T * k;
+  MOK_HIP(launch_status_reset(status, s));
 
   // reverse-combine with the router backward
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits, s_lse, T, k, E, d,
-                               gating_of(c), bf16, dgate, drouter_logits, dy, queue, 16, nullptr, nullptr, 0, s));
+                               gating_of(c), bf16, dgate, drouter_logits, dy, queue, 16, nullptr, nullptr, 0,
+                               P_max, status, s));
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;
@@ -447,7 +475,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   gx.B1 = W3;
   gx.out0 = dxp;
   MOK_STAGE(MOK_STAGE_GEMM_DX, run_gemm(c.precision, KIND_DX, gx, s));
-  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, all_local(c), dx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, bf16, all_local(c), dx, P_max, status, s));
   // weight gradients
   GroupedGemmArgs gw = g;
   gw.A = dy;
@@ -468,7 +496,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
   } else {
     // X rows again, expert-sorted (the transposed operand of dW1/dW3 wants
     // them contiguous: a gather inside its loads chains two loads)
-    MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, s));
+    MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, bf16, xp, wl.xp_rows, status, s));
     g13.B0 = xp;
   }
   g13.out0 = dW1;
@@ -544,11 +572,14 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
   uint8_t* dabq = at<uint8_t>(workspace, wl.hq);         // [P_max, 2F] codes
   uint8_t* dabs = at<uint8_t>(workspace, wl.hq_scale);   // [2F/64, P_max, 2]
   const int64_t n = (int64_t)E_loc * F * d;
+  int32_t* status = at<int32_t>(workspace, wl.status);
+  const int64_t P_max = (int64_t)T * k;
+  MOK_HIP(launch_status_reset(status, s));
 
   // reverse-combine with the router backward; dY also as MXFP8 along d
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits,
                                                       s_lse, T, k, E, d, gating_of(c), 1, dgate, drouter_logits, dy,
-                                                      queue, 16, dyq, dys, wl.xp_rows, s));
+                                                      queue, 16, dyq, dys, wl.xp_rows, P_max, status, s));
   GroupedGemmArgs g{};
   g.offsets = at<int32_t>(saved, sl.offsets);
   g.tile_prefix = at<int32_t>(saved, tp_off);
@@ -578,7 +609,7 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
   gx.b_scale0 = wt_e8m0 + n / 32;
   gx.out0 = dxp;
   MOK_STAGE(MOK_STAGE_GEMM_DX, gemm_mxfp8(KIND_DX, gx, s));
-  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, all_local(c), dx, s));
+  MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, all_local(c), dx, P_max, status, s));
   // weight gradients: bf16 products of the unquantised operands
   GroupedGemmArgs gw = g;
   gw.A = dy;
@@ -588,7 +619,7 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
   MOK_STAGE(MOK_STAGE_GEMM_DW2, gemm_bf16(KIND_DW2, gw, s));
   // x rows again, expert-sorted, into dX_perm's buffer (read by the reduction
   // above, earlier on the stream)
-  MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, 1, dxp, s));
+  MOK_STAGE(MOK_STAGE_REGATHER, launch_dispatch_gather(x, s_rop, T, k, d, 1, dxp, P_max, status, s));
   GroupedGemmArgs g13 = g;
   g13.A = dab;
   g13.B0 = dxp;

@@ -45,6 +45,30 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// ------------------------------------------------------------ status word
+// Device-side checks report into the status word at the start of the
+// workspace: word 0 becomes MOK_ERR_DEVICE (5) and word 1 gathers the bits of
+// the checks that failed.  Each layer call clears both words first.
+constexpr int32_t kStatusDevice = 5;                   // MOK_ERR_DEVICE
+constexpr int32_t kCheckLogits = 1;                    // a router logit row holds NaN or +-Inf
+constexpr int32_t kCheckIndex = 2;                     // a row or expert index outside its range
+constexpr int32_t kCheckStall = 4;                     // a bounded wait of the ring scheduler gave up
+__device__ __forceinline__ void report(int32_t* status, int32_t bit) {
+  if (status) {
+    __hip_atomic_store(status, kStatusDevice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(status + 1, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+// A row-map entry: -1 (remote slot) or a row in [0, rows).  Anything else is
+// reported and read as -1, so no access ever leaves the row buffers.
+__device__ __forceinline__ int32_t checked_row(int32_t r, int64_t rows, int32_t* status) {
+  if (r < -1 || (int64_t)r >= rows) {
+    report(status, kCheckIndex);
+    return -1;
+  }
+  return r;
+}
+
 // SiLU and its derivative pieces in fp32.
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 

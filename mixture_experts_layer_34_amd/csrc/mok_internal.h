@@ -38,9 +38,14 @@ struct WorkspaceLayout {
 // renormalised over the chosen experts.
 constexpr int kGateSigmoid = 1, kGateRenorm = 2;
 
+// Status word (two int32 at the start of the workspace): cleared by
+// launch_status_reset at the start of a call; kernels with device-side checks
+// set it (mok_device.h report()).
+hipError_t launch_status_reset(int32_t* status, hipStream_t s);
+
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int gating, int32_t* idx_out,
                               float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
-                              hipStream_t s);
+                              int32_t* status, hipStream_t s);
 
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
                                 int nchunks, int32_t* chunk_counts, int32_t* chunk_base,
@@ -48,12 +53,14 @@ hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb,
                                 int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
                                 int32_t* pair_of_row, hipStream_t s);
 
-// X_perm[row(t,j)] = x[t] (act = bf16 when bf16 != 0, else fp32).
+// X_perm[row(t,j)] = x[t] (act = bf16 when bf16 != 0, else fp32).  Row-map
+// entries outside [-1, xp_rows) are reported on `status` and skipped.
 hipError_t launch_dispatch_gather(const void* x, const int32_t* row_of_pair, int T, int k, int d,
-                                  int bf16, void* xp, hipStream_t s);
+                                  int bf16, void* xp, int64_t xp_rows, int32_t* status, hipStream_t s);
 // Same, quantising each row to MXFP8 (E4M3 + E8M0 per 32 along d).
 hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pair, int T, int k,
-                                        int d, uint8_t* xq, uint8_t* xs, int64_t xs_rows, hipStream_t s);
+                                        int d, uint8_t* xq, uint8_t* xs, int64_t xs_rows, int32_t* status,
+                                        hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q,
                                  uint8_t* sc, hipStream_t s);
 // MXFP8 of the transpose of nmat [R, C] bf16 matrices along R (R, C multiples
@@ -64,8 +71,10 @@ hipError_t launch_quantize_mxfp8_t(const void* src, int nmat, int R, int C, uint
 
 // out[t] = sum_j w[t,j] * rows[row(t,j)] (w = gate, or 1 when gate == nullptr).
 // all_local: the call owns every expert (else the kernel for mostly remote slots).
+// Row-map entries outside [-1, nrows) are reported on `status` and skipped.
 hipError_t launch_combine(const void* rows, const float* gate, const int32_t* row_of_pair, int T,
-                          int k, int d, int bf16, int all_local, void* out, hipStream_t s);
+                          int k, int d, int bf16, int all_local, void* out, int64_t nrows, int32_t* status,
+                          hipStream_t s);
 
 // Reverse-combine and router backward: dgate, dlogits and dY rows.
 hipError_t launch_backward_gate(const void* dout, const void* Y, const float* gate,
@@ -73,7 +82,7 @@ hipError_t launch_backward_gate(const void* dout, const void* Y, const float* ga
                                 const float* logits, const float* lse, int T, int k, int E, int d,
                                 int gating, int bf16, float* dgate, float* dlogits, void* dy,
                                 int32_t* queue_zero, int nqueue, uint8_t* dyq, uint8_t* dys,
-                                int64_t dys_rows, hipStream_t s);
+                                int64_t dys_rows, int64_t nrows, int32_t* status, hipStream_t s);
 
 // Grouped GEMMs of the expert FFN.  `offsets` is the global [E+1] array,
 // experts [eb, eb + E_loc) are local.  tile_prefix is the [kNumTileBM, E_loc+1]

@@ -58,7 +58,8 @@ constexpr int kSlotGroup = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restrict__ x,
                                                               const int32_t* __restrict__ rop, int ntok,
-                                                              int k, int d, T* __restrict__ xp) {
+                                                              int k, int d, T* __restrict__ xp, int64_t xp_rows,
+                                                              int32_t* __restrict__ status) {
   const int nv = d * (int)sizeof(T) / 16;
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
     const int32_t* tr = rop + (int64_t)t * k;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restric
 #pragma unroll
       for (int i = 0; i < kSlotGroup; ++i) {
         const int jc = j0 + i < k ? j0 + i : k - 1;
-        const int32_t rv = tr[jc];
+        const int32_t rv = checked_row(tr[jc], xp_rows, status);
         rv_[i] = (j0 + i < k) ? rv : -1;
         rs[i] = row_rsrc(xp, rv_[i], d * (int)sizeof(T));
       }
@@ -84,15 +85,15 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(const T* __restric
 }
 
 hipError_t launch_dispatch_gather(const void* x, const int32_t* row_of_pair, int T, int k, int d, int bf16,
-                                  void* xp, hipStream_t s) {
+                                  void* xp, int64_t xp_rows, int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = T < 16384 ? T : 16384;
   if (bf16)
     hipLaunchKernelGGL(dispatch_gather_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
-                       (const bf16_t*)x, row_of_pair, T, k, d, (bf16_t*)xp);
+                       (const bf16_t*)x, row_of_pair, T, k, d, (bf16_t*)xp, xp_rows, status);
   else
     hipLaunchKernelGGL(dispatch_gather_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)x,
-                       row_of_pair, T, k, d, (float*)xp);
+                       row_of_pair, T, k, d, (float*)xp, xp_rows, status);
   return hipGetLastError();
 }
 
@@ -130,7 +131,8 @@ __device__ __forceinline__ void mx_quant8(const uint4 v, uint2& codes, uint8_t& 
 __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t* __restrict__ x,
                                                                     const int32_t* __restrict__ rop, int ntok,
                                                                     int k, int d, uint8_t* __restrict__ xq,
-                                                                    uint8_t* __restrict__ xs, int64_t xs_rows) {
+                                                                    uint8_t* __restrict__ xs, int64_t xs_rows,
+                                                                    int32_t* __restrict__ status) {
   const int nv = d / 16;
   const int lane = lane_id();
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t
 #pragma unroll
       for (int i = 0; i < kSlotGroup; ++i) {
         const int jc = j0 + i < k ? j0 + i : k - 1;
-        const int32_t rv = tr[jc];
+        const int32_t rv = checked_row(tr[jc], xs_rows, status);
         r[i] = (j0 + i < k) ? rv : -1;
         rs[i] = row_rsrc(xq, r[i], d);
       }
@@ -182,11 +184,11 @@ __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t
 }
 
 hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pair, int T, int k, int d,
-                                        uint8_t* xq, uint8_t* xs, int64_t xs_rows, hipStream_t s) {
+                                        uint8_t* xq, uint8_t* xs, int64_t xs_rows, int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = T < 16384 ? T : 16384;
   hipLaunchKernelGGL(dispatch_gather_mxfp8_kernel, dim3(blocks), dim3(256), 0, s, (const bf16_t*)x,
-                     row_of_pair, T, k, d, xq, xs, xs_rows);
+                     row_of_pair, T, k, d, xq, xs, xs_rows, status);
   return hipGetLastError();
 }
 
@@ -354,7 +356,8 @@ template <> struct Vec8<float> {
 template <typename T, bool GATED>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows, const float* __restrict__ gate,
                                                       const int32_t* __restrict__ rop, int ntok, int k, int d,
-                                                      T* __restrict__ out) {
+                                                      T* __restrict__ out, int64_t nrows,
+                                                      int32_t* __restrict__ status) {
   const int nv = d / 8;
   for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
     const int32_t* tr = rop + (int64_t)t * k;
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows
 #pragma unroll
     for (int i = 0; i < kSlotGroup; ++i) {
       const int jc = i < k ? i : k - 1;
-      const int32_t rv = tr[jc];
+      const int32_t rv = checked_row(tr[jc], nrows, status);
       const float gv = GATED ? tg[jc] : 1.0f;
       const int32_t r = (i < k) ? rv : -1;
       w0[i] = r < 0 ? 0.f : gv;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows
           rsrc_t rs = rs0[i];
           w[i] = w0[i];
           if (j0 > 0) {
-            const int32_t r = (j0 + i < k) ? tr[j0 + i] : -1;
+            const int32_t r = (j0 + i < k) ? checked_row(tr[j0 + i], nrows, status) : -1;
             w[i] = r < 0 ? 0.f : (GATED ? tg[j0 + i] : 1.0f);
             rs = row_rsrc(rows, r, d * (int)sizeof(T));
           }
@@ -411,7 +414,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ rows
 template <typename T>
 __global__ __launch_bounds__(256) void combine_compact_kernel(const T* __restrict__ rows, const float* __restrict__ gate,
                                                       const int32_t* __restrict__ rop, int ntok, int k, int d,
-                                                      T* __restrict__ out) {
+                                                      T* __restrict__ out, int64_t nrows,
+                                                      int32_t* __restrict__ status) {
   __shared__ int32_t rr[kMaxK];
   __shared__ float ww[kMaxK];
   __shared__ int nloc;
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(const T* __restric
     if (threadIdx.x == 0) {
       int n = 0;
       for (int j = 0; j < k; ++j) {
-        int r = rop[(int64_t)t * k + j];
+        const int r = checked_row(rop[(int64_t)t * k + j], nrows, status);
         if (r >= 0) {
           rr[n] = r;
           ww[n] = gate ? gate[(int64_t)t * k + j] : 1.0f;
@@ -447,21 +451,21 @@ __global__ __launch_bounds__(256) void combine_compact_kernel(const T* __restric
 }
 
 hipError_t launch_combine(const void* rows, const float* gate, const int32_t* row_of_pair, int T, int k, int d,
-                          int bf16, int all_local, void* out, hipStream_t s) {
+                          int bf16, int all_local, void* out, int64_t nrows, int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = T < 16384 ? T : 16384;
   if (!all_local) {
     if (bf16)
       hipLaunchKernelGGL(combine_compact_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)rows, gate,
-                         row_of_pair, T, k, d, (bf16_t*)out);
+                         row_of_pair, T, k, d, (bf16_t*)out, nrows, status);
     else
       hipLaunchKernelGGL(combine_compact_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)rows, gate,
-                         row_of_pair, T, k, d, (float*)out);
+                         row_of_pair, T, k, d, (float*)out, nrows, status);
     return hipGetLastError();
   }
 #define MOK_COMBINE(TT, G)                                                                                 \
   hipLaunchKernelGGL((combine_kernel<TT, G>), dim3(blocks), dim3(256), 0, s, (const TT*)rows, gate, row_of_pair, T, \
-                     k, d, (TT*)out)
+                     k, d, (TT*)out, nrows, status)
   if (bf16) {
     if (gate) MOK_COMBINE(bf16_t, true); else MOK_COMBINE(bf16_t, false);
   } else {
@@ -498,7 +502,8 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
                                                             float* __restrict__ dlogits, T* __restrict__ dy,
                                                             int32_t* __restrict__ queue_zero, int nqueue,
                                                             uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys,
-                                                            int64_t dys_rows) {
+                                                            int64_t dys_rows, int64_t nrows,
+                                                            int32_t* __restrict__ status) {
   __shared__ float red[4][kSlotGroup];
   // the tile counters of the weight-gradient GEMMs that follow on the stream
   if (blockIdx.x == 0 && (int)threadIdx.x < nqueue) queue_zero[threadIdx.x] = 0;
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
 #pragma unroll
       for (int i = 0; i < kSlotGroup; ++i) {
         const int jc = j0 + i < k ? j0 + i : k - 1;  // clamped: all loads issued at once
-        const int32_t rv = tr[jc];
+        const int32_t rv = checked_row(tr[jc], nrows, status);
         const float gv = tg[jc];
         r[i] = (j0 + i < k) ? rv : -1;
         g[i] = (j0 + i < k) ? gv : 0.f;
@@ -584,9 +589,11 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
       __syncthreads();
       if ((int)threadIdx.x < kSlotGroup && j0 + (int)threadIdx.x < k) {
         const int i = threadIdx.x, j = j0 + i;
-        const int rj = tr[j];
+        const int rj = checked_row(tr[j], nrows, status);
         dg[j] = (rj >= 0) ? ((red[0][i] + red[1][i]) + (red[2][i] + red[3][i])) : 0.f;
-        sel[j] = idx[(int64_t)t * k + j];
+        const int32_t ej = idx[(int64_t)t * k + j];
+        if (ej < 0 || ej >= E) report(status, kCheckIndex);  // only compared below: no access through it
+        sel[j] = ej;
       }
       __syncthreads();
     }
@@ -625,12 +632,12 @@ hipError_t launch_backward_gate(const void* dout, const void* Y, const float* ga
                                 const int32_t* row_of_pair, const float* logits, const float* lse, int T, int k,
                                 int E, int d, int gating, int bf16, float* dgate, float* dlogits, void* dy,
                                 int32_t* queue_zero, int nqueue, uint8_t* dyq, uint8_t* dys, int64_t dys_rows,
-                                hipStream_t s) {
+                                int64_t nrows, int32_t* status, hipStream_t s) {
   int blocks = T < 16384 ? (T > 0 ? T : 1) : 16384;  // at least one block: it zeroes the counters
 #define MOK_BWD_GATE(TT, GV, MXV)                                                                              \
   hipLaunchKernelGGL((backward_gate_kernel<TT, GV, MXV>), dim3(blocks), dim3(256), 0, s, (const TT*)dout,      \
                      (const TT*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits, (TT*)dy,    \
-                     queue_zero, nqueue, dyq, dys, dys_rows)
+                     queue_zero, nqueue, dyq, dys, dys_rows, nrows, status)
 #define MOK_BWD_GATE_T(TT, MXV)                                         \
   switch (gating & (kGateSigmoid | kGateRenorm)) {                      \
     case 0: MOK_BWD_GATE(TT, 0, MXV); break;                            \

@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           float* __restrict__ gate_out,
                                                           int32_t* __restrict__ idx_saved,
                                                           float* __restrict__ gate_saved,
-                                                          float* __restrict__ lse_out) {
+                                                          float* __restrict__ lse_out,
+                                                          int32_t* __restrict__ status) {
   __shared__ float renorm_buf[RENORM ? 4 * kRouterMaxK : 1];
   const int lane = lane_id();
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -37,12 +38,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     const float* row = logits + (int64_t)t * E;
     float v[EPL];
     float m = -INFINITY;
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       int e = lane + 64 * i;
       v[i] = e < E ? row[e] : -INFINITY;
+      // logits must be finite: a NaN or an infinity is reported, and a NaN
+      // is ranked as -inf so that the k chosen indices stay in [0, E)
+      if (e < E && !isfinite(v[i])) {
+        bad = true;
+        if (v[i] != v[i]) v[i] = -INFINITY;
+      }
       m = fmaxf(m, v[i]);
     }
+    if (__ballot(bad) != 0 && lane == 0) report(status, kCheckLogits);
     m = wave_max(m);
     float s = 0.f;
 #pragma unroll
@@ -105,10 +114,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 template <bool SIGM, bool RENORM>
 static void launch_router_variant(dim3 g, dim3 b, hipStream_t s, const float* logits, int T, int E, int k,
                                   int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved,
-                                  float* lse) {
+                                  float* lse, int32_t* status) {
 #define MOK_ROUTER(EPLV)                                                                                   \
   hipLaunchKernelGGL((router_topk_kernel<EPLV, SIGM, RENORM>), g, b, 0, s, logits, T, E, k, idx_out, gate_out, \
-                     idx_saved, gate_saved, lse)
+                     idx_saved, gate_saved, lse, status)
   if (E <= 64) MOK_ROUTER(1);
   else if (E <= 128) MOK_ROUTER(2);
   else if (E <= 256) MOK_ROUTER(4);
@@ -119,17 +128,28 @@ static void launch_router_variant(dim3 g, dim3 b, hipStream_t s, const float* lo
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int gating, int32_t* idx_out,
                               float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
-                              hipStream_t s) {
+                              int32_t* status, hipStream_t s) {
   if (T == 0) return hipSuccess;
   int blocks = (T + 3) / 4;
   if (blocks > 8192) blocks = 8192;
   const dim3 g(blocks), b(256);
   switch (gating & (kGateSigmoid | kGateRenorm)) {
-    case 0: launch_router_variant<false, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
-    case kGateSigmoid: launch_router_variant<true, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
-    case kGateRenorm: launch_router_variant<false, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
-    default: launch_router_variant<true, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse); break;
+    case 0: launch_router_variant<false, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse, status); break;
+    case kGateSigmoid: launch_router_variant<true, false>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse, status); break;
+    case kGateRenorm: launch_router_variant<false, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse, status); break;
+    default: launch_router_variant<true, true>(g, b, s, logits, T, E, k, idx_out, gate_out, idx_saved, gate_saved, lse, status); break;
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ status word
+// Clears the status word (MOK_OK, no failed checks) at the start of a call.
+__global__ void status_reset_kernel(int32_t* status) {
+  if (threadIdx.x < 2) status[threadIdx.x] = 0;
+}
+
+hipError_t launch_status_reset(int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(status_reset_kernel, dim3(1), dim3(64), 0, s, status);
   return hipGetLastError();
 }
 

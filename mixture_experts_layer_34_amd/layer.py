@@ -60,6 +60,7 @@ class MoeBuffers:
         self.cfg = s.config()
         ws, sv = mok.mok_moe_workspace_query(self.cfg, s.k)
         self.layout = mok.mok_moe_saved_layout(self.cfg, s.k)
+        self.ws_layout = mok.mok_moe_workspace_layout(self.cfg, s.k)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
         self.saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=device)
         self.out = torch.empty((s.T, s.d), dtype=s.act_dtype, device=device)
@@ -80,6 +81,23 @@ class MoeBuffers:
             dgate=torch.empty((s.T, s.k), dtype=torch.float32, device=dev),
             dlogits=torch.empty((s.T, s.E), dtype=torch.float32, device=dev))
         return self.grads
+
+    def device_status(self):
+        """(status, failed-check bits) of the last call on this workspace: the
+        two int32 words the library's device-side checks write (synchronises
+        with the device, which the library itself never does)."""
+        off = self.ws_layout["status"]
+        w = self.workspace[off:off + 8].view(torch.int32).cpu()
+        return int(w[0]), int(w[1])
+
+    def workspace_view(self, name: str, dtype, shape):
+        """A view of one array inside the workspace (see mok_workspace_layout)."""
+        off = self.ws_layout[name]
+        n = 1
+        for v in shape:
+            n *= v
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype).view(*shape)
 
     def saved_view(self, name: str, dtype, shape):
         """A view of one array inside the saved buffer (see mok_saved_layout)."""

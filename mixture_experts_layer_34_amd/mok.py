@@ -38,6 +38,15 @@ class mok_saved_layout(ctypes.Structure):
                  "total")]
 
 
+class mok_workspace_layout(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_size_t), ("xp", ctypes.c_size_t), ("xp_scale", ctypes.c_size_t),
+                ("xp_rows", ctypes.c_int64), ("dy", ctypes.c_size_t), ("dab", ctypes.c_size_t),
+                ("dxp", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+MOK_CHECK_LOGITS, MOK_CHECK_INDEX, MOK_CHECK_STALL = 0x1, 0x2, 0x4
+
+
 class MokError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -64,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.mok_moe_saved_layout.restype = ctypes.c_int
         L.mok_moe_saved_layout.argtypes = [ctypes.POINTER(mok_moe_config), ctypes.c_int32,
                                            ctypes.POINTER(mok_saved_layout)]
+        L.mok_moe_workspace_layout.restype = ctypes.c_int
+        L.mok_moe_workspace_layout.argtypes = [ctypes.POINTER(mok_moe_config), ctypes.c_int32,
+                                               ctypes.POINTER(mok_workspace_layout)]
         L.mok_moe_forward.restype = ctypes.c_int
         L.mok_moe_forward.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P]
@@ -126,6 +138,12 @@ def mok_moe_saved_layout(cfg: mok_moe_config, k: int) -> dict:
     out = mok_saved_layout()
     _check(lib().mok_moe_saved_layout(ctypes.byref(cfg), k, ctypes.byref(out)), "mok_moe_saved_layout")
     return {n: getattr(out, n) for n, _ in mok_saved_layout._fields_}
+
+
+def mok_moe_workspace_layout(cfg: mok_moe_config, k: int) -> dict:
+    out = mok_workspace_layout()
+    _check(lib().mok_moe_workspace_layout(ctypes.byref(cfg), k, ctypes.byref(out)), "mok_moe_workspace_layout")
+    return {n: getattr(out, n) for n, _ in mok_workspace_layout._fields_}
 
 
 def mok_moe_forward(x, router_logits, W1, W3, W2, k, cfg, w_scales, out, topk_idx, topk_gate, expert_counts,

@@ -1,0 +1,130 @@
+"""How exactly the gfx950 scaled matrix instruction sums (the MXFP8 GEMMs'
+v_mfma_scale_f32_32x32x64_f8f6f4), measured on one block of fixed E4M3 codes
+and E8M0 scales against the exact sum of the same products.
+
+Every E4M3 product times its two power-of-two scales is exact in float64, and
+so is the sum of 64 of them at the magnitudes used here, so the reference is
+the exact value; its nearest fp32 is what an exactly rounded fp32 sum would
+give.  The probe reports how far the hardware lands from it.  The only hard
+bar is a loose one that any fp32-class accumulation meets; the measured
+figures are printed for the record."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mok_oracle as O
+from tests.gpu_case import note
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "mixture_experts_layer_34_amd",
+                   "libmok_diag.so")
+
+
+def _lib():
+    L = ctypes.CDLL(LIB)
+    L.mok_diag_mfma_scale_block.restype = ctypes.c_int32
+    L.mok_diag_mfma_scale_block.argtypes = [ctypes.c_void_p] * 7
+    return L
+
+
+def _finite_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] ^= 0x01          # S.1111.111 is NaN: take its neighbour
+    return c
+
+
+def _run(a, b, sa, sb, c_in):
+    dev = torch.device("cuda")
+    t = [torch.from_numpy(np.ascontiguousarray(v)).to(dev) for v in (a, b, sa, sb, c_in)]
+    out = torch.empty((32, 32), dtype=torch.float32, device=dev)
+    rc = _lib().mok_diag_mfma_scale_block(*[v.data_ptr() for v in t], out.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _exact(a, b, sa, sb, c_in):
+    va = O.e4m3_decode(a) * np.ldexp(1.0, np.repeat(sa.astype(np.int64) - 127, 32, axis=1))
+    vb = O.e4m3_decode(b) * np.ldexp(1.0, np.repeat(sb.astype(np.int64) - 127, 32, axis=1))
+    prod = va[:, None, :] * vb[None, :, :]            # [32, 32, 64], each exact
+    return c_in.astype(np.float64) + prod.sum(axis=2), np.abs(prod).sum(axis=2) + np.abs(c_in)
+
+
+def _report(case, hw, exact, mag):
+    rne = exact.astype(np.float32).astype(np.float64)
+    ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
+    err_ulp = np.abs(hw - exact) / np.maximum(ulp, np.finfo(np.float32).tiny)
+    off = int((hw != rne).sum())
+    note(f"  {case}: {off} of {hw.size} differ from the exactly rounded fp32 sum; max error {err_ulp.max():.1f} ulp "
+         f"of the result, {np.abs(hw - exact).max() / max(mag.max(), 1e-300):.2e} of the largest sum of magnitudes")
+    return off, err_ulp
+
+
+def _codes_with_exponent(rng, shape, lo, hi):
+    """Random E4M3 codes whose exponent field lies in [lo, hi] (0: subnormal)."""
+    e = rng.integers(lo, hi + 1, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    m = np.where((e == 15) & (m == 7), 6, m)          # S.1111.111 is NaN
+    m = np.where((e == 0) & (m == 0), 1, m)           # no zeros among the subnormals
+    s = rng.integers(0, 2, size=shape)
+    return ((s << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def test_normal_operands_sum_exactly_rounded():
+    """Normal E4M3 operands only, unit scales: the hardware sum against the
+    exactly rounded fp32 sum."""
+    rng = np.random.default_rng(1)
+    a, b = _codes_with_exponent(rng, (32, 64), 1, 15), _codes_with_exponent(rng, (32, 64), 1, 15)
+    sa = np.full((32, 2), 127, np.uint8)
+    sb = np.full((32, 2), 127, np.uint8)
+    c_in = np.zeros((32, 32), np.float32)
+    hw = _run(a, b, sa, sb, c_in)
+    exact, mag = _exact(a, b, sa, sb, c_in)
+    off, err = _report("normal operands", hw, exact, mag)
+    assert (np.abs(hw - exact) <= 65 * 2.0 ** -23 * mag).all()
+
+
+def test_subnormal_operands():
+    """One non-zero product per output, A subnormal (2^-9 .. 7 * 2^-9), B = 1:
+    the value the hardware gives it (exact, or flushed to zero)."""
+    a = np.zeros((32, 64), np.uint8)
+    for i in range(32):
+        a[i, i % 64] = 1 + (i % 7)                     # subnormal codes 0x01 .. 0x07
+    b = np.full((32, 64), 0x38, np.uint8)              # 1.0
+    sa = np.full((32, 2), 127, np.uint8)
+    sb = np.full((32, 2), 127, np.uint8)
+    hw = _run(a, b, sa, sb, np.zeros((32, 32), np.float32))
+    exact, mag = _exact(a, b, sa, sb, np.zeros((32, 32), np.float32))
+    flushed = int((hw == 0).sum())
+    note(f"  subnormal A operands: {flushed} of 1024 results are 0 (exact values {exact[0, 0]:.3e} ..)")
+    _report("subnormal operands", hw, exact, mag)
+    assert ((hw == exact) | (hw == 0)).all(), "a subnormal product is neither exact nor flushed"
+
+
+@pytest.mark.parametrize("case", ["random", "one-large-many-small", "accumulate"])
+def test_scaled_mfma_block_against_exact_sum(case):
+    """Random codes (subnormals included) and scales; the record of how far
+    the result lands from the exact sum, with a loose bar of 2^-12 of the sum
+    of magnitudes."""
+    rng = np.random.default_rng({"random": 1, "one-large-many-small": 2, "accumulate": 3}[case])
+    a, b = _finite_codes(rng, (32, 64)), _finite_codes(rng, (32, 64))
+    sa = rng.integers(124, 131, size=(32, 2)).astype(np.uint8)
+    sb = rng.integers(124, 131, size=(32, 2)).astype(np.uint8)
+    c_in = np.zeros((32, 32), np.float32)
+    if case == "one-large-many-small":
+        a[:, 1:] = 0x08 | (a[:, 1:] & 0x80)            # +-2^-6: small terms
+        a[:, 0] = 0x70                                 # 2^7 = 128: one large term
+        b[:, :] = 0x38 | (b & 0x80)                    # +-1
+        sa[:] = 127
+        sb[:] = 127
+    if case == "accumulate":
+        c_in = rng.normal(size=(32, 32)).astype(np.float32) * 64
+    hw = _run(a, b, sa, sb, c_in)
+    exact, mag = _exact(a, b, sa, sb, c_in)
+    _report(case, hw, exact, mag)
+    assert (np.abs(hw - exact) <= 2.0 ** -12 * mag + 1e-30).all()

@@ -1,16 +1,17 @@
 """GPU parity of the MXFP8 path against the oracle's OCP MX v1.0 emulation.
 
-Quantisation (weights through mok_quantize_mxfp8, activations inside the
-dispatch) must match the oracle bit for bit: both sides compute the same
-exact power-of-two scaling and round-to-nearest-even from exactly
-representable bf16 inputs."""
+Quantisation must match the oracle bit for bit: the weights through
+mok_quantize_mxfp8, and inside the layer the x rows quantised by the dispatch
+and the dY rows (gate * dout, an fp32 product) quantised by the reverse-
+combine, read back from the workspace.  Both sides compute the same exact
+power-of-two scaling and round-to-nearest-even from the same fp32 values."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import mok_oracle as O
-from mixture_experts_layer_34_amd.layer import quantize_mxfp8, scales_by_row
-from tests.gpu_case import note
+from mixture_experts_layer_34_amd.layer import MoeBuffers, quantize_mxfp8, scales_by_row
+from tests.gpu_case import note, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -120,3 +121,88 @@ def test_mxfp8_forward_ep_share_full_size_sampled():
     err = _run_and_oracle(w, inp, toks)
     note(f"  T={T} sampled {len(toks)} tokens, out error {err:.3e}")
     assert err <= 3e-2
+
+
+# ------------------------------------------------------------------ in-layer quantisers, bit for bit
+
+def _plane_scales(flat, rows, K, take):
+    """Rows `take` of pair-plane scales [K/64, rows, 2] as [len(take), K/32]."""
+    sc = flat[:(K // 64) * rows * 2].reshape(K // 64, rows, 2)
+    return sc[:, take, :].transpose(1, 0, 2).reshape(len(take), K // 32)
+
+
+def _dispatch_codes_match(w, inp, buf, rows_to_check):
+    """The dispatch's E4M3 codes and E8M0 scales of x rows against the
+    oracle's quantiser applied to the token row each expert row holds."""
+    from tests.gpu_case import saved_arrays, to_np
+    s = buf.shape
+    lay = buf.ws_layout
+    xr = lay["xp_rows"]
+    codes = buf.workspace_view("xp", torch.uint8, (xr, s.d))
+    flat = to_np(buf.workspace_view("xp_scale", torch.uint8, (xr * s.d // 32,)))
+    por = saved_arrays(buf)["pair_of_row"]
+    x = inp["x"].float().cpu().numpy()
+    take = np.asarray(rows_to_check)
+    rq, rs = O.mxfp8_quantize(x[por[take] // s.k])
+    assert np.array_equal(to_np(codes[torch.as_tensor(take, device=codes.device)]), rq), "x codes differ"
+    assert np.array_equal(_plane_scales(flat, xr, s.d, take), rs), "x scales differ"
+
+
+def _dy_codes_match(w, inp, buf, rows_to_check):
+    """The reverse-combine's dY codes and scales (written where the x codes
+    were) against the oracle's quantiser of gate * dout, the product taken
+    in fp32 as the layer takes it."""
+    from tests.gpu_case import saved_arrays, to_np
+    s = buf.shape
+    xr = buf.ws_layout["xp_rows"]
+    codes = buf.workspace_view("xp", torch.uint8, (xr, s.d))
+    flat = to_np(buf.workspace_view("xp_scale", torch.uint8, (xr * s.d // 32,)))
+    por = saved_arrays(buf)["pair_of_row"]
+    take = np.asarray(rows_to_check)
+    p = por[take]
+    gate = to_np(buf.topk_gate).reshape(-1).astype(np.float32)[p]
+    dout = inp["dout"].float().cpu().numpy()[p // s.k]
+    z = (gate[:, None] * dout).astype(np.float32)          # one fp32 product per element
+    rq, rs = O.mxfp8_quantize(z.astype(np.float64))
+    assert np.array_equal(to_np(codes[torch.as_tensor(take, device=codes.device)]), rq), "dY codes differ"
+    assert np.array_equal(_plane_scales(flat, xr, s.d, take), rs), "dY scales differ"
+
+
+@pytest.mark.parametrize("name,base,over", [
+    ("ragged", "bf16_train", dict(T=700, d=256, E=8, k=2, F=384)),
+    ("local", "bf16_fwd", dict(T=600, d=384, E=12, k=3, F=256, expert_begin=4, expert_end=9)),
+])
+def test_in_layer_quantisers_bit_exact(name, base, over):
+    """Every row: x codes written by the dispatch after an MXFP8 forward, then
+    the dY codes written by the reverse-combine of the MXFP8 backward."""
+    import workloads as W
+    from tests.gpu_case import run_layer
+    w = W.scaled(base, precision="mxfp8", backward=True, **over)
+    note(f"in-layer quantisers {name}")
+    inp = W.make_inputs(w, device="cuda")
+    # the forward alone first (buffers of the training configuration), so
+    # that the dispatch buffer still holds the x codes
+    buf = MoeBuffers(shape_of(w, w.T, True))
+    buf = run_layer(w, inp, backward=False, buf=buf)
+    P = int(buf.offsets[-1].item())
+    _dispatch_codes_match(w, inp, buf, np.arange(P))
+    buf = run_layer(w, inp, backward=True, buf=buf)
+    _dy_codes_match(w, inp, buf, np.arange(P))
+
+
+def test_in_layer_quantisers_train_full_size_sampled():
+    """The training shape (T 8192, d 4096, k 8): 4,096 sampled rows, the first
+    and last row of every expert among them."""
+    import workloads as W
+    from tests.gpu_case import run_layer
+    w = W.scaled("bf16_train", precision="mxfp8")
+    note("in-layer quantisers full size")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=False, buf=MoeBuffers(shape_of(w, w.T, True)))
+    off = buf.offsets.cpu().numpy()
+    P = int(off[-1])
+    ends = np.concatenate([off[:-1][off[1:] > off[:-1]], off[1:][off[1:] > off[:-1]] - 1])
+    rows = np.unique(np.concatenate([np.random.default_rng(11).choice(P, 4096, replace=False), ends]))
+    _dispatch_codes_match(w, inp, buf, rows)
+    buf = run_layer(w, inp, backward=True, buf=buf)
+    _dy_codes_match(w, inp, buf, rows)

@@ -102,10 +102,27 @@ def test_mxfp8_backward_small_matches_oracle(name, base, over):
     assert not bad, bad
 
 
+@pytest.mark.xfail(strict=False, reason=(
+    "d 128, F 256, k 1 with one expert taking nearly every row: d(logits) measured at 4.0e-2 against the "
+    "3e-2 bar (every other output under it); attributed to the scaled MFMA's accumulation, which is less "
+    "exact than an fp32 sum of the same products (test_gpu_mfma_probe.py measures it)"))
+def test_mxfp8_backward_d128_one_hot_over_the_bar():
+    w = W.scaled("bf16_train", precision="mxfp8", backward=True, T=520, d=128, E=6, k=1, F=256,
+                 notes={"zipf": 4.0})
+    note("mxfp8 backward d128 one-hot")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True)
+    errs = _errors(w, inp, buf)
+    note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items() if "[" not in k))
+    note(f"  max errors: {max(errs.values()):.3e} ({max(errs, key=errs.get)})")
+    bad = {k: v for k, v in errs.items() if v > TOL_MX}
+    assert not bad, bad
+
+
 def test_mxfp8_train_full_size_sampled():
     """The training workload (T 8192, d 4096, E 128, k 8, F 1536) in MXFP8,
     forward + backward: sampled tokens for out/dx/dgate/dlogits, and the
-    weight gradients of the lightest and the median expert."""
+    weight gradients of the lightest, the median and the heaviest expert."""
     w = W.scaled("bf16_train", precision="mxfp8")
     note("mxfp8 train full size forward+backward")
     inp = W.make_inputs(w, device="cuda")
@@ -130,7 +147,7 @@ def test_mxfp8_train_full_size_sampled():
             "dlogits": rel_inf(dlog[toks], np.stack(ref["dlogits"]))}
     _, offsets, _, por = O.layout(idx, w.E)
     order = np.argsort(counts, kind="stable")
-    for e in (int(order[0]), int(order[len(order) // 2])):
+    for e in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
         rows = por[offsets[e]:offsets[e + 1]]
         tok, slot = rows // w.k, rows % w.k
         r1, r3, r2 = O.expert_weight_grads(h["x"][tok], gate[tok, slot], h["dout"][tok], W1[e], W3[e], W2[e],

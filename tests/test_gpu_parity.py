@@ -203,7 +203,7 @@ def test_forward_full_size_sampled(name):
 def test_train_full_size_sampled():
     """bf16_train (T 8192, d 4096, E 128, k 8, F 1536) forward + backward, as
     the benchmark runs it: sampled tokens for out/dx/dgate/dlogits, and the
-    weight gradients of the lightest and the median expert."""
+    weight gradients of the lightest, the median and the heaviest expert."""
     w = W.get("bf16_train")
     note("train full size forward+backward")
     inp = _inputs(w)
@@ -226,7 +226,9 @@ def test_train_full_size_sampled():
     _, gate, _, _ = O.route(h["logits"], w.k)
     _, offsets, _, por = O.layout(idx, w.E)
     order = np.argsort(counts, kind="stable")
-    for e in (int(order[0]), int(order[len(order) // 2])):
+    # the lightest, the median and the heaviest expert (its tiles run the
+    # longest K loops and its run is shared among several XCD queues)
+    for e in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
         rows = por[offsets[e]:offsets[e + 1]]
         tok, slot = rows // w.k, rows % w.k
         r1, r3, r2 = O.expert_weight_grads(h["x"][tok], gate[tok, slot], h["dout"][tok], W1[e], W3[e], W2[e])
