@@ -96,7 +96,9 @@ typedef struct mok_moe_config {
                                 R > 0 (BF16 only) runs the ring pipeline: one
                                 launch per minibatch m copies minibatch m+1
                                 into its ring slot while UP runs on m and DOWN
-                                on m-1.  Results are bitwise those of R = 0.  */
+                                on m-1.  Results are bitwise those of R = 0.
+                                T*d*2 < 2^31 (the copies and the backward's
+                                gathered x rows use 32-bit offsets).        */
   int64_t ring_bytes;        /* fixed ring token buffer for dispatched rows
                                 ([fluid], [kucoin §02] "macrobatch"), used
                                 with R > 0: floor(ring_bytes / (2 d R)) slots
@@ -175,9 +177,6 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *                                 a backward call reads from `saved` lies
  *                                 outside its range (the slot is then treated
  *                                 as remote, so no access leaves a buffer);
- *               MOK_CHECK_STALL   a bounded wait of the ring pipeline gave up
- *                                 (the persistent kernel then drains without
- *                                 finishing its work).
  *             The library never synchronises: read the words (8 bytes at this
  *             offset) once the stream has passed the call, e.g. with a device
  *             to host copy at the caller's own synchronisation point.
@@ -191,7 +190,6 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *   total     workspace_bytes. */
 #define MOK_CHECK_LOGITS 0x1
 #define MOK_CHECK_INDEX 0x2
-#define MOK_CHECK_STALL 0x4
 typedef struct mok_workspace_layout {
   size_t status;
   size_t xp;

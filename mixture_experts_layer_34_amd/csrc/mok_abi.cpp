@@ -101,6 +101,11 @@ void saved_layout(const mok_moe_config& c, int32_t k, mok_saved_layout* s, size_
   s->total = o;
 }
 
+template <typename T> T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+template <typename T> const T* at(const void* base, size_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
 void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   const size_t Tk = (size_t)c.T * k, A = act_size(c);
   const int64_t nchunks = ((int64_t)Tk + kSortChunk - 1) / kSortChunk;
@@ -128,10 +133,7 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->total = o;
 }
 
-template <typename T> T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
-template <typename T> const T* at(const void* base, size_t off) {
-  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
-}
+
 
 hipError_t run_gemm(int prec, int kind, const GroupedGemmArgs& g, hipStream_t s) {
   if (prec == MOK_PREC_F32) return gemm_f32(kind, g, s);
@@ -186,90 +188,20 @@ static int gating_of(const mok_moe_config& c) {
     if ((call) != hipSuccess) return MOK_ERR_HIP; \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-const char* mok_status_string(mok_status s) {
-  switch (s) {
-    case MOK_OK: return "MOK_OK";
-    case MOK_ERR_INVALID_ARG: return "MOK_ERR_INVALID_ARG: invalid argument (null pointer, shape or alignment)";
-    case MOK_ERR_UNSUPPORTED: return "MOK_ERR_UNSUPPORTED: request not implemented by this library";
-    case MOK_ERR_WORKSPACE: return "MOK_ERR_WORKSPACE: ring buffer smaller than two minibatch slots";
-    case MOK_ERR_HIP: return "MOK_ERR_HIP: a HIP runtime call failed";
-    case MOK_ERR_DEVICE: return "MOK_ERR_DEVICE: a device-side check failed";
-  }
-  return "unknown mok_status";
-}
-
-int32_t mok_version(void) { return 100; }
-
-mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k, size_t* workspace_bytes,
-                                   size_t* saved_bytes) {
-  mok_status st = validate_config(cfg, k);
-  if (st != MOK_OK) return st;
-  if (!workspace_bytes || !saved_bytes) return MOK_ERR_INVALID_ARG;
-  WorkspaceLayout w;
-  workspace_layout(*cfg, k, &w);
-  mok_saved_layout s;
-  size_t tp, eo;
-  saved_layout(*cfg, k, &s, &tp, &eo);
-  *workspace_bytes = w.total;
-  *saved_bytes = s.total;
-  return MOK_OK;
-}
-
-mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_workspace_layout* out) {
-  mok_status st = validate_config(cfg, k);
-  if (st != MOK_OK) return st;
-  if (!out) return MOK_ERR_INVALID_ARG;
-  WorkspaceLayout w;
-  workspace_layout(*cfg, k, &w);
-  out->status = w.status;
-  out->xp = w.xp;
-  out->xp_scale = w.xp_scale;
-  out->xp_rows = w.xp_rows;
-  out->dy = w.dy;
-  out->dab = w.dab;
-  out->dxp = w.dxp;
-  out->total = w.total;
-  return MOK_OK;
-}
-
-mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out) {
-  mok_status st = validate_config(cfg, k);
-  if (st != MOK_OK) return st;
-  if (!out) return MOK_ERR_INVALID_ARG;
-  size_t tp, eo;
-  saved_layout(*cfg, k, out, &tp, &eo);
-  return MOK_OK;
-}
-
-mok_status mok_moe_forward(const void* x, const float* router_logits, const void* W1, const void* W3,
-                           const void* W2, int32_t k, const mok_moe_config* cfg, const uint8_t* w_scales,
+// The forward launch sequence, arguments already checked, with the workspace
+// at `workspace` laid out as `wl`.
+mok_status forward_checked(const void* x, const float* router_logits, const void* W1, const void* W3,
+                           const void* W2, int32_t k, const mok_moe_config& c, const uint8_t* w_scales,
                            void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
-                           int32_t* expert_offsets, void* saved, void* workspace, void* stream) {
-  mok_status st = validate_config(cfg, k);
-  if (st != MOK_OK) return st;
-  const mok_moe_config& c = *cfg;
-  const void* always[] = {W1, W3, W2, expert_counts, expert_offsets, saved, workspace};
-  const void* per_token[] = {x, router_logits, out, topk_idx, topk_gate};
-  for (const void* p : always)
-    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
-  for (const void* p : per_token)
-    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+                           int32_t* expert_offsets, void* saved, void* workspace, const WorkspaceLayout& wl,
+                           void* stream) {
   const bool mx = c.precision == MOK_PREC_MXFP8;
-  if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
-  if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
-
   hipStream_t s = (hipStream_t)stream;
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
   const int bf16 = c.precision != MOK_PREC_F32;
   mok_saved_layout sl;
   size_t tp_off, eo_off;
   saved_layout(c, k, &sl, &tp_off, &eo_off);
-  WorkspaceLayout wl;
-  workspace_layout(c, k, &wl);
 
   int32_t* s_idx = at<int32_t>(saved, sl.topk_idx);
   float* s_gate = at<float>(saved, sl.topk_gate);
@@ -407,6 +339,89 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
                                               P_max, status, s));
   return MOK_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+const char* mok_status_string(mok_status s) {
+  switch (s) {
+    case MOK_OK: return "MOK_OK";
+    case MOK_ERR_INVALID_ARG: return "MOK_ERR_INVALID_ARG: invalid argument (null pointer, shape or alignment)";
+    case MOK_ERR_UNSUPPORTED: return "MOK_ERR_UNSUPPORTED: request not implemented by this library";
+    case MOK_ERR_WORKSPACE: return "MOK_ERR_WORKSPACE: ring buffer smaller than two minibatch slots";
+    case MOK_ERR_HIP: return "MOK_ERR_HIP: a HIP runtime call failed";
+    case MOK_ERR_DEVICE: return "MOK_ERR_DEVICE: a device-side check failed";
+  }
+  return "unknown mok_status";
+}
+
+int32_t mok_version(void) { return 100; }
+
+mok_status mok_moe_workspace_query(const mok_moe_config* cfg, int32_t k, size_t* workspace_bytes,
+                                   size_t* saved_bytes) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!workspace_bytes || !saved_bytes) return MOK_ERR_INVALID_ARG;
+  WorkspaceLayout w;
+  workspace_layout(*cfg, k, &w);
+  mok_saved_layout s;
+  size_t tp, eo;
+  saved_layout(*cfg, k, &s, &tp, &eo);
+  *workspace_bytes = w.total;
+  *saved_bytes = s.total;
+  return MOK_OK;
+}
+
+mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_workspace_layout* out) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!out) return MOK_ERR_INVALID_ARG;
+  WorkspaceLayout w;
+  workspace_layout(*cfg, k, &w);
+  out->status = w.status;
+  out->xp = w.xp;
+  out->xp_scale = w.xp_scale;
+  out->xp_rows = w.xp_rows;
+  out->dy = w.dy;
+  out->dab = w.dab;
+  out->dxp = w.dxp;
+  out->total = w.total;
+  return MOK_OK;
+}
+
+mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_layout* out) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  if (!out) return MOK_ERR_INVALID_ARG;
+  size_t tp, eo;
+  saved_layout(*cfg, k, out, &tp, &eo);
+  return MOK_OK;
+}
+
+mok_status mok_moe_forward(const void* x, const float* router_logits, const void* W1, const void* W3,
+                           const void* W2, int32_t k, const mok_moe_config* cfg, const uint8_t* w_scales,
+                           void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                           int32_t* expert_offsets, void* saved, void* workspace, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  const void* always[] = {W1, W3, W2, expert_counts, expert_offsets, saved, workspace};
+  const void* per_token[] = {x, router_logits, out, topk_idx, topk_gate};
+  for (const void* p : always)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  const bool mx = c.precision == MOK_PREC_MXFP8;
+  if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
+  if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
+
+  WorkspaceLayout wl;
+  workspace_layout(c, k, &wl);
+  return forward_checked(x, router_logits, W1, W3, W2, k, c, w_scales, out, topk_idx, topk_gate, expert_counts,
+                         expert_offsets, saved, workspace, wl, stream);
+}
+
 
 mok_status mok_moe_backward(const void* dout, const void* x, const float* router_logits, const void* W1,
                             const void* W3, const void* W2, int32_t k, const mok_moe_config* cfg,

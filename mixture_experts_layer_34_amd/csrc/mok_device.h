@@ -52,7 +52,6 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 constexpr int32_t kStatusDevice = 5;                   // MOK_ERR_DEVICE
 constexpr int32_t kCheckLogits = 1;                    // a router logit row holds NaN or +-Inf
 constexpr int32_t kCheckIndex = 2;                     // a row or expert index outside its range
-constexpr int32_t kCheckStall = 4;                     // a bounded wait of the ring scheduler gave up
 __device__ __forceinline__ void report(int32_t* status, int32_t bit) {
   if (status) {
     __hip_atomic_store(status, kStatusDevice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

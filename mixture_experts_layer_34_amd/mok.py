@@ -44,7 +44,7 @@ class mok_workspace_layout(ctypes.Structure):
                 ("dxp", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
-MOK_CHECK_LOGITS, MOK_CHECK_INDEX, MOK_CHECK_STALL = 0x1, 0x2, 0x4
+MOK_CHECK_LOGITS, MOK_CHECK_INDEX = 0x1, 0x2
 
 
 class MokError(RuntimeError):

@@ -179,6 +179,12 @@ def test_ring_mode_validation():
     with pytest.raises(mok.MokError) as ei:
         mok.mok_moe_workspace_query(_cfg(minibatch_rows=64, ring_bytes=64 * 128 * 2), 2)
     assert ei.value.status == mok.MOK_ERR_WORKSPACE
+    # x of 2 GiB or more: the ring's row copies and the backward's gathered x
+    # rows address it with 32-bit offsets
+    with pytest.raises(mok.MokError) as ei:
+        mok.mok_moe_workspace_query(_cfg(T=262144, d=4096, ffn=256, minibatch_rows=4096, ring_bytes=1 << 26), 1)
+    assert ei.value.status == mok.MOK_ERR_INVALID_ARG
+    mok.mok_moe_workspace_query(_cfg(T=262143, d=4096, ffn=256, minibatch_rows=4096, ring_bytes=1 << 26), 1)
     # the dispatch buffer shrinks to the ring
     full_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096), 2)
     ring_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096, minibatch_rows=256, ring_bytes=2 * 256 * 128 * 2), 2)
