@@ -237,6 +237,32 @@ mok_status mok_moe_forward(const void* x, const float* router_logits,
                            void* saved, void* workspace, void* stream);
 
 /*
+ * Forward for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid allocation.  The
+ * same computation and arguments as mok_moe_forward without `workspace`: its
+ * scratch (the status words and the counting sort's chunk tables) lives in a
+ * static device array of the library, 4 MiB per GPU, held until the process
+ * ends.  Nothing is allocated or freed by the call.
+ *   Supports the bf16 whole layer (MOK_PREC_BF16, minibatch_rows = 0, x below
+ *   2 GiB) with or without MOK_FLAG_SAVE_FOR_BACKWARD and the router variant
+ *   flags; other configurations return MOK_ERR_UNSUPPORTED.  The scratch
+ *   needed is about 8 * E * ceil(T*k / 512) bytes; beyond 4 MiB the call
+ *   returns MOK_ERR_WORKSPACE (at E 128, up to T*k of about 2 million pairs).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, other threads) race and must be serialised by the
+ *   caller.  The array is taken on the device current when the call is made,
+ *   which must be the device of `stream`.  The device status words are kept
+ *   in the array and are not readable by the caller.
+ * `saved` is still the caller's (as for mok_moe_forward; a later
+ * mok_moe_backward needs a workspace of its own).
+ */
+mok_status mok_moe_forward_noalloc(const void* x, const float* router_logits,
+                                   const void* W1, const void* W3, const void* W2, int32_t k,
+                                   const mok_moe_config* cfg, void* out, int32_t* topk_idx,
+                                   float* topk_gate, int32_t* expert_counts, int32_t* expert_offsets,
+                                   void* saved, void* stream);
+
+/*
  * Backward pass: gradients of L = sum(out * dout), mirroring the forward
  * ([kucoin §01]: two more communication steps in the reverse direction;
  * [kucoin §02]: reverse-combine, then reverse-dispatch).  Requires a forward

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mok.h"
 #include "mok_internal.h"
@@ -340,6 +341,50 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
   return MOK_OK;
 }
 
+// ------------------------------------------------------------ no-allocation forward
+// mok_moe_forward_noalloc keeps its scratch (the status words and the counting
+// sort's chunk tables) in this array instead of a caller's workspace.  One copy
+// per GPU, held until the process ends; every call on a GPU shares it.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The array's device address on each GPU, taken once per device with that
+// device current (the name itself is only a host-side stand-in).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mok_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOK_ERR_HIP;
+    size_t bytes = 0;  // the symbol found is the whole array
+    if (hipGetSymbolSize(&bytes, HIP_SYMBOL(scratch)) != hipSuccess || bytes != kScratchBytes) return MOK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOK_OK;
+}
+
+// Scratch of a bf16 whole-layer forward whose dispatch is fused into UP's
+// loads: the status words and the two chunk tables of the counting sort.
+WorkspaceLayout compact_forward_layout(const mok_moe_config& c, int32_t k) {
+  WorkspaceLayout w{};
+  const int64_t nchunks = ((int64_t)c.T * k + kSortChunk - 1) / kSortChunk;
+  w.nchunks = (int)nchunks;
+  size_t o = 0;
+  w.status = o;        o = align256(o + 256);
+  w.chunk_counts = o;  o = align256(o + (size_t)nchunks * c.E * 4);
+  w.chunk_base = o;    o = align256(o + (size_t)nchunks * c.E * 4);
+  w.tile_prefix = w.xp = w.xp_scale = w.hq = w.hq_scale = w.dy = w.dab = w.dxp = w.queue = o;
+  w.xp_rows = 0;
+  w.total = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -422,6 +467,29 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
                          expert_offsets, saved, workspace, wl, stream);
 }
 
+mok_status mok_moe_forward_noalloc(const void* x, const float* router_logits, const void* W1, const void* W3,
+                                   const void* W2, int32_t k, const mok_moe_config* cfg, void* out,
+                                   int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                                   int32_t* expert_offsets, void* saved, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  // the bf16 whole layer with the dispatch fused into UP: no row buffer
+  if (c.precision != MOK_PREC_BF16 || c.minibatch_rows != 0 || !fused_pull(c)) return MOK_ERR_UNSUPPORTED;
+  const void* always[] = {W1, W3, W2, expert_counts, expert_offsets, saved};
+  const void* per_token[] = {x, router_logits, out, topk_idx, topk_gate};
+  for (const void* p : always)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  const WorkspaceLayout wl = compact_forward_layout(c, k);
+  if (wl.total > kScratchBytes) return MOK_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MOK_OK) return st;
+  return forward_checked(x, router_logits, W1, W3, W2, k, c, nullptr, out, topk_idx, topk_gate, expert_counts,
+                         expert_offsets, saved, ws, wl, stream);
+}
 
 mok_status mok_moe_backward(const void* dout, const void* x, const float* router_logits, const void* W1,
                             const void* W3, const void* W2, int32_t k, const mok_moe_config* cfg,
