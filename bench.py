@@ -120,17 +120,21 @@ def roof_of(flops_n, bytes_n, ms, peak_tflops):
             "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_bf16_train_hbm_traffic.md")
+TRAFFIC_FILES = {"bf16_train": os.path.join(ROOT, "profiles", "grouped_gemm_bf16_train_hbm_traffic.md"),
+                 "mxfp8_train": os.path.join(ROOT, "profiles", "grouped_gemm_mxfp8_train_hbm_traffic.md")}
 
 
 def measured_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from the committed FETCH_SIZE/WRITE_SIZE
-    record (calibrated counter passes), or None when there is no record for
-    this workload and kernel or the kernel sources changed since it was taken."""
+    record of this workload (calibrated counter passes on the same inputs), or
+    None when there is no record for this workload and kernel or the kernel
+    sources changed since it was taken."""
     import hashlib
     import re
+    if workload not in TRAFFIC_FILES:
+        return None
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILES[workload]).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
     except (OSError, AttributeError, ValueError):
         return None

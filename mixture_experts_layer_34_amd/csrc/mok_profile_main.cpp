@@ -3,13 +3,19 @@
 //
 //   mok_profile [--T 8192] [--d 4096] [--E 128] [--k 8] [--F 1536] [--zipf 1.2]
 //               [--steps 3] [--warmup 1] [--forward-only] [--copy-mib 0]
+//               [--inputs DIR] [--mxfp8]
 //
-// Inputs are synthetic: x and weights hashed uniform values (N(0,1)-like and
-// N(0, 0.02^2)-like spread), router logits log(pi_e) + Gumbel noise with
-// pi_r proportional to r^-zipf and expert 0 hottest — the same routing model
-// as the training workload of the Python benchmark (values differ; shapes and
-// expert loads follow the same distribution).  --copy-mib runs one plain
-// device copy kernel of that size first (HBM byte-counter calibration).
+// Inputs: with --inputs, the raw arrays that profile_inputs.py writes from the
+// benchmark's own workload generator (x, logits, dout as bf16 / fp32 / bf16,
+// W1, W3, W2 as bf16, row-major, native byte order), so that the counters
+// are taken on exactly the benchmarked layer call.  Without it, synthetic
+// values: x and weights hashed uniform values, router logits log(pi_e) +
+// Gumbel noise with pi_r proportional to r^-zipf and expert 0 hottest (the
+// same routing model; values and expert loads differ).  --mxfp8 runs the
+// MXFP8 layer (weights quantised by mok_quantize_mxfp8 and
+// mok_quantize_mxfp8_backward_weights before the timed steps).  --copy-mib
+// runs one plain device copy kernel of that size first (HBM byte-counter
+// calibration).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -69,7 +75,8 @@ __global__ void copy_kernel(const uint4* a, uint4* b, int64_t n) {
 int main(int argc, char** argv) {
   int T = 8192, d = 4096, E = 128, k = 8, F = 1536, steps = 3, warmup = 1, copy_mib = 0;
   float zipf = 1.2f;
-  bool backward = true;
+  bool backward = true, mxfp8 = false;
+  std::string inputs;
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
     auto next = [&]() { return (i + 1 < argc) ? argv[++i] : (fprintf(stderr, "missing value\n"), exit(2), ""); };
@@ -83,6 +90,8 @@ int main(int argc, char** argv) {
     else if (a == "--warmup") warmup = atoi(next());
     else if (a == "--copy-mib") copy_mib = atoi(next());
     else if (a == "--forward-only") backward = false;
+    else if (a == "--inputs") inputs = next();
+    else if (a == "--mxfp8") mxfp8 = true;
     else { fprintf(stderr, "unknown argument %s\n", a.c_str()); return 2; }
   }
   if (copy_mib > 0) {
@@ -100,7 +109,7 @@ int main(int argc, char** argv) {
   mok_moe_config cfg;
   memset(&cfg, 0, sizeof(cfg));
   cfg.T = T; cfg.d = d; cfg.E = E; cfg.ffn = F; cfg.expert_begin = 0; cfg.expert_end = E;
-  cfg.precision = MOK_PREC_BF16;
+  cfg.precision = mxfp8 ? MOK_PREC_MXFP8 : MOK_PREC_BF16;
   cfg.flags = backward ? MOK_FLAG_SAVE_FOR_BACKWARD : 0;
   size_t ws_bytes, sv_bytes;
   MOKCHECK(mok_moe_workspace_query(&cfg, k, &ws_bytes, &sv_bytes));
@@ -118,14 +127,56 @@ int main(int argc, char** argv) {
   CHECK(hipMalloc(&saved, sv_bytes)); CHECK(hipMalloc(&ws, ws_bytes));
   double norm = 0;
   for (int r = 1; r <= E; ++r) norm += std::pow((double)r, -(double)zipf);
-  hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, x, xw, 1.7f, 1u);
-  hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, dout, xw, 1.7f, 2u);
-  hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W1, ww, 0.035f, 3u);
-  hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W3, ww, 0.035f, 4u);
-  hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W2, ww, 0.035f, 5u);
-  hipLaunchKernelGGL(fill_logits, dim3(1024), dim3(256), 0, 0, logits, T, E, zipf, (float)std::log(norm), 6u);
+  if (inputs.empty()) {
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, x, xw, 1.7f, 1u);
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, dout, xw, 1.7f, 2u);
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W1, ww, 0.035f, 3u);
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W3, ww, 0.035f, 4u);
+    hipLaunchKernelGGL(fill_bf16, dim3(4096), dim3(256), 0, 0, W2, ww, 0.035f, 5u);
+    hipLaunchKernelGGL(fill_logits, dim3(1024), dim3(256), 0, 0, logits, T, E, zipf, (float)std::log(norm), 6u);
+  } else {
+    // the raw arrays of the benchmark's workload, each checked for its exact size
+    auto load = [&](const char* name, void* dst, int64_t bytes) {
+      const std::string path = inputs + "/" + name;
+      FILE* f = fopen(path.c_str(), "rb");
+      if (!f) { fprintf(stderr, "cannot open %s\n", path.c_str()); exit(2); }
+      std::vector<char> buf(bytes);
+      const size_t got = fread(buf.data(), 1, bytes, f);
+      const bool extra = fgetc(f) != EOF;
+      fclose(f);
+      if ((int64_t)got != bytes || extra) { fprintf(stderr, "%s: expected %lld bytes\n", path.c_str(), (long long)bytes); exit(2); }
+      CHECK(hipMemcpy(dst, buf.data(), bytes, hipMemcpyHostToDevice));
+    };
+    load("x.bin", x, xw * 2);
+    load("dout.bin", dout, xw * 2);
+    load("logits.bin", logits, (int64_t)T * E * 4);
+    load("W1.bin", W1, ww * 2);
+    load("W3.bin", W3, ww * 2);
+    load("W2.bin", W2, ww * 2);
+  }
   CHECK(hipDeviceSynchronize());
+  // MXFP8: forward weights along d (W1, W3) and F (W2), scales concatenated;
+  // the backward's transposed copies
+  uint8_t *q1 = nullptr, *q3 = nullptr, *q2 = nullptr, *wsc = nullptr, *wtq = nullptr, *wts = nullptr;
+  if (mxfp8) {
+    CHECK(hipMalloc(&q1, ww)); CHECK(hipMalloc(&q3, ww)); CHECK(hipMalloc(&q2, ww));
+    CHECK(hipMalloc(&wsc, 3 * ww / 32));
+    CHECK(hipMalloc(&wtq, 3 * ww)); CHECK(hipMalloc(&wts, 3 * ww / 32));
+    MOKCHECK(mok_quantize_mxfp8(W1, (int64_t)E * F, d, q1, wsc, nullptr));
+    MOKCHECK(mok_quantize_mxfp8(W3, (int64_t)E * F, d, q3, wsc + ww / 32, nullptr));
+    MOKCHECK(mok_quantize_mxfp8(W2, (int64_t)E * d, F, q2, wsc + 2 * ww / 32, nullptr));
+    MOKCHECK(mok_quantize_mxfp8_backward_weights(W1, W3, W2, E, d, F, wtq, wts, nullptr));
+    CHECK(hipDeviceSynchronize());
+  }
   auto step = [&]() {
+    if (mxfp8) {
+      MOKCHECK(mok_moe_forward(x, logits, q1, q3, q2, k, &cfg, wsc, out, idx, gate, counts, offsets, saved, ws,
+                               nullptr));
+      if (backward)
+        MOKCHECK(mok_moe_backward_mxfp8(dout, x, logits, k, &cfg, wtq, wts, saved, dx, dW1, dW3, dW2, dgate, dlog,
+                                        ws, nullptr));
+      return;
+    }
     MOKCHECK(mok_moe_forward(x, logits, W1, W3, W2, k, &cfg, nullptr, out, idx, gate, counts, offsets, saved, ws,
                              nullptr));
     if (backward)
@@ -161,7 +212,8 @@ int main(int argc, char** argv) {
   CHECK(hipEventElapsedTime(&ms, a, b));
   std::vector<int32_t> h_off(E + 1);
   CHECK(hipMemcpy(h_off.data(), offsets, (E + 1) * 4, hipMemcpyDeviceToHost));
-  printf("T=%d d=%d E=%d k=%d F=%d zipf=%.2f %s: %.3f ms/step, P=%d\n", T, d, E, k, F, zipf,
-         backward ? "forward+backward" : "forward", ms / steps, h_off[E]);
+  printf("T=%d d=%d E=%d k=%d F=%d zipf=%.2f %s %s%s: %.3f ms/step, P=%d\n", T, d, E, k, F, zipf,
+         mxfp8 ? "mxfp8" : "bf16", backward ? "forward+backward" : "forward",
+         inputs.empty() ? " (synthetic inputs)" : " (benchmark workload inputs)", ms / steps, h_off[E]);
   return 0;
 }

@@ -19,20 +19,21 @@ def _write_record(tmp_path, src_text: str, digest: str):
 def test_traffic_used_when_sources_match(tmp_path, monkeypatch):
     text = "kernel source"
     md = _write_record(tmp_path, text, hashlib.sha256(text.encode()).hexdigest()[:16])
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(md))
+    monkeypatch.setattr(bench, "TRAFFIC_FILES", {"wl": str(md), "other": str(md)})
     assert bench.measured_traffic("wl", "gemm_x") == 1234
-    assert bench.measured_traffic("other", "gemm_x") is None
+    assert bench.measured_traffic("other", "gemm_x") is None   # the record is the other workload's
+    assert bench.measured_traffic("unknown", "gemm_x") is None
     assert bench.measured_traffic("wl", "gemm_y") is None
 
 
 def test_traffic_null_after_source_change(tmp_path, monkeypatch):
     md = _write_record(tmp_path, "kernel source v2", hashlib.sha256(b"kernel source").hexdigest()[:16])
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(md))
+    monkeypatch.setattr(bench, "TRAFFIC_FILES", {"wl": str(md)})
     assert bench.measured_traffic("wl", "gemm_x") is None
 
 
 def test_traffic_null_without_record(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
+    monkeypatch.setattr(bench, "TRAFFIC_FILES", {"wl": str(tmp_path / "missing.md")})
     assert bench.measured_traffic("wl", "gemm_x") is None
 
 
