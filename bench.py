@@ -426,6 +426,74 @@ def measure(name: str, args, extras: bool):
     return result, w, inp, (K, Wm, ev, sh)
 
 
+def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256, 512)):
+    """Forward-only calls of a few tokens on the training layer's weights (a
+    decode step): microseconds per call with the router and the counting sort
+    fused into one launch (the default for T * k <= 4096) and as separate
+    launches, eagerly and replayed from a HIP graph, plus the routing part
+    alone (the router stage, or router + sort) from the library's stage events."""
+    import torch
+
+    import workloads as W
+    from mixture_experts_layer_34_amd import mok
+    from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape
+
+    dev = inp["x"].device
+    n = max(K, 50)
+    out = {}
+    for T in Ts:
+        wT = W.scaled(w.name, T=T)
+        small = W.make_inputs(wT, device=dev, weights=False)
+        row = {"pairs": T * w.k}
+        for sep in (False, True):
+            tag = "separate" if sep else "fused"
+            buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision,
+                                      separate_route_sort=sep), device=dev)
+
+            def fwd(events=None, stream=sh):
+                buf.cfg.stage_events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+                buf.forward(small["x"], small["logits"], inp["W1"], inp["W3"], inp["W2"], stream=stream)
+
+            for _ in range(5):
+                fwd()
+            torch.cuda.synchronize()
+            a, b = ev.create(2)
+            ev.record(a, sh)
+            for _ in range(n):
+                fwd()
+            ev.record(b, sh)
+            row[f"{tag}_us"] = round(ev.elapsed_ms(a, b) * 1e3 / n, 2)
+            st = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(n)]
+            for i in range(n):
+                fwd(st[i])
+            torch.cuda.synchronize()
+            stages = ["router"] + ([] if not sep else ["sort"])
+            row[f"{tag}_route_sort_us"] = round(sum(
+                ev.elapsed_ms(st[i][2 * mok.STAGES.index(g)], st[i][2 * mok.STAGES.index(g) + 1])
+                for i in range(n) for g in stages) * 1e3 / n, 2)
+            buf.cfg.stage_events = None
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                fwd(stream=side.cuda_stream)
+            torch.cuda.current_stream(dev).wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fwd(stream=torch.cuda.current_stream(dev).cuda_stream)
+            graph.replay()
+            torch.cuda.synchronize()
+            a, b = ev.create(2)
+            ev.record(a, sh)
+            for _ in range(n):
+                graph.replay()
+            ev.record(b, sh)
+            row[f"{tag}_graph_us"] = round(ev.elapsed_ms(a, b) * 1e3 / n, 2)
+            del graph, buf
+        out[str(T)] = row
+    return {"workload": f"{w.name} weights, forward only, T tokens per call", "calls": n, "per_T": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +514,10 @@ def main():
                     help="skip the extra timing of steps that start with the last-level cache flushed")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8 forward+backward leg after the bf16 training workload")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the forward-only few-token latency leg after the bf16 training workload")
+    ap.add_argument("--decode-tokens", type=lambda v: [int(x) for x in v.split(",") if x], default=[1, 16, 64, 256],
+                    help="tokens per call of the few-token latency leg (comma list)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (HBM counter calibration)")
     args = ap.parse_args()
@@ -486,6 +558,9 @@ def main():
                                 "whole_layer_forward_ms": round(sum(result["stages_ms"].get(n, 0.0) for n in
                                                                     ("dispatch", "gemm_up", "gemm_down",
                                                                      "combine")), 4)}
+    if args.workload == "bf16_train" and not (args.no_decode or args.minibatch_rows or args.forward_only):
+        result["decode_latency"] = decode_latency(w, inp, K, ev, sh, args.decode_tokens)
+        torch.cuda.empty_cache()
     if args.workload == "bf16_train" and not (args.no_mxfp8 or args.minibatch_rows or args.forward_only):
         # the MXFP8 leg of the metric: the same layer, inputs and routing with
         # MXFP8 forward GEMMs and MXFP8 dx products in the backward

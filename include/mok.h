@@ -81,6 +81,14 @@ typedef enum {
  * affinity (softmax Jacobian, or a (1 - a) for the sigmoid). */
 #define MOK_FLAG_SIGMOID_GATES 0x2u
 #define MOK_FLAG_RENORM_GATES 0x4u
+/* A forward call of 1 <= T <= 32 tokens and T * k <= 4096 pairs (a decode
+ * step, where the launches, not the bytes, set the time of routing and
+ * sorting) runs the
+ * router and the layout step ([kucoin §01]: count each expert's tokens, then
+ * place them, one expert's rows together) as one single-workgroup launch; its stage events then cover MOK_STAGE_ROUTER only,
+ * and MOK_STAGE_SORT is not run.  Results are bitwise those of the separate
+ * router and sort launches, which this flag selects at any size. */
+#define MOK_FLAG_SEPARATE_ROUTE_SORT 0x8u
 
 typedef struct mok_moe_config {
   int32_t T;                 /* tokens in this call (>= 0)                      */

@@ -42,7 +42,8 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
     return MOK_ERR_INVALID_ARG;
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
-  if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES))
+  if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES |
+                  MOK_FLAG_SEPARATE_ROUTE_SORT))
     return MOK_ERR_INVALID_ARG;
   if (c.precision == MOK_PREC_MXFP8) {
     // every E8M0 scale array (x and H rows, each weight matrix) fits a 32-bit buffer range
@@ -215,12 +216,20 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
 
   int32_t* status = at<int32_t>(workspace, wl.status);
   const int64_t P_max = (int64_t)T * k;
-  MOK_HIP(launch_status_reset(status, s));
-  MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx,
-                                                 s_gate, s_lse, status, s));
-  MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks, at<int32_t>(workspace, wl.chunk_counts),
-                               at<int32_t>(workspace, wl.chunk_base), expert_counts, expert_offsets, s_off, s_tp,
-                               s_order, s_rop, s_por, s));
+  if (T >= 1 && T <= kSmallTokens && P_max <= kSmallPairs && !(c.flags & MOK_FLAG_SEPARATE_ROUTE_SORT)) {
+    // small call: status reset, router and counting sort in one workgroup
+    MOK_STAGE(MOK_STAGE_ROUTER, launch_route_sort_small(router_logits, T, E, k, gating_of(c), eb, c.expert_end,
+                                                        topk_idx, topk_gate, s_idx, s_gate, s_lse, expert_counts,
+                                                        expert_offsets, s_off, s_tp, s_order, s_rop, s_por, status, s));
+  } else {
+    MOK_HIP(launch_status_reset(status, s));
+    MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx,
+                                                   s_gate, s_lse, status, s));
+    MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks,
+                                                   at<int32_t>(workspace, wl.chunk_counts),
+                                                   at<int32_t>(workspace, wl.chunk_base), expert_counts,
+                                                   expert_offsets, s_off, s_tp, s_order, s_rop, s_por, s));
+  }
   GroupedGemmArgs g{};
   g.offsets = s_off;
   g.tile_prefix = s_tp;

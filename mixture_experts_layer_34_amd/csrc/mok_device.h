@@ -45,6 +45,32 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Unsigned 64-bit maximum over a wave through DPP lane moves (no LDS
+// crossbar): swaps within quads, rotations by 4 and 8 within each row of 16
+// lanes, then the broadcasts of lane 15 of each row to the next row and of
+// lane 31 to rows 2 and 3; lane 63 ends with the maximum, which is returned
+// to every lane.  A lane with no source in a step reads 0, the identity.
+template <int CTRL>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xf, 0xf, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xf, 0xf, false);
+  const bool gt = ohi > hi || (ohi == hi && olo > lo);
+  hi = gt ? ohi : hi;
+  lo = gt ? olo : lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
+  uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+  dpp_max_step<0xb1>(hi, lo);   // quad_perm [1,0,3,2]
+  dpp_max_step<0x4e>(hi, lo);   // quad_perm [2,3,0,1]
+  dpp_max_step<0x124>(hi, lo);  // row_ror 4
+  dpp_max_step<0x128>(hi, lo);  // row_ror 8
+  dpp_max_step<0x142>(hi, lo);  // row_bcast 15
+  dpp_max_step<0x143>(hi, lo);  // row_bcast 31
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // ------------------------------------------------------------ status word
 // Device-side checks report into the status word at the start of the
 // workspace: word 0 becomes MOK_ERR_DEVICE (5) and word 1 gathers the bits of

@@ -47,6 +47,20 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int gati
                               float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
                               int32_t* status, hipStream_t s);
 
+// Small-T path: status reset, router and counting sort in one single-workgroup
+// launch, for 1 <= T <= kSmallTokens and T * k <= kSmallPairs; the same
+// outputs as launch_status_reset + launch_router_topk + launch_counting_sort.
+// The 16 waves of the one workgroup route two tokens each at most: past that
+// the router's arithmetic on one compute unit costs more than the launches
+// saved.
+constexpr int kSmallTokens = 32;
+constexpr int kSmallPairs = 4096;
+hipError_t launch_route_sort_small(const float* logits, int T, int E, int k, int gating, int eb, int ee,
+                                   int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved,
+                                   float* lse, int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
+                                   int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
+                                   int32_t* pair_of_row, int32_t* status, hipStream_t s);
+
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
                                 int nchunks, int32_t* chunk_counts, int32_t* chunk_base,
                                 int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,

@@ -22,6 +22,92 @@ namespace mok {
 // probability of the chosen expert, or its sigmoid (SIGM); with RENORM each
 // is divided by their sum over the k chosen experts (slot order, fp32).
 constexpr int kRouterMaxK = 1024;  // k <= E <= 1024
+// One token's routing by one wave: top-k of the raw logits, gates, lse.
+// graw: this wave's k floats of LDS (renormalised gates only).
+template <int EPL, bool SIGM, bool RENORM>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+                                            int32_t* __restrict__ idx_saved, float* __restrict__ gate_saved,
+                                            float* __restrict__ lse_out, int32_t* __restrict__ status,
+                                            float* graw) {
+  const int lane = lane_id();
+  const float* row = logits + (int64_t)t * E;
+  float v[EPL];
+  float m = -INFINITY;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+    // logits must be finite: a NaN or an infinity is reported, and a NaN
+    // is ranked as -inf so that the k chosen indices stay in [0, E)
+    if (e < E && !isfinite(v[i])) {
+      bad = true;
+      if (v[i] != v[i]) v[i] = -INFINITY;
+    }
+    m = fmaxf(m, v[i]);
+  }
+  if (__ballot(bad) != 0 && lane == 0) report(status, kCheckLogits);
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    int e = lane + 64 * i;
+    if (e < E) s += expf(v[i] - m);
+  }
+  s = wave_sum(s);
+  const float inv_s = 1.0f / s;
+  // Selection key of each candidate: the logit mapped to an order-preserving
+  // unsigned code (with -0 taken as +0, so that equal values tie) in the high
+  // word, 2^32 - 1 - e in the low word: the largest key is the largest
+  // value, lowest index first.  A chosen or absent candidate has key 0, below
+  // every real key (-inf maps to 0x007fffff).
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    uint32_t u = __float_as_uint(v[i]);
+    if ((u << 1) == 0) u = 0;
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[i] = e < E ? ((uint64_t)ord << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  float gsum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const uint32_t ord = (uint32_t)(best >> 32);
+    const float bv = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i == be) key[i] = 0ull;
+    if (lane == 0) {
+      const float g = SIGM ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) * inv_s;
+      idx_out[(int64_t)t * k + j] = be;
+      idx_saved[(int64_t)t * k + j] = be;
+      if constexpr (RENORM) {
+        graw[j] = g;
+        gsum += g;
+      } else {
+        gate_out[(int64_t)t * k + j] = g;
+        gate_saved[(int64_t)t * k + j] = g;
+      }
+    }
+  }
+  if (lane == 0) {
+    lse_out[t] = m + logf(s);
+    if constexpr (RENORM) {
+      for (int j = 0; j < k; ++j) {
+        const float g = graw[j] / gsum;
+        gate_out[(int64_t)t * k + j] = g;
+        gate_saved[(int64_t)t * k + j] = g;
+      }
+    }
+  }
+}
+
 template <int EPL, bool SIGM, bool RENORM>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int32_t* __restrict__ idx_out,
@@ -31,84 +117,11 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           float* __restrict__ lse_out,
                                                           int32_t* __restrict__ status) {
   __shared__ float renorm_buf[RENORM ? 4 * kRouterMaxK : 1];
-  const int lane = lane_id();
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  for (int t = wave; t < T; t += nwaves) {
-    const float* row = logits + (int64_t)t * E;
-    float v[EPL];
-    float m = -INFINITY;
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      int e = lane + 64 * i;
-      v[i] = e < E ? row[e] : -INFINITY;
-      // logits must be finite: a NaN or an infinity is reported, and a NaN
-      // is ranked as -inf so that the k chosen indices stay in [0, E)
-      if (e < E && !isfinite(v[i])) {
-        bad = true;
-        if (v[i] != v[i]) v[i] = -INFINITY;
-      }
-      m = fmaxf(m, v[i]);
-    }
-    if (__ballot(bad) != 0 && lane == 0) report(status, kCheckLogits);
-    m = wave_max(m);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      int e = lane + 64 * i;
-      if (e < E) s += expf(v[i] - m);
-    }
-    s = wave_sum(s);
-    const float inv_s = 1.0f / s;
-    uint32_t taken = 0;
-    float gsum = 0.f;
-    float* graw = RENORM ? renorm_buf + (threadIdx.x >> 6) * kRouterMaxK : renorm_buf;  // this wave's raw gates
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-          bv = v[i];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o, 64);
-        int oe = __shfl_xor(be, o, 64);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == 0) {
-        const float g = SIGM ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) * inv_s;
-        idx_out[(int64_t)t * k + j] = be;
-        idx_saved[(int64_t)t * k + j] = be;
-        if constexpr (RENORM) {
-          graw[j] = g;
-          gsum += g;
-        } else {
-          gate_out[(int64_t)t * k + j] = g;
-          gate_saved[(int64_t)t * k + j] = g;
-        }
-      }
-    }
-    if (lane == 0) {
-      lse_out[t] = m + logf(s);
-      if constexpr (RENORM) {
-        for (int j = 0; j < k; ++j) {
-          const float g = graw[j] / gsum;
-          gate_out[(int64_t)t * k + j] = g;
-          gate_saved[(int64_t)t * k + j] = g;
-        }
-      }
-    }
-  }
+  float* graw = RENORM ? renorm_buf + (threadIdx.x >> 6) * kRouterMaxK : renorm_buf;  // this wave's raw gates
+  for (int t = wave; t < T; t += nwaves)
+    route_token<EPL, SIGM, RENORM>(logits, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out, status, graw);
 }
 
 template <bool SIGM, bool RENORM>
@@ -213,36 +226,20 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
 // block scans the totals over experts (offsets), each share then writes its
 // chunk bases, and the row-tile prefix of the local experts is written for
 // each tile height.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restrict__ chunk_counts,
-                                                         int nchunks, int E, int eb, int ee,
-                                                         int32_t* __restrict__ chunk_base,
-                                                         int32_t* __restrict__ counts_out,
-                                                         int32_t* __restrict__ offsets_out,
-                                                         int32_t* __restrict__ offsets_saved,
-                                                         int32_t* __restrict__ tile_prefix,
-                                                         int32_t* __restrict__ expert_order) {
+// Offsets, counts, tile prefixes and the heaviest-first weight-gradient
+// schedule of the experts, from each expert's pair count: called by every
+// thread of a 1024-thread block with run = the count of expert threadIdx.x
+// (0 past E).  Writes s_offE[e] (the expert's first row, visible to the
+// whole block on return) and returns it.
+__device__ int scan_and_schedule(int run, int E, int eb, int ee, int32_t* __restrict__ counts_out,
+                                 int32_t* __restrict__ offsets_out, int32_t* __restrict__ offsets_saved,
+                                 int32_t* __restrict__ tile_prefix, int32_t* __restrict__ expert_order,
+                                 int32_t* s_offE) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t tsum[kNumTileBM][16];
-  __shared__ int32_t s_part[1024], s_offE[1024];
   const int e = threadIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  // shares: thread (tg, te) = (threadIdx.x / E, threadIdx.x % E), tg < G
-  const int G = 1024 / E;
-  const int te = threadIdx.x % E, tg = threadIdx.x / E;
-  const bool share = tg < G;
-  const int c0 = share ? (int)((int64_t)nchunks * tg / G) : 0;
-  const int c1 = share ? (int)((int64_t)nchunks * (tg + 1) / G) : 0;
-  {
-    int part = 0;
-#pragma unroll 8
-    for (int c = c0; c < c1; ++c) part += chunk_counts[(int64_t)c * E + te];
-    if (share) s_part[threadIdx.x] = part;
-  }
-  __syncthreads();
-  int run = 0;  // expert e's total
-  if (e < E)
-    for (int q = 0; q < G; ++q) run += s_part[q * E + e];
   // exclusive scan of run over e (1024 threads = 16 waves)
   int incl = run;
 #pragma unroll
@@ -299,18 +296,6 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
     s_off[i_loc] = off;
   }
   __syncthreads();
-  if (share) {
-    // chunk bases of this share: the expert's first row, the counts of the
-    // earlier shares, then a running sum over the share's chunks
-    int r = s_offE[te];
-    for (int q = 0; q < tg; ++q) r += s_part[q * E + te];
-#pragma unroll 8
-    for (int c = c0; c < c1; ++c) {
-      const int v = chunk_counts[(int64_t)c * E + te];
-      chunk_base[(int64_t)c * E + te] = r;
-      r += v;
-    }
-  }
   if (i_loc >= 0 && i_loc < E_loc) {
     int rank = 0;
     for (int q = 0; q < E_loc; ++q) {
@@ -358,6 +343,50 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restri
       if (i_loc == 0) tp[0] = 0;
     }
   }
+  return off;
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                         int nchunks, int E, int eb, int ee,
+                                                         int32_t* __restrict__ chunk_base,
+                                                         int32_t* __restrict__ counts_out,
+                                                         int32_t* __restrict__ offsets_out,
+                                                         int32_t* __restrict__ offsets_saved,
+                                                         int32_t* __restrict__ tile_prefix,
+                                                         int32_t* __restrict__ expert_order) {
+  __shared__ int32_t s_part[1024], s_offE[1024];
+  const int e = threadIdx.x;
+  // shares: thread (tg, te) = (threadIdx.x / E, threadIdx.x % E), tg < G
+  const int G = 1024 / E;
+  const int te = threadIdx.x % E, tg = threadIdx.x / E;
+  const bool share = tg < G;
+  const int c0 = share ? (int)((int64_t)nchunks * tg / G) : 0;
+  const int c1 = share ? (int)((int64_t)nchunks * (tg + 1) / G) : 0;
+  {
+    int part = 0;
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) part += chunk_counts[(int64_t)c * E + te];
+    if (share) s_part[threadIdx.x] = part;
+  }
+  __syncthreads();
+  int run = 0;  // expert e's total
+  if (e < E)
+    for (int q = 0; q < G; ++q) run += s_part[q * E + e];
+  const int off = scan_and_schedule(run, E, eb, ee, counts_out, offsets_out, offsets_saved, tile_prefix,
+                                    expert_order, s_offE);
+  (void)off;
+  if (share) {
+    // chunk bases of this share: the expert's first row, the counts of the
+    // earlier shares, then a running sum over the share's chunks
+    int r = s_offE[te];
+    for (int q = 0; q < tg; ++q) r += s_part[q * E + te];
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const int v = chunk_counts[(int64_t)c * E + te];
+      chunk_base[(int64_t)c * E + te] = r;
+      r += v;
+    }
+  }
 }
 
 // Pass 3: stable placement.  Each wave re-walks its chunk in pair order with a
@@ -395,6 +424,112 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     if (inb) row_of_pair[p] = row;
     if (valid) pair_of_row[row] = (int32_t)p;
   }
+}
+
+// ------------------------------------------------------------------ small-T path
+// Router and counting sort in one workgroup of 1024 threads, for calls of at
+// most kSmallTokens tokens and kSmallPairs token-expert pairs (a decode-style
+// step): the status words
+// are cleared, each of the 16 waves routes every 16th token (route_token, as
+// the router kernel), then the block counts the local pairs per expert,
+// scans them (scan_and_schedule, as the scan kernel) and places the pairs in
+// chunks of 1024, stably: a pair's row is its expert's first row, plus the
+// pairs of that expert in earlier chunks, in earlier waves of its chunk and in
+// lower lanes of its wave.  The outputs are those of the router kernel and
+// the three counting-sort kernels, bit for bit, in one launch instead of five.
+template <int EPL, bool SIGM, bool RENORM>
+__global__ __launch_bounds__(1024) void route_sort_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int eb, int ee, int nbits,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out, int32_t* __restrict__ idx_saved,
+    float* __restrict__ gate_saved, float* __restrict__ lse_out, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ offsets_saved, int32_t* __restrict__ tile_prefix,
+    int32_t* __restrict__ expert_order, int32_t* __restrict__ row_of_pair, int32_t* __restrict__ pair_of_row,
+    int32_t* __restrict__ status) {
+  // s_wcnt[w][e]: the pairs of expert e in wave w of the current chunk; while
+  // the tokens are routed, wave w's row holds its raw gates (RENORM)
+  __shared__ int32_t s_wcnt[16][1024];
+  __shared__ int32_t s_hist[1024], s_base[1024], s_offE[1024];
+  const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+  if (tid < 2) status[tid] = 0;
+  __syncthreads();  // cleared before any check reports
+  static_assert(kRouterMaxK <= 1024, "a wave's raw gates fit its row of s_wcnt");
+  float* graw = reinterpret_cast<float*>(&s_wcnt[w][0]);
+  for (int t = w; t < T; t += 16)
+    route_token<EPL, SIGM, RENORM>(logits, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out, status, graw);
+  if (tid < E) s_hist[tid] = 0;
+  __syncthreads();  // the block's index writes are visible to the block
+  const int npairs = T * k;
+  for (int p = tid; p < npairs; p += 1024) {
+    const int e = idx_saved[p];
+    if (e >= eb && e < ee) atomicAdd(&s_hist[e], 1);
+  }
+  __syncthreads();
+  const int run = tid < E ? s_hist[tid] : 0;
+  scan_and_schedule(run, E, eb, ee, counts_out, offsets_out, offsets_saved, tile_prefix, expert_order, s_offE);
+  if (tid < E) s_base[tid] = s_offE[tid];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < npairs; c0 += 1024) {
+    for (int e = lane; e < E; e += 64) s_wcnt[w][e] = 0;
+    __syncthreads();  // s_wcnt cleared; s_base holds this chunk's first rows
+    const int p = c0 + tid;
+    const int e = p < npairs ? idx_saved[p] : -1;
+    const bool valid = e >= eb && e < ee;
+    const uint64_t m = peer_mask(e, valid, nbits);
+    if (valid && lane == __ffsll((unsigned long long)m) - 1) s_wcnt[w][e] = __popcll(m);
+    __syncthreads();
+    int row = -1;
+    if (valid) {
+      row = s_base[e] + __popcll(m & lt);
+      for (int q = 0; q < w; ++q) row += s_wcnt[q][e];
+    }
+    int chunk_total = 0;
+    if (tid < E)
+      for (int q = 0; q < 16; ++q) chunk_total += s_wcnt[q][tid];
+    __syncthreads();  // s_base and s_wcnt read for this chunk
+    if (tid < E) s_base[tid] += chunk_total;
+    if (p < npairs) row_of_pair[p] = row;
+    if (valid) pair_of_row[row] = p;
+  }
+}
+
+template <bool SIGM, bool RENORM>
+static void launch_small_variant(hipStream_t s, const float* logits, int T, int E, int k, int eb, int ee, int nbits,
+                                 int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved,
+                                 float* lse, int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
+                                 int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
+                                 int32_t* pair_of_row, int32_t* status) {
+#define MOK_SMALL(EPLV)                                                                                         \
+  hipLaunchKernelGGL((route_sort_small_kernel<EPLV, SIGM, RENORM>), dim3(1), dim3(1024), 0, s, logits, T, E, k, eb, \
+                     ee, nbits, idx_out, gate_out, idx_saved, gate_saved, lse, counts_out, offsets_out,          \
+                     offsets_saved, tile_prefix, expert_order, row_of_pair, pair_of_row, status)
+  if (E <= 64) MOK_SMALL(1);
+  else if (E <= 128) MOK_SMALL(2);
+  else if (E <= 256) MOK_SMALL(4);
+  else if (E <= 512) MOK_SMALL(8);
+  else MOK_SMALL(16);
+#undef MOK_SMALL
+}
+
+hipError_t launch_route_sort_small(const float* logits, int T, int E, int k, int gating, int eb, int ee,
+                                   int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved,
+                                   float* lse, int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
+                                   int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
+                                   int32_t* pair_of_row, int32_t* status, hipStream_t s) {
+  if (T < 1 || T > kSmallTokens || (int64_t)T * k > kSmallPairs) return hipErrorInvalidValue;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  switch (gating & (kGateSigmoid | kGateRenorm)) {
+#define MOK_SMALL_G(SG, RN)                                                                                     \
+  launch_small_variant<SG, RN>(s, logits, T, E, k, eb, ee, nbits, idx_out, gate_out, idx_saved, gate_saved, lse, \
+                               counts_out, offsets_out, offsets_saved, tile_prefix, expert_order, row_of_pair,     \
+                               pair_of_row, status)
+    case 0: MOK_SMALL_G(false, false); break;
+    case kGateSigmoid: MOK_SMALL_G(true, false); break;
+    case kGateRenorm: MOK_SMALL_G(false, true); break;
+    default: MOK_SMALL_G(true, true); break;
+#undef MOK_SMALL_G
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee, int nchunks,

@@ -25,6 +25,7 @@ class MoeShape:
     save_for_backward: bool = False
     gating: str = "softmax"       # router affinities: "softmax" or "sigmoid"
     renorm: bool = False          # gates renormalised over the k chosen experts
+    separate_route_sort: bool = False  # never the one-launch router + sort of small calls
 
     @property
     def e_end(self):
@@ -39,7 +40,8 @@ class MoeShape:
             raise ValueError(f"gating must be 'softmax' or 'sigmoid', not {self.gating!r}")
         flags = ((mok.MOK_FLAG_SAVE_FOR_BACKWARD if self.save_for_backward else 0)
                  | (mok.MOK_FLAG_SIGMOID_GATES if self.gating == "sigmoid" else 0)
-                 | (mok.MOK_FLAG_RENORM_GATES if self.renorm else 0))
+                 | (mok.MOK_FLAG_RENORM_GATES if self.renorm else 0)
+                 | (mok.MOK_FLAG_SEPARATE_ROUTE_SORT if self.separate_route_sort else 0))
         return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
                                self.minibatch_rows, self.ring_bytes, flags)
 

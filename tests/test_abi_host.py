@@ -52,7 +52,8 @@ def test_workspace_query_rejects_bad_configs(over, k):
 
 
 @pytest.mark.parametrize("flags", [mok.MOK_FLAG_SIGMOID_GATES, mok.MOK_FLAG_RENORM_GATES,
-                                   mok.MOK_FLAG_SIGMOID_GATES | mok.MOK_FLAG_RENORM_GATES | mok.MOK_FLAG_SAVE_FOR_BACKWARD])
+                                   mok.MOK_FLAG_SIGMOID_GATES | mok.MOK_FLAG_RENORM_GATES | mok.MOK_FLAG_SAVE_FOR_BACKWARD,
+                                   mok.MOK_FLAG_SEPARATE_ROUTE_SORT])
 def test_workspace_query_accepts_router_variants(flags):
     ws, sv = mok.mok_moe_workspace_query(_cfg(flags=flags), 2)
     assert ws > 0 and sv > 0
