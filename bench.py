@@ -426,12 +426,15 @@ def measure(name: str, args, extras: bool):
     return result, w, inp, (K, Wm, ev, sh)
 
 
-def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256, 512)):
+def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
     """Forward-only calls of a few tokens on the training layer's weights (a
-    decode step): microseconds per call with the router and the counting sort
-    fused into one launch (the default for T * k <= 4096) and as separate
-    launches, eagerly and replayed from a HIP graph, plus the routing part
-    alone (the router stage, or router + sort) from the library's stage events."""
+    decode step), microseconds per call, eagerly and replayed from a HIP
+    graph: the small-call path (router and sort in one launch up to T 32,
+    weight-streaming UP and DOWN up to 4096 pairs) against the tiled GEMMs
+    with separate router and sort launches.  For the small-call path also
+    the per-stage times (library stage events) and the HBM roofline of the
+    two GEMMs: the weights of the experts the call touches, read once, plus
+    their activation rows, over 8 TB/s."""
     import torch
 
     import workloads as W
@@ -445,10 +448,10 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256, 512)):
         wT = W.scaled(w.name, T=T)
         small = W.make_inputs(wT, device=dev, weights=False)
         row = {"pairs": T * w.k}
-        for sep in (False, True):
-            tag = "separate" if sep else "fused"
+        for tag, tiled in (("small_path", False), ("tiled", True)):
             buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision,
-                                      separate_route_sort=sep), device=dev)
+                                      separate_route_sort=tiled, gemm_path="tiled" if tiled else "auto"),
+                             device=dev)
 
             def fwd(events=None, stream=sh):
                 buf.cfg.stage_events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
@@ -462,16 +465,31 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256, 512)):
             for _ in range(n):
                 fwd()
             ev.record(b, sh)
-            row[f"{tag}_us"] = round(ev.elapsed_ms(a, b) * 1e3 / n, 2)
-            st = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(n)]
-            for i in range(n):
-                fwd(st[i])
-            torch.cuda.synchronize()
-            stages = ["router"] + ([] if not sep else ["sort"])
-            row[f"{tag}_route_sort_us"] = round(sum(
-                ev.elapsed_ms(st[i][2 * mok.STAGES.index(g)], st[i][2 * mok.STAGES.index(g) + 1])
-                for i in range(n) for g in stages) * 1e3 / n, 2)
-            buf.cfg.stage_events = None
+            rec = {"us": round(ev.elapsed_ms(a, b) * 1e3 / n, 2)}
+            if not tiled:
+                st = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(n)]
+                for i in range(n):
+                    fwd(st[i])
+                torch.cuda.synchronize()
+                ran = ["router", "gemm_up", "gemm_down", "combine"] + (["sort"] if T > 32 else [])
+                stage_us = {g: round(sum(ev.elapsed_ms(st[i][2 * mok.STAGES.index(g)],
+                                                       st[i][2 * mok.STAGES.index(g) + 1])
+                                         for i in range(n)) * 1e3 / n, 2) for g in ran}
+                rec["stages_us"] = stage_us
+                buf.cfg.stage_events = None
+                counts = buf.counts.cpu()
+                ne = int((counts > 0).sum())
+                P = int(counts.sum())
+                up_b = ne * 2 * w.F * w.d * 2 + T * w.d * 2 + P * w.F * 2
+                dn_b = ne * w.d * w.F * 2 + P * w.F * 2 + P * w.d * 2
+                rec["experts_touched"] = ne
+                rec["gemm_hbm"] = {
+                    "up": {"bytes": up_b, "gbs": round(up_b / (stage_us["gemm_up"] * 1e-6) / 1e9, 1),
+                           "frac": round(up_b / (stage_us["gemm_up"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)},
+                    "down": {"bytes": dn_b, "gbs": round(dn_b / (stage_us["gemm_down"] * 1e-6) / 1e9, 1),
+                             "frac": round(dn_b / (stage_us["gemm_down"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)}}
+                floor = (ne * 3 * w.F * w.d * 2 + 2 * T * w.d * 2) / (PEAK_HBM_GBS * 1e9) * 1e6
+                rec["floor_us"] = round(floor, 2)
             side = torch.cuda.Stream(dev)
             side.wait_stream(torch.cuda.current_stream(dev))
             with torch.cuda.stream(side):
@@ -488,10 +506,13 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256, 512)):
             for _ in range(n):
                 graph.replay()
             ev.record(b, sh)
-            row[f"{tag}_graph_us"] = round(ev.elapsed_ms(a, b) * 1e3 / n, 2)
+            rec["graph_us"] = round(ev.elapsed_ms(a, b) * 1e3 / n, 2)
             del graph, buf
+            row[tag] = rec
+        row["speedup"] = round(row["tiled"]["us"] / row["small_path"]["us"], 3)
         out[str(T)] = row
-    return {"workload": f"{w.name} weights, forward only, T tokens per call", "calls": n, "per_T": out}
+    return {"workload": f"{w.name} weights (d={w.d} E={w.E} k={w.k} F={w.F}), forward only, T tokens per call",
+            "calls": n, "per_T": out}
 
 
 def main():

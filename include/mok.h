@@ -89,6 +89,22 @@ typedef enum {
  * and MOK_STAGE_SORT is not run.  Results are bitwise those of the separate
  * router and sort launches, which this flag selects at any size. */
 #define MOK_FLAG_SEPARATE_ROUTE_SORT 0x8u
+/* Expert products of small BF16 forward calls.  With few rows per expert the
+ * two forward products are bound by reading the chosen experts' weights
+ * ([kucoin §01]: the expert-grouped GEMM; [fluid], section "Quand la
+ * communication devient le vrai problème", names an MoE inference decode
+ * kernel as earlier work), so a call of the whole layer with at most 4096
+ * token-expert pairs and d, F multiples of 128 may run them as
+ * weight-streaming kernels: each weight row read once per 32-row tile straight
+ * into registers, the K range split over up to four waves whose fp32 partial
+ * sums are added in a fixed order.  Without either flag below they run when
+ * T * k <= 4 * (expert_end - expert_begin) (a few rows per expert on
+ * average); MOK_FLAG_STREAM_GEMMS selects them for every such call,
+ * MOK_FLAG_TILED_GEMMS never (both: MOK_ERR_INVALID_ARG).  The results are
+ * deterministic and within the BF16 tolerance of the oracle, but not bitwise
+ * those of the tiled kernels (another summation order). */
+#define MOK_FLAG_TILED_GEMMS 0x10u
+#define MOK_FLAG_STREAM_GEMMS 0x20u
 
 typedef struct mok_moe_config {
   int32_t T;                 /* tokens in this call (>= 0)                      */

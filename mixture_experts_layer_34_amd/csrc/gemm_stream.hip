@@ -1,0 +1,253 @@
+// Weight-streaming expert GEMMs for forward calls with few rows per expert (a
+// decode step).  With tens of rows per expert the two forward products are
+// bound by reading the experts' weights from HBM once, not by the matrix
+// cores; the tiled kernels' 256-row tiles would then spend most of their MFMA
+// work on padding and leave most compute units idle.  Here a workgroup takes
+// one (32-row tile of an expert, 16 * NWN weight rows) unit at a time and
+// streams those weight rows once, straight from HBM into registers:
+//   UP    H = silu(X W1^T) * (X W3^T)   (x rows pulled through pair_of_row;
+//                                         A = X W1^T and B = X W3^T saved
+//                                         when the call saves for backward)
+//   DOWN  Y = H W2^T
+// Both weight matrices hold K contiguous per output column (W1, W3: [F, d];
+// W2: [d, F]), so a lane reads 64 contiguous bytes of one weight row per
+// 128-K chunk.  Products on v_mfma_f32_16x16x32_bf16: the lane holding
+// weight row n (lane % 16) and K-group g (lane / 16) feeds the MFMA B operand,
+// the lane holding activation row lane % 16 of the same K-group the A
+// operand; inside a 128-K chunk, K-group g's 32 elements are the MFMA K steps
+// s = 0..3 (eight each), the same K permutation on both operands, so every
+// product term is summed exactly once.  KS waves split the K range of one
+// 16-column group; their fp32 partial sums meet in LDS and are added in wave
+// order (0 + 1 + 2 + 3), so the result is run-to-run identical.
+#include "gemm_common.h"
+#include "gemm_pipe.h"
+#include "mok_device.h"
+
+namespace mok {
+namespace {
+
+constexpr int kChunkK = 128;  // K elements per lane-group round (64 bytes per lane)
+
+// Chunks in flight ahead of the one being multiplied (registers: NB + RG
+// 16-byte quads x 4 per chunk and lane).  One: the occupancy it leaves (three
+// workgroups per CU for UP with one row group) moves more bytes than deeper
+// rings at two (same-box A/B at d 4096, E 128, k 8, F 1536: UP 36.0 / 46.0 /
+// 46.2 us at T 1 for depths 1 / 2 / 3, 166 / 185 / 186 us at T 8).  DOWN
+// splits K over two waves at most (F / 2 per wave; splits 1 / 2 / 4: 41.1 /
+// 22.2 / 23.6 us at T 1, 260 / 256 / 272 us at T 64).  For scale: a plain
+// grid-stride read of 4 GiB on the same box reaches 5.3-6.3 TB/s; UP at T 8
+// moves 5.9 TB/s.
+#ifndef MOK_STREAM_DEPTH
+#define MOK_STREAM_DEPTH 1
+#endif
+#ifndef MOK_STREAM_KS_DOWN
+#define MOK_STREAM_KS_DOWN 2
+#endif
+
+// RG: 16-row groups per tile that the kernel multiplies (1 when no expert can
+// have more than 16 rows, T <= 16; else 2, the whole 32-row tile).
+template <int KIND, int KS, int RG>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(GroupedGemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NB = Traits<KIND>::NB;  // UP pairs W1 with W3
+  constexpr int NWN = 4 / KS;           // 16-column groups per workgroup
+  constexpr int D = MOK_STREAM_DEPTH, NBUF = D + 1;
+  const GemmGeom G = geom_of<KIND>(a.d, a.F);
+  const int N = G.N, K = G.K;
+  const int ntn = N / (16 * NWN);
+  const int E_loc = a.E_loc;
+  const int32_t* tp = a.tile_prefix + kStreamTileTable * (E_loc + 1);
+  const int total = sload(tp + E_loc) * ntn;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = w % NWN, kr = w / NWN;
+  const int kw = K / KS;  // this wave's K range: [kr * kw, (kr + 1) * kw)
+  const int nchunk = kw / kChunkK;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  __shared__ f32x4_t red[KS > 1 ? (KS - 1) * NWN : 1][RG][NB][64];
+
+  // XCD-aware order: workgroup b (on XCD b % 8) takes the units of the
+  // contiguous run [x G/8, (x+1) G/8) of each round of G units, so that the
+  // row tiles of one expert and weight rows (adjacent units) share one L2.
+  const int Gd = gridDim.x;
+  const int vb = (Gd % 8 == 0) ? (blockIdx.x % 8) * (Gd / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int u = vb; u < total; u += Gd) {
+    // expert: the last local expert whose first unit is at or before u (its
+    // units [tp[e] ntn, tp[e+1] ntn), column group major, row tile minor)
+    const int q = u / ntn;
+    int lo = 0, hi = E_loc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sload(tp + mid) <= q) lo = mid; else hi = mid - 1;
+    }
+    const int t0 = sload(tp + lo), nte = sload(tp + lo + 1) - t0;
+    const int li = u - t0 * ntn;
+    const int mt = li % nte, nt = li / nte;
+    const int e = a.eb + lo;
+    const int row0 = sload(a.offsets + e) + mt * kStreamTileRows;
+    const int erow_end = sload(a.offsets + e + 1);
+    const int row_end = erow_end < row0 + 16 * RG ? erow_end : row0 + 16 * RG;
+    const bool two = RG == 2 && row_end - row0 > 16;  // the tile's second 16-row group is used
+    const int n0 = (nt * NWN + cg) * 16;
+
+    // operand rows of this lane, at its first K element
+    const int64_t kb = (int64_t)kr * kw + 32 * g4;
+    const bf16_t* bp[NB];
+    bp[0] = (const bf16_t*)a.B0 + (int64_t)lo * G.b_estride + (int64_t)(n0 + r16) * G.ldb + kb;
+    if constexpr (NB == 2) bp[1] = (const bf16_t*)a.B1 + (int64_t)lo * G.b_estride + (int64_t)(n0 + r16) * G.ldb + kb;
+    const bf16_t* ap[RG];
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+      int r = row0 + 16 * gi + r16;
+      if (r >= row_end) r = row0;  // padding rows repeat the first row; never stored
+      int64_t src = r;
+      if constexpr (KIND == KIND_UP) src = a.gather_rows[r] / a.k_top;  // pull dispatch: the token's x row
+      ap[gi] = (const bf16_t*)a.A + src * G.lda + kb;
+    }
+
+    f32x4_t acc[RG][NB];
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[gi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t bq[NBUF][NB][4], aq[NBUF][RG][4];
+    auto load = [&](int buf, int c) {
+      const int64_t ko = (int64_t)c * kChunkK;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bq[buf][b][j] = *reinterpret_cast<const u32x4_t*>(bp[b] + ko + 8 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) aq[buf][0][j] = *reinterpret_cast<const u32x4_t*>(ap[0] + ko + 8 * j);
+      if constexpr (RG == 2)
+        if (two)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) aq[buf][RG - 1][j] = *reinterpret_cast<const u32x4_t*>(ap[RG - 1] + ko + 8 * j);
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[buf][b][s]);
+          acc[0][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aq[buf][0][s]), bf,
+                                                              acc[0][b], 0, 0, 0);
+          if constexpr (RG == 2)
+            if (two)
+              acc[RG - 1][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, aq[buf][RG - 1][s]), bf, acc[RG - 1][b], 0, 0, 0);
+        }
+    };
+    // a ring of NBUF register buffers: chunk c + D is in flight while c is used
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < nchunk) load(i, i);
+    for (int c = 0; c < nchunk; c += NBUF) {
+#pragma unroll
+      for (int bb = 0; bb < NBUF; ++bb) {
+        if (c + bb < nchunk) {
+          if (c + bb + D < nchunk) load((bb + D) % NBUF, c + bb + D);
+          compute(bb);
+        }
+      }
+    }
+
+    if constexpr (KS > 1) {
+      if (kr > 0)
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) red[(kr - 1) * NWN + cg][gi][b][lane] = acc[gi][b];
+      __syncthreads();
+      if (kr == 0)
+#pragma unroll
+        for (int qk = 1; qk < KS; ++qk)
+#pragma unroll
+          for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[gi][b] += red[(qk - 1) * NWN + cg][gi][b][lane];
+      __syncthreads();  // the partials are read before the next unit writes them
+    }
+    if (kr == 0) {
+      // D layout of the 16x16 MFMA: lane holds column lane % 16, rows 4 (lane / 16) + i
+      const int col = n0 + r16;
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = row0 + 16 * gi + 4 * g4 + i;
+          if (row < row_end) {
+            const int64_t o = (int64_t)row * N + col;
+            if constexpr (KIND == KIND_UP) {
+              const float va = acc[gi][0][i], vb_ = acc[gi][1][i];
+              ((bf16_t*)a.out0)[o] = f2bf(va * sigmoidf_(va) * vb_);
+              if (a.save) {
+                ((bf16_t*)a.save_a)[o] = f2bf(va);
+                ((bf16_t*)a.save_b)[o] = f2bf(vb_);
+              }
+            } else {
+              ((bf16_t*)a.out0)[o] = f2bf(acc[gi][0][i]);
+            }
+          }
+        }
+    }
+  }
+#endif
+}
+
+template <int KIND, int KS, int RG>
+hipError_t run_stream(const GroupedGemmArgs& g, hipStream_t s) {
+  constexpr int NWN = 4 / KS;
+  const GemmGeom G = geom_of<KIND>(g.d, g.F);
+  const int64_t ntn = G.N / (16 * NWN);
+  const int64_t worst = ((g.P_max + kStreamTileRows - 1) / kStreamTileRows + g.E_loc) * ntn;
+  // persistent workgroups: as many as fit on the device at once
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_gemm_kernel<KIND, KS, RG>, 256, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    return n;
+  }();
+  const int64_t cap = (int64_t)kNumCUs * per_cu;
+  const int blocks = (int)(worst < cap ? worst : cap);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((stream_gemm_kernel<KIND, KS, RG>), dim3(blocks), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int KIND, int RG>
+hipError_t run_stream_k(int ks, const GroupedGemmArgs& g, hipStream_t s) {
+  switch (ks) {
+    case 4: return run_stream<KIND, 4, RG>(g, s);
+    case 2: return run_stream<KIND, 2, RG>(g, s);
+    case 1: return run_stream<KIND, 1, RG>(g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int stream_ksplit(int K) {
+  if (K % (kChunkK * 4) == 0) return 4;
+  if (K % (kChunkK * 2) == 0) return 2;
+  if (K % kChunkK == 0) return 1;
+  return 0;
+}
+
+hipError_t gemm_stream_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {
+  // an expert holds at most one row per token: with T <= 16 every tile has
+  // at most 16 rows
+  const bool one_group = g.P_max / (g.k_top > 0 ? g.k_top : 1) <= 16;
+  if (kind == KIND_UP) {
+    const int ks = stream_ksplit(g.d);
+    return one_group ? run_stream_k<KIND_UP, 1>(ks, g, s) : run_stream_k<KIND_UP, 2>(ks, g, s);
+  }
+  if (kind == KIND_DOWN) {
+    int ks = stream_ksplit(g.F);
+    if (ks > MOK_STREAM_KS_DOWN) ks = MOK_STREAM_KS_DOWN;
+    return one_group ? run_stream_k<KIND_DOWN, 1>(ks, g, s) : run_stream_k<KIND_DOWN, 2>(ks, g, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mok

@@ -43,8 +43,9 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
     return MOK_ERR_INVALID_ARG;
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
   if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES |
-                  MOK_FLAG_SEPARATE_ROUTE_SORT))
+                  MOK_FLAG_SEPARATE_ROUTE_SORT | MOK_FLAG_TILED_GEMMS | MOK_FLAG_STREAM_GEMMS))
     return MOK_ERR_INVALID_ARG;
+  if ((c.flags & MOK_FLAG_TILED_GEMMS) && (c.flags & MOK_FLAG_STREAM_GEMMS)) return MOK_ERR_INVALID_ARG;
   if (c.precision == MOK_PREC_MXFP8) {
     // every E8M0 scale array (x and H rows, each weight matrix) fits a 32-bit buffer range
     const int64_t Tk = (int64_t)c.T * k, kmax = c.d > c.ffn ? c.d : c.ffn;
@@ -169,6 +170,24 @@ inline void mark_empty_stage(const mok_moe_config& c, hipStream_t s, int stage) 
 // GEMM loads (32-bit buffer offsets: x must stay below 2 GB).
 inline bool fused_pull(const mok_moe_config& c) {
   return c.precision == MOK_PREC_BF16 && c.minibatch_rows == 0 && (int64_t)c.T * c.d * 2 < (int64_t(1) << 31);
+}
+
+// The forward's UP and DOWN run the weight-streaming kernels: bf16 with pull
+// dispatch, at most kStreamMaxPairs token-expert pairs, K dimensions in whole
+// 128-element chunks; then MOK_FLAG_STREAM_GEMMS selects them, and without
+// either GEMM flag they run while the call has at most four rows per local
+// expert on average (each 32-row tile reads its expert's weights again, so
+// with more rows the tiled kernels win: same-box at d 4096, E 128, k 8,
+// F 1536, 725 / 742 us at T 64 against 968 / 917 us at T 128, streaming /
+// tiled).
+constexpr int64_t kStreamMaxPairs = 4096;
+constexpr int64_t kStreamAutoRowsPerExpert = 4;
+inline bool streaming_gemms(const mok_moe_config& c, int32_t k) {
+  const int64_t P = (int64_t)c.T * k, E_loc = c.expert_end - c.expert_begin;
+  if (!fused_pull(c) || (c.flags & MOK_FLAG_TILED_GEMMS) || P > kStreamMaxPairs || stream_ksplit(c.d) == 0 ||
+      stream_ksplit(c.ffn) == 0)
+    return false;
+  return (c.flags & MOK_FLAG_STREAM_GEMMS) || P <= kStreamAutoRowsPerExpert * E_loc;
 }
 
 // The call owns every expert (no remote slots).
@@ -335,7 +354,8 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
     g.save_a = at<void>(saved, sl.A);
     g.save_b = at<void>(saved, sl.B);
     g.save = (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ? 1 : 0;
-    MOK_STAGE(MOK_STAGE_GEMM_UP, run_gemm(c.precision, KIND_UP, g, s));
+    const bool stream = streaming_gemms(c, k);
+    MOK_STAGE(MOK_STAGE_GEMM_UP, stream ? gemm_stream_bf16(KIND_UP, g, s) : run_gemm(c.precision, KIND_UP, g, s));
     GroupedGemmArgs g2 = g;
     g2.A = at<void>(saved, sl.H);
     g2.B0 = W2;
@@ -343,7 +363,8 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
     g2.out0 = at<void>(saved, sl.Y);
     g2.save = 0;
     g2.gather_rows = nullptr;
-    MOK_STAGE(MOK_STAGE_GEMM_DOWN, run_gemm(c.precision, KIND_DOWN, g2, s));
+    MOK_STAGE(MOK_STAGE_GEMM_DOWN,
+              stream ? gemm_stream_bf16(KIND_DOWN, g2, s) : run_gemm(c.precision, KIND_DOWN, g2, s));
   }
   MOK_STAGE(MOK_STAGE_COMBINE, launch_combine(at<void>(saved, sl.Y), s_gate, s_rop, T, k, d, bf16, all_local(c), out,
                                               P_max, status, s));

@@ -10,8 +10,12 @@ namespace mok {
 // Pairs handled by one wave in the counting sort.
 constexpr int kSortChunk = 512;
 // Row-tile heights for which per-expert tile prefixes are precomputed.
-constexpr int kNumTileBM = 3;
-constexpr int kTileBM[kNumTileBM] = {64, 128, 256};
+constexpr int kNumTileBM = 4;
+constexpr int kTileBM[kNumTileBM] = {64, 128, 256, 32};
+// The weight-streaming forward GEMMs take 32-row tiles (table 3).
+constexpr int kStreamTileTable = 3;
+constexpr int kStreamTileRows = 32;
+constexpr int kNumCUs = 256;  // MI355X compute units
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -135,6 +139,15 @@ struct GroupedGemmArgs {
 // 0 UP (H = silu(X W1^T) * (X W3^T)), 1 DOWN (Y = H W2^T), 2 DH (dA, dB from
 // dY W2), 3 DX (dA W1 + dB W3), 4 DW2 (dY^T H), 5 DW13 (dA^T X, dB^T X).
 hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
+
+// Weight-streaming bf16 UP and DOWN for calls with few rows per expert: one
+// workgroup per (32-row tile, 16-64 weight rows) unit, the weight rows read
+// once per tile straight into registers, 16x16x32 MFMA.  Same arguments and
+// outputs as gemm_bf16's UP (with pull dispatch: gather_rows set) and DOWN.
+// stream_ksplit(K): the waves splitting K (4, 2 or 1), 0 when K is not a
+// multiple of 128 (then only the tiled kernels apply).
+int stream_ksplit(int K);
+hipError_t gemm_stream_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
 
 // One step of the ring-buffer minibatch pipeline (bf16): in a single launch,
 // mover tiles copy the rows of minibatch m+1 into their ring slot, compute

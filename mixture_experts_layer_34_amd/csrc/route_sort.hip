@@ -266,7 +266,7 @@ __device__ int scan_and_schedule(int run, int E, int eb, int ee, int32_t* __rest
   }
   __syncthreads();
   int wbase = 0;
-  int tbase[kNumTileBM] = {0, 0, 0};
+  int tbase[kNumTileBM] = {};
   for (int q = 0; q < w; ++q) {
     wbase += wsum[q];
 #pragma unroll

@@ -26,6 +26,7 @@ class MoeShape:
     gating: str = "softmax"       # router affinities: "softmax" or "sigmoid"
     renorm: bool = False          # gates renormalised over the k chosen experts
     separate_route_sort: bool = False  # never the one-launch router + sort of small calls
+    gemm_path: str = "auto"            # forward expert products: "auto", "tiled" or "stream" (small calls)
 
     @property
     def e_end(self):
@@ -38,10 +39,14 @@ class MoeShape:
     def config(self) -> mok.mok_moe_config:
         if self.gating not in ("softmax", "sigmoid"):
             raise ValueError(f"gating must be 'softmax' or 'sigmoid', not {self.gating!r}")
+        if self.gemm_path not in ("auto", "tiled", "stream"):
+            raise ValueError(f"gemm_path must be 'auto', 'tiled' or 'stream', not {self.gemm_path!r}")
         flags = ((mok.MOK_FLAG_SAVE_FOR_BACKWARD if self.save_for_backward else 0)
                  | (mok.MOK_FLAG_SIGMOID_GATES if self.gating == "sigmoid" else 0)
                  | (mok.MOK_FLAG_RENORM_GATES if self.renorm else 0)
-                 | (mok.MOK_FLAG_SEPARATE_ROUTE_SORT if self.separate_route_sort else 0))
+                 | (mok.MOK_FLAG_SEPARATE_ROUTE_SORT if self.separate_route_sort else 0)
+                 | (mok.MOK_FLAG_TILED_GEMMS if self.gemm_path == "tiled" else 0)
+                 | (mok.MOK_FLAG_STREAM_GEMMS if self.gemm_path == "stream" else 0))
         return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
                                self.minibatch_rows, self.ring_bytes, flags)
 

@@ -19,6 +19,8 @@ MOK_FLAG_SAVE_FOR_BACKWARD = 0x1
 MOK_FLAG_SIGMOID_GATES = 0x2
 MOK_FLAG_RENORM_GATES = 0x4
 MOK_FLAG_SEPARATE_ROUTE_SORT = 0x8
+MOK_FLAG_TILED_GEMMS = 0x10
+MOK_FLAG_STREAM_GEMMS = 0x20
 STAGES = ["router", "sort", "dispatch", "gemm_up", "gemm_down", "combine", "bwd_gate", "gemm_dh", "gemm_dx",
           "reduce_dx", "gemm_dw2", "regather", "gemm_dw13"]
 MOK_NUM_STAGES = len(STAGES)

@@ -42,7 +42,7 @@ def _cfg(**over):
 @pytest.mark.parametrize("over,k", [
     (dict(E=0), 1), (dict(E=1025), 2), (dict(), 0), (dict(), 9), (dict(T=-1), 2), (dict(d=100), 2),
     (dict(ffn=96), 2), (dict(precision=7), 2), (dict(expert_begin=3, expert_end=3), 2),
-    (dict(expert_end=9), 2), (dict(reserved=1), 2), (dict(flags=0x10), 2), (dict(minibatch_rows=-1), 2),
+    (dict(expert_end=9), 2), (dict(reserved=1), 2), (dict(flags=0x40), 2), (dict(flags=0x30), 2), (dict(minibatch_rows=-1), 2),
     (dict(precision="f32", d=24), 2),
 ])
 def test_workspace_query_rejects_bad_configs(over, k):
@@ -53,7 +53,8 @@ def test_workspace_query_rejects_bad_configs(over, k):
 
 @pytest.mark.parametrize("flags", [mok.MOK_FLAG_SIGMOID_GATES, mok.MOK_FLAG_RENORM_GATES,
                                    mok.MOK_FLAG_SIGMOID_GATES | mok.MOK_FLAG_RENORM_GATES | mok.MOK_FLAG_SAVE_FOR_BACKWARD,
-                                   mok.MOK_FLAG_SEPARATE_ROUTE_SORT])
+                                   mok.MOK_FLAG_SEPARATE_ROUTE_SORT, mok.MOK_FLAG_TILED_GEMMS,
+                                   mok.MOK_FLAG_STREAM_GEMMS])
 def test_workspace_query_accepts_router_variants(flags):
     ws, sv = mok.mok_moe_workspace_query(_cfg(flags=flags), 2)
     assert ws > 0 and sv > 0
