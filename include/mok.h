@@ -122,7 +122,15 @@ typedef struct mok_moe_config {
                                 into its ring slot while UP runs on m and DOWN
                                 on m-1.  Results are bitwise those of R = 0.
                                 T*d*2 < 2^31 (the copies and the backward's
-                                gathered x rows use 32-bit offsets).        */
+                                gathered x rows use 32-bit offsets).
+                                No compute-unit split between copying and
+                                computing (the pages' explicit split of SMs
+                                between the two, [kucoin §02]): each launch's
+                                256 workgroups take from one queue the copy
+                                tasks of minibatch m+1 (16 rows each) first,
+                                then the UP tiles of m and the DOWN tiles of
+                                m-1, so the share of copy work follows R
+                                instead of a fixed count of mover units.    */
   int64_t ring_bytes;        /* fixed ring token buffer for dispatched rows
                                 ([fluid], [kucoin §02] "macrobatch"), used
                                 with R > 0: floor(ring_bytes / (2 d R)) slots
