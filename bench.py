@@ -58,10 +58,13 @@ class HipEvents:
         return ms.value if r == 0 else float("nan")
 
 
-def stage_work(w, P, U, save_for_backward=True):
+def stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=False):
     """Algorithmic work of one launch of each stage: FLOPs for the GEMMs,
     HBM bytes for every stage (each operand read once, each output written
-    once; a GEMM's weights are those of the E_loc local experts)."""
+    once; a GEMM's weights are those of the E_loc local experts).  With
+    mxfp8_wgrad the weight gradients read MXFP8 operands quantised along the
+    rows, which the regather stage writes from the bf16 dY, H, [dA | dB] and
+    the x rows."""
     d, F, E, k, T = w.d, w.F, w.E, w.k, U
     El = w.e_end - w.expert_begin
     s = 4 if w.precision == "f32" else 2
@@ -93,16 +96,22 @@ def stage_work(w, P, U, save_for_backward=True):
         "gemm_dw2": P * d * s + P * F * s + El * d * F * 4,
         "gemm_dw13": 2 * P * F * s + P * d * s + 2 * El * F * d * 4,
     }
+    if mx and mxfp8_wgrad:
+        gemm_bytes["gemm_dw2"] = P * d * q + P * F * q + El * d * F * 4
+        gemm_bytes["gemm_dw13"] = 2 * P * F * q + P * d * q + 2 * El * F * d * 4
+        nbytes["regather"] = (P * d + P * F + 2 * P * F) * s + U * d * s + (2 * d + 3 * F) * P * q
     nbytes.update(gemm_bytes)
     return flops, nbytes
 
 
-def gemm_peak(precision: str, name: str) -> float:
+def gemm_peak(precision: str, name: str, mxfp8_wgrad: bool = False) -> float:
     """Dense MFMA peak of one GEMM: in an MXFP8 layer the forward GEMMs and
     the two backward products that lead to dx run on scaled MFMA (MXFP8
-    peak); the weight-gradient GEMMs stay bf16."""
+    peak); the weight-gradient GEMMs stay bf16 unless mxfp8_wgrad."""
     if precision == "mxfp8":
-        return PEAK_TFLOPS["bf16"] if name in ("gemm_dw2", "gemm_dw13") else PEAK_TFLOPS["mxfp8"]
+        if name in ("gemm_dw2", "gemm_dw13") and not mxfp8_wgrad:
+            return PEAK_TFLOPS["bf16"]
+        return PEAK_TFLOPS["mxfp8"]
     return PEAK_TFLOPS[precision]
 
 
@@ -248,9 +257,10 @@ def measure(name: str, args, extras: bool):
     torch.cuda.set_device(dev)
     inp = W.make_inputs(w, device=dev)
     T = inp["x"].shape[0]
+    mxw = w.precision == "mxfp8" and backward and getattr(args, "mxfp8_wgrad", False)
     shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision, expert_begin=w.expert_begin,
                      expert_end=w.e_end, save_for_backward=backward, minibatch_rows=args.minibatch_rows,
-                     ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0)
+                     ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0, mxfp8_wgrad=mxw)
     buf = MoeBuffers(shape, device=dev)
     W1, W3, W2, scales = inp["W1"], inp["W3"], inp["W2"], None
     if w.precision == "mxfp8":
@@ -364,28 +374,28 @@ def measure(name: str, args, extras: bool):
         stages[name] = sum(vals) / len(vals)
     P = int(buf.offsets[-1].item())
     U = int((buf.topk_idx.ge(w.expert_begin) & buf.topk_idx.lt(w.e_end)).any(dim=1).sum().item())
-    flops, nbytes = stage_work(w, P, U, save_for_backward=backward)
+    flops, nbytes = stage_work(w, P, U, save_for_backward=backward, mxfp8_wgrad=mxw)
     if w.precision == "bf16" and not args.minibatch_rows and T * w.d * 2 < (1 << 31):
         # the library fuses the dispatch into the UP GEMM's loads (pull
         # dispatch): the stage is recorded empty and moves no bytes of its own
         nbytes.pop("dispatch", None)
     dom = max(stages, key=stages.get)
-    roof = roof_of(flops.get(dom, 0.0), nbytes[dom], stages[dom], gemm_peak(w.precision, dom))
+    roof = roof_of(flops.get(dom, 0.0), nbytes[dom], stages[dom], gemm_peak(w.precision, dom, mxw))
     roof.update({"traffic": measured_traffic(w.name, dom) if dom in flops and not args.minibatch_rows else None,
                  "kernel": dom, "avg_ms": round(stages[dom], 4),
                  "per_launch": (f"{flops[dom] / 1e9:.1f} GFLOP, " if dom in flops else "")
                  + f"{nbytes[dom] / 1e6:.1f} MB"})
     gemm = {n: {"ms": round(stages[n], 4), "tflops": round(flops[n] / (stages[n] * 1e-3) / 1e12, 1),
-                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / gemm_peak(w.precision, n), 4),
+                "frac_peak": round(flops[n] / (stages[n] * 1e-3) / 1e12 / gemm_peak(w.precision, n, mxw), 4),
                 "roof": {k_: v for k_, v in roof_of(flops[n], nbytes[n], stages[n],
-                                                    gemm_peak(w.precision, n)).items()
+                                                    gemm_peak(w.precision, n, mxw)).items()
                          if k_ in ("bound", "frac")}}
             for n in flops if n in stages}
     gemm_ms = sum(stages[n] for n in flops if n in stages)
     gemm_flops = sum(flops[n] for n in flops if n in stages)
     # the GEMMs' combined peak: their FLOPs over the time they would take,
     # each at its own peak
-    gemm_peak_all = gemm_flops / sum(flops[n] / gemm_peak(w.precision, n) for n in flops if n in stages)
+    gemm_peak_all = gemm_flops / sum(flops[n] / gemm_peak(w.precision, n, mxw) for n in flops if n in stages)
     hbm = {n: {"ms": round(stages[n], 4), "gbs": round(nbytes[n] / (stages[n] * 1e-3) / 1e9, 1)}
            for n in nbytes if n in stages and n not in flops}
 
@@ -535,6 +545,10 @@ def main():
                     help="skip the extra timing of steps that start with the last-level cache flushed")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8 forward+backward leg after the bf16 training workload")
+    ap.add_argument("--mxfp8-wgrad", action="store_true",
+                    help="with --workload mxfp8_train: MXFP8 weight gradients (MOK_FLAG_MXFP8_WGRAD)")
+    ap.add_argument("--no-mxfp8-bf16-wgrad", action="store_true",
+                    help="skip the comparison run of the MXFP8 step with bf16 weight gradients")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the forward-only few-token latency leg after the bf16 training workload")
     ap.add_argument("--decode-tokens", type=lambda v: [int(x) for x in v.split(",") if x], default=[1, 16, 64, 256],
@@ -587,10 +601,21 @@ def main():
         # MXFP8 forward GEMMs and MXFP8 dx products in the backward
         del inp
         torch.cuda.empty_cache()
-        mx, _, _, _ = measure("mxfp8_train", args, extras=False)
+        a2 = argparse.Namespace(**vars(args))
+        a2.mxfp8_wgrad = True
+        mx, _, _, _ = measure("mxfp8_train", a2, extras=False)
         result["mxfp8_train"] = {k_: mx[k_] for k_ in ("value", "unit", "ms_per_step", "dtype", "roofline",
                                                         "grouped_gemm", "data_movement", "stages_ms", "eager")}
-        result["mxfp8_train"]["config"] = mx["config"]["workload"]
+        result["mxfp8_train"]["config"] = mx["config"]["workload"] + ", MXFP8 weight gradients"
+        torch.cuda.empty_cache()
+        if not args.no_mxfp8_bf16_wgrad:
+            # the same MXFP8 step with the weight gradients in bf16 (the
+            # backward's products that lead to dx stay MXFP8)
+            a2.mxfp8_wgrad = False
+            mb, _, _, _ = measure("mxfp8_train", a2, extras=False)
+            result["mxfp8_train"]["bf16_weight_gradients"] = {
+                "ms_per_step": mb["ms_per_step"], "tokens_per_s": mb["value"],
+                "stages_ms": {k_: v for k_, v in mb["stages_ms"].items() if k_ in ("gemm_dw2", "regather", "gemm_dw13")}}
     print(json.dumps(result), flush=True)
 
 

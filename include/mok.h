@@ -105,6 +105,21 @@ typedef enum {
  * those of the tiled kernels (another summation order). */
 #define MOK_FLAG_TILED_GEMMS 0x10u
 #define MOK_FLAG_STREAM_GEMMS 0x20u
+/* MXFP8 weight gradients (with MOK_PREC_MXFP8 and MOK_FLAG_SAVE_FOR_BACKWARD
+ * only; the pages report the layer's backward time in MXFP8, [kucoin §03],
+ * with no recipe): mok_moe_backward_mxfp8 then also computes dW2, dW1 and
+ * dW3 on the scaled MFMA.  Their contraction runs over an expert's rows, so
+ * each operand (dY, H = silu(A) * B before its quantisation, dA, dB and the x
+ * rows) is quantised along the rows: per column, blocks of 32 consecutive
+ * rows of the expert's segment from its first row in placement order, the
+ * last block taking its scale from the rows it has; then
+ *   dW2_e = Qr(dY_e)^T Qr(H_e),  dW1_e = Qr(dA_e)^T Qr(X_e),
+ *   dW3_e = Qr(dB_e)^T Qr(X_e),  fp32 results.
+ * Requires d to be a multiple of 256 (MOK_ERR_INVALID_ARG otherwise).
+ * Without the flag the MXFP8 backward takes these products in bf16.  The
+ * workspace of such a configuration holds the transposed codes (see
+ * mok_workspace_layout.wq). */
+#define MOK_FLAG_MXFP8_WGRAD 0x40u
 
 typedef struct mok_moe_config {
   int32_t T;                 /* tokens in this call (>= 0)                      */
@@ -219,6 +234,15 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *   dy, dab, dxp  backward row buffers dY [P_max, d], [dA | dB] [P_max, 2F],
  *             dX_perm [P_max, d] (bf16; absent from an MXFP8 forward-only
  *             configuration);
+ *   wq, wq_scale, k_pad  with MOK_FLAG_MXFP8_WGRAD: the row-quantised
+ *             operands of the weight gradients, transposed: E4M3 codes of dY
+ *             (d rows), H (F rows), [dA | dB] (2F rows) and x (d rows), each
+ *             row k_pad = 128 (floor(T k / 128) + E_loc) bytes long, local
+ *             expert e's rows at columns [128 p_e, 128 p_(e+1)) with p the
+ *             prefix of ceil(rows / 128) over the local experts (zero codes
+ *             past its rows); then their E8M0 scales, for each matrix in pair
+ *             planes [k_pad / 64, rows, 2] (byte (j, c, b) = scale of block
+ *             2 j + b of row c).  k_pad = 0 and no bytes otherwise;
  *   total     workspace_bytes. */
 #define MOK_CHECK_LOGITS 0x1
 #define MOK_CHECK_INDEX 0x2
@@ -230,6 +254,9 @@ typedef struct mok_workspace_layout {
   size_t dy;
   size_t dab;
   size_t dxp;
+  size_t wq;
+  size_t wq_scale;
+  int64_t k_pad;
   size_t total;
 } mok_workspace_layout;
 

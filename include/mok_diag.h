@@ -29,6 +29,21 @@ extern "C" {
 int32_t mok_diag_mfma_scale_block(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
                                   const float* c_in, float* c_out, void* stream);
 
+/*
+ * The E4M3 encoding the layer's MXFP8 quantisers use (the gfx950 conversion
+ * instruction on the value clamped to +-448, one value and four packed
+ * little-endian) against a software encoder written from the OCP E4M3
+ * definition (round to nearest even, saturation to +-448, sign of zero kept),
+ * over every float32 bit pattern u < n and its negation (n <= 0x44000000,
+ * the magnitudes below 2^9 that scaled MX elements take).
+ *   count, first  device, uint32 [blocks * 256]: per thread, the number of
+ *                 mismatching values and the first one's bit pattern
+ *                 (0xFFFFFFFF when none)
+ * Returns 0, 1 for a null pointer or an out-of-range n or blocks, 4 for a
+ * failed launch.
+ */
+int32_t mok_diag_e4m3_check(uint32_t n, uint32_t* count, uint32_t* first, int32_t blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmok.so")
 DIAG = os.path.join(PKG, "libmok_diag.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["route_sort.hip", "permute_combine.hip", "gemm_bf16.hip", "gemm_stream.hip", "gemm_f32.hip", "gemm_mxfp8.hip", "router_gemm.hip",
+SOURCES = ["route_sort.hip", "permute_combine.hip", "gemm_bf16.hip", "gemm_stream.hip", "quantize_rows.hip", "gemm_f32.hip", "gemm_mxfp8.hip", "router_gemm.hip",
            "mok_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -1,4 +1,5 @@
-// Diagnostic: one gfx950 scaled-MFMA block (v_mfma_scale_f32_32x32x64_f8f6f4,
+// Diagnostics of the gfx950 instructions the MXFP8 path relies on.  One
+// scaled-MFMA block (v_mfma_scale_f32_32x32x64_f8f6f4,
 // E4M3 operands, one E8M0 scale per 32 K values of each row) on caller-given
 // codes and scales, so that a test can compare the matrix core's fp32 result
 // with the exact sum of the same products.  Not part of the layer.
@@ -38,7 +39,43 @@ __global__ __launch_bounds__(64) void mfma_scale_block_kernel(const uint8_t* __r
 #endif
 }
 
+// Every float32 of magnitude below 2^9 (bit patterns [0, n), both signs)
+// through the layer's E4M3 encoders: the conversion instruction (e4m3_rne,
+// and e4m3x4 with the value in each of its four byte places) against the
+// software encoder of the format's definition.  Per thread: mismatches and
+// the first mismatching bit pattern (0xFFFFFFFF: none).
+__global__ __launch_bounds__(256) void e4m3_check_kernel(uint32_t n, uint32_t* __restrict__ count,
+                                                         uint32_t* __restrict__ first) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t tid = blockIdx.x * 256 + threadIdx.x, stride = gridDim.x * 256;
+  uint32_t cnt = 0, f = 0xFFFFFFFFu;
+  for (uint32_t u = tid; u < n; u += stride)
+    for (int sgn = 0; sgn < 2; ++sgn) {
+      const uint32_t bits = u | (sgn ? 0x80000000u : 0u);
+      const float x = __uint_as_float(bits);
+      const uint32_t sw = e4m3_rne_sw(x);
+      const uint32_t q = (u >> 7) & 3u;  // the byte place this value takes in e4m3x4
+      const uint32_t w = e4m3x4(q == 0 ? x : 1.0f, q == 1 ? x : 1.0f, q == 2 ? x : 1.0f, q == 3 ? x : 1.0f);
+      const uint32_t one = 0x38u;  // E4M3 code of 1.0
+      uint32_t expect = 0;
+      for (uint32_t i = 0; i < 4; ++i) expect |= (i == q ? sw : one) << (8 * i);
+      if (e4m3_rne(x) != sw || w != expect) {
+        ++cnt;
+        if (f == 0xFFFFFFFFu) f = bits;
+      }
+    }
+  count[tid] = cnt;
+  first[tid] = f;
+#endif
+}
+
 }  // namespace
+
+extern "C" int32_t mok_diag_e4m3_check(uint32_t n, uint32_t* count, uint32_t* first, int32_t blocks, void* stream) {
+  if (!count || !first || blocks < 1 || n > 0x44000000u) return 1;
+  hipLaunchKernelGGL(e4m3_check_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, n, count, first);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
 
 extern "C" int32_t mok_diag_mfma_scale_block(const uint8_t* a, const uint8_t* b, const uint8_t* sa,
                                              const uint8_t* sb, const float* c_in, float* c_out, void* stream) {

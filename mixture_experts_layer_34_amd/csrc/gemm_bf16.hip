@@ -69,6 +69,9 @@
 #ifndef MOK_ROW_NT_A
 #define MOK_ROW_NT_A 0
 #endif
+#ifndef MOK_DW_NT_STORE
+#define MOK_DW_NT_STORE 0  // non-temporal fp32 weight-gradient stores
+#endif
 #ifndef MOK_ROW_NT_B
 #define MOK_ROW_NT_B 0
 #endif
@@ -461,8 +464,11 @@ struct TileJob {
         for (int j = 0; j < FN; ++j) {
           if (c.n0 + wcol0 + j * 32 >= G.N) continue;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            lp[(int64_t)(i * 32 + (r >> 2) * 8 + (r & 3)) * G.N + j * 32] = acc[0][i][j][r];
+          for (int r = 0; r < 16; ++r) {
+            float* q = lp + (int64_t)(i * 32 + (r >> 2) * 8 + (r & 3)) * G.N + j * 32;
+            if constexpr (MOK_DW_NT_STORE) __builtin_nontemporal_store(acc[0][i][j][r], q);
+            else *q = acc[0][i][j][r];
+          }
         }
       }
     } else if constexpr (NB == 2) {

@@ -7,6 +7,12 @@
 //   DH    dH_e = dY_e (W2_e^T)^T, then the SwiGLU backward: dA, dB (bf16, for
 //         the weight gradients) and [dA | dB] quantised along F
 //   DX    dX_e = [dA | dB]_e [W1_e^T | W3_e^T]^T (bf16), K = 2F
+// and the weight gradients, whose contraction runs over the expert's rows:
+//   DW2   dW2_e = Qr(dY_e)^T Qr(H_e)                 (fp32 [d, F])
+//   DW13  [dW1_e; dW3_e] = Qr([dA | dB]_e)^T Qr(X_e) (fp32 [F, d] each)
+// with the operands quantised along the rows and stored transposed, so that
+// they too are K-contiguous (see quantize_rows.hip): A row m is column m of
+// the row-major operand, K runs over the expert's padded row segment.
 // Operands are E4M3 with one E8M0 scale per 32 consecutive K values (OCP MX
 // v1.0).  MXFP8 activation quantisation sits in the dispatch, grouped-GEMM and
 // SwiGLU data paths instead of a standalone kernel (kucoin.com, "Cursor's MoK
@@ -48,6 +54,15 @@ constexpr int kMxNS = 5;     // LDS stage buffers (4-wave workgroups)
 #ifndef MOK_MX_WAVES
 #define MOK_MX_WAVES 8
 #endif
+// Weight-gradient kinds: non-temporal fp32 stores, so that the dW lines do
+// not take L2 space from the operands (same-box A/B at T 8192, d 4096, E 128,
+// k 8, F 1536: dW1/dW3 2.69 -> 2.50 ms, dW2 1.32 -> 1.27 ms).  Measured and
+// dropped: dealing whole experts to the XCDs (snake order of their rank,
+// row-tile-major tiles on each XCD's own workgroups, so that an expert's
+// operands are fetched into one L2 only): 3.43 and 1.60 ms.
+#ifndef MOK_MXW_NT_STORE
+#define MOK_MXW_NT_STORE 1
+#endif
 constexpr int kMxWaves = MOK_MX_WAVES;
 
 __device__ __forceinline__ u32x4_t pack_bf16x8(const float* v) {
@@ -83,8 +98,11 @@ template <int KIND> __host__ __device__ inline int mx_k(int d, int F) {
   return KIND == KIND_UP || KIND == KIND_DH ? d : (KIND == KIND_DX ? 2 * F : F);
 }
 template <int KIND> __host__ __device__ inline int mx_n(int d, int F) {
-  return KIND == KIND_UP || KIND == KIND_DH ? F : d;
+  return KIND == KIND_UP || KIND == KIND_DH || KIND == KIND_DW2 ? F : d;
 }
+// Weight-gradient kinds: output rows (dW2: d; DW13: dW1 rows then dW3 rows).
+template <int KIND> __host__ __device__ inline int mx_m(int d, int F) { return KIND == KIND_DW2 ? d : 2 * F; }
+template <int KIND> constexpr bool mx_wgrad() { return KIND == KIND_DW2 || KIND == KIND_DW13; }
 
 // NW waves per workgroup: NW = 4 as 2 x 2 waves of 128 x TN (128
 // accumulators); NW = 8 as 4 x 2 waves of 64 x TN (64 accumulators, two waves
@@ -124,6 +142,7 @@ struct MxJob {
 
   const GroupedGemmArgs* args;
   int K, N;
+  uint32_t lda, ldb;  // bytes per operand row (K for the row kinds, k_pad for the weight gradients)
   uint32_t psA, psB;  // bytes per scale plane of A (P_max rows) and of B (E_loc * N rows)
   TileCoord c;
   int wid, lane, wm, wn, nk;
@@ -133,15 +152,20 @@ struct MxJob {
 
   __device__ __forceinline__ void init(const GroupedGemmArgs& a, const TileCoord& tc) {
     args = &a;
-    K = mx_k<KIND>(a.d, a.F);
     N = mx_n<KIND>(a.d, a.F);
     c = tc;
     lane = threadIdx.x & 63;
     wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wm = wid >> 1;
     wn = wid & 1;
-    nk = K / kMxBK;
     nvb = FM;
+    if constexpr (mx_wgrad<KIND>()) {
+      init_wgrad(a);
+      return;
+    }
+    K = mx_k<KIND>(a.d, a.F);
+    lda = ldb = (uint32_t)K;
+    nk = K / kMxBK;
     if (MOK_SKIP_PAD) {
       // rows past the expert's end are zero padding and are never stored:
       // their MFMAs are skipped (less work, less power)
@@ -166,16 +190,44 @@ struct MxJob {
     rsSA = make_rsrc(a.a_scale + (int64_t)c.row0 * 2, (uint32_t)(planes * pa - (int64_t)c.row0 * 2));
     rsSB0 = make_rsrc(a.b_scale0 + fb, (uint32_t)(planes * pb - fb));
     rsSB1 = make_rsrc((NB == 2 ? a.b_scale1 : a.b_scale0) + fb, (uint32_t)(planes * pb - fb));
+    init_offsets();
+  }
+
+  // Weight-gradient tile: rows m0 .. m0 + 255 of the output (columns of the
+  // row-major A operand), columns n0 .. n0 + 127, K over the expert's padded
+  // segment [row0, row_end) of the transposed operands (row stride k_pad
+  // bytes; scale planes of M_total resp. N rows).  Every output row is real:
+  // no row blocks are skipped; an expert without rows has nk = 0 and stores
+  // zeros.
+  __device__ __forceinline__ void init_wgrad(const GroupedGemmArgs& a) {
+    const int M = mx_m<KIND>(a.d, a.F);
+    const int kbeg = c.row0;
+    K = c.row_end - c.row0;
+    nk = K / kMxBK;
+    lda = ldb = (uint32_t)a.k_pad;
+    rsA = make_rsrc((const uint8_t*)a.A + (int64_t)c.m0 * a.k_pad + kbeg, (uint32_t)(BM * a.k_pad - kbeg));
+    rsB0 = make_rsrc((const uint8_t*)a.B0 + (int64_t)c.n0 * a.k_pad + kbeg, (uint32_t)(BN * a.k_pad - kbeg));
+    rsB1 = rsB0;
+    psA = (uint32_t)(M * 2);
+    psB = (uint32_t)(N * 2);
+    const int64_t p0 = kbeg / 64, planes = K / 64;
+    rsSA = make_rsrc(a.a_scale + p0 * psA + (int64_t)c.m0 * 2, (uint32_t)(planes * psA - (int64_t)c.m0 * 2));
+    rsSB0 = make_rsrc(a.b_scale0 + p0 * psB + (int64_t)c.n0 * 2, (uint32_t)(planes * psB - (int64_t)c.n0 * 2));
+    rsSB1 = rsSB0;
+    init_offsets();
+  }
+
+  __device__ __forceinline__ void init_offsets() {
 #pragma unroll
     for (int q = 0; q < IA; ++q) {
       const int r = (wid * IA + q) * (64 / kMxLPR) + lane / kMxLPR;
-      offA[q] = (uint32_t)(r * K + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
+      offA[q] = (uint32_t)(r * lda + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
     }
 #pragma unroll
     for (int q = 0; q < IB; ++q) {
       const int r = (wid * IB + q) * (64 / kMxLPR) + lane / kMxLPR;
       const int rl = (NB == 2 && r >= BN) ? r - BN : r;
-      offB[q] = (uint32_t)(rl * K + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
+      offB[q] = (uint32_t)(rl * ldb + swz_k<kMxBK / 2>(r, lane % kMxLPR) * 16);
     }
     // scale copies: wave w brings A rows 64 w .. 64 w + 63 and, in lanes 0-31,
     // B rows 32 w .. 32 w + 31 (UP: of W1 for w < 2, of W3 after); lanes 32-63
@@ -385,7 +437,37 @@ struct MxJob {
     float* ep = reinterpret_cast<float*>(staging + wid * 4096);
     const GroupedGemmArgs& a = *args;
     const int wrow0 = wm * TM, wcol0 = wn * TN;
-    if constexpr (KIND == KIND_UP) {
+    if constexpr (mx_wgrad<KIND>()) {
+      // fp32 weight gradients straight from the accumulators: each half-wave
+      // writes 32 consecutive floats of one row.  DW13: output rows below F
+      // are dW1's, the rest dW3's (F is a multiple of 32, so a 32-row block
+      // lies in one of them).
+      (void)staging;
+      (void)pre;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = c.m0 + wrow0 + i * 32;
+        float* outp;
+        int mr = m;
+        if constexpr (KIND == KIND_DW13) {
+          const bool w3 = m >= a.F;
+          outp = (float*)(w3 ? a.out1 : a.out0);
+          mr = w3 ? m - a.F : m;
+        } else {
+          outp = (float*)a.out0;
+        }
+        const int Mo = KIND == KIND_DW13 ? a.F : a.d;
+        float* lp = outp + ((int64_t)c.e_loc * Mo + mr + (lane >> 5) * 4) * N + c.n0 + wcol0 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float* q = lp + (int64_t)((r >> 2) * 8 + (r & 3)) * N + j * 32;
+            if constexpr (MOK_MXW_NT_STORE) __builtin_nontemporal_store(acc[0][i][j][r], q);
+            else *q = acc[0][i][j][r];
+          }
+      }
+    } else if constexpr (KIND == KIND_UP) {
       // gate and up of 16 rows x 32 columns per round; 4 consecutive lanes
       // hold the 32 columns (one MX block) of a row
       uint8_t* hq = (uint8_t*)a.out0;
@@ -600,6 +682,77 @@ __global__ __launch_bounds__(NW * 64) void grouped_gemm_mxfp8_kernel(GroupedGemm
 #endif
 }
 
+// Weight-gradient kinds: every (local expert, 256-row, 128-column) tile of
+// the output, experts taken heaviest first (the counting sort's rank order)
+// so that the longest K loops start first, tiles of one expert in raster
+// groups of two row tiles; a static round-robin over the persistent
+// workgroups, XCD-contiguous as above.  Expert e's K range is its padded
+// segment [128 tp128[e], 128 tp128[e + 1]) of the transposed operands.
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void grouped_wgrad_mxfp8_kernel(GroupedGemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using Job = MxJob<KIND, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[Job::NS * Job::STAGE + Job::STAGING];
+  uint8_t* const staging = arena + Job::NS * Job::STAGE;
+  const int N = mx_n<KIND>(args.d, args.F), M = mx_m<KIND>(args.d, args.F);
+  const int E_loc = args.E_loc;
+  const int ntn = N / Job::BN, ntm = M / Job::BM;
+  const int per_e = ntm * ntn;
+  const int total = E_loc * per_e;
+  const int32_t* tp = args.tile_prefix + 1 * (E_loc + 1);  // 128-row tiles: the padded segments
+  const int G_ = gridDim.x;
+  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+  auto coord = [&](int tile) -> TileCoord {
+    TileCoord c{};
+    const int rank = tile / per_e;
+    c.e_loc = sload(args.expert_order + 4 * rank);
+    c.row0 = 128 * sload(tp + c.e_loc);
+    c.row_end = 128 * sload(tp + c.e_loc + 1);
+    int mt, nt;
+    tile_mn<2>(tile - rank * per_e, ntm, ntn, mt, nt);
+    c.m0 = mt * Job::BM;
+    c.n0 = nt * Job::BN;
+    return uniform(c);
+  };
+  const int step = G_;
+  auto valid = [&](int tile) { return tile < total; };
+  int tile = vb;
+  if (tile >= total) return;
+  Job cur;
+  cur.init(args, coord(tile));
+  for (int s = 0; s < Job::NS && s < cur.nk; ++s) cur.issue(s, arena);
+  f32x16_t acc[Job::NB][Job::FM][Job::FN];
+  typename Job::SavedPre pre;
+  while (true) {
+    cur.mainloop(acc, arena);
+    lds_barrier();  // every wave is done with the stage buffers
+    const int nt = tile + step;
+    const bool more = valid(nt);
+    Job nxt = cur;
+    if (more) {
+      nxt.init(args, coord(nt));
+      for (int s = 0; s < Job::NS && s < nxt.nk; ++s) nxt.issue(s, arena);
+    }
+    cur.epilogue(acc, staging, pre);
+    if (!more) break;
+    cur = nxt;
+    tile = nt;
+  }
+#endif
+}
+
+template <int KIND, int NW>
+static hipError_t run_mx_wgrad(const GroupedGemmArgs& g, hipStream_t s) {
+  using Job = MxJob<KIND, NW>;
+  const int N = mx_n<KIND>(g.d, g.F), M = mx_m<KIND>(g.d, g.F);
+  if (N % Job::BN || M % Job::BM || g.k_pad % kMxBK) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)g.E_loc * (M / Job::BM) * (N / Job::BN);
+  const int blocks = (int)(tiles < 256 ? tiles : 256);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_wgrad_mxfp8_kernel<KIND, NW>), dim3(blocks), dim3(NW * 64), 0, s, g);
+  return hipGetLastError();
+}
+
 template <int KIND, int NW>
 static hipError_t run_mx(const GroupedGemmArgs& g, hipStream_t s) {
   using Job = MxJob<KIND, NW>;
@@ -618,6 +771,8 @@ hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_DOWN: return run_mx<KIND_DOWN, kMxWaves>(g, s);
     case KIND_DH:   return run_mx<KIND_DH, kMxWaves>(g, s);
     case KIND_DX:   return run_mx<KIND_DX, kMxWaves>(g, s);
+    case KIND_DW2:  return run_mx_wgrad<KIND_DW2, kMxWaves>(g, s);
+    case KIND_DW13: return run_mx_wgrad<KIND_DW13, kMxWaves>(g, s);
   }
   return hipErrorNotSupported;
 }

@@ -43,8 +43,17 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
     return MOK_ERR_INVALID_ARG;
   if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
   if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES |
-                  MOK_FLAG_SEPARATE_ROUTE_SORT | MOK_FLAG_TILED_GEMMS | MOK_FLAG_STREAM_GEMMS))
+                  MOK_FLAG_SEPARATE_ROUTE_SORT | MOK_FLAG_TILED_GEMMS | MOK_FLAG_STREAM_GEMMS |
+                  MOK_FLAG_MXFP8_WGRAD))
     return MOK_ERR_INVALID_ARG;
+  if (c.flags & MOK_FLAG_MXFP8_WGRAD) {
+    // MXFP8 training only; the GEMMs address 256 rows of the transposed
+    // operands (k_pad bytes each) through one 32-bit buffer range
+    if (c.precision != MOK_PREC_MXFP8 || !(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
+    if (c.d % 256) return MOK_ERR_INVALID_ARG;  // dW2 rows come in tiles of 256 (2F is a multiple of 256)
+    const int64_t kp = 128 * ((int64_t)c.T * k / 128 + (c.expert_end - c.expert_begin));
+    if (kp * 256 >= (int64_t(1) << 32)) return MOK_ERR_INVALID_ARG;
+  }
   if ((c.flags & MOK_FLAG_TILED_GEMMS) && (c.flags & MOK_FLAG_STREAM_GEMMS)) return MOK_ERR_INVALID_ARG;
   if (c.precision == MOK_PREC_MXFP8) {
     // every E8M0 scale array (x and H rows, each weight matrix) fits a 32-bit buffer range
@@ -133,6 +142,12 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->dab = o;           o = align256(o + (mx && !mxb ? 0 : Tk * 2 * c.ffn * A));
   w->dxp = o;           o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
   w->queue = o;         o = align256(o + 256);
+  const bool mxw = mxb && (c.flags & MOK_FLAG_MXFP8_WGRAD);
+  const int64_t E_loc_ = c.expert_end - c.expert_begin;
+  w->k_pad = mxw ? 128 * ((int64_t)Tk / 128 + E_loc_) : 0;
+  const size_t wq_rows = (size_t)(2 * c.d + 3 * c.ffn);
+  w->wq = o;            o = align256(o + wq_rows * (size_t)w->k_pad);
+  w->wq_scale = o;      o = align256(o + wq_rows * (size_t)w->k_pad / 32);
   w->total = o;
 }
 
@@ -409,7 +424,7 @@ WorkspaceLayout compact_forward_layout(const mok_moe_config& c, int32_t k) {
   w.status = o;        o = align256(o + 256);
   w.chunk_counts = o;  o = align256(o + (size_t)nchunks * c.E * 4);
   w.chunk_base = o;    o = align256(o + (size_t)nchunks * c.E * 4);
-  w.tile_prefix = w.xp = w.xp_scale = w.hq = w.hq_scale = w.dy = w.dab = w.dxp = w.queue = o;
+  w.tile_prefix = w.xp = w.xp_scale = w.hq = w.hq_scale = w.dy = w.dab = w.dxp = w.queue = w.wq = w.wq_scale = o;
   w.xp_rows = 0;
   w.total = o;
   return w;
@@ -461,6 +476,9 @@ mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_wo
   out->dy = w.dy;
   out->dab = w.dab;
   out->dxp = w.dxp;
+  out->wq = w.wq;
+  out->wq_scale = w.wq_scale;
+  out->k_pad = w.k_pad;
   out->total = w.total;
   return MOK_OK;
 }
@@ -723,6 +741,45 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
   gx.out0 = dxp;
   MOK_STAGE(MOK_STAGE_GEMM_DX, gemm_mxfp8(KIND_DX, gx, s));
   MOK_STAGE(MOK_STAGE_REDUCE_DX, launch_combine(dxp, nullptr, s_rop, T, k, d, 1, all_local(c), dx, P_max, status, s));
+  if (c.flags & MOK_FLAG_MXFP8_WGRAD) {
+    // weight gradients in MXFP8: dY, H, [dA | dB] and the x rows quantised
+    // along each expert's rows (transposed codes), then the scaled-MFMA
+    // products into the fp32 dW
+    const int64_t kp = wl.k_pad;
+    uint8_t* q = at<uint8_t>(workspace, wl.wq);
+    uint8_t* qs = at<uint8_t>(workspace, wl.wq_scale);
+    uint8_t *dyT = q, *hT = dyT + d * kp, *abT = hT + F * kp, *xT = abT + 2 * F * kp;
+    uint8_t *dyS = qs, *hS = dyS + d * kp / 32, *abS = hS + F * kp / 32, *xS = abS + 2 * F * kp / 32;
+    const int32_t* offs = at<int32_t>(saved, sl.offsets);
+    const int32_t* tp128 = at<int32_t>(saved, tp_off) + 1 * (E_loc + 1);
+    const int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
+    const void* Hs = at<void>(saved, sl.H);
+    {
+      StageMark mark(c, s, MOK_STAGE_REGATHER);
+      MOK_HIP(launch_quantize_rows_t(dy, d, nullptr, 1, d, offs, eb, E_loc, tp128, P_max, kp, dyT, dyS, s));
+      MOK_HIP(launch_quantize_rows_t(Hs, F, nullptr, 1, F, offs, eb, E_loc, tp128, P_max, kp, hT, hS, s));
+      MOK_HIP(launch_quantize_rows_t(dab, 2 * F, nullptr, 1, 2 * F, offs, eb, E_loc, tp128, P_max, kp, abT, abS, s));
+      MOK_HIP(launch_quantize_rows_t(x, d, s_por, k, d, offs, eb, E_loc, tp128, P_max, kp, xT, xS, s));
+    }
+    GroupedGemmArgs w2 = g;
+    w2.k_pad = kp;
+    w2.A = dyT;
+    w2.a_scale = dyS;
+    w2.B0 = hT;
+    w2.b_scale0 = hS;
+    w2.out0 = dW2;
+    MOK_STAGE(MOK_STAGE_GEMM_DW2, gemm_mxfp8(KIND_DW2, w2, s));
+    GroupedGemmArgs w13 = g;
+    w13.k_pad = kp;
+    w13.A = abT;
+    w13.a_scale = abS;
+    w13.B0 = xT;
+    w13.b_scale0 = xS;
+    w13.out0 = dW1;
+    w13.out1 = dW3;
+    MOK_STAGE(MOK_STAGE_GEMM_DW13, gemm_mxfp8(KIND_DW13, w13, s));
+    return MOK_OK;
+  }
   // weight gradients: bf16 products of the unquantised operands
   GroupedGemmArgs gw = g;
   gw.A = dy;

@@ -98,8 +98,13 @@ __device__ __forceinline__ int32_t checked_row(int32_t r, int64_t rows, int32_t*
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // OCP E4M3 (bias 7, no infinities) from an fp32 value: round to nearest even,
-// saturate to +-448, keep the sign of zero.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+// saturate to +-448, keep the sign of zero.  The layer uses the gfx950
+// conversion instruction on the value clamped to +-448 (e4m3_rne, e4m3x4);
+// this software encoder, written from the format's definition, is the
+// reference the diagnostic library checks that instruction against (equal on
+// every float32 of magnitude below 512, both signs, subnormals included; the
+// clamp makes the rest equal too).
+__device__ __forceinline__ uint32_t e4m3_rne_sw(float v) {
   uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   float a = fminf(fabsf(v), 448.0f);
   uint32_t au = __float_as_uint(a);
@@ -114,6 +119,18 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
     code = ((uint32_t)(e2 + 7) << 3) | ((r >> 20) & 7u);
   }
   return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_clamp(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const float c = e4m3_clamp(v);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+// Four codes packed little-endian: a | b << 8 | c << 16 | d << 24.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+  return (uint32_t)w;
 }
 
 // Shared-scale exponent of an MX block from its amax (>= 0): floor(log2 amax) - 8,

@@ -32,6 +32,10 @@ struct WorkspaceLayout {
   size_t dab;           // backward: act [P_max, 2F]  (dA | dB)
   size_t dxp;           // backward: act [P_max, d]
   size_t queue;         // int32 tile counters of the weight-gradient GEMMs
+  size_t wq;            // MXFP8 weight gradients: row-quantised transposed codes,
+                        // [d | F | 2F | d] rows of k_pad bytes (dY, H, dA|dB, X)
+  size_t wq_scale;      // their E8M0 scales, pair planes [k_pad / 64, C, 2] each
+  int64_t k_pad;        // padded rows: 128 (P_max / 128 + E_loc), 0 without MXFP8 weight gradients
   size_t total;
   int nchunks;
   int64_t xp_rows;      // rows held by the dispatch buffer (P_max, or the ring)
@@ -64,6 +68,16 @@ hipError_t launch_route_sort_small(const float* logits, int T, int E, int k, int
                                    float* lse, int32_t* counts_out, int32_t* offsets_out, int32_t* offsets_saved,
                                    int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
                                    int32_t* pair_of_row, int32_t* status, hipStream_t s);
+
+// MXFP8 quantisation of a bf16 [rows, C] matrix (row stride ld elements;
+// gathered: row r is src row gather_rows[r] / k_top) along its rows, per local
+// expert in blocks of 32 from the expert's first row, written transposed:
+// codes [C, P_pad] at column 128 tp128[e] + (r - offsets[e]), scales in pair
+// planes [P_pad / 64, C, 2].  C a multiple of 64, P_pad of 128 and at least
+// 128 (P_max / 128 + E_loc).
+hipError_t launch_quantize_rows_t(const void* src, int64_t ld, const int32_t* gather_rows, int k_top, int C,
+                                  const int32_t* offsets, int eb, int E_loc, const int32_t* tp128, int64_t P_max,
+                                  int64_t P_pad, uint8_t* dst, uint8_t* dsc, hipStream_t s);
 
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
                                 int nchunks, int32_t* chunk_counts, int32_t* chunk_base,
@@ -133,6 +147,9 @@ struct GroupedGemmArgs {
   int64_t gather_src_rows;
   // Ring mode: the A operand of UP holds row r at A row r - a_row_shift.
   int64_t a_row_shift;
+  // MXFP8 weight gradients: row stride (bytes) of the transposed, row-quantised
+  // operands; expert e's K range is [128 tp128[e], 128 tp128[e + 1]).
+  int64_t k_pad;
 };
 
 // Expert-grouped GEMM of one kind (GemmKind in gemm_common.h) per precision:

@@ -3,7 +3,7 @@
 //
 //   mok_profile [--T 8192] [--d 4096] [--E 128] [--k 8] [--F 1536] [--zipf 1.2]
 //               [--steps 3] [--warmup 1] [--forward-only] [--copy-mib 0]
-//               [--inputs DIR] [--mxfp8]
+//               [--inputs DIR] [--mxfp8] [--mxfp8-wgrad]
 //
 // Inputs: with --inputs, the raw arrays that profile_inputs.py writes from the
 // benchmark's own workload generator (x, logits, dout as bf16 / fp32 / bf16,
@@ -13,7 +13,8 @@
 // Gumbel noise with pi_r proportional to r^-zipf and expert 0 hottest (the
 // same routing model; values and expert loads differ).  --mxfp8 runs the
 // MXFP8 layer (weights quantised by mok_quantize_mxfp8 and
-// mok_quantize_mxfp8_backward_weights before the timed steps).  --copy-mib
+// mok_quantize_mxfp8_backward_weights before the timed steps); --mxfp8-wgrad
+// also its weight gradients (MOK_FLAG_MXFP8_WGRAD).  --copy-mib
 // runs one plain device copy kernel of that size first (HBM byte-counter
 // calibration).
 #include <hip/hip_runtime.h>
@@ -75,7 +76,7 @@ __global__ void copy_kernel(const uint4* a, uint4* b, int64_t n) {
 int main(int argc, char** argv) {
   int T = 8192, d = 4096, E = 128, k = 8, F = 1536, steps = 3, warmup = 1, copy_mib = 0;
   float zipf = 1.2f;
-  bool backward = true, mxfp8 = false;
+  bool backward = true, mxfp8 = false, mxfp8_wgrad = false;
   std::string inputs;
   for (int i = 1; i < argc; ++i) {
     std::string a = argv[i];
@@ -92,6 +93,7 @@ int main(int argc, char** argv) {
     else if (a == "--forward-only") backward = false;
     else if (a == "--inputs") inputs = next();
     else if (a == "--mxfp8") mxfp8 = true;
+    else if (a == "--mxfp8-wgrad") mxfp8 = mxfp8_wgrad = true;
     else { fprintf(stderr, "unknown argument %s\n", a.c_str()); return 2; }
   }
   if (copy_mib > 0) {
@@ -111,6 +113,7 @@ int main(int argc, char** argv) {
   cfg.T = T; cfg.d = d; cfg.E = E; cfg.ffn = F; cfg.expert_begin = 0; cfg.expert_end = E;
   cfg.precision = mxfp8 ? MOK_PREC_MXFP8 : MOK_PREC_BF16;
   cfg.flags = backward ? MOK_FLAG_SAVE_FOR_BACKWARD : 0;
+  if (mxfp8_wgrad && backward) cfg.flags |= MOK_FLAG_MXFP8_WGRAD;
   size_t ws_bytes, sv_bytes;
   MOKCHECK(mok_moe_workspace_query(&cfg, k, &ws_bytes, &sv_bytes));
   const int64_t xw = (int64_t)T * d, ww = (int64_t)E * F * d;

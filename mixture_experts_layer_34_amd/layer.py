@@ -27,6 +27,7 @@ class MoeShape:
     renorm: bool = False          # gates renormalised over the k chosen experts
     separate_route_sort: bool = False  # never the one-launch router + sort of small calls
     gemm_path: str = "auto"            # forward expert products: "auto", "tiled" or "stream" (small calls)
+    mxfp8_wgrad: bool = False          # MXFP8 training: weight gradients on the scaled MFMA too
 
     @property
     def e_end(self):
@@ -46,7 +47,8 @@ class MoeShape:
                  | (mok.MOK_FLAG_RENORM_GATES if self.renorm else 0)
                  | (mok.MOK_FLAG_SEPARATE_ROUTE_SORT if self.separate_route_sort else 0)
                  | (mok.MOK_FLAG_TILED_GEMMS if self.gemm_path == "tiled" else 0)
-                 | (mok.MOK_FLAG_STREAM_GEMMS if self.gemm_path == "stream" else 0))
+                 | (mok.MOK_FLAG_STREAM_GEMMS if self.gemm_path == "stream" else 0)
+                 | (mok.MOK_FLAG_MXFP8_WGRAD if self.mxfp8_wgrad else 0))
         return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
                                self.minibatch_rows, self.ring_bytes, flags)
 

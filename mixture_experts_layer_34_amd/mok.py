@@ -21,6 +21,7 @@ MOK_FLAG_RENORM_GATES = 0x4
 MOK_FLAG_SEPARATE_ROUTE_SORT = 0x8
 MOK_FLAG_TILED_GEMMS = 0x10
 MOK_FLAG_STREAM_GEMMS = 0x20
+MOK_FLAG_MXFP8_WGRAD = 0x40
 STAGES = ["router", "sort", "dispatch", "gemm_up", "gemm_down", "combine", "bwd_gate", "gemm_dh", "gemm_dx",
           "reduce_dx", "gemm_dw2", "regather", "gemm_dw13"]
 MOK_NUM_STAGES = len(STAGES)
@@ -44,7 +45,8 @@ class mok_saved_layout(ctypes.Structure):
 class mok_workspace_layout(ctypes.Structure):
     _fields_ = [("status", ctypes.c_size_t), ("xp", ctypes.c_size_t), ("xp_scale", ctypes.c_size_t),
                 ("xp_rows", ctypes.c_int64), ("dy", ctypes.c_size_t), ("dab", ctypes.c_size_t),
-                ("dxp", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+                ("dxp", ctypes.c_size_t), ("wq", ctypes.c_size_t), ("wq_scale", ctypes.c_size_t),
+                ("k_pad", ctypes.c_int64), ("total", ctypes.c_size_t)]
 
 
 MOK_CHECK_LOGITS, MOK_CHECK_INDEX = 0x1, 0x2

@@ -62,7 +62,7 @@ __all__ = [
     "route", "route_backward", "router_logits", "router_logits_backward",
     "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
-    "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq", "mxfp8_qdq_rows",
+    "bf16_round", "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq", "mxfp8_qdq_rows",
     "forward_token", "backward_token", "expert_weight_grads",
 ]
 
@@ -282,6 +282,18 @@ def e4m3_decode(codes):
     return s * val
 
 
+def bf16_round(v):
+    """A float32 computation stored as bfloat16: each value is rounded to
+    float32, then to the nearest bfloat16 (8 significant bits; spacing
+    2^(e-7) in [2^e, 2^(e+1)), 2^-133 below 2^-126), ties to even.  Finite
+    inputs."""
+    f = np.asarray(_f64(v), np.float32).astype(np.float64)
+    _, ex = np.frexp(f)
+    e = np.maximum(ex - 1, -126)
+    q = np.ldexp(1.0, e - 7)
+    return np.rint(f / q) * q
+
+
 def mxfp8_quantize(v, block: int = 32):
     """MX block quantisation along the last axis [kucoin §02: MXFP8 activation
     quantisation fused into the dispatch, grouped GEMM and SwiGLU paths].
@@ -439,8 +451,12 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     mxfp8_wgrad (with mxfp8) also runs the weight gradients in MXFP8: their
     contraction runs over the expert's rows, so each operand is quantised
     along the rows of the expert's segment (mxfp8_qdq_rows, blocks of 32 rows
-    from the expert's first row in the placement order):
-      dW2_e = Qr(dy_e)^T Qr(h_e),  dW1_e = Qr(da_e)^T Qr(x_e),  dW3_e = Qr(db_e)^T Qr(x_e).
+    from the expert's first row in the placement order).  The operands
+    quantised are the tensors as the layer holds them, at the precision of
+    its activations: dy, h, da and db rounded to bfloat16 (bf16_round; x
+    already is), the reading taken where the pages give no recipe:
+      dW2_e = Qr(bf16(dy_e))^T Qr(bf16(h_e)),
+      dW1_e = Qr(bf16(da_e))^T Qr(x_e),  dW3_e = Qr(bf16(db_e))^T Qr(x_e).
     """
     x = _f64(x)
     g = _f64(dout)
@@ -498,9 +514,9 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
             dXp[r0:r1] = da @ _f64(W1[i]) + db @ _f64(W3[i])
         if mxfp8_wgrad:
             xq = mxfp8_qdq_rows(Xp[r0:r1])
-            dW2[i] = mxfp8_qdq_rows(dy).T @ mxfp8_qdq_rows(h)
-            dW1[i] = mxfp8_qdq_rows(da).T @ xq
-            dW3[i] = mxfp8_qdq_rows(db).T @ xq
+            dW2[i] = mxfp8_qdq_rows(bf16_round(dy)).T @ mxfp8_qdq_rows(bf16_round(h))
+            dW1[i] = mxfp8_qdq_rows(bf16_round(da)).T @ xq
+            dW3[i] = mxfp8_qdq_rows(bf16_round(db)).T @ xq
         else:
             dW2[i] = dy.T @ h
             dW1[i] = da.T @ Xp[r0:r1]
@@ -587,6 +603,6 @@ def expert_weight_grads(X_e, gate_e, dout_e, W1e, W3e, W2e, mxfp8: bool = False,
         if not mxfp8:
             raise ValueError("mxfp8_wgrad needs mxfp8")
         xq = mxfp8_qdq_rows(X)
-        return (mxfp8_qdq_rows(da).T @ xq, mxfp8_qdq_rows(db).T @ xq,
-                mxfp8_qdq_rows(dy).T @ mxfp8_qdq_rows(h))
+        return (mxfp8_qdq_rows(bf16_round(da)).T @ xq, mxfp8_qdq_rows(bf16_round(db)).T @ xq,
+                mxfp8_qdq_rows(bf16_round(dy)).T @ mxfp8_qdq_rows(bf16_round(h)))
     return da.T @ X, db.T @ X, dy.T @ h

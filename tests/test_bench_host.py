@@ -63,3 +63,20 @@ def test_stage_work_mxfp8_bytes():
     assert nb["gemm_dx"] == 2 * P * F * q + 2 * E * F * d * q + P * d * 2
     assert nb["gemm_up"] == P * d * q + 2 * E * F * d * q + P * F * q + 3 * P * F * 2
     assert nb["gemm_dw13"] == nbb["gemm_dw13"] and nb["gemm_dw2"] == nbb["gemm_dw2"]
+
+
+def test_stage_work_mxfp8_weight_gradients():
+    """With MXFP8 weight gradients: the dW GEMMs read one byte (plus a scale
+    per 32) per operand element and count against the MXFP8 peak; the
+    regather stage reads the bf16 dY, H, [dA | dB] and x rows and writes the
+    row-quantised codes of all four."""
+    import workloads as W
+    w = W.get("mxfp8_train")
+    P, U = 1024, 200
+    q, d, F, E = 1 + 1 / 32, w.d, w.F, w.E
+    _, nb = bench.stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=True)
+    assert nb["gemm_dw2"] == P * d * q + P * F * q + E * d * F * 4
+    assert nb["gemm_dw13"] == 2 * P * F * q + P * d * q + 2 * E * F * d * 4
+    assert nb["regather"] == (P * d + 3 * P * F) * 2 + U * d * 2 + (2 * d + 3 * F) * P * q
+    for n in ("gemm_dw2", "gemm_dw13"):
+        assert bench.gemm_peak("mxfp8", n, True) == bench.PEAK_TFLOPS["mxfp8"]

@@ -28,7 +28,28 @@ def _lib():
     L = ctypes.CDLL(LIB)
     L.mok_diag_mfma_scale_block.restype = ctypes.c_int32
     L.mok_diag_mfma_scale_block.argtypes = [ctypes.c_void_p] * 7
+    L.mok_diag_e4m3_check.restype = ctypes.c_int32
+    L.mok_diag_e4m3_check.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p]
     return L
+
+
+def test_e4m3_conversion_instruction_matches_the_definition():
+    """The E4M3 encoding the layer's quantisers use (the conversion
+    instruction on the value clamped to +-448, alone and four packed) equals
+    the software encoder of the OCP definition on every float32 of magnitude
+    below 2^9, both signs: 2.28e9 values."""
+    note("e4m3 conversion instruction, exhaustive")
+    blocks = 4096
+    dev = torch.device("cuda")
+    count = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
+    first = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
+    assert _lib().mok_diag_e4m3_check(0x44000000, count.data_ptr(), first.data_ptr(), blocks,
+                                      torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    bad = int(count.to(torch.int64).sum())
+    firsts = [hex(int(v) & 0xFFFFFFFF) for v in first.cpu().numpy() if int(v) != -1][:5]
+    assert bad == 0, (bad, firsts)
 
 
 def _finite_codes(rng, shape):

@@ -1,0 +1,241 @@
+"""GPU parity of the MXFP8 weight gradients (MOK_FLAG_MXFP8_WGRAD).
+
+Three checks, each pinning one step:
+  * the row quantiser: the transposed operands (dY, H, [dA | dB] and the x
+    rows) equal the oracle's quantiser applied to the same bf16 rows bit for
+    bit (codes per column and expert segment, pair-plane scales, zero codes
+    past each expert's rows);
+  * the scaled-MFMA products: dW1, dW3, dW2 against the float64 product of
+    the device's own dequantised codes, within 1e-3 (infinity norm, relative;
+    measured 1e-4 - 3e-4, the MFMA's accumulation);
+  * the whole backward against the oracle's backward(mxfp8=True,
+    mxfp8_wgrad=True): relative Frobenius error within 3e-2, empty experts
+    exactly zero.  The Frobenius norm, not the infinity norm: quantising along
+    the rows turns the operands' last-bit differences (the device's dA, dB,
+    dY and H come out of MFMA accumulations and bf16 storage, the oracle's are
+    exact) into whole E4M3 steps on the few elements that sit near a rounding
+    boundary, each moving one product term by up to 1/8 of it.  Rounding the
+    oracle's own operands to bf16 alone moves its dW by up to 8.6e-2 in the
+    infinity norm (T 700, d 256, E 8, k 2, F 384, on the CPU), so no
+    element-wise bar near 3e-2 holds for any implementation that stores the
+    operands in bf16; the measured infinity-norm errors are reported.
+Every other output equals the MXFP8 backward without the flag bit for bit
+(the flag changes only the weight-gradient products); reruns are bitwise
+identical."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mok_oracle as O
+from mixture_experts_layer_34_amd.layer import MoeBuffers
+from tests.gpu_case import LazyExperts, host_inputs, note, rel_inf, run_layer, saved_arrays, shape_of, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL_MX = 3e-2      # relative Frobenius error against the oracle
+TOL_OWN = 1e-3     # infinity norm against the product of the device's own codes
+
+
+def _buf(w, wgrad):
+    shape = shape_of(w, w.T, True)
+    shape.mxfp8_wgrad = wgrad
+    return MoeBuffers(shape)
+
+
+def _pad128(n):
+    return (n + 127) // 128 * 128
+
+
+def _operands(w, inp, buf):
+    """The device's bf16 operands (rows in placement order) and its
+    transposed codes and scales of each: [(name, rows [P, C], codes [C, k_pad],
+    scales [C, k_pad / 32])]."""
+    lay = buf.ws_layout
+    kp = lay["k_pad"]
+    d, F = w.d, w.F
+    s = buf.shape
+    P = int(to_np(buf.offsets)[w.e_end])
+    codes = buf.workspace[lay["wq"]:lay["wq"] + (2 * d + 3 * F) * kp].cpu().numpy()
+    scales = buf.workspace[lay["wq_scale"]:lay["wq_scale"] + (2 * d + 3 * F) * kp // 32].cpu().numpy()
+    dy = buf.workspace_view("dy", torch.bfloat16, (s.T * s.k, d))[:P].float().cpu().numpy()
+    dab = buf.workspace_view("dab", torch.bfloat16, (s.T * s.k, 2 * F))[:P].float().cpu().numpy()
+    H = buf.saved_view("H", torch.bfloat16, (s.T * s.k, F))[:P].float().cpu().numpy()
+    por = saved_arrays(buf)["pair_of_row"][:P]
+    X = to_np(inp["x"])[por // w.k]
+    out, c_off, s_off = [], 0, 0
+    for name, M in (("dY", dy), ("H", H), ("dA|dB", dab), ("X", X)):
+        C = M.shape[1]
+        cod = codes[c_off:c_off + C * kp].reshape(C, kp)
+        sc = scales[s_off:s_off + C * kp // 32].reshape(kp // 64, C, 2).transpose(1, 0, 2).reshape(C, kp // 32)
+        out.append((name, M, cod, sc))
+        c_off += C * kp
+        s_off += C * kp // 32
+    return out
+
+
+def _segments(w, buf):
+    """(local expert, first row, end row, first padded column) of each local expert."""
+    offs = to_np(buf.offsets)
+    segs, pos = [], 0
+    for e in range(w.expert_begin, w.e_end):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        segs.append((e - w.expert_begin, r0, r1, pos))
+        pos += _pad128(r1 - r0)
+    return segs
+
+
+def _check_codes(w, inp, buf, experts=None):
+    """The four transposed operands against O.mxfp8_quantize of the device's
+    own bf16 rows, expert by expert."""
+    for name, M, cod, sc in _operands(w, inp, buf):
+        C = M.shape[1]
+        for i, r0, r1, pos in _segments(w, buf):
+            if experts is not None and i not in experts:
+                continue
+            n = _pad128(r1 - r0)
+            seg = np.zeros((n, C))
+            seg[:r1 - r0] = M[r0:r1]
+            rq, rs = O.mxfp8_quantize(seg.T)      # along the rows, blocks of 32 from the expert's first row
+            assert np.array_equal(cod[:, pos:pos + n], rq), f"{name} codes of local expert {i}"
+            assert np.array_equal(sc[:, pos // 32:(pos + n) // 32], rs), f"{name} scales of local expert {i}"
+
+
+def _own_product_errors(w, inp, buf, experts=None):
+    """dW against the float64 product of the device's own dequantised codes."""
+    ops = {name: O.mxfp8_dequantize(cod, sc) for name, _, cod, sc in _operands(w, inp, buf)}
+    g = buf.grads
+    F = w.F
+    errs = {}
+    for i, r0, r1, pos in _segments(w, buf):
+        if experts is not None and i not in experts:
+            continue
+        n = _pad128(r1 - r0)
+        ab, x = ops["dA|dB"][:, pos:pos + n], ops["X"][:, pos:pos + n]
+        errs[f"dW1[{i}]"] = rel_inf(to_np(g["dW1"][i]), ab[:F] @ x.T)
+        errs[f"dW3[{i}]"] = rel_inf(to_np(g["dW3"][i]), ab[F:] @ x.T)
+        errs[f"dW2[{i}]"] = rel_inf(to_np(g["dW2"][i]), ops["dY"][:, pos:pos + n] @ ops["H"][:, pos:pos + n].T)
+    return errs
+
+
+def rel_fro(gpu, ref) -> float:
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    den = np.linalg.norm(r)
+    return float(np.linalg.norm(g - r) / (den if den > 0 else 1.0))
+
+
+def _wgrad_errors(w, inp, buf):
+    """Per local expert: (relative Frobenius, relative infinity-norm) errors
+    of dW1, dW3, dW2 against the oracle."""
+    h = host_inputs(inp)
+    W1, W3, W2 = (to_np(inp[n]).astype(np.float64) for n in ("W1", "W3", "W2"))
+    fw = O.forward(h["x"], h["logits"], W1, W3, W2, w.k, w.expert_begin, w.e_end, mxfp8=True)
+    bw = O.backward(h["dout"], h["x"], h["logits"], W1, W3, W2, w.k, fw, w.expert_begin, w.e_end, mxfp8=True,
+                    mxfp8_wgrad=True)
+    g = buf.grads
+    counts = to_np(buf.counts)
+    fro, inf = {}, {}
+    for n in ("dW1", "dW3", "dW2"):
+        gw = to_np(g[n])
+        for i in range(w.E_loc):
+            fro[f"{n}[{i}]"] = rel_fro(gw[i], bw[n][i])
+            inf[f"{n}[{i}]"] = rel_inf(gw[i], bw[n][i])
+            if counts[w.expert_begin + i] == 0:
+                assert not gw[i].any(), f"{n}[{i}] of an empty expert is not zero"
+    return fro, inf
+
+
+CASES = [
+    # ragged segments: partial 32-row blocks and 128-row padding in most experts
+    ("ragged", "bf16_train", dict(T=700, d=256, E=8, k=2, F=384)),
+    # every expert holds T rows: 33 (a 32-row block boundary, then one row)
+    ("rows-33", "bf16_fwd", dict(T=33, d=256, E=4, k=4, F=128)),
+    # 129 rows: a 128-row padded block boundary, then one row
+    ("rows-129", "bf16_fwd", dict(T=129, d=512, E=3, k=3, F=256)),
+    # a local expert range (remote slots skipped)
+    ("local", "bf16_fwd", dict(T=600, d=256, E=12, k=3, F=256, expert_begin=4, expert_end=9)),
+    # one expert takes nearly every row, the others few or none
+    ("one-hot", "bf16_train", dict(T=520, d=256, E=6, k=1, F=512, notes={"zipf": 4.0})),
+    ("one-token", "bf16_fwd", dict(T=1, d=256, E=8, k=3, F=256)),
+]
+
+
+@pytest.mark.parametrize("name,base,over", CASES, ids=[c[0] for c in CASES])
+def test_mxfp8_wgrad_small_matches_oracle(name, base, over):
+    w = W.scaled(base, precision="mxfp8", backward=True, **over)
+    note(f"mxfp8 wgrad {name} {over}")
+    inp = W.make_inputs(w, device="cuda")
+    ref = run_layer(w, inp, backward=True, buf=_buf(w, False))
+    ref_out = {n: ref.grads[n].clone() for n in ("dx", "dgate", "dlogits")}
+    buf = run_layer(w, inp, backward=True, buf=_buf(w, True))
+    for n, v in ref_out.items():
+        assert torch.equal(v, buf.grads[n]), f"{n} differs from the backward without MXFP8 weight gradients"
+    _check_codes(w, inp, buf)
+    own = _own_product_errors(w, inp, buf)
+    note(f"  own codes: max {max(own.values()):.3e} ({max(own, key=own.get)})")
+    assert max(own.values()) <= TOL_OWN, own
+    fro, inf = _wgrad_errors(w, inp, buf)
+    note(f"  oracle: Frobenius max {max(fro.values()):.3e} ({max(fro, key=fro.get)}), "
+         f"infinity norm max {max(inf.values()):.3e} ({max(inf, key=inf.get)})")
+    bad = {k: v for k, v in fro.items() if v > TOL_MX}
+    assert not bad, bad
+
+
+def test_mxfp8_wgrad_zero_tokens():
+    w = W.scaled("bf16_fwd", precision="mxfp8", backward=True, T=0, d=256, E=8, k=2, F=128)
+    note("mxfp8 wgrad zero tokens")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True, buf=_buf(w, True))
+    for n in ("dW1", "dW3", "dW2"):
+        assert not buf.grads[n].any(), f"{n} not zero"
+
+
+def test_mxfp8_wgrad_full_size_sampled():
+    """The training workload in MXFP8 with MXFP8 weight gradients: the
+    lightest, median and heaviest experts' dW1, dW3, dW2 against the oracle's
+    per-expert gradients (rows in placement order), and the codes of the
+    heaviest expert's operands bit for bit."""
+    w = W.scaled("bf16_train", precision="mxfp8")
+    note("mxfp8 wgrad full size")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True, buf=_buf(w, True))
+    h = host_inputs(inp)
+    idx = to_np(buf.topk_idx)
+    counts = to_np(buf.counts)
+    _, gate, _, _ = O.route(h["logits"], w.k)
+    _, offsets, _, por = O.layout(idx, w.E)
+    W1, W3, W2 = LazyExperts(inp["W1"]), LazyExperts(inp["W3"]), LazyExperts(inp["W2"])
+    g = buf.grads
+    fro, inf = {}, {}
+    order = np.argsort(counts, kind="stable")
+    picks = (int(order[0]), int(order[len(order) // 2]), int(order[-1]))
+    _check_codes(w, inp, buf, experts=set(picks))
+    own = _own_product_errors(w, inp, buf, experts=set(picks))
+    note("  own codes " + ", ".join(f"{k}={v:.2e}" for k, v in own.items()))
+    assert max(own.values()) <= TOL_OWN, own
+    for e in picks:
+        rows = por[offsets[e]:offsets[e + 1]]
+        tok, slot = rows // w.k, rows % w.k
+        r1, r3, r2 = O.expert_weight_grads(h["x"][tok], gate[tok, slot], h["dout"][tok], W1[e], W3[e], W2[e],
+                                           mxfp8=True, mxfp8_wgrad=True)
+        for n, r in (("dW1", r1), ("dW3", r3), ("dW2", r2)):
+            fro[f"{n}[{e}]"] = rel_fro(to_np(g[n][e]), r)
+            inf[f"{n}[{e}]"] = rel_inf(to_np(g[n][e]), r)
+    note("  oracle Frobenius " + ", ".join(f"{k}={v:.2e}" for k, v in fro.items()))
+    note("  oracle infinity norm " + ", ".join(f"{k}={v:.2e}" for k, v in inf.items()))
+    bad = {k: v for k, v in fro.items() if v > TOL_MX}
+    assert not bad, bad
+
+
+def test_mxfp8_wgrad_reruns_bitwise_identical():
+    w = W.scaled("bf16_train", precision="mxfp8", backward=True, T=777, d=256, E=16, k=4, F=384)
+    note("mxfp8 wgrad determinism")
+    inp = W.make_inputs(w, device="cuda")
+    buf = run_layer(w, inp, backward=True, buf=_buf(w, True))
+    first = {n: buf.grads[n].clone() for n in ("dW1", "dW3", "dW2")}
+    for rep in range(2):
+        buf.workspace.fill_(0xFF)
+        buf = run_layer(w, inp, backward=True, buf=buf)
+        for n, v in first.items():
+            assert torch.equal(v, buf.grads[n]), f"rerun {rep}: {n} differs"

@@ -18,6 +18,7 @@ import math
 import os
 
 import numpy as np
+import torch
 
 from oracle import mok_oracle as O
 
@@ -205,6 +206,11 @@ def test_mxfp8_token_and_expert_views_match_the_layer():
     assert (rop >= 0).all()
 
 
+def _bf16(vals):
+    """bfloat16 rounding of a float32 computation, by torch's own conversion."""
+    return torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16).double().tolist()
+
+
 def _brute_wgrad_rows(x, logits, g, W1, W3, W2, k):
     """MXFP8 weight gradients by scalar loops, each operand quantised along
     the rows of its expert's segment: the segment lists the expert's (token,
@@ -232,7 +238,8 @@ def _brute_wgrad_rows(x, logits, g, W1, W3, W2, k):
             dh = _matmul_nt([_qdq_row(dy)], w2tq[e])[0]
             da = [dh[f] * b[f] * _sig(a[f]) * (1.0 + a[f] * (1.0 - _sig(a[f]))) for f in range(F)]
             db = [dh[f] * _silu(a[f]) for f in range(F)]
-            seg[e].append((list(map(float, x[t])), dy, h, da, db))
+            # the operands as the layer holds them: bf16 (x already is)
+            seg[e].append((list(map(float, x[t])), _bf16(dy), _bf16(h), _bf16(da), _bf16(db)))
     out = {"dW1": np.zeros((E, F, d)), "dW3": np.zeros((E, F, d)), "dW2": np.zeros((E, d, F))}
     for e in range(E):
         if not seg[e]:
@@ -315,3 +322,23 @@ def test_expert_view_row_quantised():
                                     mxfp8=True, mxfp8_wgrad=True)
         for gv, name in zip(got, ("dW1", "dW3", "dW2")):
             np.testing.assert_allclose(gv, bw[name][e], rtol=1e-10, atol=1e-12)
+
+
+def test_bf16_round_matches_torch_and_hand_cases():
+    """bf16_round: torch's bfloat16 conversion of the same values (float64 to
+    float32 to bfloat16, nearest-even at each step), ties to even by hand,
+    subnormal spacing, idempotence."""
+    rng = np.random.default_rng(17)
+    v = np.concatenate([rng.standard_normal(20000) * np.exp(rng.uniform(-60, 60, 20000)),
+                        rng.standard_normal(1000) * 1e-39, [0.0, -0.0, 1.0, -3.5]])
+    ref = torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(O.bf16_round(v), ref)
+    # spacing 2^-7 at 1: halfway cases go to the even mantissa
+    assert O.bf16_round(1 + 2.0 ** -8) == 1.0
+    assert O.bf16_round(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert O.bf16_round(-(1 + 3 * 2.0 ** -8)) == -(1 + 2.0 ** -6)
+    assert O.bf16_round(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7
+    # below 2^-126 the spacing is 2^-133
+    assert O.bf16_round(3 * 2.0 ** -134) == 2 * 2.0 ** -133
+    r = O.bf16_round(v)
+    np.testing.assert_array_equal(O.bf16_round(r), r)
