@@ -754,13 +754,14 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
     const int32_t* tp128 = at<int32_t>(saved, tp_off) + 1 * (E_loc + 1);
     const int32_t* s_por = at<int32_t>(saved, sl.pair_of_row);
     const void* Hs = at<void>(saved, sl.H);
-    {
-      StageMark mark(c, s, MOK_STAGE_REGATHER);
-      MOK_HIP(launch_quantize_rows_t(dy, d, nullptr, 1, d, offs, eb, E_loc, tp128, P_max, kp, dyT, dyS, s));
-      MOK_HIP(launch_quantize_rows_t(Hs, F, nullptr, 1, F, offs, eb, E_loc, tp128, P_max, kp, hT, hS, s));
-      MOK_HIP(launch_quantize_rows_t(dab, 2 * F, nullptr, 1, 2 * F, offs, eb, E_loc, tp128, P_max, kp, abT, abS, s));
-      MOK_HIP(launch_quantize_rows_t(x, d, s_por, k, d, offs, eb, E_loc, tp128, P_max, kp, xT, xS, s));
-    }
+    // dY is formed again from dout and the gates (the reverse-combine's
+    // product and rounding), which reads T rows of dout instead of P of dY
+    const QrJob jobs[4] = {
+        {(const uint16_t*)dout, d, s_por, s_gate, d, dyT, dyS},
+        {(const uint16_t*)Hs, F, nullptr, nullptr, F, hT, hS},
+        {(const uint16_t*)dab, 2 * F, nullptr, nullptr, 2 * F, abT, abS},
+        {(const uint16_t*)x, d, s_por, nullptr, d, xT, xS}};
+    MOK_STAGE(MOK_STAGE_REGATHER, launch_quantize_rows_t(jobs, 4, k, offs, eb, E_loc, tp128, P_max, kp, s));
     GroupedGemmArgs w2 = g;
     w2.k_pad = kp;
     w2.A = dyT;

@@ -69,15 +69,25 @@ hipError_t launch_route_sort_small(const float* logits, int T, int E, int k, int
                                    int32_t* tile_prefix, int32_t* expert_order, int32_t* row_of_pair,
                                    int32_t* pair_of_row, int32_t* status, hipStream_t s);
 
-// MXFP8 quantisation of a bf16 [rows, C] matrix (row stride ld elements;
-// gathered: row r is src row gather_rows[r] / k_top) along its rows, per local
+// MXFP8 quantisation of bf16 [rows, C] matrices along their rows, per local
 // expert in blocks of 32 from the expert's first row, written transposed:
 // codes [C, P_pad] at column 128 tp128[e] + (r - offsets[e]), scales in pair
-// planes [P_pad / 64, C, 2].  C a multiple of 64, P_pad of 128 and at least
-// 128 (P_max / 128 + E_loc).
-hipError_t launch_quantize_rows_t(const void* src, int64_t ld, const int32_t* gather_rows, int k_top, int C,
-                                  const int32_t* offsets, int eb, int E_loc, const int32_t* tp128, int64_t P_max,
-                                  int64_t P_pad, uint8_t* dst, uint8_t* dsc, hipStream_t s);
+// planes [P_pad / 64, C, 2].  Row r of a job is src row r (row stride ld
+// elements), or with `gather` src row gather[r] / k_top, times gate[gather[r]]
+// and rounded to bf16 when `gate` is set.  C a multiple of 64, P_pad of 128
+// and at least 128 (P_max / 128 + E_loc).  All jobs in one launch.
+constexpr int kQrMaxJobs = 4;
+struct QrJob {
+  const uint16_t* src;  // bf16
+  int64_t ld;
+  const int32_t* gather;
+  const float* gate;
+  int C;
+  uint8_t* dst;
+  uint8_t* dsc;
+};
+hipError_t launch_quantize_rows_t(const QrJob* jobs, int njobs, int k_top, const int32_t* offsets, int eb,
+                                  int E_loc, const int32_t* tp128, int64_t P_max, int64_t P_pad, hipStream_t s);
 
 hipError_t launch_counting_sort(const int32_t* idx, int T, int k, int E, int eb, int ee,
                                 int nchunks, int32_t* chunk_counts, int32_t* chunk_base,

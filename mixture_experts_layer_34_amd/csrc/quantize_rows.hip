@@ -22,48 +22,75 @@ namespace {
 
 constexpr int kQrRows = 128;  // rows per unit (one padded K stage of the GEMMs)
 constexpr int kQrCols = 64;   // columns per unit
+static_assert(kQrMaxJobs >= 4, "dY, H, [dA | dB] and x in one launch");
 
-// One workgroup of 256 threads per (128-row block of a local expert's padded
-// segment, 64 columns) unit, persistent over the units.  The block's rows
-// come in coalesced (16 bytes per thread, 8 threads per 128-byte row piece)
-// into LDS; thread (c = tid / 4, b = tid % 4) then takes column c of the
-// block's 32-row sub-block b: amax, scale, 32 codes (two 16-byte stores), so
-// that the four threads of a column, adjacent lanes, write its 128 bytes of
-// the block together.  In LDS the 16-byte column chunks of row r are XOR-ed
-// with its sub-block (r / 32) so that those four threads, reading the same
-// column of rows 32 apart, hit different banks.
-template <bool GATHER>
-__global__ __launch_bounds__(256) void quantize_rows_t_kernel(const bf16_t* __restrict__ src, int64_t ld,
-                                                              const int32_t* __restrict__ gather_rows, int k_top,
-                                                              int C, const int32_t* __restrict__ offsets, int eb,
-                                                              int E_loc, const int32_t* __restrict__ tp128,
-                                                              int64_t P_pad, uint8_t* __restrict__ dst,
-                                                              uint8_t* __restrict__ dsc) {
+// One workgroup of 256 threads per (matrix, 128-row block of a local
+// expert's padded segment, 64 columns) unit, persistent over the units of all
+// the matrices of one launch.  The block's rows come in coalesced (16 bytes
+// per thread, 8 threads per 128-byte row piece) into LDS; thread (c = tid /
+// 4, b = tid % 4) then takes column c of the block's 32-row sub-block b:
+// amax, scale, 32 codes (two 16-byte stores), so that the four threads of a
+// column, adjacent lanes, write its 128 bytes of the block together.  In LDS
+// the 16-byte column chunks of row r are XOR-ed with its sub-block (r / 32)
+// so that those four threads, reading the same column of rows 32 apart, hit
+// different banks.  A gated matrix (dY) is formed while loading: row r is
+// bf16(gate[p] * src[p / k]), p = gather[r], the same product and rounding
+// as the reverse-combine's dY rows.
+struct QrJobs {
+  QrJob job[kQrMaxJobs];
+  int njobs, k_top, eb, E_loc;
+  const int32_t* offsets;
+  const int32_t* tp128;
+  int64_t P_pad;
+};
+
+__global__ __launch_bounds__(256) void quantize_rows_t_kernel(QrJobs a) {
   __shared__ bf16_t tile[kQrRows][kQrCols];
   const int tid = threadIdx.x;
-  const int ncb = C / kQrCols;
-  const int total = sload(tp128 + E_loc) * ncb;
+  const int nblk = sload(a.tp128 + a.E_loc);
+  int total = 0;
+  for (int j = 0; j < a.njobs; ++j) total += nblk * (a.job[j].C / kQrCols);
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
-    const int t = u / ncb, cb = u % ncb;
-    int lo = 0, hi = E_loc - 1;  // the local expert whose 128-row blocks hold t
+    int j = 0, uj = u;
+    while (uj >= nblk * (a.job[j].C / kQrCols)) {
+      uj -= nblk * (a.job[j].C / kQrCols);
+      ++j;
+    }
+    const QrJob& jb = a.job[j];
+    const int ncb = jb.C / kQrCols;
+    const int t = uj / ncb, cb = uj % ncb;
+    int lo = 0, hi = a.E_loc - 1;  // the local expert whose 128-row blocks hold t
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (sload(tp128 + mid) <= t) lo = mid; else hi = mid - 1;
+      if (sload(a.tp128 + mid) <= t) lo = mid; else hi = mid - 1;
     }
-    const int blk = t - sload(tp128 + lo);
-    const int r0 = sload(offsets + eb + lo) + blk * kQrRows;
-    const int rend = sload(offsets + eb + lo + 1);
+    const int blk = t - sload(a.tp128 + lo);
+    const int r0 = sload(a.offsets + a.eb + lo) + blk * kQrRows;
+    const int rend = sload(a.offsets + a.eb + lo + 1);
     const int c0 = cb * kQrCols;
     __syncthreads();  // the previous unit's tile is read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = tid + 256 * j;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int q = tid + 256 * q4;
       const int rr = q >> 3, ch = q & 7;
       const int row = r0 + rr;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (row < rend) {
-        const int64_t srow = GATHER ? (int64_t)(gather_rows[row] / k_top) : (int64_t)row;
-        v = *reinterpret_cast<const u32x4_t*>(src + srow * ld + c0 + ch * 8);
+        int64_t srow = row;
+        float g = 1.0f;
+        if (jb.gather) {
+          const int p = jb.gather[row];
+          srow = p / a.k_top;
+          if (jb.gate) g = jb.gate[p];
+        }
+        v = *reinterpret_cast<const u32x4_t*>(jb.src + srow * jb.ld + c0 + ch * 8);
+        if (jb.gate) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo_ = g * __uint_as_float(v[i] << 16), hi_ = g * __uint_as_float(v[i] & 0xFFFF0000u);
+            v[i] = (uint32_t)f2bf(lo_) | ((uint32_t)f2bf(hi_) << 16);
+          }
+        }
       }
       *reinterpret_cast<u32x4_t*>(&tile[rr][(ch ^ (rr >> 5)) * 8]) = v;
     }
@@ -84,30 +111,38 @@ __global__ __launch_bounds__(256) void quantize_rows_t_kernel(const bf16_t* __re
       w[q] = e4m3x4(ldexpf(v[4 * q], -se), ldexpf(v[4 * q + 1], -se), ldexpf(v[4 * q + 2], -se),
                     ldexpf(v[4 * q + 3], -se));
     const int64_t pos = (int64_t)t * kQrRows + 32 * b;
-    uint8_t* out = dst + (int64_t)(c0 + c) * P_pad + pos;
+    uint8_t* out = jb.dst + (int64_t)(c0 + c) * a.P_pad + pos;
     *reinterpret_cast<u32x4_t*>(out) = u32x4_t{w[0], w[1], w[2], w[3]};
     *reinterpret_cast<u32x4_t*>(out + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-    dsc[(pos / 64) * 2 * C + 2 * (c0 + c) + ((pos / 32) & 1)] = (uint8_t)(se + 127);
+    jb.dsc[(pos / 64) * 2 * jb.C + 2 * (c0 + c) + ((pos / 32) & 1)] = (uint8_t)(se + 127);
   }
 }
 
 }  // namespace
 
-hipError_t launch_quantize_rows_t(const void* src, int64_t ld, const int32_t* gather_rows, int k_top, int C,
-                                  const int32_t* offsets, int eb, int E_loc, const int32_t* tp128, int64_t P_max,
-                                  int64_t P_pad, uint8_t* dst, uint8_t* dsc, hipStream_t s) {
-  if (C % kQrCols || P_pad % kQrRows) return hipErrorInvalidValue;
-  // units: at most (P_max / 128 + E_loc) blocks of 128 rows, times C / 64
-  const int64_t worst = (P_max / kQrRows + E_loc) * (int64_t)(C / kQrCols);
+hipError_t launch_quantize_rows_t(const QrJob* jobs, int njobs, int k_top, const int32_t* offsets, int eb,
+                                  int E_loc, const int32_t* tp128, int64_t P_max, int64_t P_pad, hipStream_t s) {
+  if (njobs < 1 || njobs > kQrMaxJobs || P_pad % kQrRows) return hipErrorInvalidValue;
+  QrJobs a{};
+  int64_t cols = 0;
+  for (int j = 0; j < njobs; ++j) {
+    if (jobs[j].C % kQrCols || (jobs[j].gate && !jobs[j].gather)) return hipErrorInvalidValue;
+    a.job[j] = jobs[j];
+    cols += jobs[j].C / kQrCols;
+  }
+  a.njobs = njobs;
+  a.k_top = k_top;
+  a.eb = eb;
+  a.E_loc = E_loc;
+  a.offsets = offsets;
+  a.tp128 = tp128;
+  a.P_pad = P_pad;
+  // units: at most (P_max / 128 + E_loc) blocks of 128 rows per 64 columns
+  const int64_t worst = (P_max / kQrRows + E_loc) * cols;
   const int64_t cap = (int64_t)kNumCUs * 8;
   const int blocks = (int)(worst < cap ? worst : cap);
   if (blocks == 0) return hipSuccess;
-  if (gather_rows)
-    hipLaunchKernelGGL(quantize_rows_t_kernel<true>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)src, ld,
-                       gather_rows, k_top, C, offsets, eb, E_loc, tp128, P_pad, dst, dsc);
-  else
-    hipLaunchKernelGGL(quantize_rows_t_kernel<false>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)src, ld,
-                       nullptr, 1, C, offsets, eb, E_loc, tp128, P_pad, dst, dsc);
+  hipLaunchKernelGGL(quantize_rows_t_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
