@@ -441,7 +441,8 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
     decode step), microseconds per call, eagerly and replayed from a HIP
     graph: the small-call path (router and sort in one launch up to T 32,
     weight-streaming UP and DOWN up to 4096 pairs) against the tiled GEMMs
-    with separate router and sort launches.  For the small-call path also
+    with separate router and sort launches; the same calls with the weights
+    in MXFP8 (eager).  For the small-call path also
     the per-stage times (library stage events) and the HBM roofline of the
     two GEMMs: the weights of the experts the call touches, read once, plus
     their activation rows, over 8 TB/s."""
@@ -454,6 +455,11 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
     dev = inp["x"].device
     n = max(K, 50)
     out = {}
+    mx_w = None
+    if w.d % 256 == 0 and w.F % 128 == 0:
+        from mixture_experts_layer_34_amd.layer import quantize_mxfp8
+        q = [quantize_mxfp8(inp[nm]) for nm in ("W1", "W3", "W2")]
+        mx_w = (q[0][0], q[1][0], q[2][0], torch.cat([sc.reshape(-1) for _, sc in q]))
     for T in Ts:
         wT = W.scaled(w.name, T=T)
         small = W.make_inputs(wT, device=dev, weights=False)
@@ -520,6 +526,27 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
             del graph, buf
             row[tag] = rec
         row["speedup"] = round(row["tiled"]["us"] / row["small_path"]["us"], 3)
+        if mx_w is not None:
+            # the same calls with MXFP8 weights (inference: nothing saved)
+            for tag, tiled in (("mxfp8_small_path", False), ("mxfp8_tiled", True)):
+                buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision="mxfp8",
+                                          separate_route_sort=tiled, gemm_path="tiled" if tiled else "auto"),
+                                 device=dev)
+
+                def fwd_mx(stream=sh):
+                    buf.forward(small["x"], small["logits"], mx_w[0], mx_w[1], mx_w[2], mx_w[3], stream=stream)
+
+                for _ in range(5):
+                    fwd_mx()
+                torch.cuda.synchronize()
+                a, b = ev.create(2)
+                ev.record(a, sh)
+                for _ in range(n):
+                    fwd_mx()
+                ev.record(b, sh)
+                row[tag] = {"us": round(ev.elapsed_ms(a, b) * 1e3 / n, 2)}
+                del buf
+            row["mxfp8_speedup"] = round(row["mxfp8_tiled"]["us"] / row["mxfp8_small_path"]["us"], 3)
         out[str(T)] = row
     return {"workload": f"{w.name} weights (d={w.d} E={w.E} k={w.k} F={w.F}), forward only, T tokens per call",
             "calls": n, "per_T": out}

@@ -102,7 +102,12 @@ typedef enum {
  * average); MOK_FLAG_STREAM_GEMMS selects them for every such call,
  * MOK_FLAG_TILED_GEMMS never (both: MOK_ERR_INVALID_ARG).  The results are
  * deterministic and within the BF16 tolerance of the oracle, but not bitwise
- * those of the tiled kernels (another summation order). */
+ * those of the tiled kernels (another summation order).  An MXFP8 forward
+ * that saves nothing for backward (d a multiple of 256) follows the same
+ * rule, with up to 8 * (expert_end - expert_begin) pairs by default, with
+ * MXFP8 weight-streaming kernels (E4M3 codes and their scales read once per
+ * 32-row tile; H quantised along F in UP's epilogue as in the tiled path);
+ * within the MXFP8 tolerance of the oracle. */
 #define MOK_FLAG_TILED_GEMMS 0x10u
 #define MOK_FLAG_STREAM_GEMMS 0x20u
 /* MXFP8 weight gradients (with MOK_PREC_MXFP8 and MOK_FLAG_SAVE_FOR_BACKWARD

@@ -225,6 +225,180 @@ hipError_t run_stream_k(int ks, const GroupedGemmArgs& g, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------------ MXFP8
+// The same weight streaming for MXFP8 weights (E4M3 codes with one E8M0
+// scale per 32 along K, pair-plane scales as mok_quantize_mxfp8 writes
+// them), on v_mfma_scale_f32_32x32x64_f8f6f4: a unit is (32-row tile, 32 * NWN
+// weight rows) and K steps of 64 bytes.  The instruction's operand layout
+// (as the tiled MXFP8 GEMMs feed it): lane l holds row l % 32 and, with
+// h = l / 32, bytes [16 h, 16 h + 16) and [32 + 16 h, 48 + 16 h) of the step,
+// and the scale of the step's 32-block h.  UP quantises H along F in its
+// epilogue (one 32-column block per column group: the unit's rows of H are
+// whole MX blocks) for DOWN, which writes bf16 Y.  Forward only (no saved A,
+// B, H).
+template <int KIND, int KS>
+__global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NB = Traits<KIND>::NB;
+  constexpr int NWN = 4 / KS;  // 32-column groups per workgroup
+  const int N = KIND == KIND_UP ? a.F : a.d, K = KIND == KIND_UP ? a.d : a.F;
+  const int ntn = N / (32 * NWN);
+  const int E_loc = a.E_loc;
+  const int32_t* tp = a.tile_prefix + kStreamTileTable * (E_loc + 1);
+  const int total = sload(tp + E_loc) * ntn;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = w % NWN, kr = w / NWN;
+  const int kw = K / KS;        // bytes of K per wave
+  const int nstep = kw / 64;    // MFMA K steps per wave
+  const int r32 = lane & 31, h = lane >> 5;
+  __shared__ f32x16_t red[KS > 1 ? (KS - 1) * NWN : 1][NB][64];
+  __shared__ float hs[NWN][32][33];  // UP: H of a column group, 32 rows x 32 columns (+1: no bank conflicts)
+  const int64_t a_planes = a.P_max * 2;                        // bytes per scale plane of A (P_max rows)
+  const int64_t b_planes = (int64_t)E_loc * N * 2;             // of the weights
+  const int Gd = gridDim.x;
+  const int vb = (Gd % 8 == 0) ? (blockIdx.x % 8) * (Gd / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int u = vb; u < total; u += Gd) {
+    const int q = u / ntn;
+    int lo = 0, hi = E_loc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sload(tp + mid) <= q) lo = mid; else hi = mid - 1;
+    }
+    const int t0 = sload(tp + lo), nte = sload(tp + lo + 1) - t0;
+    const int li = u - t0 * ntn;
+    const int mt = li % nte, nt = li / nte;
+    const int e = a.eb + lo;
+    const int row0 = sload(a.offsets + e) + mt * kStreamTileRows;
+    const int erow_end = sload(a.offsets + e + 1);
+    const int row_end = erow_end < row0 + 32 ? erow_end : row0 + 32;
+    const int n0 = (nt * NWN + cg) * 32;
+    // this lane's operand rows: A row (padding rows repeat the first; never
+    // stored) and weight row n0 + r32, at the wave's first K byte
+    const int arow = row0 + r32 < row_end ? row0 + r32 : row0;
+    const int64_t kb = (int64_t)kr * kw;
+    const uint8_t* ap = (const uint8_t*)a.A + (int64_t)arow * K + kb;
+    const int64_t wrow = (int64_t)lo * N + n0 + r32;
+    const uint8_t* bp0 = (const uint8_t*)a.B0 + wrow * K + kb;
+    const uint8_t* bp1 = NB == 2 ? (const uint8_t*)a.B1 + wrow * K + kb : bp0;
+    const uint8_t* asc = a.a_scale + (int64_t)arow * 2 + h;
+    const uint8_t* bsc0 = a.b_scale0 + wrow * 2 + h;
+    const uint8_t* bsc1 = NB == 2 ? a.b_scale1 + wrow * 2 + h : bsc0;
+    const int p0 = kr * nstep;  // the wave's first scale plane
+
+    f32x16_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+    i32x8_t av[2], bv[2][NB];
+    int as_[2], bs_[2][NB];
+    auto load = [&](int buf, int st) {
+      const int64_t o = (int64_t)st * 64 + 16 * h;
+      const i32x4_t lo_ = *reinterpret_cast<const i32x4_t*>(ap + o), hi_ = *reinterpret_cast<const i32x4_t*>(ap + o + 32);
+      av[buf] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);
+      as_[buf] = asc[(int64_t)(p0 + st) * a_planes];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint8_t* bp = b ? bp1 : bp0;
+        const i32x4_t l2 = *reinterpret_cast<const i32x4_t*>(bp + o), h2 = *reinterpret_cast<const i32x4_t*>(bp + o + 32);
+        bv[buf][b] = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
+        bs_[buf][b] = (b ? bsc1 : bsc0)[(int64_t)(p0 + st) * b_planes];
+      }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[buf], bv[buf][b], acc[b], 0, 0, 0, as_[buf], 0,
+                                                                  bs_[buf][b]);
+    };
+    load(0, 0);
+    for (int st = 0; st < nstep; st += 2) {
+      if (st + 1 < nstep) load(1, st + 1);
+      compute(0);
+      if (st + 1 < nstep) {
+        if (st + 2 < nstep) load(0, st + 2);
+        compute(1);
+      }
+    }
+
+    if constexpr (KS > 1) {
+      if (kr > 0)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[(kr - 1) * NWN + cg][b][lane] = acc[b];
+      __syncthreads();
+      if (kr == 0)
+#pragma unroll
+        for (int qk = 1; qk < KS; ++qk)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[b] += red[(qk - 1) * NWN + cg][b][lane];
+      __syncthreads();  // the partials are read before the next unit writes them
+    }
+    if (kr == 0) {
+      // lane holds column n0 + r32 of rows (i / 4) 8 + 4 h + i % 4
+      if constexpr (KIND == KIND_UP) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float va = acc[0][i], vb_ = acc[1][i];
+          hs[cg][(i >> 2) * 8 + 4 * h + (i & 3)][r32] = va * sigmoidf_(va) * vb_;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < 32 && row0 + lane < row_end) {
+          // lane r quantises row r of the block: 32 values, one MX block
+          float v[32];
+          float amax = 0.f;
+#pragma unroll
+          for (int c = 0; c < 32; ++c) {
+            v[c] = hs[cg][lane][c];
+            amax = fmaxf(amax, fabsf(v[c]));
+          }
+          const int se = mx_scale_exp(amax);
+          const int row = row0 + lane;
+          uint8_t* dst = (uint8_t*)a.out0 + (int64_t)row * N + n0;
+#pragma unroll
+          for (int q4 = 0; q4 < 2; ++q4) {
+            u32x4_t wq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int c = 16 * q4 + 4 * j;
+              wq[j] = e4m3x4(ldexpf(v[c], -se), ldexpf(v[c + 1], -se), ldexpf(v[c + 2], -se), ldexpf(v[c + 3], -se));
+            }
+            *reinterpret_cast<u32x4_t*>(dst + 16 * q4) = wq;
+          }
+          const int blk = n0 / 32;  // H scales: pair planes [F / 64, P_max, 2]
+          a.out_scale[(int64_t)(blk >> 1) * a.P_max * 2 + (int64_t)row * 2 + (blk & 1)] = (uint8_t)(se + 127);
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = row0 + (i >> 2) * 8 + 4 * h + (i & 3);
+          if (row < row_end) ((bf16_t*)a.out0)[(int64_t)row * N + n0 + r32] = f2bf(acc[0][i]);
+        }
+      }
+    }
+  }
+#endif
+}
+
+template <int KIND, int KS>
+hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
+  constexpr int NWN = 4 / KS;
+  const int N = KIND == KIND_UP ? g.F : g.d;
+  const int64_t ntn = N / (32 * NWN);
+  const int64_t worst = ((g.P_max + kStreamTileRows - 1) / kStreamTileRows + g.E_loc) * ntn;
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_mx_kernel<KIND, KS>, 256, 0) != hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  const int64_t cap = (int64_t)kNumCUs * per_cu;
+  const int blocks = (int)(worst < cap ? worst : cap);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((stream_mx_kernel<KIND, KS>), dim3(blocks), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int stream_ksplit(int K) {
@@ -232,6 +406,16 @@ int stream_ksplit(int K) {
   if (K % (kChunkK * 2) == 0) return 2;
   if (K % kChunkK == 0) return 1;
   return 0;
+}
+
+// MXFP8: K split over 4 waves for UP (d / 4 bytes each), 2 for DOWN; K
+// multiple of 64 bytes per wave.
+int stream_mx_ok(int d, int F) { return d % 256 == 0 && F % 128 == 0 && F % 64 == 0; }
+
+hipError_t gemm_stream_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
+  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4>(g, s);
+  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2>(g, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemm_stream_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s) {

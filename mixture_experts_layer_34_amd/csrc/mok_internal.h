@@ -175,6 +175,11 @@ hipError_t gemm_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
 // multiple of 128 (then only the tiled kernels apply).
 int stream_ksplit(int K);
 hipError_t gemm_stream_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
+// The MXFP8 forward's UP (E4M3 x rows from the dispatch, H quantised along F)
+// and DOWN (bf16 Y) the same way, on the 32x32x64 scaled MFMA: 32-row tiles,
+// 32-column units; forward only.  stream_mx_ok: d % 256 == 0, F % 128 == 0.
+int stream_mx_ok(int d, int F);
+hipError_t gemm_stream_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
 
 // One step of the ring-buffer minibatch pipeline (bf16): in a single launch,
 // mover tiles copy the rows of minibatch m+1 into their ring slot, compute

@@ -135,3 +135,69 @@ def test_auto_choice(T, expect):
     inp = W.make_inputs(w, device="cuda")
     auto, chosen = _run(w, inp, False, path="auto"), _run(w, inp, False, path=expect)
     assert torch.equal(auto.out, chosen.out)
+
+
+# ------------------------------------------------------------------ MXFP8 weight streaming (inference)
+
+TOL_MX = 3e-2
+
+MX_CASES = [
+    ("mx-one-token", dict(T=1, d=512, E=16, k=4, F=256)),
+    ("mx-tiles-ragged", dict(T=100, d=256, E=8, k=2, F=384)),           # up to ~50 rows: two 32-row tiles
+    ("mx-local", dict(T=64, d=512, E=32, k=4, F=256, expert_begin=8, expert_end=20)),
+    ("mx-k-eq-E", dict(T=40, d=256, E=4, k=4, F=128)),                  # every expert 40 rows
+]
+
+
+def _run_mx(w, inp, path):
+    from tests.gpu_case import run_layer
+    T = inp["x"].shape[0]
+    shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision="mxfp8", expert_begin=w.expert_begin,
+                     expert_end=w.e_end, save_for_backward=False, gemm_path=path)
+    buf = run_layer(w, inp, backward=False, buf=MoeBuffers(shape))
+    assert buf.device_status() == (mok.MOK_OK, 0)
+    return buf
+
+
+@pytest.mark.parametrize("name,over", MX_CASES, ids=[c[0] for c in MX_CASES])
+def test_stream_mxfp8_forward_matches_oracle(name, over):
+    """MXFP8 forward without saving (inference): the streaming UP and DOWN
+    against the oracle's MXFP8 forward (out and Y rows), next to the tiled
+    MXFP8 kernels on the same inputs."""
+    w = W.scaled("bf16_fwd", precision="mxfp8", backward=False, **over)
+    note(f"stream mxfp8 {name} {over}")
+    inp = W.make_inputs(w, device="cuda")
+    h = host_inputs(inp)
+    W1, W3, W2 = (to_np(inp[n]).astype(np.float64) for n in ("W1", "W3", "W2"))
+    fw = O.forward(h["x"], h["logits"], W1, W3, W2, w.k, w.expert_begin, w.e_end, mxfp8=True)
+    for path in ("stream", "tiled"):
+        buf = _run_mx(w, inp, path)
+        assert np.array_equal(to_np(buf.topk_idx), fw["idx"])
+        P = int(to_np(buf.offsets)[w.e_end])
+        Y = to_np(buf.saved_view("Y", torch.bfloat16, (w.T * w.k, w.d))[:P])
+        errs = {"out": rel_inf(to_np(buf.out), fw["out"]), "Y": rel_inf(Y, fw["Y"])}
+        note(f"  {path}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        bad = {k: v for k, v in errs.items() if v > TOL_MX}
+        assert not bad, (path, bad)
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_stream_mxfp8_train_shape_sampled(T):
+    """d 4096, E 128, k 8, F 1536 in MXFP8, forward only, the default choice
+    (streaming up to four rows per expert): sampled tokens against the
+    oracle's per-token MXFP8 forward; reruns bitwise."""
+    from tests.gpu_case import LazyExperts
+    w = W.scaled("bf16_train", precision="mxfp8", backward=False, T=T)
+    note(f"stream mxfp8 train shape T={T}")
+    inp = W.make_inputs(w, device="cuda")
+    buf = _run_mx(w, inp, "auto")
+    out = to_np(buf.out).copy()
+    again = _run_mx(w, inp, "auto")
+    assert np.array_equal(out, to_np(again.out)), "rerun differs"
+    h = host_inputs(inp)
+    W1, W3, W2 = LazyExperts(inp["W1"]), LazyExperts(inp["W3"]), LazyExperts(inp["W2"])
+    toks = sorted(set(np.random.default_rng(T).choice(T, size=min(T, 3), replace=False).tolist()) | {T - 1})
+    ref = np.stack([O.forward_token(t, h["x"][t], h["logits"][t], W1, W3, W2, w.k, mxfp8=True)[2] for t in toks])
+    err = rel_inf(out[toks], ref)
+    note(f"  out sampled {err:.2e}")
+    assert err <= TOL_MX
