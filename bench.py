@@ -63,8 +63,8 @@ def stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=False):
     HBM bytes for every stage (each operand read once, each output written
     once; a GEMM's weights are those of the E_loc local experts).  With
     mxfp8_wgrad the weight gradients read MXFP8 operands quantised along the
-    rows, which the regather stage writes from the bf16 dY, H, [dA | dB] and
-    the x rows."""
+    rows, which the regather stage writes from dout (dY rebuilt with the
+    gates), the bf16 H and [dA | dB], and the x rows."""
     d, F, E, k, T = w.d, w.F, w.E, w.k, U
     El = w.e_end - w.expert_begin
     s = 4 if w.precision == "f32" else 2
@@ -99,7 +99,8 @@ def stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=False):
     if mx and mxfp8_wgrad:
         gemm_bytes["gemm_dw2"] = P * d * q + P * F * q + El * d * F * 4
         gemm_bytes["gemm_dw13"] = 2 * P * F * q + P * d * q + 2 * El * F * d * 4
-        nbytes["regather"] = (P * d + P * F + 2 * P * F) * s + U * d * s + (2 * d + 3 * F) * P * q
+        # dY is formed again from dout (U token rows) and the gates
+        nbytes["regather"] = (P * F + 2 * P * F) * s + 2 * U * d * s + (2 * d + 3 * F) * P * q
     nbytes.update(gemm_bytes)
     return flops, nbytes
 

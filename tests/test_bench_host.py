@@ -68,8 +68,8 @@ def test_stage_work_mxfp8_bytes():
 def test_stage_work_mxfp8_weight_gradients():
     """With MXFP8 weight gradients: the dW GEMMs read one byte (plus a scale
     per 32) per operand element and count against the MXFP8 peak; the
-    regather stage reads the bf16 dY, H, [dA | dB] and x rows and writes the
-    row-quantised codes of all four."""
+    regather stage reads dout, the bf16 H, [dA | dB] and x rows and writes the
+    row-quantised codes of all four (dY rebuilt from dout and the gates)."""
     import workloads as W
     w = W.get("mxfp8_train")
     P, U = 1024, 200
@@ -77,6 +77,6 @@ def test_stage_work_mxfp8_weight_gradients():
     _, nb = bench.stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=True)
     assert nb["gemm_dw2"] == P * d * q + P * F * q + E * d * F * 4
     assert nb["gemm_dw13"] == 2 * P * F * q + P * d * q + 2 * E * F * d * 4
-    assert nb["regather"] == (P * d + 3 * P * F) * 2 + U * d * 2 + (2 * d + 3 * F) * P * q
+    assert nb["regather"] == 3 * P * F * 2 + 2 * U * d * 2 + (2 * d + 3 * F) * P * q
     for n in ("gemm_dw2", "gemm_dw13"):
         assert bench.gemm_peak("mxfp8", n, True) == bench.PEAK_TFLOPS["mxfp8"]
