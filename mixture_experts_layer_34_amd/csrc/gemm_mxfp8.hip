@@ -73,12 +73,9 @@ __device__ __forceinline__ u32x4_t pack_bf16x8(const float* v) {
 }
 // E4M3 codes of v[0..7] / 2^se
 __device__ __forceinline__ u32x2_t pack_e4m3x8(const float* v, int se) {
-  uint32_t cd[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) cd[t] = e4m3_rne(ldexpf(v[t], -se));
   u32x2_t w;
-  w[0] = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-  w[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+  w[0] = e4m3x4(ldexpf(v[0], -se), ldexpf(v[1], -se), ldexpf(v[2], -se), ldexpf(v[3], -se));
+  w[1] = e4m3x4(ldexpf(v[4], -se), ldexpf(v[5], -se), ldexpf(v[6], -se), ldexpf(v[7], -se));
   return w;
 }
 #ifndef MOK_MX_BK
@@ -508,13 +505,8 @@ struct MxJob {
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
             const int se = mx_scale_exp(amax);
-            uint32_t cd[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) cd[t] = e4m3_rne(ldexpf(hv[t], -se));
             if (row < c.row_end && col < N) {
-              u32x2_t codes;
-              codes[0] = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-              codes[1] = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+              const u32x2_t codes = pack_e4m3x8(hv, se);
               *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
               if (c8 == 0) {
                 const int b = col / 32;  // pair-plane layout of H's scales, P_max rows per plane

@@ -114,11 +114,8 @@ __device__ __forceinline__ void mx_quant8(const uint4 v, uint2& codes, uint8_t& 
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int se = mx_scale_exp(amax);
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e4m3_rne(ldexpf(f[i], -se));
-  codes.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  codes.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  codes.x = e4m3x4(ldexpf(f[0], -se), ldexpf(f[1], -se), ldexpf(f[2], -se), ldexpf(f[3], -se));
+  codes.y = e4m3x4(ldexpf(f[4], -se), ldexpf(f[5], -se), ldexpf(f[6], -se), ldexpf(f[7], -se));
   scale_byte = (uint8_t)(se + 127);
 }
 
@@ -161,13 +158,12 @@ __global__ __launch_bounds__(256) void dispatch_gather_mxfp8_kernel(const bf16_t
         }
         amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
         const int se = mx_scale_exp(amax);
-        uint32_t c[16];
+        uint32_t c[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = e4m3_rne(ldexpf(f[i], -se));
-        const uint4 codes = make_uint4(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24),
-                                       c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24),
-                                       c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24));
+        for (int i = 0; i < 4; ++i)
+          c[i] = e4m3x4(ldexpf(f[4 * i], -se), ldexpf(f[4 * i + 1], -se), ldexpf(f[4 * i + 2], -se),
+                        ldexpf(f[4 * i + 3], -se));
+        const uint4 codes = make_uint4(c[0], c[1], c[2], c[3]);
         // scale byte of the second block of this 64-wide step, from lane + 2
         const int se_hi = __shfl(se, (lane & ~3) + 2, 64);
         const uint16_t pair = (uint16_t)((se + 127) | ((se_hi + 127) << 8));
@@ -265,14 +261,16 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_t_kernel(const bf16_t* __r
   }
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // lanes 2b, 2b + 1 share block b
   const int se = mx_scale_exp(amax);
-  uint32_t cd[16];
+  uint32_t cd[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cd[i] = e4m3_rne(ldexpf(f[i], -se));
+  for (int i = 0; i < 4; ++i)
+    cd[i] = e4m3x4(ldexpf(f[4 * i], -se), ldexpf(f[4 * i + 1], -se), ldexpf(f[4 * i + 2], -se),
+                   ldexpf(f[4 * i + 3], -se));
   uint4 out;
-  out.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-  out.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
-  out.z = cd[8] | (cd[9] << 8) | (cd[10] << 16) | (cd[11] << 24);
-  out.w = cd[12] | (cd[13] << 8) | (cd[14] << 16) | (cd[15] << 24);
+  out.x = cd[0];
+  out.y = cd[1];
+  out.z = cd[2];
+  out.w = cd[3];
   const int64_t orow = (int64_t)m * C + c0 + c;
   *reinterpret_cast<uint4*>(q + (int64_t)m * q_mat + (int64_t)(c0 + c) * q_ld + q_koff + r0 + 16 * qd) = out;
   if ((qd & 1) == 0) sc[(int64_t)((q_koff + r0) / 64) * rows * 2 + orow * 2 + (qd >> 1)] = (uint8_t)(se + 127);
@@ -566,13 +564,12 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
             // the second block of this 64-wide K step is four lanes up; the
             // two scale bytes are adjacent in the pair plane (d % 64 == 0)
             const int se_hi = __shfl(se, (lane & ~7) + 4, 64);
-            uint32_t cd[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) cd[q] = e4m3_rne(ldexpf(z[q], -se));
+            const uint32_t c0 = e4m3x4(ldexpf(z[0], -se), ldexpf(z[1], -se), ldexpf(z[2], -se), ldexpf(z[3], -se));
+            const uint32_t c1 = e4m3x4(ldexpf(z[4], -se), ldexpf(z[5], -se), ldexpf(z[6], -se), ldexpf(z[7], -se));
             if (r[i] >= 0) {
               uint2 codes;
-              codes.x = cd[0] | (cd[1] << 8) | (cd[2] << 16) | (cd[3] << 24);
-              codes.y = cd[4] | (cd[5] << 8) | (cd[6] << 16) | (cd[7] << 24);
+              codes.x = c0;
+              codes.y = c1;
               reinterpret_cast<uint2*>(dyq + (int64_t)r[i] * d)[v] = codes;
               if ((v & 7) == 0)
                 *reinterpret_cast<uint16_t*>(dys + (int64_t)(v >> 3) * dys_rows * 2 + (int64_t)r[i] * 2) =
