@@ -53,6 +53,12 @@ Readings taken where the pages are silent:
   * MXFP8 follows the OCP Microscaling v1.0 conversion (blocks of 32 along the
     contraction axis, E8M0 shared scale 2^(floor(log2 amax) - 8), elements
     rounded to nearest-even E4M3 with saturation at +-448).
+  * MXFP4, the analogue on this hardware of the NVFP4 kernels the pages say
+    were tried before the megakernel ([fluid], «Quand la communication devient
+    le vrai problème»; the pages give no recipe): the MXFP8 forward with E2M1
+    elements instead of E4M3 (OCP Microscaling v1.0 MXFP4: blocks of 32, E8M0
+    scale 2^(floor(log2 amax) - 2), elements rounded to nearest-even E2M1 with
+    saturation at +-6) for x, the three weights and h; forward only.
 """
 from __future__ import annotations
 
@@ -63,6 +69,7 @@ __all__ = [
     "layout", "permute", "unpermute_sum", "silu", "expert_ffn",
     "forward", "backward", "combine", "loss",
     "bf16_round", "e4m3_encode", "e4m3_decode", "mxfp8_quantize", "mxfp8_dequantize", "mxfp8_qdq", "mxfp8_qdq_rows",
+    "e2m1_encode", "e2m1_decode", "mxfp4_quantize", "mxfp4_dequantize", "mxfp4_qdq",
     "forward_token", "backward_token", "expert_weight_grads",
 ]
 
@@ -339,19 +346,99 @@ def mxfp8_qdq_rows(M, block: int = 32):
     return mxfp8_qdq(Mp.T, block).T[:R]
 
 
+# ------------------------------------------------------------------ MXFP4
+
+E2M1_MAX = 6.0
+_E2M1_EMAX = 2          # exponent of the largest power of two <= 6
+
+
+def e2m1_encode(v):
+    """Round float64 values to OCP E2M1 codes (S.EE.M, exponent bias 1, no
+    infinities or NaN; OCP Microscaling v1.0, FP4 element format).
+
+    Round to nearest, ties to even; magnitudes above 6 saturate to 6; the sign
+    of zero is kept.  Normal values (from 1 up) have one fraction bit, so the
+    spacing in [2^e, 2^(e+1)) is 2^(e-1); below 1 the spacing is 0.5 (the one
+    subnormal, 0.5).  The eight magnitudes: 0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    v = _f64(v)
+    if not np.isfinite(v).all():
+        raise ValueError("e2m1_encode expects finite values")
+    sign = np.signbit(v)
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    _, ex = np.frexp(a)                       # a = m * 2^ex, m in [0.5, 1)
+    e = np.maximum(ex - 1, 0)                 # floor(log2 a), at least 0
+    q = np.ldexp(1.0, e - 1)                  # spacing of representable values
+    val = np.rint(a / q) * q                  # exact division by a power of 2; RNE
+    _, ex2 = np.frexp(val)
+    e2 = ex2 - 1
+    normal = val >= 1.0
+    code_norm = ((e2 + 1) << 1) | (np.rint(np.ldexp(val, -e2) * 2).astype(np.int64) - 2)
+    code_sub = np.rint(val / 0.5).astype(np.int64)
+    code = np.where(normal, code_norm, code_sub)
+    return (code | (sign.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def e2m1_decode(codes):
+    """Value of E2M1 codes (S.EE.M, bias 1; exponent field 0 is the subnormal
+    M * 0.5)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    val = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.ldexp(1.0, e - 1))
+    return s * val
+
+
+def mxfp4_quantize(v, block: int = 32):
+    """MXFP4 block quantisation along the last axis (OCP Microscaling v1.0).
+
+    Per block of 32: X = 2^(floor(log2 amax) - 2), stored as E8M0 byte
+    (unbiased exponent + 127, exponent clamped to [-127, 127]); an all-zero
+    block stores byte 0.  Elements become E2M1(v / X), one code (0..15) per
+    element.  Returns (codes uint8 of v's shape, scales uint8 [..., K/32])."""
+    v = _f64(v)
+    K = v.shape[-1]
+    if K % block:
+        raise ValueError("last axis must be a multiple of the block size")
+    vb = v.reshape(v.shape[:-1] + (K // block, block))
+    amax = np.abs(vb).max(axis=-1)
+    _, ex = np.frexp(amax)
+    sexp = np.clip(ex - 1 - _E2M1_EMAX, -127, 127)
+    sexp = np.where(amax == 0, -127, sexp)
+    codes = e2m1_encode(vb / np.ldexp(1.0, sexp)[..., None])
+    return codes.reshape(v.shape), (sexp + 127).astype(np.uint8)
+
+
+def mxfp4_dequantize(codes, scales, block: int = 32):
+    c = e2m1_decode(codes)
+    K = c.shape[-1]
+    cb = c.reshape(c.shape[:-1] + (K // block, block))
+    x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)[..., None]
+    return (cb * x).reshape(c.shape)
+
+
+def mxfp4_qdq(v, block: int = 32):
+    return mxfp4_dequantize(*mxfp4_quantize(v, block), block)
+
+
 # ------------------------------------------------------------------ forward
 
 def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: int | None = None,
-            mxfp8: bool = False, gating: str = "softmax", renorm: bool = False):
+            mxfp8: bool = False, gating: str = "softmax", renorm: bool = False, mxfp4: bool = False):
     """Whole-layer forward in float64.
 
     x [T,d]; logits [T,E] float32; W1, W3 [E_loc,F,d]; W2 [E_loc,d,F] with
     E_loc = expert_end - expert_begin (weights of expert e at e - expert_begin).
     In MXFP8 mode x rows and W1/W3 rows are quantised along d, W2 rows along F,
     and h along F before the second product (gates, softmax and the combine stay
-    float64).  Returns a dict with idx, gate, lse, p, counts, offsets,
-    row_of_pair, pair_of_row, A, B, H, Y (per row, unscaled) and out [T,d].
+    float64).  MXFP4 mode quantises the same operands along the same axes to
+    MXFP4 (mxfp4_qdq) instead.  Returns a dict with idx, gate, lse, p, counts,
+    offsets, row_of_pair, pair_of_row, A, B, H, Y (per row, unscaled) and out
+    [T,d].
     """
+    if mxfp8 and mxfp4:
+        raise ValueError("one of mxfp8, mxfp4")
+    qdq = mxfp8_qdq if mxfp8 else (mxfp4_qdq if mxfp4 else None)
     x = _f64(x)
     T, d = x.shape
     E = np.asarray(logits).shape[1]
@@ -369,11 +456,11 @@ def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: in
             continue
         w1, w3, w2 = W1[e - expert_begin], W3[e - expert_begin], W2[e - expert_begin]
         Xe = Xp[r0:r1]
-        if mxfp8:
-            Xe, w1, w3, w2 = mxfp8_qdq(Xe), mxfp8_qdq(w1), mxfp8_qdq(w3), mxfp8_qdq(w2)
+        if qdq is not None:
+            Xe, w1, w3, w2 = qdq(Xe), qdq(w1), qdq(w3), qdq(w2)
             a = Xe @ _f64(w1).T
             b = Xe @ _f64(w3).T
-            h = mxfp8_qdq(silu(a) * b)
+            h = qdq(silu(a) * b)
             y = h @ _f64(w2).T
         else:
             a, b, h, y = expert_ffn(Xe, w1, w3, w2)
@@ -381,15 +468,18 @@ def forward(x, logits, W1, W3, W2, k: int, expert_begin: int = 0, expert_end: in
     out = combine(Y, gate, row_of_pair, T, k)
     return dict(idx=idx, gate=gate, lse=lse, p=p, counts=counts, offsets=offsets,
                 row_of_pair=row_of_pair, pair_of_row=pair_of_row, A=A, B=B, H=H, Y=Y, out=out,
-                gating=gating, renorm=renorm, mxfp8=mxfp8)
+                gating=gating, renorm=renorm, mxfp8=mxfp8, mxfp4=mxfp4)
 
 
 def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int = 0,
                   expert_end: int | None = None, mxfp8: bool = False, gating: str = "softmax",
-                  renorm: bool = False):
+                  renorm: bool = False, mxfp4: bool = False):
     """Output of one token alone (for sampled checks at full size): its top-k
     experts from its own logits, the FFN of each local one, the gate-weighted
     sum in slot order.  Returns (idx [k], gate [k], out [d], y per slot)."""
+    if mxfp8 and mxfp4:
+        raise ValueError("one of mxfp8, mxfp4")
+    qdq = mxfp8_qdq if mxfp8 else (mxfp4_qdq if mxfp4 else None)
     idx, gate, _, _ = route(np.asarray(logits_t, dtype=np.float32)[None, :], k, gating, renorm)
     E = np.asarray(logits_t).shape[0]
     if expert_end is None:
@@ -403,10 +493,10 @@ def forward_token(t: int, x_t, logits_t, W1, W3, W2, k: int, expert_begin: int =
             ys.append(None)
             continue
         w1, w3, w2 = W1[e - expert_begin], W3[e - expert_begin], W2[e - expert_begin]
-        if mxfp8:
-            xq = mxfp8_qdq(xt)
-            h = mxfp8_qdq(silu(xq @ mxfp8_qdq(w1).T) * (xq @ mxfp8_qdq(w3).T))
-            y = (h @ mxfp8_qdq(w2).T)[0]
+        if qdq is not None:
+            xq = qdq(xt)
+            h = qdq(silu(xq @ qdq(w1).T) * (xq @ qdq(w3).T))
+            y = (h @ qdq(w2).T)[0]
         else:
             y = expert_ffn(xt, w1, w3, w2)[3][0]
         ys.append(y)
@@ -470,6 +560,8 @@ def backward(dout, x, logits, W1, W3, W2, k: int, fwd: dict | None = None,
     gating, renorm = fwd.get("gating", gating), fwd.get("renorm", renorm)
     if mxfp8 != fwd.get("mxfp8", False):
         raise ValueError("backward(mxfp8=...) needs the forward of the same precision")
+    if fwd.get("mxfp4", False):
+        raise ValueError("the MXFP4 mode is forward only")
     if mxfp8_wgrad and not mxfp8:
         raise ValueError("mxfp8_wgrad needs mxfp8")
     gate, p, Y = fwd["gate"], fwd["p"], fwd["Y"]
