@@ -30,6 +30,20 @@ int32_t mok_diag_mfma_scale_block(const uint8_t* a, const uint8_t* b, const uint
                                   const float* c_in, float* c_out, void* stream);
 
 /*
+ * The same instruction on raw operand registers, for establishing its
+ * register-to-K mapping per operand format: lane l (0..63) supplies A dwords
+ * a[8 l .. 8 l + 7], B dwords b[8 l .. 8 l + 7], scale bytes sa[l], sb[l] and
+ * accumulators c_in[16 l .. 16 l + 15]; c_out[16 l + i] is its result
+ * register i.  fmt_a / fmt_b: 0 = E4M3, 4 = E2M1 (FP4 codes; the instruction
+ * then reads the first four dwords of each lane); supported pairs (0, 0),
+ * (4, 4) and (4, 0).  All pointers device memory.  One wave on `stream`;
+ * returns 0, 1 for a null pointer or an unsupported pair, 4 for a failed
+ * launch.
+ */
+int32_t mok_diag_mfma_scale_raw(const uint32_t* a, const uint32_t* b, const uint8_t* sa, const uint8_t* sb,
+                                const float* c_in, float* c_out, int32_t fmt_a, int32_t fmt_b, void* stream);
+
+/*
  * The E4M3 encoding the layer's MXFP8 quantisers use (the gfx950 conversion
  * instruction on the value clamped to +-448, one value and four packed
  * little-endian) against a software encoder written from the OCP E4M3

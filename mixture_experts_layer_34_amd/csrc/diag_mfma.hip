@@ -1,4 +1,4 @@
-// Diagnostics of the gfx950 instructions the MXFP8 path relies on.  One
+// Diagnostics of the gfx950 instructions the MXFP8 and MXFP4 paths rely on.  One
 // scaled-MFMA block (v_mfma_scale_f32_32x32x64_f8f6f4,
 // E4M3 operands, one E8M0 scale per 32 K values of each row) on caller-given
 // codes and scales, so that a test can compare the matrix core's fp32 result
@@ -39,6 +39,35 @@ __global__ __launch_bounds__(64) void mfma_scale_block_kernel(const uint8_t* __r
 #endif
 }
 
+// The same instruction on caller-given operand registers: lane l's eight A
+// and eight B dwords, its two scale bytes and its sixteen accumulators, for
+// operand formats FA (A) and FB (B) (0 E4M3, 4 E2M1: then only the first four
+// dwords are read), so that a test can establish how the instruction maps
+// register bits to K for a format.
+template <int FA, int FB>
+__global__ __launch_bounds__(64) void mfma_scale_raw_kernel(const uint32_t* __restrict__ a,
+                                                            const uint32_t* __restrict__ b,
+                                                            const uint8_t* __restrict__ sa,
+                                                            const uint8_t* __restrict__ sb,
+                                                            const float* __restrict__ c_in,
+                                                            float* __restrict__ c_out) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int l = threadIdx.x;
+  i32x8_t av, bv;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    av[i] = (int32_t)a[l * 8 + i];
+    bv[i] = (int32_t)b[l * 8 + i];
+  }
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = c_in[l * 16 + i];
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FA, FB, 0, (int)sa[l], 0, (int)sb[l]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c_out[l * 16 + i] = acc[i];
+#endif
+}
+
 // Every float32 of magnitude below 2^9 (bit patterns [0, n), both signs)
 // through the layer's E4M3 encoders: the conversion instruction (e4m3_rne,
 // and e4m3x4 with the value in each of its four byte places) against the
@@ -74,6 +103,22 @@ __global__ __launch_bounds__(256) void e4m3_check_kernel(uint32_t n, uint32_t* _
 extern "C" int32_t mok_diag_e4m3_check(uint32_t n, uint32_t* count, uint32_t* first, int32_t blocks, void* stream) {
   if (!count || !first || blocks < 1 || n > 0x44000000u) return 1;
   hipLaunchKernelGGL(e4m3_check_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, n, count, first);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int32_t mok_diag_mfma_scale_raw(const uint32_t* a, const uint32_t* b, const uint8_t* sa,
+                                           const uint8_t* sb, const float* c_in, float* c_out, int32_t fmt_a,
+                                           int32_t fmt_b, void* stream) {
+  if (!a || !b || !sa || !sb || !c_in || !c_out) return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  if (fmt_a == 0 && fmt_b == 0)
+    hipLaunchKernelGGL((mfma_scale_raw_kernel<0, 0>), dim3(1), dim3(64), 0, s, a, b, sa, sb, c_in, c_out);
+  else if (fmt_a == 4 && fmt_b == 4)
+    hipLaunchKernelGGL((mfma_scale_raw_kernel<4, 4>), dim3(1), dim3(64), 0, s, a, b, sa, sb, c_in, c_out);
+  else if (fmt_a == 4 && fmt_b == 0)
+    hipLaunchKernelGGL((mfma_scale_raw_kernel<4, 0>), dim3(1), dim3(64), 0, s, a, b, sa, sb, c_in, c_out);
+  else
+    return 1;
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

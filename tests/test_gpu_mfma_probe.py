@@ -158,3 +158,83 @@ def test_scaled_mfma_block_against_exact_sum(case):
     exact, mag = _exact(a, b, sa, sb, c_in)
     _report(case, hw, exact, mag)
     assert (np.abs(hw - exact) <= 2.0 ** -10 * mag.max()).all()
+
+
+# ------------------------------------------------------------------ E2M1 operands
+
+def _raw(areg, breg, sa_l, sb_l, fa, fb):
+    """The instruction on raw lane registers (uint8 [64, 32] each), lane scale
+    bytes [64]; returns C [32, 32] (C[m][n], m = A row, n = B row)."""
+    L = _lib()
+    L.mok_diag_mfma_scale_raw.restype = ctypes.c_int32
+    L.mok_diag_mfma_scale_raw.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    dev = torch.device("cuda")
+    t = [torch.from_numpy(np.ascontiguousarray(v)).to(dev) for v in (areg, breg, sa_l, sb_l)]
+    c_in = torch.zeros(64 * 16, dtype=torch.float32, device=dev)
+    out = torch.zeros_like(c_in)
+    rc = L.mok_diag_mfma_scale_raw(*[v.data_ptr() for v in t], c_in.data_ptr(), out.data_ptr(), fa, fb,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(64, 16).astype(np.float64)
+    C = np.zeros((32, 32))
+    for l in range(64):
+        for i in range(16):
+            C[(i // 4) * 8 + (l // 32) * 4 + i % 4, l % 32] = o[l, i]
+    return C
+
+
+def _fp4_regs(M):
+    """E2M1 codes M [32, 64] into lane registers as the MXFP4 kernels feed
+    them: lane l holds row l % 32 and K [32 h, 32 h + 32) (h = l / 32) as 16
+    packed bytes, element 2i in the low nibble of byte i."""
+    regs = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        r, h = l % 32, l // 32
+        row = M[r, 32 * h:32 * h + 32].astype(np.uint8)
+        regs[l, :16] = row[0::2] | (row[1::2] << 4)
+    return regs
+
+
+def _fp8_regs(M):
+    regs = np.zeros((64, 32), np.uint8)
+    for l in range(64):
+        r, h = l % 32, l // 32
+        regs[l, :16] = M[r, 16 * h:16 * h + 16]
+        regs[l, 16:] = M[r, 32 + 16 * h:48 + 16 * h]
+    return regs
+
+
+def _lane_scales(S):
+    return np.array([S[l % 32, l // 32] for l in range(64)], np.uint8)
+
+
+@pytest.mark.parametrize("fb", [4, 0], ids=["e2m1xe2m1", "e2m1xe4m3"])
+def test_e2m1_operand_layout(fb):
+    """The register layout the MXFP4 kernels rely on: E2M1 operands as 16
+    packed bytes per lane, K [32 h, 32 h + 32) for lanes 32 h .. 32 h + 31,
+    low nibble first, the lane group h supplying the scale of K block h.
+    Against an E4M3 B operand in its own (established) layout the nibble
+    order is fixed too.  E2M1 x E2M1 with scales of 2^-1 .. 2^1: every
+    product and partial sum is exact in fp32, so the bar is equality; against
+    E4M3 a layout mistake moves results by O(1) of the largest, so the bar
+    there is 2^-16 of it."""
+    rng = np.random.default_rng(7)
+    A = rng.integers(0, 16, (32, 64))
+    sa = rng.integers(126, 129, (32, 2)).astype(np.uint8)
+    sb = rng.integers(126, 129, (32, 2)).astype(np.uint8)
+    if fb == 4:
+        B = rng.integers(0, 16, (32, 64))
+        breg, vb = _fp4_regs(B), O.e2m1_decode(B)
+    else:
+        B = _codes_with_exponent(rng, (32, 64), 4, 9)   # 2^-3 .. 2^2
+        breg, vb = _fp8_regs(B), O.e4m3_decode(B)
+    hw = _raw(_fp4_regs(A), breg, _lane_scales(sa), _lane_scales(sb), 4, fb)
+    va = O.e2m1_decode(A) * np.repeat(np.ldexp(1.0, sa.astype(np.int64) - 127), 32, axis=1)
+    vb = vb * np.repeat(np.ldexp(1.0, sb.astype(np.int64) - 127), 32, axis=1)
+    exact = va @ vb.T
+    note(f"  e2m1 x {'e2m1' if fb == 4 else 'e4m3'}: max |hw - exact| {np.abs(hw - exact).max():.3e}")
+    if fb == 4:
+        np.testing.assert_array_equal(hw, exact)
+    else:
+        assert np.abs(hw - exact).max() <= 2.0 ** -16 * np.abs(exact).max()
