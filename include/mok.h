@@ -31,8 +31,8 @@
  *     expert FFN width F (cfg->ffn).  Local experts are
  *     [expert_begin, expert_end); E_loc = expert_end - expert_begin and the
  *     weights of expert e sit at index e - expert_begin.
- *   - Activation element type: bf16 for MOK_PREC_BF16 and MOK_PREC_MXFP8
- *     (x, out, dout, dx), fp32 for MOK_PREC_F32.
+ *   - Activation element type: bf16 for MOK_PREC_BF16, MOK_PREC_MXFP8 and
+ *     MOK_PREC_MXFP4 (x, out, dout, dx), fp32 for MOK_PREC_F32.
  *   - Pair id p = t*k + j (slot j = 0 is the highest-ranked expert).
  *   - Errors: a non-MOK_OK status is returned and nothing is enqueued.
  *     No exception crosses the ABI.  Results are bit-identical from run to
@@ -62,7 +62,9 @@ typedef enum {
 typedef enum {
   MOK_PREC_F32 = 0,          /* fp32 activations and weights, fp32 arithmetic   */
   MOK_PREC_BF16 = 1,         /* bf16 operands, fp32 accumulation (MFMA)         */
-  MOK_PREC_MXFP8 = 2         /* E4M3 operands + E8M0 scale per 32 along K       */
+  MOK_PREC_MXFP8 = 2,        /* E4M3 operands + E8M0 scale per 32 along K       */
+  MOK_PREC_MXFP4 = 3         /* E2M1 operands + E8M0 scale per 32 along K;
+                                forward only (see mok_moe_forward)              */
 } mok_precision;
 
 /* Forward writes the intermediates backward needs (A, B pre-activations). */
@@ -233,9 +235,15 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *             offset) once the stream has passed the call, e.g. with a device
  *             to host copy at the caller's own synchronisation point.
  *   xp        the dispatch buffer, or the ring of minibatch slots, then (MXFP8
- *             backward) the dY codes [P_max, d];
- *   xp_scale  MXFP8: its E8M0 scales in pair planes [d/64, xp_rows, 2];
+ *             backward) the dY codes [P_max, d]; MXFP4: E2M1 codes
+ *             [xp_rows, d/2] bytes, element 2i in the low nibble of byte i;
+ *   xp_scale  MXFP8, MXFP4: its E8M0 scales in pair planes [d/64, xp_rows, 2];
  *   xp_rows   rows held by xp (P_max = T*k, or the ring's rows);
+ *   hq, hq_scale  MXFP8 and MXFP4: the H rows [P_max, F] as the first product
+ *             quantises them along F for the second (E4M3 bytes, or E2M1
+ *             codes two per byte, [P_max, F/2]), and their E8M0 scales in
+ *             pair planes [F/64, P_max, 2] (an MXFP8 backward then reuses
+ *             both for [dA | dB], 2F wide); nothing otherwise;
  *   dy, dab, dxp  backward row buffers dY [P_max, d], [dA | dB] [P_max, 2F],
  *             dX_perm [P_max, d] (bf16; absent from an MXFP8 forward-only
  *             configuration);
@@ -256,6 +264,8 @@ typedef struct mok_workspace_layout {
   size_t xp;
   size_t xp_scale;
   int64_t xp_rows;
+  size_t hq;
+  size_t hq_scale;
   size_t dy;
   size_t dab;
   size_t dxp;
@@ -274,12 +284,15 @@ mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_wo
  *   x              act   [T, d]
  *   router_logits  float [T, E]    finite values
  *   W1, W3         [E_loc, F, d]   gate / up projections (act type; E4M3
- *                                  bytes for MXFP8)
- *   W2             [E_loc, d, F]   down projection (act type; E4M3 for MXFP8)
- *   w_scales       MXFP8 only, else NULL: E8M0 bytes, concatenated: those
- *                  of W1 as a [E_loc*F, d] matrix, then of W3 (same), then
- *                  of W2 as a [E_loc*d, F] matrix, each in the pair-plane
- *                  layout that mok_quantize_mxfp8 writes
+ *                                  bytes for MXFP8; for MXFP4 E2M1 codes,
+ *                                  two per byte: [E_loc, F, d/2] bytes)
+ *   W2             [E_loc, d, F]   down projection (act type; E4M3 for MXFP8;
+ *                                  E2M1 [E_loc, d, F/2] bytes for MXFP4)
+ *   w_scales       MXFP8 and MXFP4 only, else NULL: E8M0 bytes,
+ *                  concatenated: those of W1 as a [E_loc*F, d] matrix, then of
+ *                  W3 (same), then of W2 as a [E_loc*d, F] matrix, each in the
+ *                  pair-plane layout that mok_quantize_mxfp8 (and
+ *                  mok_quantize_mxfp4) writes
  *   out            act   [T, d]    sum_j gate[t,j] * y(t,j), j ascending, in
  *                                  fp32, rounded once; rows of tokens with no
  *                                  local pair are 0
@@ -291,7 +304,15 @@ mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_wo
  *   saved          mok_saved_layout.total bytes
  *   workspace      workspace_bytes bytes
  * Alignment: every pointer 16-byte aligned.  Constraints: 1 <= k <= E <= 1024,
- * d and F multiples of 64 (bf16), 128 (MXFP8) or 16 (fp32), T*k < 2^31.
+ * d and F multiples of 64 (bf16), 128 (MXFP8), 256 (MXFP4) or 16 (fp32),
+ * T*k < 2^31.
+ * MXFP4 (an MXFP4 analogue of the NVFP4 kernels tried before the
+ * megakernel, [fluid «Quand la communication devient le vrai problème»]):
+ * the MXFP8 forward with E2M1 elements (OCP Microscaling v1.0 MXFP4: scale
+ * 2^(floor(log2 amax) - 2) per 32 values, elements rounded to nearest even,
+ * saturating at 6): x rows quantised by the dispatch, H along F by the first
+ * product's epilogue, the weights by mok_quantize_mxfp4.  Forward only:
+ * MOK_FLAG_SAVE_FOR_BACKWARD (and a ring) give MOK_ERR_UNSUPPORTED.
  */
 mok_status mok_moe_forward(const void* x, const float* router_logits,
                            const void* W1, const void* W3, const void* W2, int32_t k,
@@ -413,6 +434,25 @@ mok_status mok_quantize_mxfp8_backward_weights(const void* W1, const void* W3, c
  */
 mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K,
                               uint8_t* dst_e4m3, uint8_t* dst_e8m0, void* stream);
+
+/*
+ * MXFP4 quantisation of a bf16 matrix along its rows, for the weights of an
+ * MXFP4 forward (OCP Microscaling v1.0 MXFP4; the analogue of the NVFP4
+ * attempt of [fluid «Quand la communication devient le vrai problème»]): per
+ * block of 32 consecutive elements of a row, scale X = 2^(floor(log2 amax) -
+ * 2) stored as an E8M0 byte (exponent + 127, clamped to [0, 254]; an all-zero
+ * block stores 0), elements E2M1(v / X) (S.EE.M, bias 1: magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6) rounded to nearest even, saturating at 6, the sign of
+ * zero kept.
+ *   src_bf16  [rows, K]      K a multiple of 64, rows * K / 32 < 2^32
+ *   dst_e2m1  [rows, K / 2]  bytes; element 2i of a row in the low nibble of
+ *             byte i, element 2i + 1 in the high nibble
+ *   dst_e8m0  rows * K / 32 bytes in the pair planes of mok_quantize_mxfp8
+ * Errors: MOK_ERR_INVALID_ARG for a null or misaligned pointer, K not a
+ * multiple of 64, or a scale array of 2^32 bytes or more.
+ */
+mok_status mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t K,
+                              uint8_t* dst_e2m1, uint8_t* dst_e8m0, void* stream);
 
 /*
  * Router GEMM: the scores the router step consumes ([kucoin §01]: the router

@@ -81,9 +81,14 @@ __device__ __forceinline__ u32x2_t pack_e4m3x8(const float* v, int se) {
 #ifndef MOK_MX_BK
 #define MOK_MX_BK 128
 #endif
-constexpr int kMxBK = MOK_MX_BK;    // K (bytes) per stage: one (64) or two (128) MFMA K steps
-constexpr int kMxSub = kMxBK / 64;  // MFMA K steps per stage
+constexpr int kMxBK = MOK_MX_BK;    // bytes of K per stage (E4M3: one (64) or two (128) MFMA K steps)
 constexpr int kMxLPR = kMxBK / 16;  // lanes per row in a 1 KB copy
+// Operand formats, as the scaled MFMA encodes them.  E2M1 (MXFP4) operands
+// hold two codes per byte, so a stage of kMxBK bytes holds twice the K
+// values, and an MFMA K step (64 values) is 32 bytes: a lane (row l % 32,
+// h = l / 32) then holds the 16 bytes [16 h, 16 h + 16) of the step, K values
+// [32 h, 32 h + 32), the lower one in the low nibble (checked on the device).
+constexpr int kFmtE4M3 = 0, kFmtE2M1 = 4;
 
 // One MXFP8 output tile (UP: 256 rows x 64 columns of W1 and W3; DOWN:
 // 256 x 128): 128 accumulators per lane, which leaves the register file room
@@ -105,13 +110,17 @@ template <int KIND> constexpr bool mx_wgrad() { return KIND == KIND_DW2 || KIND 
 // accumulators); NW = 8 as 4 x 2 waves of 64 x TN (64 accumulators, two waves
 // per SIMD, so that one wave's MFMAs can run while the other waits to issue
 // its copies).
-template <int KIND, int NW>
+template <int KIND, int NW, int FMT = kFmtE4M3>
 struct MxJob {
+  static constexpr int EPB = FMT == kFmtE2M1 ? 2 : 1;  // K values per byte
+  static constexpr int SUB = kMxBK * EPB / 64;         // MFMA K steps per stage
+  static constexpr int KST = kMxBK * EPB;              // K values per stage
+  static_assert(FMT == kFmtE4M3 || (KIND == KIND_UP || KIND == KIND_DOWN), "E2M1: forward kinds only");
   static constexpr int NB = KIND == KIND_UP ? 2 : 1;
   static constexpr int BM = 256, BN = KIND == KIND_UP ? 64 : 128, BROWS = NB * BN;
   static constexpr int WM = NW / 2;                   // waves along M (2 along N)
   static constexpr int TM = BM / WM, TN = BN / 2, FM = TM / 32, FN = TN / 32;
-  static constexpr int NS = NW == 4 ? kMxNS : (kMxSub == 1 ? 4 : 2);  // LDS stage buffers
+  static constexpr int NS = NW == 4 ? kMxNS : (SUB == 1 ? 4 : 2);  // LDS stage buffers
   static constexpr int A_BYTES = BM * kMxBK, B_BYTES = BROWS * kMxBK;
   // Scale dwords (each 2-byte copy lands zero-extended in one dword); every
   // wave issues one A-scale and one B-scale copy of RA resp. RB rows, whose
@@ -119,10 +128,10 @@ struct MxJob {
   //   A row r at dword 64 (r / RA) + r % RA, B row r at dword 64 (r / RB) + r % RB.
   static constexpr int RA = BM / NW, RB = BROWS / NW;
   static constexpr int SCA = A_BYTES + B_BYTES;
-  static constexpr int SCB = SCA + kMxSub * NW * 256;   // (one scale set per MFMA K step)
-  static constexpr int STAGE = SCB + kMxSub * NW * 256;
+  static constexpr int SCB = SCA + SUB * NW * 256;   // (one scale set per MFMA K step)
+  static constexpr int STAGE = SCB + SUB * NW * 256;
   static constexpr int IA = A_BYTES / 1024 / NW, IB = B_BYTES / 1024 / NW;  // 1 KB copies per wave
-  static constexpr int D = IA + IB + 2 * kMxSub;      // + one 2-byte copy per wave for each scale set
+  static constexpr int D = IA + IB + 2 * SUB;         // + one 2-byte copy per wave for each scale set
   static constexpr int STAGING = NW * 4096;           // epilogue staging, 4 KB per wave
   static_assert(BM == 256 && BROWS == 128 && FM % 2 == 0, "tile");
   static_assert((NS - 1) * D <= 63, "vmcnt holds at most 63");
@@ -139,7 +148,7 @@ struct MxJob {
 
   const GroupedGemmArgs* args;
   int K, N;
-  uint32_t lda, ldb;  // bytes per operand row (K for the row kinds, k_pad for the weight gradients)
+  uint32_t lda, ldb;  // bytes per operand row (K / EPB for the row kinds, k_pad for the weight gradients)
   uint32_t psA, psB;  // bytes per scale plane of A (P_max rows) and of B (E_loc * N rows)
   TileCoord c;
   int wid, lane, wm, wn, nk;
@@ -161,8 +170,9 @@ struct MxJob {
       return;
     }
     K = mx_k<KIND>(a.d, a.F);
-    lda = ldb = (uint32_t)K;
-    nk = K / kMxBK;
+    const int Kb = K / EPB;  // bytes per operand row
+    lda = ldb = (uint32_t)Kb;
+    nk = K / KST;
     if (MOK_SKIP_PAD) {
       // rows past the expert's end are zero padding and are never stored:
       // their MFMAs are skipped (less work, less power)
@@ -171,11 +181,11 @@ struct MxJob {
     }
     const int rows = c.row_end - c.row0 < BM ? c.row_end - c.row0 : BM;
     const int nb_rows = N - c.n0 < BN ? N - c.n0 : BN;
-    const int64_t wst = (int64_t)N * K;  // bytes per expert of one weight matrix
-    rsA = make_rsrc((const uint8_t*)a.A + (int64_t)c.row0 * K, (uint32_t)(rows * K));
-    rsB0 = make_rsrc((const uint8_t*)a.B0 + c.e_loc * wst + (int64_t)c.n0 * K, (uint32_t)(nb_rows * K));
-    rsB1 = make_rsrc((const uint8_t*)(NB == 2 ? a.B1 : a.B0) + c.e_loc * wst + (int64_t)c.n0 * K,
-                     (uint32_t)(nb_rows * K));
+    const int64_t wst = (int64_t)N * Kb;  // bytes per expert of one weight matrix
+    rsA = make_rsrc((const uint8_t*)a.A + (int64_t)c.row0 * Kb, (uint32_t)(rows * Kb));
+    rsB0 = make_rsrc((const uint8_t*)a.B0 + c.e_loc * wst + (int64_t)c.n0 * Kb, (uint32_t)(nb_rows * Kb));
+    rsB1 = make_rsrc((const uint8_t*)(NB == 2 ? a.B1 : a.B0) + c.e_loc * wst + (int64_t)c.n0 * Kb,
+                     (uint32_t)(nb_rows * Kb));
     // scale resources from this tile's first row to the end of the last
     // plane; rows past the tile read other rows' bytes (finite E8M0 codes, or
     // zero past the end), which only reach output rows that are not stored
@@ -248,8 +258,8 @@ struct MxJob {
         dma_b128((NB == 2 && (wid * IB + q) * (64 / kMxLPR) >= BN) ? rsB1 : rsB0,
                  lds_addr(st + A_BYTES + (wid * IB + q) * 1024), offB[q], k0);
 #pragma unroll
-    for (int p = 0; p < kMxSub; ++p) {  // scale plane s * kMxSub + p
-      const uint32_t plane = (uint32_t)(s * kMxSub + p);
+    for (int p = 0; p < SUB; ++p) {  // scale plane s * SUB + p
+      const uint32_t plane = (uint32_t)(s * SUB + p);
       if (IA + IB + 2 * p >= Q0 && IA + IB + 2 * p < Q1)
         dma_u16(rsSA, lds_addr(st + SCA + (p * NW + wid) * 256), offSA, plane * psA);
       if (IA + IB + 2 * p + 1 >= Q0 && IA + IB + 2 * p + 1 < Q1)
@@ -259,15 +269,26 @@ struct MxJob {
   }
   __device__ __forceinline__ void issue(int s, uint8_t* arena) const { issue_part<0, D>(s, arena); }
 
-  // Fragments of MFMA K step `sub` of a stage: 16-byte chunks 4 sub + h and
-  // 4 sub + 2 + h of the row (h = lane / 32), and that step's scale set.
+  // One operand row's fragment for MFMA K step `sub` of a stage (h = lane /
+  // 32): E4M3, the 16-byte chunks 4 sub + h and 4 sub + 2 + h of the row;
+  // E2M1, the chunk 2 sub + h (the upper half of the operand is not read).
+  __device__ __forceinline__ static i32x8_t frag(const uint8_t* row, int r, int sub, int h) {
+    if constexpr (FMT == kFmtE2M1) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 2 * sub + h) * 16);
+      const i32x4_t z = {0, 0, 0, 0};
+      return __builtin_shufflevector(lo, z, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + h) * 16);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + 2 + h) * 16);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+  // Fragments of MFMA K step `sub` of a stage, and that step's scale set.
   __device__ __forceinline__ void read_a(int buf, int i, int sub, const uint8_t* arena, AFrag& f) const {
     const uint8_t* st = arena + buf * STAGE;
     const int h = lane >> 5;
     const int r = wm * TM + i * 32 + (lane & 31);
-    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + r * kMxBK + swz_k<kMxBK / 2>(r, 4 * sub + h) * 16);
-    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + r * kMxBK + swz_k<kMxBK / 2>(r, 4 * sub + 2 + h) * 16);
-    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = frag(st + r * kMxBK, r, sub, h);
     f.s = *reinterpret_cast<const uint32_t*>(st + SCA + sub * NW * 256 + (64 * (r / RA) + r % RA) * 4) >> (8 * h);
   }
   __device__ __forceinline__ void read_b(int buf, int sub, const uint8_t* arena, BFrags& f) const {
@@ -278,10 +299,7 @@ struct MxJob {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int r = b * BN + wn * TN + j * 32 + (lane & 31);
-        const uint8_t* row = st + A_BYTES + r * kMxBK;
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + h) * 16);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + swz_k<kMxBK / 2>(r, 4 * sub + 2 + h) * 16);
-        f.v[b][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.v[b][j] = frag(st + A_BYTES + r * kMxBK, r, sub, h);
         f.s[b][j] =
             *reinterpret_cast<const uint32_t*>(st + SCB + sub * NW * 256 + (64 * (r / RB) + r % RB) * 4) >> (8 * h);
       }
@@ -299,8 +317,8 @@ struct MxJob {
       for (int j = 0; j < FN; ++j) {
         const int L = b * FN + j;
         if (L >= L0 && L < L1)
-          acc[b][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa.v, fb.v[b][j], acc[b][i][j], 0, 0, 0,
-                                                                          (int)fa.s, 0, (int)fb.s[b][j]);
+          acc[b][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa.v, fb.v[b][j], acc[b][i][j], FMT, FMT,
+                                                                          0, (int)fa.s, 0, (int)fb.s[b][j]);
       }
   }
 
@@ -339,7 +357,7 @@ struct MxJob {
     AFrag a0, a1;
     read_b(0, 0, arena, b0);
     read_a(0, 0, 0, arena, a0);
-    if constexpr (kMxSub == 1) {
+    if constexpr (SUB == 1) {
       // two stages per iteration so that the roles of b0 and b1 are fixed
       int kt = 0;
       for (; kt + 2 <= nk; kt += 2) {
@@ -348,28 +366,34 @@ struct MxJob {
       }
       if (kt < nk) step(acc, arena, kt, 0, b0, b1, a0, a1);
     } else {
-      // two K steps per stage: the first reads the second's fragments from
-      // the same buffer, the second waits for the next stage
+      // SUB (even) K steps per stage: each but the last reads the next
+      // step's fragments from the same buffer, the last waits for the next
+      // stage
+      static_assert(SUB % 2 == 0, "b0 / b1 alternate within a stage");
       for (int kt = 0; kt < nk; ++kt) {
-        first_half(acc, arena, kt, b0, b1, a0, a1);
-        step(acc, arena, kt, 1, b1, b0, a0, a1);
+#pragma unroll
+        for (int sub = 0; sub + 1 < SUB; ++sub) {
+          if (sub % 2 == 0) first_half(acc, arena, kt, sub, b0, b1, a0, a1);
+          else first_half(acc, arena, kt, sub, b1, b0, a0, a1);
+        }
+        step(acc, arena, kt, SUB - 1, b1, b0, a0, a1);
       }
     }
   }
 
-  // K step 0 of stage kt (two-step stages): its B blocks are in bc and its
-  // first A block in a0; on return step 1's are in bn and a0.
-  __device__ __forceinline__ void first_half(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, BFrags& bc,
-                                             BFrags& bn, AFrag& a0, AFrag& a1) const {
+  // K step `sub` of stage kt, not its last: its B blocks are in bc and its
+  // first A block in a0; on return step sub + 1's are in bn and a0.
+  __device__ __forceinline__ void first_half(f32x16_t (&acc)[NB][FM][FN], uint8_t* arena, int kt, int sub,
+                                             BFrags& bc, BFrags& bn, AFrag& a0, AFrag& a1) const {
     const int buf = kt % NS;
 #pragma unroll
     for (int i = 0; i + 1 < FM; ++i) {
-      read_a(buf, i + 1, 0, arena, (i & 1) ? a0 : a1);
+      read_a(buf, i + 1, sub, arena, (i & 1) ? a0 : a1);
       __builtin_amdgcn_sched_barrier(0);
       mma_row<0, 1>(acc, i, (i & 1) ? a1 : a0, bc);
     }
-    read_b(buf, 1, arena, bn);
-    read_a(buf, 0, 1, arena, a0);
+    read_b(buf, sub + 1, arena, bn);
+    read_a(buf, 0, sub + 1, arena, a0);
     __builtin_amdgcn_sched_barrier(0);
     mma_row<0, 1>(acc, FM - 1, a1, bc);
   }
@@ -504,10 +528,14 @@ struct MxJob {
             }
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-            const int se = mx_scale_exp(amax);
+            const int se = FMT == kFmtE2M1 ? mx4_scale_exp(amax) : mx_scale_exp(amax);
             if (row < c.row_end && col < N) {
-              const u32x2_t codes = pack_e4m3x8(hv, se);
-              *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
+              if constexpr (FMT == kFmtE2M1) {
+                *reinterpret_cast<uint32_t*>(hq + ((int64_t)row * N + col) / 2) = e2m1x8(hv, se);
+              } else {
+                const u32x2_t codes = pack_e4m3x8(hv, se);
+                *reinterpret_cast<u32x2_t*>(hq + (int64_t)row * N + col) = codes;
+              }
               if (c8 == 0) {
                 const int b = col / 32;  // pair-plane layout of H's scales, P_max rows per plane
                 a.out_scale[(int64_t)(b >> 1) * a.P_max * 2 + (int64_t)row * 2 + (b & 1)] = (uint8_t)(se + 127);
@@ -619,10 +647,10 @@ struct MxJob {
 // Persistent loop over the row tiles of the local experts (same order and
 // XCD-aware mapping as the bf16 kernel); the next tile's first stages are
 // issued before the current tile's epilogue.
-template <int KIND, int NW>
+template <int KIND, int NW, int FMT>
 __global__ __launch_bounds__(NW * 64) void grouped_gemm_mxfp8_kernel(GroupedGemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using Job = MxJob<KIND, NW>;
+  using Job = MxJob<KIND, NW, FMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t arena[Job::NS * Job::STAGE + Job::STAGING];
   uint8_t* const staging = arena + Job::NS * Job::STAGE;
   const int N = mx_n<KIND>(args.d, args.F);
@@ -745,15 +773,16 @@ static hipError_t run_mx_wgrad(const GroupedGemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KIND, int NW>
+template <int KIND, int NW, int FMT = kFmtE4M3>
 static hipError_t run_mx(const GroupedGemmArgs& g, hipStream_t s) {
-  using Job = MxJob<KIND, NW>;
+  using Job = MxJob<KIND, NW, FMT>;
   const int N = mx_n<KIND>(g.d, g.F);
+  if (mx_k<KIND>(g.d, g.F) % Job::KST) return hipErrorInvalidValue;
   const int ntn = (N + Job::BN - 1) / Job::BN;
   const int64_t worst = ((g.P_max + Job::BM - 1) / Job::BM + g.E_loc) * (int64_t)ntn;
   const int blocks = (int)(worst < 256 ? worst : 256);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND, NW>), dim3(blocks), dim3(NW * 64), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_mxfp8_kernel<KIND, NW, FMT>), dim3(blocks), dim3(NW * 64), 0, s, g);
   return hipGetLastError();
 }
 
@@ -765,6 +794,14 @@ hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
     case KIND_DX:   return run_mx<KIND_DX, kMxWaves>(g, s);
     case KIND_DW2:  return run_mx_wgrad<KIND_DW2, kMxWaves>(g, s);
     case KIND_DW13: return run_mx_wgrad<KIND_DW13, kMxWaves>(g, s);
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t gemm_mxfp4(int kind, const GroupedGemmArgs& g, hipStream_t s) {
+  switch (kind) {
+    case KIND_UP:   return run_mx<KIND_UP, kMxWaves, kFmtE2M1>(g, s);
+    case KIND_DOWN: return run_mx<KIND_DOWN, kMxWaves, kFmtE2M1>(g, s);
   }
   return hipErrorNotSupported;
 }

@@ -225,31 +225,40 @@ hipError_t run_stream_k(int ks, const GroupedGemmArgs& g, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// ------------------------------------------------------------------ MXFP8
-// The same weight streaming for MXFP8 weights (E4M3 codes with one E8M0
-// scale per 32 along K, pair-plane scales as mok_quantize_mxfp8 writes
-// them), on v_mfma_scale_f32_32x32x64_f8f6f4: a unit is (32-row tile, 32 * NWN
-// weight rows) and K steps of 64 bytes.  The instruction's operand layout
-// (as the tiled MXFP8 GEMMs feed it): lane l holds row l % 32 and, with
-// h = l / 32, bytes [16 h, 16 h + 16) and [32 + 16 h, 48 + 16 h) of the step,
-// and the scale of the step's 32-block h.  UP quantises H along F in its
-// epilogue (one 32-column block per column group: the unit's rows of H are
-// whole MX blocks) for DOWN, which writes bf16 Y.  Forward only (no saved A,
-// B, H).
-template <int KIND, int KS>
+// ------------------------------------------------------------------ MXFP8 / MXFP4
+// The same weight streaming for MX weights (E4M3 codes, or E2M1 codes two
+// per byte, with one E8M0 scale per 32 along K, pair-plane scales as
+// mok_quantize_mxfp8 / mok_quantize_mxfp4 write them), on
+// v_mfma_scale_f32_32x32x64_f8f6f4: a unit is (32-row tile, 32 * NWN weight
+// rows) and K steps of 64 values.  The instruction's operand layout (as the
+// tiled MX GEMMs feed it): lane l holds row l % 32 and, with h = l / 32,
+// E4M3: bytes [16 h, 16 h + 16) and [32 + 16 h, 48 + 16 h) of the step;
+// E2M1: bytes [16 h, 16 h + 16) of the step's 32; and the scale of the
+// step's 32-block h.  Loads go in chunks of CS steps, 128 bytes of each
+// operand row (64 per lane), the next chunk in flight while one is
+// multiplied.  UP quantises H along F in its epilogue (one 32-column block
+// per column group: the unit's rows of H are whole MX blocks) for DOWN,
+// which writes bf16 Y.  Forward only (no saved A, B, H).
+template <int KIND, int KS, int FMT>
 __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NB = Traits<KIND>::NB;
   constexpr int NWN = 4 / KS;  // 32-column groups per workgroup
+  constexpr bool FP4 = FMT == 4;
+  constexpr int EPB = FP4 ? 2 : 1;  // K values per byte
+  constexpr int SB = 64 / EPB;      // bytes of one MFMA K step
+  constexpr int CS = 2 * EPB;       // steps per chunk: 128 bytes of a row
   const int N = KIND == KIND_UP ? a.F : a.d, K = KIND == KIND_UP ? a.d : a.F;
+  const int Kb = K / EPB;  // bytes per operand row
   const int ntn = N / (32 * NWN);
   const int E_loc = a.E_loc;
   const int32_t* tp = a.tile_prefix + kStreamTileTable * (E_loc + 1);
   const int total = sload(tp + E_loc) * ntn;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cg = w % NWN, kr = w / NWN;
-  const int kw = K / KS;        // bytes of K per wave
-  const int nstep = kw / 64;    // MFMA K steps per wave
+  const int kw = Kb / KS;       // bytes of K per wave
+  const int nstep = kw / SB;    // MFMA K steps per wave
+  const int nch = (nstep + CS - 1) / CS;
   const int r32 = lane & 31, h = lane >> 5;
   __shared__ f32x16_t red[KS > 1 ? (KS - 1) * NWN : 1][NB][64];
   __shared__ float hs[NWN][32][33];  // UP: H of a column group, 32 rows x 32 columns (+1: no bank conflicts)
@@ -276,10 +285,10 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
     // stored) and weight row n0 + r32, at the wave's first K byte
     const int arow = row0 + r32 < row_end ? row0 + r32 : row0;
     const int64_t kb = (int64_t)kr * kw;
-    const uint8_t* ap = (const uint8_t*)a.A + (int64_t)arow * K + kb;
+    const uint8_t* ap = (const uint8_t*)a.A + (int64_t)arow * Kb + kb;
     const int64_t wrow = (int64_t)lo * N + n0 + r32;
-    const uint8_t* bp0 = (const uint8_t*)a.B0 + wrow * K + kb;
-    const uint8_t* bp1 = NB == 2 ? (const uint8_t*)a.B1 + wrow * K + kb : bp0;
+    const uint8_t* bp0 = (const uint8_t*)a.B0 + wrow * Kb + kb;
+    const uint8_t* bp1 = NB == 2 ? (const uint8_t*)a.B1 + wrow * Kb + kb : bp0;
     const uint8_t* asc = a.a_scale + (int64_t)arow * 2 + h;
     const uint8_t* bsc0 = a.b_scale0 + wrow * 2 + h;
     const uint8_t* bsc1 = NB == 2 ? a.b_scale1 + wrow * 2 + h : bsc0;
@@ -290,34 +299,55 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
-    i32x8_t av[2], bv[2][NB];
-    int as_[2], bs_[2][NB];
-    auto load = [&](int buf, int st) {
-      const int64_t o = (int64_t)st * 64 + 16 * h;
-      const i32x4_t lo_ = *reinterpret_cast<const i32x4_t*>(ap + o), hi_ = *reinterpret_cast<const i32x4_t*>(ap + o + 32);
-      av[buf] = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);
-      as_[buf] = asc[(int64_t)(p0 + st) * a_planes];
+    // per step and operand: E4M3 the lane's two 16-byte pieces, E2M1 its one
+    // (the operand's upper half is not read for E2M1 and stays zero)
+    constexpr int NQ = FP4 ? 1 : 2;
+    i32x4_t av[2][CS][NQ], bv[2][CS][NB][NQ];
+    int as_[2][CS], bs_[2][CS][NB];
+    auto ld = [&](i32x4_t (&dst)[NQ], const uint8_t* p, int st) {
+      const int64_t o = (int64_t)st * SB + 16 * h;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint8_t* bp = b ? bp1 : bp0;
-        const i32x4_t l2 = *reinterpret_cast<const i32x4_t*>(bp + o), h2 = *reinterpret_cast<const i32x4_t*>(bp + o + 32);
-        bv[buf][b] = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-        bs_[buf][b] = (b ? bsc1 : bsc0)[(int64_t)(p0 + st) * b_planes];
+      for (int qq = 0; qq < NQ; ++qq) dst[qq] = *reinterpret_cast<const i32x4_t*>(p + o + 32 * qq);
+    };
+    auto op = [&](const i32x4_t (&v)[NQ]) -> i32x8_t {
+      if constexpr (FP4) {
+        const i32x4_t z = {0, 0, 0, 0};
+        return __builtin_shufflevector(v[0], z, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        return __builtin_shufflevector(v[0], v[NQ - 1], 0, 1, 2, 3, 4, 5, 6, 7);
       }
     };
-    auto compute = [&](int buf) {
+    auto load = [&](int buf, int c) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[buf], bv[buf][b], acc[b], 0, 0, 0, as_[buf], 0,
-                                                                  bs_[buf][b]);
+      for (int j = 0; j < CS; ++j) {
+        const int st = c * CS + j;
+        if (st < nstep) {
+          ld(av[buf][j], ap, st);
+          as_[buf][j] = asc[(int64_t)(p0 + st) * a_planes];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            ld(bv[buf][j][b], b ? bp1 : bp0, st);
+            bs_[buf][j][b] = (b ? bsc1 : bsc0)[(int64_t)(p0 + st) * b_planes];
+          }
+        }
+      }
+    };
+    auto compute = [&](int buf, int c) {
+#pragma unroll
+      for (int j = 0; j < CS; ++j)
+        if (c * CS + j < nstep)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(av[buf][j]), op(bv[buf][j][b]), acc[b], FMT,
+                                                                      FMT, 0, as_[buf][j], 0, bs_[buf][j][b]);
     };
     load(0, 0);
-    for (int st = 0; st < nstep; st += 2) {
-      if (st + 1 < nstep) load(1, st + 1);
-      compute(0);
-      if (st + 1 < nstep) {
-        if (st + 2 < nstep) load(0, st + 2);
-        compute(1);
+    for (int c = 0; c < nch; c += 2) {
+      if (c + 1 < nch) load(1, c + 1);
+      compute(0, c);
+      if (c + 1 < nch) {
+        if (c + 2 < nch) load(0, c + 2);
+        compute(1, c + 1);
       }
     }
 
@@ -351,18 +381,27 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
             v[c] = hs[cg][lane][c];
             amax = fmaxf(amax, fabsf(v[c]));
           }
-          const int se = mx_scale_exp(amax);
           const int row = row0 + lane;
-          uint8_t* dst = (uint8_t*)a.out0 + (int64_t)row * N + n0;
-#pragma unroll
-          for (int q4 = 0; q4 < 2; ++q4) {
+          int se;
+          if constexpr (FP4) {
+            se = mx4_scale_exp(amax);
             u32x4_t wq;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = 16 * q4 + 4 * j;
-              wq[j] = e4m3x4(ldexpf(v[c], -se), ldexpf(v[c + 1], -se), ldexpf(v[c + 2], -se), ldexpf(v[c + 3], -se));
+            for (int j = 0; j < 4; ++j) wq[j] = e2m1x8(v + 8 * j, se);
+            *reinterpret_cast<u32x4_t*>((uint8_t*)a.out0 + (int64_t)row * (N / 2) + n0 / 2) = wq;
+          } else {
+            se = mx_scale_exp(amax);
+            uint8_t* dst = (uint8_t*)a.out0 + (int64_t)row * N + n0;
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+              u32x4_t wq;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int c = 16 * q4 + 4 * j;
+                wq[j] = e4m3x4(ldexpf(v[c], -se), ldexpf(v[c + 1], -se), ldexpf(v[c + 2], -se), ldexpf(v[c + 3], -se));
+              }
+              *reinterpret_cast<u32x4_t*>(dst + 16 * q4) = wq;
             }
-            *reinterpret_cast<u32x4_t*>(dst + 16 * q4) = wq;
           }
           const int blk = n0 / 32;  // H scales: pair planes [F / 64, P_max, 2]
           a.out_scale[(int64_t)(blk >> 1) * a.P_max * 2 + (int64_t)row * 2 + (blk & 1)] = (uint8_t)(se + 127);
@@ -380,7 +419,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
 #endif
 }
 
-template <int KIND, int KS>
+template <int KIND, int KS, int FMT>
 hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
   constexpr int NWN = 4 / KS;
   const int N = KIND == KIND_UP ? g.F : g.d;
@@ -388,14 +427,15 @@ hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
   const int64_t worst = ((g.P_max + kStreamTileRows - 1) / kStreamTileRows + g.E_loc) * ntn;
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_mx_kernel<KIND, KS>, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_mx_kernel<KIND, KS, FMT>, 256, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     return n;
   }();
   const int64_t cap = (int64_t)kNumCUs * per_cu;
   const int blocks = (int)(worst < cap ? worst : cap);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_mx_kernel<KIND, KS>), dim3(blocks), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((stream_mx_kernel<KIND, KS, FMT>), dim3(blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -413,8 +453,16 @@ int stream_ksplit(int K) {
 int stream_mx_ok(int d, int F) { return d % 256 == 0 && F % 128 == 0 && F % 64 == 0; }
 
 hipError_t gemm_stream_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
-  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4>(g, s);
-  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2>(g, s);
+  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4, 0>(g, s);
+  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2, 0>(g, s);
+  return hipErrorInvalidValue;
+}
+
+// MXFP4: the same split (UP d / 8 bytes per wave, DOWN F / 4), a multiple of
+// the 32-byte K step when d % 256 == 0 and F % 128 == 0.
+hipError_t gemm_stream_mxfp4(int kind, const GroupedGemmArgs& g, hipStream_t s) {
+  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4, 4>(g, s);
+  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2, 4>(g, s);
   return hipErrorInvalidValue;
 }
 

@@ -33,10 +33,14 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if (c.T < 0 || c.d <= 0 || c.ffn <= 0 || c.E < 1 || c.E > 1024) return MOK_ERR_INVALID_ARG;
   if (k < 1 || k > c.E) return MOK_ERR_INVALID_ARG;
   if (c.expert_begin < 0 || c.expert_end <= c.expert_begin || c.expert_end > c.E) return MOK_ERR_INVALID_ARG;
-  if (c.precision != MOK_PREC_F32 && c.precision != MOK_PREC_BF16 && c.precision != MOK_PREC_MXFP8)
+  if (c.precision != MOK_PREC_F32 && c.precision != MOK_PREC_BF16 && c.precision != MOK_PREC_MXFP8 &&
+      c.precision != MOK_PREC_MXFP4)
     return MOK_ERR_INVALID_ARG;
-  // bf16: K steps of 64; MXFP8: K steps of 128 bytes (and whole MX blocks); fp32: 16
-  const int mult = c.precision == MOK_PREC_F32 ? 16 : (c.precision == MOK_PREC_MXFP8 ? 128 : 64);
+  // bf16: K steps of 64; MXFP8: K steps of 128 bytes (and whole MX blocks);
+  // MXFP4: 128 bytes = 256 values; fp32: 16
+  const int mult = c.precision == MOK_PREC_F32
+                       ? 16
+                       : (c.precision == MOK_PREC_MXFP8 ? 128 : (c.precision == MOK_PREC_MXFP4 ? 256 : 64));
   if (c.d % mult || c.ffn % mult) return MOK_ERR_INVALID_ARG;
   if ((int64_t)c.T * k >= (int64_t(1) << 31)) return MOK_ERR_INVALID_ARG;
   if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
@@ -55,7 +59,9 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
     if (kp * 256 >= (int64_t(1) << 32)) return MOK_ERR_INVALID_ARG;
   }
   if ((c.flags & MOK_FLAG_TILED_GEMMS) && (c.flags & MOK_FLAG_STREAM_GEMMS)) return MOK_ERR_INVALID_ARG;
-  if (c.precision == MOK_PREC_MXFP8) {
+  // MXFP4 is a forward (inference) precision: nothing is saved for a backward
+  if (c.precision == MOK_PREC_MXFP4 && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_UNSUPPORTED;
+  if (c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4) {
     // every E8M0 scale array (x and H rows, each weight matrix) fits a 32-bit buffer range
     const int64_t Tk = (int64_t)c.T * k, kmax = c.d > c.ffn ? c.d : c.ffn;
     const int64_t E_loc = c.expert_end - c.expert_begin;
@@ -122,7 +128,8 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   const size_t Tk = (size_t)c.T * k, A = act_size(c);
   const int64_t nchunks = ((int64_t)Tk + kSortChunk - 1) / kSortChunk;
   const size_t E_loc = (size_t)(c.expert_end - c.expert_begin);
-  const bool mx = c.precision == MOK_PREC_MXFP8;
+  const bool mx = c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4;
+  const size_t epb = c.precision == MOK_PREC_MXFP4 ? 2 : 1;  // MX codes per byte
   // MXFP8 training: the backward's bf16 buffers as in bf16 mode; its MXFP8 dY
   // reuses the dispatch buffer and [dA | dB] the (then twice as wide) H buffer
   const bool mxb = mx && (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD);
@@ -134,9 +141,9 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->chunk_counts = o;  o = align256(o + (size_t)nchunks * c.E * 4);
   w->chunk_base = o;    o = align256(o + (size_t)nchunks * c.E * 4);
   w->tile_prefix = o;   o = align256(o + (size_t)kNumTileBM * (E_loc + 1) * 4);
-  w->xp = o;            o = align256(o + (size_t)w->xp_rows * c.d * (mx ? 1 : A));
+  w->xp = o;            o = align256(o + (mx ? (size_t)w->xp_rows * c.d / epb : (size_t)w->xp_rows * c.d * A));
   w->xp_scale = o;      o = align256(o + (mx ? (size_t)w->xp_rows * (c.d / 32) : 0));
-  w->hq = o;            o = align256(o + (mx ? Tk * hq_cols : 0));
+  w->hq = o;            o = align256(o + (mx ? Tk * hq_cols / epb : 0));
   w->hq_scale = o;      o = align256(o + (mx ? Tk * (hq_cols / 32) : 0));
   w->dy = o;            o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
   w->dab = o;           o = align256(o + (mx && !mxb ? 0 : Tk * 2 * c.ffn * A));
@@ -156,6 +163,7 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
 hipError_t run_gemm(int prec, int kind, const GroupedGemmArgs& g, hipStream_t s) {
   if (prec == MOK_PREC_F32) return gemm_f32(kind, g, s);
   if (prec == MOK_PREC_MXFP8) return gemm_mxfp8(kind, g, s);
+  if (prec == MOK_PREC_MXFP4) return gemm_mxfp4(kind, g, s);
   return gemm_bf16(kind, g, s);
 }
 
@@ -205,13 +213,15 @@ inline bool streaming_gemms(const mok_moe_config& c, int32_t k) {
   return (c.flags & MOK_FLAG_STREAM_GEMMS) || P <= kStreamAutoRowsPerExpert * E_loc;
 }
 // The same choice for an MXFP8 forward that saves nothing for backward
-// (inference): whole layer, d a multiple of 256; up to eight rows per local
-// expert on average (same-box at d 4096, E 128, k 8, F 1536: 653 / 788 us at
-// T 128, streaming / tiled; 266 / 347 us at T 16).
+// (inference), and for every MXFP4 forward: whole layer, d a multiple of 256;
+// up to eight rows per local expert on average (MXFP8, same-box at d 4096,
+// E 128, k 8, F 1536: 653 / 788 us at T 128, streaming / tiled; 266 / 347 us
+// at T 16).
 constexpr int64_t kStreamAutoRowsPerExpertMx = 8;
 inline bool streaming_gemms_mx(const mok_moe_config& c, int32_t k) {
   const int64_t P = (int64_t)c.T * k, E_loc = c.expert_end - c.expert_begin;
-  if (c.precision != MOK_PREC_MXFP8 || c.minibatch_rows != 0 || (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ||
+  const bool mx = c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4;
+  if (!mx || c.minibatch_rows != 0 || (c.flags & MOK_FLAG_SAVE_FOR_BACKWARD) ||
       (c.flags & MOK_FLAG_TILED_GEMMS) || P > kStreamMaxPairs || !stream_mx_ok(c.d, c.ffn))
     return false;
   return (c.flags & MOK_FLAG_STREAM_GEMMS) || P <= kStreamAutoRowsPerExpertMx * E_loc;
@@ -243,7 +253,8 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
                            void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
                            int32_t* expert_offsets, void* saved, void* workspace, const WorkspaceLayout& wl,
                            void* stream) {
-  const bool mx = c.precision == MOK_PREC_MXFP8;
+  const bool mx4 = c.precision == MOK_PREC_MXFP4;
+  const bool mx = c.precision == MOK_PREC_MXFP8 || mx4;
   hipStream_t s = (hipStream_t)stream;
   const int T = c.T, E = c.E, d = c.d, F = c.ffn, eb = c.expert_begin, E_loc = c.expert_end - c.expert_begin;
   const int bf16 = c.precision != MOK_PREC_F32;
@@ -288,7 +299,8 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
   if (mx) {
     uint8_t* xq = at<uint8_t>(workspace, wl.xp);
     uint8_t* xs = at<uint8_t>(workspace, wl.xp_scale);
-    MOK_STAGE(MOK_STAGE_DISPATCH, launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, wl.xp_rows, status, s));
+    MOK_STAGE(MOK_STAGE_DISPATCH, mx4 ? launch_dispatch_gather_mxfp4(x, s_rop, T, k, d, xq, xs, wl.xp_rows, status, s)
+                                      : launch_dispatch_gather_mxfp8(x, s_rop, T, k, d, xq, xs, wl.xp_rows, status, s));
     const size_t w13_scales = (size_t)E_loc * F * (d / 32);
     g.A = xq;
     g.a_scale = xs;
@@ -305,7 +317,8 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
       g.out1 = at<void>(saved, sl.H);
     }
     const bool stream_mx = streaming_gemms_mx(c, k);
-    MOK_STAGE(MOK_STAGE_GEMM_UP, stream_mx ? gemm_stream_mxfp8(KIND_UP, g, s) : run_gemm(c.precision, KIND_UP, g, s));
+    auto stream_gemm = mx4 ? gemm_stream_mxfp4 : gemm_stream_mxfp8;
+    MOK_STAGE(MOK_STAGE_GEMM_UP, stream_mx ? stream_gemm(KIND_UP, g, s) : run_gemm(c.precision, KIND_UP, g, s));
     GroupedGemmArgs g2 = g;
     g2.save = 0;
     g2.out1 = nullptr;
@@ -318,7 +331,7 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
     g2.out0 = at<void>(saved, sl.Y);
     g2.out_scale = nullptr;
     MOK_STAGE(MOK_STAGE_GEMM_DOWN,
-              stream_mx ? gemm_stream_mxfp8(KIND_DOWN, g2, s) : run_gemm(c.precision, KIND_DOWN, g2, s));
+              stream_mx ? stream_gemm(KIND_DOWN, g2, s) : run_gemm(c.precision, KIND_DOWN, g2, s));
   } else if (c.minibatch_rows > 0) {
     // Ring-buffer minibatch pipeline ([kucoin §02]: tunable minibatches drawn
     // from a fixed ring token buffer; [fluid «Comment MoK…»]): launch m copies
@@ -487,6 +500,8 @@ mok_status mok_moe_workspace_layout(const mok_moe_config* cfg, int32_t k, mok_wo
   out->xp = w.xp;
   out->xp_scale = w.xp_scale;
   out->xp_rows = w.xp_rows;
+  out->hq = w.hq;
+  out->hq_scale = w.hq_scale;
   out->dy = w.dy;
   out->dab = w.dab;
   out->dxp = w.dxp;
@@ -519,7 +534,7 @@ mok_status mok_moe_forward(const void* x, const float* router_logits, const void
     if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
   for (const void* p : per_token)
     if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
-  const bool mx = c.precision == MOK_PREC_MXFP8;
+  const bool mx = c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4;
   if (mx && !w_scales) return MOK_ERR_INVALID_ARG;
   if (!mx && w_scales) return MOK_ERR_INVALID_ARG;
 
@@ -566,7 +581,7 @@ mok_status mok_moe_backward(const void* dout, const void* x, const float* router
     if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
   for (const void* p : per_token)
     if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
-  if (c.precision == MOK_PREC_MXFP8) return MOK_ERR_UNSUPPORTED;
+  if (c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4) return MOK_ERR_UNSUPPORTED;
   if (!(c.flags & MOK_FLAG_SAVE_FOR_BACKWARD)) return MOK_ERR_INVALID_ARG;
 
   hipStream_t s = (hipStream_t)stream;
@@ -658,6 +673,16 @@ mok_status mok_quantize_mxfp8(const void* src_bf16, int64_t rows, int64_t K, uin
   if (rows == 0) return MOK_OK;
   if (!src_bf16 || !dst_e4m3 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e4m3)) return MOK_ERR_INVALID_ARG;
   MOK_HIP(launch_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, (hipStream_t)stream));
+  return MOK_OK;
+}
+
+mok_status mok_quantize_mxfp4(const void* src_bf16, int64_t rows, int64_t K, uint8_t* dst_e2m1, uint8_t* dst_e8m0,
+                              void* stream) {
+  if (rows < 0 || K <= 0 || K % 64) return MOK_ERR_INVALID_ARG;
+  if (rows * (K / 32) >= (int64_t(1) << 32)) return MOK_ERR_INVALID_ARG;  // scale planes addressed in 32 bits
+  if (rows == 0) return MOK_OK;
+  if (!src_bf16 || !dst_e2m1 || !dst_e8m0 || !aligned16(src_bf16) || !aligned16(dst_e2m1)) return MOK_ERR_INVALID_ARG;
+  MOK_HIP(launch_quantize_mxfp4(src_bf16, rows, K, dst_e2m1, dst_e8m0, (hipStream_t)stream));
   return MOK_OK;
 }
 

@@ -142,6 +142,37 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
+// OCP E2M1 (FP4: sign, two exponent bits with bias 1, one mantissa bit;
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) from an fp32 value: round to nearest
+// even, saturate to +-6, keep the sign of zero.  The magnitude code is the
+// number of rounding thresholds |v| reaches; at a midpoint the even code
+// (mantissa bit 0) wins, i.e. the magnitude below for the midpoints 0.25,
+// 1.25, 2.5 and 5, the one above for 0.75, 1.75 and 3.5.
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+// E2M1 codes of v[0..7] * 2^-se, element i in bits [4 i, 4 i + 4) (the byte
+// order the scaled MFMA reads: the lower K element in the low nibble).
+__device__ __forceinline__ uint32_t e2m1x8(const float* v, int se) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_rne(ldexpf(v[i], -se)) << (4 * i);
+  return w;
+}
+
+// Shared-scale exponent of an MXFP4 block: floor(log2 amax) - 2 (the largest
+// E2M1 power of two is 2^2), clamped to [-127, 127]; amax = 0 (or
+// fp32-subnormal) gives -127.
+__device__ __forceinline__ int mx4_scale_exp(float amax) {
+  int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;
+  int s = ef - 127 - 2;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
 // ------------------------------------------------------------ HBM -> LDS DMA
 // Buffer resource (V#) of `bytes` bytes at p: stride 0, raw addressing;
 // offsets at or past `bytes` read as zero.  All fields must be wave-uniform.

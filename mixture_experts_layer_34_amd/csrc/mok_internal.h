@@ -105,6 +105,13 @@ hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pai
                                         hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8_t* q,
                                  uint8_t* sc, hipStream_t s);
+// MXFP4: E2M1 codes two per byte (the lower element in the low nibble), xq
+// rows of d / 2 bytes; scales in the same pair planes as MXFP8.
+hipError_t launch_dispatch_gather_mxfp4(const void* x, const int32_t* row_of_pair, int T, int k,
+                                        int d, uint8_t* xq, uint8_t* xs, int64_t xs_rows, int32_t* status,
+                                        hipStream_t s);
+hipError_t launch_quantize_mxfp4(const void* src, int64_t rows, int64_t K, uint8_t* q,
+                                 uint8_t* sc, hipStream_t s);
 // MXFP8 of the transpose of nmat [R, C] bf16 matrices along R (R, C multiples
 // of 64): row c of matrix m at q + m q_mat + c q_ld + q_koff, scales in pair
 // planes of `rows` rows, global row m C + c, K step (q_koff + r) / 64.
@@ -180,6 +187,8 @@ hipError_t gemm_stream_bf16(int kind, const GroupedGemmArgs& g, hipStream_t s);
 // 32-column units; forward only.  stream_mx_ok: d % 256 == 0, F % 128 == 0.
 int stream_mx_ok(int d, int F);
 hipError_t gemm_stream_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
+// The same with E2M1 operands (MXFP4 forward): d % 256 == 0, F % 128 == 0.
+hipError_t gemm_stream_mxfp4(int kind, const GroupedGemmArgs& g, hipStream_t s);
 
 // One step of the ring-buffer minibatch pipeline (bf16): in a single launch,
 // mover tiles copy the rows of minibatch m+1 into their ring slot, compute
@@ -200,5 +209,9 @@ struct MinibatchStepArgs {
 hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s);
 hipError_t gemm_f32(int kind, const GroupedGemmArgs& g, hipStream_t s);
 hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
+// MXFP4 forward (inference) UP and DOWN: the MXFP8 kernels with E2M1 operands
+// (two codes per byte, activations as written by launch_dispatch_gather_mxfp4,
+// H quantised to MXFP4 along F in UP's epilogue); K a multiple of 256.
+hipError_t gemm_mxfp4(int kind, const GroupedGemmArgs& g, hipStream_t s);
 
 }  // namespace mok

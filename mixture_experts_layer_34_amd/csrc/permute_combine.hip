@@ -47,6 +47,11 @@ __device__ __forceinline__ void buf_store16(rsrc_t rs, int off, uint4 u) {
                                          rs, off, 0, 0);
 }
 
+__device__ __forceinline__ void buf_store8(rsrc_t rs, int off, uint2 u) {
+  __builtin_amdgcn_raw_buffer_store_b64(decltype(__builtin_amdgcn_raw_buffer_load_b64(rs, 0, 0, 0)){u.x, u.y}, rs, off,
+                                        0, 0);
+}
+
 // ------------------------------------------------------------------ dispatch
 // One block per token: read x[t] once (16-byte vectors), write it to the
 // rows of its local pairs.  The token's row indices are the same for every
@@ -188,6 +193,67 @@ hipError_t launch_dispatch_gather_mxfp8(const void* x, const int32_t* row_of_pai
   return hipGetLastError();
 }
 
+// MXFP4 counterpart (E2M1 codes, two per byte, the lower element in the low
+// nibble): 16 elements per lane, two lanes per MX block of 32, four per 64-wide
+// K step; each lane writes its 8 code bytes, the first of four lanes the
+// step's two scale bytes.
+__global__ __launch_bounds__(256) void dispatch_gather_mxfp4_kernel(const bf16_t* __restrict__ x,
+                                                                    const int32_t* __restrict__ rop, int ntok,
+                                                                    int k, int d, uint8_t* __restrict__ xq,
+                                                                    uint8_t* __restrict__ xs, int64_t xs_rows,
+                                                                    int32_t* __restrict__ status) {
+  const int nv = d / 16;
+  const int lane = lane_id();
+  for (int t = blockIdx.x; t < ntok; t += gridDim.x) {
+    const int32_t* tr = rop + (int64_t)t * k;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * d);
+    for (int j0 = 0; j0 < k; j0 += kSlotGroup) {
+      int32_t r[kSlotGroup];
+      rsrc_t rs[kSlotGroup];
+#pragma unroll
+      for (int i = 0; i < kSlotGroup; ++i) {
+        const int jc = j0 + i < k ? j0 + i : k - 1;
+        const int32_t rv = checked_row(tr[jc], xs_rows, status);
+        r[i] = (j0 + i < k) ? rv : -1;
+        rs[i] = row_rsrc(xq, r[i], d / 2);
+      }
+      for (int v = threadIdx.x; v < nv; v += 256) {
+        const uint4 w0 = src[2 * v], w1 = src[2 * v + 1];
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float f[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          f[2 * i] = __uint_as_float(w[i] << 16);
+          f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+          amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const int se = mx4_scale_exp(amax);
+        const uint2 codes = make_uint2(e2m1x8(f, se), e2m1x8(f + 8, se));
+        const int se_hi = __shfl(se, (lane & ~3) + 2, 64);
+        const uint16_t pair = (uint16_t)((se + 127) | ((se_hi + 127) << 8));
+#pragma unroll
+        for (int i = 0; i < kSlotGroup; ++i) {
+          if (r[i] < 0) continue;  // remote slot
+          buf_store8(rs[i], 8 * v, codes);
+          if ((v & 3) == 0)  // pair plane v / 4, row r
+            *reinterpret_cast<uint16_t*>(xs + (int64_t)(v >> 2) * xs_rows * 2 + (int64_t)r[i] * 2) = pair;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch_gather_mxfp4(const void* x, const int32_t* row_of_pair, int T, int k, int d,
+                                        uint8_t* xq, uint8_t* xs, int64_t xs_rows, int32_t* status, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int blocks = T < 16384 ? T : 16384;
+  hipLaunchKernelGGL(dispatch_gather_mxfp4_kernel, dim3(blocks), dim3(256), 0, s, (const bf16_t*)x,
+                     row_of_pair, T, k, d, xq, xs, xs_rows, status);
+  return hipGetLastError();
+}
+
 // Quantise a [rows, K] bf16 matrix along its rows.  Vector i covers elements
 // [8i, 8i + 8); K % 64 == 0 keeps each block of 32 (and each pair of blocks)
 // inside one row.  Scales in pair planes: block b of row r at
@@ -222,6 +288,52 @@ hipError_t launch_quantize_mxfp8(const void* src, int64_t rows, int64_t K, uint8
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)src, nvec,
                      rows, K, q, sc);
+  return hipGetLastError();
+}
+
+// MXFP4 quantisation of a [rows, K] bf16 matrix along its rows: vector i
+// covers elements [8i, 8i + 8) and becomes one dword of eight E2M1 codes
+// (the lower element in the low nibble); scales as above.
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const bf16_t* __restrict__ src, int64_t nvec,
+                                                             int64_t rows, int64_t K, uint32_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sc) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t iters = (nvec + stride - 1) / stride;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t v = it * stride + (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool act = v < nvec;
+    const uint4 val = act ? reinterpret_cast<const uint4*>(src)[v] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+    float f[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int se = mx4_scale_exp(amax);
+    const uint32_t codes = e2m1x8(f, se);
+    if (act) {
+      q[v] = codes;
+      if ((v & 3) == 0) {
+        const int64_t r = (8 * v) / K, b = ((8 * v) % K) / 32;
+        sc[(b >> 1) * rows * 2 + r * 2 + (b & 1)] = (uint8_t)(se + 127);
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_mxfp4(const void* src, int64_t rows, int64_t K, uint8_t* q, uint8_t* sc,
+                                 hipStream_t s) {
+  const int64_t nvec = rows * K / 8;
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const bf16_t*)src, nvec,
+                     rows, K, (uint32_t*)q, sc);
   return hipGetLastError();
 }
 

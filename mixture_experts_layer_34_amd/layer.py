@@ -165,6 +165,18 @@ def quantize_mxfp8(w: torch.Tensor):
     return q, sc
 
 
+def quantize_mxfp4(w: torch.Tensor):
+    """E2M1 codes (two per byte, the lower element in the low nibble; shape
+    [..., K/2]) and E8M0 scales [K/64, rows, 2] of a bf16 tensor along its
+    last axis, for the weights of an MXFP4 forward."""
+    K = w.shape[-1]
+    rows = w.numel() // K
+    q = torch.empty(w.shape[:-1] + (K // 2,), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((K // 64, rows, 2), dtype=torch.uint8, device=w.device)
+    mok.mok_quantize_mxfp4(w, rows, K, q, sc, _stream())
+    return q, sc
+
+
 def scales_by_row(sc: torch.Tensor) -> torch.Tensor:
     """[rows, K/32] view (a copy) of pair-plane scales [K/64, rows, 2]."""
     planes, rows, _ = sc.shape

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmok.so")
 
 MOK_OK, MOK_ERR_INVALID_ARG, MOK_ERR_UNSUPPORTED, MOK_ERR_WORKSPACE, MOK_ERR_HIP, MOK_ERR_DEVICE = range(6)
-MOK_PREC_F32, MOK_PREC_BF16, MOK_PREC_MXFP8 = range(3)
+MOK_PREC_F32, MOK_PREC_BF16, MOK_PREC_MXFP8, MOK_PREC_MXFP4 = range(4)
 MOK_FLAG_SAVE_FOR_BACKWARD = 0x1
 MOK_FLAG_SIGMOID_GATES = 0x2
 MOK_FLAG_RENORM_GATES = 0x4
@@ -25,7 +25,7 @@ MOK_FLAG_MXFP8_WGRAD = 0x40
 STAGES = ["router", "sort", "dispatch", "gemm_up", "gemm_down", "combine", "bwd_gate", "gemm_dh", "gemm_dx",
           "reduce_dx", "gemm_dw2", "regather", "gemm_dw13"]
 MOK_NUM_STAGES = len(STAGES)
-PRECISIONS = {"f32": MOK_PREC_F32, "bf16": MOK_PREC_BF16, "mxfp8": MOK_PREC_MXFP8}
+PRECISIONS = {"f32": MOK_PREC_F32, "bf16": MOK_PREC_BF16, "mxfp8": MOK_PREC_MXFP8, "mxfp4": MOK_PREC_MXFP4}
 
 
 class mok_moe_config(ctypes.Structure):
@@ -44,7 +44,8 @@ class mok_saved_layout(ctypes.Structure):
 
 class mok_workspace_layout(ctypes.Structure):
     _fields_ = [("status", ctypes.c_size_t), ("xp", ctypes.c_size_t), ("xp_scale", ctypes.c_size_t),
-                ("xp_rows", ctypes.c_int64), ("dy", ctypes.c_size_t), ("dab", ctypes.c_size_t),
+                ("xp_rows", ctypes.c_int64), ("hq", ctypes.c_size_t), ("hq_scale", ctypes.c_size_t),
+                ("dy", ctypes.c_size_t), ("dab", ctypes.c_size_t),
                 ("dxp", ctypes.c_size_t), ("wq", ctypes.c_size_t), ("wq_scale", ctypes.c_size_t),
                 ("k_pad", ctypes.c_int64), ("total", ctypes.c_size_t)]
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
                                        _P, _P, _P, _P, _P, _P, _P, _P]
         L.mok_quantize_mxfp8.restype = ctypes.c_int
         L.mok_quantize_mxfp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]
+        L.mok_quantize_mxfp4.restype = ctypes.c_int
+        L.mok_quantize_mxfp4.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]
         L.mok_moe_backward_mxfp8.restype = ctypes.c_int
         L.mok_moe_backward_mxfp8.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P, _P, _P,
                                              _P, _P, _P, _P, _P, _P, _P, _P]
@@ -181,6 +184,11 @@ def mok_moe_backward(dout, x, router_logits, W1, W3, W2, k, cfg, saved, dx, dW1,
 def mok_quantize_mxfp8(src_bf16, rows, K, dst_e4m3, dst_e8m0, stream=0):
     _check(lib().mok_quantize_mxfp8(_ptr(src_bf16), rows, K, _ptr(dst_e4m3), _ptr(dst_e8m0), stream or None),
            "mok_quantize_mxfp8")
+
+
+def mok_quantize_mxfp4(src_bf16, rows, K, dst_e2m1, dst_e8m0, stream=0):
+    _check(lib().mok_quantize_mxfp4(_ptr(src_bf16), rows, K, _ptr(dst_e2m1), _ptr(dst_e8m0), stream or None),
+           "mok_quantize_mxfp4")
 
 
 def mok_moe_backward_mxfp8(dout, x, router_logits, k, cfg, wt_e4m3, wt_e8m0, saved, dx, dW1, dW3, dW2, dgate,

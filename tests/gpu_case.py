@@ -6,7 +6,8 @@ import numpy as np
 import torch
 
 import workloads as W
-from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp8, quantize_mxfp8_backward_weights
+from mixture_experts_layer_34_amd.layer import (MoeBuffers, MoeShape, quantize_mxfp4, quantize_mxfp8,
+                                                quantize_mxfp8_backward_weights)
 
 
 def note(msg: str):
@@ -65,6 +66,14 @@ def run_layer(w: W.Workload, inp: dict, backward: bool = False, buf: MoeBuffers 
             inp["W1q"], inp["W3q"], inp["W2q"] = q1, q3, q2
             inp["w_scales"] = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
         W1, W3, W2, scales = inp["W1q"], inp["W3q"], inp["W2q"], inp["w_scales"]
+    elif w.precision == "mxfp4":
+        if "W1q4" not in inp:
+            q1, s1 = quantize_mxfp4(inp["W1"])
+            q3, s3 = quantize_mxfp4(inp["W3"])
+            q2, s2 = quantize_mxfp4(inp["W2"])
+            inp["W1q4"], inp["W3q4"], inp["W2q4"] = q1, q3, q2
+            inp["w_scales4"] = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
+        W1, W3, W2, scales = inp["W1q4"], inp["W3q4"], inp["W2q4"], inp["w_scales4"]
     buf.forward(inp["x"], inp["logits"], W1, W3, W2, scales)
     if backward and w.precision == "mxfp8":
         if "wt" not in inp:

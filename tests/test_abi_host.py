@@ -222,3 +222,38 @@ def test_ring_mode_validation():
     full_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096), 2)
     ring_ws, _ = mok.mok_moe_workspace_query(_cfg(T=4096, minibatch_rows=256, ring_bytes=2 * 256 * 128 * 2), 2)
     assert full_ws - ring_ws >= (4096 * 2 - 512) * 128 * 2
+
+
+def test_mxfp4_config_rules_and_layout():
+    """MOK_PREC_MXFP4: a forward (inference) precision with d and F multiples
+    of 256; saving for backward or a ring is unsupported; its code buffers
+    hold two E2M1 codes per byte (half the MXFP8 bytes), the scales as many
+    bytes as MXFP8's."""
+    for over in (dict(d=384), dict(ffn=384), dict(d=128)):
+        with pytest.raises(mok.MokError) as ei:
+            mok.mok_moe_workspace_query(_cfg(**{**dict(precision="mxfp4", flags=0, d=256, ffn=256), **over}), 2)
+        assert ei.value.status == mok.MOK_ERR_INVALID_ARG
+    for over in (dict(flags=mok.MOK_FLAG_SAVE_FOR_BACKWARD), dict(flags=0, minibatch_rows=64, ring_bytes=1 << 20)):
+        with pytest.raises(mok.MokError) as ei:
+            mok.mok_moe_workspace_query(_cfg(precision="mxfp4", d=256, ffn=256, **over), 2)
+        assert ei.value.status == mok.MOK_ERR_UNSUPPORTED
+    T, d, F, E, k = 300, 512, 768, 8, 2
+    l4 = mok.mok_moe_workspace_layout(_cfg(precision="mxfp4", T=T, d=d, ffn=F, E=E, flags=0), k)
+    l8 = mok.mok_moe_workspace_layout(_cfg(precision="mxfp8", T=T, d=d, ffn=F, E=E, flags=0), k)
+    assert l4["xp_rows"] == T * k
+    assert l4["xp_scale"] - l4["xp"] >= T * k * d // 2
+    assert l4["xp_scale"] - l4["xp"] < l8["xp_scale"] - l8["xp"]
+    assert l4["total"] < l8["total"]
+    # forward checks before any launch: scales required, d % 256
+    assert _fwd(_cfg(precision="mxfp4", flags=0, d=256, ffn=256)) == mok.MOK_ERR_INVALID_ARG
+    assert _fwd(_cfg(precision="mxfp4", flags=0, d=384, ffn=256), scales=0xD0000) == mok.MOK_ERR_INVALID_ARG
+    assert _fwd(_cfg(precision="mxfp4", d=256, ffn=256), scales=0xD0000) == mok.MOK_ERR_UNSUPPORTED
+
+
+def test_quantize_mxfp4_rejects_bad_shapes():
+    L = mok.lib()
+    assert L.mok_quantize_mxfp4(0x1000, 4, 96, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG  # K % 64
+    assert L.mok_quantize_mxfp4(0x1000, -1, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_quantize_mxfp4(None, 4, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_quantize_mxfp4(0x1000, 4, 64, 0x2008, 0x3000, None) == mok.MOK_ERR_INVALID_ARG  # misaligned
+    assert L.mok_quantize_mxfp4(0x1000, 0, 64, 0x2000, 0x3000, None) == mok.MOK_OK

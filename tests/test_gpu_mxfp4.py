@@ -1,0 +1,228 @@
+"""GPU parity of the MXFP4 forward (E2M1 elements, OCP MX v1.0) against the
+oracle's MXFP4 mode.
+
+Bit for bit: the weights through mok_quantize_mxfp4, and the x rows the
+dispatch quantises (read back from the workspace).  Both sides take the
+same exact power-of-two scaling and round-to-nearest-even of the same bf16
+values.
+
+H codes: the first product's epilogue quantises H from fp32 sums, the
+oracle from float64 ones.  Products of E2M1 values with power-of-two scales
+are exact, and so are their fp32 sums at these sizes (each sum spans few
+binades), so both sides hold the same A and B; h = silu(a) * b then differs
+by the fp32 rounding of the device's silu and product.  A code may differ
+only where h lies within that rounding of a decision point: a rounding
+midpoint of the E2M1 magnitudes, or a power of two for the block scale.  The
+test requires every differing code or scale to be such a case, and such
+cases to be rare.
+
+DOWN and the combine: Y against the device's own H codes times the oracle's
+W2 codes (exact products, one bf16 rounding: 2^-8 of the largest), out
+against the combine of the device's Y.  End to end, out and Y against the
+oracle within 2e-2 of the largest (bf16 outputs, plus the rare decision
+differences above)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from mixture_experts_layer_34_amd import mok
+from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, quantize_mxfp4, scales_by_row
+from oracle import mok_oracle as O
+from tests.gpu_case import LazyExperts, host_inputs, note, rel_inf, run_layer, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL_E2E = 2e-2
+TOL_BF16 = 2.0 ** -8
+_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])   # E2M1 rounding midpoints
+_REL = 1e-5                                                  # fp32 slack of the device's h
+
+
+def _unpack(b: np.ndarray) -> np.ndarray:
+    """E2M1 codes from bytes (element 2i in the low nibble of byte i)."""
+    b = np.asarray(b, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def _special_rows():
+    """Blocks at the rule's edges: all zero, amax a power of two, amax / X in
+    (6, 8) (saturation), every E2M1 rounding midpoint (ties to even), values
+    rounding to +-0, huge values."""
+    rows = np.zeros((6, 64), np.float32)
+    rows[1, 32:] = np.linspace(-4, 4, 32)
+    rows[2, 3] = -32.0
+    rows[2, 9] = 1.0
+    rows[2, 40] = 15.0                        # X = 2: 7.5 saturates to 6
+    rows[3, :] = np.float32(2.0 ** -20)
+    rows[3, 0] = 1.0                          # X = 2^-2: the rest round to 0 (signs kept)
+    rows[3, 5] = -np.float32(2.0 ** -20)
+    rows[4, :7] = _MIDS                       # amax 5 -> X = 1: the midpoints themselves
+    rows[4, 7:14] = -_MIDS
+    rows[4, 32:39] = _MIDS * 2.0 ** -6        # the same one scale lower
+    rows[4, 39] = 4.0 * 2.0 ** -6
+    rows[5, :] = np.float32(1e30)
+    return rows
+
+
+def test_quantize_mxfp4_bit_exact():
+    g = torch.Generator().manual_seed(13)
+    base = torch.randn(256, 512, generator=g) * torch.exp(torch.randn(256, 1, generator=g) * 4)
+    special = torch.nn.functional.pad(torch.from_numpy(_special_rows()), (0, 512 - 64))
+    w = torch.cat([base, special]).to(torch.bfloat16)
+    note(f"quantize mxfp4 {tuple(w.shape)}")
+    q, sc = quantize_mxfp4(w.cuda())
+    torch.cuda.synchronize()
+    assert q.shape == (w.shape[0], 256) and sc.shape == (512 // 64, w.shape[0], 2)
+    ref_q, ref_s = O.mxfp4_quantize(w.float().numpy())
+    assert np.array_equal(scales_by_row(sc).cpu().numpy(), ref_s), "E8M0 scales differ"
+    got = _unpack(q.cpu().numpy())
+    bad = np.argwhere(got != ref_q)
+    assert bad.size == 0, f"{len(bad)} E2M1 codes differ, first at {bad[:3].tolist()}"
+
+
+def test_quantize_mxfp4_batched_weights_layout():
+    g = torch.Generator().manual_seed(14)
+    w = (torch.randn(3, 64, 256, generator=g) * 0.02).to(torch.bfloat16)
+    q, sc = quantize_mxfp4(w.cuda())
+    torch.cuda.synchronize()
+    assert q.shape == (3, 64, 128) and sc.shape == (4, 3 * 64, 2)
+    by_row = scales_by_row(sc).reshape(3, 64, 8)
+    for e in range(3):
+        rq, rs = O.mxfp4_quantize(w[e].float().numpy())
+        assert np.array_equal(_unpack(q[e].cpu().numpy()), rq) and np.array_equal(by_row[e].cpu().numpy(), rs)
+
+
+def _layer(w, inp, path):
+    T = inp["x"].shape[0]
+    shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision="mxfp4", expert_begin=w.expert_begin,
+                     expert_end=w.e_end, save_for_backward=False, gemm_path=path)
+    buf = run_layer(w, inp, backward=False, buf=MoeBuffers(shape))
+    assert buf.device_status() == (mok.MOK_OK, 0)
+    return buf
+
+
+def _ws_codes(buf, name, scale_name, rows, cols):
+    """(codes [rows, cols], scales [rows, cols / 32]) of a workspace MXFP4
+    array whose scale planes hold P_max rows."""
+    s = buf.shape
+    P_max = s.T * s.k
+    codes = _unpack(to_np(buf.workspace_view(name, torch.uint8, (P_max, cols // 2)))[:rows])
+    sc = buf.workspace_view(scale_name, torch.uint8, (cols // 64, P_max, 2))
+    return codes, to_np(scales_by_row(sc))[:rows]
+
+
+def _decision_points_only(h, dev_codes, dev_scales):
+    """Checks device H codes against the oracle's quantisation of float64 h:
+    equal except where h lies within _REL of a decision point.  Returns the
+    number of differing codes."""
+    ref_codes, ref_scales = O.mxfp4_quantize(h)
+    nb = h.shape[1] // 32
+    hb = np.abs(h).reshape(h.shape[0], nb, 32)
+    amax = hb.max(axis=2)
+    sdiff = dev_scales != ref_scales
+    if sdiff.any():
+        a = amax[sdiff]
+        near_pow2 = np.abs(a / np.exp2(np.round(np.log2(np.maximum(a, 1e-300)))) - 1) <= _REL
+        assert near_pow2.all(), f"{(~near_pow2).sum()} block scales differ away from a power of two"
+    same = np.repeat(~sdiff, 32, axis=1)
+    cdiff = (dev_codes != ref_codes) & same
+    if cdiff.any():
+        X = np.repeat(np.ldexp(1.0, ref_scales.astype(np.int64) - 127), 32, axis=1)
+        v = np.abs(h[cdiff]) / X[cdiff]
+        near = (np.abs(v[:, None] - _MIDS[None, :]) <= _REL * np.maximum(v[:, None], 1e-30)).any(axis=1)
+        adj = np.abs((dev_codes[cdiff].astype(int) & 7) - (ref_codes[cdiff].astype(int) & 7)) <= 1
+        assert near.all() and adj.all(), f"{(~near).sum()} H codes differ away from a rounding midpoint"
+    n = int(cdiff.sum() + 32 * sdiff.sum())
+    assert n <= max(8, 1e-4 * h.size), f"{n} H code decisions differ"
+    return n
+
+
+CASES = [
+    ("small", dict(T=200, d=512, E=16, k=4, F=768)),
+    ("ragged", dict(T=333, d=256, E=6, k=2, F=512)),
+    ("local", dict(T=256, d=512, E=32, k=4, F=256, expert_begin=8, expert_end=20)),
+    ("one-token", dict(T=1, d=1024, E=64, k=8, F=512)),
+    ("skewed", dict(T=400, d=256, E=5, k=1, F=256, notes={"zipf": 5.0})),
+]
+
+
+@pytest.mark.parametrize("path", ["tiled", "stream"])
+@pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
+def test_mxfp4_forward_matches_oracle(name, over, path):
+    base = "bf16_train" if "zipf" in over.get("notes", {}) else "bf16_fwd"
+    w = W.scaled(base, precision="mxfp4", backward=False, **over)
+    note(f"mxfp4 {name} {path} {over}")
+    inp = W.make_inputs(w, device="cuda")
+    buf = _layer(w, inp, path)
+    h = host_inputs(inp)
+    W1, W3, W2 = (to_np(inp[n]).astype(np.float64) for n in ("W1", "W3", "W2"))
+    fw = O.forward(h["x"], h["logits"], W1, W3, W2, w.k, w.expert_begin, w.e_end, mxfp4=True)
+    assert np.array_equal(to_np(buf.topk_idx), fw["idx"])
+    off = fw["offsets"]
+    P = int(off[w.e_end] - off[w.expert_begin])
+    if P == 0:
+        assert not to_np(buf.out).any()
+        return
+    # x rows: bit-exact
+    xc, xs = _ws_codes(buf, "xp", "xp_scale", P, w.d)
+    rc, rs = O.mxfp4_quantize(h["x"][fw["pair_of_row"][:P] // w.k])
+    assert np.array_equal(xs, rs) and np.array_equal(xc, rc), "dispatched x codes differ"
+    # H: equal up to decisions at their boundaries
+    hc, hs = _ws_codes(buf, "hq", "hq_scale", P, w.F)
+    r0 = int(off[w.expert_begin])
+    href = O.silu(fw["A"][r0:r0 + P]) * fw["B"][r0:r0 + P]
+    nd = _decision_points_only(href, hc, hs)
+    # DOWN on the device's own H codes; the combine of the device's Y
+    Hd = O.mxfp4_dequantize(hc, hs)
+    Y = to_np(buf.saved_view("Y", torch.bfloat16, (w.T * w.k, w.d))[:P])
+    yref = np.zeros_like(Y, dtype=np.float64)
+    for e in range(w.expert_begin, w.e_end):
+        a, b = int(off[e]) - r0, int(off[e + 1]) - r0
+        if a < b:
+            yref[a:b] = Hd[a:b] @ O.mxfp4_qdq(W2[e - w.expert_begin]).T
+    e_y = rel_inf(Y, yref)
+    full_y = np.zeros((w.T * w.k, w.d))
+    full_y[r0:r0 + P] = Y
+    e_out = rel_inf(to_np(buf.out), O.combine(full_y, fw["gate"], fw["row_of_pair"], w.T, w.k))
+    errs = {"out": rel_inf(to_np(buf.out), fw["out"]), "Y": rel_inf(Y, fw["Y"][r0:r0 + P])}
+    note(f"  H decisions differing {nd}; Y on own H {e_y:.2e}, out on own Y {e_out:.2e}; end to end "
+         + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert e_y <= TOL_BF16 and e_out <= TOL_BF16
+    assert max(errs.values()) <= TOL_E2E, errs
+
+
+def test_mxfp4_empty_and_rerun_bitwise():
+    w = W.scaled("bf16_fwd", precision="mxfp4", backward=False, T=0, d=256, E=8, k=2, F=256)
+    note("mxfp4 T=0")
+    buf = _layer(w, W.make_inputs(w, device="cuda"), "auto")
+    assert to_np(buf.counts).sum() == 0
+    w = W.scaled("bf16_fwd", precision="mxfp4", backward=False, T=300, d=512, E=16, k=4, F=512)
+    note("mxfp4 reruns")
+    inp = W.make_inputs(w, device="cuda")
+    for path in ("tiled", "stream"):
+        a = to_np(_layer(w, inp, path).out).copy()
+        for rep in range(3):
+            assert np.array_equal(a, to_np(_layer(w, inp, path).out)), (path, rep)
+
+
+@pytest.mark.parametrize("T", [16, 8192])
+def test_mxfp4_train_shape_sampled(T):
+    """d 4096, E 128, k 8, F 1536 in MXFP4, the default GEMM choice
+    (streaming at T 16, tiled at T 8192): sampled tokens against the oracle's
+    per-token MXFP4 forward."""
+    w = W.scaled("bf16_train", precision="mxfp4", backward=False, T=T)
+    note(f"mxfp4 train shape T={T}")
+    inp = W.make_inputs(w, device="cuda")
+    buf = _layer(w, inp, "auto")
+    out = to_np(buf.out).copy()
+    h = host_inputs(inp)
+    W1, W3, W2 = LazyExperts(inp["W1"]), LazyExperts(inp["W3"]), LazyExperts(inp["W2"])
+    toks = sorted(set(np.random.default_rng(T).choice(T, size=min(T, 3), replace=False).tolist()) | {T - 1})
+    ref = np.stack([O.forward_token(t, h["x"][t], h["logits"][t], W1, W3, W2, w.k, mxfp4=True)[2] for t in toks])
+    err = rel_inf(out[toks], ref)
+    note(f"  out sampled {err:.2e}")
+    assert err <= TOL_E2E

@@ -106,7 +106,7 @@ class Workload:
     E: int
     k: int
     F: int
-    precision: str                    # "f32" | "bf16" | "mxfp8"
+    precision: str                    # "f32" | "bf16" | "mxfp8" | "mxfp4" (forward only)
     seed: int
     expert_begin: int = 0
     expert_end: int = -1              # -1 means E
@@ -238,7 +238,7 @@ def make_inputs(w: Workload, device="cpu", weights: bool = True) -> dict:
     """All inputs of one layer call, on `device`.
 
     Returns x [T,d], logits [T,E] fp32, W1/W3 [E_loc,F,d], W2 [E_loc,d,F]
-    (bf16 for bf16/mxfp8 workloads, fp32 for f32), dout [T,d] when the workload
+    (bf16 for bf16/mxfp8/mxfp4 workloads, fp32 for f32), dout [T,d] when the workload
     has a backward pass, token_ids [T], and Wr [d,E] for tiny_fp32."""
     dt = w.act_dtype
     out = {}
