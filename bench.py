@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/s fwd+bwd (BF16, MXFP8) + grouped-GEMM % MFMA peak, 1 GPU"
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -76,10 +76,10 @@ def stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=False):
               "bwd_gate": T * d * s + 2 * P * d * s + 2 * T * E * 4 + P * 8,
               "reduce_dx": P * d * s + T * d * s + P * 4,
               "sort": T * k * 4 * 4 + P * 4}
-    # GEMM operands: bf16 (or fp32) elements, or MXFP8 codes plus one E8M0
-    # scale per 32; fp32 weight gradients.
-    mx = w.precision == "mxfp8"
-    q = 1 + 1 / 32 if mx else s
+    # GEMM operands: bf16 (or fp32) elements, or MXFP8 codes (MXFP4: half a
+    # byte) plus one E8M0 scale per 32; fp32 weight gradients.
+    mx = w.precision in ("mxfp8", "mxfp4")
+    q = (0.5 if w.precision == "mxfp4" else 1) + 1 / 32 if mx else s
     # MXFP8: the dispatch writes MXFP8 rows; UP also saves H before its
     # quantisation; the reverse-combine also writes dY in MXFP8; DH and DX read
     # MXFP8 operands, and DH writes [dA | dB] both as bf16 (for the weight
@@ -113,7 +113,7 @@ def gemm_peak(precision: str, name: str, mxfp8_wgrad: bool = False) -> float:
         if name in ("gemm_dw2", "gemm_dw13") and not mxfp8_wgrad:
             return PEAK_TFLOPS["bf16"]
         return PEAK_TFLOPS["mxfp8"]
-    return PEAK_TFLOPS[precision]
+    return PEAK_TFLOPS[precision]  # MXFP4: forward only, both products on E2M1 operands
 
 
 def roof_of(flops_n, bytes_n, ms, peak_tflops):
@@ -249,7 +249,7 @@ def measure(name: str, args, extras: bool):
 
     import workloads as W
     from mixture_experts_layer_34_amd import mok
-    from mixture_experts_layer_34_amd.layer import (MoeBuffers, MoeShape, quantize_mxfp8,
+    from mixture_experts_layer_34_amd.layer import (MoeBuffers, MoeShape, quantize_mxfp4, quantize_mxfp8,
                                                     quantize_mxfp8_backward_weights)
 
     w = W.get(name)
@@ -264,13 +264,15 @@ def measure(name: str, args, extras: bool):
                      ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0, mxfp8_wgrad=mxw)
     buf = MoeBuffers(shape, device=dev)
     W1, W3, W2, scales = inp["W1"], inp["W3"], inp["W2"], None
-    if w.precision == "mxfp8":
-        q1, s1 = quantize_mxfp8(W1)
-        q3, s3 = quantize_mxfp8(W3)
-        q2, s2 = quantize_mxfp8(W2)
+    if w.precision in ("mxfp8", "mxfp4"):
+        quant = quantize_mxfp8 if w.precision == "mxfp8" else quantize_mxfp4
+        q1, s1 = quant(W1)
+        q3, s3 = quant(W3)
+        q2, s2 = quant(W2)
         W1, W3, W2 = q1, q3, q2
         scales = torch.cat([s1.reshape(-1), s3.reshape(-1), s2.reshape(-1)])
-    wt = quantize_mxfp8_backward_weights(inp["W1"], inp["W3"], inp["W2"]) if w.precision == "mxfp8" else None
+    wt = (quantize_mxfp8_backward_weights(inp["W1"], inp["W3"], inp["W2"])
+          if w.precision == "mxfp8" and backward else None)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -456,11 +458,12 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
     dev = inp["x"].device
     n = max(K, 50)
     out = {}
-    mx_w = None
-    if w.d % 256 == 0 and w.F % 128 == 0:
-        from mixture_experts_layer_34_amd.layer import quantize_mxfp8
-        q = [quantize_mxfp8(inp[nm]) for nm in ("W1", "W3", "W2")]
-        mx_w = (q[0][0], q[1][0], q[2][0], torch.cat([sc.reshape(-1) for _, sc in q]))
+    mx_w = {}
+    if w.d % 256 == 0 and w.F % 256 == 0:
+        from mixture_experts_layer_34_amd.layer import quantize_mxfp4, quantize_mxfp8
+        for prec, quant in (("mxfp8", quantize_mxfp8), ("mxfp4", quantize_mxfp4)):
+            q = [quant(inp[nm]) for nm in ("W1", "W3", "W2")]
+            mx_w[prec] = (q[0][0], q[1][0], q[2][0], torch.cat([sc.reshape(-1) for _, sc in q]))
     for T in Ts:
         wT = W.scaled(w.name, T=T)
         small = W.make_inputs(wT, device=dev, weights=False)
@@ -527,15 +530,20 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
             del graph, buf
             row[tag] = rec
         row["speedup"] = round(row["tiled"]["us"] / row["small_path"]["us"], 3)
-        if mx_w is not None:
-            # the same calls with MXFP8 weights (inference: nothing saved)
-            for tag, tiled in (("mxfp8_small_path", False), ("mxfp8_tiled", True)):
-                buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision="mxfp8",
+        for prec, mw in mx_w.items():
+            # the same calls with MXFP8 or MXFP4 weights (inference: nothing
+            # saved); for the small path also the two GEMMs' stage times and
+            # their HBM bytes (codes of half a byte or one byte per weight,
+            # plus one scale byte per 32)
+            qb = (0.5 if prec == "mxfp4" else 1.0) + 1 / 32
+            for tag, tiled in ((f"{prec}_small_path", False), (f"{prec}_tiled", True)):
+                buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=prec,
                                           separate_route_sort=tiled, gemm_path="tiled" if tiled else "auto"),
                                  device=dev)
 
-                def fwd_mx(stream=sh):
-                    buf.forward(small["x"], small["logits"], mx_w[0], mx_w[1], mx_w[2], mx_w[3], stream=stream)
+                def fwd_mx(events=None, stream=sh):
+                    buf.cfg.stage_events = ctypes.cast(events, ctypes.c_void_p) if events is not None else None
+                    buf.forward(small["x"], small["logits"], mw[0], mw[1], mw[2], mw[3], stream=stream)
 
                 for _ in range(5):
                     fwd_mx()
@@ -545,12 +553,52 @@ def decode_latency(w, inp, K, ev, sh, Ts=(1, 16, 64, 256)):
                 for _ in range(n):
                     fwd_mx()
                 ev.record(b, sh)
-                row[tag] = {"us": round(ev.elapsed_ms(a, b) * 1e3 / n, 2)}
+                rec = {"us": round(ev.elapsed_ms(a, b) * 1e3 / n, 2)}
+                if not tiled:
+                    st = [ev.create(2 * mok.MOK_NUM_STAGES) for _ in range(n)]
+                    for i in range(n):
+                        fwd_mx(st[i])
+                    torch.cuda.synchronize()
+                    ran = ["router", "dispatch", "gemm_up", "gemm_down", "combine"] + (["sort"] if T > 32 else [])
+                    stage_us = {g: round(sum(ev.elapsed_ms(st[i][2 * mok.STAGES.index(g)],
+                                                           st[i][2 * mok.STAGES.index(g) + 1])
+                                             for i in range(n)) * 1e3 / n, 2) for g in ran}
+                    buf.cfg.stage_events = None
+                    rec["stages_us"] = stage_us
+                    counts = buf.counts.cpu()
+                    ne = int((counts > 0).sum())
+                    P = int(counts.sum())
+                    up_b = ne * 2 * w.F * w.d * qb + P * w.d * qb + P * w.F * qb
+                    dn_b = ne * w.d * w.F * qb + P * w.F * qb + P * w.d * 2
+                    rec["gemm_hbm"] = {
+                        "up": {"bytes": int(up_b), "gbs": round(up_b / (stage_us["gemm_up"] * 1e-6) / 1e9, 1),
+                               "frac": round(up_b / (stage_us["gemm_up"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)},
+                        "down": {"bytes": int(dn_b), "gbs": round(dn_b / (stage_us["gemm_down"] * 1e-6) / 1e9, 1),
+                                 "frac": round(dn_b / (stage_us["gemm_down"] * 1e-6) / (PEAK_HBM_GBS * 1e9), 4)}}
+                row[tag] = rec
                 del buf
-            row["mxfp8_speedup"] = round(row["mxfp8_tiled"]["us"] / row["mxfp8_small_path"]["us"], 3)
+            row[f"{prec}_speedup"] = round(row[f"{prec}_tiled"]["us"] / row[f"{prec}_small_path"]["us"], 3)
         out[str(T)] = row
     return {"workload": f"{w.name} weights (d={w.d} E={w.E} k={w.k} F={w.F}), forward only, T tokens per call",
             "calls": n, "per_T": out}
+
+
+def inference_legs(args):
+    """The training layer's forward alone (nothing saved, T 8192) with the
+    weights in MXFP8 and in MXFP4: throughput, stage times and the GEMMs'
+    MFMA fractions of their own peaks."""
+    import torch
+    out = {}
+    for name in ("mxfp8_infer", "mxfp4_infer"):
+        a2 = argparse.Namespace(**vars(args))
+        a2.forward_only = True
+        a2.no_cold = True
+        r, _, _, _ = measure(name, a2, extras=False)
+        out[name] = {k_: r[k_] for k_ in ("value", "unit", "ms_per_step", "dtype", "roofline", "grouped_gemm",
+                                          "stages_ms")}
+        out[name]["config"] = r["config"]["workload"]
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -577,6 +625,8 @@ def main():
                     help="with --workload mxfp8_train: MXFP8 weight gradients (MOK_FLAG_MXFP8_WGRAD)")
     ap.add_argument("--no-mxfp8-bf16-wgrad", action="store_true",
                     help="skip the comparison run of the MXFP8 step with bf16 weight gradients")
+    ap.add_argument("--no-inference", action="store_true",
+                    help="skip the forward-only MXFP8 / MXFP4 legs at the training shape")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the forward-only few-token latency leg after the bf16 training workload")
     ap.add_argument("--decode-tokens", type=lambda v: [int(x) for x in v.split(",") if x], default=[1, 16, 64, 256],
@@ -624,6 +674,8 @@ def main():
     if args.workload == "bf16_train" and not (args.no_decode or args.minibatch_rows or args.forward_only):
         result["decode_latency"] = decode_latency(w, inp, K, ev, sh, args.decode_tokens)
         torch.cuda.empty_cache()
+    if args.workload == "bf16_train" and not (args.no_inference or args.minibatch_rows or args.forward_only):
+        result["inference"] = inference_legs(args)
     if args.workload == "bf16_train" and not (args.no_mxfp8 or args.minibatch_rows or args.forward_only):
         # the MXFP8 leg of the metric: the same layer, inputs and routing with
         # MXFP8 forward GEMMs and MXFP8 dx products in the backward

@@ -80,3 +80,20 @@ def test_stage_work_mxfp8_weight_gradients():
     assert nb["regather"] == 3 * P * F * 2 + 2 * U * d * 2 + (2 * d + 3 * F) * P * q
     for n in ("gemm_dw2", "gemm_dw13"):
         assert bench.gemm_peak("mxfp8", n, True) == bench.PEAK_TFLOPS["mxfp8"]
+
+
+def test_stage_work_mxfp4_forward_bytes():
+    """MXFP4 GEMM operands move half a byte per element plus one scale byte
+    per 32; the forward saves nothing; the peak is the MXFP4 one."""
+    import workloads as W
+    w4, w8 = W.get("mxfp4_infer"), W.get("mxfp8_infer")
+    P, U, d, F, E = 65536, 8192, w4.d, w4.F, w4.E
+    f4, b4 = bench.stage_work(w4, P, U, save_for_backward=False)
+    f8, b8 = bench.stage_work(w8, P, U, save_for_backward=False)
+    q4, q8 = 0.5 + 1 / 32, 1 + 1 / 32
+    assert f4["gemm_up"] == f8["gemm_up"] == 4.0 * P * d * F
+    assert abs(b4["gemm_up"] - (P * d * q4 + 2 * E * F * d * q4 + P * F * q4)) < 1
+    assert abs(b4["gemm_down"] - (P * F * q4 + E * d * F * q4 + P * d * 2)) < 1
+    assert abs(b8["gemm_up"] - (P * d * q8 + 2 * E * F * d * q8 + P * F * q8)) < 1
+    assert abs(b4["dispatch"] - (U * d * 2 + P * d * q4)) < 1
+    assert bench.gemm_peak("mxfp4", "gemm_up") == 10100.0

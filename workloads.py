@@ -29,6 +29,8 @@ performances de 2,37x sur NVIDIA GB300 NVL72», sections 02 and 03):
               popularity; the tokens with a pair on local experts 0..3; d=7168 F=2048
   ep_mxfp8    ep_share in MXFP8
   bf16_train  T=8192 d=4096 E=128 k=8 F=1536, Zipf(1.2) popularity (expert 0 hottest)
+  mxfp8_train bf16_train in MXFP8
+  mxfp8_infer, mxfp4_infer  bf16_train's forward alone in MXFP8 / MXFP4
 """
 from __future__ import annotations
 
@@ -148,6 +150,11 @@ WORKLOADS = {
     # the same layer, inputs and routing in MXFP8 (forward and backward)
     "mxfp8_train": Workload("mxfp8_train", T=8192, d=4096, E=128, k=8, F=1536, precision="mxfp8", seed=5,
                             backward=True, notes={"zipf": 1.2}),
+    # the same layer's forward alone (inference: nothing saved) in MXFP8 and MXFP4
+    "mxfp8_infer": Workload("mxfp8_infer", T=8192, d=4096, E=128, k=8, F=1536, precision="mxfp8", seed=5,
+                            notes={"zipf": 1.2}),
+    "mxfp4_infer": Workload("mxfp4_infer", T=8192, d=4096, E=128, k=8, F=1536, precision="mxfp4", seed=5,
+                            notes={"zipf": 1.2}),
 }
 
 
