@@ -239,7 +239,7 @@ hipError_t run_stream_k(int ks, const GroupedGemmArgs& g, hipStream_t s) {
 // multiplied.  UP quantises H along F in its epilogue (one 32-column block
 // per column group: the unit's rows of H are whole MX blocks) for DOWN,
 // which writes bf16 Y.  Forward only (no saved A, B, H).
-template <int KIND, int KS, int FMT>
+template <int KIND, int KS, int FMT, int D>
 __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NB = Traits<KIND>::NB;
@@ -302,8 +302,9 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
     // per step and operand: E4M3 the lane's two 16-byte pieces, E2M1 its one
     // (the operand's upper half is not read for E2M1 and stays zero)
     constexpr int NQ = FP4 ? 1 : 2;
-    i32x4_t av[2][CS][NQ], bv[2][CS][NB][NQ];
-    int as_[2][CS], bs_[2][CS][NB];
+    constexpr int NBUF = D + 1;  // chunk c + D is in flight while c is multiplied
+    i32x4_t av[NBUF][CS][NQ], bv[NBUF][CS][NB][NQ];
+    int as_[NBUF][CS], bs_[NBUF][CS][NB];
     auto ld = [&](i32x4_t (&dst)[NQ], const uint8_t* p, int st) {
       const int64_t o = (int64_t)st * SB + 16 * h;
 #pragma unroll
@@ -341,13 +342,16 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
             acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op(av[buf][j]), op(bv[buf][j][b]), acc[b], FMT,
                                                                       FMT, 0, as_[buf][j], 0, bs_[buf][j][b]);
     };
-    load(0, 0);
-    for (int c = 0; c < nch; c += 2) {
-      if (c + 1 < nch) load(1, c + 1);
-      compute(0, c);
-      if (c + 1 < nch) {
-        if (c + 2 < nch) load(0, c + 2);
-        compute(1, c + 1);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < nch) load(i, i);
+    for (int c = 0; c < nch; c += NBUF) {
+#pragma unroll
+      for (int bb = 0; bb < NBUF; ++bb) {
+        if (c + bb < nch) {
+          if (c + bb + D < nch) load((bb + D) % NBUF, c + bb + D);
+          compute(bb, c + bb);
+        }
       }
     }
 
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256) void stream_mx_kernel(GroupedGemmArgs a) {
 #endif
 }
 
-template <int KIND, int KS, int FMT>
+template <int KIND, int KS, int FMT, int D>
 hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
   constexpr int NWN = 4 / KS;
   const int N = KIND == KIND_UP ? g.F : g.d;
@@ -427,7 +431,7 @@ hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
   const int64_t worst = ((g.P_max + kStreamTileRows - 1) / kStreamTileRows + g.E_loc) * ntn;
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_mx_kernel<KIND, KS, FMT>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stream_mx_kernel<KIND, KS, FMT, D>, 256, 0) != hipSuccess ||
         n < 1)
       n = 1;
     return n;
@@ -435,7 +439,7 @@ hipError_t run_stream_mx(const GroupedGemmArgs& g, hipStream_t s) {
   const int64_t cap = (int64_t)kNumCUs * per_cu;
   const int blocks = (int)(worst < cap ? worst : cap);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_mx_kernel<KIND, KS, FMT>), dim3(blocks), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((stream_mx_kernel<KIND, KS, FMT, D>), dim3(blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -448,21 +452,43 @@ int stream_ksplit(int K) {
   return 0;
 }
 
-// MXFP8: K split over 4 waves for UP (d / 4 bytes each), 2 for DOWN; K
-// multiple of 64 bytes per wave.
-int stream_mx_ok(int d, int F) { return d % 256 == 0 && F % 128 == 0 && F % 64 == 0; }
+// MX weight streaming: waves splitting K (UP, DOWN) and chunks in flight,
+// per operand format.
+#ifndef MOK_MX8_STREAM_KS_UP
+#define MOK_MX8_STREAM_KS_UP 4
+#endif
+#ifndef MOK_MX8_STREAM_KS_DOWN
+#define MOK_MX8_STREAM_KS_DOWN 2
+#endif
+#ifndef MOK_MX8_STREAM_DEPTH
+#define MOK_MX8_STREAM_DEPTH 1
+#endif
+#ifndef MOK_MX4_STREAM_KS_UP
+#define MOK_MX4_STREAM_KS_UP 4
+#endif
+#ifndef MOK_MX4_STREAM_KS_DOWN
+#define MOK_MX4_STREAM_KS_DOWN 2
+#endif
+#ifndef MOK_MX4_STREAM_DEPTH
+#define MOK_MX4_STREAM_DEPTH 1
+#endif
+constexpr int kMaxKsUp = MOK_MX8_STREAM_KS_UP > MOK_MX4_STREAM_KS_UP ? MOK_MX8_STREAM_KS_UP : MOK_MX4_STREAM_KS_UP;
+constexpr int kMaxKsDown =
+    MOK_MX8_STREAM_KS_DOWN > MOK_MX4_STREAM_KS_DOWN ? MOK_MX8_STREAM_KS_DOWN : MOK_MX4_STREAM_KS_DOWN;
+
+// Each wave's K range is a whole number of 64-value steps (E4M3 64 bytes,
+// E2M1 32): d a multiple of 64 times UP's split, F of 64 times DOWN's.
+int stream_mx_ok(int d, int F) { return d % (64 * kMaxKsUp) == 0 && F % (64 * kMaxKsDown) == 0; }
 
 hipError_t gemm_stream_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s) {
-  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4, 0>(g, s);
-  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2, 0>(g, s);
+  if (kind == KIND_UP) return run_stream_mx<KIND_UP, MOK_MX8_STREAM_KS_UP, 0, MOK_MX8_STREAM_DEPTH>(g, s);
+  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, MOK_MX8_STREAM_KS_DOWN, 0, MOK_MX8_STREAM_DEPTH>(g, s);
   return hipErrorInvalidValue;
 }
 
-// MXFP4: the same split (UP d / 8 bytes per wave, DOWN F / 4), a multiple of
-// the 32-byte K step when d % 256 == 0 and F % 128 == 0.
 hipError_t gemm_stream_mxfp4(int kind, const GroupedGemmArgs& g, hipStream_t s) {
-  if (kind == KIND_UP) return run_stream_mx<KIND_UP, 4, 4>(g, s);
-  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, 2, 4>(g, s);
+  if (kind == KIND_UP) return run_stream_mx<KIND_UP, MOK_MX4_STREAM_KS_UP, 4, MOK_MX4_STREAM_DEPTH>(g, s);
+  if (kind == KIND_DOWN) return run_stream_mx<KIND_DOWN, MOK_MX4_STREAM_KS_DOWN, 4, MOK_MX4_STREAM_DEPTH>(g, s);
   return hipErrorInvalidValue;
 }
 
