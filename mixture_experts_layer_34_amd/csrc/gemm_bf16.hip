@@ -69,8 +69,15 @@
 #ifndef MOK_ROW_NT_A
 #define MOK_ROW_NT_A 0
 #endif
-#ifndef MOK_DW_NT_STORE
-#define MOK_DW_NT_STORE 0  // non-temporal fp32 weight-gradient stores
+// Non-temporal fp32 weight-gradient stores, per kind (same-box A/B at T 8192,
+// d 4096, E 128, k 8, F 1536, three alternating rounds: dW1/dW3 2.73-2.74 ->
+// 2.67-2.71 ms with the hint, training step 10.58-10.65 -> 10.53-10.63 ms;
+// dW2 1.42 -> 1.47-1.49 ms with it, so dW2 keeps the default policy).
+#ifndef MOK_DW2_NT_STORE
+#define MOK_DW2_NT_STORE 0
+#endif
+#ifndef MOK_DW13_NT_STORE
+#define MOK_DW13_NT_STORE 1
 #endif
 #ifndef MOK_ROW_NT_B
 #define MOK_ROW_NT_B 0
@@ -466,7 +473,8 @@ struct TileJob {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float* q = lp + (int64_t)(i * 32 + (r >> 2) * 8 + (r & 3)) * G.N + j * 32;
-            if constexpr (MOK_DW_NT_STORE) __builtin_nontemporal_store(acc[0][i][j][r], q);
+            if constexpr (KIND == KIND_DW13 ? MOK_DW13_NT_STORE : MOK_DW2_NT_STORE)
+              __builtin_nontemporal_store(acc[0][i][j][r], q);
             else *q = acc[0][i][j][r];
           }
         }
