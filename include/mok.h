@@ -488,6 +488,31 @@ mok_status mok_router_logits(const void* x, const void* Wr, int32_t T, int32_t d
 mok_status mok_router_logits_backward(const void* x, const void* Wr, const float* dlogits, int32_t T,
                                       int32_t d, int32_t E, float* dx, float* dWr, void* stream);
 
+/*
+ * Forward pass with the router GEMM in front: x . Wr^T -> softmax / top-k ->
+ * the layer ([kucoin §01]: the router scores every token against every
+ * expert and picks its experts; the router GEMM fused into the router step,
+ * so the [T, E] logits are not read back).  Equivalent, bit for bit in every
+ * output, to mok_router_logits(x, Wr, ..., router_logits) followed by
+ * mok_moe_forward(x, router_logits, ...).
+ *   Wr             bf16  [E, d]   router vectors, one row per expert
+ *   router_logits  float [T, E]   output (the backward reads them)
+ *   all other arguments as mok_moe_forward
+ * For E <= 128 one kernel computes a tile of 32 tokens' logits, writes them,
+ * and routes those tokens from the copy it holds in LDS; for E > 128 the
+ * router GEMM and the router step are two launches; calls of at most 32
+ * tokens run the router GEMM and then the one-launch router and sort.
+ * Constraints: those of mok_moe_forward and of mok_router_logits (d <= 65536);
+ * bf16 activations (MOK_PREC_BF16, MOK_PREC_MXFP8, MOK_PREC_MXFP4).
+ * Errors: MOK_ERR_INVALID_ARG for MOK_PREC_F32, a null or misaligned Wr or
+ * router_logits, or any error of mok_moe_forward.
+ */
+mok_status mok_moe_forward_router(const void* x, const void* Wr, const void* W1, const void* W3, const void* W2,
+                                  int32_t k, const mok_moe_config* cfg, const uint8_t* w_scales,
+                                  float* router_logits, void* out, int32_t* topk_idx, float* topk_gate,
+                                  int32_t* expert_counts, int32_t* expert_offsets, void* saved, void* workspace,
+                                  void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* mok_status_string(mok_status s);
 

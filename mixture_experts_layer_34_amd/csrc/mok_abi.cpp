@@ -247,12 +247,14 @@ static int gating_of(const mok_moe_config& c) {
   } while (0)
 
 // The forward launch sequence, arguments already checked, with the workspace
-// at `workspace` laid out as `wl`.
+// at `workspace` laid out as `wl`.  With Wr, the router logits are first
+// computed from x and Wr into router_logits (the router GEMM; for E <= 128
+// fused with the router step).
 mok_status forward_checked(const void* x, const float* router_logits, const void* W1, const void* W3,
                            const void* W2, int32_t k, const mok_moe_config& c, const uint8_t* w_scales,
                            void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
                            int32_t* expert_offsets, void* saved, void* workspace, const WorkspaceLayout& wl,
-                           void* stream) {
+                           void* stream, const void* Wr = nullptr) {
   const bool mx4 = c.precision == MOK_PREC_MXFP4;
   const bool mx = c.precision == MOK_PREC_MXFP8 || mx4;
   hipStream_t s = (hipStream_t)stream;
@@ -273,15 +275,25 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
 
   int32_t* status = at<int32_t>(workspace, wl.status);
   const int64_t P_max = (int64_t)T * k;
+  float* logits_out = const_cast<float*>(router_logits);  // written only when Wr is given
   if (T >= 1 && T <= kSmallTokens && P_max <= kSmallPairs && !(c.flags & MOK_FLAG_SEPARATE_ROUTE_SORT)) {
     // small call: status reset, router and counting sort in one workgroup
-    MOK_STAGE(MOK_STAGE_ROUTER, launch_route_sort_small(router_logits, T, E, k, gating_of(c), eb, c.expert_end,
-                                                        topk_idx, topk_gate, s_idx, s_gate, s_lse, expert_counts,
-                                                        expert_offsets, s_off, s_tp, s_order, s_rop, s_por, status, s));
+    StageMark mark(c, s, MOK_STAGE_ROUTER);
+    if (Wr) MOK_HIP(launch_router_logits(x, Wr, T, d, E, logits_out, s));
+    MOK_HIP(launch_route_sort_small(router_logits, T, E, k, gating_of(c), eb, c.expert_end, topk_idx, topk_gate,
+                                    s_idx, s_gate, s_lse, expert_counts, expert_offsets, s_off, s_tp, s_order, s_rop,
+                                    s_por, status, s));
   } else {
     MOK_HIP(launch_status_reset(status, s));
-    MOK_STAGE(MOK_STAGE_ROUTER, launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx,
-                                                   s_gate, s_lse, status, s));
+    if (Wr && E <= kRouterFusedMaxE) {
+      MOK_STAGE(MOK_STAGE_ROUTER, launch_router_fused(x, Wr, T, d, E, k, gating_of(c), logits_out, topk_idx,
+                                                      topk_gate, s_idx, s_gate, s_lse, status, s));
+    } else {
+      StageMark mark(c, s, MOK_STAGE_ROUTER);
+      if (Wr) MOK_HIP(launch_router_logits(x, Wr, T, d, E, logits_out, s));
+      MOK_HIP(launch_router_topk(router_logits, T, E, k, gating_of(c), topk_idx, topk_gate, s_idx, s_gate, s_lse,
+                                 status, s));
+    }
     MOK_STAGE(MOK_STAGE_SORT, launch_counting_sort(s_idx, T, k, E, eb, c.expert_end, wl.nchunks,
                                                    at<int32_t>(workspace, wl.chunk_counts),
                                                    at<int32_t>(workspace, wl.chunk_base), expert_counts,
@@ -861,6 +873,30 @@ mok_status mok_router_logits(const void* x, const void* Wr, int32_t T, int32_t d
   if (!logits) return MOK_ERR_INVALID_ARG;
   MOK_HIP(launch_router_logits(x, Wr, T, d, E, logits, (hipStream_t)stream));
   return MOK_OK;
+}
+
+mok_status mok_moe_forward_router(const void* x, const void* Wr, const void* W1, const void* W3, const void* W2,
+                                  int32_t k, const mok_moe_config* cfg, const uint8_t* w_scales, float* router_logits,
+                                  void* out, int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                                  int32_t* expert_offsets, void* saved, void* workspace, void* stream) {
+  mok_status st = validate_config(cfg, k);
+  if (st != MOK_OK) return st;
+  const mok_moe_config& c = *cfg;
+  if (c.precision == MOK_PREC_F32) return MOK_ERR_INVALID_ARG;  // the router GEMM takes bf16 x
+  st = validate_router(x, Wr, c.T, c.d, c.E);
+  if (st != MOK_OK) return st;
+  const void* always[] = {W1, W3, W2, expert_counts, expert_offsets, saved, workspace};
+  const void* per_token[] = {x, router_logits, out, topk_idx, topk_gate};
+  for (const void* p : always)
+    if (!p || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  for (const void* p : per_token)
+    if ((c.T > 0 && !p) || !aligned16(p)) return MOK_ERR_INVALID_ARG;
+  const bool mx = c.precision == MOK_PREC_MXFP8 || c.precision == MOK_PREC_MXFP4;
+  if (mx != (w_scales != nullptr)) return MOK_ERR_INVALID_ARG;
+  WorkspaceLayout wl;
+  workspace_layout(c, k, &wl);
+  return forward_checked(x, router_logits, W1, W3, W2, k, c, w_scales, out, topk_idx, topk_gate, expert_counts,
+                         expert_offsets, saved, workspace, wl, stream, Wr);
 }
 
 mok_status mok_router_logits_backward(const void* x, const void* Wr, const float* dlogits, int32_t T, int32_t d,

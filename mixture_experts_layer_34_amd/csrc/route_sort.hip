@@ -13,101 +13,12 @@
 // pair id p = t*k + j.  Both are integer-exact and run-to-run identical.
 #include "mok_device.h"
 #include "mok_internal.h"
+#include "route_token.h"
 
 namespace mok {
 
 // ------------------------------------------------------------------ router
-// One wave per token; lane l holds logits e = l + 64 i.  k rounds of a wave
-// arg-max under the (value desc, index asc) order.  Gates: the softmax
-// probability of the chosen expert, or its sigmoid (SIGM); with RENORM each
-// is divided by their sum over the k chosen experts (slot order, fp32).
-constexpr int kRouterMaxK = 1024;  // k <= E <= 1024
-// One token's routing by one wave: top-k of the raw logits, gates, lse.
-// graw: this wave's k floats of LDS (renormalised gates only).
-template <int EPL, bool SIGM, bool RENORM>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-                                            int32_t* __restrict__ idx_saved, float* __restrict__ gate_saved,
-                                            float* __restrict__ lse_out, int32_t* __restrict__ status,
-                                            float* graw) {
-  const int lane = lane_id();
-  const float* row = logits + (int64_t)t * E;
-  float v[EPL];
-  float m = -INFINITY;
-  bool bad = false;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
-    // logits must be finite: a NaN or an infinity is reported, and a NaN
-    // is ranked as -inf so that the k chosen indices stay in [0, E)
-    if (e < E && !isfinite(v[i])) {
-      bad = true;
-      if (v[i] != v[i]) v[i] = -INFINITY;
-    }
-    m = fmaxf(m, v[i]);
-  }
-  if (__ballot(bad) != 0 && lane == 0) report(status, kCheckLogits);
-  m = wave_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    int e = lane + 64 * i;
-    if (e < E) s += expf(v[i] - m);
-  }
-  s = wave_sum(s);
-  const float inv_s = 1.0f / s;
-  // Selection key of each candidate: the logit mapped to an order-preserving
-  // unsigned code (with -0 taken as +0, so that equal values tie) in the high
-  // word, 2^32 - 1 - e in the low word: the largest key is the largest
-  // value, lowest index first.  A chosen or absent candidate has key 0, below
-  // every real key (-inf maps to 0x007fffff).
-  uint64_t key[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    uint32_t u = __float_as_uint(v[i]);
-    if ((u << 1) == 0) u = 0;
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    key[i] = e < E ? ((uint64_t)ord << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
-  }
-  float gsum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int be = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const uint32_t ord = (uint32_t)(best >> 32);
-    const float bv = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i == be) key[i] = 0ull;
-    if (lane == 0) {
-      const float g = SIGM ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) * inv_s;
-      idx_out[(int64_t)t * k + j] = be;
-      idx_saved[(int64_t)t * k + j] = be;
-      if constexpr (RENORM) {
-        graw[j] = g;
-        gsum += g;
-      } else {
-        gate_out[(int64_t)t * k + j] = g;
-        gate_saved[(int64_t)t * k + j] = g;
-      }
-    }
-  }
-  if (lane == 0) {
-    lse_out[t] = m + logf(s);
-    if constexpr (RENORM) {
-      for (int j = 0; j < k; ++j) {
-        const float g = graw[j] / gsum;
-        gate_out[(int64_t)t * k + j] = g;
-        gate_saved[(int64_t)t * k + j] = g;
-      }
-    }
-  }
-}
-
+// One wave per token (route_token.h), grid-stride over the tokens.
 template <int EPL, bool SIGM, bool RENORM>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int32_t* __restrict__ idx_out,
@@ -121,7 +32,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
   float* graw = RENORM ? renorm_buf + (threadIdx.x >> 6) * kRouterMaxK : renorm_buf;  // this wave's raw gates
   for (int t = wave; t < T; t += nwaves)
-    route_token<EPL, SIGM, RENORM>(logits, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out, status, graw);
+    route_token<EPL, SIGM, RENORM>(logits + (int64_t)t * E, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out,
+                                   status, graw);
 }
 
 template <bool SIGM, bool RENORM>
@@ -455,7 +367,8 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
   static_assert(kRouterMaxK <= 1024, "a wave's raw gates fit its row of s_wcnt");
   float* graw = reinterpret_cast<float*>(&s_wcnt[w][0]);
   for (int t = w; t < T; t += 16)
-    route_token<EPL, SIGM, RENORM>(logits, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out, status, graw);
+    route_token<EPL, SIGM, RENORM>(logits + (int64_t)t * E, t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse_out,
+                                   status, graw);
   if (tid < E) s_hist[tid] = 0;
   __syncthreads();  // the block's index writes are visible to the block
   const int npairs = T * k;

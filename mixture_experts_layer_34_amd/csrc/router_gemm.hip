@@ -24,6 +24,8 @@
 
 #include "gemm_pipe.h"
 #include "mok_device.h"
+#include "mok_internal.h"
+#include "route_token.h"
 #include "router_gemm.h"
 
 namespace mok {
@@ -149,19 +151,15 @@ constexpr int kFwdStage = kFwdA + kFwdBN * kFwdBK * 2;
 constexpr int kFwdCopies = kFwdStage / 1024 / 4;  // 16-byte copies per lane per stage
 static_assert(kFwdA == 4 * 1024 && kFwdCopies == 5, "one A copy and four B copies per wave");
 
-// Grid: 8 * ceil(nT / 8) * nE workgroups.  Workgroup b runs on XCD b % 8;
-// the nE expert tiles of a token tile take consecutive slots of one XCD.
-__global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x,
-                                                            const bf16_t* __restrict__ Wr, int T, int d, int E,
-                                                            int nT, int nE, float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kFwdNS * kFwdStage];
-  const int b = blockIdx.x;
-  const int slot = b >> 3;
-  const int tt = (slot / nE) * 8 + (b & 7), et = slot % nE;
-  if (tt >= nT) return;
+// One 32-token x 128-expert tile of the logits (tokens m0.., experts e0..):
+// wave w returns experts e0 + 32 w .. as a 32 x 32 MFMA accumulator (lane l:
+// expert column l % 32, token rows (r / 4) 8 + 4 (l / 32) + r % 4).  The K
+// loop is fed by direct-to-LDS copies, kFwdNS stages deep; on return every
+// copy has landed and every wave has passed the barrier after its last read
+// of the arena.
+__device__ __forceinline__ f32x16_t logits_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr, int d,
+                                                int m0, int e0, int mrows, int erows, uint8_t* arena) {
   const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = tt * kFwdBM, e0 = et * kFwdBN;
-  const int mrows = min(kFwdBM, T - m0), erows = min(kFwdBN, E - e0);
   // rows past the token / expert count read as zero
   const i32x4_t rsA = make_rsrc(x + (int64_t)m0 * d, (uint32_t)(mrows * d * 2));
   const i32x4_t rsB = make_rsrc(Wr + (int64_t)e0 * d, (uint32_t)(erows * d * 2));
@@ -205,7 +203,65 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __rest
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) acc = mfma(fa[kk], fb[kk], acc);
   }
+  return acc;
+}
+
+// Grid: 8 * ceil(nT / 8) * nE workgroups.  Workgroup b runs on XCD b % 8;
+// the nE expert tiles of a token tile take consecutive slots of one XCD.
+__global__ __launch_bounds__(256) void router_logits_kernel(const bf16_t* __restrict__ x,
+                                                            const bf16_t* __restrict__ Wr, int T, int d, int E,
+                                                            int nT, int nE, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kFwdNS * kFwdStage];
+  const int b = blockIdx.x;
+  const int slot = b >> 3;
+  const int tt = (slot / nE) * 8 + (b & 7), et = slot % nE;
+  if (tt >= nT) return;
+  const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = tt * kFwdBM, e0 = et * kFwdBN;
+  const int mrows = min(kFwdBM, T - m0), erows = min(kFwdBN, E - e0);
+  const f32x16_t acc = logits_tile(x, Wr, d, m0, e0, mrows, erows, arena);
   store_tile(logits + (int64_t)m0 * E + e0, E, acc, 0, wid * 32, mrows, erows, lane);
+}
+
+// The router GEMM with the router step fused behind it, for E <= 128 (one
+// expert tile holds every logit of its 32 tokens): the tile's logits go to
+// `logits` (for the backward) and to LDS, where each wave routes every
+// fourth token of the tile (route_token: the same top-k, gates and lse as
+// the router kernel on those logits, bit for bit).  Grid: 8 * ceil(nT / 8).
+template <int EPL, bool SIGM, bool RENORM>
+__global__ __launch_bounds__(256) void router_fused_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ Wr,
+                                                           int T, int d, int E, int k, int nT,
+                                                           float* __restrict__ logits, int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ gate_out,
+                                                           int32_t* __restrict__ idx_saved,
+                                                           float* __restrict__ gate_saved, float* __restrict__ lse,
+                                                           int32_t* __restrict__ status) {
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kFwdNS * kFwdStage];
+  static_assert(kFwdBM * kFwdBN * 4 + 4 * kRouterMaxK * 4 <= kFwdNS * kFwdStage, "logits and gates fit the arena");
+  const int b = blockIdx.x;
+  const int tt = (b >> 3) * 8 + (b & 7);
+  if (tt >= nT) return;
+  const int lane = lane_id(), wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = tt * kFwdBM;
+  const int mrows = min(kFwdBM, T - m0);
+  const f32x16_t acc = logits_tile(x, Wr, d, m0, 0, mrows, E, arena);
+  store_tile(logits + (int64_t)m0 * E, E, acc, 0, wid * 32, mrows, E, lane);
+  lds_barrier();
+  float* lg = reinterpret_cast<float*>(arena);  // [mrows][E]
+  {
+    const int c = wid * 32 + (lane & 31);
+    if (c < E)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row < mrows) lg[row * E + c] = acc[r];
+      }
+  }
+  __syncthreads();
+  float* graw = lg + kFwdBM * kFwdBN + (RENORM ? wid * kRouterMaxK : 0);  // this wave's raw gates
+  for (int t = wid; t < mrows; t += 4)
+    route_token<EPL, SIGM, RENORM>(lg + t * E, m0 + t, E, k, idx_out, gate_out, idx_saved, gate_saved, lse, status,
+                                   graw);
 }
 
 // Both backward kernels stream K in chunks of 32 through one LDS buffer,
@@ -364,6 +420,29 @@ hipError_t launch_router_logits(const void* x, const void* Wr, int T, int d, int
   const int grid = 8 * cdiv(nT, 8) * nE;
   hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)Wr, T, d,
                      E, nT, nE, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_fused(const void* x, const void* Wr, int T, int d, int E, int k, int gating, float* logits,
+                               int32_t* idx_out, float* gate_out, int32_t* idx_saved, float* gate_saved, float* lse,
+                               int32_t* status, hipStream_t s) {
+  if (E > kFwdBN || E < 1 || k < 1 || k > E) return hipErrorInvalidValue;
+  const int nT = cdiv(T, kFwdBM);
+  if (nT == 0) return hipSuccess;
+  const dim3 g(8 * cdiv(nT, 8)), blk(256);
+  const bool sg = gating & kGateSigmoid, rn = gating & kGateRenorm;
+#define MOK_FUSED(EPLV, SG, RN)                                                                                      \
+  hipLaunchKernelGGL((router_fused_kernel<EPLV, SG, RN>), g, blk, 0, s, (const bf16_t*)x, (const bf16_t*)Wr, T, d, E, k, \
+                     nT, logits, idx_out, gate_out, idx_saved, gate_saved, lse, status)
+#define MOK_FUSED_E(SG, RN)        \
+  if (E <= 64) MOK_FUSED(1, SG, RN); \
+  else MOK_FUSED(2, SG, RN);
+  if (!sg && !rn) { MOK_FUSED_E(false, false) }
+  else if (sg && !rn) { MOK_FUSED_E(true, false) }
+  else if (!sg && rn) { MOK_FUSED_E(false, true) }
+  else { MOK_FUSED_E(true, true) }
+#undef MOK_FUSED_E
+#undef MOK_FUSED
   return hipGetLastError();
 }
 

@@ -123,6 +123,22 @@ class MoeBuffers:
                             _stream() if stream is None else stream)
         return self.out
 
+    def forward_router(self, x, Wr, W1, W3, W2, w_scales=None, logits=None, stream=None):
+        """The forward with the router GEMM in front: logits = x . Wr^T are
+        computed (into `logits`, or a buffer of this object) and routed in
+        the same call; returns out.  The logits are kept in self.logits for
+        the backward."""
+        s = self.shape
+        if logits is None:
+            logits = getattr(self, "logits", None)
+            if logits is None or tuple(logits.shape) != (s.T, s.E):
+                logits = torch.empty((s.T, s.E), dtype=torch.float32, device=self.out.device)
+        self.logits = logits
+        mok.mok_moe_forward_router(x, Wr, W1, W3, W2, s.k, self.cfg, w_scales, logits, self.out, self.topk_idx,
+                                   self.topk_gate, self.counts, self.offsets, self.saved, self.workspace,
+                                   _stream() if stream is None else stream)
+        return self.out
+
     def backward(self, dout, x, logits, W1, W3, W2, stream=None):
         g = self.grads or self.alloc_grads()
         mok.mok_moe_backward(dout, x, logits, W1, W3, W2, self.shape.k, self.cfg, self.saved, g["dx"], g["dW1"],

@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.mok_moe_forward.restype = ctypes.c_int
         L.mok_moe_forward.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P]
+        L.mok_moe_forward_router.restype = ctypes.c_int
+        L.mok_moe_forward_router.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.mok_moe_forward_noalloc.restype = ctypes.c_int
         L.mok_moe_forward_noalloc.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.POINTER(mok_moe_config), _P,
                                               _P, _P, _P, _P, _P, _P]
@@ -163,6 +166,14 @@ def mok_moe_forward(x, router_logits, W1, W3, W2, k, cfg, w_scales, out, topk_id
                                  _ptr(w_scales), _ptr(out), _ptr(topk_idx), _ptr(topk_gate), _ptr(expert_counts),
                                  _ptr(expert_offsets), _ptr(saved), _ptr(workspace), stream or None),
            "mok_moe_forward")
+
+
+def mok_moe_forward_router(x, Wr, W1, W3, W2, k, cfg, w_scales, router_logits, out, topk_idx, topk_gate,
+                           expert_counts, expert_offsets, saved, workspace, stream=0):
+    _check(lib().mok_moe_forward_router(_ptr(x), _ptr(Wr), _ptr(W1), _ptr(W3), _ptr(W2), k, ctypes.byref(cfg),
+                                        _ptr(w_scales), _ptr(router_logits), _ptr(out), _ptr(topk_idx),
+                                        _ptr(topk_gate), _ptr(expert_counts), _ptr(expert_offsets), _ptr(saved),
+                                        _ptr(workspace), stream or None), "mok_moe_forward_router")
 
 
 def mok_moe_forward_noalloc(x, router_logits, W1, W3, W2, k, cfg, out, topk_idx, topk_gate, expert_counts,

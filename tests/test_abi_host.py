@@ -257,3 +257,23 @@ def test_quantize_mxfp4_rejects_bad_shapes():
     assert L.mok_quantize_mxfp4(None, 4, 64, 0x2000, 0x3000, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_quantize_mxfp4(0x1000, 4, 64, 0x2008, 0x3000, None) == mok.MOK_ERR_INVALID_ARG  # misaligned
     assert L.mok_quantize_mxfp4(0x1000, 0, 64, 0x2000, 0x3000, None) == mok.MOK_OK
+
+
+def test_forward_router_error_paths_before_launch():
+    L = mok.lib()
+
+    def call(cfg, k=2, **over):
+        p = dict(x=0x10000, Wr=0xF0000, W1=0x30000, W3=0x40000, W2=0x50000, scales=None, logits=0x20000,
+                 out=0x60000, idx=0x70000, gate=0x80000, counts=0x90000, offsets=0xA0000, saved=0xB0000,
+                 ws=0xC0000)
+        p.update(over)
+        return L.mok_moe_forward_router(p["x"], p["Wr"], p["W1"], p["W3"], p["W2"], k, ctypes.byref(cfg), p["scales"],
+                                        p["logits"], p["out"], p["idx"], p["gate"], p["counts"], p["offsets"],
+                                        p["saved"], p["ws"], None)
+    assert call(_cfg(precision="f32", d=128)) == mok.MOK_ERR_INVALID_ARG     # the router GEMM takes bf16 x
+    assert call(_cfg(), Wr=None) == mok.MOK_ERR_INVALID_ARG
+    assert call(_cfg(), Wr=0xF0008) == mok.MOK_ERR_INVALID_ARG               # misaligned
+    assert call(_cfg(), logits=None) == mok.MOK_ERR_INVALID_ARG
+    assert call(_cfg(precision="mxfp8")) == mok.MOK_ERR_INVALID_ARG          # MXFP8 needs scales
+    assert call(_cfg(), scales=0xD0000) == mok.MOK_ERR_INVALID_ARG           # scales outside MX
+    assert call(_cfg(), k=0) == mok.MOK_ERR_INVALID_ARG
