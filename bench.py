@@ -240,6 +240,46 @@ def router_gemm_bench(w, x, K, Wm, ev, sh):
     return out
 
 
+def fused_router_bench(w, inp, K, Wm, ev, sh):
+    """The layer's forward (nothing saved) with the router GEMM in front, at
+    this workload's shape: mok_router_logits followed by mok_moe_forward,
+    against mok_moe_forward_router (for E <= 128 the GEMM and the router
+    step in one kernel).  Milliseconds per call, eager launches."""
+    import torch
+
+    import workloads as W
+    from mixture_experts_layer_34_amd.layer import MoeBuffers, MoeShape, router_logits
+
+    x = inp["x"]
+    T, d = x.shape
+    Wr = W.make_router_inputs(w.seed, 1, w.d, w.E, device=x.device)["Wr"]
+    buf = MoeBuffers(MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision), device=x.device)
+    logits = torch.empty((T, w.E), dtype=torch.float32, device=x.device)
+
+    def separate():
+        router_logits(x, Wr, out=logits)
+        buf.forward(x, logits, inp["W1"], inp["W3"], inp["W2"], stream=sh)
+
+    def fused():
+        buf.forward_router(x, Wr, inp["W1"], inp["W3"], inp["W2"], logits=logits, stream=sh)
+
+    out = {"shape": f"T={T} d={w.d} E={w.E} k={w.k} F={w.F}, {w.precision}, forward only"}
+    for name, fn in (("router_gemm_then_forward", separate), ("forward_router", fused)):
+        for _ in range(Wm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev.create(2)
+        ev.record(a, sh)
+        for _ in range(K):
+            fn()
+        ev.record(b, sh)
+        out[name] = {"ms": round(ev.elapsed_ms(a, b) / K, 4)}
+    out["saved_ms"] = round(out["router_gemm_then_forward"]["ms"] - out["forward_router"]["ms"], 4)
+    del buf
+    torch.cuda.synchronize()
+    return out
+
+
 def measure(name: str, args, extras: bool):
     """Times `steps` layer steps of one workload (after `warmup` untimed
     ones); `extras` adds the copy calibration and the graph-replay timing.
@@ -648,6 +688,8 @@ def main():
     result, w, inp, (K, Wm, ev, sh) = measure(args.workload, args, extras=True)
     if inp["x"].dtype == torch.bfloat16 and not args.minibatch_rows:
         result["router_gemm"] = router_gemm_bench(w, inp["x"], K, Wm, ev, sh)
+        if w.precision == "bf16":
+            result["router_gemm"]["fused_into_layer"] = fused_router_bench(w, inp, K, Wm, ev, sh)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_sample_tokens)
     else:
