@@ -142,6 +142,8 @@ def _decision_points_only(h, dev_codes, dev_scales):
 
 
 CASES = [
+    ("many-experts", dict(T=64, d=256, E=1024, k=8, F=256)),      # most of 1024 experts empty
+    ("max-stream-pairs", dict(T=512, d=256, E=64, k=8, F=256)),  # 4096 pairs: the largest streaming call
     ("small", dict(T=200, d=512, E=16, k=4, F=768)),
     ("ragged", dict(T=333, d=256, E=6, k=2, F=512)),
     ("local", dict(T=256, d=512, E=32, k=4, F=256, expert_begin=8, expert_end=20)),
@@ -248,3 +250,13 @@ def test_mxfp4_ep_share_sampled():
     err = rel_inf(out[toks], ref)
     note(f"  out sampled {err:.2e}")
     assert err <= TOL_E2E
+
+
+def test_mxfp4_stream_not_used_past_its_range():
+    """4097 pairs: the tiled kernels run even when streaming is asked for,
+    so the flag changes nothing, bit for bit."""
+    w = W.scaled("bf16_fwd", precision="mxfp4", backward=False, T=513, d=256, E=64, k=8, F=256)
+    note("mxfp4 stream range")
+    inp = W.make_inputs(w, device="cuda")
+    a = to_np(_layer(w, inp, "stream").out).copy()
+    assert np.array_equal(a, to_np(_layer(w, inp, "tiled").out))

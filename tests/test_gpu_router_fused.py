@@ -80,6 +80,8 @@ CASES = [
     ("fused-E5", 77, 128, 5, 2, 128, {}),
     ("fused-E1", 40, 64, 1, 1, 64, {}),
     ("two-launch-E256", 200, 256, 256, 8, 256, {}),
+    ("two-launch-E1024", 1000, 128, 1024, 8, 128, {}),
+    ("two-launch-E129", 64, 128, 129, 4, 128, {}),
     ("small-T", 5, 256, 128, 8, 256, {}),
     ("local", 256, 256, 64, 4, 256, dict(eb=8, ee=20)),
     ("sigmoid-renorm", 150, 256, 96, 6, 256, dict(gating="sigmoid", renorm=True)),
