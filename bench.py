@@ -301,7 +301,8 @@ def measure(name: str, args, extras: bool):
     mxw = w.precision == "mxfp8" and backward and getattr(args, "mxfp8_wgrad", False)
     shape = MoeShape(T=T, d=w.d, E=w.E, k=w.k, F=w.F, precision=w.precision, expert_begin=w.expert_begin,
                      expert_end=w.e_end, save_for_backward=backward, minibatch_rows=args.minibatch_rows,
-                     ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0, mxfp8_wgrad=mxw)
+                     ring_bytes=(args.ring_mib << 20) if args.minibatch_rows else 0, mxfp8_wgrad=mxw,
+                     mover_cus=getattr(args, "mover_cus", 0) if args.minibatch_rows else 0)
     buf = MoeBuffers(shape, device=dev)
     W1, W3, W2, scales = inp["W1"], inp["W3"], inp["W2"], None
     if w.precision in ("mxfp8", "mxfp4"):
@@ -461,6 +462,7 @@ def measure(name: str, args, extras: bool):
                                f"local experts [{w.expert_begin},{w.e_end}) pairs P={P}, "
                                f"{'forward+backward' if backward else 'forward'}"
                                + (f", ring pipeline R={args.minibatch_rows} rows, {args.ring_mib} MiB ring"
+                                  + (f", {args.mover_cus} copy-only CUs" if getattr(args, "mover_cus", 0) else "")
                                   if args.minibatch_rows else ""),
                    "global_batch": T, "parallelism": "none (1 GPU)",
                    "launch": "the whole step replayed from a HIP graph" if use_graph
@@ -653,6 +655,10 @@ def main():
     ap.add_argument("--minibatch-rows", type=int, default=0,
                     help="ring pipeline minibatch rows R (0 = whole layer at once)")
     ap.add_argument("--ring-mib", type=int, default=256, help="ring buffer size with --minibatch-rows")
+    ap.add_argument("--mover-cus", type=int, default=0,
+                    help="with --minibatch-rows: workgroups that only copy rows (0 = one shared task queue)")
+    ap.add_argument("--mover-sweep", type=lambda v: [int(x) for x in v.split(",") if x], default=[16, 32],
+                    help="mover_cus values timed at R = 1024 in the ring sweep (comma list; empty: none)")
     ap.add_argument("--ring-sweep", type=lambda v: [int(x) for x in v.split(",") if x], default=[512, 1024, 2048],
                     help="minibatch sizes R of the ring-pipeline sweep after the headline (comma list; empty: none)")
     ap.add_argument("--no-graph", action="store_true",
@@ -709,7 +715,19 @@ def main():
                              "forward_pipeline_ms": rr["stages_ms"].get("gemm_up"),
                              "launch": rr["config"]["launch"]}
             torch.cuda.empty_cache()
+        split = {}
+        if 1024 in args.ring_sweep:
+            # an explicit split of the compute units between copying and the
+            # tiles, against the shared queue (mover_cus = 0) at the same R
+            for mc in args.mover_sweep:
+                a2 = argparse.Namespace(**vars(args))
+                a2.minibatch_rows, a2.mover_cus, a2.no_cold = 1024, mc, True
+                rr, _, _, _ = measure("bf16_train", a2, extras=False)
+                split[str(mc)] = {"ms_per_step": rr["ms_per_step"],
+                                  "forward_pipeline_ms": rr["stages_ms"].get("gemm_up")}
+                torch.cuda.empty_cache()
         result["ring_sweep"] = {"ring_mib": args.ring_mib, "per_R": sweep,
+                                "mover_split_R1024": split,
                                 "whole_layer_forward_ms": round(sum(result["stages_ms"].get(n, 0.0) for n in
                                                                     ("dispatch", "gemm_up", "gemm_down",
                                                                      "combine")), 4)}

@@ -145,21 +145,25 @@ typedef struct mok_moe_config {
                                 on m-1.  Results are bitwise those of R = 0.
                                 T*d*2 < 2^31 (the copies and the backward's
                                 gathered x rows use 32-bit offsets).
-                                No compute-unit split between copying and
-                                computing (the pages' explicit split of SMs
-                                between the two, [kucoin §02]): each launch's
-                                256 workgroups take from one queue the copy
-                                tasks of minibatch m+1 (16 rows each) first,
-                                then the UP tiles of m and the DOWN tiles of
-                                m-1, so the share of copy work follows R
-                                instead of a fixed count of mover units.    */
+                                How the workgroups share the copying and the
+                                computing: see mover_cus.                    */
   int64_t ring_bytes;        /* fixed ring token buffer for dispatched rows
                                 ([fluid], [kucoin §02] "macrobatch"), used
                                 with R > 0: floor(ring_bytes / (2 d R)) slots
                                 of R rows, at least 2 (else
                                 MOK_ERR_WORKSPACE); must be 0 when R = 0.       */
   uint32_t flags;            /* MOK_FLAG_*                                      */
-  uint32_t reserved;         /* must be 0                                       */
+  int32_t mover_cus;         /* R > 0: compute units (one workgroup each) that
+                                do only the row copies of each ring launch,
+                                the others only the UP and DOWN tiles (the
+                                pages' explicit split of SMs between moving
+                                tokens and expert compute, [kucoin §02]);
+                                0 = no split: all 256 workgroups take from one
+                                queue the copy tasks of minibatch m+1 (16 rows
+                                each) first, then the UP tiles of m and the
+                                DOWN tiles of m-1.  0..255; must be 0 when
+                                R = 0.  Results are the same bits for every
+                                value.                                         */
   void* const* stage_events; /* NULL, or 2*MOK_NUM_STAGES hipEvent_t handles
                                 (created by the caller): the call records
                                 events[2s] on its stream before stage s and

@@ -953,8 +953,27 @@ __global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a
   const int n_dn = s_dn[gu.E_loc] * ntn_dn;
   const int total = n_cp + n_up + n_dn;
   const int G_ = gridDim.x;
-  const int vb = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
-  for (int t = vb; t < total; t += G_) {
+  // Task t of this workgroup's sequence: with movers, workgroups b < movers
+  // (spread over the XCDs, b % 8) take the copy tasks b, b + movers, ..., the
+  // others the tiles (index b - movers, step G - movers); without, every
+  // workgroup takes from the one sequence of copies, UP and DOWN tiles
+  // (XCD-contiguous order).
+  const int movers = a.movers > 0 && a.movers < G_ ? a.movers : 0;
+  int t0, step, t_end;
+  if (movers == 0) {
+    t0 = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
+    step = G_;
+    t_end = total;
+  } else if ((int)blockIdx.x < movers) {
+    t0 = blockIdx.x;
+    step = movers;
+    t_end = n_cp;
+  } else {
+    t0 = n_cp + (int)blockIdx.x - movers;
+    step = G_ - movers;
+    t_end = total;
+  }
+  for (int t = t0; t < t_end; t += step) {
     if (t < n_cp) {
       // mover task: rows [c0 + t*16, ...) of the next minibatch into its slot
       const int d = gu.d, nv = d / 8;

@@ -45,7 +45,8 @@ mok_status validate_config(const mok_moe_config* cfg, int32_t k) {
   if ((int64_t)c.T * k >= (int64_t(1) << 31)) return MOK_ERR_INVALID_ARG;
   if ((int64_t)c.T * k * (int64_t)(c.d > 2 * c.ffn ? c.d : 2 * c.ffn) >= (int64_t(1) << 40))
     return MOK_ERR_INVALID_ARG;
-  if (c.reserved != 0 || c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
+  if (c.minibatch_rows < 0 || c.ring_bytes < 0) return MOK_ERR_INVALID_ARG;
+  if (c.mover_cus < 0 || c.mover_cus > 255 || (c.mover_cus > 0 && c.minibatch_rows == 0)) return MOK_ERR_INVALID_ARG;
   if (c.flags & ~(MOK_FLAG_SAVE_FOR_BACKWARD | MOK_FLAG_SIGMOID_GATES | MOK_FLAG_RENORM_GATES |
                   MOK_FLAG_SEPARATE_ROUTE_SORT | MOK_FLAG_TILED_GEMMS | MOK_FLAG_STREAM_GEMMS |
                   MOK_FLAG_MXFP8_WGRAD))
@@ -367,6 +368,7 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
     ms.x = x;
     ms.pair_of_row = s_por;
     ms.k = k;
+    ms.movers = c.mover_cus;
     mark_empty_stage(c, s, MOK_STAGE_DISPATCH);
     {
       StageMark mark(c, s, MOK_STAGE_GEMM_UP);  // the whole pipeline

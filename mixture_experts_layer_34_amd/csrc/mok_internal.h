@@ -205,6 +205,7 @@ struct MinibatchStepArgs {
   const int32_t* pair_of_row;
   int k;
   void* ring_dst;         // ring slot receiving row cp0
+  int movers;             // workgroups that only copy (0: one queue for every task)
 };
 hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s);
 hipError_t gemm_f32(int kind, const GroupedGemmArgs& g, hipStream_t s);

@@ -28,6 +28,7 @@ class MoeShape:
     separate_route_sort: bool = False  # never the one-launch router + sort of small calls
     gemm_path: str = "auto"            # forward expert products: "auto", "tiled" or "stream" (small calls)
     mxfp8_wgrad: bool = False          # MXFP8 training: weight gradients on the scaled MFMA too
+    mover_cus: int = 0                 # ring pipeline: workgroups that only copy (0: one shared queue)
 
     @property
     def e_end(self):
@@ -50,7 +51,7 @@ class MoeShape:
                  | (mok.MOK_FLAG_STREAM_GEMMS if self.gemm_path == "stream" else 0)
                  | (mok.MOK_FLAG_MXFP8_WGRAD if self.mxfp8_wgrad else 0))
         return mok.make_config(self.T, self.d, self.E, self.F, self.expert_begin, self.e_end, self.precision,
-                               self.minibatch_rows, self.ring_bytes, flags)
+                               self.minibatch_rows, self.ring_bytes, flags, self.mover_cus)
 
     @property
     def act_dtype(self):

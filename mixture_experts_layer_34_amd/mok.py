@@ -32,7 +32,7 @@ class mok_moe_config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("expert_begin", ctypes.c_int32), ("expert_end", ctypes.c_int32),
                 ("precision", ctypes.c_int32), ("minibatch_rows", ctypes.c_int32),
-                ("ring_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("ring_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32), ("mover_cus", ctypes.c_int32),
                 ("stage_events", ctypes.c_void_p)]
 
 
@@ -127,10 +127,10 @@ def _check(status: int, where: str):
 
 
 def make_config(T, d, E, ffn, expert_begin=0, expert_end=None, precision="bf16", minibatch_rows=0,
-                ring_bytes=0, flags=0, reserved=0) -> mok_moe_config:
+                ring_bytes=0, flags=0, mover_cus=0) -> mok_moe_config:
     prec = PRECISIONS[precision] if isinstance(precision, str) else int(precision)
     return mok_moe_config(T, d, E, ffn, expert_begin, E if expert_end is None else expert_end, prec,
-                          minibatch_rows, ring_bytes, flags, reserved)
+                          minibatch_rows, ring_bytes, flags, mover_cus)
 
 
 def mok_status_string(status: int) -> str:

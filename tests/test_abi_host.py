@@ -52,7 +52,7 @@ def _cfg(**over):
 @pytest.mark.parametrize("over,k", [
     (dict(E=0), 1), (dict(E=1025), 2), (dict(), 0), (dict(), 9), (dict(T=-1), 2), (dict(d=100), 2),
     (dict(ffn=96), 2), (dict(precision=7), 2), (dict(expert_begin=3, expert_end=3), 2),
-    (dict(expert_end=9), 2), (dict(reserved=1), 2), (dict(flags=0x80), 2), (dict(flags=0x30), 2), (dict(minibatch_rows=-1), 2),
+    (dict(expert_end=9), 2), (dict(mover_cus=1), 2), (dict(mover_cus=-1), 2), (dict(flags=0x80), 2), (dict(flags=0x30), 2), (dict(minibatch_rows=-1), 2),
     (dict(precision="f32", d=24), 2),
 ])
 def test_workspace_query_rejects_bad_configs(over, k):

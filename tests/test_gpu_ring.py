@@ -130,3 +130,37 @@ def test_ring_pipeline_train_full_size(train_reference, R):
     note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if v > TOL_BF16}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("movers", [1, 8, 32, 255])
+def test_ring_pipeline_mover_split_bitwise(movers):
+    """The explicit split of the workgroups between row copies and tiles:
+    which workgroup runs a task never changes what it computes, so every
+    mover_cus gives the whole layer's bits (1: one copier; 255: one tile
+    workgroup for every UP and DOWN tile)."""
+    w = W.scaled("bf16_train", T=777, d=128, E=16, k=4, F=320)
+    inp = W.make_inputs(w, device="cuda")
+    ref = _outputs(run_layer(w, inp, backward=True))
+    note(f"ring mover_cus={movers}")
+    shape = shape_of(w, w.T, True)
+    shape.minibatch_rows, shape.ring_bytes, shape.mover_cus = 200, 3 * 200 * w.d * 2, movers
+    buf = run_layer(w, inp, backward=True, buf=MoeBuffers(shape))
+    assert buf.device_status() == (mok.MOK_OK, 0)
+    got = _outputs(buf)
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), f"{k} differs (mover_cus={movers})"
+
+
+def test_ring_pipeline_mover_split_train_full_size(train_reference):
+    """bf16_train at R = 1024 with 32 copy-only workgroups: the whole layer's bits."""
+    w, inp, ref = train_reference
+    note("ring full size R=1024 mover_cus=32")
+    shape = shape_of(w, w.T, True)
+    shape.minibatch_rows = 1024
+    shape.ring_bytes = w.ring_bytes
+    shape.mover_cus = 32
+    buf = run_layer(w, inp, backward=True, buf=MoeBuffers(shape))
+    assert buf.device_status() == (mok.MOK_OK, 0)
+    got = _outputs(buf)
+    for k in ref["whole"]:
+        assert torch.equal(ref["whole"][k], got[k]), f"{k} differs from the whole layer (mover_cus=32)"
