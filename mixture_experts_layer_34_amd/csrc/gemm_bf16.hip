@@ -132,7 +132,9 @@ struct TileJob {
   static constexpr int A_BYTES = GA::BYTES;
   static constexpr int STAGE = GA::BYTES + GB::BYTES;
   static constexpr int D = GA::INST + GB::INST;  // DMA instructions per wave per stage
-  static_assert(STAGE / 4 >= 8192, "epilogue staging needs 8 KB per wave");
+  // Weight-gradient kinds stage their fp32 epilogue in the stage buffers;
+  // the row kinds' callers give them a staging area of NW * EP_BYTES.
+  static_assert(!Tr::GROUP_K || STAGE / 4 >= 8192, "epilogue staging needs 8 KB per wave");
   static_assert(NS >= 2 && NS <= 5 && (NS - 1) * D <= 63, "stage count (vmcnt holds at most 63)");
   static_assert(!(NB == 2 && Tr::B_MN), "paired B matrices are K-contiguous");
   // Which operand copies carry the non-temporal hint (see the macros above).
@@ -914,11 +916,18 @@ __device__ __forceinline__ TileCoord range_tile(const GroupedGemmArgs& g, const 
 }
 
 // A whole tile with no overlap between tiles (issue, K loop, epilogue), with
-// four stage buffers (the ring kernel keeps its range tables in LDS too).
+// four stage buffers in an arena of kRingArena bytes (the ring kernel keeps
+// its range tables in LDS too).  The epilogue staging (8 KB per wave) sits
+// behind the stage buffers where they leave room, else in the last stage
+// buffer, free once the K loop is done.
 constexpr int kRingStages = 4;
+constexpr int kRingArena = 128 * 1024;
 template <int KIND, int BM, int BN>
 __device__ __forceinline__ void run_tile(const GroupedGemmArgs& g, const TileCoord& c, uint8_t* arena) {
   using Job = TileJob<KIND, BM, BN, kRingStages, 32>;
+  constexpr int kStaging = 4 * Job::EP_BYTES;
+  constexpr bool kBehind = kRingStages * Job::STAGE + kStaging <= kRingArena;
+  static_assert(kRingStages * Job::STAGE <= kRingArena && (kBehind || Job::STAGE >= kStaging), "ring arena");
   Job job;
   job.init(g, c);
   job.prologue(arena);
@@ -927,17 +936,59 @@ __device__ __forceinline__ void run_tile(const GroupedGemmArgs& g, const TileCoo
   lds_barrier();
   typename Job::SavedAB pre;
   job.epilogue_prefetch(pre);
-  job.epilogue(acc, arena + (kRingStages - 1) * Job::STAGE, pre);  // the last stage buffer, free now
+  job.epilogue(acc, arena + (kBehind ? kRingStages : kRingStages - 1) * Job::STAGE, pre);
   lds_barrier();
 }
 
-[[maybe_unused]] constexpr int kCopyRows = 16;  // rows per mover task
+// Row tiles of the ring kernel's two GEMMs: UP tiles of 128 rows (128 F
+// columns of both W1 and W3 over K = d) and DOWN tiles of 256 rows (256
+// columns over K = F), so that a minibatch of R rows makes about twice as
+// many UP tiles as 256-row tiles would, each half as long: a launch lasts
+// about as long as its longest tile.  Each output element is still the same
+// MFMA sequence over K as in the whole-layer GEMMs.
+#ifndef MOK_RING_BM_UP
+#define MOK_RING_BM_UP 128
+#endif
+#ifndef MOK_RING_BM_DOWN
+#define MOK_RING_BM_DOWN 256
+#endif
+// 16-byte loads each lane of a copy task issues before their stores.
+#ifndef MOK_RING_COPY_UNROLL
+#define MOK_RING_COPY_UNROLL 8
+#endif
+
+[[maybe_unused]] constexpr int kCopyRows = 16;  // rows per copy task
+
+// Copy task t: rows [c0 + 16 t, ...) of the next minibatch (at most c1) from
+// their tokens' rows of x into the ring slot, MOK_RING_COPY_UNROLL 16-byte
+// loads per lane issued before their stores.
+__device__ __forceinline__ void copy_task(const MinibatchStepArgs& a, int t, int c0, int c1) {
+  constexpr int CU = MOK_RING_COPY_UNROLL;
+  const int tid = threadIdx.x, d = a.up.d, nv = d / 8;
+  const int rb = c0 + t * kCopyRows, re = min(rb + kCopyRows, c1);
+  const int n = (re - rb) * nv;
+  for (int v0 = tid; v0 < n; v0 += 256 * CU) {
+    u32x4_t val[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int v = v0 + u * 256;
+      if (v < n) {
+        const int tok = a.pair_of_row[rb + v / nv] / a.k;
+        val[u] = reinterpret_cast<const u32x4_t*>((const bf16_t*)a.x + (int64_t)tok * d)[v % nv];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int v = v0 + u * 256;
+      if (v < n) reinterpret_cast<u32x4_t*>((bf16_t*)a.ring_dst + (int64_t)(rb + v / nv - c0) * d)[v % nv] = val[u];
+    }
+  }
+}
 
 __global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using JobUp = TileJob<KIND_UP, 256, 128, kRingStages, 32>;
-  static_assert(JobUp::STAGE == TileJob<KIND_DOWN, 256, 256, kRingStages, 32>::STAGE, "one arena");
-  __shared__ __attribute__((aligned(1024))) uint8_t arena[kRingStages * JobUp::STAGE];
+  constexpr int BMU = MOK_RING_BM_UP, BMD = MOK_RING_BM_DOWN;
+  __shared__ __attribute__((aligned(1024))) uint8_t arena[kRingArena];
   __shared__ int32_t s_up[1025], s_dn[1025], s_wsum[4];
   const int tid = threadIdx.x;
   const GroupedGemmArgs& gu = a.up;
@@ -945,57 +996,85 @@ __global__ __launch_bounds__(256) void minibatch_step_kernel(MinibatchStepArgs a
   const int u0 = min(a.up0, P), u1 = min(a.up1, P);
   const int d0 = min(a.dn0, P), d1 = min(a.dn1, P);
   const int c0 = min(a.cp0, P), c1 = min(a.cp1, P);
-  range_tile_prefix<256>(gu, u0, u1, s_up, s_wsum);
-  range_tile_prefix<256>(a.down, d0, d1, s_dn, s_wsum);
+  range_tile_prefix<BMU>(gu, u0, u1, s_up, s_wsum);
+  range_tile_prefix<BMD>(a.down, d0, d1, s_dn, s_wsum);
   const int ntn_up = (gu.F + 127) / 128, ntn_dn = (gu.d + 255) / 256;
   const int n_cp = (c1 - c0 + kCopyRows - 1) / kCopyRows;
   const int n_up = s_up[gu.E_loc] * ntn_up;
   const int n_dn = s_dn[gu.E_loc] * ntn_dn;
-  const int total = n_cp + n_up + n_dn;
   const int G_ = gridDim.x;
-  // Task t of this workgroup's sequence: with movers, workgroups b < movers
-  // (spread over the XCDs, b % 8) take the copy tasks b, b + movers, ..., the
-  // others the tiles (index b - movers, step G - movers); without, every
-  // workgroup takes from the one sequence of copies, UP and DOWN tiles
-  // (XCD-contiguous order).
   const int movers = a.movers > 0 && a.movers < G_ ? a.movers : 0;
-  int t0, step, t_end;
-  if (movers == 0) {
-    t0 = (G_ % 8 == 0) ? (blockIdx.x % 8) * (G_ / 8) + blockIdx.x / 8 : blockIdx.x;
-    step = G_;
-    t_end = total;
-  } else if ((int)blockIdx.x < movers) {
-    t0 = blockIdx.x;
-    step = movers;
-    t_end = n_cp;
+  // Tasks: n_cp row copies, n_up UP tiles, n_dn DOWN tiles.  With movers,
+  // workgroups b < movers (spread over the XCDs, b % 8) take the copies b,
+  // b + movers, ... and the other workgroups only the tiles.  The tiles (and,
+  // without movers, the copies) are cut into eight runs: run x holds the x-th
+  // eighth of the UP tiles, then of the DOWN tiles, then of the copies, so
+  // the longest tasks of a run come first and neighbouring tiles, which read
+  // the same weight columns, share an XCD's L2.  The workgroups of XCD x take
+  // run x's tasks in order from counter x and, once it is exhausted, those of
+  // the next runs in turn; which workgroup runs a task never changes what it
+  // computes.  The last workgroup to finish leaves every counter at zero for
+  // the next launch.
+  const int n_rcp = movers ? 0 : n_cp;
+  auto cut = [](int n, int x) { return (int)(((int64_t)n * x) >> 3); };
+  auto run_len = [&](int x) {
+    return cut(n_up, x + 1) - cut(n_up, x) + cut(n_dn, x + 1) - cut(n_dn, x) + cut(n_rcp, x + 1) - cut(n_rcp, x);
+  };
+  // Task index (copies first, then UP, then DOWN) of position v of run x.
+  auto run_task = [&](int x, int v) {
+    const int lu = cut(n_up, x + 1) - cut(n_up, x);
+    if (v < lu) return n_cp + cut(n_up, x) + v;
+    v -= lu;
+    const int ld = cut(n_dn, x + 1) - cut(n_dn, x);
+    if (v < ld) return n_cp + n_up + cut(n_dn, x) + v;
+    return cut(n_rcp, x) + v - ld;
+  };
+  __shared__ int s_take;
+  auto take = [&](int x) -> int {
+    if (tid == 0) s_take = atomicAdd(a.ctr + x, 1);
+    __syncthreads();
+    const int v = __builtin_amdgcn_readfirstlane(s_take);
+    __syncthreads();
+    return v;
+  };
+  if ((int)blockIdx.x < movers) {
+    for (int t = blockIdx.x; t < n_cp; t += movers) copy_task(a, t, c0, c1);
   } else {
-    t0 = n_cp + (int)blockIdx.x - movers;
-    step = G_ - movers;
-    t_end = total;
-  }
-  for (int t = t0; t < t_end; t += step) {
-    if (t < n_cp) {
-      // mover task: rows [c0 + t*16, ...) of the next minibatch into its slot
-      const int d = gu.d, nv = d / 8;
-      const int rb = c0 + t * kCopyRows, re = min(rb + kCopyRows, c1);
-      for (int v = tid; v < (re - rb) * nv; v += 256) {
-        const int r = rb + v / nv, c = v % nv;
-        const int tok = a.pair_of_row[r] / a.k;
-        const u32x4_t val = reinterpret_cast<const u32x4_t*>((const bf16_t*)a.x + (int64_t)tok * d)[c];
-        reinterpret_cast<u32x4_t*>((bf16_t*)a.ring_dst + (int64_t)(r - c0) * d)[c] = val;
+    int x = blockIdx.x % 8;
+    for (int hop = 0; hop < 8; ++hop, x = (x + 1) & 7) {
+      const int len = run_len(x);
+      for (int v = take(x); v < len; v = take(x)) {
+        const int t = run_task(x, v);
+        if (t < n_cp) {
+          copy_task(a, t, c0, c1);
+        } else if (t < n_cp + n_up) {
+          run_tile<KIND_UP, BMU, 128>(gu, range_tile(gu, s_up, ntn_up, BMU, u0, u1, t - n_cp, 128), arena);
+        } else {
+          run_tile<KIND_DOWN, BMD, 256>(a.down, range_tile(a.down, s_dn, ntn_dn, BMD, d0, d1, t - n_cp - n_up, 256),
+                                        arena);
+        }
       }
-    } else if (t < n_cp + n_up) {
-      run_tile<KIND_UP, 256, 128>(gu, range_tile(gu, s_up, ntn_up, 256, u0, u1, t - n_cp, 128), arena);
-    } else {
-      run_tile<KIND_DOWN, 256, 256>(a.down, range_tile(a.down, s_dn, ntn_dn, 256, d0, d1, t - n_cp - n_up, 256),
-                                    arena);
     }
+  }
+  if (tid == 0) {
+    // every workgroup has taken its last task index once this count is full
+    if (atomicAdd(a.ctr + 8, 1) == G_ - 1)
+      for (int i = 0; i < kRingCounters; ++i) atomicExch(a.ctr + i, 0);
   }
 #endif
 }
 
 hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(minibatch_step_kernel, dim3(256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ void ring_reset_kernel(int32_t* ctr) {
+  if (threadIdx.x < kRingCounters) ctr[threadIdx.x] = 0;
+}
+
+hipError_t launch_ring_reset(int32_t* ctr, hipStream_t s) {
+  hipLaunchKernelGGL(ring_reset_kernel, dim3(1), dim3(64), 0, s, ctr);
   return hipGetLastError();
 }
 

@@ -369,7 +369,10 @@ mok_status forward_checked(const void* x, const float* router_logits, const void
     ms.pair_of_row = s_por;
     ms.k = k;
     ms.movers = c.mover_cus;
+    ms.ctr = at<int32_t>(workspace, wl.queue) + 32;  // past the backward's 16 queue counters
+    static_assert(32 + kRingCounters <= 64, "queue region");
     mark_empty_stage(c, s, MOK_STAGE_DISPATCH);
+    MOK_HIP(launch_ring_reset(ms.ctr, s));
     {
       StageMark mark(c, s, MOK_STAGE_GEMM_UP);  // the whole pipeline
       for (int m = -1; m <= M; ++m) {

@@ -206,8 +206,12 @@ struct MinibatchStepArgs {
   int k;
   void* ring_dst;         // ring slot receiving row cp0
   int movers;             // workgroups that only copy (0: one queue for every task)
+  int32_t* ctr;           // kRingCounters task counters, zero before the launch and left zero by it
 };
+constexpr int kRingCounters = 9;  // one per XCD run, and the count of finished workgroups
 hipError_t launch_minibatch_step(const MinibatchStepArgs& a, hipStream_t s);
+// Zeroes the ring kernel's task counters (before the first launch of a call).
+hipError_t launch_ring_reset(int32_t* ctr, hipStream_t s);
 hipError_t gemm_f32(int kind, const GroupedGemmArgs& g, hipStream_t s);
 hipError_t gemm_mxfp8(int kind, const GroupedGemmArgs& g, hipStream_t s);
 // MXFP4 forward (inference) UP and DOWN: the MXFP8 kernels with E2M1 operands
