@@ -158,12 +158,12 @@ typedef struct mok_moe_config {
                                 the others only the UP and DOWN tiles (the
                                 pages' explicit split of SMs between moving
                                 tokens and expert compute, [kucoin §02]);
-                                0 = no split: all 256 workgroups take from one
-                                queue the copy tasks of minibatch m+1 (16 rows
-                                each) first, then the UP tiles of m and the
-                                DOWN tiles of m-1.  0..255; must be 0 when
-                                R = 0.  Results are the same bits for every
-                                value.                                         */
+                                0 = no split: all 256 workgroups take every
+                                task (the copies of minibatch m+1, 16 rows
+                                each, the UP tiles of m and the DOWN tiles of
+                                m-1) from eight per-XCD runs through device
+                                counters.  0..255; must be 0 when R = 0.
+                                Results are the same bits for every value. */
   void* const* stage_events; /* NULL, or 2*MOK_NUM_STAGES hipEvent_t handles
                                 (created by the caller): the call records
                                 events[2s] on its stream before stage s and
