@@ -99,8 +99,10 @@ def stage_work(w, P, U, save_for_backward=True, mxfp8_wgrad=False):
     if mx and mxfp8_wgrad:
         gemm_bytes["gemm_dw2"] = P * d * q + P * F * q + El * d * F * 4
         gemm_bytes["gemm_dw13"] = 2 * P * F * q + P * d * q + 2 * El * F * d * 4
-        # dY is formed again from dout (U token rows) and the gates
+        # dY is formed again from dout (U token rows) and the gates, so the
+        # reverse-combine writes no bf16 dY rows
         nbytes["regather"] = (P * F + 2 * P * F) * s + 2 * U * d * s + (2 * d + 3 * F) * P * q
+        nbytes["bwd_gate"] -= P * d * s
     nbytes.update(gemm_bytes)
     return flops, nbytes
 

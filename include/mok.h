@@ -250,7 +250,8 @@ mok_status mok_moe_saved_layout(const mok_moe_config* cfg, int32_t k, mok_saved_
  *             both for [dA | dB], 2F wide); nothing otherwise;
  *   dy, dab, dxp  backward row buffers dY [P_max, d], [dA | dB] [P_max, 2F],
  *             dX_perm [P_max, d] (bf16; absent from an MXFP8 forward-only
- *             configuration);
+ *             configuration; no dY rows with MOK_FLAG_MXFP8_WGRAD, whose
+ *             weight gradients form dY again from dout and the gates);
  *   wq, wq_scale, k_pad  with MOK_FLAG_MXFP8_WGRAD: the row-quantised
  *             operands of the weight gradients, transposed: E4M3 codes of dY
  *             (d rows), H (F rows), [dA | dB] (2F rows) and x (d rows), each

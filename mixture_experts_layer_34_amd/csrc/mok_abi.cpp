@@ -146,7 +146,9 @@ void workspace_layout(const mok_moe_config& c, int32_t k, WorkspaceLayout* w) {
   w->xp_scale = o;      o = align256(o + (mx ? (size_t)w->xp_rows * (c.d / 32) : 0));
   w->hq = o;            o = align256(o + (mx ? Tk * hq_cols / epb : 0));
   w->hq_scale = o;      o = align256(o + (mx ? Tk * (hq_cols / 32) : 0));
-  w->dy = o;            o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
+  // MXFP8 weight gradients form dY again from dout: no bf16 dY rows
+  const bool mxw_dy = mxb && (c.flags & MOK_FLAG_MXFP8_WGRAD);
+  w->dy = o;            o = align256(o + ((mx && !mxb) || mxw_dy ? 0 : Tk * c.d * A));
   w->dab = o;           o = align256(o + (mx && !mxb ? 0 : Tk * 2 * c.ffn * A));
   w->dxp = o;           o = align256(o + (mx && !mxb ? 0 : Tk * c.d * A));
   w->queue = o;         o = align256(o + 256);
@@ -765,7 +767,8 @@ mok_status mok_moe_backward_mxfp8(const void* dout, const void* x, const float* 
 
   // reverse-combine with the router backward; dY also as MXFP8 along d
   MOK_STAGE(MOK_STAGE_BWD_GATE, launch_backward_gate(dout, at<void>(saved, sl.Y), s_gate, s_idx, s_rop, router_logits,
-                                                      s_lse, T, k, E, d, gating_of(c), 1, dgate, drouter_logits, dy,
+                                                      s_lse, T, k, E, d, gating_of(c), 1, dgate, drouter_logits,
+                                                      (c.flags & MOK_FLAG_MXFP8_WGRAD) ? nullptr : dy,
                                                       queue, 16, dyq, dys, wl.xp_rows, P_max, status, s));
   GroupedGemmArgs g{};
   g.offsets = at<int32_t>(saved, sl.offsets);

@@ -662,7 +662,7 @@ __global__ __launch_bounds__(256) void backward_gate_kernel(const T* __restrict_
             part[i] = fmaf(o[q], y[q], part[i]);
             z[q] = g[i] * o[q];
           }
-          Vec8<T>::store(dyr[i], v, z);
+          if (dy) Vec8<T>::store(dyr[i], v, z);  // no bf16 dY rows: MXFP8 codes only
           if constexpr (MX) {
             // lanes 4m .. 4m + 3 hold the 32 values of one block (d % 64 == 0
             // in MXFP8, so a group of eight lanes is active or inactive as a
@@ -743,6 +743,7 @@ hipError_t launch_backward_gate(const void* dout, const void* Y, const float* ga
                                 int32_t* queue_zero, int nqueue, uint8_t* dyq, uint8_t* dys, int64_t dys_rows,
                                 int64_t nrows, int32_t* status, hipStream_t s) {
   int blocks = T < 16384 ? (T > 0 ? T : 1) : 16384;  // at least one block: it zeroes the counters
+  if (!dy && !dyq) return hipErrorInvalidValue;  // dY goes somewhere
 #define MOK_BWD_GATE(TT, GV, MXV)                                                                              \
   hipLaunchKernelGGL((backward_gate_kernel<TT, GV, MXV>), dim3(blocks), dim3(256), 0, s, (const TT*)dout,      \
                      (const TT*)Y, gate, idx, row_of_pair, logits, lse, T, k, E, d, dgate, dlogits, (TT*)dy,    \

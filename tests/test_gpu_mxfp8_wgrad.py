@@ -4,7 +4,8 @@ Three checks, each pinning one step:
   * the row quantiser: the transposed operands (dY, H, [dA | dB] and the x
     rows) equal the oracle's quantiser applied to the same bf16 rows bit for
     bit (codes per column and expert segment, pair-plane scales, zero codes
-    past each expert's rows);
+    past each expert's rows); the bf16 dY rows, which this mode never
+    stores, formed on the host as the kernels form them;
   * the scaled-MFMA products: dW1, dW3, dW2 against the float64 product of
     the device's own dequantised codes, within 1e-3 (infinity norm, relative;
     measured 1e-4 - 3e-4, the MFMA's accumulation);
@@ -58,10 +59,15 @@ def _operands(w, inp, buf):
     P = int(to_np(buf.offsets)[w.e_end])
     codes = buf.workspace[lay["wq"]:lay["wq"] + (2 * d + 3 * F) * kp].cpu().numpy()
     scales = buf.workspace[lay["wq_scale"]:lay["wq_scale"] + (2 * d + 3 * F) * kp // 32].cpu().numpy()
-    dy = buf.workspace_view("dy", torch.bfloat16, (s.T * s.k, d))[:P].float().cpu().numpy()
+    por = saved_arrays(buf)["pair_of_row"][:P]
+    # dY rows as the kernels form them (no bf16 dY buffer in this mode): one
+    # fp32 product of the pair's gate and its token's dout row, rounded to
+    # bf16 to nearest even
+    gate = buf.topk_gate.reshape(-1).cpu()[torch.from_numpy(por).long()]
+    dout = inp["dout"].cpu()[torch.from_numpy(por // w.k).long()].float()
+    dy = (gate[:, None] * dout).to(torch.bfloat16).float().numpy()
     dab = buf.workspace_view("dab", torch.bfloat16, (s.T * s.k, 2 * F))[:P].float().cpu().numpy()
     H = buf.saved_view("H", torch.bfloat16, (s.T * s.k, F))[:P].float().cpu().numpy()
-    por = saved_arrays(buf)["pair_of_row"][:P]
     X = to_np(inp["x"])[por // w.k]
     out, c_off, s_off = [], 0, 0
     for name, M in (("dY", dy), ("H", H), ("dA|dB", dab), ("X", X)):
